@@ -1,0 +1,788 @@
+/*
+ * CPU oracle for SPIN-4DGS-style decode + render.  TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the plain, slow definition that the HIP path is checked
+ * against.  Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg load it.  It shares no source, header, table or constant with the HIP
+ * library; both sides are written independently from the pages:
+ *
+ *   [SPIN] "Implicit 4D Gaussian Splatting for Fast Motion with Large
+ *          Inter-Frame Displacements" (SPIN-4DGS), §3.1 Eq. 1-4, §3.3 Eq. 7-11.
+ *   [HEX]  "4D Gaussian Splatting详解：动态场景实时渲染的范式突破",
+ *          §2.2, §3.1 (HexPlane six planes), §3.2 (deformation MLP), §6.1.
+ *
+ * Precision.  Interpolation, MLPs, activations and compositing run in fp64.
+ * Two steps whose floating-point result decides an integer run in fp32 with a
+ * fixed operation order (one IEEE op per step, left to right, no FMA,
+ * correctly rounded '/' and sqrt), exactly as the kernels do:
+ *   - position normalisation (decides the hash-grid cell), and
+ *   - projection (decides the tile rectangle and the depth bits of the sort
+ *     key).
+ * Build with -ffp-contract=off and without fast-math.
+ *
+ * Parity status: every exported function is pinned by tests/test_oracle_*.py
+ * (closed forms, library routines, brute force, invariants).  Agreement with
+ * trained SPIN-4DGS images is "parity unpinned" (no data or weights exist).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 <-> double, from the format definition                      */
+/* ------------------------------------------------------------------------ */
+
+EXPORT double orc_half_to_double(uint16_t h) {
+    int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* Round to nearest, ties to even. */
+EXPORT uint16_t orc_double_to_half(double x) {
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x)) return 0x7e00;
+    if (a >= 65520.0) return sign | 0x7c00; /* halfway above 65504 -> inf */
+    if (a < ldexp(1.0, -14)) {              /* subnormal range, quantum 2^-24 */
+        double m = nearbyint(a * 16777216.0);
+        return (uint16_t)(sign | (uint16_t)m); /* m == 1024 encodes 2^-14 */
+    }
+    int e;
+    frexp(a, &e);                    /* a in [2^(e-1), 2^e) */
+    double m = nearbyint(ldexp(a, 11 - e)); /* in [1024, 2048] */
+    if (m == 2048.0) { m = 1024.0; e += 1; }
+    int E = e - 1 + 15;
+    if (E >= 31) return sign | 0x7c00;
+    return (uint16_t)(sign | (E << 10) | ((int)m - 1024));
+}
+
+static double round_f16(double x) { return orc_half_to_double(orc_double_to_half(x)); }
+
+/* ------------------------------------------------------------------------ */
+/* Hash encoder description ([SPIN] §3.3 Eq. 9; Instant-NGP extended by t)   */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int L, F, log2T;
+    double base_res, growth;
+    int temporal_res; /* 0: same as the level's spatial resolution */
+    int table_f16;
+    float t_min, t_max;
+} orc_hash;
+
+/* Level resolution res_l = floor(base * growth^l) (vertices per axis). */
+EXPORT void orc_level_res(const orc_hash* h, int* res_s, int* res_t, int* dense) {
+    double T = ldexp(1.0, h->log2T);
+    for (int l = 0; l < h->L; ++l) {
+        int r = (int)floor(h->base_res * pow(h->growth, (double)l));
+        int rt = h->temporal_res > 0 ? h->temporal_res : r;
+        res_s[l] = r;
+        res_t[l] = rt;
+        dense[l] = ((double)r * (double)r * (double)r * (double)rt) <= T;
+    }
+}
+
+/*
+ * Normalisation, [SPIN] §3.3 Eq. 7 (scene contraction, L2 norm) and Eq. 8
+ * (time).  fp32, fixed order:
+ *   n2 = (x*x + y*y) + z*z;  n = sqrt(n2)
+ *   n <= 1: c = mu;  else k = (2 - 1/n) / n, c = mu * k
+ *   mu_bar = 0.25*c + 0.5
+ *   t_norm = clamp((t - t_min) / (t_max - t_min), 0, 1)
+ * pos has `stride` floats per point (3: xyz with the scalar t, 4: xyzt).
+ */
+EXPORT void orc_normalize(const orc_hash* h, const float* pos, int stride, float t_scalar, long N,
+                          float* xt) {
+    for (long i = 0; i < N; ++i) {
+        const float* p = pos + i * stride;
+        float x = p[0], y = p[1], z = p[2];
+        float n2 = x * x + y * y;
+        n2 = n2 + z * z;
+        float n = sqrtf(n2);
+        float c0 = x, c1 = y, c2 = z;
+        if (!(n <= 1.0f)) {
+            float k = 2.0f - 1.0f / n;
+            k = k / n;
+            c0 = x * k;
+            c1 = y * k;
+            c2 = z * k;
+        }
+        float t = stride == 4 ? p[3] : t_scalar;
+        float tn = (t - h->t_min) / (h->t_max - h->t_min);
+        tn = tn < 0.0f ? 0.0f : (tn > 1.0f ? 1.0f : tn);
+        float a0 = 0.25f * c0, a1 = 0.25f * c1, a2 = 0.25f * c2;
+        xt[i * 4 + 0] = a0 + 0.5f;
+        xt[i * 4 + 1] = a1 + 0.5f;
+        xt[i * 4 + 2] = a2 + 0.5f;
+        xt[i * 4 + 3] = tn;
+    }
+}
+
+/* Spatial hash of a 4D vertex: XOR of coordinate * prime, mod T.  The first
+ * three primes are Instant-NGP's; the fourth (time) is a fixed odd constant. */
+static uint32_t hash4(uint32_t ix, uint32_t iy, uint32_t iz, uint32_t it, uint32_t mask) {
+    uint32_t hsh = ix * 1u;
+    hsh ^= iy * 2654435761u;
+    hsh ^= iz * 805459861u;
+    hsh ^= it * 3674653429u;
+    return hsh & mask;
+}
+
+static double table_at(const orc_hash* h, const void* tables, long level, long idx, int k) {
+    long T = 1L << h->log2T;
+    long off = (level * T + idx) * h->F + k;
+    if (h->table_f16) return orc_half_to_double(((const uint16_t*)tables)[off]);
+    return (double)((const float*)tables)[off];
+}
+
+/*
+ * 4D multiresolution hash encoding, [SPIN] §3.3 Eq. 9, with quadrilinear
+ * interpolation over the 16 corners of the cell.  Per axis (fp32, the cell
+ * decision): p = xt*(res-1), i = clamp(floor(p), 0, res-2), f = p - i.  The
+ * corner weights and the weighted sum are fp64.  Corner c: bit k adds one on
+ * axis k (x, y, z, t); weight = prod_k (bit ? f_k : 1 - f_k).  Level l is
+ * dense (row-major x fastest) iff res^3 * res_t <= T, otherwise hashed.
+ * z[l*F + k] = sum_c w_c * table[l][idx_c][k].
+ */
+EXPORT void orc_encode(const orc_hash* h, const void* tables, const float* xt, long N, double* z) {
+    int res_s[64], res_t[64], dense[64];
+    orc_level_res(h, res_s, res_t, dense);
+    uint32_t mask = (uint32_t)((1UL << h->log2T) - 1);
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; ++i) {
+        for (int l = 0; l < h->L; ++l) {
+            int res[4] = {res_s[l], res_s[l], res_s[l], res_t[l]};
+            int ci[4];
+            double f[4];
+            for (int a = 0; a < 4; ++a) {
+                float p = xt[i * 4 + a] * (float)(res[a] - 1);
+                float fl = floorf(p);
+                int c = (int)fl;
+                if (c < 0) c = 0;
+                if (c > res[a] - 2) c = res[a] - 2;
+                ci[a] = c;
+                f[a] = (double)p - (double)c;
+            }
+            double acc[8] = {0};
+            for (int corner = 0; corner < 16; ++corner) {
+                double w = 1.0;
+                uint32_t v[4];
+                for (int a = 0; a < 4; ++a) {
+                    int bit = (corner >> a) & 1;
+                    v[a] = (uint32_t)(ci[a] + bit);
+                    w *= bit ? f[a] : 1.0 - f[a];
+                }
+                long idx;
+                if (dense[l])
+                    idx = (long)v[0] + (long)res[0] * ((long)v[1] + (long)res[1] * ((long)v[2] + (long)res[2] * (long)v[3]));
+                else
+                    idx = (long)hash4(v[0], v[1], v[2], v[3], mask);
+                for (int k = 0; k < h->F; ++k) acc[k] += w * table_at(h, tables, l, idx, k);
+            }
+            for (int k = 0; k < h->F; ++k) z[i * (long)(h->L * h->F) + l * h->F + k] = acc[k];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MLP, [SPIN] §3.3 Eq. 10-11                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int n_layers;  /* number of linear layers (the last one is the head block) */
+    int dims[8];   /* dims[0] = input width, dims[l+1] = output width of layer l */
+    int act;       /* hidden activation: 0 = ReLU, 1 = GELU (exact erf) */
+    int w_f16;     /* weights stored as binary16 (else fp32) */
+} orc_mlp;
+
+static double act_fn(int act, double x) {
+    if (act == 0) return x > 0.0 ? x : 0.0;
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
+
+/*
+ * y = act(W x + b) for every layer but the last, which stays linear.
+ * W is row-major [out][in].  mode 0: fp64 throughout.  mode 1 ("fp16
+ * emulation"): the input and every hidden activation are rounded to binary16
+ * (RNE) before they enter the next layer, as an fp16-in/fp32-accumulate
+ * device path does; sums stay fp64.
+ */
+EXPORT void orc_mlp_forward(const orc_mlp* m, const void* const* W, const float* const* b,
+                            const double* in, long N, int mode, double* out) {
+    int in_dim = m->dims[0], out_dim = m->dims[m->n_layers];
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; ++i) {
+        double bufa[512], bufb[512];
+        double* x = bufa;
+        double* y = bufb;
+        for (int k = 0; k < in_dim; ++k) x[k] = mode ? round_f16(in[i * in_dim + k]) : in[i * in_dim + k];
+        for (int l = 0; l < m->n_layers; ++l) {
+            int di = m->dims[l], dout = m->dims[l + 1];
+            for (int o = 0; o < dout; ++o) {
+                double s = 0.0;
+                for (int k = 0; k < di; ++k) {
+                    double w = m->w_f16 ? orc_half_to_double(((const uint16_t*)W[l])[(long)o * di + k])
+                                        : (double)((const float*)W[l])[(long)o * di + k];
+                    s += w * x[k];
+                }
+                s += (double)b[l][o];
+                if (l + 1 < m->n_layers) {
+                    s = act_fn(m->act, s);
+                    if (mode) s = round_f16(s);
+                }
+                y[o] = s;
+            }
+            double* tmp = x; x = y; y = tmp;
+        }
+        for (int o = 0; o < out_dim; ++o) out[i * out_dim + o] = x[o];
+    }
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/*
+ * Eq. 11 activations on the 11 head outputs [s(3) | r(4) w,x,y,z | c(3) | o]:
+ *   s = exp(min(s_hat, 20))   (the pre-activation clip at 20, §3.3 scale head)
+ *   r = r_hat / max(||r_hat||, 1e-12)
+ *   c = sigmoid(c_hat),  o = sigmoid(o_hat)
+ */
+EXPORT void orc_activate(const double* raw, long N, double* scales, double* quats, double* colors,
+                         double* opacity) {
+    for (long i = 0; i < N; ++i) {
+        const double* r = raw + i * 11;
+        for (int k = 0; k < 3; ++k) scales[i * 3 + k] = exp(r[k] < 20.0 ? r[k] : 20.0);
+        double n = sqrt(r[3] * r[3] + r[4] * r[4] + r[5] * r[5] + r[6] * r[6]);
+        if (n < 1e-12) n = 1e-12;
+        for (int k = 0; k < 4; ++k) quats[i * 4 + k] = r[3 + k] / n;
+        for (int k = 0; k < 3; ++k) colors[i * 3 + k] = sigmoid(r[7 + k]);
+        opacity[i] = sigmoid(r[10]);
+    }
+}
+
+/* Full decode: normalise -> encode -> MLP -> activations.  raw is [N][11]. */
+EXPORT void orc_decode(const orc_hash* h, const void* tables, const orc_mlp* m, const void* const* W,
+                       const float* const* b, const float* pos, int stride, float t_scalar, long N,
+                       int mode, double* raw, double* scales, double* quats, double* colors,
+                       double* opacity) {
+    long LF = (long)h->L * h->F;
+    float* xt = (float*)malloc(sizeof(float) * 4 * (size_t)(N > 0 ? N : 1));
+    double* z = (double*)malloc(sizeof(double) * (size_t)LF * (size_t)(N > 0 ? N : 1));
+    orc_normalize(h, pos, stride, t_scalar, N, xt);
+    orc_encode(h, tables, xt, N, z);
+    orc_mlp_forward(m, W, b, z, N, mode, raw);
+    orc_activate(raw, N, scales, quats, colors, opacity);
+    free(xt);
+    free(z);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Real spherical harmonics, degree 3 (16 functions, l-major, m = -l..l)      */
+/* ------------------------------------------------------------------------ */
+
+/* Orthonormal real basis built from the complex harmonics with the
+ * Condon-Shortley phase: Y_l0, and sqrt(2) Re / Im of Y_l^|m| for m > 0 / m < 0.
+ * Written as polynomials in the unit direction (x, y, z). */
+EXPORT void orc_sh_basis(const double* dirs, long N, double* Y) {
+    const double pi = 3.14159265358979323846;
+    const double k00 = 0.5 * sqrt(1.0 / pi);
+    const double k1 = sqrt(3.0 / (4.0 * pi));
+    const double k2a = 0.5 * sqrt(15.0 / pi), k2b = 0.25 * sqrt(5.0 / pi), k2c = 0.25 * sqrt(15.0 / pi);
+    const double k3a = 0.25 * sqrt(35.0 / (2.0 * pi)), k3b = 0.5 * sqrt(105.0 / pi);
+    const double k3c = 0.25 * sqrt(21.0 / (2.0 * pi)), k3d = 0.25 * sqrt(7.0 / pi);
+    const double k3e = 0.25 * sqrt(105.0 / pi);
+    for (long i = 0; i < N; ++i) {
+        double x = dirs[i * 3], y = dirs[i * 3 + 1], z = dirs[i * 3 + 2];
+        double* o = Y + i * 16;
+        double xx = x * x, yy = y * y, zz = z * z;
+        o[0] = k00;
+        o[1] = -k1 * y;
+        o[2] = k1 * z;
+        o[3] = -k1 * x;
+        o[4] = k2a * x * y;
+        o[5] = -k2a * y * z;
+        o[6] = k2b * (2.0 * zz - xx - yy);
+        o[7] = -k2a * x * z;
+        o[8] = k2c * (xx - yy);
+        o[9] = -k3a * y * (3.0 * xx - yy);
+        o[10] = k3b * x * y * z;
+        o[11] = -k3c * y * (4.0 * zz - xx - yy);
+        o[12] = k3d * z * (2.0 * zz - 3.0 * xx - 3.0 * yy);
+        o[13] = -k3c * x * (4.0 * zz - xx - yy);
+        o[14] = k3e * z * (xx - yy);
+        o[15] = -k3a * x * (xx - 3.0 * yy);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* HexPlane deformation, [HEX] §3.1-§3.2, §6.1                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int res_xyz, res_t, C;
+    float aabb; /* positions map to [0,1] through [-aabb, aabb]^3, clamped */
+} orc_hexplane;
+
+/*
+ * Features: six planes XY, XZ, YZ (res_xyz^2) and XT, YT, ZT (res_xyz x res_t,
+ * time on the second axis), each [res_b][res_a][C] binary16; bilinear per
+ * plane with vertices at 0..res-1; concatenated in that order (6*C values).
+ * Cell decision in fp32: u = clamp((x + aabb) / (2 aabb), 0, 1),
+ * p = u*(res-1), i = clamp(floor(p), 0, res-2), f = p - i.  t is used as is
+ * (already in [0,1]).
+ */
+EXPORT void orc_hexplane_features(const orc_hexplane* hp, const uint16_t* const* planes,
+                                  const float* means, float t, long N, double* feat) {
+    static const int pa[6] = {0, 0, 1, 0, 1, 2}; /* first axis of each plane */
+    static const int pb[6] = {1, 2, 2, 3, 3, 3}; /* second axis (3 = time) */
+    float tt = t < 0.0f ? 0.0f : (t > 1.0f ? 1.0f : t);
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; ++i) {
+        float u[4];
+        for (int a = 0; a < 3; ++a) {
+            float v = means[i * 3 + a] + hp->aabb;
+            v = v / (2.0f * hp->aabb);
+            u[a] = v < 0.0f ? 0.0f : (v > 1.0f ? 1.0f : v);
+        }
+        u[3] = tt;
+        for (int p = 0; p < 6; ++p) {
+            int ra = hp->res_xyz, rb = pb[p] == 3 ? hp->res_t : hp->res_xyz;
+            float qa = u[pa[p]] * (float)(ra - 1), qb = u[pb[p]] * (float)(rb - 1);
+            int ia = (int)floorf(qa), ib = (int)floorf(qb);
+            if (ia < 0) ia = 0;
+            if (ia > ra - 2) ia = ra - 2;
+            if (ib < 0) ib = 0;
+            if (ib > rb - 2) ib = rb - 2;
+            double fa = (double)qa - ia, fb = (double)qb - ib;
+            const uint16_t* P = planes[p];
+            for (int c = 0; c < hp->C; ++c) {
+                double v00 = orc_half_to_double(P[((long)ib * ra + ia) * hp->C + c]);
+                double v01 = orc_half_to_double(P[((long)ib * ra + ia + 1) * hp->C + c]);
+                double v10 = orc_half_to_double(P[((long)(ib + 1) * ra + ia) * hp->C + c]);
+                double v11 = orc_half_to_double(P[((long)(ib + 1) * ra + ia + 1) * hp->C + c]);
+                feat[i * 6L * hp->C + p * hp->C + c] = (1 - fa) * (1 - fb) * v00 + fa * (1 - fb) * v01 +
+                                                       (1 - fa) * fb * v10 + fa * fb * v11;
+            }
+        }
+    }
+}
+
+/*
+ * Deform canonical Gaussians at time t: features -> MLP (ReLU hidden) -> 58
+ * outputs [dpos(3) | dquat(4) | dlog_scale(3) | dsh(48)], then
+ *   mu' = mu + dpos;  q' = (q + dq) / ||q + dq||;  s' = s * exp(dlog_scale)
+ *   sh' = sh + dsh;   opacity unchanged ([HEX] §6.1).
+ */
+EXPORT void orc_hexplane_deform(const orc_hexplane* hp, const uint16_t* const* planes, const orc_mlp* m,
+                                const void* const* W, const float* const* b, const float* means,
+                                const float* scales, const float* quats, const float* sh, float t, long N,
+                                int mode, double* o_means, double* o_scales, double* o_quats, double* o_sh) {
+    long D = 6L * hp->C;
+    double* feat = (double*)malloc(sizeof(double) * (size_t)D * (size_t)(N > 0 ? N : 1));
+    double* raw = (double*)malloc(sizeof(double) * 58 * (size_t)(N > 0 ? N : 1));
+    orc_hexplane_features(hp, planes, means, t, N, feat);
+    orc_mlp_forward(m, W, b, feat, N, mode, raw);
+    for (long i = 0; i < N; ++i) {
+        const double* r = raw + i * 58;
+        for (int k = 0; k < 3; ++k) o_means[i * 3 + k] = (double)means[i * 3 + k] + r[k];
+        double q[4], n = 0.0;
+        for (int k = 0; k < 4; ++k) { q[k] = (double)quats[i * 4 + k] + r[3 + k]; n += q[k] * q[k]; }
+        n = sqrt(n);
+        if (n < 1e-12) n = 1e-12;
+        for (int k = 0; k < 4; ++k) o_quats[i * 4 + k] = q[k] / n;
+        for (int k = 0; k < 3; ++k) o_scales[i * 3 + k] = (double)scales[i * 3 + k] * exp(r[7 + k]);
+        for (int k = 0; k < 48; ++k) o_sh[i * 48 + k] = (double)sh[i * 48 + k] + r[10 + k];
+    }
+    free(feat);
+    free(raw);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Projection, [SPIN] §3.1 Eq. 2-3 (EWA splatting)                            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    float R[9]; /* world -> camera rotation, row-major */
+    float t[3];
+    float fx, fy, cx, cy, near_z;
+    int W, H;
+    float bg[3];
+} orc_camera;
+
+/*
+ * One Gaussian, fp32, one IEEE op per step in the order written:
+ *   p = ((R_k0*mu0 + R_k1*mu1) + R_k2*mu2) + t_k;  cull unless p_z > near
+ *   q /= sqrt(((w*w + x*x) + y*y) + z*z);  R_q from q (w,x,y,z)
+ *   M = R_q diag(s);  Sigma_ij = (M_i0 M_j0 + M_i1 M_j1) + M_i2 M_j2          (Eq. 2)
+ *   J = [[fx/z, 0, -(fx x)/(z z)], [0, fy/z, -(fy y)/(z z)]];  T = J R
+ *   Sigma2D = T Sigma T^T  (U = T Sigma, then U T^T)                            (Eq. 3)
+ *   det = a c - b b (cull det <= 0);  conic = (c, -b, a) / det
+ *   lambda1 = mid + sqrt(max(0, mid*mid - det)), mid = 0.5 (a + c);  r = ceil(3 sqrt(lambda1))
+ *   (u, v) = ((fx x)/z + cx, (fy y)/z + cy)
+ *   pixel rect: x in [max(0, ceil((u - r) - 0.5)), min(W-1, floor((u + r) - 0.5))], same for y
+ *   tile rect = pixel rect / 16;  tiles = tile-rect area; any non-finite value culls.
+ * Returns 1 if visible.
+ */
+typedef struct {
+    float u, v, A, B, C, depth;
+    int px0, px1, py0, py1; /* pixel rect, inclusive */
+    int tx0, tx1, ty0, ty1; /* tile rect, inclusive */
+} orc_proj;
+
+static int project_one(const orc_camera* cam, const float* mu, const float* s, const float* q,
+                       orc_proj* o) {
+    const float* R = cam->R;
+    float px = R[0] * mu[0] + R[1] * mu[1];
+    px = px + R[2] * mu[2];
+    px = px + cam->t[0];
+    float py = R[3] * mu[0] + R[4] * mu[1];
+    py = py + R[5] * mu[2];
+    py = py + cam->t[1];
+    float pz = R[6] * mu[0] + R[7] * mu[1];
+    pz = pz + R[8] * mu[2];
+    pz = pz + cam->t[2];
+    if (!(pz > cam->near_z)) return 0;
+
+    float qn = q[0] * q[0] + q[1] * q[1];
+    qn = qn + q[2] * q[2];
+    qn = qn + q[3] * q[3];
+    qn = sqrtf(qn);
+    float w = q[0] / qn, x = q[1] / qn, y = q[2] / qn, z = q[3] / qn;
+    float Rq[9];
+    Rq[0] = 1.0f - 2.0f * (y * y + z * z);
+    Rq[1] = 2.0f * (x * y - w * z);
+    Rq[2] = 2.0f * (x * z + w * y);
+    Rq[3] = 2.0f * (x * y + w * z);
+    Rq[4] = 1.0f - 2.0f * (x * x + z * z);
+    Rq[5] = 2.0f * (y * z - w * x);
+    Rq[6] = 2.0f * (x * z - w * y);
+    Rq[7] = 2.0f * (y * z + w * x);
+    Rq[8] = 1.0f - 2.0f * (x * x + y * y);
+    float M[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) M[i * 3 + j] = Rq[i * 3 + j] * s[j];
+    float S[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            float acc = M[i * 3 + 0] * M[j * 3 + 0] + M[i * 3 + 1] * M[j * 3 + 1];
+            S[i * 3 + j] = acc + M[i * 3 + 2] * M[j * 3 + 2];
+        }
+    float zz = pz * pz;
+    float j00 = cam->fx / pz;
+    float j02 = -(cam->fx * px) / zz;
+    float j11 = cam->fy / pz;
+    float j12 = -(cam->fy * py) / zz;
+    float T[6];
+    for (int k = 0; k < 3; ++k) {
+        T[k] = j00 * R[k] + j02 * R[6 + k];
+        T[3 + k] = j11 * R[3 + k] + j12 * R[6 + k];
+    }
+    float U[6];
+    for (int i = 0; i < 2; ++i)
+        for (int k = 0; k < 3; ++k) {
+            float acc = T[i * 3 + 0] * S[0 * 3 + k] + T[i * 3 + 1] * S[1 * 3 + k];
+            U[i * 3 + k] = acc + T[i * 3 + 2] * S[2 * 3 + k];
+        }
+    float c2[4];
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) {
+            float acc = U[i * 3 + 0] * T[j * 3 + 0] + U[i * 3 + 1] * T[j * 3 + 1];
+            c2[i * 2 + j] = acc + U[i * 3 + 2] * T[j * 3 + 2];
+        }
+    float a = c2[0], b = c2[1], c = c2[3];
+    float det = a * c - b * b;
+    if (!(det > 0.0f)) return 0;
+    float inv = 1.0f / det;
+    float A = c * inv, B = -b * inv, C = a * inv;
+    float mid = 0.5f * (a + c);
+    float disc = mid * mid - det;
+    disc = disc > 0.0f ? disc : 0.0f;
+    float lam = mid + sqrtf(disc);
+    float r = ceilf(3.0f * sqrtf(lam));
+    float u = (cam->fx * px) / pz + cam->cx;
+    float v = (cam->fy * py) / pz + cam->cy;
+    if (!(isfinite(u) && isfinite(v) && isfinite(A) && isfinite(B) && isfinite(C) && isfinite(r))) return 0;
+    float x0 = ceilf((u - r) - 0.5f), x1 = floorf((u + r) - 0.5f);
+    float y0 = ceilf((v - r) - 0.5f), y1 = floorf((v + r) - 0.5f);
+    x0 = x0 > 0.0f ? x0 : 0.0f;
+    y0 = y0 > 0.0f ? y0 : 0.0f;
+    x1 = x1 < (float)(cam->W - 1) ? x1 : (float)(cam->W - 1);
+    y1 = y1 < (float)(cam->H - 1) ? y1 : (float)(cam->H - 1);
+    if (!(x0 <= x1 && y0 <= y1)) return 0;
+    o->u = u; o->v = v; o->A = A; o->B = B; o->C = C; o->depth = pz;
+    o->px0 = (int)x0; o->px1 = (int)x1; o->py0 = (int)y0; o->py1 = (int)y1;
+    o->tx0 = o->px0 / 16; o->tx1 = o->px1 / 16; o->ty0 = o->py0 / 16; o->ty1 = o->py1 / 16;
+    return 1;
+}
+
+static int frame_of(const long* frame_offsets, int F, long i) {
+    int lo = 0, hi = F - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (frame_offsets[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+/*
+ * Project a batch of frames.  Outputs (per Gaussian): mean2d[2], conic[3],
+ * depth, pixel rect [x0,x1,y0,y1], tile rect [tx0,ty0,tx1,ty1], tiles
+ * touched (0 = culled).
+ */
+EXPORT void orc_preprocess(const orc_camera* cams, int F, const long* frame_offsets, const float* means,
+                           const float* scales, const float* quats, float* mean2d, float* conic,
+                           float* depth, int* pix_rect, int* tile_rect, uint32_t* tiles) {
+    long N = frame_offsets[F];
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; ++i) {
+        int f = frame_of(frame_offsets, F, i);
+        orc_proj o;
+        int vis = project_one(&cams[f], means + i * 3, scales + i * 3, quats + i * 4, &o);
+        if (!vis) {
+            memset(&o, 0, sizeof(o));
+            o.px0 = o.py0 = o.tx0 = o.ty0 = 0;
+            o.px1 = o.py1 = o.tx1 = o.ty1 = -1;
+        }
+        mean2d[i * 2] = o.u; mean2d[i * 2 + 1] = o.v;
+        conic[i * 3] = o.A; conic[i * 3 + 1] = o.B; conic[i * 3 + 2] = o.C;
+        depth[i] = o.depth;
+        pix_rect[i * 4] = o.px0; pix_rect[i * 4 + 1] = o.px1; pix_rect[i * 4 + 2] = o.py0; pix_rect[i * 4 + 3] = o.py1;
+        tile_rect[i * 4] = o.tx0; tile_rect[i * 4 + 1] = o.ty0; tile_rect[i * 4 + 2] = o.tx1; tile_rect[i * 4 + 3] = o.ty1;
+        tiles[i] = vis ? (uint32_t)((o.tx1 - o.tx0 + 1) * (o.ty1 - o.ty0 + 1)) : 0u;
+    }
+}
+
+/*
+ * Colour of each Gaussian seen from its frame's camera, degree-3 SH:
+ * dir = normalize(mu - centre), centre = -R^T t;  rgb = max(0, sum_k sh_k Y_k(dir) + 0.5).
+ */
+EXPORT void orc_sh_colors(const orc_camera* cams, int F, const long* frame_offsets, const float* means,
+                          const float* sh, double* rgb) {
+    long N = frame_offsets[F];
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; ++i) {
+        const orc_camera* c = &cams[frame_of(frame_offsets, F, i)];
+        double ctr[3];
+        for (int k = 0; k < 3; ++k)
+            ctr[k] = -((double)c->R[0 * 3 + k] * c->t[0] + (double)c->R[1 * 3 + k] * c->t[1] +
+                       (double)c->R[2 * 3 + k] * c->t[2]);
+        double d[3], n = 0.0;
+        for (int k = 0; k < 3; ++k) { d[k] = (double)means[i * 3 + k] - ctr[k]; n += d[k] * d[k]; }
+        n = sqrt(n);
+        for (int k = 0; k < 3; ++k) d[k] /= n;
+        double Y[16];
+        orc_sh_basis(d, 1, Y);
+        for (int ch = 0; ch < 3; ++ch) {
+            double s = 0.5;
+            for (int k = 0; k < 16; ++k) s += (double)sh[i * 48 + k * 3 + ch] * Y[k];
+            rgb[i * 3 + ch] = s > 0.0 ? s : 0.0;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Binning and sort (16x16 tiles)                                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct { uint64_t key; uint64_t seq; uint32_t val; } orc_entry;
+
+static int cmp_entry(const void* a, const void* b) {
+    const orc_entry* x = (const orc_entry*)a;
+    const orc_entry* y = (const orc_entry*)b;
+    if (x->key != y->key) return x->key < y->key ? -1 : 1;
+    if (x->seq != y->seq) return x->seq < y->seq ? -1 : 1;
+    return 0;
+}
+
+static uint32_t float_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/*
+ * Emit one entry per (visible Gaussian, touched tile): Gaussians in ascending
+ * index, tiles by row then column; key = ((frame*ntiles + ty*tiles_x + tx) << 32)
+ * | bits(depth), val = Gaussian index.  Stable ascending sort on the key (ties
+ * keep emission order), then per-tile [start, end) ranges (empty = [0,0)).
+ * Returns the entry count E; writes at most cap entries.
+ */
+EXPORT long orc_bin(int F, int W, int H, const long* frame_offsets, const float* depth, const int* tile_rect,
+                    const uint32_t* tiles, long cap, uint64_t* keys, uint32_t* vals, uint32_t* ranges) {
+    long N = frame_offsets[F];
+    int tx_n = (W + 15) / 16, ty_n = (H + 15) / 16;
+    long ntiles = (long)tx_n * ty_n;
+    long E = 0;
+    for (long i = 0; i < N; ++i) E += tiles[i];
+    orc_entry* ent = (orc_entry*)malloc(sizeof(orc_entry) * (size_t)(E > 0 ? E : 1));
+    long e = 0;
+    for (long i = 0; i < N; ++i) {
+        if (!tiles[i]) continue;
+        long f = frame_of(frame_offsets, F, i);
+        for (int ty = tile_rect[i * 4 + 1]; ty <= tile_rect[i * 4 + 3]; ++ty)
+            for (int tx = tile_rect[i * 4 + 0]; tx <= tile_rect[i * 4 + 2]; ++tx) {
+                uint64_t tile = (uint64_t)(f * ntiles + (long)ty * tx_n + tx);
+                ent[e].key = (tile << 32) | float_bits(depth[i]);
+                ent[e].seq = (uint64_t)e;
+                ent[e].val = (uint32_t)i;
+                ++e;
+            }
+    }
+    qsort(ent, (size_t)E, sizeof(orc_entry), cmp_entry);
+    for (long k = 0; k < (long)F * ntiles * 2; ++k) ranges[k] = 0;
+    for (long k = 0; k < E; ++k) {
+        if (k < cap) { keys[k] = ent[k].key; vals[k] = ent[k].val; }
+        uint64_t tile = ent[k].key >> 32;
+        if (k == 0 || (ent[k - 1].key >> 32) != tile) ranges[tile * 2] = (uint32_t)k;
+        if (k == E - 1 || (ent[k + 1].key >> 32) != tile) ranges[tile * 2 + 1] = (uint32_t)(k + 1);
+    }
+    free(ent);
+    return E;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Compositing, [SPIN] §3.1 Eq. 1 and Eq. 4                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float* mean2d;
+    const float* conic;
+    const float* opacity;
+    const double* color;
+} orc_splats;
+
+/*
+ * One pixel over an ordered list of Gaussians, fp64:
+ *   d = (px + 0.5 - u, py + 0.5 - v);  power = -0.5 (A dx^2 + C dy^2) - B dx dy
+ *   skip if power < -4.5 (outside 3 sigma) or power > 0
+ *   alpha = min(0.99, o exp(power));  skip if alpha < 1/255
+ *   C += c alpha T;  T *= 1 - alpha;  stop once T < 1e-4 (after compositing)
+ * n_contrib = 1 + list position of the last composited Gaussian.
+ * flag = 1 if any decision lies within its rounding band of a threshold, so
+ * that an fp32 evaluation may legitimately decide it the other way.
+ */
+static void composite(const orc_splats* g, const uint32_t* list, long n, int px, int py, double out[3],
+                      double* T_out, uint32_t* nc_out, int* flag) {
+    double T = 1.0, C[3] = {0, 0, 0};
+    double relT = 0.0; /* bound on the relative error an fp32 evaluation of T may carry */
+    uint32_t last = 0;
+    int fl = 0;
+    for (long j = 0; j < n; ++j) {
+        uint32_t i = list[j];
+        double dx = (double)px + 0.5 - (double)g->mean2d[i * 2];
+        double dy = (double)py + 0.5 - (double)g->mean2d[i * 2 + 1];
+        double A = g->conic[i * 3], B = g->conic[i * 3 + 1], Cc = g->conic[i * 3 + 2];
+        double quad = A * dx * dx + Cc * dy * dy;
+        double cross = B * dx * dy;
+        double power = -0.5 * quad - cross;
+        /* fp32 error of power is a few roundings of its largest term */
+        double mag = 0.5 * fabs(quad) + fabs(cross);
+        double err_p = 1e-6 * mag;
+        if (fabs(power + 4.5) <= 1e-5 * 4.5 + err_p) fl = 1;
+        if (fabs(power) <= err_p && mag > 0.0) fl = 1;
+        if (power < -4.5 || power > 0.0) continue;
+        double ga = (double)g->opacity[i] * exp(power);
+        double rel_a = 1e-5 + 2.0 * err_p; /* relative band on alpha */
+        if (fabs(ga - 0.99) <= rel_a * 0.99) fl = 1;
+        double alpha = ga < 0.99 ? ga : 0.99;
+        if (fabs(alpha - 1.0 / 255.0) <= rel_a / 255.0) fl = 1;
+        if (alpha < 1.0 / 255.0) continue;
+        for (int k = 0; k < 3; ++k) C[k] += g->color[i * 3 + k] * alpha * T;
+        T = T * (1.0 - alpha);
+        last = (uint32_t)(j + 1);
+        /* an error d in alpha moves 1 - alpha by alpha/(1 - alpha) * d relative */
+        relT += 1.2e-7 + alpha / (1.0 - alpha) * (2e-7 + 2.0 * err_p);
+        double band = 1e-5 > 4.0 * relT ? 1e-5 : 4.0 * relT;
+        if (fabs(T - 1e-4) <= band * 1e-4) fl = 1;
+        if (T < 1e-4) break;
+    }
+    for (int k = 0; k < 3; ++k) out[k] = C[k];
+    *T_out = T;
+    *nc_out = last;
+    *flag = fl;
+}
+
+/* Tiled raster: each pixel composites its tile's sorted list.  Output
+ * image [F][3][H][W] = C + T bg, T_final and n_contrib [F][H][W], flags. */
+EXPORT void orc_raster_tiles(int F, const orc_camera* cams, const uint32_t* vals, const uint32_t* ranges,
+                             const float* mean2d, const float* conic, const float* opacity, const double* color,
+                             double* image, double* T_final, uint32_t* n_contrib, uint8_t* flags) {
+    int W = cams[0].W, H = cams[0].H;
+    int tx_n = (W + 15) / 16, ty_n = (H + 15) / 16;
+    orc_splats g = {mean2d, conic, opacity, color};
+#pragma omp parallel for collapse(2) schedule(dynamic, 64)
+    for (long f = 0; f < F; ++f)
+        for (long pix = 0; pix < (long)W * H; ++pix) {
+            int px = (int)(pix % W), py = (int)(pix / W);
+            long tile = f * (long)tx_n * ty_n + (long)(py / 16) * tx_n + px / 16;
+            uint32_t s = ranges[tile * 2], e = ranges[tile * 2 + 1];
+            double c[3], T;
+            uint32_t nc;
+            int fl;
+            composite(&g, vals + s, (long)e - (long)s, px, py, c, &T, &nc, &fl);
+            for (int k = 0; k < 3; ++k) image[((f * 3 + k) * H + py) * (long)W + px] = c[k] + T * cams[f].bg[k];
+            T_final[f * (long)W * H + pix] = T;
+            n_contrib[f * (long)W * H + pix] = nc;
+            flags[f * (long)W * H + pix] = (uint8_t)fl;
+        }
+}
+
+typedef struct { uint32_t depth_bits; uint32_t idx; } orc_dorder;
+
+static int cmp_dorder(const void* a, const void* b) {
+    const orc_dorder* x = (const orc_dorder*)a;
+    const orc_dorder* y = (const orc_dorder*)b;
+    if (x->depth_bits != y->depth_bits) return x->depth_bits < y->depth_bits ? -1 : 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+/*
+ * Brute-force raster of the listed pixels (or all pixels when n_pix < 0) of
+ * one frame: every visible Gaussian of the frame in (depth, index) order; with
+ * restrict_tiles only those whose tile rect holds the pixel's tile, which is
+ * the tiled renderer's list by construction.  pix is [n_pix][2] (x, y);
+ * outputs are per listed pixel: rgb[3], T, n_contrib (counted over the
+ * per-pixel list), flag.
+ */
+EXPORT void orc_raster_brute(const orc_camera* cam, long g0, long g1, const float* mean2d, const float* conic,
+                             const float* opacity, const double* color, const float* depth,
+                             const int* tile_rect, const uint32_t* tiles, int restrict_tiles, const int* pix,
+                             long n_pix, double* rgb, double* T_out, uint32_t* nc_out, uint8_t* flags) {
+    long n = 0;
+    orc_dorder* ord = (orc_dorder*)malloc(sizeof(orc_dorder) * (size_t)(g1 - g0 > 0 ? g1 - g0 : 1));
+    for (long i = g0; i < g1; ++i)
+        if (tiles[i]) { ord[n].depth_bits = float_bits(depth[i]); ord[n].idx = (uint32_t)i; ++n; }
+    qsort(ord, (size_t)n, sizeof(orc_dorder), cmp_dorder);
+    long npx = n_pix < 0 ? (long)cam->W * cam->H : n_pix;
+    orc_splats g = {mean2d, conic, opacity, color};
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long p = 0; p < npx; ++p) {
+        int px = n_pix < 0 ? (int)(p % cam->W) : pix[p * 2];
+        int py = n_pix < 0 ? (int)(p / cam->W) : pix[p * 2 + 1];
+        int tx = px / 16, ty = py / 16;
+        uint32_t* list = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
+        long m = 0;
+        for (long k = 0; k < n; ++k) {
+            uint32_t i = ord[k].idx;
+            if (restrict_tiles && !(tile_rect[i * 4] <= tx && tx <= tile_rect[i * 4 + 2] &&
+                                    tile_rect[i * 4 + 1] <= ty && ty <= tile_rect[i * 4 + 3]))
+                continue;
+            list[m++] = i;
+        }
+        double c[3], T;
+        uint32_t nc;
+        int fl;
+        composite(&g, list, m, px, py, c, &T, &nc, &fl);
+        for (int k = 0; k < 3; ++k) rgb[p * 3 + k] = c[k] + T * cam->bg[k];
+        T_out[p] = T;
+        nc_out[p] = nc;
+        flags[p] = (uint8_t)fl;
+        free(list);
+    }
+    free(ord);
+}
