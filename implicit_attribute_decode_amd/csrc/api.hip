@@ -1,0 +1,482 @@
+// C ABI of libia.so (declared in include/ia.h): argument validation, handle
+// management and launch orchestration.  Every check runs before the first
+// HIP call of an entry point, so invalid arguments never enqueue work.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "ia_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ia_status fail(ia_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+ia_status hip_fail(hipError_t e, const char* what) {
+    return fail(IA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Copy bytes into a fresh device allocation; host sources are copied
+// synchronously so the caller may free them on return.
+ia_status upload_param(void** dst, const void* src, size_t bytes, bool on_device, hipStream_t s) {
+    void* d = nullptr;
+    hipError_t e = hipMalloc(&d, bytes);
+    if (e != hipSuccess) return fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
+    if (on_device)
+        e = hipMemcpyAsync(d, src, bytes, hipMemcpyDeviceToDevice, s);
+    else
+        e = hipMemcpy(d, src, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e, "parameter copy");
+    }
+    *dst = d;
+    return IA_OK;
+}
+
+}  // namespace
+
+// ============================================================== decoder
+
+struct ia_decoder {
+    ia_hash_desc hash;
+    ia_mlp_desc mlp;
+    ia::HashLevels lv;
+    int n_layers;
+    int dims[6];  // dims[0] = in, dims[k+1] = out of layer k; last = 11
+    void* tables = nullptr;
+    void* W[4] = {nullptr, nullptr, nullptr, nullptr};
+    float* b[4] = {nullptr, nullptr, nullptr, nullptr};
+    bool ready = false;
+};
+
+namespace {
+
+void free_decoder_params(ia_decoder* d) {
+    if (d->tables) (void)hipFree(d->tables);
+    for (int k = 0; k < 4; ++k) {
+        if (d->W[k]) (void)hipFree(d->W[k]);
+        if (d->b[k]) (void)hipFree(d->b[k]);
+        d->W[k] = nullptr;
+        d->b[k] = nullptr;
+    }
+    d->tables = nullptr;
+    d->ready = false;
+}
+
+ia_status check_hash(const ia_hash_desc* h, ia::HashLevels* lv) {
+    if (h->L < 1 || h->L > ia::kMaxLevels) return fail(IA_ERR_INVALID_ARG, "hash.L must be in 1..32");
+    if (h->F != 2) return fail(IA_ERR_UNSUPPORTED, "hash.F must be 2");
+    if (h->log2T < 4 || h->log2T > 24) return fail(IA_ERR_INVALID_ARG, "hash.log2T must be in 4..24");
+    if (!(std::isfinite(h->base_res) && h->base_res >= 2.0)) return fail(IA_ERR_INVALID_ARG, "hash.base_res must be >= 2");
+    if (!(std::isfinite(h->growth) && h->growth >= 1.0)) return fail(IA_ERR_INVALID_ARG, "hash.growth must be >= 1");
+    if (h->temporal_res < 0 || h->temporal_res == 1) return fail(IA_ERR_INVALID_ARG, "hash.temporal_res must be 0 or >= 2");
+    if (h->table_dtype != IA_DTYPE_F32 && h->table_dtype != IA_DTYPE_F16)
+        return fail(IA_ERR_INVALID_ARG, "hash.table_dtype must be F32 or F16");
+    if (!(std::isfinite(h->t_min) && std::isfinite(h->t_max) && h->t_max > h->t_min))
+        return fail(IA_ERR_INVALID_ARG, "hash.t_max must exceed hash.t_min");
+    lv->L = h->L;
+    lv->F = h->F;
+    lv->T = 1u << h->log2T;
+    lv->mask = lv->T - 1u;
+    lv->table_f16 = h->table_dtype == IA_DTYPE_F16;
+    lv->t_min = h->t_min;
+    lv->t_max = h->t_max;
+    for (int l = 0; l < h->L; ++l) {
+        double r = std::floor(h->base_res * std::pow(h->growth, (double)l));
+        if (r > 1e6) return fail(IA_ERR_INVALID_ARG, "level resolution above 1e6");
+        int res = (int)r;
+        int rt = h->temporal_res > 0 ? h->temporal_res : res;
+        lv->res_s[l] = res;
+        lv->res_t[l] = rt;
+        lv->dense[l] = ((double)res * res * res * rt) <= (double)lv->T;
+    }
+    return IA_OK;
+}
+
+ia_status check_mlp(const ia_hash_desc* h, const ia_mlp_desc* m) {
+    if (m->in_dim != h->L * h->F) return fail(IA_ERR_INVALID_ARG, "mlp.in_dim must equal L*F");
+    if (m->n_hidden < 1 || m->n_hidden > 2) return fail(IA_ERR_UNSUPPORTED, "mlp.n_hidden must be 1 or 2");
+    if (m->activation != IA_ACT_RELU && m->activation != IA_ACT_GELU)
+        return fail(IA_ERR_INVALID_ARG, "mlp.activation must be RELU or GELU");
+    for (int k = 0; k < m->n_hidden; ++k)
+        if (m->hidden[k] < 1 || m->hidden[k] > 1024) return fail(IA_ERR_INVALID_ARG, "mlp.hidden width out of range");
+    if (m->dtype == IA_DTYPE_F16) {
+        if (!(m->in_dim == 32 && m->n_hidden == 2 && m->hidden[0] == 64 && m->hidden[1] == 64))
+            return fail(IA_ERR_UNSUPPORTED, "fp16 decoder supports 32 -> 64 -> 64 -> 11 only");
+        if (h->table_dtype != IA_DTYPE_F16) return fail(IA_ERR_UNSUPPORTED, "fp16 decoder needs an fp16 hash table");
+        return IA_OK;
+    }
+    if (m->dtype != IA_DTYPE_F32) return fail(IA_ERR_INVALID_ARG, "mlp.dtype must be F32 or F16");
+    const bool ok = (m->in_dim == 8 && m->n_hidden == 1 && m->hidden[0] == 32) ||
+                    (m->in_dim == 32 && m->n_hidden == 1 && m->hidden[0] == 64) ||
+                    (m->in_dim == 32 && m->n_hidden == 2 && m->hidden[0] == 64 && m->hidden[1] == 64);
+    if (!ok) return fail(IA_ERR_UNSUPPORTED, "fp32 decoder supports 8->32->11, 32->64->11 and 32->64->64->11");
+    return IA_OK;
+}
+
+bool outputs_ok(const ia_gaussians* o) { return o && o->scales && o->quats && o->colors && o->opacity; }
+
+ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, float t, int64_t N,
+                        const ia_gaussians* out, void* stream) {
+    if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
+    if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    if (N == 0) return IA_OK;
+    if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
+    if (!outputs_ok(out)) return fail(IA_ERR_INVALID_ARG, "output scales/quats/colors/opacity must be non-null");
+    if (N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N too large");
+    ia::DecodeArgs a{};
+    a.h = dec->lv;
+    a.tables = dec->tables;
+    for (int k = 0; k < dec->n_layers; ++k) {
+        a.W[k] = dec->W[k];
+        a.b[k] = dec->b[k];
+    }
+    a.in_dim = dec->mlp.in_dim;
+    a.n_hidden = dec->mlp.n_hidden;
+    for (int k = 0; k < 4; ++k) a.hidden[k] = dec->mlp.hidden[k];
+    a.act = dec->mlp.activation;
+    a.pos = pos;
+    a.stride = stride;
+    a.t_scalar = t;
+    a.N = N;
+    a.scales = out->scales;
+    a.quats = out->quats;
+    a.colors = out->colors;
+    a.opacity = out->opacity;
+    hipError_t e = ia::launch_decode(a, dec->mlp.dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return IA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ia_last_error(void) { return g_err.c_str(); }
+
+ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* mlp, ia_decoder** out) {
+    if (!hash || !mlp || !out) return fail(IA_ERR_INVALID_ARG, "null argument");
+    ia::HashLevels lv{};
+    ia_status s = check_hash(hash, &lv);
+    if (s != IA_OK) return s;
+    s = check_mlp(hash, mlp);
+    if (s != IA_OK) return s;
+    ia_decoder* d = new (std::nothrow) ia_decoder();
+    if (!d) return fail(IA_ERR_OUT_OF_MEMORY, "host allocation failed");
+    d->hash = *hash;
+    d->mlp = *mlp;
+    d->lv = lv;
+    d->n_layers = mlp->n_hidden + 1;
+    d->dims[0] = mlp->in_dim;
+    for (int k = 0; k < mlp->n_hidden; ++k) d->dims[k + 1] = mlp->hidden[k];
+    d->dims[d->n_layers] = 11;
+    *out = d;
+    return IA_OK;
+}
+
+ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
+                                const float* const* biases, int32_t params_on_device, void* stream) {
+    if (!dec || !tables || !weights || !biases) return fail(IA_ERR_INVALID_ARG, "null argument");
+    for (int k = 0; k < dec->n_layers; ++k)
+        if (!weights[k] || !biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias pointer");
+    const bool dev = params_on_device != 0;
+    hipStream_t s = (hipStream_t)stream;
+    if (dec->tables) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        free_decoder_params(dec);
+    }
+    const size_t tsize = dec->hash.table_dtype == IA_DTYPE_F16 ? 2 : 4;
+    const size_t tbytes = (size_t)dec->hash.L * dec->lv.T * dec->hash.F * tsize;
+    ia_status st = upload_param(&dec->tables, tables, tbytes, dev, s);
+    const size_t wsize = dec->mlp.dtype == IA_DTYPE_F16 ? 2 : 4;
+    for (int k = 0; st == IA_OK && k < dec->n_layers; ++k) {
+        const size_t nw = (size_t)dec->dims[k + 1] * dec->dims[k];
+        st = upload_param(&dec->W[k], weights[k], nw * wsize, dev, s);
+        if (st == IA_OK) st = upload_param(reinterpret_cast<void**>(&dec->b[k]), biases[k], 4 * (size_t)dec->dims[k + 1], dev, s);
+    }
+    if (st != IA_OK) {
+        free_decoder_params(dec);
+        return st;
+    }
+    dec->ready = true;
+    return IA_OK;
+}
+
+ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t, const ia_gaussians* out,
+                    void* stream) {
+    if (!std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
+    return decode_common(dec, xyz, 3, t, N, out, stream);
+}
+
+ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
+                         void* stream) {
+    return decode_common(dec, xyzt, 4, 0.0f, N, out, stream);
+}
+
+void ia_decoder_destroy(ia_decoder* dec) {
+    if (!dec) return;
+    if (dec->tables) (void)hipDeviceSynchronize();
+    free_decoder_params(dec);
+    delete dec;
+}
+
+}  // extern "C"
+
+// ============================================================== HexPlane
+
+struct ia_hexplane {
+    ia_hexplane_desc d;
+    void* planes[6] = {};
+    void* W[3] = {};
+    float* b[3] = {};
+    bool ready = false;
+};
+
+namespace {
+
+void free_hex(ia_hexplane* h) {
+    for (int k = 0; k < 6; ++k) {
+        if (h->planes[k]) (void)hipFree(h->planes[k]);
+        h->planes[k] = nullptr;
+    }
+    for (int k = 0; k < 3; ++k) {
+        if (h->W[k]) (void)hipFree(h->W[k]);
+        if (h->b[k]) (void)hipFree(h->b[k]);
+        h->W[k] = nullptr;
+        h->b[k] = nullptr;
+    }
+    h->ready = false;
+}
+
+}  // namespace
+
+extern "C" {
+
+ia_status ia_hexplane_create(const ia_hexplane_desc* desc, ia_hexplane** out) {
+    if (!desc || !out) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (desc->channels != 32) return fail(IA_ERR_UNSUPPORTED, "HexPlane supports 32 channels per plane");
+    if (desc->res_xyz < 2 || desc->res_xyz > 4096 || desc->res_t < 2 || desc->res_t > 4096)
+        return fail(IA_ERR_INVALID_ARG, "plane resolutions must be in 2..4096");
+    if (!(std::isfinite(desc->aabb) && desc->aabb > 0.0f)) return fail(IA_ERR_INVALID_ARG, "aabb must be > 0");
+    ia_hexplane* h = new (std::nothrow) ia_hexplane();
+    if (!h) return fail(IA_ERR_OUT_OF_MEMORY, "host allocation failed");
+    h->d = *desc;
+    *out = h;
+    return IA_OK;
+}
+
+ia_status ia_hexplane_set_params(ia_hexplane* hp, const void* const* planes, const void* const* weights,
+                                 const float* const* biases, int32_t params_on_device, void* stream) {
+    if (!hp || !planes || !weights || !biases) return fail(IA_ERR_INVALID_ARG, "null argument");
+    for (int k = 0; k < 6; ++k)
+        if (!planes[k]) return fail(IA_ERR_INVALID_ARG, "null plane pointer");
+    for (int k = 0; k < 3; ++k)
+        if (!weights[k] || !biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias pointer");
+    if (hp->ready) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        free_hex(hp);
+    }
+    const bool dev = params_on_device != 0;
+    hipStream_t s = (hipStream_t)stream;
+    const int C = hp->d.channels;
+    ia_status st = IA_OK;
+    for (int k = 0; st == IA_OK && k < 6; ++k) {
+        const size_t rb = k < 3 ? hp->d.res_xyz : hp->d.res_t;
+        st = upload_param(&hp->planes[k], planes[k], rb * hp->d.res_xyz * C * 2, dev, s);
+    }
+    const int dims[4] = {6 * C, 256, 256, 58};
+    for (int k = 0; st == IA_OK && k < 3; ++k) {
+        st = upload_param(&hp->W[k], weights[k], (size_t)dims[k + 1] * dims[k] * 2, dev, s);
+        if (st == IA_OK) st = upload_param(reinterpret_cast<void**>(&hp->b[k]), biases[k], 4 * (size_t)dims[k + 1], dev, s);
+    }
+    if (st != IA_OK) {
+        free_hex(hp);
+        return st;
+    }
+    hp->ready = true;
+    return IA_OK;
+}
+
+ia_status ia_hexplane_deform(const ia_hexplane* hp, const ia_gaussians* cn, int64_t N, float t, const ia_gaussians* out,
+                             void* stream) {
+    if (!hp) return fail(IA_ERR_INVALID_ARG, "hexplane is null");
+    if (!hp->ready) return fail(IA_ERR_INVALID_ARG, "hexplane parameters not set");
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    if (!std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
+    if (N == 0) return IA_OK;
+    if (!cn || !out) return fail(IA_ERR_INVALID_ARG, "null Gaussian buffers");
+    if (!cn->means || !cn->scales || !cn->quats || !cn->sh || !cn->opacity)
+        return fail(IA_ERR_INVALID_ARG, "canonical means/scales/quats/sh/opacity must be non-null");
+    if (!out->means || !out->scales || !out->quats || !out->sh || !out->opacity)
+        return fail(IA_ERR_INVALID_ARG, "output means/scales/quats/sh/opacity must be non-null");
+    if ((cn->means_stride != 0 && cn->means_stride != 3) || (out->means_stride != 0 && out->means_stride != 3))
+        return fail(IA_ERR_INVALID_ARG, "HexPlane means must be packed [N,3]");
+    ia::HexArgs a{};
+    a.res_xyz = hp->d.res_xyz;
+    a.res_t = hp->d.res_t;
+    a.C = hp->d.channels;
+    a.aabb = hp->d.aabb;
+    for (int k = 0; k < 6; ++k) a.planes[k] = (const _Float16*)hp->planes[k];
+    for (int k = 0; k < 3; ++k) {
+        a.W[k] = (const _Float16*)hp->W[k];
+        a.b[k] = hp->b[k];
+    }
+    a.means = cn->means;
+    a.scales = cn->scales;
+    a.quats = cn->quats;
+    a.sh = cn->sh;
+    a.opacity = cn->opacity;
+    a.t = t;
+    a.N = N;
+    a.o_means = out->means;
+    a.o_scales = out->scales;
+    a.o_quats = out->quats;
+    a.o_sh = out->sh;
+    a.o_opacity = out->opacity;
+    hipError_t e = ia::launch_hexplane(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hexplane launch");
+    return IA_OK;
+}
+
+void ia_hexplane_destroy(ia_hexplane* hp) {
+    if (!hp) return;
+    if (hp->ready) (void)hipDeviceSynchronize();
+    free_hex(hp);
+    delete hp;
+}
+
+// ============================================================== render
+
+ia_status ia_render_workspace_size(int64_t N_total, int32_t frames, int32_t W, int32_t H, int64_t max_entries,
+                                   size_t* bytes) {
+    if (!bytes) return fail(IA_ERR_INVALID_ARG, "bytes is null");
+    if (N_total < 0 || N_total >= ((int64_t)1 << 32)) return fail(IA_ERR_INVALID_ARG, "N_total must be in [0, 2^32)");
+    if (frames < 1 || frames > 65535) return fail(IA_ERR_INVALID_ARG, "frames must be in 1..65535");
+    if (W < 1 || H < 1 || W > 16 * 4096 || H > 16 * 4096) return fail(IA_ERR_INVALID_ARG, "W, H must be in 1..65536");
+    if (max_entries < 1 || max_entries >= ((int64_t)1 << 32) - 1)
+        return fail(IA_ERR_INVALID_ARG, "max_entries must be in [1, 2^32 - 1)");
+    const int64_t tiles = (int64_t)frames * ((W + 15) / 16) * ((H + 15) / 16);
+    if (tiles >= ((int64_t)1 << 32)) return fail(IA_ERR_INVALID_ARG, "frames * tiles must be below 2^32");
+    *bytes = ia::render_layout(N_total, frames, W, H, max_entries).total;
+    return IA_OK;
+}
+
+ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames, const ia_camera* cams,
+                    void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux, void* stream) {
+    if (!g || !frame_offsets || !cams || !image) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (frames < 1 || frames > 65535) return fail(IA_ERR_INVALID_ARG, "frames must be in 1..65535");
+    if (frame_offsets[0] != 0) return fail(IA_ERR_INVALID_ARG, "frame_offsets[0] must be 0");
+    for (int f = 0; f < frames; ++f)
+        if (frame_offsets[f + 1] < frame_offsets[f]) return fail(IA_ERR_INVALID_ARG, "frame_offsets must be non-decreasing");
+    const int64_t N = frame_offsets[frames];
+    const int W = cams[0].W, H = cams[0].H;
+    for (int f = 0; f < frames; ++f) {
+        const ia_camera& c = cams[f];
+        if (c.W != W || c.H != H) return fail(IA_ERR_INVALID_ARG, "all cameras must share W and H");
+        bool fin = std::isfinite(c.fx) && std::isfinite(c.fy) && std::isfinite(c.cx) && std::isfinite(c.cy) &&
+                   std::isfinite(c.near_z);
+        for (int k = 0; k < 9; ++k) fin = fin && std::isfinite(c.R[k]);
+        for (int k = 0; k < 3; ++k) fin = fin && std::isfinite(c.t[k]) && std::isfinite(c.bg[k]);
+        if (!fin) return fail(IA_ERR_INVALID_ARG, "camera parameters must be finite");
+    }
+    size_t need = 0;
+    ia_status st = ia_render_workspace_size(N, frames, W, H, max_entries, &need);
+    if (st != IA_OK) return st;
+    if (N > 0) {
+        if (!g->means || !g->scales || !g->quats || !g->opacity)
+            return fail(IA_ERR_INVALID_ARG, "means/scales/quats/opacity must be non-null");
+        if (g->sh_degree == -1) {
+            if (!g->colors) return fail(IA_ERR_INVALID_ARG, "colors must be non-null when sh_degree = -1");
+        } else if (g->sh_degree == 3) {
+            if (!g->sh) return fail(IA_ERR_INVALID_ARG, "sh must be non-null when sh_degree = 3");
+        } else {
+            return fail(IA_ERR_UNSUPPORTED, "sh_degree must be -1 or 3");
+        }
+        if (g->means_stride != 0 && g->means_stride < 3) return fail(IA_ERR_INVALID_ARG, "means_stride must be 0 or >= 3");
+    }
+    if (!ws || !aligned(ws, 256)) return fail(IA_ERR_INVALID_ARG, "workspace must be non-null and 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(IA_ERR_WORKSPACE_TOO_SMALL, "workspace too small: need " + std::to_string(need) + " bytes");
+
+    // camera table (centre = -R^T t, for SH view directions)
+    std::string err;
+    ia::DevCamera* dc = new (std::nothrow) ia::DevCamera[frames];
+    if (!dc) return fail(IA_ERR_OUT_OF_MEMORY, "host allocation failed");
+    for (int f = 0; f < frames; ++f) {
+        const ia_camera& c = cams[f];
+        ia::DevCamera& d = dc[f];
+        std::memcpy(d.R, c.R, sizeof(d.R));
+        std::memcpy(d.t, c.t, sizeof(d.t));
+        d.fx = c.fx;
+        d.fy = c.fy;
+        d.cx = c.cx;
+        d.cy = c.cy;
+        d.near_z = c.near_z;
+        for (int k = 0; k < 3; ++k) {
+            double s = 0.0;
+            for (int r = 0; r < 3; ++r) s += (double)c.R[r * 3 + k] * (double)c.t[r];
+            d.centre[k] = (float)(-s);
+            d.bg[k] = c.bg[k];
+        }
+        d.W = c.W;
+        d.H = c.H;
+    }
+    ia::RenderArgs a{};
+    a.means = g->means;
+    a.means_stride = g->means_stride == 0 ? 3 : g->means_stride;
+    a.scales = g->scales;
+    a.quats = g->quats;
+    a.colors = g->colors;
+    a.sh = g->sh;
+    a.opacity = g->opacity;
+    a.sh_degree = g->sh_degree;
+    a.frames = frames;
+    a.W = W;
+    a.H = H;
+    a.frame_offsets_host = frame_offsets;
+    a.cams_host = dc;
+    a.ws = static_cast<unsigned char*>(ws);
+    a.lay = ia::render_layout(N, frames, W, H, max_entries);
+    a.image = image;
+    a.T_final = aux ? aux->T_final : nullptr;
+    a.n_contrib = aux ? aux->n_contrib : nullptr;
+    a.n_entries_out = aux ? aux->n_entries : nullptr;
+    a.overflow_out = aux ? aux->overflow : nullptr;
+    int tile_bits = 1;
+    while (((int64_t)1 << tile_bits) < a.lay.ntiles_all) ++tile_bits;
+    a.sort_passes = (32 + tile_bits + 7) / 8;
+    const uint64_t* keys = nullptr;
+    const uint32_t* vals = nullptr;
+    hipError_t e = ia::launch_render(a, (hipStream_t)stream, &keys, &vals);
+    delete[] dc;
+    if (e != hipSuccess) return hip_fail(e, "render launch");
+    if (aux) {
+        unsigned char* w = static_cast<unsigned char*>(ws);
+        aux->sorted_keys = keys;
+        aux->sorted_vals = vals;
+        aux->tile_ranges = reinterpret_cast<const uint32_t*>(w + a.lay.ranges);
+        aux->proj_a = reinterpret_cast<const float*>(w + a.lay.pa);
+        aux->proj_b = reinterpret_cast<const float*>(w + a.lay.pb);
+        aux->proj_c = reinterpret_cast<const float*>(w + a.lay.pc);
+        aux->depth = reinterpret_cast<const float*>(w + a.lay.depth);
+        aux->tiles_touched = reinterpret_cast<const uint32_t*>(w + a.lay.tiles);
+        aux->tile_rect = reinterpret_cast<const uint16_t*>(w + a.lay.rect);
+    }
+    return IA_OK;
+}
+
+}  // extern "C"

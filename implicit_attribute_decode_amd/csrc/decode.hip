@@ -1,0 +1,420 @@
+// Implicit attribute decode (SPIN-4DGS, "Implicit 4D Gaussian Splatting for
+// Fast Motion with Large Inter-Frame Displacements", §3.3 Eq. 7-11):
+//   position + t -> contraction / normalisation (Eq. 7-8)
+//               -> 4D multiresolution hash encoding, 16-corner quadrilinear
+//                  interpolation per level, levels concatenated (Eq. 9)
+//               -> shared MLP trunk + linear head block (Eq. 10)
+//               -> exp / normalise / sigmoid activations (Eq. 11).
+//
+// Two kernels:
+//   decode_f32_kernel  : fp32 VALU, one thread per Gaussian, weights in LDS.
+//   decode_mfma_kernel : 16 levels x 2 features, 32->64->64->11, fp16 MFMA
+//                        (v_mfma_f32_16x16x16_f16) with fp32 accumulation.
+//                        A wave decodes 64 Gaussians; Gaussians are the MFMA
+//                        columns and neurons the rows, so a layer's output
+//                        registers are already the next layer's B operand and
+//                        the hash gather writes its features straight into
+//                        the first layer's B operand (no LDS round trip).
+//
+// Position normalisation and the per-axis cell decision are computed one IEEE
+// fp32 operation at a time in the order written (the library is built with
+// -ffp-contract=off), so the chosen cell matches any other implementation of
+// the same formula bit for bit; interpolation and the MLP allow contraction.
+#include <hip/hip_runtime.h>
+
+#include "ia_internal.h"
+
+namespace ia {
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kP1 = 1u, kP2 = 2654435761u, kP3 = 805459861u, kP4 = 3674653429u;
+
+// Eq. 7 (contraction with the L2 norm, mapped to [0,1]^3) and Eq. 8.
+__device__ __forceinline__ void normalize_pos(float x, float y, float z, float t, float t_min, float t_max,
+                                              float xt[4]) {
+    float n2 = x * x + y * y;
+    n2 = n2 + z * z;
+    float n = sqrtf(n2);
+    float c0 = x, c1 = y, c2 = z;
+    if (!(n <= 1.0f)) {
+        float k = 2.0f - 1.0f / n;
+        k = k / n;
+        c0 = x * k;
+        c1 = y * k;
+        c2 = z * k;
+    }
+    float tn = (t - t_min) / (t_max - t_min);
+    tn = tn < 0.0f ? 0.0f : (tn > 1.0f ? 1.0f : tn);
+    float a0 = 0.25f * c0, a1 = 0.25f * c1, a2 = 0.25f * c2;
+    xt[0] = a0 + 0.5f;
+    xt[1] = a1 + 0.5f;
+    xt[2] = a2 + 0.5f;
+    xt[3] = tn;
+}
+
+// Per-axis cell: p = x*(res-1), i = clamp(floor p, 0, res-2), f = p - i.
+__device__ __forceinline__ void cell_axis(float x, int res, int& i, float& f) {
+    float p = x * (float)(res - 1);
+    int c = (int)floorf(p);
+    c = c < 0 ? 0 : (c > res - 2 ? res - 2 : c);
+    i = c;
+    f = p - (float)c;
+}
+
+// Quadrilinear interpolation of one level with F = 2 features.  The table of
+// the level starts at `tab` (T entries of 2 features).  Index per corner is
+// a separable combination of per-axis terms: sum (dense, row-major x fastest)
+// or XOR of coordinate * prime (hashed), then mod T.
+template <bool F16>
+__device__ __forceinline__ void interp_level2(const void* tab, const float xt[4], int res, int res_t, int dense,
+                                              uint32_t mask, float& z0, float& z1) {
+#pragma clang fp contract(fast)
+    int ci[4];
+    float f[4];
+    cell_axis(xt[0], res, ci[0], f[0]);
+    cell_axis(xt[1], res, ci[1], f[1]);
+    cell_axis(xt[2], res, ci[2], f[2]);
+    cell_axis(xt[3], res_t, ci[3], f[3]);
+    uint32_t tx[2], ty[2], tz[2], tt[2];
+    if (dense) {
+        uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
+        tx[0] = (uint32_t)ci[0];
+        tx[1] = tx[0] + 1u;
+        ty[0] = (uint32_t)ci[1] * r;
+        ty[1] = ty[0] + r;
+        tz[0] = (uint32_t)ci[2] * r2;
+        tz[1] = tz[0] + r2;
+        tt[0] = (uint32_t)ci[3] * r3;
+        tt[1] = tt[0] + r3;
+    } else {
+        tx[0] = (uint32_t)ci[0] * kP1;
+        tx[1] = (uint32_t)(ci[0] + 1) * kP1;
+        ty[0] = (uint32_t)ci[1] * kP2;
+        ty[1] = (uint32_t)(ci[1] + 1) * kP2;
+        tz[0] = (uint32_t)ci[2] * kP3;
+        tz[1] = (uint32_t)(ci[2] + 1) * kP3;
+        tt[0] = (uint32_t)ci[3] * kP4;
+        tt[1] = (uint32_t)(ci[3] + 1) * kP4;
+    }
+    float wx[2] = {1.0f - f[0], f[0]}, wy[2] = {1.0f - f[1], f[1]};
+    float wz[2] = {1.0f - f[2], f[2]}, wt[2] = {1.0f - f[3], f[3]};
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        int bx = c & 1, by = (c >> 1) & 1, bz = (c >> 2) & 1, bt = (c >> 3) & 1;
+        uint32_t idx = dense ? (tx[bx] + ty[by] + tz[bz] + tt[bt]) : (tx[bx] ^ ty[by] ^ tz[bz] ^ tt[bt]);
+        idx &= mask;
+        float w = ((wx[bx] * wy[by]) * wz[bz]) * wt[bt];
+        float v0, v1;
+        if (F16) {
+            uint32_t raw = reinterpret_cast<const uint32_t*>(tab)[idx];
+            _Float16 h0 = __builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
+            _Float16 h1 = __builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+            v0 = (float)h0;
+            v1 = (float)h1;
+        } else {
+            float2 v = reinterpret_cast<const float2*>(tab)[idx];
+            v0 = v.x;
+            v1 = v.y;
+        }
+        a0 += w * v0;
+        a1 += w * v1;
+    }
+    z0 = a0;
+    z1 = a1;
+}
+
+__device__ __forceinline__ float act_fn(int act, float x) {
+    if (act == IA_ACT_RELU) return x > 0.0f ? x : 0.0f;
+    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// ---------------------------------------------------------------- fp32 path
+
+constexpr int kF32MaxIn = 32, kF32MaxH = 64;
+
+template <int LF, int H1, int H2>
+__global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
+    // weights: W1 [H1][LF], W2 [H2][H1] (if H2 > 0), Wh [11][HL]
+    constexpr int HL = H2 > 0 ? H2 : H1;
+    __shared__ float sW1[H1 * LF];
+    __shared__ float sW2[H2 > 0 ? H2 * H1 : 1];
+    __shared__ float sWh[11 * HL];
+    __shared__ float sb1[H1], sb2[H2 > 0 ? H2 : 1], sbh[11];
+    const float* W1 = (const float*)a.W[0];
+    const float* W2 = (const float*)a.W[1];
+    const float* Wh = (const float*)a.W[H2 > 0 ? 2 : 1];
+    for (int k = threadIdx.x; k < H1 * LF; k += blockDim.x) sW1[k] = W1[k];
+    if (H2 > 0)
+        for (int k = threadIdx.x; k < H2 * H1; k += blockDim.x) sW2[k] = W2[k];
+    for (int k = threadIdx.x; k < 11 * HL; k += blockDim.x) sWh[k] = Wh[k];
+    for (int k = threadIdx.x; k < H1; k += blockDim.x) sb1[k] = a.b[0][k];
+    if (H2 > 0)
+        for (int k = threadIdx.x; k < H2; k += blockDim.x) sb2[k] = a.b[1][k];
+    for (int k = threadIdx.x; k < 11; k += blockDim.x) sbh[k] = a.b[H2 > 0 ? 2 : 1][k];
+    __syncthreads();
+
+    const int L = LF / 2;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < a.N) {
+        const float* p = a.pos + i * a.stride;
+        float xt[4];
+        normalize_pos(p[0], p[1], p[2], a.stride == 4 ? p[3] : a.t_scalar, a.h.t_min, a.h.t_max, xt);
+        float z[LF];
+#pragma unroll
+        for (int l = 0; l < L; ++l) {
+            const size_t off = (size_t)l * a.h.T * 2;
+            if (a.h.table_f16)
+                interp_level2<true>((const _Float16*)a.tables + off, xt, a.h.res_s[l], a.h.res_t[l], a.h.dense[l],
+                                    a.h.mask, z[2 * l], z[2 * l + 1]);
+            else
+                interp_level2<false>((const float*)a.tables + off, xt, a.h.res_s[l], a.h.res_t[l], a.h.dense[l],
+                                     a.h.mask, z[2 * l], z[2 * l + 1]);
+        }
+        float h1[H1];
+#pragma unroll
+        for (int o = 0; o < H1; ++o) {
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < LF; ++k) s = fmaf(sW1[o * LF + k], z[k], s);
+            h1[o] = act_fn(a.act, s + sb1[o]);
+        }
+        float hl[HL];
+        if (H2 > 0) {
+#pragma unroll
+            for (int o = 0; o < HL; ++o) {
+                float s = 0.0f;
+#pragma unroll
+                for (int k = 0; k < H1; ++k) s = fmaf(sW2[o * H1 + k], h1[k], s);
+                hl[o] = act_fn(a.act, s + sb2[o]);
+            }
+        } else {
+#pragma unroll
+            for (int o = 0; o < HL; ++o) hl[o] = h1[o];
+        }
+        float r[11];
+#pragma unroll
+        for (int o = 0; o < 11; ++o) {
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < HL; ++k) s = fmaf(sWh[o * HL + k], hl[k], s);
+            r[o] = s + sbh[o];
+        }
+        // Eq. 11
+        a.scales[i * 3 + 0] = expf(fminf(r[0], 20.0f));
+        a.scales[i * 3 + 1] = expf(fminf(r[1], 20.0f));
+        a.scales[i * 3 + 2] = expf(fminf(r[2], 20.0f));
+        float n = sqrtf(r[3] * r[3] + r[4] * r[4] + r[5] * r[5] + r[6] * r[6]);
+        n = fmaxf(n, 1e-12f);
+        a.quats[i * 4 + 0] = r[3] / n;
+        a.quats[i * 4 + 1] = r[4] / n;
+        a.quats[i * 4 + 2] = r[5] / n;
+        a.quats[i * 4 + 3] = r[6] / n;
+        a.colors[i * 3 + 0] = sigmoidf_(r[7]);
+        a.colors[i * 3 + 1] = sigmoidf_(r[8]);
+        a.colors[i * 3 + 2] = sigmoidf_(r[9]);
+        a.opacity[i] = sigmoidf_(r[10]);
+    }
+}
+
+// ---------------------------------------------------------------- fp16 MFMA path
+//
+// Register layout of v_mfma_f32_16x16x16_f16 (wave64, lane l, q = l/16,
+// c = l%16): A supplies row c, k-slots 4q..4q+3; B supplies column c, the
+// same k-slots; D holds rows 4q..4q+3 of column c.  Because A and B use the
+// same k-slots, any assignment of features to slots works as long as both
+// operands agree; we give slot (q, e) of k-block kb feature 16 kb + 4 q + e.
+
+__device__ __forceinline__ half4_t load_h4(const _Float16* p) {
+    return *reinterpret_cast<const half4_t*>(p);
+}
+
+__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int q = lane >> 4, c = lane & 15;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const _Float16* W1 = (const _Float16*)a.W[0];  // [64][32]
+    const _Float16* W2 = (const _Float16*)a.W[1];  // [64][64]
+    const _Float16* Wh = (const _Float16*)a.W[2];  // [11][64]
+
+    half4_t A1[4][2], A2[4][4], A3[4];
+    float B1[4][4], B2[4][4], B3[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) A1[rb][kb] = load_h4(W1 + (16 * rb + c) * 32 + 16 * kb + 4 * q);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) A2[rb][kb] = load_h4(W2 + (16 * rb + c) * 64 + 16 * kb + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            B1[rb][e] = a.b[0][16 * rb + 4 * q + e];
+            B2[rb][e] = a.b[1][16 * rb + 4 * q + e];
+        }
+    }
+    const half4_t zero4 = {0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) A3[kb] = c < 11 ? load_h4(Wh + c * 64 + 16 * kb + 4 * q) : zero4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) B3[e] = (4 * q + e) < 11 ? a.b[2][4 * q + e] : 0.0f;
+
+    // Levels handled by this lane: 8 kb + 2 q + lv.  Their parameters are
+    // picked with unrolled selects (uniform kernel-argument reads) instead of
+    // a lane-dependent index into the argument block.
+    int lres[2][2], lrest[2][2], ldense[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int lv = 0; lv < 2; ++lv) {
+            const int want = 8 * kb + 2 * q + lv;
+            int r = 0, rt = 0, dn = 0;
+#pragma unroll
+            for (int l = 0; l < 16; ++l) {
+                r = l == want ? a.h.res_s[l] : r;
+                rt = l == want ? a.h.res_t[l] : rt;
+                dn = l == want ? a.h.dense[l] : dn;
+            }
+            lres[kb][lv] = r;
+            lrest[kb][lv] = rt;
+            ldense[kb][lv] = dn;
+        }
+
+    __shared__ half4_t s_z[4 * 8 * 64];
+    half4_t* sZ = s_z + (threadIdx.x >> 6) * (8 * 64);  // this wave's [kb][g][lane]
+    const bool gelu = a.act == IA_ACT_GELU;
+    for (int64_t base = wave * 64; base < a.N; base += nwaves * 64) {
+        // ---- hash gather: lane (q, c) computes levels {2q, 2q+1, 8+2q, 9+2q}
+        // of Gaussians base + 16 g + c, g = 0..3, into its own LDS slots
+        // (a rolled loop over g keeps the number of loads in flight bounded).
+#pragma unroll 1
+        for (int g = 0; g < 4; ++g) {
+            int64_t gi = base + 16 * g + c;
+            if (gi >= a.N) gi = a.N - 1;
+            const float* p = a.pos + gi * a.stride;
+            float xt[4];
+            normalize_pos(p[0], p[1], p[2], a.stride == 4 ? p[3] : a.t_scalar, a.h.t_min, a.h.t_max, xt);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                half4_t zz;
+#pragma unroll
+                for (int lv = 0; lv < 2; ++lv) {
+                    const int l = 8 * kb + 2 * q + lv;
+                    float z0, z1;
+                    interp_level2<true>((const _Float16*)a.tables + (size_t)l * a.h.T * 2, xt, lres[kb][lv],
+                                        lrest[kb][lv], ldense[kb][lv], a.h.mask, z0, z1);
+                    zz[2 * lv] = (_Float16)z0;
+                    zz[2 * lv + 1] = (_Float16)z1;
+                }
+                sZ[(kb * 4 + g) * 64 + lane] = zz;
+            }
+        }
+        half4_t Z[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) Z[kb][g] = sZ[(kb * 4 + g) * 64 + lane];
+        // ---- trunk layer 1: 32 -> 64
+        half4_t H1[4][4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                floatx4 acc = {0, 0, 0, 0};
+                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A1[rb][0], Z[0][g], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A1[rb][1], Z[1][g], acc, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = acc[e] + B1[rb][e];
+                    v = gelu ? act_fn(IA_ACT_GELU, v) : act_fn(IA_ACT_RELU, v);
+                    H1[rb][g][e] = (_Float16)v;
+                }
+            }
+        // ---- trunk layer 2: 64 -> 64
+        half4_t H2[4][4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                floatx4 acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A2[rb][kb], H1[kb][g], acc, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = acc[e] + B2[rb][e];
+                    v = gelu ? act_fn(IA_ACT_GELU, v) : act_fn(IA_ACT_RELU, v);
+                    H2[rb][g][e] = (_Float16)v;
+                }
+            }
+        // ---- head block 64 -> 11 (rows 11..15 are zero) and Eq. 11
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            floatx4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A3[kb], H2[kb][g], acc, 0, 0, 0);
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = acc[e] + B3[e];
+            // lane q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
+            float part = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
+            float other = __shfl_xor(part, 16);
+            float n = fmaxf(sqrtf(part + other), 1e-12f);
+            const int64_t gi = base + 16 * g + c;
+            if (gi < a.N) {
+                if (q == 0) {
+                    a.scales[gi * 3 + 0] = expf(fminf(o[0], 20.0f));
+                    a.scales[gi * 3 + 1] = expf(fminf(o[1], 20.0f));
+                    a.scales[gi * 3 + 2] = expf(fminf(o[2], 20.0f));
+                    a.quats[gi * 4 + 0] = o[3] / n;
+                } else if (q == 1) {
+                    a.quats[gi * 4 + 1] = o[0] / n;
+                    a.quats[gi * 4 + 2] = o[1] / n;
+                    a.quats[gi * 4 + 3] = o[2] / n;
+                    a.colors[gi * 3 + 0] = sigmoidf_(o[3]);
+                } else if (q == 2) {
+                    a.colors[gi * 3 + 1] = sigmoidf_(o[0]);
+                    a.colors[gi * 3 + 2] = sigmoidf_(o[1]);
+                    a.opacity[gi] = sigmoidf_(o[2]);
+                }
+            }
+        }
+    }
+}
+
+int grid_for(int64_t items_per_block, int64_t N, int cap_blocks) {
+    int64_t b = (N + items_per_block - 1) / items_per_block;
+    if (b < 1) b = 1;
+    if (b > cap_blocks) b = cap_blocks;
+    return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
+    if (a.N <= 0) return hipSuccess;
+    if (dtype == IA_DTYPE_F16) {
+        // 256 threads = 4 waves x 64 Gaussians per block-iteration
+        int grid = grid_for(256, a.N, 256 * 64);
+        hipLaunchKernelGGL(decode_mfma_kernel, dim3(grid), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    int grid = grid_for(256, a.N, 1 << 30);
+    const int LF = a.in_dim, H1 = a.hidden[0], H2 = a.n_hidden > 1 ? a.hidden[1] : 0;
+    if (LF == 8 && H1 == 32 && H2 == 0)
+        hipLaunchKernelGGL((decode_f32_kernel<8, 32, 0>), dim3(grid), dim3(256), 0, s, a);
+    else if (LF == 32 && H1 == 64 && H2 == 64)
+        hipLaunchKernelGGL((decode_f32_kernel<32, 64, 64>), dim3(grid), dim3(256), 0, s, a);
+    else if (LF == 32 && H1 == 64 && H2 == 0)
+        hipLaunchKernelGGL((decode_f32_kernel<32, 64, 0>), dim3(grid), dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace ia

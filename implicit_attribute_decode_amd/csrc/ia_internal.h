@@ -1,0 +1,121 @@
+// Internal declarations shared by the translation units of libia.so.
+// Kernels live in decode.hip, hexplane.hip and render.hip; each file exports
+// host-side launchers that api.hip calls after validating arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ia.h"
+
+namespace ia {
+
+constexpr int kMaxLevels = 32;
+
+// Per-level geometry of the 4D hash encoder (SPIN-4DGS §3.3, Eq. 9).
+struct HashLevels {
+    int L;
+    int F;
+    uint32_t mask;  // 2^log2T - 1
+    uint32_t T;     // 2^log2T
+    int table_f16;
+    float t_min, t_max;
+    int res_s[kMaxLevels];  // vertices per spatial axis
+    int res_t[kMaxLevels];  // vertices on the t axis
+    int dense[kMaxLevels];  // 1: row-major dense indexing, 0: hashed
+};
+
+struct DecodeArgs {
+    HashLevels h;
+    const void* tables;
+    const void* W[4];  // trunk layers then the 11-row head block, row-major [out][in]
+    const float* b[4];
+    int in_dim;
+    int n_hidden;
+    int hidden[4];
+    int act;
+    const float* pos;  // [N, stride]
+    int stride;        // 3 (scalar t) or 4 (per-point t)
+    float t_scalar;
+    int64_t N;
+    float* scales;
+    float* quats;
+    float* colors;
+    float* opacity;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
+
+struct HexArgs {
+    int res_xyz, res_t, C;
+    float aabb;
+    const _Float16* planes[6];
+    const _Float16* W[3];
+    const float* b[3];
+    const float* means;
+    const float* scales;
+    const float* quats;
+    const float* sh;
+    const float* opacity;
+    float t;
+    int64_t N;
+    float* o_means;
+    float* o_scales;
+    float* o_quats;
+    float* o_sh;
+    float* o_opacity;
+};
+
+hipError_t launch_hexplane(const HexArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- render
+
+// Camera in the device-side table.  centre = -R^T t (for SH view directions).
+struct DevCamera {
+    float R[9];
+    float t[3];
+    float fx, fy, cx, cy, near_z;
+    float centre[3];
+    float bg[3];
+    int W, H;
+};
+
+// Byte offsets of every buffer inside the render workspace.
+struct RenderLayout {
+    size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum2, boff, keys0, keys1, vals0, vals1,
+        counts, digit_tot, ranges, nent, total;
+    int64_t N, cap, ntiles_all;
+    int frames, tiles_x, tiles_y, nb1, nb2, sort_blocks;
+};
+
+RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entries);
+
+struct RenderArgs {
+    const float* means;
+    int means_stride;
+    const float* scales;
+    const float* quats;
+    const float* colors;
+    const float* sh;
+    const float* opacity;
+    int sh_degree;
+    int frames, W, H;
+    const int64_t* frame_offsets_host;
+    const DevCamera* cams_host;
+    unsigned char* ws;
+    RenderLayout lay;
+    float* image;
+    float* T_final;
+    uint32_t* n_contrib;
+    uint64_t* n_entries_out;
+    uint32_t* overflow_out;
+    int sort_passes;  // number of 8-bit LSD passes over the key
+};
+
+// Enqueue the whole render.  Returns the pointers of the final sorted key /
+// value buffers through keys_out / vals_out.
+hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** keys_out, const uint32_t** vals_out);
+
+}  // namespace ia

@@ -1,0 +1,760 @@
+// Tile rasteriser for 3D Gaussians (SPIN-4DGS, "Implicit 4D Gaussian
+// Splatting for Fast Motion with Large Inter-Frame Displacements", §3.1):
+// Eq. 2 covariance from scale and quaternion, Eq. 3 EWA projection to a 2D
+// conic, Eq. 1 / Eq. 4 front-to-back alpha compositing, on 16x16-pixel tiles.
+//
+// Pipeline for a batch of frames (all kernels on one stream, no host sync):
+//   preprocess  one thread per Gaussian: project, cull, conic, 3-sigma tile
+//               rect, tiles touched; per-block sum of tiles touched
+//   scan        two-level exclusive prefix sum of the block sums; the total
+//               entry count stays in device memory
+//   emit        each block spreads its Gaussians' entries over all its
+//               threads: key = (frame*tiles + tile) << 32 | depth bits,
+//               value = Gaussian index, written in emission order
+//   sort        stable LSD radix sort, 8-bit digits, only over the key bits
+//               that can be non-zero (32 depth bits + tile-index bits); per
+//               pass: per-block digit histograms, a per-digit scan over
+//               blocks, and a stable scatter ranked by wave ballots
+//   ranges      [start, end) of every tile in the sorted list
+//   raster      one 256-thread block per tile; Gaussians staged through LDS
+//               in batches of 256; per pixel the 3-sigma test, alpha =
+//               min(0.99, o G), skip alpha < 1/255, stop once T < 1e-4; a wave
+//               whose pixels are all saturated skips the batch (ballot), and
+//               the block stops once every pixel is.
+//
+// Projection runs one IEEE fp32 operation at a time in source order (the
+// library is built with -ffp-contract=off, and '/' and sqrt are correctly
+// rounded), which makes tile rects and depth keys reproducible bit for bit.
+#include <hip/hip_runtime.h>
+
+#include "ia_internal.h"
+
+namespace ia {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kSortItems = 8;                      // keys per thread per sort tile
+constexpr int kSortTile = kBlock * kSortItems;     // 2048
+constexpr int kScanChunk = 1024;                   // block sums per second-level group
+
+// ---------------------------------------------------------------- helpers
+
+struct Payload {
+    uint32_t w[896];
+};
+
+__global__ void upload_kernel(uint32_t* dst, Payload p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = p.w[i];
+}
+
+hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(src);
+    size_t words = (bytes + 3) / 4;
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+    for (size_t off = 0; off < words; off += 896) {
+        Payload p;
+        int n = (int)(words - off < 896 ? words - off : 896);
+        for (int i = 0; i < n; ++i) p.w[i] = w[off + i];
+        hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, d + off, p, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+__device__ __forceinline__ int frame_of(const int64_t* fo, int F, int64_t i) {
+    int lo = 0, hi = F - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (fo[mid] <= i)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Inclusive wave-level prefix sum (wave64).
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        T o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive block-level prefix sum over 256 threads; returns the block total.
+template <typename T>
+__device__ __forceinline__ T block_excl_scan(T v, T& total) {
+    __shared__ T s_w[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    T inc = wave_incl_scan(v);
+    if (lane == 63) s_w[w] = inc;
+    __syncthreads();
+    T off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        T x = s_w[k];
+        if (k < w) off += x;
+        tot += x;
+    }
+    __syncthreads();
+    total = tot;
+    return off + inc - v;
+}
+
+// ---------------------------------------------------------------- preprocess
+
+struct PreArgs {
+    const float* means;
+    int stride;
+    const float* scales;
+    const float* quats;
+    const float* colors;
+    const float* sh;
+    const float* opacity;
+    int sh_degree;
+    const DevCamera* cams;
+    const int64_t* fo;
+    int F;
+    int64_t N;
+    float4* pa;
+    float4* pb;
+    float* pc;
+    float* depth;
+    ushort4* rect;
+    uint32_t* tiles;
+    uint32_t* bsum;
+};
+
+// Degree-3 real spherical harmonics (orthonormal, l-major, m = -l..l, the
+// Condon-Shortley sign convention) at unit direction (x, y, z).
+__device__ __forceinline__ void sh_basis16(float x, float y, float z, float Y[16]) {
+    const float xx = x * x, yy = y * y, zz = z * z;
+    Y[0] = 0.28209479177387814f;
+    Y[1] = -0.48860251190291992f * y;
+    Y[2] = 0.48860251190291992f * z;
+    Y[3] = -0.48860251190291992f * x;
+    Y[4] = 1.0925484305920792f * x * y;
+    Y[5] = -1.0925484305920792f * y * z;
+    Y[6] = 0.31539156525252005f * (2.0f * zz - xx - yy);
+    Y[7] = -1.0925484305920792f * x * z;
+    Y[8] = 0.54627421529603959f * (xx - yy);
+    Y[9] = -0.59004358992664352f * y * (3.0f * xx - yy);
+    Y[10] = 2.8906114426405538f * x * y * z;
+    Y[11] = -0.45704579946446572f * y * (4.0f * zz - xx - yy);
+    Y[12] = 0.37317633259011546f * z * (2.0f * zz - 3.0f * xx - 3.0f * yy);
+    Y[13] = -0.45704579946446572f * x * (4.0f * zz - xx - yy);
+    Y[14] = 1.4453057213202769f * z * (xx - yy);
+    Y[15] = -0.59004358992664352f * x * (xx - 3.0f * yy);
+}
+
+__global__ void __launch_bounds__(kBlock) preprocess_kernel(PreArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    uint32_t ntouch = 0;
+    if (i < a.N) {
+        const DevCamera& cam = a.cams[frame_of(a.fo, a.F, i)];
+        const float* mu = a.means + i * a.stride;
+        const float* R = cam.R;
+        const float m0 = mu[0], m1 = mu[1], m2 = mu[2];
+        float px = R[0] * m0 + R[1] * m1;
+        px = px + R[2] * m2;
+        px = px + cam.t[0];
+        float py = R[3] * m0 + R[4] * m1;
+        py = py + R[5] * m2;
+        py = py + cam.t[1];
+        float pz = R[6] * m0 + R[7] * m1;
+        pz = pz + R[8] * m2;
+        pz = pz + cam.t[2];
+        bool vis = pz > cam.near_z;
+        float u = 0, v = 0, A = 0, B = 0, C = 0;
+        int x0 = 0, x1 = -1, y0 = 0, y1 = -1;
+        if (vis) {
+            const float* q = a.quats + i * 4;
+            const float* s = a.scales + i * 3;
+            float qn = q[0] * q[0] + q[1] * q[1];
+            qn = qn + q[2] * q[2];
+            qn = qn + q[3] * q[3];
+            qn = sqrtf(qn);
+            const float w = q[0] / qn, x = q[1] / qn, y = q[2] / qn, z = q[3] / qn;
+            float Rq[9];
+            Rq[0] = 1.0f - 2.0f * (y * y + z * z);
+            Rq[1] = 2.0f * (x * y - w * z);
+            Rq[2] = 2.0f * (x * z + w * y);
+            Rq[3] = 2.0f * (x * y + w * z);
+            Rq[4] = 1.0f - 2.0f * (x * x + z * z);
+            Rq[5] = 2.0f * (y * z - w * x);
+            Rq[6] = 2.0f * (x * z - w * y);
+            Rq[7] = 2.0f * (y * z + w * x);
+            Rq[8] = 1.0f - 2.0f * (x * x + y * y);
+            float M[9];
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) M[r * 3 + k] = Rq[r * 3 + k] * s[k];
+            // Eq. 2: Sigma = (R S)(R S)^T
+            float S[9];
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    float acc = M[r * 3 + 0] * M[k * 3 + 0] + M[r * 3 + 1] * M[k * 3 + 1];
+                    S[r * 3 + k] = acc + M[r * 3 + 2] * M[k * 3 + 2];
+                }
+            // Eq. 3: Sigma2D = J W Sigma W^T J^T with T = J W (2x3)
+            const float zz = pz * pz;
+            const float j00 = cam.fx / pz;
+            const float j02 = -(cam.fx * px) / zz;
+            const float j11 = cam.fy / pz;
+            const float j12 = -(cam.fy * py) / zz;
+            float T[6];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                T[k] = j00 * R[k] + j02 * R[6 + k];
+                T[3 + k] = j11 * R[3 + k] + j12 * R[6 + k];
+            }
+            float U[6];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    float acc = T[r * 3 + 0] * S[0 * 3 + k] + T[r * 3 + 1] * S[1 * 3 + k];
+                    U[r * 3 + k] = acc + T[r * 3 + 2] * S[2 * 3 + k];
+                }
+            float c2[4];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    float acc = U[r * 3 + 0] * T[k * 3 + 0] + U[r * 3 + 1] * T[k * 3 + 1];
+                    c2[r * 2 + k] = acc + U[r * 3 + 2] * T[k * 3 + 2];
+                }
+            const float ca = c2[0], cb = c2[1], cc = c2[3];
+            const float det = ca * cc - cb * cb;
+            vis = det > 0.0f;
+            if (vis) {
+                const float inv = 1.0f / det;
+                A = cc * inv;
+                B = -cb * inv;
+                C = ca * inv;
+                const float mid = 0.5f * (ca + cc);
+                float disc = mid * mid - det;
+                disc = disc > 0.0f ? disc : 0.0f;
+                const float lam = mid + sqrtf(disc);
+                const float rr = ceilf(3.0f * sqrtf(lam));
+                u = (cam.fx * px) / pz + cam.cx;
+                v = (cam.fy * py) / pz + cam.cy;
+                vis = isfinite(u) && isfinite(v) && isfinite(A) && isfinite(B) && isfinite(C) && isfinite(rr);
+                if (vis) {
+                    float fx0 = ceilf((u - rr) - 0.5f), fx1 = floorf((u + rr) - 0.5f);
+                    float fy0 = ceilf((v - rr) - 0.5f), fy1 = floorf((v + rr) - 0.5f);
+                    fx0 = fx0 > 0.0f ? fx0 : 0.0f;
+                    fy0 = fy0 > 0.0f ? fy0 : 0.0f;
+                    fx1 = fx1 < (float)(cam.W - 1) ? fx1 : (float)(cam.W - 1);
+                    fy1 = fy1 < (float)(cam.H - 1) ? fy1 : (float)(cam.H - 1);
+                    vis = fx0 <= fx1 && fy0 <= fy1;
+                    if (vis) {
+                        x0 = (int)fx0 >> 4;
+                        x1 = (int)fx1 >> 4;
+                        y0 = (int)fy0 >> 4;
+                        y1 = (int)fy1 >> 4;
+                    }
+                }
+            }
+        }
+        float r = 0, g = 0, b = 0, o = 0;
+        if (vis) {
+            o = a.opacity[i];
+            if (a.sh_degree == 3) {
+                float d0 = m0 - cam.centre[0], d1 = m1 - cam.centre[1], d2 = m2 - cam.centre[2];
+                const float inv = 1.0f / sqrtf(d0 * d0 + d1 * d1 + d2 * d2);
+                float Y[16];
+                sh_basis16(d0 * inv, d1 * inv, d2 * inv, Y);
+                const float* shc = a.sh + i * 48;
+                float acc[3] = {0.5f, 0.5f, 0.5f};
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    acc[0] += shc[k * 3 + 0] * Y[k];
+                    acc[1] += shc[k * 3 + 1] * Y[k];
+                    acc[2] += shc[k * 3 + 2] * Y[k];
+                }
+                r = fmaxf(acc[0], 0.0f);
+                g = fmaxf(acc[1], 0.0f);
+                b = fmaxf(acc[2], 0.0f);
+            } else {
+                r = a.colors[i * 3 + 0];
+                g = a.colors[i * 3 + 1];
+                b = a.colors[i * 3 + 2];
+            }
+            ntouch = (uint32_t)((x1 - x0 + 1) * (y1 - y0 + 1));
+        }
+        a.pa[i] = make_float4(u, v, A, B);
+        a.pb[i] = make_float4(C, o, r, g);
+        a.pc[i] = b;
+        a.depth[i] = vis ? pz : 0.0f;
+        a.rect[i] = vis ? make_ushort4((unsigned short)x0, (unsigned short)y0, (unsigned short)x1, (unsigned short)y1)
+                        : make_ushort4(0, 0, 0, 0);
+        a.tiles[i] = ntouch;
+    }
+    uint32_t total;
+    block_excl_scan<uint32_t>(ntouch, total);
+    if (threadIdx.x == 0) a.bsum[blockIdx.x] = total;
+}
+
+// ---------------------------------------------------------------- scan of block sums
+
+__global__ void __launch_bounds__(kBlock) scan_reduce_kernel(const uint32_t* bsum, int nb1, uint64_t* bsum2) {
+    uint64_t v = 0;
+    const int base = blockIdx.x * kScanChunk;
+#pragma unroll
+    for (int k = 0; k < kScanChunk / kBlock; ++k) {
+        int idx = base + k * kBlock + threadIdx.x;
+        if (idx < nb1) v += bsum[idx];
+    }
+    uint64_t total;
+    block_excl_scan<uint64_t>(v, total);
+    if (threadIdx.x == 0) bsum2[blockIdx.x] = total;
+}
+
+__global__ void __launch_bounds__(kBlock) scan_top_kernel(uint64_t* bsum2, int nb2, uint64_t cap, uint64_t* nent,
+                                                          uint64_t* nent_out, uint32_t* ovf_out) {
+    uint64_t carry = 0;
+    for (int base = 0; base < nb2; base += kBlock) {
+        int idx = base + threadIdx.x;
+        uint64_t v = idx < nb2 ? bsum2[idx] : 0;
+        uint64_t total;
+        uint64_t ex = block_excl_scan<uint64_t>(v, total);
+        if (idx < nb2) bsum2[idx] = carry + ex;
+        carry += total;
+    }
+    if (threadIdx.x == 0) {
+        nent[0] = carry;
+        nent[1] = carry > cap ? 1 : 0;
+        if (nent_out) *nent_out = carry;
+        if (ovf_out) *ovf_out = carry > cap ? 1u : 0u;
+    }
+}
+
+__global__ void __launch_bounds__(kBlock) scan_down_kernel(const uint32_t* bsum, int nb1, const uint64_t* bsum2,
+                                                           uint64_t* boff) {
+    const int base = blockIdx.x * kScanChunk;
+    uint64_t carry = bsum2[blockIdx.x];
+#pragma unroll
+    for (int k = 0; k < kScanChunk / kBlock; ++k) {
+        int idx = base + k * kBlock + threadIdx.x;
+        uint64_t v = idx < nb1 ? bsum[idx] : 0;
+        uint64_t total;
+        uint64_t ex = block_excl_scan<uint64_t>(v, total);
+        if (idx < nb1) boff[idx] = carry + ex;
+        carry += total;
+    }
+}
+
+// ---------------------------------------------------------------- key emission
+
+struct EmitArgs {
+    const uint32_t* tiles;
+    const ushort4* rect;
+    const float* depth;
+    const uint64_t* boff;
+    const int64_t* fo;
+    int F;
+    int64_t N;
+    int tiles_x;
+    uint32_t ntiles;
+    uint64_t cap;
+    uint64_t* keys;
+    uint32_t* vals;
+};
+
+__global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
+    __shared__ uint32_t s_off[kBlock + 1];
+    __shared__ ushort4 s_rect[kBlock];
+    __shared__ uint32_t s_dbits[kBlock];
+    __shared__ uint32_t s_tbase[kBlock];  // frame * ntiles
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    uint32_t n = 0;
+    if (i < a.N) {
+        n = a.tiles[i];
+        s_rect[threadIdx.x] = a.rect[i];
+        s_dbits[threadIdx.x] = __float_as_uint(a.depth[i]);
+        s_tbase[threadIdx.x] = (uint32_t)frame_of(a.fo, a.F, i) * a.ntiles;
+    }
+    uint32_t total;
+    uint32_t ex = block_excl_scan<uint32_t>(n, total);
+    s_off[threadIdx.x] = ex;
+    if (threadIdx.x == 0) s_off[kBlock] = total;
+    __syncthreads();
+    const uint64_t base = a.boff[blockIdx.x];
+    for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
+        // owner: last j with s_off[j] <= e (entries of culled Gaussians are empty)
+        int lo = 0, hi = kBlock - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= e)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const ushort4 rc = s_rect[lo];
+        const uint32_t k = e - s_off[lo];
+        const uint32_t w = (uint32_t)rc.z - rc.x + 1;
+        const uint32_t ty = rc.y + k / w, tx = rc.x + k % w;
+        const uint64_t tile = (uint64_t)(s_tbase[lo] + ty * (uint32_t)a.tiles_x + tx);
+        const uint64_t pos = base + e;
+        if (pos < a.cap) {
+            a.keys[pos] = (tile << 32) | s_dbits[lo];
+            a.vals[pos] = (uint32_t)((int64_t)blockIdx.x * kBlock + lo);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- radix sort
+
+struct SortPass {
+    const uint64_t* keys_in;
+    const uint32_t* vals_in;
+    uint64_t* keys_out;
+    uint32_t* vals_out;
+    const uint64_t* nent;  // [0] = entries emitted
+    uint64_t cap;
+    int shift;
+    int nblocks;
+    uint32_t* counts;     // [256][nblocks]
+    uint32_t* digit_tot;  // [256]
+};
+
+__device__ __forceinline__ void sort_chunk(const SortPass& p, uint32_t& begin, uint32_t& end) {
+    uint64_t E = p.nent[0];
+    if (E > p.cap) E = p.cap;
+    uint64_t per = (E + p.nblocks - 1) / p.nblocks;
+    per = (per + kSortTile - 1) / kSortTile * kSortTile;
+    uint64_t b = (uint64_t)blockIdx.x * per, e = b + per;
+    if (b > E) b = E;
+    if (e > E) e = E;
+    begin = (uint32_t)b;
+    end = (uint32_t)e;
+}
+
+__global__ void __launch_bounds__(kBlock) sort_upsweep_kernel(SortPass p) {
+    __shared__ uint32_t hist[4][256];
+    const int w = threadIdx.x >> 6;
+    for (int k = threadIdx.x; k < 4 * 256; k += kBlock) (&hist[0][0])[k] = 0;
+    __syncthreads();
+    uint32_t begin, end;
+    sort_chunk(p, begin, end);
+    for (uint32_t idx = begin + threadIdx.x; idx < end; idx += kBlock) {
+        uint32_t d = (uint32_t)(p.keys_in[idx] >> p.shift) & 255u;
+        atomicAdd(&hist[w][d], 1u);
+    }
+    __syncthreads();
+    const int d = threadIdx.x;
+    p.counts[d * p.nblocks + blockIdx.x] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+}
+
+// One block per digit: exclusive scan of that digit's counts over blocks.
+__global__ void __launch_bounds__(kBlock) sort_scan_kernel(SortPass p) {
+    uint32_t* c = p.counts + blockIdx.x * p.nblocks;
+    uint32_t carry = 0;
+    for (int base = 0; base < p.nblocks; base += kBlock) {
+        int idx = base + threadIdx.x;
+        uint32_t v = idx < p.nblocks ? c[idx] : 0;
+        uint32_t total;
+        uint32_t ex = block_excl_scan<uint32_t>(v, total);
+        if (idx < p.nblocks) c[idx] = carry + ex;
+        carry += total;
+    }
+    if (threadIdx.x == 0) p.digit_tot[blockIdx.x] = carry;
+}
+
+// Stable scatter.  Sort tile = 4 waves x 8 steps x 64 lanes, item order
+// wave-major then step then lane (the chunk order).  Per step each lane finds
+// the lanes holding the same digit with eight ballots; its rank is the count
+// of such lanes below it plus the wave's running count for the digit.
+__global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
+    __shared__ uint32_t s_base[256];
+    __shared__ uint32_t s_wc[4][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    {
+        uint32_t v = p.digit_tot[threadIdx.x];
+        uint32_t total;
+        uint32_t ex = block_excl_scan<uint32_t>(v, total);
+        s_base[threadIdx.x] = ex + p.counts[threadIdx.x * p.nblocks + blockIdx.x];
+    }
+    uint32_t begin, end;
+    sort_chunk(p, begin, end);
+    const uint64_t end_all = p.nent[0] < p.cap ? p.nent[0] : p.cap;  // bound on every destination
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (uint32_t tile = begin; tile < end; tile += kSortTile) {
+        for (int k = threadIdx.x; k < 4 * 256; k += kBlock) (&s_wc[0][0])[k] = 0;
+        __syncthreads();
+        uint64_t key[kSortItems];
+        uint32_t val[kSortItems], dig[kSortItems], rank[kSortItems];
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t idx = tile + w * (64 * kSortItems) + j * 64 + lane;
+            const bool valid = idx < end;
+            key[j] = valid ? p.keys_in[idx] : 0ull;
+            val[j] = valid ? p.vals_in[idx] : 0u;
+            const uint32_t d = (uint32_t)(key[j] >> p.shift) & 255u;
+            dig[j] = valid ? d : 256u;
+            uint64_t peers = __ballot(valid);
+#pragma unroll
+            for (int bit = 0; bit < 8; ++bit) {
+                const uint64_t b = __ballot((d >> bit) & 1u);
+                peers &= ((d >> bit) & 1u) ? b : ~b;
+            }
+            uint32_t prior = 0;
+            if (valid) prior = s_wc[w][d];
+            const uint32_t below = (uint32_t)__popcll(peers & lt_mask);
+            // the lowest lane of each peer group advances the wave's counter
+            if (valid && below == 0) s_wc[w][d] = prior + (uint32_t)__popcll(peers);
+            rank[j] = prior + below;
+        }
+        __syncthreads();
+        // per digit: offsets of each wave inside this tile
+        {
+            const int d = threadIdx.x;
+            uint32_t c0 = s_wc[0][d], c1 = s_wc[1][d], c2 = s_wc[2][d], c3 = s_wc[3][d];
+            s_wc[0][d] = s_base[d];
+            s_wc[1][d] = s_base[d] + c0;
+            s_wc[2][d] = s_base[d] + c0 + c1;
+            s_wc[3][d] = s_base[d] + c0 + c1 + c2;
+            s_base[d] += c0 + c1 + c2 + c3;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t dst = dig[j] < 256u ? s_wc[w][dig[j]] + rank[j] : 0xffffffffu;
+            if (dst < end_all) {
+                p.keys_out[dst] = key[j];
+                p.vals_out[dst] = val[j];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- tile ranges
+
+__global__ void ranges_kernel(const uint64_t* keys, const uint64_t* nent, uint64_t cap, uint2* ranges,
+                              uint32_t ntiles_all) {
+    uint64_t E = nent[0];
+    if (E > cap) E = cap;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < E; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t t = (uint32_t)(keys[i] >> 32);
+        if (t >= ntiles_all) continue;  // cannot happen for emitted keys; keeps a bad key in bounds
+        if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[t].x = (uint32_t)i;
+        if (i + 1 == E || (uint32_t)(keys[i + 1] >> 32) != t) ranges[t].y = (uint32_t)(i + 1);
+    }
+}
+
+// ---------------------------------------------------------------- raster
+
+struct RasterArgs {
+    const uint2* ranges;
+    const uint32_t* vals;
+    const float4* pa;
+    const float4* pb;
+    const float* pc;
+    const DevCamera* cams;
+    int W, H, tiles_x;
+    uint32_t ntiles;
+    uint64_t cap;
+    int64_t N;
+    float* image;
+    float* T_final;
+    uint32_t* n_contrib;
+};
+
+__global__ void __launch_bounds__(kBlock) raster_kernel(RasterArgs a) {
+#pragma clang fp contract(fast)
+    __shared__ float4 s_a[kBlock];
+    __shared__ float4 s_b[kBlock];
+    __shared__ float s_c[kBlock];
+    const int f = blockIdx.z;
+    const uint32_t tile = (uint32_t)f * a.ntiles + blockIdx.y * (uint32_t)a.tiles_x + blockIdx.x;
+    uint2 rg = a.ranges[tile];
+    if (rg.y > a.cap) rg.y = (uint32_t)a.cap;
+    if (rg.x > rg.y) rg.x = rg.y;
+    const int px = blockIdx.x * 16 + (threadIdx.x & 15);
+    const int py = blockIdx.y * 16 + (threadIdx.x >> 4);
+    const bool inside = px < a.W && py < a.H;
+    const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
+    float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
+    uint32_t last = 0;
+    bool done = !inside;
+    for (uint32_t start = rg.x; start < rg.y; start += kBlock) {
+        if (__syncthreads_count(done) == kBlock) break;
+        const uint32_t idx = start + threadIdx.x;
+        if (idx < rg.y) {
+            uint32_t gid = a.vals[idx];
+            if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
+            s_a[threadIdx.x] = a.pa[gid];
+            s_b[threadIdx.x] = a.pb[gid];
+            s_c[threadIdx.x] = a.pc[gid];
+        }
+        __syncthreads();
+        const int n = (int)min((uint32_t)kBlock, rg.y - start);
+        if (__ballot(!done) != 0ull && !done) {
+            for (int j = 0; j < n; ++j) {
+                const float4 ga = s_a[j];
+                const float dx = fx - ga.x, dy = fy - ga.y;
+                const float4 gb = s_b[j];
+                const float power = -0.5f * (ga.z * dx * dx + gb.x * dy * dy) - ga.w * dx * dy;
+                if (power < -4.5f || power > 0.0f) continue;
+                const float alpha = fminf(0.99f, gb.y * __expf(power));
+                if (alpha < (1.0f / 255.0f)) continue;
+                const float wgt = alpha * T;
+                cr += gb.z * wgt;
+                cg += gb.w * wgt;
+                cb += s_c[j] * wgt;
+                T = T * (1.0f - alpha);
+                last = start - rg.x + (uint32_t)j + 1u;
+                if (T < 1e-4f) {
+                    done = true;
+                    break;
+                }
+            }
+        }
+    }
+    if (inside) {
+        const DevCamera& cam = a.cams[f];
+        const size_t plane = (size_t)a.W * a.H;
+        const size_t pix = (size_t)py * a.W + px;
+        float* img = a.image + (size_t)f * 3 * plane;
+        img[pix] = cr + T * cam.bg[0];
+        img[plane + pix] = cg + T * cam.bg[1];
+        img[2 * plane + pix] = cb + T * cam.bg[2];
+        if (a.T_final) a.T_final[(size_t)f * plane + pix] = T;
+        if (a.n_contrib) a.n_contrib[(size_t)f * plane + pix] = last;
+    }
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int grid_cap(int64_t n, int per, int cap) {
+    int64_t g = (n + per - 1) / per;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+}  // namespace
+
+RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entries) {
+    RenderLayout L{};
+    L.N = N;
+    L.cap = max_entries;
+    L.frames = frames;
+    L.tiles_x = (W + 15) / 16;
+    L.tiles_y = (H + 15) / 16;
+    L.ntiles_all = (int64_t)frames * L.tiles_x * L.tiles_y;
+    const int64_t n1 = N > 0 ? N : 1;
+    L.nb1 = (int)((n1 + kBlock - 1) / kBlock);
+    L.nb2 = (L.nb1 + kScanChunk - 1) / kScanChunk;
+    int64_t sb = (max_entries + kSortTile - 1) / kSortTile;
+    L.sort_blocks = (int)(sb < 1 ? 1 : (sb > 1024 ? 1024 : sb));
+    const int64_t cap1 = max_entries > 0 ? max_entries : 1;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L.cams = take(sizeof(DevCamera) * frames);
+    L.fo = take(sizeof(int64_t) * (frames + 1));
+    L.pa = take(16 * (size_t)n1);
+    L.pb = take(16 * (size_t)n1);
+    L.pc = take(4 * (size_t)n1);
+    L.depth = take(4 * (size_t)n1);
+    L.rect = take(8 * (size_t)n1);
+    L.tiles = take(4 * (size_t)n1);
+    L.bsum = take(4 * (size_t)L.nb1);
+    L.bsum2 = take(8 * (size_t)L.nb2);
+    L.boff = take(8 * (size_t)L.nb1);
+    L.keys0 = take(8 * (size_t)cap1);
+    L.keys1 = take(8 * (size_t)cap1);
+    L.vals0 = take(4 * (size_t)cap1);
+    L.vals1 = take(4 * (size_t)cap1);
+    L.counts = take(4 * 256 * (size_t)L.sort_blocks);
+    L.digit_tot = take(4 * 256);
+    L.ranges = take(8 * (size_t)(L.ntiles_all > 0 ? L.ntiles_all : 1));
+    L.nent = take(16);
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** keys_out, const uint32_t** vals_out) {
+    const RenderLayout& L = a.lay;
+    unsigned char* ws = a.ws;
+    DevCamera* cams = reinterpret_cast<DevCamera*>(ws + L.cams);
+    int64_t* fo = reinterpret_cast<int64_t*>(ws + L.fo);
+    hipError_t e = upload(cams, a.cams_host, sizeof(DevCamera) * a.frames, s);
+    if (e != hipSuccess) return e;
+    e = upload(fo, a.frame_offsets_host, sizeof(int64_t) * (a.frames + 1), s);
+    if (e != hipSuccess) return e;
+
+    float4* pa = reinterpret_cast<float4*>(ws + L.pa);
+    float4* pb = reinterpret_cast<float4*>(ws + L.pb);
+    float* pc = reinterpret_cast<float*>(ws + L.pc);
+    float* depth = reinterpret_cast<float*>(ws + L.depth);
+    ushort4* rect = reinterpret_cast<ushort4*>(ws + L.rect);
+    uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
+    uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + L.bsum);
+    uint64_t* bsum2 = reinterpret_cast<uint64_t*>(ws + L.bsum2);
+    uint64_t* boff = reinterpret_cast<uint64_t*>(ws + L.boff);
+    uint64_t* keys[2] = {reinterpret_cast<uint64_t*>(ws + L.keys0), reinterpret_cast<uint64_t*>(ws + L.keys1)};
+    uint32_t* vals[2] = {reinterpret_cast<uint32_t*>(ws + L.vals0), reinterpret_cast<uint32_t*>(ws + L.vals1)};
+    uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
+    uint32_t* digit_tot = reinterpret_cast<uint32_t*>(ws + L.digit_tot);
+    uint2* ranges = reinterpret_cast<uint2*>(ws + L.ranges);
+    uint64_t* nent = reinterpret_cast<uint64_t*>(ws + L.nent);
+    const int64_t N = L.N;
+    const uint32_t ntiles = (uint32_t)(L.tiles_x * L.tiles_y);
+
+    if (N > 0) {
+        PreArgs pre{a.means, a.means_stride, a.scales, a.quats, a.colors, a.sh, a.opacity, a.sh_degree,
+                    cams, fo, a.frames, N, pa, pb, pc, depth, rect, tiles, bsum};
+        hipLaunchKernelGGL(preprocess_kernel, dim3(L.nb1), dim3(kBlock), 0, s, pre);
+        hipLaunchKernelGGL(scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
+    }
+    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, N > 0 ? L.nb2 : 0, (uint64_t)L.cap, nent,
+                       a.n_entries_out, a.overflow_out);
+    if (N > 0) {
+        hipLaunchKernelGGL(scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
+        EmitArgs em{tiles, rect, depth, boff, fo, a.frames, N, L.tiles_x, ntiles, (uint64_t)L.cap, keys[0], vals[0]};
+        hipLaunchKernelGGL(emit_kernel, dim3(L.nb1), dim3(kBlock), 0, s, em);
+    }
+    int cur = 0;
+    for (int pass = 0; pass < a.sort_passes; ++pass) {
+        SortPass sp{keys[cur], vals[cur], keys[cur ^ 1], vals[cur ^ 1], nent, (uint64_t)L.cap, 8 * pass,
+                    L.sort_blocks, counts, digit_tot};
+        hipLaunchKernelGGL(sort_upsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
+        hipLaunchKernelGGL(sort_scan_kernel, dim3(256), dim3(kBlock), 0, s, sp);
+        hipLaunchKernelGGL(sort_downsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
+        cur ^= 1;
+    }
+    const int64_t nr = 2 * L.ntiles_all;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_cap(nr, kBlock, 4096)), dim3(kBlock), 0, s,
+                       reinterpret_cast<uint32_t*>(ranges), 0u, nr);
+    hipLaunchKernelGGL(ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, keys[cur], nent,
+                       (uint64_t)L.cap, ranges, (uint32_t)L.ntiles_all);
+    RasterArgs ra{ranges, vals[cur], pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, (uint64_t)L.cap, N,
+                  a.image, a.T_final, a.n_contrib};
+    hipLaunchKernelGGL(raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kBlock), 0, s, ra);
+    e = hipGetLastError();
+    *keys_out = keys[cur];
+    *vals_out = vals[cur];
+    return e;
+}
+
+}  // namespace ia

@@ -1,0 +1,215 @@
+"""ctypes binding of libia.so (include/ia.h), argument marshalling only.
+
+The functions here carry the C names (ia_decoder_create, ia_decode, ...)
+and take torch tensors for device buffers; every step of decode and render
+runs in the HIP kernels of libia.so.  There is no CPU fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libia.so")
+
+IA_OK = 0
+IA_ERR_INVALID_ARG = -1
+IA_ERR_UNSUPPORTED = -2
+IA_ERR_WORKSPACE_TOO_SMALL = -3
+IA_ERR_DEVICE = -4
+IA_ERR_OUT_OF_MEMORY = -5
+IA_DTYPE_F32, IA_DTYPE_F16 = 0, 1
+IA_ACT_RELU, IA_ACT_GELU = 0, 1
+
+# Every entry point include/ia.h declares.
+EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
+           "ia_decoder_destroy", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
+           "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render")
+
+
+class IAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ia status {status}: {msg}")
+        self.status = status
+
+
+class HashDesc(C.Structure):
+    _fields_ = [("L", C.c_int32), ("F", C.c_int32), ("log2T", C.c_int32), ("base_res", C.c_double),
+                ("growth", C.c_double), ("temporal_res", C.c_int32), ("table_dtype", C.c_int32),
+                ("t_min", C.c_float), ("t_max", C.c_float)]
+
+
+class MLPDesc(C.Structure):
+    _fields_ = [("in_dim", C.c_int32), ("n_hidden", C.c_int32), ("hidden", C.c_int32 * 4),
+                ("activation", C.c_int32), ("dtype", C.c_int32)]
+
+
+class Gaussians(C.Structure):
+    _fields_ = [("means", C.c_void_p), ("means_stride", C.c_int32), ("scales", C.c_void_p),
+                ("quats", C.c_void_p), ("colors", C.c_void_p), ("sh", C.c_void_p), ("opacity", C.c_void_p),
+                ("sh_degree", C.c_int32)]
+
+
+class HexPlaneDesc(C.Structure):
+    _fields_ = [("res_xyz", C.c_int32), ("res_t", C.c_int32), ("channels", C.c_int32), ("aabb", C.c_float)]
+
+
+class Camera(C.Structure):
+    _fields_ = [("R", C.c_float * 9), ("t", C.c_float * 3), ("fx", C.c_float), ("fy", C.c_float),
+                ("cx", C.c_float), ("cy", C.c_float), ("near_z", C.c_float), ("W", C.c_int32),
+                ("H", C.c_int32), ("bg", C.c_float * 3)]
+
+
+class RenderAux(C.Structure):
+    _fields_ = [("T_final", C.c_void_p), ("n_contrib", C.c_void_p), ("n_entries", C.c_void_p),
+                ("overflow", C.c_void_p), ("sorted_keys", C.c_void_p), ("sorted_vals", C.c_void_p),
+                ("tile_ranges", C.c_void_p), ("proj_a", C.c_void_p), ("proj_b", C.c_void_p),
+                ("proj_c", C.c_void_p), ("depth", C.c_void_p), ("tiles_touched", C.c_void_p),
+                ("tile_rect", C.c_void_p)]
+
+
+_lib = None
+P = C.c_void_p
+
+
+def load(path: str = LIB_PATH):
+    """Load libia.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with implicit_attribute_decode_amd/build.py "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = C.CDLL(path)
+        L.ia_last_error.restype = C.c_char_p
+        L.ia_last_error.argtypes = []
+        L.ia_decoder_create.argtypes = [P, P, P]
+        L.ia_decoder_set_params.argtypes = [P, P, P, P, C.c_int32, P]
+        L.ia_decode.argtypes = [P, P, C.c_int64, C.c_float, P, P]
+        L.ia_decode_xyzt.argtypes = [P, P, C.c_int64, P, P]
+        L.ia_decoder_destroy.argtypes = [P]
+        L.ia_decoder_destroy.restype = None
+        L.ia_hexplane_create.argtypes = [P, P]
+        L.ia_hexplane_set_params.argtypes = [P, P, P, P, C.c_int32, P]
+        L.ia_hexplane_deform.argtypes = [P, P, C.c_int64, C.c_float, P, P]
+        L.ia_hexplane_destroy.argtypes = [P]
+        L.ia_hexplane_destroy.restype = None
+        L.ia_render_workspace_size.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int64, P]
+        L.ia_render.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P]
+        for name in EXPORTS[1:]:
+            if getattr(L, name).restype is C.c_int:
+                getattr(L, name).restype = C.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != IA_OK:
+        raise IAError(status, load().ia_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream=None) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------- decoder
+
+
+def ia_last_error() -> str:
+    return load().ia_last_error().decode()
+
+
+def ia_decoder_create(hash_desc: HashDesc, mlp_desc: MLPDesc) -> C.c_void_p:
+    h = C.c_void_p()
+    _check(load().ia_decoder_create(C.byref(hash_desc), C.byref(mlp_desc), C.byref(h)))
+    return h
+
+
+def ia_decoder_set_params(dec, tables, weights, biases, stream=None):
+    """tables / weights / biases: torch tensors on the device (kept alive by the caller until the copy runs)."""
+    W = (C.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    B = (C.c_void_p * len(biases))(*[_ptr(b) for b in biases])
+    _check(load().ia_decoder_set_params(dec, _ptr(tables), W, B, 1, _stream(stream)))
+
+
+def gaussians(means=None, scales=None, quats=None, colors=None, sh=None, opacity=None, means_stride=0,
+              sh_degree=-1) -> Gaussians:
+    return Gaussians(_ptr(means), means_stride, _ptr(scales), _ptr(quats), _ptr(colors), _ptr(sh), _ptr(opacity),
+                     sh_degree)
+
+
+def ia_decode(dec, xyz, N: int, t: float, out: Gaussians, stream=None):
+    _check(load().ia_decode(dec, _ptr(xyz), int(N), float(t), C.byref(out), _stream(stream)))
+
+
+def ia_decode_xyzt(dec, xyzt, N: int, out: Gaussians, stream=None):
+    _check(load().ia_decode_xyzt(dec, _ptr(xyzt), int(N), C.byref(out), _stream(stream)))
+
+
+def ia_decoder_destroy(dec):
+    load().ia_decoder_destroy(dec)
+
+
+# ----------------------------------------------------------------- HexPlane
+
+
+def ia_hexplane_create(desc: HexPlaneDesc) -> C.c_void_p:
+    h = C.c_void_p()
+    _check(load().ia_hexplane_create(C.byref(desc), C.byref(h)))
+    return h
+
+
+def ia_hexplane_set_params(hp, planes, weights, biases, stream=None):
+    Pl = (C.c_void_p * 6)(*[_ptr(p) for p in planes])
+    W = (C.c_void_p * 3)(*[_ptr(w) for w in weights])
+    B = (C.c_void_p * 3)(*[_ptr(b) for b in biases])
+    _check(load().ia_hexplane_set_params(hp, Pl, W, B, 1, _stream(stream)))
+
+
+def ia_hexplane_deform(hp, canonical: Gaussians, N: int, t: float, out: Gaussians, stream=None):
+    _check(load().ia_hexplane_deform(hp, C.byref(canonical), int(N), float(t), C.byref(out), _stream(stream)))
+
+
+def ia_hexplane_destroy(hp):
+    load().ia_hexplane_destroy(hp)
+
+
+# ----------------------------------------------------------------- render
+
+
+def ia_render_workspace_size(N_total: int, frames: int, W: int, H: int, max_entries: int) -> int:
+    n = C.c_size_t()
+    _check(load().ia_render_workspace_size(int(N_total), int(frames), int(W), int(H), int(max_entries), C.byref(n)))
+    return int(n.value)
+
+
+def camera(cam) -> Camera:
+    """Camera struct from any object with R, t, fx, fy, cx, cy, near, W, H, bg."""
+    c = Camera()
+    c.R[:] = [float(v) for v in np.asarray(cam.R, np.float32).ravel()]
+    c.t[:] = [float(v) for v in np.asarray(cam.t, np.float32).ravel()]
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    c.near_z = float(cam.near)
+    c.W, c.H = int(cam.W), int(cam.H)
+    c.bg[:] = [float(v) for v in np.asarray(cam.bg, np.float32).ravel()]
+    return c
+
+
+def ia_render(g: Gaussians, frame_offsets, cams, ws, max_entries: int, image, aux: RenderAux | None = None,
+              stream=None):
+    fo = np.ascontiguousarray(frame_offsets, np.int64)
+    F = len(cams)
+    arr = (Camera * F)(*[camera(c) for c in cams])
+    _check(load().ia_render(C.byref(g), fo.ctypes.data_as(C.c_void_p), F, arr, _ptr(ws),
+                            int(ws.numel() * ws.element_size()), int(max_entries), _ptr(image),
+                            None if aux is None else C.byref(aux), _stream(stream)))

@@ -1,0 +1,162 @@
+"""Convenience objects over the C ABI: Decoder, HexPlane, Renderer.
+
+Argument marshalling only (torch tensors in, torch tensors out); the work is
+done by libia.so.  Parameter objects are duck-typed like the ones in
+scenes.py (DecoderParams, HexPlaneParams, Camera).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import ia
+
+
+def _dev(a, dtype=None, device="cuda"):
+    t = torch.as_tensor(np.ascontiguousarray(a), device=device)
+    return t if dtype is None else t.to(dtype)
+
+
+class Decoder:
+    """Hash encoder + decoder MLP handle (SPIN-4DGS §3.3)."""
+
+    def __init__(self, params, device="cuda"):
+        h, m = params.hash, params.mlp
+        f16 = bool(m.f16)
+        hd = ia.HashDesc(int(h.L), int(h.F), int(h.log2T), float(h.base_res), float(h.growth), int(h.temporal_res),
+                         ia.IA_DTYPE_F16 if h.table_f16 else ia.IA_DTYPE_F32, float(h.t_min), float(h.t_max))
+        hidden = list(m.dims[1:-1])
+        md = ia.MLPDesc(int(m.dims[0]), len(hidden), (ia.C.c_int32 * 4)(*(hidden + [0] * (4 - len(hidden)))),
+                        ia.IA_ACT_GELU if m.act == "gelu" else ia.IA_ACT_RELU,
+                        ia.IA_DTYPE_F16 if f16 else ia.IA_DTYPE_F32)
+        self.handle = ia.ia_decoder_create(hd, md)
+        self.device = device
+        self._tables = _dev(params.tables, device=device)
+        self._W = [_dev(w, device=device) for w in params.weights]
+        self._b = [_dev(b, torch.float32, device=device) for b in params.biases]
+        ia.ia_decoder_set_params(self.handle, self._tables, self._W, self._b)
+        torch.cuda.current_stream().synchronize()
+
+    def _out(self, N, out):
+        if out is None:
+            out = dict(scales=torch.empty((N, 3), device=self.device), quats=torch.empty((N, 4), device=self.device),
+                       colors=torch.empty((N, 3), device=self.device), opacity=torch.empty((N,), device=self.device))
+        return out
+
+    def decode(self, xyz: torch.Tensor, t: float, out: dict | None = None) -> dict:
+        N = int(xyz.shape[0])
+        out = self._out(N, out)
+        g = ia.gaussians(scales=out["scales"], quats=out["quats"], colors=out["colors"], opacity=out["opacity"])
+        ia.ia_decode(self.handle, xyz, N, t, g)
+        return out
+
+    def decode_xyzt(self, xyzt: torch.Tensor, out: dict | None = None) -> dict:
+        N = int(xyzt.shape[0])
+        out = self._out(N, out)
+        g = ia.gaussians(scales=out["scales"], quats=out["quats"], colors=out["colors"], opacity=out["opacity"])
+        ia.ia_decode_xyzt(self.handle, xyzt, N, g)
+        return out
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            ia.ia_decoder_destroy(h)
+            self.handle = None
+
+
+class HexPlane:
+    """HexPlane deformation handle ("4D Gaussian Splatting详解", §3.1-3.2)."""
+
+    def __init__(self, params, device="cuda"):
+        self.handle = ia.ia_hexplane_create(ia.HexPlaneDesc(int(params.res_xyz), int(params.res_t),
+                                                            int(params.channels), float(params.aabb)))
+        self.device = device
+        self._planes = [_dev(p, device=device) for p in params.planes]
+        self._W = [_dev(w, device=device) for w in params.weights]
+        self._b = [_dev(b, torch.float32, device=device) for b in params.biases]
+        ia.ia_hexplane_set_params(self.handle, self._planes, self._W, self._b)
+        torch.cuda.current_stream().synchronize()
+
+    def deform(self, canon: dict, t: float, out: dict | None = None) -> dict:
+        N = int(canon["means"].shape[0])
+        if out is None:
+            out = {k: torch.empty_like(canon[k]) for k in ("means", "scales", "quats", "sh", "opacity")}
+        cg = ia.gaussians(means=canon["means"], scales=canon["scales"], quats=canon["quats"], sh=canon["sh"],
+                          opacity=canon["opacity"], sh_degree=3)
+        og = ia.gaussians(means=out["means"], scales=out["scales"], quats=out["quats"], sh=out["sh"],
+                          opacity=out["opacity"], sh_degree=3)
+        ia.ia_hexplane_deform(self.handle, cg, N, t, og)
+        return out
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            ia.ia_hexplane_destroy(h)
+            self.handle = None
+
+
+_VIEW_TYPES = {
+    "sorted_keys": (torch.int64, 1), "sorted_vals": (torch.int32, 1), "tile_ranges": (torch.int32, 2),
+    "proj_a": (torch.float32, 4), "proj_b": (torch.float32, 4), "proj_c": (torch.float32, 1),
+    "depth": (torch.float32, 1), "tiles_touched": (torch.int32, 1), "tile_rect": (torch.int16, 4),
+}
+
+
+class Renderer:
+    """Owns a render workspace (a torch uint8 tensor) and calls ia_render."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.ws = None
+
+    def workspace(self, N, frames, W, H, max_entries):
+        need = ia.ia_render_workspace_size(N, frames, W, H, max_entries)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = None
+            self.ws = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.ws.data_ptr()) % 256
+        return self.ws[off:off + need]
+
+    def render(self, g: dict, frame_offsets, cams, max_entries: int, aux: bool = False, out: dict | None = None):
+        """g: means [N,k>=3], scales, quats, colors | sh, opacity (cuda tensors).
+        Returns image [F,3,H,W] and, with aux, T_final, n_contrib, n_entries,
+        overflow and workspace views (sorted keys/vals, ranges, projections)."""
+        fo = np.asarray(frame_offsets, np.int64)
+        F, W, H = len(cams), int(cams[0].W), int(cams[0].H)
+        N = int(fo[-1])
+        ws = self.workspace(N, F, W, H, max_entries)
+        out = out or {}
+        image = out.get("image")
+        if image is None:
+            image = torch.empty((F, 3, H, W), device=self.device)
+        means = g["means"]
+        stride = int(means.stride(0)) if means.dim() == 2 else 3
+        sh = g.get("sh")
+        G = ia.gaussians(means=means, scales=g["scales"], quats=g["quats"], colors=g.get("colors"), sh=sh,
+                         opacity=g["opacity"], means_stride=stride, sh_degree=3 if sh is not None else -1)
+        res = {"image": image}
+        A = None
+        if aux:
+            res["T_final"] = torch.empty((F, H, W), device=self.device)
+            res["n_contrib"] = torch.empty((F, H, W), dtype=torch.int32, device=self.device)
+            res["n_entries"] = torch.zeros(1, dtype=torch.int64, device=self.device)
+            res["overflow"] = torch.zeros(1, dtype=torch.int32, device=self.device)
+            A = ia.RenderAux(ia._ptr(res["T_final"]), ia._ptr(res["n_contrib"]), ia._ptr(res["n_entries"]),
+                             ia._ptr(res["overflow"]))
+        ia.ia_render(G, fo, cams, ws, max_entries, image, A)
+        if aux:
+            base = ws.data_ptr()
+            for name, (dt, width) in _VIEW_TYPES.items():
+                p = getattr(A, name)
+                res["_view_" + name] = (int(p) - base, dt, width)
+            res["_ws"] = ws
+        return res
+
+    @staticmethod
+    def view(res: dict, name: str, count: int) -> torch.Tensor:
+        """A workspace view of `count` rows (e.g. sorted_keys of n_entries rows)."""
+        off, dt, width = res["_view_" + name]
+        ws = res["_ws"]
+        nbytes = count * width * torch.empty((), dtype=dt).element_size()
+        t = ws[off:off + nbytes].view(dt)
+        return t.view(count, width) if width > 1 else t

@@ -1,0 +1,243 @@
+/*
+ * ia.h - C ABI of libia.so: implicit attribute decode + tile rasterisation of
+ * 4D Gaussian splats on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow two pages:
+ *   [SPIN] "Implicit 4D Gaussian Splatting for Fast Motion with Large
+ *          Inter-Frame Displacements" (SPIN-4DGS): §3.1 Eq. 1-4 (Gaussians,
+ *          covariance, EWA projection, alpha compositing), §3.3 Eq. 7-11
+ *          (normalisation, 4D hash encoder, multibranch decoder, activations).
+ *   [HEX]  "4D Gaussian Splatting详解：动态场景实时渲染的范式突破":
+ *          §3.1 (HexPlane six-plane encoder), §3.2 (deformation MLP), §6.1
+ *          (opacity is not deformed).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers point to memory the caller allocated on the current
+ *     HIP device (e.g. torch tensors); host pointers are marked "host".
+ *   - All floating-point buffers are fp32 unless stated; every [N,k] buffer is
+ *     row-major and densely packed.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *     it and the call returns without waiting, except where stated.
+ *   - Return value: IA_OK (0) or a negative ia_status.  Argument and size
+ *     errors are detected before anything is enqueued; the message is
+ *     available from ia_last_error() on the calling thread.  No C++
+ *     exception crosses this boundary.
+ *   - Handles are immutable after their set_params call; concurrent calls that
+ *     only read a handle (decode, deform) on different streams are safe.
+ *     Calls that share a render workspace must not overlap.
+ */
+#ifndef IA_H_
+#define IA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IA_API __attribute__((visibility("default")))
+
+typedef int32_t ia_status;
+#define IA_OK 0
+#define IA_ERR_INVALID_ARG (-1)        /* null/misaligned pointer, bad size, bad descriptor */
+#define IA_ERR_UNSUPPORTED (-2)        /* valid but not implemented shape/dtype combination */
+#define IA_ERR_WORKSPACE_TOO_SMALL (-3)
+#define IA_ERR_DEVICE (-4)             /* a HIP call or kernel launch failed */
+#define IA_ERR_OUT_OF_MEMORY (-5)
+
+#define IA_DTYPE_F32 0
+#define IA_DTYPE_F16 1
+
+#define IA_ACT_RELU 0
+#define IA_ACT_GELU 1 /* exact: 0.5 x (1 + erf(x / sqrt 2)) */
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+IA_API const char* ia_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Gaussian attribute buffers (structure of arrays, all device, fp32)        */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    float* means;          /* [N, means_stride]: x, y, z (+ anything after)  */
+    int32_t means_stride;  /* floats between consecutive means; 0 means 3    */
+    float* scales;         /* [N,3] linear scales                            */
+    float* quats;          /* [N,4] rotation (w, x, y, z), any non-zero norm */
+    float* colors;         /* [N,3] RGB in [0,1] (sh_degree < 0)             */
+    float* sh;             /* [N,16,3] SH coefficients, coefficient-major    */
+    float* opacity;        /* [N]                                            */
+    int32_t sh_degree;     /* -1: use colors; 3: evaluate sh (render only)   */
+} ia_gaussians;
+
+/* ------------------------------------------------------------------------ */
+/* Decoder: [SPIN] §3.3 Eq. 7-11                                             */
+/* ------------------------------------------------------------------------ */
+
+/* 4D multiresolution hash encoder ([SPIN] §3.3 Eq. 9).  Level l has
+ * floor(base_res * growth^l) vertices per spatial axis and temporal_res
+ * vertices on t (0 = same as spatial).  A level is stored densely when
+ * res^3 * res_t <= 2^log2T, otherwise it is hashed with
+ * (ix*1 ^ iy*2654435761 ^ iz*805459861 ^ it*3674653429) mod 2^log2T. */
+typedef struct {
+    int32_t L;            /* levels: 4 or 16 (in_dim = 2 L)                 */
+    int32_t F;            /* features per level: 2                          */
+    int32_t log2T;        /* table entries per level = 2^log2T, 4..24       */
+    double base_res;      /* vertices per axis at level 0, >= 2             */
+    double growth;        /* per-level growth factor, >= 1                  */
+    int32_t temporal_res; /* vertices on the t axis, 0 = spatial res        */
+    int32_t table_dtype;  /* IA_DTYPE_F32 or IA_DTYPE_F16                   */
+    float t_min, t_max;   /* time normalisation of Eq. 8, t_max > t_min     */
+} ia_hash_desc;
+
+/* Decoder MLP ([SPIN] §3.3 Eq. 10): a shared trunk of n_hidden layers
+ * act(W x + b) followed by one linear head block of 11 outputs in the order
+ * scale(3) | rotation(4: w,x,y,z) | colour(3) | opacity(1).  Supported:
+ *   dtype F32: (in_dim, hidden) = (8, {32}), (32, {64}) or (32, {64, 64})
+ *   dtype F16: in_dim = 32, n_hidden = 2, hidden = {64, 64}, fp16 MFMA with
+ *              fp32 accumulation; hidden activations rounded to fp16. */
+typedef struct {
+    int32_t in_dim;
+    int32_t n_hidden;
+    int32_t hidden[4];
+    int32_t activation; /* IA_ACT_RELU or IA_ACT_GELU */
+    int32_t dtype;      /* IA_DTYPE_F32 or IA_DTYPE_F16 (weights and math) */
+} ia_mlp_desc;
+
+typedef struct ia_decoder ia_decoder;
+
+/* Validate the descriptors and create an empty handle (no device memory yet).
+ * Errors: INVALID_ARG (null pointers, out-of-range fields), UNSUPPORTED. */
+IA_API ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* mlp, ia_decoder** out);
+
+/* Copy the parameters into device memory owned by the handle.
+ *   tables : [L][2^log2T][F] of table_dtype
+ *   weights: n_hidden + 1 pointers, layer k row-major [out][in] of mlp dtype
+ *            (the last one is the [11][hidden] head block)
+ *   biases : n_hidden + 1 pointers to fp32 [out]
+ * params_on_device: 1 if all the above are device pointers, 0 if host.
+ * The copies are enqueued on `stream`; host sources may be freed on return
+ * (host copies are synchronous).  May be called again to replace parameters.
+ * Errors: INVALID_ARG, OUT_OF_MEMORY, DEVICE. */
+IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
+                                const float* const* biases, int32_t params_on_device, void* stream);
+
+/* Decode N Gaussians at one time t ([SPIN] §3.3 Eq. 7-11):
+ *   xyz : device [N,3] positions mu
+ *   out : device scales[N,3] = exp(min(s_hat,20)), quats[N,4] = r_hat/|r_hat|,
+ *         colors[N,3] = sigmoid(c_hat), opacity[N] = sigmoid(o_hat);
+ *         out->means is not written (the input positions are the means).
+ * N = 0 is a no-op.  Errors: INVALID_ARG (null, N < 0, params not set). */
+IA_API ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t, const ia_gaussians* out,
+                    void* stream);
+
+/* As ia_decode with a per-Gaussian time: xyzt is device [N,4] (x, y, z, t).
+ * One launch decodes any mix of frames (spatiotemporal slicing: every frame
+ * is its own set of positions, [SPIN] §3.2). */
+IA_API ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
+                         void* stream);
+
+IA_API void ia_decoder_destroy(ia_decoder* dec);
+
+/* ------------------------------------------------------------------------ */
+/* HexPlane deformation: [HEX] §3.1-3.2, §6.1                                */
+/* ------------------------------------------------------------------------ */
+
+/* Six planes XY, XZ, YZ ([res_xyz][res_xyz][C]) and XT, YT, ZT
+ * ([res_t][res_xyz][C], time on the slow axis), fp16, bilinear with vertices
+ * at 0..res-1, positions mapped to [0,1] by the box [-aabb, aabb]^3 (clamped),
+ * concatenated to 6C features -> MLP 6C -> 256 -> 256 -> 58 (ReLU hidden,
+ * fp16 MFMA, fp32 accumulate).  Supported: C = 32, res_xyz, res_t in 2..4096. */
+typedef struct {
+    int32_t res_xyz;
+    int32_t res_t;
+    int32_t channels;
+    float aabb;
+} ia_hexplane_desc;
+
+typedef struct ia_hexplane ia_hexplane;
+
+IA_API ia_status ia_hexplane_create(const ia_hexplane_desc* desc, ia_hexplane** out);
+
+/* planes: 6 pointers (order XY XZ YZ XT YT ZT) to fp16 [res_b][res_a][C];
+ * weights: 3 pointers to fp16 [256][6C], [256][256], [58][256];
+ * biases: 3 pointers to fp32.  Same ownership rules as ia_decoder_set_params. */
+IA_API ia_status ia_hexplane_set_params(ia_hexplane* hp, const void* const* planes, const void* const* weights,
+                                 const float* const* biases, int32_t params_on_device, void* stream);
+
+/* Deform N canonical Gaussians to time t in [0,1]:
+ *   means' = means + dpos;  quats' = normalize(quats + dquat);
+ *   scales' = scales * exp(dlog_scale);  sh' = sh + dsh;  opacity' = opacity.
+ * canonical: means[N,3], scales, quats, sh[N,16,3], opacity (device);
+ * out: the same fields (device, may not alias canonical).  means_stride must be
+ * 0 or 3.  Errors: INVALID_ARG, params not set. */
+IA_API ia_status ia_hexplane_deform(const ia_hexplane* hp, const ia_gaussians* canonical, int64_t N, float t,
+                             const ia_gaussians* out, void* stream);
+
+IA_API void ia_hexplane_destroy(ia_hexplane* hp);
+
+/* ------------------------------------------------------------------------ */
+/* Render: [SPIN] §3.1 Eq. 1-4, 16x16 tiles                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Pinhole camera, OpenCV axes (x right, y down, z forward).
+ * p_cam = R p_world + t; u = fx x/z + cx; v = fy y/z + cy; pixel (i, j) has
+ * its centre at (i + 0.5, j + 0.5).  Gaussians with z <= near_z are culled. */
+typedef struct {
+    float R[9]; /* row-major world->camera rotation */
+    float t[3];
+    float fx, fy, cx, cy, near_z;
+    int32_t W, H;
+    float bg[3]; /* background colour added as T_final * bg */
+} ia_camera;
+
+/* Optional outputs of ia_render.  Device pointers may be NULL.  The view
+ * fields are filled by ia_render (host-side) and point into the workspace;
+ * they stay valid until the workspace is reused. */
+typedef struct {
+    float* T_final;      /* device [F,H,W] final transmittance, or NULL          */
+    uint32_t* n_contrib; /* device [F,H,W] 1 + list position of the last
+                            composited Gaussian (0 = none), or NULL               */
+    uint64_t* n_entries; /* device [1] tile entries emitted (true count), or NULL */
+    uint32_t* overflow;  /* device [1] 1 if n_entries > max_entries, or NULL       */
+    /* views (written by ia_render) */
+    const uint64_t* sorted_keys;  /* [min(E,max_entries)] (tile<<32 | depth bits) */
+    const uint32_t* sorted_vals;  /* [min(E,max_entries)] Gaussian index          */
+    const uint32_t* tile_ranges;  /* [F*tiles][2] [start,end), empty = [0,0)      */
+    const float* proj_a;          /* [N][4] u, v, conic A, conic B                */
+    const float* proj_b;          /* [N][4] conic C, opacity, red, green          */
+    const float* proj_c;          /* [N] blue                                     */
+    const float* depth;           /* [N] camera-space z                           */
+    const uint32_t* tiles_touched;/* [N] 0 = culled                               */
+    const uint16_t* tile_rect;    /* [N][4] tx0, ty0, tx1, ty1 (inclusive)        */
+} ia_render_aux;
+
+/* Bytes of workspace ia_render needs for N_total Gaussians over `frames`
+ * frames of W x H with room for max_entries tile entries.
+ * Errors: INVALID_ARG (negative or zero sizes, max_entries >= 2^32). */
+IA_API ia_status ia_render_workspace_size(int64_t N_total, int32_t frames, int32_t W, int32_t H,
+                                   int64_t max_entries, size_t* bytes);
+
+/* Render a batch of frames.  Gaussians [frame_offsets[f], frame_offsets[f+1])
+ * of g belong to frame f and are seen by cams[f]; all cameras share W x H.
+ *   frame_offsets: host [frames+1], frame_offsets[0] = 0, non-decreasing.
+ *   cams: host [frames].  Both host arrays may be freed on return.
+ *   ws: device workspace of ws_bytes >= ia_render_workspace_size(...).
+ *   image: device [frames,3,H,W] = C + T_final * bg.
+ * Steps: EWA projection -> tiles touched -> prefix sum -> one key per
+ * (Gaussian, tile) = (frame*tiles + tile) << 32 | depth bits -> stable LSD
+ * radix sort -> per-tile ranges -> front-to-back compositing per pixel with
+ * a 3-sigma cutoff, alpha = min(0.99, o G), skip alpha < 1/255, stop once
+ * T < 1e-4.  No host synchronisation: if more than max_entries entries are
+ * needed, the surplus is dropped, aux->overflow is set to 1 and
+ * aux->n_entries holds the needed count; the image is then incomplete and
+ * the caller retries with a larger max_entries.
+ * Errors: INVALID_ARG, UNSUPPORTED (sh_degree not -1/3),
+ * WORKSPACE_TOO_SMALL, DEVICE. */
+IA_API ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames, const ia_camera* cams,
+                    void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IA_H_ */

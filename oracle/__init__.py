@@ -61,6 +61,8 @@ P = C.c_void_p
 
 
 def _declare(L):
+    L.orc_num_threads.restype = C.c_int
+    L.orc_num_threads.argtypes = []
     L.orc_half_to_double.restype = C.c_double
     L.orc_half_to_double.argtypes = [C.c_uint16]
     L.orc_double_to_half.restype = C.c_uint16
@@ -82,6 +84,10 @@ def _declare(L):
     L.orc_raster_tiles.argtypes = [C.c_int, P, P, P, P, P, P, P, P, P, P, P]
     L.orc_raster_brute.argtypes = [P, C.c_long, C.c_long, P, P, P, P, P, P, P, C.c_int, P, C.c_long,
                                    P, P, P, P]
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
 
 
 def _p(a: np.ndarray):

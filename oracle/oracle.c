@@ -31,6 +31,19 @@
 
 #define EXPORT __attribute__((visibility("default")))
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops of this file use (1 without OpenMP). */
+EXPORT int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* IEEE binary16 <-> double, from the format definition                      */
 /* ------------------------------------------------------------------------ */

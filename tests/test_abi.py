@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: libia.so loads, exports every entry point
+include/ia.h declares, and rejects invalid arguments on the host before any
+HIP call is made."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from implicit_attribute_decode_amd import ia
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "ia.h")).read()
+    return sorted(set(re.findall(r"^IA_API\s+[\w\s\*]*?\b(ia_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(ia.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ia.load()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _hash(**kw):
+    d = dict(L=16, F=2, log2T=19, base_res=16.0, growth=1.5, temporal_res=150, table_dtype=ia.IA_DTYPE_F16,
+             t_min=0.0, t_max=1.0)
+    d.update(kw)
+    return ia.HashDesc(**d)
+
+
+def _mlp(**kw):
+    d = dict(in_dim=32, n_hidden=2, hidden=(C.c_int32 * 4)(64, 64, 0, 0), activation=ia.IA_ACT_GELU,
+             dtype=ia.IA_DTYPE_F16)
+    d.update(kw)
+    return ia.MLPDesc(**d)
+
+
+def test_decoder_create_accepts_the_supported_shapes():
+    h = ia.ia_decoder_create(_hash(), _mlp())
+    ia.ia_decoder_destroy(h)
+    tiny = ia.HashDesc(4, 2, 12, 8.0, 2.0, 0, ia.IA_DTYPE_F32, 0.0, 1.0)
+    h = ia.ia_decoder_create(tiny, ia.MLPDesc(8, 1, (C.c_int32 * 4)(32, 0, 0, 0), ia.IA_ACT_RELU, ia.IA_DTYPE_F32))
+    ia.ia_decoder_destroy(h)
+
+
+@pytest.mark.parametrize("hkw,mkw,status", [
+    (dict(L=0), {}, ia.IA_ERR_INVALID_ARG),
+    (dict(F=4), {}, ia.IA_ERR_UNSUPPORTED),
+    (dict(log2T=30), {}, ia.IA_ERR_INVALID_ARG),
+    (dict(base_res=1.0), {}, ia.IA_ERR_INVALID_ARG),
+    (dict(t_max=0.0), {}, ia.IA_ERR_INVALID_ARG),
+    (dict(temporal_res=1), {}, ia.IA_ERR_INVALID_ARG),
+    ({}, dict(in_dim=31), ia.IA_ERR_INVALID_ARG),
+    ({}, dict(n_hidden=3), ia.IA_ERR_UNSUPPORTED),
+    ({}, dict(activation=7), ia.IA_ERR_INVALID_ARG),
+    ({}, dict(hidden=(C.c_int32 * 4)(128, 64, 0, 0)), ia.IA_ERR_UNSUPPORTED),
+    (dict(table_dtype=ia.IA_DTYPE_F32), {}, ia.IA_ERR_UNSUPPORTED),
+])
+def test_decoder_create_rejects(hkw, mkw, status):
+    with pytest.raises(ia.IAError) as e:
+        ia.ia_decoder_create(_hash(**hkw), _mlp(**mkw))
+    assert e.value.status == status
+    assert ia.ia_last_error() != ""
+
+
+def test_decode_without_params_is_rejected_before_any_gpu_work():
+    L = ia.load()
+    h = ia.ia_decoder_create(_hash(), _mlp())
+    g = ia.Gaussians()
+    assert L.ia_decode(h, None, 10, C.c_float(0.5), C.byref(g), None) == ia.IA_ERR_INVALID_ARG
+    assert "not set" in ia.ia_last_error()
+    ia.ia_decoder_destroy(h)
+    assert L.ia_decode(None, None, 10, C.c_float(0.5), C.byref(g), None) == ia.IA_ERR_INVALID_ARG
+
+
+def test_workspace_size_validation_and_growth():
+    n = ia.ia_render_workspace_size(200_000, 1, 640, 360, 1_000_000)
+    assert n > 24 * 1_000_000
+    assert ia.ia_render_workspace_size(200_000, 1, 640, 360, 2_000_000) > n
+    assert ia.ia_render_workspace_size(0, 1, 64, 64, 1) > 0
+    for args in [(-1, 1, 64, 64, 10), (10, 0, 64, 64, 10), (10, 1, 0, 64, 10), (10, 1, 64, 64, 0),
+                 (10, 1, 64, 64, 1 << 32)]:
+        with pytest.raises(ia.IAError) as e:
+            ia.ia_render_workspace_size(*args)
+        assert e.value.status == ia.IA_ERR_INVALID_ARG
+
+
+def test_render_argument_errors_are_synchronous():
+    L = ia.load()
+    cam = ia.Camera()
+    cam.W, cam.H, cam.fx, cam.fy = 64, 64, 60.0, 60.0
+    fo = (C.c_int64 * 2)(0, 0)
+    g = ia.Gaussians()
+    # null image
+    assert L.ia_render(C.byref(g), fo, 1, C.byref(cam), None, 0, 10, None, None, None) == ia.IA_ERR_INVALID_ARG
+    # non-monotone frame offsets
+    fo2 = (C.c_int64 * 3)(0, 5, 3)
+    cams = (ia.Camera * 2)(cam, cam)
+    img = C.c_void_p(256)
+    assert L.ia_render(C.byref(g), fo2, 2, cams, img, 1 << 20, 10, img, None, None) == ia.IA_ERR_INVALID_ARG
+    # mismatched camera sizes
+    cam2 = ia.Camera()
+    cam2.W, cam2.H = 32, 64
+    cams = (ia.Camera * 2)(cam, cam2)
+    fo3 = (C.c_int64 * 3)(0, 0, 0)
+    assert L.ia_render(C.byref(g), fo3, 2, cams, img, 1 << 20, 10, img, None, None) == ia.IA_ERR_INVALID_ARG
+    # workspace too small (fake aligned address: nothing is dereferenced)
+    assert L.ia_render(C.byref(g), fo, 1, C.byref(cam), img, 16, 10, img, None, None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
+    # unsupported SH degree with Gaussians present
+    fo4 = (C.c_int64 * 2)(0, 4)
+    g2 = ia.Gaussians(1024, 0, 1024, 1024, 1024, 1024, 1024, 2)
+    assert L.ia_render(C.byref(g2), fo4, 1, C.byref(cam), img, 1 << 30, 10, img, None, None) == ia.IA_ERR_UNSUPPORTED
