@@ -34,9 +34,15 @@ def _gpu_decode(dec, pos, t=None):
 
 
 def _check_f32(g, o):
-    for k in KEYS:
+    """1e-5 relative to each attribute's magnitude: per element for scales,
+    colours and opacity; the vector norm for the unit quaternion, whose
+    components all carry rounding errors of the size of its norm."""
+    for k in ("scales", "colors", "opacity"):
         ok = rel_ok(g[k], o[k], 1e-5, 1e-7)
         assert ok.all(), (k, int((~ok).sum()), np.abs(g[k] - o[k]).max())
+    qn = np.linalg.norm(o["quats"], axis=1, keepdims=True)
+    ok = np.abs(g["quats"] - o["quats"]) <= 1e-5 * qn + 1e-7
+    assert ok.all(), ("quats", int((~ok).sum()), np.abs(g["quats"] - o["quats"]).max())
 
 
 def _check_f16(g, o, emu, tag):
