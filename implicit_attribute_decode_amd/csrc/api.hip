@@ -57,6 +57,7 @@ struct ia_decoder {
     void* tables = nullptr;
     void* W[4] = {nullptr, nullptr, nullptr, nullptr};
     float* b[4] = {nullptr, nullptr, nullptr, nullptr};
+    uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [L][ia::kDecodeChunk]
     bool ready = false;
 };
 
@@ -71,6 +72,8 @@ void free_decoder_params(ia_decoder* d) {
         d->b[k] = nullptr;
     }
     d->tables = nullptr;
+    if (d->zbuf) (void)hipFree(d->zbuf);
+    d->zbuf = nullptr;
     d->ready = false;
 }
 
@@ -155,6 +158,8 @@ ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, flo
     a.quats = out->quats;
     a.colors = out->colors;
     a.opacity = out->opacity;
+    a.zbuf = dec->zbuf;
+    a.zcap = ia::kDecodeChunk;
     hipError_t e = ia::launch_decode(a, dec->mlp.dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return IA_OK;
@@ -206,6 +211,11 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
         const size_t nw = (size_t)dec->dims[k + 1] * dec->dims[k];
         st = upload_param(&dec->W[k], weights[k], nw * wsize, dev, s);
         if (st == IA_OK) st = upload_param(reinterpret_cast<void**>(&dec->b[k]), biases[k], 4 * (size_t)dec->dims[k + 1], dev, s);
+    }
+    if (st == IA_OK && dec->mlp.dtype == IA_DTYPE_F16) {
+        // [L][chunk] packed feature pairs, then [chunk] normalised positions (float4)
+        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 4 + 16) * ia::kDecodeChunk);
+        if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
     }
     if (st != IA_OK) {
         free_decoder_params(dec);

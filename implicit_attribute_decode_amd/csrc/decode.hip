@@ -6,15 +6,15 @@
 //               -> shared MLP trunk + linear head block (Eq. 10)
 //               -> exp / normalise / sigmoid activations (Eq. 11).
 //
-// Two kernels:
-//   decode_f32_kernel  : fp32 VALU, one thread per Gaussian, weights in LDS.
-//   decode_mfma_kernel : 16 levels x 2 features, 32->64->64->11, fp16 MFMA
-//                        (v_mfma_f32_16x16x16_f16) with fp32 accumulation.
-//                        A wave decodes 64 Gaussians; Gaussians are the MFMA
-//                        columns and neurons the rows, so a layer's output
-//                        registers are already the next layer's B operand and
-//                        the hash gather writes its features straight into
-//                        the first layer's B operand (no LDS round trip).
+// Paths:
+//   decode_f32_kernel : fp32 VALU, one thread per Gaussian, weights in LDS
+//                       (small tables: the 4-level fp32 grid).
+//   fp16 path         : 16 levels x 2 features, 32->64->64->11 decoder.  A
+//                       level-major gather kernel (one level's table resident
+//                       in L2 at a time) writes the features to a scratch
+//                       buffer owned by the decoder handle; an MLP kernel runs
+//                       the decoder on v_mfma_f32_16x16x16_f16 with fp32
+//                       accumulation and applies Eq. 11.
 //
 // Position normalisation and the per-axis cell decision are computed one IEEE
 // fp32 operation at a time in the order written (the library is built with
@@ -134,6 +134,23 @@ __device__ __forceinline__ float act_fn(int act, float x) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// GELU for the fp16 path, whose hidden activations are rounded to fp16
+// (relative step 2^-11) right after: erf from Abramowitz & Stegun, Handbook
+// of Mathematical Functions, formula 7.1.26, |error| <= 1.5e-7:
+//   erf(u) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2),
+//   t = 1 / (1 + p u), u >= 0, erf odd.
+__device__ __forceinline__ float gelu_fp16path(float x) {
+    const float u = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    const float e = __expf(-(u * u));
+    const float erf_u = fmaf(-(poly * t), e, 1.0f);
+    return 0.5f * x * (1.0f + copysignf(erf_u, x));
+}
+
 // ---------------------------------------------------------------- fp32 path
 
 constexpr int kF32MaxIn = 32, kF32MaxH = 64;
@@ -222,19 +239,123 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- fp16 MFMA path
+// ---------------------------------------------------------------- fp16 path
 //
-// Register layout of v_mfma_f32_16x16x16_f16 (wave64, lane l, q = l/16,
-// c = l%16): A supplies row c, k-slots 4q..4q+3; B supplies column c, the
-// same k-slots; D holds rows 4q..4q+3 of column c.  Because A and B use the
-// same k-slots, any assignment of features to slots works as long as both
-// operands agree; we give slot (q, e) of k-block kb feature 16 kb + 4 q + e.
+// Two kernels per chunk of at most zcap Gaussians:
+//
+// normalize_kernel: Eq. 7-8 once per Gaussian -> x~ (fp32 x4) in the scratch.
+//
+// gather_f16_kernel: level-major.  Block b handles level b / nchunk and
+// Gaussians [1024 (b % nchunk), +1024).  Blocks are dispatched in index order
+// and spread round-robin over the XCDs, so at any moment all XCDs work on the
+// same level and that level's 2^log2T x 4-byte table stays resident in every
+// XCD's L2 instead of being fetched line by line from HBM / Infinity Cache.
+// Four lanes share one (Gaussian, level): lane s takes the x-corner s & 1 and
+// the y-corner s >> 1 and loops over the four (z, t) corners.  Under the hash
+// (first prime 1) the two x-corners differ only in their low index bits, so
+// neighbouring lanes usually hit the same cache line inside one load
+// instruction, halving the distinct lines each gather touches.  Two quad
+// shuffles sum the four partial results.  Output z[level][i] = two fp16
+// features packed in 32 bits (RNE).
+//
+// mlp_f16_kernel: the 32 -> 64 -> 64 -> 11 decoder on v_mfma_f32_16x16x16_f16.
+// Register layout (wave64, lane l, q = l/16, c = l%16): A supplies row c,
+// k-slots 4q..4q+3; B supplies column c, the same k-slots; D holds rows
+// 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows, so a
+// layer's D registers are the next layer's B operand; slot (q, e) of k-block
+// kb is feature 16 kb + 4 q + e, i.e. levels 8 kb + 2 q (e = 0, 1) and
+// 8 kb + 2 q + 1 (e = 2, 3).
+
+constexpr int kGatherPerBlock = 1024;  // Gaussians per gather block (64 per pass x 16 passes)
+
+__global__ void __launch_bounds__(256) normalize_kernel(DecodeArgs a, const float* pos, int64_t n, float4* xt) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float* p = pos + i * a.stride;
+    float v[4];
+    normalize_pos(p[0], p[1], p[2], a.stride == 4 ? p[3] : a.t_scalar, a.h.t_min, a.h.t_max, v);
+    xt[i] = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__global__ void __launch_bounds__(256) gather_f16_kernel(const float4* xt, int64_t n, int nchunk, HashLevels h,
+                                                         const uint32_t* tables, uint32_t* zbuf, int64_t zstride) {
+#pragma clang fp contract(fast)
+    const int level = blockIdx.x / nchunk;
+    const int64_t first = (int64_t)(blockIdx.x % nchunk) * kGatherPerBlock;
+    const int res = h.res_s[level], res_t = h.res_t[level];
+    const bool dense = h.dense[level] != 0;
+    const uint32_t* tab = tables + (size_t)level * h.T;
+    uint32_t* zl = zbuf + (size_t)level * zstride;
+    const int s = threadIdx.x & 3;           // corner pair this lane takes
+    const int bx = s & 1, by = s >> 1;
+    const int sub = threadIdx.x >> 2;        // Gaussian slot within a pass (0..63)
+    const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
+#pragma unroll 4
+    for (int j = 0; j < kGatherPerBlock / 64; ++j) {
+        const int64_t i = first + j * 64 + sub;
+        if (i >= n) break;  // uniform across each group of four lanes
+        const float4 p = xt[i];
+        int cx, cy, cz, ct;
+        float fx, fy, fz, ft;
+        cell_axis(p.x, res, cx, fx);
+        cell_axis(p.y, res, cy, fy);
+        cell_axis(p.z, res, cz, fz);
+        cell_axis(p.w, res_t, ct, ft);
+        const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
+        uint32_t txy, tz0, tz1, tt0, tt1;
+        if (dense) {
+            txy = ux + uy * r;
+            tz0 = (uint32_t)cz * r2;
+            tz1 = tz0 + r2;
+            tt0 = (uint32_t)ct * r3;
+            tt1 = tt0 + r3;
+        } else {
+            txy = (ux * kP1) ^ (uy * kP2);
+            tz0 = (uint32_t)cz * kP3;
+            tz1 = (uint32_t)(cz + 1) * kP3;
+            tt0 = (uint32_t)ct * kP4;
+            tt1 = (uint32_t)(ct + 1) * kP4;
+        }
+        const float wxy = (bx ? fx : 1.0f - fx) * (by ? fy : 1.0f - fy);
+        const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
+        const uint32_t tz[2] = {tz0, tz1}, tt[2] = {tt0, tt1};
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int bz = c & 1, bt = c >> 1;
+            const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
+            const float w = (wxy * wz[bz]) * wt[bt];
+            const uint32_t raw = tab[idx];
+            a0 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
+            a1 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+        }
+        a0 += __shfl_xor(a0, 1, 4);
+        a1 += __shfl_xor(a1, 1, 4);
+        a0 += __shfl_xor(a0, 2, 4);
+        a1 += __shfl_xor(a1, 2, 4);
+        if (s == 0) {
+            const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);
+            const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
+            zl[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        }
+    }
+}
 
 __device__ __forceinline__ half4_t load_h4(const _Float16* p) {
     return *reinterpret_cast<const half4_t*>(p);
 }
 
-__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ half4_t unpack2(uint32_t a, uint32_t b) {
+    half4_t r;
+    r[0] = __builtin_bit_cast(_Float16, (uint16_t)(a & 0xffffu));
+    r[1] = __builtin_bit_cast(_Float16, (uint16_t)(a >> 16));
+    r[2] = __builtin_bit_cast(_Float16, (uint16_t)(b & 0xffffu));
+    r[3] = __builtin_bit_cast(_Float16, (uint16_t)(b >> 16));
+    return r;
+}
+
+__global__ void __launch_bounds__(256, 2) mlp_f16_kernel(DecodeArgs a, const uint32_t* zbuf, int64_t zstride,
+                                                         int64_t n, int64_t out_off) {
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, c = lane & 15;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -263,61 +384,29 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) B3[e] = (4 * q + e) < 11 ? a.b[2][4 * q + e] : 0.0f;
 
-    // Levels handled by this lane: 8 kb + 2 q + lv.  Their parameters are
-    // picked with unrolled selects (uniform kernel-argument reads) instead of
-    // a lane-dependent index into the argument block.
-    int lres[2][2], lrest[2][2], ldense[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int lv = 0; lv < 2; ++lv) {
-            const int want = 8 * kb + 2 * q + lv;
-            int r = 0, rt = 0, dn = 0;
-#pragma unroll
-            for (int l = 0; l < 16; ++l) {
-                r = l == want ? a.h.res_s[l] : r;
-                rt = l == want ? a.h.res_t[l] : rt;
-                dn = l == want ? a.h.dense[l] : dn;
-            }
-            lres[kb][lv] = r;
-            lrest[kb][lv] = rt;
-            ldense[kb][lv] = dn;
-        }
-
-    __shared__ half4_t s_z[4 * 8 * 64];
-    half4_t* sZ = s_z + (threadIdx.x >> 6) * (8 * 64);  // this wave's [kb][g][lane]
     const bool gelu = a.act == IA_ACT_GELU;
-    for (int64_t base = wave * 64; base < a.N; base += nwaves * 64) {
-        // ---- hash gather: lane (q, c) computes levels {2q, 2q+1, 8+2q, 9+2q}
-        // of Gaussians base + 16 g + c, g = 0..3, into its own LDS slots
-        // (a rolled loop over g keeps the number of loads in flight bounded).
-#pragma unroll 1
+    // features of the next 64 Gaussians are loaded while this tile computes
+    auto load_z = [&](int64_t b0, half4_t (&Zo)[2][4]) {
+#pragma unroll
         for (int g = 0; g < 4; ++g) {
-            int64_t gi = base + 16 * g + c;
-            if (gi >= a.N) gi = a.N - 1;
-            const float* p = a.pos + gi * a.stride;
-            float xt[4];
-            normalize_pos(p[0], p[1], p[2], a.stride == 4 ? p[3] : a.t_scalar, a.h.t_min, a.h.t_max, xt);
+            int64_t gi = b0 + 16 * g + c;
+            if (gi >= n) gi = n - 1;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                half4_t zz;
-#pragma unroll
-                for (int lv = 0; lv < 2; ++lv) {
-                    const int l = 8 * kb + 2 * q + lv;
-                    float z0, z1;
-                    interp_level2<true>((const _Float16*)a.tables + (size_t)l * a.h.T * 2, xt, lres[kb][lv],
-                                        lrest[kb][lv], ldense[kb][lv], a.h.mask, z0, z1);
-                    zz[2 * lv] = (_Float16)z0;
-                    zz[2 * lv + 1] = (_Float16)z1;
-                }
-                sZ[(kb * 4 + g) * 64 + lane] = zz;
+                const int l = 8 * kb + 2 * q;
+                Zo[kb][g] = unpack2(zbuf[(size_t)l * zstride + gi], zbuf[(size_t)(l + 1) * zstride + gi]);
             }
         }
+    };
+    half4_t Zn[2][4];
+    if (wave * 64 < n) load_z(wave * 64, Zn);
+    for (int64_t base = wave * 64; base < n; base += nwaves * 64) {
         half4_t Z[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) Z[kb][g] = sZ[(kb * 4 + g) * 64 + lane];
+            for (int g = 0; g < 4; ++g) Z[kb][g] = Zn[kb][g];
+        if (base + nwaves * 64 < n) load_z(base + nwaves * 64, Zn);
         // ---- trunk layer 1: 32 -> 64
         half4_t H1[4][4];
 #pragma unroll
@@ -330,7 +419,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float v = acc[e] + B1[rb][e];
-                    v = gelu ? act_fn(IA_ACT_GELU, v) : act_fn(IA_ACT_RELU, v);
+                    v = gelu ? gelu_fp16path(v) : act_fn(IA_ACT_RELU, v);
                     H1[rb][g][e] = (_Float16)v;
                 }
             }
@@ -347,7 +436,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float v = acc[e] + B2[rb][e];
-                    v = gelu ? act_fn(IA_ACT_GELU, v) : act_fn(IA_ACT_RELU, v);
+                    v = gelu ? gelu_fp16path(v) : act_fn(IA_ACT_RELU, v);
                     H2[rb][g][e] = (_Float16)v;
                 }
             }
@@ -364,18 +453,19 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(DecodeArgs a) {
             // lane q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
             float part = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
             float other = __shfl_xor(part, 16);
-            float n = fmaxf(sqrtf(part + other), 1e-12f);
-            const int64_t gi = base + 16 * g + c;
-            if (gi < a.N) {
+            float nrm = fmaxf(sqrtf(part + other), 1e-12f);
+            const int64_t gl = base + 16 * g + c;
+            if (gl < n) {
+                const int64_t gi = out_off + gl;
                 if (q == 0) {
                     a.scales[gi * 3 + 0] = expf(fminf(o[0], 20.0f));
                     a.scales[gi * 3 + 1] = expf(fminf(o[1], 20.0f));
                     a.scales[gi * 3 + 2] = expf(fminf(o[2], 20.0f));
-                    a.quats[gi * 4 + 0] = o[3] / n;
+                    a.quats[gi * 4 + 0] = o[3] / nrm;
                 } else if (q == 1) {
-                    a.quats[gi * 4 + 1] = o[0] / n;
-                    a.quats[gi * 4 + 2] = o[1] / n;
-                    a.quats[gi * 4 + 3] = o[2] / n;
+                    a.quats[gi * 4 + 1] = o[0] / nrm;
+                    a.quats[gi * 4 + 2] = o[1] / nrm;
+                    a.quats[gi * 4 + 3] = o[2] / nrm;
                     a.colors[gi * 3 + 0] = sigmoidf_(o[3]);
                 } else if (q == 2) {
                     a.colors[gi * 3 + 1] = sigmoidf_(o[0]);
@@ -399,9 +489,19 @@ int grid_for(int64_t items_per_block, int64_t N, int cap_blocks) {
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
     if (a.N <= 0) return hipSuccess;
     if (dtype == IA_DTYPE_F16) {
-        // 256 threads = 4 waves x 64 Gaussians per block-iteration
-        int grid = grid_for(256, a.N, 256 * 64);
-        hipLaunchKernelGGL(decode_mfma_kernel, dim3(grid), dim3(256), 0, s, a);
+        if (!a.zbuf || a.zcap <= 0) return hipErrorInvalidValue;
+        for (int64_t off = 0; off < a.N; off += a.zcap) {
+            const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
+            const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
+            float4* xt = reinterpret_cast<float4*>(a.zbuf + (size_t)a.h.L * a.zcap);
+            hipLaunchKernelGGL(normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
+                               a.pos + off * a.stride, n, xt);
+            hipLaunchKernelGGL(gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n, nchunk,
+                               a.h, (const uint32_t*)a.tables, a.zbuf, a.zcap);
+            // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
+            int grid = grid_for(256, n, 256 * 8);
+            hipLaunchKernelGGL(mlp_f16_kernel, dim3(grid), dim3(256), 0, s, a, a.zbuf, a.zcap, n, off);
+        }
         return hipGetLastError();
     }
     int grid = grid_for(256, a.N, 1 << 30);

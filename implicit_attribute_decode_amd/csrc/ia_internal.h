@@ -44,7 +44,12 @@ struct DecodeArgs {
     float* quats;
     float* colors;
     float* opacity;
+    uint32_t* zbuf;  // fp16 path: level-major feature scratch [L][zcap] (packed fp16 pairs)
+    int64_t zcap;    // Gaussians per chunk the scratch holds
 };
+
+// Gaussians per fp16-decode chunk; the handle owns L * kDecodeChunk * 4 bytes.
+constexpr int64_t kDecodeChunk = int64_t(1) << 22;
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 

@@ -22,9 +22,11 @@
  *     errors are detected before anything is enqueued; the message is
  *     available from ia_last_error() on the calling thread.  No C++
  *     exception crosses this boundary.
- *   - Handles are immutable after their set_params call; concurrent calls that
- *     only read a handle (decode, deform) on different streams are safe.
- *     Calls that share a render workspace must not overlap.
+ *   - Handles are immutable after their set_params call.  HexPlane deform
+ *     calls on different streams may overlap.  An fp16 decoder handle owns a
+ *     feature scratch buffer ((4 L + 16) x 2^22 bytes), so decode calls on one
+ *     such handle must be stream-ordered (use one handle per concurrent
+ *     stream).  Calls that share a render workspace must not overlap.
  */
 #ifndef IA_H_
 #define IA_H_
@@ -116,7 +118,10 @@ IA_API ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* 
  *   biases : n_hidden + 1 pointers to fp32 [out]
  * params_on_device: 1 if all the above are device pointers, 0 if host.
  * The copies are enqueued on `stream`; host sources may be freed on return
- * (host copies are synchronous).  May be called again to replace parameters.
+ * (host copies are synchronous).  For the fp16 decoder this call also
+ * allocates the handle's feature scratch ((4 L + 16) x 2^22 bytes; decode
+ * processes at most 2^22 Gaussians per gather/MLP kernel pair).  May be
+ * called again to replace parameters (waits for the device first).
  * Errors: INVALID_ARG, OUT_OF_MEMORY, DEVICE. */
 IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
                                 const float* const* biases, int32_t params_on_device, void* stream);

@@ -693,14 +693,21 @@ static void composite(const orc_splats* g, const uint32_t* list, long n, int px,
         double quad = A * dx * dx + Cc * dy * dy;
         double cross = B * dx * dy;
         double power = -0.5 * quad - cross;
-        /* fp32 error of power is a few roundings of its largest term */
+        /* Rounding bands of an fp32 evaluation (u = 2^-24), doubled for margin:
+         *   power: six roundings of terms no larger than mag -> 6 u mag;
+         *   alpha = o exp(power): exp2 of a rounded product plus one ulp,
+         *     a further rounding for o *, and the power error -> (10 u + 6 u mag)
+         *     relative;
+         *   T *= 1 - alpha: two roundings, plus alpha's error scaled by
+         *     alpha / (1 - alpha). */
+        const double u = 5.9604644775390625e-08;
         double mag = 0.5 * fabs(quad) + fabs(cross);
-        double err_p = 1e-6 * mag;
-        if (fabs(power + 4.5) <= 1e-5 * 4.5 + err_p) fl = 1;
+        double err_p = 2.0 * 6.0 * u * mag;
+        if (fabs(power + 4.5) <= err_p) fl = 1;
         if (fabs(power) <= err_p && mag > 0.0) fl = 1;
         if (power < -4.5 || power > 0.0) continue;
         double ga = (double)g->opacity[i] * exp(power);
-        double rel_a = 1e-5 + 2.0 * err_p; /* relative band on alpha */
+        double rel_a = 2.0 * (10.0 * u + 6.0 * u * mag);
         if (fabs(ga - 0.99) <= rel_a * 0.99) fl = 1;
         double alpha = ga < 0.99 ? ga : 0.99;
         if (fabs(alpha - 1.0 / 255.0) <= rel_a / 255.0) fl = 1;
@@ -708,10 +715,8 @@ static void composite(const orc_splats* g, const uint32_t* list, long n, int px,
         for (int k = 0; k < 3; ++k) C[k] += g->color[i * 3 + k] * alpha * T;
         T = T * (1.0 - alpha);
         last = (uint32_t)(j + 1);
-        /* an error d in alpha moves 1 - alpha by alpha/(1 - alpha) * d relative */
-        relT += 1.2e-7 + alpha / (1.0 - alpha) * (2e-7 + 2.0 * err_p);
-        double band = 1e-5 > 4.0 * relT ? 1e-5 : 4.0 * relT;
-        if (fabs(T - 1e-4) <= band * 1e-4) fl = 1;
+        relT += 2.0 * (2.0 * u + alpha / (1.0 - alpha) * rel_a * 0.5);
+        if (fabs(T - 1e-4) <= relT * 1e-4) fl = 1;
         if (T < 1e-4) break;
     }
     for (int k = 0; k < 3; ++k) out[k] = C[k];
