@@ -1,14 +1,17 @@
 """Benchmark: decode + render of the 150-frame sports-like sequence.
 
 Workload (one "step"): 150 frames x 200k Gaussians = 30M (x, y, z, t)
-positions, already resident in HBM.  One ia_decode_xyzt launch decodes all
-of them (16-level 4D hash grid, fp16 MFMA 32-64-64-11 decoder), then one
+positions, already resident in HBM: one ia_decode_xyzt call decodes all of
+them (16-level 4D hash grid, fp16 MFMA 32-64-64-11 decoder), then one
 ia_render call renders the 150 frames at 640x360 from a 27-camera ring
-(projection, binning, radix sort, tile raster).  Prints one JSON line.
+(projection, binning, radix sort, tile raster), both on one stream.  The
+level-major hash gather needs the L2 to itself, so decode and render are not
+overlapped across streams.  Prints one JSON line.
 
 Also reported: the per-frame mode (150 separate decode + render calls), the
-decode kernel's roofline (HBM, algorithmic bytes per Gaussian), and the CPU
-oracle's rate on a bounded sample of the same workload.
+roofline of the dominant kernel (the level-major hash gather) from HIP events
+recorded around its launches, and the CPU oracle's rate on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
@@ -25,10 +28,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# Algorithmic bytes per Gaussian of the decode kernel: 16 B (x,y,z,t) in,
-# 16 levels x 16 corners x 2 fp16 features = 1024 B gathered, 44 B out
-# (scales 12, quats 16, colours 12, opacity 4).
-DECODE_BYTES_PER_GAUSSIAN = 16 + 16 * 16 * 2 * 2 + 44
+LEVELS, CORNERS, FEAT_BYTES = 16, 16, 4  # fp16 x 2 features per table entry
+# Algorithmic bytes of the gather kernel per (Gaussian, level): 16 corner
+# entries of 4 bytes, the 16-byte normalised position, the 4-byte feature
+# pair written -> 84 B; 16 levels -> 1344 B per Gaussian.
+GATHER_BYTES_PER_GAUSSIAN = LEVELS * (CORNERS * FEAT_BYTES + 16 + 4)
+# Whole decode per Gaussian: 16 B position in, 1024 B gathered, 44 B out.
+DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
 
 
 def log(*a):
@@ -43,9 +49,8 @@ def cpu_baseline(seq, dec, budget_s: float = 15.0, max_frames: int = 12) -> dict
     def one(f):
         x = seq.xyzt([f])
         d = O.decode(dec, x, mode=0)
-        cam = seq.camera(f)
         fo = np.array([0, x.shape[0]])
-        O.render([cam], fo, x[:, :3], d["scales"].astype(np.float32), d["quats"].astype(np.float32),
+        O.render([seq.camera(f)], fo, x[:, :3], d["scales"].astype(np.float32), d["quats"].astype(np.float32),
                  d["opacity"].astype(np.float32), d["colors"])
 
     t0 = time.perf_counter()
@@ -61,6 +66,19 @@ def cpu_baseline(seq, dec, budget_s: float = 15.0, max_frames: int = 12) -> dict
                       f"decode (fp64) + render, {dt:.1f} s"}
 
 
+def timed(fn, reps, stream):
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,7 +86,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--frames", type=int, default=150)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-per-frame", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-frame comparison")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (a reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -89,24 +109,28 @@ def main():
     xyzt = torch.as_tensor(seq.xyzt(), device=dev)
     log(f"positions: {N} in {time.perf_counter() - t0:.1f} s")
     dec = S.single_decoder()
-    D = Decoder(dec)
-    R = Renderer()
     cams = [seq.camera(f) for f in range(F)]
     fo = np.arange(F + 1, dtype=np.int64) * per
-    attrs = D.decode_xyzt(xyzt)
-    g = dict(means=xyzt[:, :3], **attrs)
+    attrs = {k: torch.empty((N, w), device=dev) for k, w in (("scales", 3), ("quats", 4), ("colors", 3))}
+    attrs["opacity"] = torch.empty((N,), device=dev)
     image = torch.empty((F, 3, seq.H, seq.W), device=dev)
-
-    # capacity: first call with a guess, then exactly what the frames need
-    cap = 4 * N
-    probe = R.render(g, fo, cams, cap, aux=True, out={"image": image})
-    torch.cuda.synchronize()
-    E = int(probe["n_entries"].item())
-    if E > cap or cap > 2 * E + 4096:
-        cap = int(E * 1.02) + 4096
-    log(f"tile entries: {E}, capacity {cap}")
-
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    D = Decoder(dec)
+    R = Renderer()
+    g = dict(means=xyzt[:, :3], **attrs)
+    D.decode_xyzt(xyzt, out=attrs)
+    probe = R.render(g, fo, cams, 4 * N, aux=True, out={"image": image})
+    E = Renderer.count_entries(probe)
+    cap = int(E * 1.02) + 4096
+    del probe
+    log(f"tile entries: {E}, capacity {cap}")
 
     def step():
         D.decode_xyzt(xyzt, out=attrs)
@@ -115,60 +139,44 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    ms_step = timed(step, args.steps, stream)
+    wall = (time.perf_counter() - wall0) / args.steps
+    log(f"step: {ms_step:.3f} ms (wall {1e3 * wall:.3f} ms)")
+
+    # dominant kernel: HIP events around every library launch, same streams
+    ia.ia_profile_reset()
+    ia.ia_profile_enable(True)
+    for _ in range(3):
         step()
-    ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"step: {ms_step:.3f} ms (wall {1e3 * wall / args.steps:.3f} ms)")
+    prof = ia.ia_profile_report()
+    ia.ia_profile_enable(False)
+    calls, gather_ms = prof["gather_f16_kernel"]
+    gather_avg_ms = gather_ms / calls
+    gaussians_per_launch = N * 3 / calls
+    achieved = GATHER_BYTES_PER_GAUSSIAN * gaussians_per_launch / (gather_avg_ms / 1e3) / 1e9
+    kernels = {k: {"calls_per_step": round(v[0] / 3, 2), "ms_per_step": round(v[1] / 3, 4)}
+               for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
+    log("per-kernel (ms/step): " + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
 
-    # the decode kernel alone (one launch per call), same stream, HIP events
-    reps = max(3, args.steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        D.decode_xyzt(xyzt, out=attrs)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_decode = e0.elapsed_time(e1) / reps
-    e0.record(stream)
-    for _ in range(reps):
-        R.render(g, fo, cams, cap, out={"image": image})
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_render = e0.elapsed_time(e1) / reps
-    log(f"decode {ms_decode:.3f} ms, render {ms_render:.3f} ms")
-
-    per_frame_fps = None
-    if not args.no_per_frame:
-        # 150 independent decode + render calls (one frame each)
+    extra = {}
+    if not args.no_extra:
+        # per-frame: 150 x (decode 200k, render 1 frame)
         Rf = Renderer()
-        outs = [None] * F
-        capf = int(cap / F * 3) + 4096
+        capf = int(E / F * 3) + 4096
 
         def frame_pass():
             for f in range(F):
                 sl = slice(f * per, (f + 1) * per)
                 a = D.decode_xyzt(xyzt[sl], out={k: v[sl] for k, v in attrs.items()})
-                gf = dict(means=xyzt[sl, :3], **a)
-                outs[f] = Rf.render(gf, [0, per], [cams[f]], capf, out={"image": image[f:f + 1]})
+                Rf.render(dict(means=xyzt[sl, :3], **a), [0, per], [cams[f]], capf, out={"image": image[f:f + 1]})
 
         frame_pass()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        frame_pass()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per_frame_fps = F / (e0.elapsed_time(e1) / 1e3)
+        extra["per_frame_mode_fps"] = round(F / (timed(frame_pass, 1, stream) / 1e3), 2)
+        log(f"per-frame mode {extra['per_frame_mode_fps']} fps")
 
     fps = F / (ms_step / 1e3)
-    achieved = DECODE_BYTES_PER_GAUSSIAN * N / (ms_decode / 1e3) / 1e9
     result = {
         "metric": "frames/sec and Gaussians/sec (decode+render) at 640×360, 200k Gaussians/frame",
         "value": round(fps, 2),
@@ -186,12 +194,11 @@ def main():
         "config": {"workload": f"sequence: {F} frames x {per} Gaussians = {N} (x,y,z,t), 640x360, "
                                "27-camera ring, 16-level fp16 hash (2^19), 32-64-64-11 GELU decoder",
                    "frames": F, "gaussians_per_frame": per, "tile_entries": E,
-                   "ms_decode": round(ms_decode, 4), "ms_render": round(ms_render, 4),
-                   "per_frame_mode_fps": None if per_frame_fps is None else round(per_frame_fps, 2)},
-        "roofline": {"kernel": "decode_mfma_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                   "kernels": kernels, **extra},
+        "roofline": {"kernel": "gather_f16_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "bytes_per_unit": DECODE_BYTES_PER_GAUSSIAN, "units_per_launch": N},
+                     "traffic": None, "bytes_per_unit": GATHER_BYTES_PER_GAUSSIAN,
+                     "units_per_launch": round(gaussians_per_launch), "avg_launch_ms": round(gather_avg_ms, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

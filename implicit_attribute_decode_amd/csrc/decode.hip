@@ -325,9 +325,14 @@ __global__ void __launch_bounds__(256) gather_f16_kernel(const float4* xt, int64
             const int bz = c & 1, bt = c >> 1;
             const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
             const float w = (wxy * wz[bz]) * wt[bt];
-            const uint32_t raw = tab[idx];
-            a0 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
-            a1 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+            // A corner of exactly zero weight adds exactly zero (finite table
+            // entries): it is not fetched.  This happens whenever a coordinate
+            // sits on a grid vertex, e.g. frames whose time is a temporal vertex.
+            if (w != 0.0f) {
+                const uint32_t raw = tab[idx];
+                a0 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
+                a1 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+            }
         }
         a0 += __shfl_xor(a0, 1, 4);
         a1 += __shfl_xor(a1, 1, 4);
@@ -494,24 +499,24 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
             const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
             float4* xt = reinterpret_cast<float4*>(a.zbuf + (size_t)a.h.L * a.zcap);
-            hipLaunchKernelGGL(normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
+            IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
                                a.pos + off * a.stride, n, xt);
-            hipLaunchKernelGGL(gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n, nchunk,
+            IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n, nchunk,
                                a.h, (const uint32_t*)a.tables, a.zbuf, a.zcap);
             // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
             int grid = grid_for(256, n, 256 * 8);
-            hipLaunchKernelGGL(mlp_f16_kernel, dim3(grid), dim3(256), 0, s, a, a.zbuf, a.zcap, n, off);
+            IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel, dim3(grid), dim3(256), 0, s, a, a.zbuf, a.zcap, n, off);
         }
         return hipGetLastError();
     }
     int grid = grid_for(256, a.N, 1 << 30);
     const int LF = a.in_dim, H1 = a.hidden[0], H2 = a.n_hidden > 1 ? a.hidden[1] : 0;
     if (LF == 8 && H1 == 32 && H2 == 0)
-        hipLaunchKernelGGL((decode_f32_kernel<8, 32, 0>), dim3(grid), dim3(256), 0, s, a);
+        IA_LAUNCH("decode_f32_kernel", (decode_f32_kernel<8, 32, 0>), dim3(grid), dim3(256), 0, s, a);
     else if (LF == 32 && H1 == 64 && H2 == 64)
-        hipLaunchKernelGGL((decode_f32_kernel<32, 64, 64>), dim3(grid), dim3(256), 0, s, a);
+        IA_LAUNCH("decode_f32_kernel", (decode_f32_kernel<32, 64, 64>), dim3(grid), dim3(256), 0, s, a);
     else if (LF == 32 && H1 == 64 && H2 == 0)
-        hipLaunchKernelGGL((decode_f32_kernel<32, 64, 0>), dim3(grid), dim3(256), 0, s, a);
+        IA_LAUNCH("decode_f32_kernel", (decode_f32_kernel<32, 64, 0>), dim3(grid), dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -235,7 +235,7 @@ hipError_t launch_hexplane(const HexArgs& a, hipStream_t s) {
     int64_t per_block = 4 * 16 * kG;
     int64_t grid = (a.N + per_block - 1) / per_block;
     if (grid > 4096) grid = 4096;
-    hipLaunchKernelGGL(hexplane_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+    IA_LAUNCH("hexplane_kernel", hexplane_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -12,6 +12,26 @@
 
 namespace ia {
 
+// Brackets one kernel launch with HIP events on its stream when profiling is
+// enabled (ia_profile_enable); a no-op otherwise.
+class ProfScope {
+  public:
+    ProfScope(const char* name, hipStream_t s);
+    ~ProfScope();
+
+  private:
+    const char* name_;
+    hipStream_t s_;
+    hipEvent_t start_{}, stop_{};
+    bool active_ = false;
+};
+
+#define IA_LAUNCH(name, kernel, grid, block, shmem, stream, ...)               \
+    do {                                                                       \
+        ::ia::ProfScope ia_prof_scope_(name, stream);                          \
+        hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);   \
+    } while (0)
+
 constexpr int kMaxLevels = 32;
 
 // Per-level geometry of the 4D hash encoder (SPIN-4DGS §3.3, Eq. 9).

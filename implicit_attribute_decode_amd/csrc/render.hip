@@ -55,7 +55,7 @@ hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
         Payload p;
         int n = (int)(words - off < 896 ? words - off : 896);
         for (int i = 0; i < n; ++i) p.w[i] = w[off + i];
-        hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, d + off, p, n);
+        IA_LAUNCH("upload_kernel", upload_kernel, dim3(1), dim3(256), 0, s, d + off, p, n);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -724,33 +724,33 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
     if (N > 0) {
         PreArgs pre{a.means, a.means_stride, a.scales, a.quats, a.colors, a.sh, a.opacity, a.sh_degree,
                     cams, fo, a.frames, N, pa, pb, pc, depth, rect, tiles, bsum};
-        hipLaunchKernelGGL(preprocess_kernel, dim3(L.nb1), dim3(kBlock), 0, s, pre);
-        hipLaunchKernelGGL(scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
+        IA_LAUNCH("preprocess_kernel", preprocess_kernel, dim3(L.nb1), dim3(kBlock), 0, s, pre);
+        IA_LAUNCH("scan_reduce_kernel", scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
     }
-    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, N > 0 ? L.nb2 : 0, (uint64_t)L.cap, nent,
+    IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, N > 0 ? L.nb2 : 0, (uint64_t)L.cap, nent,
                        a.n_entries_out, a.overflow_out);
     if (N > 0) {
-        hipLaunchKernelGGL(scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
+        IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
         EmitArgs em{tiles, rect, depth, boff, fo, a.frames, N, L.tiles_x, ntiles, (uint64_t)L.cap, keys[0], vals[0]};
-        hipLaunchKernelGGL(emit_kernel, dim3(L.nb1), dim3(kBlock), 0, s, em);
+        IA_LAUNCH("emit_kernel", emit_kernel, dim3(L.nb1), dim3(kBlock), 0, s, em);
     }
     int cur = 0;
     for (int pass = 0; pass < a.sort_passes; ++pass) {
         SortPass sp{keys[cur], vals[cur], keys[cur ^ 1], vals[cur ^ 1], nent, (uint64_t)L.cap, 8 * pass,
                     L.sort_blocks, counts, digit_tot};
-        hipLaunchKernelGGL(sort_upsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
-        hipLaunchKernelGGL(sort_scan_kernel, dim3(256), dim3(kBlock), 0, s, sp);
-        hipLaunchKernelGGL(sort_downsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
+        IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
+        IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(256), dim3(kBlock), 0, s, sp);
+        IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
         cur ^= 1;
     }
     const int64_t nr = 2 * L.ntiles_all;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_cap(nr, kBlock, 4096)), dim3(kBlock), 0, s,
+    IA_LAUNCH("fill_u32_kernel", fill_u32_kernel, dim3(grid_cap(nr, kBlock, 4096)), dim3(kBlock), 0, s,
                        reinterpret_cast<uint32_t*>(ranges), 0u, nr);
-    hipLaunchKernelGGL(ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, keys[cur], nent,
+    IA_LAUNCH("ranges_kernel", ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, keys[cur], nent,
                        (uint64_t)L.cap, ranges, (uint32_t)L.ntiles_all);
     RasterArgs ra{ranges, vals[cur], pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, (uint64_t)L.cap, N,
                   a.image, a.T_final, a.n_contrib};
-    hipLaunchKernelGGL(raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kBlock), 0, s, ra);
+    IA_LAUNCH("raster_kernel", raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kBlock), 0, s, ra);
     e = hipGetLastError();
     *keys_out = keys[cur];
     *vals_out = vals[cur];

@@ -27,7 +27,8 @@ IA_ACT_RELU, IA_ACT_GELU = 0, 1
 # Every entry point include/ia.h declares.
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
            "ia_decoder_destroy", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
-           "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render")
+           "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render", "ia_profile_enable",
+           "ia_profile_report", "ia_profile_reset")
 
 
 class IAError(RuntimeError):
@@ -98,6 +99,10 @@ def load(path: str = LIB_PATH):
         L.ia_hexplane_destroy.restype = None
         L.ia_render_workspace_size.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int64, P]
         L.ia_render.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P]
+        L.ia_profile_enable.argtypes = [C.c_int32]
+        L.ia_profile_report.argtypes = [P, C.c_size_t, P]
+        L.ia_profile_reset.argtypes = []
+        L.ia_profile_reset.restype = None
         for name in EXPORTS[1:]:
             if getattr(L, name).restype is C.c_int:
                 getattr(L, name).restype = C.c_int32
@@ -213,3 +218,25 @@ def ia_render(g: Gaussians, frame_offsets, cams, ws, max_entries: int, image, au
     _check(load().ia_render(C.byref(g), fo.ctypes.data_as(C.c_void_p), F, arr, _ptr(ws),
                             int(ws.numel() * ws.element_size()), int(max_entries), _ptr(image),
                             None if aux is None else C.byref(aux), _stream(stream)))
+
+
+# ----------------------------------------------------------------- diagnostics
+
+
+def ia_profile_enable(on: bool = True):
+    _check(load().ia_profile_enable(1 if on else 0))
+
+
+def ia_profile_reset():
+    load().ia_profile_reset()
+
+
+def ia_profile_report() -> dict:
+    """{kernel name: (calls, total ms)} since the last reset (waits for the events)."""
+    import json
+
+    need = C.c_size_t()
+    load().ia_profile_report(None, 0, C.byref(need))
+    buf = C.create_string_buffer(int(need.value) + 64)
+    _check(load().ia_profile_report(buf, len(buf), None))
+    return {k: (int(v[0]), float(v[1])) for k, v in json.loads(buf.value.decode()).items()}

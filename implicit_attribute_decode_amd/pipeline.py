@@ -153,6 +153,10 @@ class Renderer:
         return res
 
     @staticmethod
+    def count_entries(res: dict) -> int:
+        return int(res["n_entries"].item())
+
+    @staticmethod
     def view(res: dict, name: str, count: int) -> torch.Tensor:
         """A workspace view of `count` rows (e.g. sorted_keys of n_entries rows)."""
         off, dt, width = res["_view_" + name]
@@ -160,3 +164,4 @@ class Renderer:
         nbytes = count * width * torch.empty((), dtype=dt).element_size()
         t = ws[off:off + nbytes].view(dt)
         return t.view(count, width) if width > 1 else t
+

@@ -242,6 +242,25 @@ IA_API ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, 
                     void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux,
                     void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Diagnostics: per-kernel timing with HIP events                            */
+/* ------------------------------------------------------------------------ */
+
+/* Enable (on != 0) or disable timing.  While enabled, every kernel launch of
+ * the library is bracketed by two HIP events recorded on its launch stream.
+ * Process-wide; safe to call at any time.  Returns IA_OK. */
+IA_API ia_status ia_profile_enable(int32_t on);
+
+/* Wait for the recorded events and write a JSON object
+ * {"kernel name": [calls, total milliseconds], ...} accumulated since the last
+ * reset into buf (host, len bytes).  *needed (nullable) receives the size
+ * required including the terminating zero.  Errors: INVALID_ARG if buf is
+ * null or too small (needed is still set). */
+IA_API ia_status ia_profile_report(char* buf, size_t len, size_t* needed);
+
+/* Drop all recorded timings. */
+IA_API void ia_profile_reset(void);
+
 #ifdef __cplusplus
 }
 #endif
