@@ -29,10 +29,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 LEVELS, CORNERS, FEAT_BYTES = 16, 16, 4  # fp16 x 2 features per table entry
-# Algorithmic bytes of the gather kernel per (Gaussian, level): 16 corner
-# entries of 4 bytes, the 16-byte normalised position, the 4-byte feature
-# pair written -> 84 B; 16 levels -> 1344 B per Gaussian.
-GATHER_BYTES_PER_GAUSSIAN = LEVELS * (CORNERS * FEAT_BYTES + 16 + 4)
+# Algorithmic bytes of the hash gather per Gaussian: the 16-byte (x,y,z,t)
+# position and 16 levels x 16 corners x 4-byte entries = 1040 B.  Scratch
+# traffic of this implementation (the normalised position re-read per level,
+# the packed features written) is not counted.
+GATHER_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES
 # Whole decode per Gaussian: 16 B position in, 1024 B gathered, 44 B out.
 DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
 
