@@ -13,7 +13,7 @@
 //                       level-major gather kernel (one level's table resident
 //                       in L2 at a time) writes the features to a scratch
 //                       buffer owned by the decoder handle; an MLP kernel runs
-//                       the decoder on v_mfma_f32_16x16x16_f16 with fp32
+//                       the decoder on v_mfma_f32_16x16x32_f16 with fp32
 //                       accumulation and applies Eq. 11.
 //
 // Position normalisation and the per-axis cell decision are computed one IEEE
@@ -28,6 +28,7 @@ namespace ia {
 namespace {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kP1 = 1u, kP2 = 2654435761u, kP3 = 805459861u, kP4 = 3674653429u;
@@ -258,13 +259,10 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // shuffles sum the four partial results.  Output z[level][i] = two fp16
 // features packed in 32 bits (RNE).
 //
-// mlp_f16_kernel: the 32 -> 64 -> 64 -> 11 decoder on v_mfma_f32_16x16x16_f16.
-// Register layout (wave64, lane l, q = l/16, c = l%16): A supplies row c,
-// k-slots 4q..4q+3; B supplies column c, the same k-slots; D holds rows
-// 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows, so a
-// layer's D registers are the next layer's B operand; slot (q, e) of k-block
-// kb is feature 16 kb + 4 q + e, i.e. levels 8 kb + 2 q (e = 0, 1) and
-// 8 kb + 2 q + 1 (e = 2, 3).
+// mlp_f16_kernel: the 32 -> 64 -> 64 -> 11 decoder on v_mfma_f32_16x16x32_f16.
+// Register layout (wave64, lane l, q = l/16, c = l%16): A supplies row c and
+// B column c, each with eight k-slots per lane that A and B share; D holds
+// rows 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows.
 
 constexpr int kGatherPerBlock = 1024;  // Gaussians per gather block (64 per pass x 16 passes)
 
@@ -359,6 +357,36 @@ __device__ __forceinline__ half4_t unpack2(uint32_t a, uint32_t b) {
     return r;
 }
 
+__device__ __forceinline__ half8_t cat8(half4_t lo, half4_t hi) {
+    return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// A operand of v_mfma_f32_16x16x32_f16 for row block rb, 32-wide k-block m of
+// a row-major [rows][in] fp16 matrix: slots e < 4 hold inputs 32 m + 4 q + e,
+// slots e >= 4 inputs 32 m + 16 + 4 q + (e - 4); rows >= `rows` are zero.
+__device__ __forceinline__ half8_t a_tile32(const _Float16* W, int in_dim, int rows, int rb, int m, int q, int c) {
+    const int row = 16 * rb + c;
+    if (row >= rows) return half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    const _Float16* r = W + (size_t)row * in_dim + 32 * m + 4 * q;
+    return cat8(load_h4(r), load_h4(r + 16));
+}
+
+// Bias + activation of one 16x16 D tile (rows 16 rb + 4 q + e), rounded to fp16.
+__device__ __forceinline__ half4_t act_tile(floatx4 acc, const float* bias, bool gelu) {
+    half4_t h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float v = acc[e] + bias[e];
+        h[e] = (_Float16)(gelu ? gelu_fp16path(v) : (v > 0.0f ? v : 0.0f));
+    }
+    return h;
+}
+
+// The decoder on v_mfma_f32_16x16x32_f16: a 32-wide k-block's slots (q, e)
+// map to inputs 32 m + 4 q + e and 32 m + 16 + 4 q + (e - 4), so the rows a
+// lane holds in two consecutive 16-row D tiles are exactly its B slots for
+// the next layer, and the features of levels {2q, 2q+1, 8+2q, 9+2q} the lane
+// loads are exactly its B slots of layer 1.
 __global__ void __launch_bounds__(256, 2) mlp_f16_kernel(DecodeArgs a, const uint32_t* zbuf, int64_t zstride,
                                                          int64_t n, int64_t out_off) {
     const int lane = threadIdx.x & 63;
@@ -369,89 +397,74 @@ __global__ void __launch_bounds__(256, 2) mlp_f16_kernel(DecodeArgs a, const uin
     const _Float16* W2 = (const _Float16*)a.W[1];  // [64][64]
     const _Float16* Wh = (const _Float16*)a.W[2];  // [11][64]
 
-    half4_t A1[4][2], A2[4][4], A3[4];
+    half8_t A1[4], A2[4][2], A3[2];
     float B1[4][4], B2[4][4], B3[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
+        A1[rb] = a_tile32(W1, 32, 64, rb, 0, q, c);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) A1[rb][kb] = load_h4(W1 + (16 * rb + c) * 32 + 16 * kb + 4 * q);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) A2[rb][kb] = load_h4(W2 + (16 * rb + c) * 64 + 16 * kb + 4 * q);
+        for (int m = 0; m < 2; ++m) A2[rb][m] = a_tile32(W2, 64, 64, rb, m, q, c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             B1[rb][e] = a.b[0][16 * rb + 4 * q + e];
             B2[rb][e] = a.b[1][16 * rb + 4 * q + e];
         }
     }
-    const half4_t zero4 = {0, 0, 0, 0};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) A3[kb] = c < 11 ? load_h4(Wh + c * 64 + 16 * kb + 4 * q) : zero4;
+    for (int m = 0; m < 2; ++m) A3[m] = a_tile32(Wh, 64, 11, 0, m, q, c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) B3[e] = (4 * q + e) < 11 ? a.b[2][4 * q + e] : 0.0f;
 
     const bool gelu = a.act == IA_ACT_GELU;
     // features of the next 64 Gaussians are loaded while this tile computes
-    auto load_z = [&](int64_t b0, half4_t (&Zo)[2][4]) {
+    auto load_z = [&](int64_t b0, half8_t (&Zo)[4]) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             int64_t gi = b0 + 16 * g + c;
             if (gi >= n) gi = n - 1;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int l = 8 * kb + 2 * q;
-                Zo[kb][g] = unpack2(zbuf[(size_t)l * zstride + gi], zbuf[(size_t)(l + 1) * zstride + gi]);
-            }
+            const int l = 2 * q;
+            Zo[g] = cat8(unpack2(zbuf[(size_t)l * zstride + gi], zbuf[(size_t)(l + 1) * zstride + gi]),
+                         unpack2(zbuf[(size_t)(l + 8) * zstride + gi], zbuf[(size_t)(l + 9) * zstride + gi]));
         }
     };
-    half4_t Zn[2][4];
+    half8_t Zn[4];
     if (wave * 64 < n) load_z(wave * 64, Zn);
     for (int64_t base = wave * 64; base < n; base += nwaves * 64) {
-        half4_t Z[2][4];
+        half8_t Z[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) Z[kb][g] = Zn[kb][g];
+        for (int g = 0; g < 4; ++g) Z[g] = Zn[g];
         if (base + nwaves * 64 < n) load_z(base + nwaves * 64, Zn);
         // ---- trunk layer 1: 32 -> 64
-        half4_t H1[4][4];
+        half8_t H1[2][4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                floatx4 acc = {0, 0, 0, 0};
-                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A1[rb][0], Z[0][g], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A1[rb][1], Z[1][g], acc, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float v = acc[e] + B1[rb][e];
-                    v = gelu ? gelu_fp16path(v) : act_fn(IA_ACT_RELU, v);
-                    H1[rb][g][e] = (_Float16)v;
-                }
+            for (int m = 0; m < 2; ++m) {
+                floatx4 z0 = {0, 0, 0, 0};
+                const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z[g], z0, 0, 0, 0);
+                const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z[g], z0, 0, 0, 0);
+                H1[m][g] = cat8(act_tile(lo, B1[2 * m], gelu), act_tile(hi, B1[2 * m + 1], gelu));
             }
         // ---- trunk layer 2: 64 -> 64
-        half4_t H2[4][4];
+        half8_t H2[2][4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                floatx4 acc = {0, 0, 0, 0};
+            for (int m = 0; m < 2; ++m) {
+                floatx4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A2[rb][kb], H1[kb][g], acc, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float v = acc[e] + B2[rb][e];
-                    v = gelu ? gelu_fp16path(v) : act_fn(IA_ACT_RELU, v);
-                    H2[rb][g][e] = (_Float16)v;
+                for (int k = 0; k < 2; ++k) {
+                    lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m][k], H1[k][g], lo, 0, 0, 0);
+                    hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m + 1][k], H1[k][g], hi, 0, 0, 0);
                 }
+                H2[m][g] = cat8(act_tile(lo, B2[2 * m], gelu), act_tile(hi, B2[2 * m + 1], gelu));
             }
         // ---- head block 64 -> 11 (rows 11..15 are zero) and Eq. 11
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A3[kb], H2[kb][g], acc, 0, 0, 0);
+            for (int k = 0; k < 2; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[k], H2[k][g], acc, 0, 0, 0);
             float o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = acc[e] + B3[e];

@@ -575,67 +575,106 @@ struct RasterArgs {
     uint32_t* n_contrib;
 };
 
-__global__ void __launch_bounds__(kBlock) raster_kernel(RasterArgs a) {
+// Per-pixel compositing state and one front-to-back step (Eq. 4).  A
+// Gaussian that is skipped (power outside [-4.5, 0] i.e. beyond 3 sigma,
+// alpha below 1/255, or the pixel already saturated) contributes alpha = 0,
+// which leaves C and T exactly unchanged, so the step has no branches.
+struct Pix {
+    float T, r, g, b;
+    uint32_t last;
+    bool done;
+};
+
+__device__ __forceinline__ void composite_step(Pix& p, float power, float opacity, float cr, float cg, float cb,
+                                               uint32_t pos) {
 #pragma clang fp contract(fast)
-    __shared__ float4 s_a[kBlock];
-    __shared__ float4 s_b[kBlock];
-    __shared__ float s_c[kBlock];
+    const float a0 = fminf(0.99f, opacity * __expf(power));
+    const bool take = !p.done && power >= -4.5f && power <= 0.0f && a0 >= (1.0f / 255.0f);
+    const float alpha = take ? a0 : 0.0f;
+    const float wgt = alpha * p.T;
+    p.r += cr * wgt;
+    p.g += cg * wgt;
+    p.b += cb * wgt;
+    p.T = p.T * (1.0f - alpha);
+    p.last = take ? pos : p.last;
+    p.done = p.done || p.T < 1e-4f;
+}
+
+// One 128-thread block per 16x16 tile; thread (col, row) shades pixels
+// (col, 2 row) and (col, 2 row + 1), which share dx and the dx terms of
+// power, so a wave covers a 16 x 8 pixel block.  When no pixel of the wave
+// lies within 3 sigma of a Gaussian the wave skips its compositing step
+// (the step would add alpha = 0 everywhere).
+// Gaussians of the tile's list are staged in LDS 256 at a time with the
+// conic pre-scaled by -1/2, -1, -1/2 (exact), so power = A' dx^2 + C' dy^2 +
+// B' dx dy.  A wave leaves a batch once all its pixels are saturated; the
+// block stops once all 256 are.
+constexpr int kRasterThreads = 128;
+constexpr int kRasterBatch = 256;
+
+__global__ void __launch_bounds__(kRasterThreads) raster_kernel(RasterArgs a) {
+#pragma clang fp contract(fast)
+    __shared__ float4 s_a[kRasterBatch];
+    __shared__ float4 s_b[kRasterBatch];
+    __shared__ float s_c[kRasterBatch];
     const int f = blockIdx.z;
     const uint32_t tile = (uint32_t)f * a.ntiles + blockIdx.y * (uint32_t)a.tiles_x + blockIdx.x;
     uint2 rg = a.ranges[tile];
     if (rg.y > a.cap) rg.y = (uint32_t)a.cap;
     if (rg.x > rg.y) rg.x = rg.y;
     const int px = blockIdx.x * 16 + (threadIdx.x & 15);
-    const int py = blockIdx.y * 16 + (threadIdx.x >> 4);
-    const bool inside = px < a.W && py < a.H;
-    const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
-    float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
-    uint32_t last = 0;
-    bool done = !inside;
-    for (uint32_t start = rg.x; start < rg.y; start += kBlock) {
-        if (__syncthreads_count(done) == kBlock) break;
-        const uint32_t idx = start + threadIdx.x;
-        if (idx < rg.y) {
-            uint32_t gid = a.vals[idx];
-            if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
-            s_a[threadIdx.x] = a.pa[gid];
-            s_b[threadIdx.x] = a.pb[gid];
-            s_c[threadIdx.x] = a.pc[gid];
-        }
-        __syncthreads();
-        const int n = (int)min((uint32_t)kBlock, rg.y - start);
-        if (__ballot(!done) != 0ull && !done) {
-            for (int j = 0; j < n; ++j) {
-                const float4 ga = s_a[j];
-                const float dx = fx - ga.x, dy = fy - ga.y;
-                const float4 gb = s_b[j];
-                const float power = -0.5f * (ga.z * dx * dx + gb.x * dy * dy) - ga.w * dx * dy;
-                if (power < -4.5f || power > 0.0f) continue;
-                const float alpha = fminf(0.99f, gb.y * __expf(power));
-                if (alpha < (1.0f / 255.0f)) continue;
-                const float wgt = alpha * T;
-                cr += gb.z * wgt;
-                cg += gb.w * wgt;
-                cb += s_c[j] * wgt;
-                T = T * (1.0f - alpha);
-                last = start - rg.x + (uint32_t)j + 1u;
-                if (T < 1e-4f) {
-                    done = true;
-                    break;
-                }
+    const int py0 = blockIdx.y * 16 + 2 * (threadIdx.x >> 4), py1 = py0 + 1;  // a wave: 16 x 8 pixels
+    const bool in0 = px < a.W && py0 < a.H, in1 = px < a.W && py1 < a.H;
+    const float fx = (float)px + 0.5f, fy0 = (float)py0 + 0.5f, fy1 = (float)py1 + 0.5f;
+    Pix p0{1.0f, 0.0f, 0.0f, 0.0f, 0u, !in0}, p1{1.0f, 0.0f, 0.0f, 0.0f, 0u, !in1};
+    for (uint32_t start = rg.x; start < rg.y; start += kRasterBatch) {
+        if (__syncthreads_count(p0.done && p1.done) == kRasterThreads) break;
+#pragma unroll
+        for (int k = 0; k < kRasterBatch / kRasterThreads; ++k) {
+            const uint32_t slot = threadIdx.x + k * kRasterThreads;
+            const uint32_t idx = start + slot;
+            if (idx < rg.y) {
+                uint32_t gid = a.vals[idx];
+                if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
+                const float4 pa = a.pa[gid], pb = a.pb[gid];
+                s_a[slot] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
+                s_b[slot] = make_float4(-0.5f * pb.x, pb.y, pb.z, pb.w);
+                s_c[slot] = a.pc[gid];
             }
         }
+        __syncthreads();
+        const int n = (int)min((uint32_t)kRasterBatch, rg.y - start);
+        const uint32_t pos0 = start - rg.x + 1u;
+        for (int j = 0; j < n; ++j) {
+            if (__ballot(!(p0.done && p1.done)) == 0ull) break;
+            const float4 ga = s_a[j];
+            const float4 gb = s_b[j];
+            const float gcb = s_c[j];
+            const float dx = fx - ga.x;
+            const float ta = ga.z * dx * dx, tb = ga.w * dx;
+            const float dy0 = fy0 - ga.y, dy1 = fy1 - ga.y;
+            const float pw0 = (ta + gb.x * dy0 * dy0) + tb * dy0;
+            const float pw1 = (ta + gb.x * dy1 * dy1) + tb * dy1;
+            // no pixel of the wave within 3 sigma: nothing to composite
+            const bool any = (pw0 >= -4.5f && pw0 <= 0.0f) || (pw1 >= -4.5f && pw1 <= 0.0f);
+            if (__ballot(any) == 0ull) continue;
+            composite_step(p0, pw0, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
+            composite_step(p1, pw1, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
+        }
     }
-    if (inside) {
-        const DevCamera& cam = a.cams[f];
-        const size_t plane = (size_t)a.W * a.H;
-        const size_t pix = (size_t)py * a.W + px;
-        float* img = a.image + (size_t)f * 3 * plane;
-        img[pix] = cr + T * cam.bg[0];
-        img[plane + pix] = cg + T * cam.bg[1];
-        img[2 * plane + pix] = cb + T * cam.bg[2];
-        if (a.T_final) a.T_final[(size_t)f * plane + pix] = T;
-        if (a.n_contrib) a.n_contrib[(size_t)f * plane + pix] = last;
+    const DevCamera& cam = a.cams[f];
+    const size_t plane = (size_t)a.W * a.H;
+    float* img = a.image + (size_t)f * 3 * plane;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const Pix& p = k ? p1 : p0;
+        if (!(k ? in1 : in0)) continue;
+        const size_t pix = (size_t)(k ? py1 : py0) * a.W + px;
+        img[pix] = p.r + p.T * cam.bg[0];
+        img[plane + pix] = p.g + p.T * cam.bg[1];
+        img[2 * plane + pix] = p.b + p.T * cam.bg[2];
+        if (a.T_final) a.T_final[(size_t)f * plane + pix] = p.T;
+        if (a.n_contrib) a.n_contrib[(size_t)f * plane + pix] = p.last;
     }
 }
 
@@ -750,7 +789,7 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
                        (uint64_t)L.cap, ranges, (uint32_t)L.ntiles_all);
     RasterArgs ra{ranges, vals[cur], pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, (uint64_t)L.cap, N,
                   a.image, a.T_final, a.n_contrib};
-    IA_LAUNCH("raster_kernel", raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kBlock), 0, s, ra);
+    IA_LAUNCH("raster_kernel", raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kRasterThreads), 0, s, ra);
     e = hipGetLastError();
     *keys_out = keys[cur];
     *vals_out = vals[cur];
