@@ -57,7 +57,10 @@ struct ia_decoder {
     void* tables = nullptr;
     void* W[4] = {nullptr, nullptr, nullptr, nullptr};
     float* b[4] = {nullptr, nullptr, nullptr, nullptr};
-    uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [L][ia::kDecodeChunk]
+    uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [chunk] float4
+    hipStream_t side = nullptr;  // fp16 path: MLP stream overlapping the next chunk's gather
+    hipEvent_t ev_gather[2] = {nullptr, nullptr};
+    hipEvent_t ev_mlp[2] = {nullptr, nullptr};
     bool ready = false;
 };
 
@@ -74,6 +77,13 @@ void free_decoder_params(ia_decoder* d) {
     d->tables = nullptr;
     if (d->zbuf) (void)hipFree(d->zbuf);
     d->zbuf = nullptr;
+    for (int k = 0; k < 2; ++k) {
+        if (d->ev_gather[k]) (void)hipEventDestroy(d->ev_gather[k]);
+        if (d->ev_mlp[k]) (void)hipEventDestroy(d->ev_mlp[k]);
+        d->ev_gather[k] = d->ev_mlp[k] = nullptr;
+    }
+    if (d->side) (void)hipStreamDestroy(d->side);
+    d->side = nullptr;
     d->ready = false;
 }
 
@@ -160,6 +170,11 @@ ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, flo
     a.opacity = out->opacity;
     a.zbuf = dec->zbuf;
     a.zcap = ia::kDecodeChunk;
+    a.side = dec->side;
+    for (int k = 0; k < 2; ++k) {
+        a.ev_gather[k] = dec->ev_gather[k];
+        a.ev_mlp[k] = dec->ev_mlp[k];
+    }
     hipError_t e = ia::launch_decode(a, dec->mlp.dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return IA_OK;
@@ -213,9 +228,16 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
         if (st == IA_OK) st = upload_param(reinterpret_cast<void**>(&dec->b[k]), biases[k], 4 * (size_t)dec->dims[k + 1], dev, s);
     }
     if (st == IA_OK && dec->mlp.dtype == IA_DTYPE_F16) {
-        // [L][chunk] packed feature pairs, then [chunk] normalised positions (float4)
-        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 4 + 16) * ia::kDecodeChunk);
+        // [2][L][chunk] packed feature pairs, then [chunk] normalised positions (float4)
+        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 8 + 16) * ia::kDecodeChunk);
         if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
+        // a side stream (default priority) and events for the MLP / gather overlap
+        if (st == IA_OK) e = hipStreamCreateWithFlags(&dec->side, hipStreamNonBlocking);
+        for (int k = 0; st == IA_OK && e == hipSuccess && k < 2; ++k) {
+            e = hipEventCreateWithFlags(&dec->ev_gather[k], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&dec->ev_mlp[k], hipEventDisableTiming);
+        }
+        if (st == IA_OK && e != hipSuccess) st = hip_fail(e, "stream/event creation");
     }
     if (st != IA_OK) {
         free_decoder_params(dec);

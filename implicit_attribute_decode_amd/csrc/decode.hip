@@ -508,17 +508,39 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
     if (a.N <= 0) return hipSuccess;
     if (dtype == IA_DTYPE_F16) {
         if (!a.zbuf || a.zcap <= 0) return hipErrorInvalidValue;
-        for (int64_t off = 0; off < a.N; off += a.zcap) {
+        // Chunks of at most zcap Gaussians.  With a side stream, the MLP of
+        // chunk k runs there while chunk k+1 is normalised and gathered on s;
+        // the feature scratch is double-buffered and events order the hand-offs.
+        const size_t zslot = (size_t)a.h.L * a.zcap;
+        float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
+        const bool overlap = a.side != nullptr && a.N > a.zcap;
+        int k = 0;
+        for (int64_t off = 0; off < a.N; off += a.zcap, ++k) {
             const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
             const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
-            float4* xt = reinterpret_cast<float4*>(a.zbuf + (size_t)a.h.L * a.zcap);
+            uint32_t* zb = a.zbuf + (size_t)(k & 1) * zslot;
+            hipError_t e;
+            if (overlap && k >= 2 && (e = hipStreamWaitEvent(s, a.ev_mlp[k & 1], 0)) != hipSuccess) return e;
             IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
-                               a.pos + off * a.stride, n, xt);
-            IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n, nchunk,
-                               a.h, (const uint32_t*)a.tables, a.zbuf, a.zcap);
+                      a.pos + off * a.stride, n, xt);
+            IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n,
+                      nchunk, a.h, (const uint32_t*)a.tables, zb, a.zcap);
             // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
-            int grid = grid_for(256, n, 256 * 8);
-            IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel, dim3(grid), dim3(256), 0, s, a, a.zbuf, a.zcap, n, off);
+            const int grid = grid_for(256, n, 256 * 8);
+            if (overlap) {
+                if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;
+                if ((e = hipStreamWaitEvent(a.side, a.ev_gather[k & 1], 0)) != hipSuccess) return e;
+                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel, dim3(grid), dim3(256), 0, a.side, a, zb, a.zcap, n, off);
+                if ((e = hipEventRecord(a.ev_mlp[k & 1], a.side)) != hipSuccess) return e;
+            } else {
+                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel, dim3(grid), dim3(256), 0, s, a, zb, a.zcap, n, off);
+            }
+        }
+        if (overlap) {
+            // the caller's stream resumes after the last MLPs (the side stream
+            // is in order, so the last event covers every earlier chunk)
+            hipError_t e = hipStreamWaitEvent(s, a.ev_mlp[(k - 1) & 1], 0);
+            if (e != hipSuccess) return e;
         }
         return hipGetLastError();
     }

@@ -64,8 +64,11 @@ struct DecodeArgs {
     float* quats;
     float* colors;
     float* opacity;
-    uint32_t* zbuf;  // fp16 path: level-major feature scratch [L][zcap] (packed fp16 pairs)
+    uint32_t* zbuf;  // fp16 path: feature scratch [2][L][zcap] (packed fp16 pairs), then [zcap] float4
     int64_t zcap;    // Gaussians per chunk the scratch holds
+    hipStream_t side;         // fp16 path: stream the MLP of one chunk overlaps the next gather on (or null)
+    hipEvent_t ev_gather[2];  // per scratch slot: gather done
+    hipEvent_t ev_mlp[2];     // per scratch slot: MLP done
 };
 
 // Gaussians per fp16-decode chunk; the handle owns L * kDecodeChunk * 4 bytes.

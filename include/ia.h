@@ -24,7 +24,7 @@
  *     exception crosses this boundary.
  *   - Handles are immutable after their set_params call.  HexPlane deform
  *     calls on different streams may overlap.  An fp16 decoder handle owns a
- *     feature scratch buffer ((4 L + 16) x 2^22 bytes), so decode calls on one
+ *     feature scratch buffer ((8 L + 16) x 2^22 bytes) and a side stream, so decode calls on one
  *     such handle must be stream-ordered (use one handle per concurrent
  *     stream).  Calls that share a render workspace must not overlap.
  */
@@ -119,7 +119,7 @@ IA_API ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* 
  * params_on_device: 1 if all the above are device pointers, 0 if host.
  * The copies are enqueued on `stream`; host sources may be freed on return
  * (host copies are synchronous).  For the fp16 decoder this call also
- * allocates the handle's feature scratch ((4 L + 16) x 2^22 bytes; decode
+ * allocates the handle's feature scratch ((8 L + 16) x 2^22 bytes; decode
  * processes at most 2^22 Gaussians per gather/MLP kernel pair).  May be
  * called again to replace parameters (waits for the device first).
  * Errors: INVALID_ARG, OUT_OF_MEMORY, DEVICE. */
