@@ -67,6 +67,63 @@ def cpu_baseline(seq, dec, budget_s: float = 15.0, max_frames: int = 12) -> dict
                       f"decode (fp64) + render, {dt:.1f} s"}
 
 
+HEX_FLOP_PER_GAUSSIAN = 2 * (192 * 256 + 256 * 256 + 256 * 58)  # 259,072
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def secondary(S, Decoder, HexPlane, Renderer, stream, log) -> dict:
+    """The other workloads of the hot-path table, each timed with HIP events:
+    one Single frame, the HexPlane deform + SH render, the Stress batch."""
+    import torch
+
+    out = {}
+    # Single: one frame, 100k Gaussians, decode + render
+    dec = S.single_decoder()
+    pos, t = S.single_positions(2)
+    x = torch.as_tensor(pos, device="cuda")
+    D, R = Decoder(dec), Renderer()
+    a = D.decode(x, t)
+    cam = S.ring_camera(0)
+    res = R.render(dict(means=x, **a), [0, x.shape[0]], [cam], 8 * x.shape[0], aux=True)
+    cap = Renderer.count_entries(res) + 4096
+    ms = timed(lambda: (D.decode(x, t, out=a), R.render(dict(means=x, **a), [0, x.shape[0]], [cam], cap)), 20, stream)
+    out["single_frame"] = {"gaussians": int(x.shape[0]), "ms": round(ms, 4), "fps": round(1e3 / ms, 1)}
+    # HexPlane: 300k canonical Gaussians, deform at t = 0.5, SH render at 1352x1014
+    hp = S.hexplane_params()
+    cg = S.hexplane_canonical()
+    canon = {k: torch.as_tensor(getattr(cg, k), device="cuda") for k in ("means", "scales", "quats", "sh", "opacity")}
+    H = HexPlane(hp)
+    d = H.deform(canon, 0.5)
+    hcam = S.hexplane_camera()
+    res = R.render(d, [0, cg.n], [hcam], 8 * cg.n, aux=True)
+    hcap = Renderer.count_entries(res) + 4096
+    ms_def = timed(lambda: H.deform(canon, 0.5, out=d), 10, stream)
+    ms_ren = timed(lambda: R.render(d, [0, cg.n], [hcam], hcap), 10, stream)
+    tflops = HEX_FLOP_PER_GAUSSIAN * cg.n / (ms_def / 1e3) / 1e12
+    out["hexplane"] = {"gaussians": cg.n, "deform_ms": round(ms_def, 4), "render_ms": round(ms_ren, 4),
+                       "fps": round(1e3 / (ms_def + ms_ren), 1), "mlp_tflops": round(tflops, 1),
+                       "mlp_frac_of_fp16_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    del d, res, canon, H
+    # Stress: 8 frames x 1M at 1920x1080 (drawn attributes) + decode of the same 8M positions
+    g, fo, cams, ts = S.stress_scene()
+    attrs = {k: torch.as_tensor(getattr(g, k), device="cuda") for k in ("means", "scales", "quats", "colors",
+                                                                         "opacity")}
+    Rs = Renderer()
+    res = Rs.render(attrs, fo, cams, 4 * g.n, aux=True)
+    E = Renderer.count_entries(res)
+    del res
+    res = Rs.render(attrs, fo, cams, E + 4096)
+    ms_r = timed(lambda: Rs.render(attrs, fo, cams, E + 4096, out=res), 2, stream)
+    xyzt = torch.cat([attrs["means"], torch.as_tensor(np.repeat(np.float32(ts), g.n // len(ts)),
+                                                      device="cuda")[:, None]], 1).contiguous()
+    da = D.decode_xyzt(xyzt)
+    ms_d = timed(lambda: D.decode_xyzt(xyzt, out=da), 3, stream)
+    out["stress"] = {"frames": len(cams), "gaussians": g.n, "tile_entries": E, "render_ms": round(ms_r, 3),
+                     "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3)}
+    log(f"secondary: {out}")
+    return out
+
+
 def timed(fn, reps, stream):
     import torch
 
@@ -87,7 +144,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--frames", type=int, default=150)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the per-frame comparison")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-frame comparison and the other workloads (Single, HexPlane, Stress)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (a reference for HBM byte counters)")
     args = ap.parse_args()
@@ -99,7 +157,7 @@ def main():
     import torch
 
     from implicit_attribute_decode_amd import ia, scenes as S
-    from implicit_attribute_decode_amd.pipeline import Decoder, Renderer
+    from implicit_attribute_decode_amd.pipeline import Decoder, HexPlane, Renderer
 
     ia.load()  # fails loudly when the HIP library is missing
     dev = "cuda"
@@ -176,6 +234,8 @@ def main():
         frame_pass()
         extra["per_frame_mode_fps"] = round(F / (timed(frame_pass, 1, stream) / 1e3), 2)
         log(f"per-frame mode {extra['per_frame_mode_fps']} fps")
+        del Rf
+        extra["secondary"] = secondary(S, Decoder, HexPlane, Renderer, stream, log)
 
     fps = F / (ms_step / 1e3)
     result = {
