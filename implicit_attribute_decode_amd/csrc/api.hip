@@ -488,9 +488,7 @@ ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t
     a.n_contrib = aux ? aux->n_contrib : nullptr;
     a.n_entries_out = aux ? aux->n_entries : nullptr;
     a.overflow_out = aux ? aux->overflow : nullptr;
-    int tile_bits = 1;
-    while (((int64_t)1 << tile_bits) < a.lay.ntiles_all) ++tile_bits;
-    a.sort_passes = (32 + tile_bits + 7) / 8;
+    a.unpack = aux != nullptr;
     const uint64_t* keys = nullptr;
     const uint32_t* vals = nullptr;
     hipError_t e = ia::launch_render(a, (hipStream_t)stream, &keys, &vals);

@@ -112,10 +112,11 @@ struct DevCamera {
 
 // Byte offsets of every buffer inside the render workspace.
 struct RenderLayout {
-    size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum2, boff, keys0, keys1, vals0, vals1,
-        counts, digit_tot, ranges, nent, total;
+    size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum2, boff, gk0, gk1, ent0, ent1, avals, counts,
+        digit_tot, ranges, nent, nvis, total;
     int64_t N, cap, ntiles_all;
-    int frames, tiles_x, tiles_y, nb1, nb2, sort_blocks;
+    int frames, tiles_x, tiles_y, nb1, nb2;
+    int sort_blocks_g, sort_blocks_e;  // radix-sort blocks over Gaussians / over entries
 };
 
 RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entries);
@@ -139,11 +140,11 @@ struct RenderArgs {
     uint32_t* n_contrib;
     uint64_t* n_entries_out;
     uint32_t* overflow_out;
-    int sort_passes;  // number of 8-bit LSD passes over the key
+    int unpack;  // write the sorted (tile << 32 | depth bits) keys and index values for inspection
 };
 
-// Enqueue the whole render.  Returns the pointers of the final sorted key /
-// value buffers through keys_out / vals_out.
+// Enqueue the whole render.  With unpack set, returns the sorted keys and
+// values through keys_out / vals_out (else both are null).
 hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** keys_out, const uint32_t** vals_out);
 
 }  // namespace ia

@@ -5,16 +5,20 @@
 //
 // Pipeline for a batch of frames (all kernels on one stream, no host sync):
 //   preprocess  one thread per Gaussian: project, cull, conic, 3-sigma tile
-//               rect, tiles touched; per-block sum of tiles touched
-//   scan        two-level exclusive prefix sum of the block sums; the total
-//               entry count stays in device memory
+//               rect, tiles touched; per-block count of visible Gaussians
+//   order       visible Gaussians compacted in index order and radix-sorted
+//               (stable, 8-bit digits) on their 31 depth bits
+//   scan        two-level exclusive prefix sum of the tiles touched, in that
+//               depth order; the total entry count stays in device memory
 //   emit        each block spreads its Gaussians' entries over all its
-//               threads: key = (frame*tiles + tile) << 32 | depth bits,
-//               value = Gaussian index, written in emission order
-//   sort        stable LSD radix sort, 8-bit digits, only over the key bits
-//               that can be non-zero (32 depth bits + tile-index bits); per
-//               pass: per-block digit histograms, a per-digit scan over
-//               blocks, and a stable scatter ranked by wave ballots
+//               threads: (frame*tiles + tile) << 32 | Gaussian index, in
+//               depth order
+//   sort        stable LSD radix sort of the entries on the tile bits only,
+//               digits of up to 10 bits; per pass: per-block digit
+//               histograms, a per-digit scan over blocks, and a stable
+//               scatter ranked by wave ballots.  Because the input is in
+//               (depth, index) order, the result is ordered by the key
+//               (tile << 32 | depth bits) with ties in index order
 //   ranges      [start, end) of every tile in the sorted list
 //   raster      one 256-thread block per tile; Gaussians staged through LDS
 //               in batches of 256; per pixel the 3-sigma test, alpha =
@@ -305,8 +309,8 @@ __global__ void __launch_bounds__(kBlock) preprocess_kernel(PreArgs a) {
         a.tiles[i] = ntouch;
     }
     uint32_t total;
-    block_excl_scan<uint32_t>(ntouch, total);
-    if (threadIdx.x == 0) a.bsum[blockIdx.x] = total;
+    block_excl_scan<uint32_t>(ntouch > 0 ? 1u : 0u, total);
+    if (threadIdx.x == 0) a.bsum[blockIdx.x] = total;  // visible Gaussians of the block
 }
 
 // ---------------------------------------------------------------- scan of block sums
@@ -358,34 +362,60 @@ __global__ void __launch_bounds__(kBlock) scan_down_kernel(const uint32_t* bsum,
     }
 }
 
+// ---------------------------------------------------------------- depth order of the visible Gaussians
+
+// Visible Gaussians (tiles touched > 0) of block b land at boff[b] + their
+// rank in the block, as the word depth_bits << 32 | index.  Depth is > 0, so
+// its bit pattern orders like the float and bit 63 stays clear.
+__global__ void __launch_bounds__(kBlock) compact_kernel(const uint32_t* tiles, const float* depth, int64_t N,
+                                                         const uint64_t* boff, uint64_t* gkeys) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const bool vis = i < N && tiles[i] > 0;
+    uint32_t total;
+    const uint32_t ex = block_excl_scan<uint32_t>(vis ? 1u : 0u, total);
+    if (vis) gkeys[boff[blockIdx.x] + ex] = ((uint64_t)__float_as_uint(depth[i]) << 32) | (uint32_t)i;
+}
+
+// Per block of 256 depth-ordered Gaussians: the tiles they touch.
+__global__ void __launch_bounds__(kBlock) sorted_tiles_kernel(const uint64_t* gkeys, const uint64_t* nvis,
+                                                              const uint32_t* tiles, uint32_t* bsum) {
+    const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint32_t n = j < nvis[0] ? tiles[(uint32_t)gkeys[j]] : 0u;
+    uint32_t total;
+    block_excl_scan<uint32_t>(n, total);
+    if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
 // ---------------------------------------------------------------- key emission
 
 struct EmitArgs {
+    const uint64_t* gkeys;  // depth-ordered visible Gaussians (index in the low word)
+    const uint64_t* nvis;
     const uint32_t* tiles;
     const ushort4* rect;
-    const float* depth;
-    const uint64_t* boff;
+    const uint64_t* boff;   // per block: first entry
     const int64_t* fo;
     int F;
-    int64_t N;
     int tiles_x;
     uint32_t ntiles;
     uint64_t cap;
-    uint64_t* keys;
-    uint32_t* vals;
+    uint64_t* ents;  // (frame*tiles + tile) << 32 | Gaussian index
 };
 
+// Entries are written in depth order of their Gaussians; each block spreads
+// the entries of its 256 Gaussians over all its threads.
 __global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
     __shared__ uint32_t s_off[kBlock + 1];
     __shared__ ushort4 s_rect[kBlock];
-    __shared__ uint32_t s_dbits[kBlock];
+    __shared__ uint32_t s_idx[kBlock];
     __shared__ uint32_t s_tbase[kBlock];  // frame * ntiles
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
     uint32_t n = 0;
-    if (i < a.N) {
+    if (j < a.nvis[0]) {
+        const uint32_t i = (uint32_t)a.gkeys[j];
         n = a.tiles[i];
         s_rect[threadIdx.x] = a.rect[i];
-        s_dbits[threadIdx.x] = __float_as_uint(a.depth[i]);
+        s_idx[threadIdx.x] = i;
         s_tbase[threadIdx.x] = (uint32_t)frame_of(a.fo, a.F, i) * a.ntiles;
     }
     uint32_t total;
@@ -395,7 +425,7 @@ __global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
     __syncthreads();
     const uint64_t base = a.boff[blockIdx.x];
     for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
-        // owner: last j with s_off[j] <= e (entries of culled Gaussians are empty)
+        // owner: last k with s_off[k] <= e (every listed Gaussian has >= 1 entry)
         int lo = 0, hi = kBlock - 1;
         while (lo < hi) {
             int mid = (lo + hi + 1) >> 1;
@@ -410,30 +440,31 @@ __global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
         const uint32_t ty = rc.y + k / w, tx = rc.x + k % w;
         const uint64_t tile = (uint64_t)(s_tbase[lo] + ty * (uint32_t)a.tiles_x + tx);
         const uint64_t pos = base + e;
-        if (pos < a.cap) {
-            a.keys[pos] = (tile << 32) | s_dbits[lo];
-            a.vals[pos] = (uint32_t)((int64_t)blockIdx.x * kBlock + lo);
-        }
+        if (pos < a.cap) a.ents[pos] = (tile << 32) | s_idx[lo];
     }
 }
 
 // ---------------------------------------------------------------- radix sort
 
+// One stable LSD pass over 64-bit words on the digit (word >> shift) &
+// (2^bits - 1), bits <= 10.  Items: the first min(*count, cap) words.
+constexpr int kMaxDigitBits = 10;
+constexpr int kMaxBuckets = 1 << kMaxDigitBits;
+
 struct SortPass {
-    const uint64_t* keys_in;
-    const uint32_t* vals_in;
-    uint64_t* keys_out;
-    uint32_t* vals_out;
-    const uint64_t* nent;  // [0] = entries emitted
+    const uint64_t* in;
+    uint64_t* out;
+    const uint64_t* count;
     uint64_t cap;
     int shift;
+    int bits;
     int nblocks;
-    uint32_t* counts;     // [256][nblocks]
-    uint32_t* digit_tot;  // [256]
+    uint32_t* counts;     // [buckets][nblocks]
+    uint32_t* digit_tot;  // [buckets]
 };
 
 __device__ __forceinline__ void sort_chunk(const SortPass& p, uint32_t& begin, uint32_t& end) {
-    uint64_t E = p.nent[0];
+    uint64_t E = p.count[0];
     if (E > p.cap) E = p.cap;
     uint64_t per = (E + p.nblocks - 1) / p.nblocks;
     per = (per + kSortTile - 1) / kSortTile * kSortTile;
@@ -445,19 +476,21 @@ __device__ __forceinline__ void sort_chunk(const SortPass& p, uint32_t& begin, u
 }
 
 __global__ void __launch_bounds__(kBlock) sort_upsweep_kernel(SortPass p) {
-    __shared__ uint32_t hist[4][256];
+    __shared__ uint32_t hist[4 * kMaxBuckets];  // per-wave histograms, [4][nb] flat
     const int w = threadIdx.x >> 6;
-    for (int k = threadIdx.x; k < 4 * 256; k += kBlock) (&hist[0][0])[k] = 0;
+    const int nb = 1 << p.bits;
+    const uint32_t mask = (uint32_t)nb - 1u;
+    for (int k = threadIdx.x; k < 4 * nb; k += kBlock) hist[k] = 0;
     __syncthreads();
     uint32_t begin, end;
     sort_chunk(p, begin, end);
     for (uint32_t idx = begin + threadIdx.x; idx < end; idx += kBlock) {
-        uint32_t d = (uint32_t)(p.keys_in[idx] >> p.shift) & 255u;
-        atomicAdd(&hist[w][d], 1u);
+        const uint32_t d = (uint32_t)(p.in[idx] >> p.shift) & mask;
+        atomicAdd(&hist[w * nb + d], 1u);
     }
     __syncthreads();
-    const int d = threadIdx.x;
-    p.counts[d * p.nblocks + blockIdx.x] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+    for (int d = threadIdx.x; d < nb; d += kBlock)
+        p.counts[d * p.nblocks + blockIdx.x] = hist[d] + hist[nb + d] + hist[2 * nb + d] + hist[3 * nb + d];
 }
 
 // One block per digit: exclusive scan of that digit's counts over blocks.
@@ -477,69 +510,93 @@ __global__ void __launch_bounds__(kBlock) sort_scan_kernel(SortPass p) {
 
 // Stable scatter.  Sort tile = 4 waves x 8 steps x 64 lanes, item order
 // wave-major then step then lane (the chunk order).  Per step each lane finds
-// the lanes holding the same digit with eight ballots; its rank is the count
-// of such lanes below it plus the wave's running count for the digit.
+// the lanes holding the same digit with one ballot per digit bit; its rank is
+// the count of such lanes below it plus the wave's running count for the digit.
 __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
-    __shared__ uint32_t s_base[256];
-    __shared__ uint32_t s_wc[4][256];
+    __shared__ uint32_t s_base[kMaxBuckets];
+    __shared__ uint4 s_wc4[kMaxBuckets];  // per-wave counters, [4][nb] flat
+    uint32_t* s_wc = reinterpret_cast<uint32_t*>(s_wc4);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nb = 1 << p.bits;
+    const uint32_t mask = (uint32_t)nb - 1u;
     {
-        uint32_t v = p.digit_tot[threadIdx.x];
+        // digit base = exclusive scan of digit totals + this block's offset;
+        // each thread takes kMaxBuckets / kBlock consecutive digits
+        constexpr int kPer = kMaxBuckets / kBlock;
+        const int d0 = threadIdx.x * kPer;
+        uint32_t v[kPer], sum = 0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            v[k] = d0 + k < nb ? p.digit_tot[d0 + k] : 0u;
+            sum += v[k];
+        }
         uint32_t total;
-        uint32_t ex = block_excl_scan<uint32_t>(v, total);
-        s_base[threadIdx.x] = ex + p.counts[threadIdx.x * p.nblocks + blockIdx.x];
+        uint32_t run = block_excl_scan<uint32_t>(sum, total);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            if (d0 + k < nb) s_base[d0 + k] = run + p.counts[(d0 + k) * p.nblocks + blockIdx.x];
+            run += v[k];
+        }
     }
     uint32_t begin, end;
     sort_chunk(p, begin, end);
-    const uint64_t end_all = p.nent[0] < p.cap ? p.nent[0] : p.cap;  // bound on every destination
+    const uint64_t end_all = p.count[0] < p.cap ? p.count[0] : p.cap;  // bound on every destination
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (uint32_t tile = begin; tile < end; tile += kSortTile) {
-        for (int k = threadIdx.x; k < 4 * 256; k += kBlock) (&s_wc[0][0])[k] = 0;
+        for (int k = threadIdx.x; k < nb; k += kBlock) s_wc4[k] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
         uint64_t key[kSortItems];
-        uint32_t val[kSortItems], dig[kSortItems], rank[kSortItems];
+        uint32_t dig[kSortItems], rank[kSortItems];
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             const uint32_t idx = tile + w * (64 * kSortItems) + j * 64 + lane;
             const bool valid = idx < end;
-            key[j] = valid ? p.keys_in[idx] : 0ull;
-            val[j] = valid ? p.vals_in[idx] : 0u;
-            const uint32_t d = (uint32_t)(key[j] >> p.shift) & 255u;
-            dig[j] = valid ? d : 256u;
+            key[j] = valid ? p.in[idx] : 0ull;
+            const uint32_t d = (uint32_t)(key[j] >> p.shift) & mask;
+            dig[j] = valid ? d : 0xffffffffu;
             uint64_t peers = __ballot(valid);
-#pragma unroll
-            for (int bit = 0; bit < 8; ++bit) {
+            for (int bit = 0; bit < p.bits; ++bit) {
                 const uint64_t b = __ballot((d >> bit) & 1u);
                 peers &= ((d >> bit) & 1u) ? b : ~b;
             }
             uint32_t prior = 0;
-            if (valid) prior = s_wc[w][d];
+            if (valid) prior = s_wc[w * nb + d];
             const uint32_t below = (uint32_t)__popcll(peers & lt_mask);
             // the lowest lane of each peer group advances the wave's counter
-            if (valid && below == 0) s_wc[w][d] = prior + (uint32_t)__popcll(peers);
+            if (valid && below == 0) s_wc[w * nb + d] = prior + (uint32_t)__popcll(peers);
             rank[j] = prior + below;
         }
         __syncthreads();
         // per digit: offsets of each wave inside this tile
-        {
-            const int d = threadIdx.x;
-            uint32_t c0 = s_wc[0][d], c1 = s_wc[1][d], c2 = s_wc[2][d], c3 = s_wc[3][d];
-            s_wc[0][d] = s_base[d];
-            s_wc[1][d] = s_base[d] + c0;
-            s_wc[2][d] = s_base[d] + c0 + c1;
-            s_wc[3][d] = s_base[d] + c0 + c1 + c2;
+        for (int d = threadIdx.x; d < nb; d += kBlock) {
+            uint32_t c0 = s_wc[d], c1 = s_wc[nb + d], c2 = s_wc[2 * nb + d], c3 = s_wc[3 * nb + d];
+            s_wc[d] = s_base[d];
+            s_wc[nb + d] = s_base[d] + c0;
+            s_wc[2 * nb + d] = s_base[d] + c0 + c1;
+            s_wc[3 * nb + d] = s_base[d] + c0 + c1 + c2;
             s_base[d] += c0 + c1 + c2 + c3;
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
-            const uint32_t dst = dig[j] < 256u ? s_wc[w][dig[j]] + rank[j] : 0xffffffffu;
-            if (dst < end_all) {
-                p.keys_out[dst] = key[j];
-                p.vals_out[dst] = val[j];
-            }
+            const uint32_t dst = dig[j] <= mask ? s_wc[w * nb + dig[j]] + rank[j] : 0xffffffffu;
+            if (dst < end_all) p.out[dst] = key[j];
         }
         __syncthreads();
+    }
+}
+
+// Sorted entries as (tile << 32 | depth bits) keys and Gaussian-index values.
+__global__ void unpack_kernel(const uint64_t* ents, const uint64_t* nent, uint64_t cap, const float* depth,
+                              int64_t N, uint64_t* keys, uint32_t* vals) {
+    uint64_t E = nent[0];
+    if (E > cap) E = cap;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < E; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t v = ents[i];
+        const uint32_t g = (uint32_t)v;
+        if ((int64_t)g >= N) continue;  // cannot happen for emitted entries
+        keys[i] = (v & 0xffffffff00000000ull) | __float_as_uint(depth[g]);
+        vals[i] = g;
     }
 }
 
@@ -561,7 +618,7 @@ __global__ void ranges_kernel(const uint64_t* keys, const uint64_t* nent, uint64
 
 struct RasterArgs {
     const uint2* ranges;
-    const uint32_t* vals;
+    const uint64_t* ents;  // sorted entries, Gaussian index in the low word
     const float4* pa;
     const float4* pb;
     const float* pc;
@@ -634,7 +691,7 @@ __global__ void __launch_bounds__(kRasterThreads) raster_kernel(RasterArgs a) {
             const uint32_t slot = threadIdx.x + k * kRasterThreads;
             const uint32_t idx = start + slot;
             if (idx < rg.y) {
-                uint32_t gid = a.vals[idx];
+                uint32_t gid = (uint32_t)a.ents[idx];
                 if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
                 const float4 pa = a.pa[gid], pb = a.pb[gid];
                 s_a[slot] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
@@ -700,8 +757,12 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     const int64_t n1 = N > 0 ? N : 1;
     L.nb1 = (int)((n1 + kBlock - 1) / kBlock);
     L.nb2 = (L.nb1 + kScanChunk - 1) / kScanChunk;
-    int64_t sb = (max_entries + kSortTile - 1) / kSortTile;
-    L.sort_blocks = (int)(sb < 1 ? 1 : (sb > 1024 ? 1024 : sb));
+    auto blocks = [](int64_t items) {
+        int64_t b = (items + kSortTile - 1) / kSortTile;
+        return (int)(b < 1 ? 1 : (b > 1024 ? 1024 : b));
+    };
+    L.sort_blocks_g = blocks(n1);
+    L.sort_blocks_e = blocks(max_entries);
     const int64_t cap1 = max_entries > 0 ? max_entries : 1;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -720,14 +781,17 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     L.bsum = take(4 * (size_t)L.nb1);
     L.bsum2 = take(8 * (size_t)L.nb2);
     L.boff = take(8 * (size_t)L.nb1);
-    L.keys0 = take(8 * (size_t)cap1);
-    L.keys1 = take(8 * (size_t)cap1);
-    L.vals0 = take(4 * (size_t)cap1);
-    L.vals1 = take(4 * (size_t)cap1);
-    L.counts = take(4 * 256 * (size_t)L.sort_blocks);
-    L.digit_tot = take(4 * 256);
+    L.gk0 = take(8 * (size_t)n1);
+    L.gk1 = take(8 * (size_t)n1);
+    L.ent0 = take(8 * (size_t)cap1);
+    L.ent1 = take(8 * (size_t)cap1);
+    L.avals = take(4 * (size_t)cap1);
+    L.counts = take(4 * (size_t)kMaxBuckets *
+                    (size_t)(L.sort_blocks_g > L.sort_blocks_e ? L.sort_blocks_g : L.sort_blocks_e));
+    L.digit_tot = take(4 * (size_t)kMaxBuckets);
     L.ranges = take(8 * (size_t)(L.ntiles_all > 0 ? L.ntiles_all : 1));
     L.nent = take(16);
+    L.nvis = take(16);
     L.total = off;
     return L;
 }
@@ -751,49 +815,83 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
     uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + L.bsum);
     uint64_t* bsum2 = reinterpret_cast<uint64_t*>(ws + L.bsum2);
     uint64_t* boff = reinterpret_cast<uint64_t*>(ws + L.boff);
-    uint64_t* keys[2] = {reinterpret_cast<uint64_t*>(ws + L.keys0), reinterpret_cast<uint64_t*>(ws + L.keys1)};
-    uint32_t* vals[2] = {reinterpret_cast<uint32_t*>(ws + L.vals0), reinterpret_cast<uint32_t*>(ws + L.vals1)};
+    uint64_t* gk[2] = {reinterpret_cast<uint64_t*>(ws + L.gk0), reinterpret_cast<uint64_t*>(ws + L.gk1)};
+    uint64_t* ent[2] = {reinterpret_cast<uint64_t*>(ws + L.ent0), reinterpret_cast<uint64_t*>(ws + L.ent1)};
     uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
     uint32_t* digit_tot = reinterpret_cast<uint32_t*>(ws + L.digit_tot);
     uint2* ranges = reinterpret_cast<uint2*>(ws + L.ranges);
     uint64_t* nent = reinterpret_cast<uint64_t*>(ws + L.nent);
+    uint64_t* nvis = reinterpret_cast<uint64_t*>(ws + L.nvis);
     const int64_t N = L.N;
     const uint32_t ntiles = (uint32_t)(L.tiles_x * L.tiles_y);
 
+    // LSD passes over bits [lo, lo + nbits) of 64-bit words, digits of at most
+    // kMaxDigitBits bits; returns the buffer index holding the result.
+    auto radix = [&](uint64_t** buf, const uint64_t* count, uint64_t cap, int lo, int nbits, int nblocks) {
+        const int passes = (nbits + kMaxDigitBits - 1) / kMaxDigitBits;
+        const int bits = (nbits + passes - 1) / passes;
+        int cur = 0;
+        for (int pass = 0; pass < passes; ++pass) {
+            SortPass sp{buf[cur], buf[cur ^ 1], count, cap, lo + pass * bits, bits, nblocks, counts, digit_tot};
+            IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel, dim3(nblocks), dim3(kBlock), 0, s, sp);
+            IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
+            IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel, dim3(nblocks), dim3(kBlock), 0, s, sp);
+            cur ^= 1;
+        }
+        return cur;
+    };
+
+    int ecur = 0;
     if (N > 0) {
+        // projection; visible Gaussians per block
         PreArgs pre{a.means, a.means_stride, a.scales, a.quats, a.colors, a.sh, a.opacity, a.sh_degree,
                     cams, fo, a.frames, N, pa, pb, pc, depth, rect, tiles, bsum};
         IA_LAUNCH("preprocess_kernel", preprocess_kernel, dim3(L.nb1), dim3(kBlock), 0, s, pre);
         IA_LAUNCH("scan_reduce_kernel", scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
-    }
-    IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, N > 0 ? L.nb2 : 0, (uint64_t)L.cap, nent,
-                       a.n_entries_out, a.overflow_out);
-    if (N > 0) {
+        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, L.nb2, ~0ull, nvis,
+                  (uint64_t*)nullptr, (uint32_t*)nullptr);
         IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
-        EmitArgs em{tiles, rect, depth, boff, fo, a.frames, N, L.tiles_x, ntiles, (uint64_t)L.cap, keys[0], vals[0]};
+        // visible Gaussians in ascending depth, ties in index order (stable
+        // sort of index-ordered input on the 31 depth bits above the index)
+        IA_LAUNCH("compact_kernel", compact_kernel, dim3(L.nb1), dim3(kBlock), 0, s, tiles, depth, N, boff, gk[0]);
+        const int gcur = radix(gk, nvis, (uint64_t)N, 32, 31, L.sort_blocks_g);
+        // entry offsets in that order
+        IA_LAUNCH("sorted_tiles_kernel", sorted_tiles_kernel, dim3(L.nb1), dim3(kBlock), 0, s, gk[gcur], nvis, tiles,
+                  bsum);
+        IA_LAUNCH("scan_reduce_kernel", scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
+        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, L.nb2, (uint64_t)L.cap, nent,
+                  a.n_entries_out, a.overflow_out);
+        IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
+        EmitArgs em{gk[gcur], nvis, tiles, rect, boff, fo, a.frames, L.tiles_x, ntiles, (uint64_t)L.cap, ent[0]};
         IA_LAUNCH("emit_kernel", emit_kernel, dim3(L.nb1), dim3(kBlock), 0, s, em);
-    }
-    int cur = 0;
-    for (int pass = 0; pass < a.sort_passes; ++pass) {
-        SortPass sp{keys[cur], vals[cur], keys[cur ^ 1], vals[cur ^ 1], nent, (uint64_t)L.cap, 8 * pass,
-                    L.sort_blocks, counts, digit_tot};
-        IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
-        IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(256), dim3(kBlock), 0, s, sp);
-        IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel, dim3(L.sort_blocks), dim3(kBlock), 0, s, sp);
-        cur ^= 1;
+        // stable sort of the depth-ordered entries on the tile index gives
+        // the (tile, depth, Gaussian index) order
+        int tile_bits = 1;
+        while (((int64_t)1 << tile_bits) < L.ntiles_all) ++tile_bits;
+        ecur = radix(ent, nent, (uint64_t)L.cap, 32, tile_bits, L.sort_blocks_e);
+    } else {
+        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, 0, (uint64_t)L.cap, nent,
+                  a.n_entries_out, a.overflow_out);
     }
     const int64_t nr = 2 * L.ntiles_all;
     IA_LAUNCH("fill_u32_kernel", fill_u32_kernel, dim3(grid_cap(nr, kBlock, 4096)), dim3(kBlock), 0, s,
-                       reinterpret_cast<uint32_t*>(ranges), 0u, nr);
-    IA_LAUNCH("ranges_kernel", ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, keys[cur], nent,
-                       (uint64_t)L.cap, ranges, (uint32_t)L.ntiles_all);
-    RasterArgs ra{ranges, vals[cur], pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, (uint64_t)L.cap, N,
+              reinterpret_cast<uint32_t*>(ranges), 0u, nr);
+    IA_LAUNCH("ranges_kernel", ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, ent[ecur], nent,
+              (uint64_t)L.cap, ranges, (uint32_t)L.ntiles_all);
+    RasterArgs ra{ranges, ent[ecur], pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, (uint64_t)L.cap, N,
                   a.image, a.T_final, a.n_contrib};
     IA_LAUNCH("raster_kernel", raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kRasterThreads), 0, s, ra);
-    e = hipGetLastError();
-    *keys_out = keys[cur];
-    *vals_out = vals[cur];
-    return e;
+    *keys_out = nullptr;
+    *vals_out = nullptr;
+    if (a.unpack) {
+        uint64_t* keys = ent[ecur ^ 1];
+        uint32_t* vals = reinterpret_cast<uint32_t*>(ws + L.avals);
+        IA_LAUNCH("unpack_kernel", unpack_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, ent[ecur],
+                  nent, (uint64_t)L.cap, depth, N, keys, vals);
+        *keys_out = keys;
+        *vals_out = vals;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace ia

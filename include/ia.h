@@ -205,7 +205,8 @@ typedef struct {
     uint64_t* n_entries; /* device [1] tile entries emitted (true count), or NULL */
     uint32_t* overflow;  /* device [1] 1 if n_entries > max_entries, or NULL       */
     /* views (written by ia_render) */
-    const uint64_t* sorted_keys;  /* [min(E,max_entries)] (tile<<32 | depth bits) */
+    const uint64_t* sorted_keys;  /* [min(E,max_entries)] (tile<<32 | depth bits);
+                                     written only when aux is given             */
     const uint32_t* sorted_vals;  /* [min(E,max_entries)] Gaussian index          */
     const uint32_t* tile_ranges;  /* [F*tiles][2] [start,end), empty = [0,0)      */
     const float* proj_a;          /* [N][4] u, v, conic A, conic B                */
@@ -228,9 +229,11 @@ IA_API ia_status ia_render_workspace_size(int64_t N_total, int32_t frames, int32
  *   cams: host [frames].  Both host arrays may be freed on return.
  *   ws: device workspace of ws_bytes >= ia_render_workspace_size(...).
  *   image: device [frames,3,H,W] = C + T_final * bg.
- * Steps: EWA projection -> tiles touched -> prefix sum -> one key per
- * (Gaussian, tile) = (frame*tiles + tile) << 32 | depth bits -> stable LSD
- * radix sort -> per-tile ranges -> front-to-back compositing per pixel with
+ * Steps: EWA projection -> tiles touched -> one entry per (Gaussian, tile),
+ * ordered by the key (frame*tiles + tile) << 32 | depth bits with ties in
+ * Gaussian-index order (stable radix sort of the visible Gaussians on depth,
+ * then of the entries on the tile) -> per-tile ranges -> front-to-back
+ * compositing per pixel with
  * a 3-sigma cutoff, alpha = min(0.99, o G), skip alpha < 1/255, stop once
  * T < 1e-4.  No host synchronisation: if more than max_entries entries are
  * needed, the surplus is dropped, aux->overflow is set to 1 and
