@@ -98,11 +98,13 @@ def secondary(S, Decoder, HexPlane, Renderer, stream, log) -> dict:
     res = R.render(d, [0, cg.n], [hcam], 8 * cg.n, aux=True)
     hcap = Renderer.count_entries(res) + 4096
     ms_def = timed(lambda: H.deform(canon, 0.5, out=d), 10, stream)
+    hex_kernels = profiled(lambda: H.deform(canon, 0.5, out=d), 3)
     ms_ren = timed(lambda: R.render(d, [0, cg.n], [hcam], hcap), 10, stream)
     tflops = HEX_FLOP_PER_GAUSSIAN * cg.n / (ms_def / 1e3) / 1e12
     out["hexplane"] = {"gaussians": cg.n, "deform_ms": round(ms_def, 4), "render_ms": round(ms_ren, 4),
                        "fps": round(1e3 / (ms_def + ms_ren), 1), "mlp_tflops": round(tflops, 1),
-                       "mlp_frac_of_fp16_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+                       "mlp_frac_of_fp16_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                       "deform_kernels_ms": hex_kernels}
     del d, res, canon, H
     # Stress: 8 frames x 1M at 1920x1080 (drawn attributes) + decode of the same 8M positions
     g, fo, cams, ts = S.stress_scene()
@@ -114,14 +116,34 @@ def secondary(S, Decoder, HexPlane, Renderer, stream, log) -> dict:
     del res
     res = Rs.render(attrs, fo, cams, E + 4096)
     ms_r = timed(lambda: Rs.render(attrs, fo, cams, E + 4096, out=res), 2, stream)
+    stress_kernels = profiled(lambda: Rs.render(attrs, fo, cams, E + 4096, out=res), 1)
     xyzt = torch.cat([attrs["means"], torch.as_tensor(np.repeat(np.float32(ts), g.n // len(ts)),
                                                       device="cuda")[:, None]], 1).contiguous()
     da = D.decode_xyzt(xyzt)
     ms_d = timed(lambda: D.decode_xyzt(xyzt, out=da), 3, stream)
     out["stress"] = {"frames": len(cams), "gaussians": g.n, "tile_entries": E, "render_ms": round(ms_r, 3),
-                     "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3)}
+                     "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3),
+                     "render_kernels_ms": stress_kernels}
     log(f"secondary: {out}")
     return out
+
+
+def profiled(fn, reps):
+    """Milliseconds per call of each library kernel over `reps` calls of fn
+    (HIP events around every launch), largest first."""
+    import torch
+
+    from implicit_attribute_decode_amd import ia
+
+    torch.cuda.synchronize()
+    ia.ia_profile_reset()
+    ia.ia_profile_enable(True)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    prof = ia.ia_profile_report()
+    ia.ia_profile_enable(False)
+    return {k: round(v[1] / reps, 4) for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
 
 
 def timed(fn, reps, stream):

@@ -274,6 +274,7 @@ struct ia_hexplane {
     void* planes[6] = {};
     void* W[3] = {};
     float* b[3] = {};
+    void* Wt = nullptr;  // weights in the deformation kernel's A-tile order
     bool ready = false;
 };
 
@@ -290,6 +291,8 @@ void free_hex(ia_hexplane* h) {
         h->W[k] = nullptr;
         h->b[k] = nullptr;
     }
+    if (h->Wt) (void)hipFree(h->Wt);
+    h->Wt = nullptr;
     h->ready = false;
 }
 
@@ -335,6 +338,17 @@ ia_status ia_hexplane_set_params(ia_hexplane* hp, const void* const* planes, con
         st = upload_param(&hp->W[k], weights[k], (size_t)dims[k + 1] * dims[k] * 2, dev, s);
         if (st == IA_OK) st = upload_param(reinterpret_cast<void**>(&hp->b[k]), biases[k], 4 * (size_t)dims[k + 1], dev, s);
     }
+    if (st == IA_OK) {
+        hipError_t e = hipMalloc(&hp->Wt, ia::kHexTiledWeightBytes);
+        if (e != hipSuccess) {
+            hp->Wt = nullptr;
+            st = hip_fail(e, "hipMalloc");
+        } else {
+            const _Float16* W[3] = {(const _Float16*)hp->W[0], (const _Float16*)hp->W[1], (const _Float16*)hp->W[2]};
+            e = ia::launch_hexplane_tiles(W, hp->Wt, s);
+            if (e != hipSuccess) st = hip_fail(e, "hexplane weight tiling");
+        }
+    }
     if (st != IA_OK) {
         free_hex(hp);
         return st;
@@ -379,7 +393,7 @@ ia_status ia_hexplane_deform(const ia_hexplane* hp, const ia_gaussians* cn, int6
     a.o_quats = out->quats;
     a.o_sh = out->sh;
     a.o_opacity = out->opacity;
-    hipError_t e = ia::launch_hexplane(a, (hipStream_t)stream);
+    hipError_t e = ia::launch_hexplane(a, hp->Wt, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "hexplane launch");
     return IA_OK;
 }

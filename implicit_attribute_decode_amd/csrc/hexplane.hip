@@ -26,20 +26,45 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kG = 2;  // 16-Gaussian column blocks per wave
-
 __device__ __forceinline__ half4_t ld4(const _Float16* p) { return *reinterpret_cast<const half4_t*>(p); }
 
 __device__ __forceinline__ half8_t cat8(half4_t lo, half4_t hi) {
     return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// A tile of a row-major [out][in] weight matrix: rows 16 rb + c, k-block m.
-__device__ __forceinline__ half8_t a_tile(const _Float16* W, int in_dim, int rows, int rb, int m, int q, int c) {
+constexpr int kG = 3;         // 16-Gaussian column groups per wave
+constexpr int kTileHalf8 = 64;  // one A tile = 64 lanes x 8 fp16 = 1 KiB
+
+// Tiled weight buffer (built once per parameter set): A tiles of the three
+// layers in the order the kernel streams them through LDS.
+//   layer 1: tile (rb, m), rb in 0..15, m in 0..5, at rb * 6 + m
+//   layer 2: tile (rb, m), rb in 0..15, m in 0..7, at 96 + rb * 8 + m
+//   layer 3: tile (m, rb), m in 0..7, rb in 0..3 (rows >= 58 zero), at 224 + m * 4 + rb
+// Tile content: lane (q, c) holds row 16 rb + c at the k-slots of block m.
+constexpr int kL1Tiles = 96, kL2Tiles = 128, kL3Tiles = 32;
+constexpr int kTiles = kL1Tiles + kL2Tiles + kL3Tiles;
+
+__global__ void tile_weights_kernel(const _Float16* W1, const _Float16* W2, const _Float16* W3, half8_t* Wt) {
+    const int tile = blockIdx.x, lane = threadIdx.x;
+    const int q = lane >> 4, c = lane & 15;
+    const _Float16* W;
+    int in_dim, rows, rb, m;
+    if (tile < kL1Tiles) {
+        W = W1, in_dim = 192, rows = 256, rb = tile / 6, m = tile % 6;
+    } else if (tile < kL1Tiles + kL2Tiles) {
+        const int t = tile - kL1Tiles;
+        W = W2, in_dim = 256, rows = 256, rb = t / 8, m = t % 8;
+    } else {
+        const int t = tile - kL1Tiles - kL2Tiles;
+        W = W3, in_dim = 256, rows = 58, m = t / 4, rb = t % 4;
+    }
     const int row = 16 * rb + c;
-    if (row >= rows) return half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    const _Float16* r = W + (size_t)row * in_dim + 32 * m + 4 * q;
-    return cat8(ld4(r), ld4(r + 16));
+    half8_t v = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    if (row < rows) {
+        const _Float16* r = W + (size_t)row * in_dim + 32 * m + 4 * q;
+        v = cat8(ld4(r), ld4(r + 16));
+    }
+    Wt[tile * kTileHalf8 + lane] = v;
 }
 
 __device__ __forceinline__ void axis_cell(float u, int res, int& i, float& f) {
@@ -50,192 +75,227 @@ __device__ __forceinline__ void axis_cell(float u, int res, int& i, float& f) {
     f = p - (float)c;
 }
 
-__global__ void __launch_bounds__(256, 2) hexplane_kernel(HexArgs a) {
+// Copy tiles [first, first + n) of the tiled weights into s[0, n) (all threads).
+__device__ __forceinline__ void stage_tiles(half8_t* s, const half8_t* Wt, int first, int n) {
+    for (int k = threadIdx.x; k < n * kTileHalf8; k += 256) s[k] = Wt[first * kTileHalf8 + k];
+}
+
+// One block = 4 waves x 64 Gaussians.  The weights pass through LDS in
+// chunks of four row blocks (layer 1: 24 tiles; layer 2: 32 tiles plus the
+// 8 layer-3 tiles that consume those rows), so each 1 KiB A tile read from
+// LDS feeds kG MFMAs.  Features, hidden layers and accumulators stay in
+// registers; two blocks per CU overlap one block's staging with the other's
+// MFMAs.
+__global__ void __launch_bounds__(256, 2) hexplane_kernel(HexArgs a, const half8_t* Wt) {
 #pragma clang fp contract(fast)
+    __shared__ half8_t s_w[40 * kTileHalf8];
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, c = lane & 15;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 * kG;
     const int C = 32;
     const float t = a.t < 0.0f ? 0.0f : (a.t > 1.0f ? 1.0f : a.t);
-    __shared__ half8_t s_h1[4 * 8 * kG * 64];
 
-    for (int64_t base = wave * 16 * kG; base < a.N; base += nwaves * 16 * kG) {
-        // ---- six bilinear plane lookups -> layer-1 B operand
-        half8_t X[6][kG];
+    // ---- six bilinear plane lookups -> layer-1 B operand
+    half8_t X[6][kG];
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            int64_t gi = base + 16 * g + c;
-            if (gi >= a.N) gi = a.N - 1;
-            float u[4];
+    for (int g = 0; g < kG; ++g) {
+        int64_t gi = base + 16 * g + c;
+        if (gi >= a.N) gi = a.N - 1;
+        float u[4];
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                float v = a.means[gi * 3 + k] + a.aabb;
-                v = v / (2.0f * a.aabb);
-                u[k] = v < 0.0f ? 0.0f : (v > 1.0f ? 1.0f : v);
-            }
-            u[3] = t;
-#pragma unroll
-            for (int p = 0; p < 6; ++p) {
-                const int ax = p == 2 ? 1 : (p == 4 ? 1 : (p == 5 ? 2 : 0));
-                const int bx = p == 0 ? 1 : (p == 1 || p == 2 ? 2 : 3);
-                const int ra = a.res_xyz, rb = bx == 3 ? a.res_t : a.res_xyz;
-                int ia, ib;
-                float fa, fb;
-                axis_cell(u[ax], ra, ia, fa);
-                axis_cell(u[bx], rb, ib, fb);
-                const _Float16* P = a.planes[p];
-                const _Float16* t00 = P + ((size_t)ib * ra + ia) * C + 4 * q;
-                const _Float16* t01 = t00 + C;
-                const _Float16* t10 = t00 + (size_t)ra * C;
-                const _Float16* t11 = t10 + C;
-                const float w00 = (1.0f - fa) * (1.0f - fb), w01 = fa * (1.0f - fb);
-                const float w10 = (1.0f - fa) * fb, w11 = fa * fb;
-                half8_t out;
-#pragma unroll
-                for (int hsel = 0; hsel < 2; ++hsel) {
-                    const int o = 16 * hsel;
-                    half4_t v00 = ld4(t00 + o), v01 = ld4(t01 + o), v10 = ld4(t10 + o), v11 = ld4(t11 + o);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float s = w00 * (float)v00[e] + w01 * (float)v01[e] + w10 * (float)v10[e] + w11 * (float)v11[e];
-                        out[4 * hsel + e] = (_Float16)s;
-                    }
-                }
-                X[p][g] = out;
-            }
+        for (int k = 0; k < 3; ++k) {
+            float v = a.means[gi * 3 + k] + a.aabb;
+            v = v / (2.0f * a.aabb);
+            u[k] = v < 0.0f ? 0.0f : (v > 1.0f ? 1.0f : v);
         }
-        // ---- layer 1: 192 -> 256, ReLU, fp16.  The hidden layer (eight
-        // 32-wide k-blocks of this lane's B operand) is kept in LDS so that
-        // the row-block loops need no dynamic register indexing.
-        half8_t* H1 = s_h1 + (threadIdx.x >> 6) * (8 * kG * 64);  // [m][g][lane]
-#pragma unroll 1
-        for (int rb = 0; rb < 16; ++rb) {
+        u[3] = t;
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+            const int ax = p == 2 ? 1 : (p == 4 ? 1 : (p == 5 ? 2 : 0));
+            const int bx = p == 0 ? 1 : (p == 1 || p == 2 ? 2 : 3);
+            const int ra = a.res_xyz, rb = bx == 3 ? a.res_t : a.res_xyz;
+            int ia, ib;
+            float fa, fb;
+            axis_cell(u[ax], ra, ia, fa);
+            axis_cell(u[bx], rb, ib, fb);
+            const _Float16* P = a.planes[p];
+            const _Float16* t00 = P + ((size_t)ib * ra + ia) * C + 4 * q;
+            const _Float16* t01 = t00 + C;
+            const _Float16* t10 = t00 + (size_t)ra * C;
+            const _Float16* t11 = t10 + C;
+            const float w00 = (1.0f - fa) * (1.0f - fb), w01 = fa * (1.0f - fb);
+            const float w10 = (1.0f - fa) * fb, w11 = fa * fb;
+            half8_t out;
+#pragma unroll
+            for (int hsel = 0; hsel < 2; ++hsel) {
+                const int o = 16 * hsel;
+                half4_t v00 = ld4(t00 + o), v01 = ld4(t01 + o), v10 = ld4(t10 + o), v11 = ld4(t11 + o);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float s = w00 * (float)v00[e] + w01 * (float)v01[e] + w10 * (float)v10[e] + w11 * (float)v11[e];
+                    out[4 * hsel + e] = (_Float16)s;
+                }
+            }
+            // materialise the interpolated features here: left to the
+            // compiler, the interpolation sinks to its first use and every
+            // plane's raw corner loads stay live across the staging barriers
+            asm volatile("" : "+v"(out));
+            X[p][g] = out;
+        }
+    }
+
+    // ---- layer 1: 192 -> 256, ReLU, fp16; H1[m][g] = k-block m of layer 2's B operand
+    half8_t H1[8][kG];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        __syncthreads();
+        stage_tiles(s_w, Wt, 24 * r, 24);
+        __syncthreads();
+#pragma unroll
+        for (int rbl = 0; rbl < 4; ++rbl) {
+            const int rb = 4 * r + rbl;
             floatx4 acc[kG];
 #pragma unroll
             for (int g = 0; g < kG; ++g) acc[g] = floatx4{0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < 6; ++m) {
-                const half8_t A = a_tile(a.W[0], 192, 256, rb, m, q, c);
+                const half8_t A = s_w[(rbl * 6 + m) * kTileHalf8 + lane];
 #pragma unroll
                 for (int g = 0; g < kG; ++g) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X[m][g], acc[g], 0, 0, 0);
             }
-            const int m2 = rb >> 1, hsel = rb & 1;
 #pragma unroll
-            for (int g = 0; g < kG; ++g) {
-                half8_t v8 = H1[(m2 * kG + g) * 64 + lane];
+            for (int g = 0; g < kG; ++g)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float v = acc[g][e] + a.b[0][16 * rb + 4 * q + e];
-                    const _Float16 hv = (_Float16)(v > 0.0f ? v : 0.0f);
-                    if (hsel) v8[4 + e] = hv; else v8[e] = hv;
+                    const float v = acc[g][e] + a.b[0][16 * rb + 4 * q + e];
+                    H1[rb >> 1][g][4 * (rb & 1) + e] = (_Float16)(v > 0.0f ? v : 0.0f);
                 }
-                H1[(m2 * kG + g) * 64 + lane] = v8;
-            }
+            // convert now (fp32 accumulators would otherwise stay live until
+            // layer 2) and keep later row blocks' loads from being hoisted
+#pragma unroll
+            for (int g = 0; g < kG; ++g) asm volatile("" : "+v"(H1[rb >> 1][g]));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // ---- layer 2 (256 -> 256, ReLU) streamed into layer 3 (256 -> 58)
-        floatx4 acc3[4][kG];
+    }
+
+    // ---- layer 2 (256 -> 256, ReLU) streamed into layer 3 (256 -> 58)
+    floatx4 acc3[4][kG];
 #pragma unroll
-        for (int r3 = 0; r3 < 4; ++r3)
+    for (int r3 = 0; r3 < 4; ++r3)
 #pragma unroll
-            for (int g = 0; g < kG; ++g) acc3[r3][g] = floatx4{0, 0, 0, 0};
-#pragma unroll 1
-        for (int m3 = 0; m3 < 8; ++m3) {
+        for (int g = 0; g < kG; ++g) acc3[r3][g] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        __syncthreads();
+        stage_tiles(s_w, Wt, kL1Tiles + 32 * r, 32);
+        stage_tiles(s_w + 32 * kTileHalf8, Wt, kL1Tiles + kL2Tiles + 8 * r, 8);
+        __syncthreads();
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
             half8_t H2[kG];
 #pragma unroll
             for (int hsel = 0; hsel < 2; ++hsel) {
-                const int rb = 2 * m3 + hsel;
+                const int rbl = 2 * half + hsel, rb = 4 * r + rbl;
                 floatx4 acc[kG];
 #pragma unroll
                 for (int g = 0; g < kG; ++g) acc[g] = floatx4{0, 0, 0, 0};
-#pragma unroll 2
+#pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    const half8_t A = a_tile(a.W[1], 256, 256, rb, m, q, c);
+                    const half8_t A = s_w[(rbl * 8 + m) * kTileHalf8 + lane];
 #pragma unroll
                     for (int g = 0; g < kG; ++g)
-                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, H1[(m * kG + g) * 64 + lane], acc[g], 0, 0, 0);
+                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, H1[m][g], acc[g], 0, 0, 0);
                 }
 #pragma unroll
                 for (int g = 0; g < kG; ++g)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float v = acc[g][e] + a.b[1][16 * rb + 4 * q + e];
+                        const float v = acc[g][e] + a.b[1][16 * rb + 4 * q + e];
                         H2[g][4 * hsel + e] = (_Float16)(v > 0.0f ? v : 0.0f);
                     }
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int r3 = 0; r3 < 4; ++r3) {
-                const half8_t A = a_tile(a.W[2], 256, 58, r3, m3, q, c);
+                const half8_t A = s_w[(32 + 4 * half + r3) * kTileHalf8 + lane];
 #pragma unroll
                 for (int g = 0; g < kG; ++g)
                     acc3[r3][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, H2[g], acc3[r3][g], 0, 0, 0);
             }
         }
-        // ---- apply the deltas: output o = 16 r3 + 4 q + e
+    }
+
+    // ---- apply the deltas: output o = 16 r3 + 4 q + e
 #pragma unroll
-        for (int g = 0; g < kG; ++g) {
-            const int64_t gi = base + 16 * g + c;
-            float d0[4];
+    for (int g = 0; g < kG; ++g) {
+        const int64_t gi = base + 16 * g + c;
+        float d0[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) d0[e] = acc3[0][g][e] + a.b[2][4 * q + e];
-            // quaternion: output 3 on q = 0 (e = 3), outputs 4..6 on q = 1 (e = 0..2)
-            const int64_t gq = gi < a.N ? gi : a.N - 1;
-            float qv[4];
+        for (int e = 0; e < 4; ++e) d0[e] = acc3[0][g][e] + a.b[2][4 * q + e];
+        // quaternion: output 3 on q = 0 (e = 3), outputs 4..6 on q = 1 (e = 0..2)
+        const int64_t gq = gi < a.N ? gi : a.N - 1;
+        float qv[4];
+        if (q == 0) {
+            qv[0] = a.quats[gq * 4 + 0] + d0[3];
+            qv[1] = qv[2] = qv[3] = 0.0f;
+        } else if (q == 1) {
+            qv[0] = 0.0f;
+            qv[1] = a.quats[gq * 4 + 1] + d0[0];
+            qv[2] = a.quats[gq * 4 + 2] + d0[1];
+            qv[3] = a.quats[gq * 4 + 3] + d0[2];
+        } else {
+            qv[0] = qv[1] = qv[2] = qv[3] = 0.0f;
+        }
+        const float part = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
+        const float other = __shfl_xor(part, 16);
+        const float inv = 1.0f / fmaxf(sqrtf(part + other), 1e-12f);
+        if (gi < a.N) {
             if (q == 0) {
-                qv[0] = a.quats[gq * 4 + 0] + d0[3];
-                qv[1] = qv[2] = qv[3] = 0.0f;
+                a.o_means[gi * 3 + 0] = a.means[gi * 3 + 0] + d0[0];
+                a.o_means[gi * 3 + 1] = a.means[gi * 3 + 1] + d0[1];
+                a.o_means[gi * 3 + 2] = a.means[gi * 3 + 2] + d0[2];
+                a.o_quats[gi * 4 + 0] = qv[0] * inv;
+                a.o_opacity[gi] = a.opacity[gi];
             } else if (q == 1) {
-                qv[0] = 0.0f;
-                qv[1] = a.quats[gq * 4 + 1] + d0[0];
-                qv[2] = a.quats[gq * 4 + 2] + d0[1];
-                qv[3] = a.quats[gq * 4 + 3] + d0[2];
+                a.o_quats[gi * 4 + 1] = qv[1] * inv;
+                a.o_quats[gi * 4 + 2] = qv[2] * inv;
+                a.o_quats[gi * 4 + 3] = qv[3] * inv;
+                a.o_scales[gi * 3 + 0] = a.scales[gi * 3 + 0] * expf(d0[3]);
+            } else if (q == 2) {
+                a.o_scales[gi * 3 + 1] = a.scales[gi * 3 + 1] * expf(d0[0]);
+                a.o_scales[gi * 3 + 2] = a.scales[gi * 3 + 2] * expf(d0[1]);
+                a.o_sh[gi * 48 + 0] = a.sh[gi * 48 + 0] + d0[2];
+                a.o_sh[gi * 48 + 1] = a.sh[gi * 48 + 1] + d0[3];
             } else {
-                qv[0] = qv[1] = qv[2] = qv[3] = 0.0f;
-            }
-            const float part = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
-            const float other = __shfl_xor(part, 16);
-            const float inv = 1.0f / fmaxf(sqrtf(part + other), 1e-12f);
-            if (gi < a.N) {
-                if (q == 0) {
-                    a.o_means[gi * 3 + 0] = a.means[gi * 3 + 0] + d0[0];
-                    a.o_means[gi * 3 + 1] = a.means[gi * 3 + 1] + d0[1];
-                    a.o_means[gi * 3 + 2] = a.means[gi * 3 + 2] + d0[2];
-                    a.o_quats[gi * 4 + 0] = qv[0] * inv;
-                    a.o_opacity[gi] = a.opacity[gi];
-                } else if (q == 1) {
-                    a.o_quats[gi * 4 + 1] = qv[1] * inv;
-                    a.o_quats[gi * 4 + 2] = qv[2] * inv;
-                    a.o_quats[gi * 4 + 3] = qv[3] * inv;
-                    a.o_scales[gi * 3 + 0] = a.scales[gi * 3 + 0] * expf(d0[3]);
-                } else if (q == 2) {
-                    a.o_scales[gi * 3 + 1] = a.scales[gi * 3 + 1] * expf(d0[0]);
-                    a.o_scales[gi * 3 + 2] = a.scales[gi * 3 + 2] * expf(d0[1]);
-                    a.o_sh[gi * 48 + 0] = a.sh[gi * 48 + 0] + d0[2];
-                    a.o_sh[gi * 48 + 1] = a.sh[gi * 48 + 1] + d0[3];
-                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a.o_sh[gi * 48 + 2 + e] = a.sh[gi * 48 + 2 + e] + d0[e];
+                for (int e = 0; e < 4; ++e) a.o_sh[gi * 48 + 2 + e] = a.sh[gi * 48 + 2 + e] + d0[e];
+            }
+#pragma unroll
+            for (int r3 = 1; r3 < 4; ++r3)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int o = 16 * r3 + 4 * q + e;
+                    if (o < 58) a.o_sh[gi * 48 + (o - 10)] = a.sh[gi * 48 + (o - 10)] + acc3[r3][g][e] + a.b[2][o];
                 }
-#pragma unroll
-                for (int r3 = 1; r3 < 4; ++r3)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int o = 16 * r3 + 4 * q + e;
-                        if (o < 58) a.o_sh[gi * 48 + (o - 10)] = a.sh[gi * 48 + (o - 10)] + acc3[r3][g][e] + a.b[2][o];
-                    }
-            }
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_hexplane(const HexArgs& a, hipStream_t s) {
+hipError_t launch_hexplane_tiles(const _Float16* const W[3], void* Wt, hipStream_t s) {
+    IA_LAUNCH("tile_weights_kernel", tile_weights_kernel, dim3(kTiles), dim3(64), 0, s, W[0], W[1], W[2],
+              static_cast<half8_t*>(Wt));
+    return hipGetLastError();
+}
+
+hipError_t launch_hexplane(const HexArgs& a, const void* Wt, hipStream_t s) {
     if (a.N <= 0) return hipSuccess;
-    int64_t per_block = 4 * 16 * kG;
-    int64_t grid = (a.N + per_block - 1) / per_block;
-    if (grid > 4096) grid = 4096;
-    IA_LAUNCH("hexplane_kernel", hexplane_kernel, dim3((unsigned)grid), dim3(256), 0, s, a);
+    const int64_t per_block = 4 * 16 * kG;
+    const int64_t grid = (a.N + per_block - 1) / per_block;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    IA_LAUNCH("hexplane_kernel", hexplane_kernel, dim3((unsigned)grid), dim3(256), 0, s, a,
+              static_cast<const half8_t*>(Wt));
     return hipGetLastError();
 }
 

@@ -96,7 +96,12 @@ struct HexArgs {
     float* o_opacity;
 };
 
-hipError_t launch_hexplane(const HexArgs& a, hipStream_t s);
+// Rearrange the three row-major fp16 weight matrices into the A-tile order the
+// deformation kernel stages through LDS (256 tiles of 1 KiB, Wt owns 256 KiB).
+constexpr size_t kHexTiledWeightBytes = 256 * 1024;
+hipError_t launch_hexplane_tiles(const _Float16* const W[3], void* Wt, hipStream_t s);
+
+hipError_t launch_hexplane(const HexArgs& a, const void* Wt, hipStream_t s);
 
 // ---------------------------------------------------------------- render
 
@@ -112,10 +117,10 @@ struct DevCamera {
 
 // Byte offsets of every buffer inside the render workspace.
 struct RenderLayout {
-    size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum2, boff, gk0, gk1, ent0, ent1, avals, counts,
-        digit_tot, ranges, nent, nvis, total;
+    size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum2, boff, srect, ginfo, bstart, gk0, gk1, ent0, ent1,
+        avals, counts, digit_tot, ranges, nent, nvis, total;
     int64_t N, cap, ntiles_all;
-    int frames, tiles_x, tiles_y, nb1, nb2;
+    int frames, tiles_x, tiles_y, nb1, nb2, nemit;
     int sort_blocks_g, sort_blocks_e;  // radix-sort blocks over Gaussians / over entries
 };
 

@@ -37,8 +37,8 @@ namespace ia {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kSortItems = 8;                      // keys per thread per sort tile
-constexpr int kSortTile = kBlock * kSortItems;     // 2048
+constexpr int kSortItems = 16;                     // keys per thread per sort tile
+constexpr int kSortTile = kBlock * kSortItems;     // 4096
 constexpr int kScanChunk = 1024;                   // block sums per second-level group
 
 // ---------------------------------------------------------------- helpers
@@ -376,11 +376,17 @@ __global__ void __launch_bounds__(kBlock) compact_kernel(const uint32_t* tiles, 
     if (vis) gkeys[boff[blockIdx.x] + ex] = ((uint64_t)__float_as_uint(depth[i]) << 32) | (uint32_t)i;
 }
 
-// Per block of 256 depth-ordered Gaussians: the tiles they touch.
+// Per block of 256 depth-ordered Gaussians: their tile rects in that order
+// (one gather) and the number of tiles they touch.
 __global__ void __launch_bounds__(kBlock) sorted_tiles_kernel(const uint64_t* gkeys, const uint64_t* nvis,
-                                                              const uint32_t* tiles, uint32_t* bsum) {
+                                                              const ushort4* rect, ushort4* srect, uint32_t* bsum) {
     const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    const uint32_t n = j < nvis[0] ? tiles[(uint32_t)gkeys[j]] : 0u;
+    uint32_t n = 0;
+    if (j < nvis[0]) {
+        const ushort4 r = rect[(uint32_t)gkeys[j]];
+        srect[j] = r;
+        n = ((uint32_t)r.z - r.x + 1) * ((uint32_t)r.w - r.y + 1);
+    }
     uint32_t total;
     block_excl_scan<uint32_t>(n, total);
     if (threadIdx.x == 0) bsum[blockIdx.x] = total;
@@ -388,59 +394,113 @@ __global__ void __launch_bounds__(kBlock) sorted_tiles_kernel(const uint64_t* gk
 
 // ---------------------------------------------------------------- key emission
 
-struct EmitArgs {
-    const uint64_t* gkeys;  // depth-ordered visible Gaussians (index in the low word)
+// Entries are emitted in depth order of their Gaussians, kEmitPerBlock per
+// block whatever the Gaussians' sizes (depth order groups the large near
+// Gaussians, so blocks of Gaussians would be badly unbalanced).
+constexpr int kEmitPerBlock = 16384;
+
+struct GInfo {
+    uint32_t off;    // first entry (clamped to the capacity)
+    uint32_t idx;    // Gaussian index
+    uint32_t tile0;  // global tile of the rect's top-left corner
+    uint32_t w;      // rect width in tiles
+};
+
+struct OffsetArgs {
+    const uint64_t* gkeys;
     const uint64_t* nvis;
-    const uint32_t* tiles;
-    const ushort4* rect;
-    const uint64_t* boff;   // per block: first entry
+    const ushort4* srect;
+    const uint64_t* boff;
     const int64_t* fo;
     int F;
     int tiles_x;
     uint32_t ntiles;
     uint64_t cap;
+    uint32_t nemit;    // emission blocks
+    GInfo* info;
+    uint32_t* bstart;  // per emission block: the Gaussian holding its first entry
+};
+
+__global__ void __launch_bounds__(kBlock) offsets_kernel(OffsetArgs a) {
+    const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    const bool live = j < a.nvis[0];
+    ushort4 r = make_ushort4(0, 0, 0, 0);
+    uint32_t n = 0;
+    if (live) {
+        r = a.srect[j];
+        n = ((uint32_t)r.z - r.x + 1) * ((uint32_t)r.w - r.y + 1);
+    }
+    uint32_t total;
+    const uint32_t ex = block_excl_scan<uint32_t>(n, total);
+    if (!live) return;
+    const uint64_t off = a.boff[blockIdx.x] + ex, stop = off + n;
+    const uint32_t idx = (uint32_t)a.gkeys[j];
+    GInfo g;
+    g.off = (uint32_t)(off < a.cap ? off : a.cap);
+    g.idx = idx;
+    g.tile0 = (uint32_t)frame_of(a.fo, a.F, idx) * a.ntiles + (uint32_t)r.y * (uint32_t)a.tiles_x + r.x;
+    g.w = (uint32_t)r.z - r.x + 1;
+    a.info[j] = g;
+    // emission blocks whose first entry lies in [off, stop)
+    for (uint64_t b = (off + kEmitPerBlock - 1) / kEmitPerBlock; b * kEmitPerBlock < stop && b < a.nemit; ++b)
+        a.bstart[b] = (uint32_t)j;
+}
+
+struct EmitArgs {
+    const GInfo* info;
+    const uint64_t* nvis;
+    const uint32_t* bstart;
+    const uint64_t* nent;
+    uint64_t cap;
+    int tiles_x;
     uint64_t* ents;  // (frame*tiles + tile) << 32 | Gaussian index
 };
 
-// Entries are written in depth order of their Gaussians; each block spreads
-// the entries of its 256 Gaussians over all its threads.
 __global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
     __shared__ uint32_t s_off[kBlock + 1];
-    __shared__ ushort4 s_rect[kBlock];
-    __shared__ uint32_t s_idx[kBlock];
-    __shared__ uint32_t s_tbase[kBlock];  // frame * ntiles
-    const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    uint32_t n = 0;
-    if (j < a.nvis[0]) {
-        const uint32_t i = (uint32_t)a.gkeys[j];
-        n = a.tiles[i];
-        s_rect[threadIdx.x] = a.rect[i];
-        s_idx[threadIdx.x] = i;
-        s_tbase[threadIdx.x] = (uint32_t)frame_of(a.fo, a.F, i) * a.ntiles;
-    }
-    uint32_t total;
-    uint32_t ex = block_excl_scan<uint32_t>(n, total);
-    s_off[threadIdx.x] = ex;
-    if (threadIdx.x == 0) s_off[kBlock] = total;
-    __syncthreads();
-    const uint64_t base = a.boff[blockIdx.x];
-    for (uint32_t e = threadIdx.x; e < total; e += kBlock) {
-        // owner: last k with s_off[k] <= e (every listed Gaussian has >= 1 entry)
-        int lo = 0, hi = kBlock - 1;
-        while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= e)
-                lo = mid;
-            else
-                hi = mid - 1;
+    __shared__ uint32_t s_next;
+    uint64_t Ecap = a.nent[0];
+    if (Ecap > a.cap) Ecap = a.cap;
+    const uint64_t e0 = (uint64_t)blockIdx.x * kEmitPerBlock;
+    if (e0 >= Ecap) return;
+    const uint64_t e1 = e0 + kEmitPerBlock < Ecap ? e0 + kEmitPerBlock : Ecap;
+    const uint64_t nv = a.nvis[0];
+    uint64_t jc = a.bstart[blockIdx.x];  // Gaussian holding entry ec
+    for (uint64_t ec = e0; ec < e1; ec += kBlock) {
+        // offsets of the (at most 257) Gaussians that can hold this chunk's entries
+        for (int k = threadIdx.x; k <= kBlock; k += kBlock)
+            s_off[k] = jc + k < nv ? a.info[jc + k].off : 0xffffffffu;
+        __syncthreads();
+        const uint32_t e = (uint32_t)(ec + threadIdx.x);
+        if (ec + threadIdx.x < e1) {
+            int lo = 0, hi = kBlock;  // last k with s_off[k] <= e
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= e)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const GInfo g = a.info[jc + lo];
+            const uint32_t k = e - g.off;
+            const uint32_t row = k / g.w, col = k - row * g.w;
+            const uint64_t tile = (uint64_t)(g.tile0 + row * (uint32_t)a.tiles_x + col);
+            a.ents[e] = (tile << 32) | g.idx;
         }
-        const ushort4 rc = s_rect[lo];
-        const uint32_t k = e - s_off[lo];
-        const uint32_t w = (uint32_t)rc.z - rc.x + 1;
-        const uint32_t ty = rc.y + k / w, tx = rc.x + k % w;
-        const uint64_t tile = (uint64_t)(s_tbase[lo] + ty * (uint32_t)a.tiles_x + tx);
-        const uint64_t pos = base + e;
-        if (pos < a.cap) a.ents[pos] = (tile << 32) | s_idx[lo];
+        if (threadIdx.x == 0) {
+            const uint32_t next = (uint32_t)(ec + kBlock);
+            int lo = 0, hi = kBlock;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= next)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            s_next = (uint32_t)lo;
+        }
+        __syncthreads();
+        jc += s_next;
     }
 }
 
@@ -475,8 +535,9 @@ __device__ __forceinline__ void sort_chunk(const SortPass& p, uint32_t& begin, u
     end = (uint32_t)e;
 }
 
+template <int MAXB>
 __global__ void __launch_bounds__(kBlock) sort_upsweep_kernel(SortPass p) {
-    __shared__ uint32_t hist[4 * kMaxBuckets];  // per-wave histograms, [4][nb] flat
+    __shared__ uint32_t hist[4 << MAXB];  // per-wave histograms, [4][nb] flat
     const int w = threadIdx.x >> 6;
     const int nb = 1 << p.bits;
     const uint32_t mask = (uint32_t)nb - 1u;
@@ -484,9 +545,16 @@ __global__ void __launch_bounds__(kBlock) sort_upsweep_kernel(SortPass p) {
     __syncthreads();
     uint32_t begin, end;
     sort_chunk(p, begin, end);
-    for (uint32_t idx = begin + threadIdx.x; idx < end; idx += kBlock) {
-        const uint32_t d = (uint32_t)(p.in[idx] >> p.shift) & mask;
-        atomicAdd(&hist[w * nb + d], 1u);
+    for (uint32_t tile = begin; tile < end; tile += kSortTile) {
+        uint32_t d[kSortItems];
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t idx = tile + j * kBlock + threadIdx.x;
+            d[j] = idx < end ? (uint32_t)(p.in[idx] >> p.shift) & mask : 0xffffffffu;
+        }
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j)
+            if (d[j] <= mask) atomicAdd(&hist[w * nb + d[j]], 1u);
     }
     __syncthreads();
     for (int d = threadIdx.x; d < nb; d += kBlock)
@@ -508,32 +576,40 @@ __global__ void __launch_bounds__(kBlock) sort_scan_kernel(SortPass p) {
     if (threadIdx.x == 0) p.digit_tot[blockIdx.x] = carry;
 }
 
-// Stable scatter.  Sort tile = 4 waves x 8 steps x 64 lanes, item order
+// Stable scatter.  Sort tile = 4 waves x 16 steps x 64 lanes, item order
 // wave-major then step then lane (the chunk order).  Per step each lane finds
 // the lanes holding the same digit with one ballot per digit bit; its rank is
-// the count of such lanes below it plus the wave's running count for the digit.
+// the count of such lanes below it plus the wave's running count for the
+// digit.  The tile is then laid out in LDS in digit order and written back
+// with consecutive threads on consecutive destinations, so each digit's items
+// leave as one contiguous run instead of one scattered word per lane.
+// MAXB: the largest digit width the instance handles (sizes its LDS).  The
+// next tile's keys are loaded while the current one is ranked and written.
+template <int MAXB>
 __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
-    __shared__ uint32_t s_base[kMaxBuckets];
-    __shared__ uint4 s_wc4[kMaxBuckets];  // per-wave counters, [4][nb] flat
+    constexpr int kNB = 1 << MAXB;
+    constexpr int kDigitsPerThread = kNB > kBlock ? kNB / kBlock : 1;
+    __shared__ uint64_t s_stage[kSortTile];
+    __shared__ uint32_t s_base[kNB];  // global destination of the digit's next item
+    __shared__ uint32_t s_ts[kNB];    // tile-local start of the digit
+    __shared__ uint4 s_wc4[kNB];      // per-wave counters, [4][nb] flat
     uint32_t* s_wc = reinterpret_cast<uint32_t*>(s_wc4);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int nb = 1 << p.bits;
     const uint32_t mask = (uint32_t)nb - 1u;
+    const int d0 = threadIdx.x * kDigitsPerThread;  // digits [d0, d0 + kDigitsPerThread) of this thread
     {
-        // digit base = exclusive scan of digit totals + this block's offset;
-        // each thread takes kMaxBuckets / kBlock consecutive digits
-        constexpr int kPer = kMaxBuckets / kBlock;
-        const int d0 = threadIdx.x * kPer;
-        uint32_t v[kPer], sum = 0;
+        // digit base = exclusive scan of digit totals + this block's offset
+        uint32_t v[kDigitsPerThread], sum = 0;
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
+        for (int k = 0; k < kDigitsPerThread; ++k) {
             v[k] = d0 + k < nb ? p.digit_tot[d0 + k] : 0u;
             sum += v[k];
         }
         uint32_t total;
         uint32_t run = block_excl_scan<uint32_t>(sum, total);
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) {
+        for (int k = 0; k < kDigitsPerThread; ++k) {
             if (d0 + k < nb) s_base[d0 + k] = run + p.counts[(d0 + k) * p.nblocks + blockIdx.x];
             run += v[k];
         }
@@ -542,16 +618,31 @@ __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
     sort_chunk(p, begin, end);
     const uint64_t end_all = p.count[0] < p.cap ? p.count[0] : p.cap;  // bound on every destination
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t prev_tc[kDigitsPerThread];  // previous tile's count of each of this thread's digits
+#pragma unroll
+    for (int k = 0; k < kDigitsPerThread; ++k) prev_tc[k] = 0;
+    uint64_t key[kSortItems];
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
+        const uint32_t idx = begin + w * (64 * kSortItems) + j * 64 + lane;
+        key[j] = idx < end ? p.in[idx] : 0ull;
+    }
     for (uint32_t tile = begin; tile < end; tile += kSortTile) {
+        // next tile's keys, in flight during this tile
+        uint64_t nkey[kSortItems];
+        const uint32_t ntile = tile + kSortTile;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t idx = ntile + w * (64 * kSortItems) + j * 64 + lane;
+            nkey[j] = (ntile < end && idx < end) ? p.in[idx] : 0ull;
+        }
         for (int k = threadIdx.x; k < nb; k += kBlock) s_wc4[k] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
-        uint64_t key[kSortItems];
         uint32_t dig[kSortItems], rank[kSortItems];
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             const uint32_t idx = tile + w * (64 * kSortItems) + j * 64 + lane;
             const bool valid = idx < end;
-            key[j] = valid ? p.in[idx] : 0ull;
             const uint32_t d = (uint32_t)(key[j] >> p.shift) & mask;
             dig[j] = valid ? d : 0xffffffffu;
             uint64_t peers = __ballot(valid);
@@ -567,22 +658,52 @@ __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
             rank[j] = prior + below;
         }
         __syncthreads();
-        // per digit: offsets of each wave inside this tile
-        for (int d = threadIdx.x; d < nb; d += kBlock) {
-            uint32_t c0 = s_wc[d], c1 = s_wc[nb + d], c2 = s_wc[2 * nb + d], c3 = s_wc[3 * nb + d];
-            s_wc[d] = s_base[d];
-            s_wc[nb + d] = s_base[d] + c0;
-            s_wc[2 * nb + d] = s_base[d] + c0 + c1;
-            s_wc[3 * nb + d] = s_base[d] + c0 + c1 + c2;
-            s_base[d] += c0 + c1 + c2 + c3;
+        // per digit: advance the global base past the previous tile, offsets
+        // of each wave inside the digit, and the digit's start inside the tile
+        {
+            uint32_t tc[kDigitsPerThread], sum = 0;
+#pragma unroll
+            for (int k = 0; k < kDigitsPerThread; ++k) {
+                const int d = d0 + k;
+                tc[k] = 0;
+                if (d < nb) {
+                    const uint32_t c0 = s_wc[d], c1 = s_wc[nb + d], c2 = s_wc[2 * nb + d], c3 = s_wc[3 * nb + d];
+                    s_wc[d] = 0;
+                    s_wc[nb + d] = c0;
+                    s_wc[2 * nb + d] = c0 + c1;
+                    s_wc[3 * nb + d] = c0 + c1 + c2;
+                    s_base[d] += prev_tc[k];
+                    tc[k] = c0 + c1 + c2 + c3;
+                }
+                sum += tc[k];
+            }
+            uint32_t total;
+            uint32_t run = block_excl_scan<uint32_t>(sum, total);
+#pragma unroll
+            for (int k = 0; k < kDigitsPerThread; ++k) {
+                if (d0 + k < nb) s_ts[d0 + k] = run;
+                run += tc[k];
+                prev_tc[k] = tc[k];
+            }
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kSortItems; ++j) {
-            const uint32_t dst = dig[j] <= mask ? s_wc[w * nb + dig[j]] + rank[j] : 0xffffffffu;
-            if (dst < end_all) p.out[dst] = key[j];
-        }
+        for (int j = 0; j < kSortItems; ++j)
+            if (dig[j] <= mask) s_stage[s_ts[dig[j]] + s_wc[w * nb + dig[j]] + rank[j]] = key[j];
         __syncthreads();
+        const uint32_t n = end - tile < (uint32_t)kSortTile ? end - tile : (uint32_t)kSortTile;
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t pos = j * kBlock + threadIdx.x;
+            if (pos < n) {
+                const uint64_t k = s_stage[pos];
+                const uint32_t d = (uint32_t)(k >> p.shift) & mask;
+                const uint32_t dst = s_base[d] + (pos - s_ts[d]);
+                if (dst < end_all) p.out[dst] = k;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kSortItems; ++j) key[j] = nkey[j];
     }
 }
 
@@ -602,15 +723,25 @@ __global__ void unpack_kernel(const uint64_t* ents, const uint64_t* nent, uint64
 
 // ---------------------------------------------------------------- tile ranges
 
-__global__ void ranges_kernel(const uint64_t* keys, const uint64_t* nent, uint64_t cap, uint2* ranges,
-                              uint32_t ntiles_all) {
+// A tile starts where its key differs from the previous one; the previous
+// key comes from the neighbouring lane.
+__global__ void __launch_bounds__(kBlock) ranges_kernel(const uint64_t* keys, const uint64_t* nent, uint64_t cap,
+                                                        uint2* ranges, uint32_t ntiles_all) {
     uint64_t E = nent[0];
     if (E > cap) E = cap;
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < E; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint32_t t = (uint32_t)(keys[i] >> 32);
-        if (t >= ntiles_all) continue;  // cannot happen for emitted keys; keeps a bad key in bounds
-        if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != t) ranges[t].x = (uint32_t)i;
-        if (i + 1 == E || (uint32_t)(keys[i + 1] >> 32) != t) ranges[t].y = (uint32_t)(i + 1);
+    const int lane = threadIdx.x & 63;
+    for (uint64_t i0 = (uint64_t)blockIdx.x * kBlock; i0 < E; i0 += (uint64_t)gridDim.x * kBlock) {
+        const uint64_t i = i0 + threadIdx.x;
+        const bool valid = i < E;
+        const uint32_t t = valid ? (uint32_t)(keys[i] >> 32) : 0xffffffffu;
+        uint32_t tp = __shfl_up(t, 1, 64);
+        if (lane == 0) tp = (valid && i > 0) ? (uint32_t)(keys[i - 1] >> 32) : 0xffffffffu;
+        if (valid && (i == 0 || t != tp)) {
+            // t >= ntiles_all cannot happen for emitted keys; the checks keep a bad key in bounds
+            if (t < ntiles_all) ranges[t].x = (uint32_t)i;
+            if (i > 0 && tp < ntiles_all) ranges[tp].y = (uint32_t)i;
+        }
+        if (i + 1 == E && t < ntiles_all) ranges[t].y = (uint32_t)E;
     }
 }
 
@@ -781,6 +912,10 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     L.bsum = take(4 * (size_t)L.nb1);
     L.bsum2 = take(8 * (size_t)L.nb2);
     L.boff = take(8 * (size_t)L.nb1);
+    L.nemit = (int)((cap1 + kEmitPerBlock - 1) / kEmitPerBlock);
+    L.srect = take(8 * (size_t)n1);
+    L.ginfo = take(sizeof(GInfo) * (size_t)n1);
+    L.bstart = take(4 * (size_t)L.nemit);
     L.gk0 = take(8 * (size_t)n1);
     L.gk1 = take(8 * (size_t)n1);
     L.ent0 = take(8 * (size_t)cap1);
@@ -822,6 +957,9 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
     uint2* ranges = reinterpret_cast<uint2*>(ws + L.ranges);
     uint64_t* nent = reinterpret_cast<uint64_t*>(ws + L.nent);
     uint64_t* nvis = reinterpret_cast<uint64_t*>(ws + L.nvis);
+    ushort4* srect = reinterpret_cast<ushort4*>(ws + L.srect);
+    GInfo* ginfo = reinterpret_cast<GInfo*>(ws + L.ginfo);
+    uint32_t* bstart = reinterpret_cast<uint32_t*>(ws + L.bstart);
     const int64_t N = L.N;
     const uint32_t ntiles = (uint32_t)(L.tiles_x * L.tiles_y);
 
@@ -833,9 +971,17 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
         int cur = 0;
         for (int pass = 0; pass < passes; ++pass) {
             SortPass sp{buf[cur], buf[cur ^ 1], count, cap, lo + pass * bits, bits, nblocks, counts, digit_tot};
-            IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel, dim3(nblocks), dim3(kBlock), 0, s, sp);
-            IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
-            IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel, dim3(nblocks), dim3(kBlock), 0, s, sp);
+            if (bits <= 8) {
+                IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<8>, dim3(nblocks), dim3(kBlock), 0, s, sp);
+                IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
+                IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel<8>, dim3(nblocks), dim3(kBlock), 0, s, sp);
+            } else {
+                IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<kMaxDigitBits>, dim3(nblocks), dim3(kBlock), 0,
+                          s, sp);
+                IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
+                IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel<kMaxDigitBits>, dim3(nblocks), dim3(kBlock),
+                          0, s, sp);
+            }
             cur ^= 1;
         }
         return cur;
@@ -856,14 +1002,17 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
         IA_LAUNCH("compact_kernel", compact_kernel, dim3(L.nb1), dim3(kBlock), 0, s, tiles, depth, N, boff, gk[0]);
         const int gcur = radix(gk, nvis, (uint64_t)N, 32, 31, L.sort_blocks_g);
         // entry offsets in that order
-        IA_LAUNCH("sorted_tiles_kernel", sorted_tiles_kernel, dim3(L.nb1), dim3(kBlock), 0, s, gk[gcur], nvis, tiles,
-                  bsum);
+        IA_LAUNCH("sorted_tiles_kernel", sorted_tiles_kernel, dim3(L.nb1), dim3(kBlock), 0, s, gk[gcur], nvis, rect,
+                  srect, bsum);
         IA_LAUNCH("scan_reduce_kernel", scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
         IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, L.nb2, (uint64_t)L.cap, nent,
                   a.n_entries_out, a.overflow_out);
         IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
-        EmitArgs em{gk[gcur], nvis, tiles, rect, boff, fo, a.frames, L.tiles_x, ntiles, (uint64_t)L.cap, ent[0]};
-        IA_LAUNCH("emit_kernel", emit_kernel, dim3(L.nb1), dim3(kBlock), 0, s, em);
+        OffsetArgs oa{gk[gcur], nvis, srect, boff, fo, a.frames, L.tiles_x, ntiles, (uint64_t)L.cap,
+                      (uint32_t)L.nemit, ginfo, bstart};
+        IA_LAUNCH("offsets_kernel", offsets_kernel, dim3(L.nb1), dim3(kBlock), 0, s, oa);
+        EmitArgs em{ginfo, nvis, bstart, nent, (uint64_t)L.cap, L.tiles_x, ent[0]};
+        IA_LAUNCH("emit_kernel", emit_kernel, dim3(L.nemit), dim3(kBlock), 0, s, em);
         // stable sort of the depth-ordered entries on the tile index gives
         // the (tile, depth, Gaussian index) order
         int tile_bits = 1;
