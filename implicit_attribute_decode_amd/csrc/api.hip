@@ -3,6 +3,7 @@
 // HIP call of an entry point, so invalid arguments never enqueue work.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -10,6 +11,11 @@
 #include <string>
 
 #include "ia_internal.h"
+
+namespace {
+// Binning of ia_render: 0 automatic, 1 tile sort, 2 regions (process-wide).
+std::atomic<int> g_binning{0};
+}  // namespace
 
 namespace {
 
@@ -407,6 +413,12 @@ void ia_hexplane_destroy(ia_hexplane* hp) {
 
 // ============================================================== render
 
+ia_status ia_render_set_binning(int32_t mode) {
+    if (mode < 0 || mode > 2) return fail(IA_ERR_INVALID_ARG, "binning mode must be 0, 1 or 2");
+    g_binning.store(mode, std::memory_order_relaxed);
+    return IA_OK;
+}
+
 ia_status ia_render_workspace_size(int64_t N_total, int32_t frames, int32_t W, int32_t H, int64_t max_entries,
                                    size_t* bytes) {
     if (!bytes) return fail(IA_ERR_INVALID_ARG, "bytes is null");
@@ -503,6 +515,7 @@ ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t
     a.n_entries_out = aux ? aux->n_entries : nullptr;
     a.overflow_out = aux ? aux->overflow : nullptr;
     a.unpack = aux != nullptr;
+    a.binning = g_binning.load(std::memory_order_relaxed);
     const uint64_t* keys = nullptr;
     const uint32_t* vals = nullptr;
     hipError_t e = ia::launch_render(a, (hipStream_t)stream, &keys, &vals);

@@ -117,11 +117,11 @@ struct DevCamera {
 
 // Byte offsets of every buffer inside the render workspace.
 struct RenderLayout {
-    size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum2, boff, srect, ginfo, bstart, gk0, gk1, ent0, ent1,
-        avals, counts, digit_tot, ranges, nent, nvis, total;
-    int64_t N, cap, ntiles_all;
-    int frames, tiles_x, tiles_y, nb1, nb2, nemit;
-    int sort_blocks_g, sort_blocks_e;  // radix-sort blocks over Gaussians / over entries
+    size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum_t, bsum2, boff, srect, ginfo, gframe, bstart, gk0, gk1, ent0,
+        ent1, vals, counts, digit_tot, rranges, rfirst, items, icnt, tcount, tstart, ranges, counters, total;
+    int64_t N, cap, ntiles_all, nreg, max_items;
+    int frames, tiles_x, tiles_y, regions_x, regions_y, nb1, nbr, nbt, nemit;
+    int sort_blocks_g, sort_blocks_e;  // radix-sort blocks over Gaussians / over coarse entries
 };
 
 RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entries);
@@ -146,6 +146,7 @@ struct RenderArgs {
     uint64_t* n_entries_out;
     uint32_t* overflow_out;
     int unpack;  // write the sorted (tile << 32 | depth bits) keys and index values for inspection
+    int binning; // 0 automatic, 1 tile sort, 2 regions
 };
 
 // Enqueue the whole render.  With unpack set, returns the sorted keys and

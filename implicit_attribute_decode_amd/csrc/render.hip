@@ -136,7 +136,8 @@ struct PreArgs {
     float* depth;
     ushort4* rect;
     uint32_t* tiles;
-    uint32_t* bsum;
+    uint32_t* bsum;    // per block: visible Gaussians
+    uint32_t* bsum_t;  // per block: tiles touched
 };
 
 // Degree-3 real spherical harmonics (orthonormal, l-major, m = -l..l, the
@@ -308,9 +309,13 @@ __global__ void __launch_bounds__(kBlock) preprocess_kernel(PreArgs a) {
                         : make_ushort4(0, 0, 0, 0);
         a.tiles[i] = ntouch;
     }
-    uint32_t total;
+    uint32_t total, total_t;
     block_excl_scan<uint32_t>(ntouch > 0 ? 1u : 0u, total);
-    if (threadIdx.x == 0) a.bsum[blockIdx.x] = total;  // visible Gaussians of the block
+    block_excl_scan<uint32_t>(ntouch, total_t);
+    if (threadIdx.x == 0) {
+        a.bsum[blockIdx.x] = total;
+        a.bsum_t[blockIdx.x] = total_t;
+    }
 }
 
 // ---------------------------------------------------------------- scan of block sums
@@ -376,48 +381,88 @@ __global__ void __launch_bounds__(kBlock) compact_kernel(const uint32_t* tiles, 
     if (vis) gkeys[boff[blockIdx.x] + ex] = ((uint64_t)__float_as_uint(depth[i]) << 32) | (uint32_t)i;
 }
 
+// ---------------------------------------------------------------- binning
+//
+// Two ways to turn the depth-ordered Gaussians into per-tile lists, chosen on
+// the device from the mean number of tiles a visible Gaussian touches (or
+// forced through ia_render_set_binning):
+//
+// Tile sort (small footprints): one entry (frame*tiles + tile) << 32 | index
+// per (Gaussian, tile), emitted in depth order, then a stable radix sort on
+// the tile bits; tile ranges from the sorted keys.
+//
+// Regions (large footprints): a region is kRegion x kRegion tiles of one frame.  Every visible Gaussian
+// gets one coarse entry per region its tile rect overlaps, emitted in depth
+// order; a stable radix sort on the region index then lists, per region, its
+// Gaussians in (depth, index) order.  Work items of kItemCoarse consecutive
+// coarse entries of one region expand them into per-tile entries: one pass
+// counts entries per (item, tile), scans give every tile its range and every
+// item its offset inside each tile, a second pass writes each entry at its
+// final position.  The tile lists come out in (depth, index) order without a
+// sort over the per-tile entries.
+constexpr int kRegion = 8;
+constexpr int kRegionTiles = kRegion * kRegion;  // 64: one lane per tile of a region
+constexpr int kItemCoarse = 256;                 // coarse entries per work item
+constexpr uint64_t kRegionFootprint = 4;         // tiles per visible Gaussian from which regions are used
+
+enum : uint64_t { kModeTiles = 0, kModeRegions = 1 };
+
+__device__ __forceinline__ uint32_t region_span(uint32_t a0, uint32_t a1) { return a1 / kRegion - a0 / kRegion + 1; }
+
+// mode[0] = binning used by this call (force: 0 automatic, 1 tile sort, 2 regions)
+__global__ void binning_mode_kernel(const uint64_t* nent, const uint64_t* nvis, int force, uint64_t* mode) {
+    if (threadIdx.x != 0) return;
+    uint64_t m = nent[0] >= kRegionFootprint * nvis[0] ? kModeRegions : kModeTiles;
+    if (force == 1) m = kModeTiles;
+    if (force == 2) m = kModeRegions;
+    mode[0] = m;
+}
+
+__device__ __forceinline__ uint32_t entries_of(ushort4 r, uint64_t mode) {
+    return mode == kModeRegions ? region_span(r.x, r.z) * region_span(r.y, r.w)
+                                : ((uint32_t)r.z - r.x + 1) * ((uint32_t)r.w - r.y + 1);
+}
+
 // Per block of 256 depth-ordered Gaussians: their tile rects in that order
-// (one gather) and the number of tiles they touch.
-__global__ void __launch_bounds__(kBlock) sorted_tiles_kernel(const uint64_t* gkeys, const uint64_t* nvis,
-                                                              const ushort4* rect, ushort4* srect, uint32_t* bsum) {
+// (one gather) and their entries (tiles touched, or regions overlapped).
+__global__ void __launch_bounds__(kBlock) sorted_rects_kernel(const uint64_t* gkeys, const uint64_t* nvis,
+                                                              const uint64_t* mode, const ushort4* rect,
+                                                              ushort4* srect, uint32_t* bsum) {
     const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
     uint32_t n = 0;
     if (j < nvis[0]) {
         const ushort4 r = rect[(uint32_t)gkeys[j]];
         srect[j] = r;
-        n = ((uint32_t)r.z - r.x + 1) * ((uint32_t)r.w - r.y + 1);
+        n = entries_of(r, mode[0]);
     }
     uint32_t total;
     block_excl_scan<uint32_t>(n, total);
     if (threadIdx.x == 0) bsum[blockIdx.x] = total;
 }
 
-// ---------------------------------------------------------------- key emission
-
-// Entries are emitted in depth order of their Gaussians, kEmitPerBlock per
-// block whatever the Gaussians' sizes (depth order groups the large near
-// Gaussians, so blocks of Gaussians would be badly unbalanced).
+// Entries are emitted kEmitPerBlock per block whatever the Gaussians' sizes
+// (depth order groups the large near Gaussians).
 constexpr int kEmitPerBlock = 16384;
 
 struct GInfo {
-    uint32_t off;    // first entry (clamped to the capacity)
-    uint32_t idx;    // Gaussian index
-    uint32_t tile0;  // global tile of the rect's top-left corner
-    uint32_t w;      // rect width in tiles
+    uint32_t off;  // first entry (clamped to the capacity)
+    uint32_t idx;  // Gaussian index
+    uint32_t lo;   // tile rect x0 | y0 << 16
+    uint32_t hi;   // tile rect x1 | y1 << 16
 };
 
 struct OffsetArgs {
     const uint64_t* gkeys;
     const uint64_t* nvis;
+    const uint64_t* mode;
     const ushort4* srect;
     const uint64_t* boff;
-    const int64_t* fo;
-    int F;
-    int tiles_x;
-    uint32_t ntiles;
     uint64_t cap;
     uint32_t nemit;    // emission blocks
+    const int64_t* fo;
+    int F;
     GInfo* info;
+    uint32_t* frame;   // per depth-ordered Gaussian: its frame
     uint32_t* bstart;  // per emission block: the Gaussian holding its first entry
 };
 
@@ -428,19 +473,19 @@ __global__ void __launch_bounds__(kBlock) offsets_kernel(OffsetArgs a) {
     uint32_t n = 0;
     if (live) {
         r = a.srect[j];
-        n = ((uint32_t)r.z - r.x + 1) * ((uint32_t)r.w - r.y + 1);
+        n = entries_of(r, a.mode[0]);
     }
     uint32_t total;
     const uint32_t ex = block_excl_scan<uint32_t>(n, total);
     if (!live) return;
     const uint64_t off = a.boff[blockIdx.x] + ex, stop = off + n;
-    const uint32_t idx = (uint32_t)a.gkeys[j];
     GInfo g;
     g.off = (uint32_t)(off < a.cap ? off : a.cap);
-    g.idx = idx;
-    g.tile0 = (uint32_t)frame_of(a.fo, a.F, idx) * a.ntiles + (uint32_t)r.y * (uint32_t)a.tiles_x + r.x;
-    g.w = (uint32_t)r.z - r.x + 1;
+    g.idx = (uint32_t)a.gkeys[j];
+    g.lo = (uint32_t)r.x | ((uint32_t)r.y << 16);
+    g.hi = (uint32_t)r.z | ((uint32_t)r.w << 16);
     a.info[j] = g;
+    a.frame[j] = (uint32_t)frame_of(a.fo, a.F, g.idx);
     // emission blocks whose first entry lies in [off, stop)
     for (uint64_t b = (off + kEmitPerBlock - 1) / kEmitPerBlock; b * kEmitPerBlock < stop && b < a.nemit; ++b)
         a.bstart[b] = (uint32_t)j;
@@ -448,18 +493,24 @@ __global__ void __launch_bounds__(kBlock) offsets_kernel(OffsetArgs a) {
 
 struct EmitArgs {
     const GInfo* info;
+    const uint32_t* frame;
     const uint64_t* nvis;
+    const uint64_t* mode;
     const uint32_t* bstart;
-    const uint64_t* nent;
+    const uint64_t* nsort;  // entries to emit
     uint64_t cap;
     int tiles_x;
-    uint64_t* ents;  // (frame*tiles + tile) << 32 | Gaussian index
+    uint32_t ntiles;
+    uint32_t regions_x;
+    uint32_t regions_per_frame;
+    uint64_t* ents;  // tile sort: tile << 32 | Gaussian index; regions: region << 32 | depth-order position
 };
 
 __global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
     __shared__ uint32_t s_off[kBlock + 1];
     __shared__ uint32_t s_next;
-    uint64_t Ecap = a.nent[0];
+    const bool regions = a.mode[0] == kModeRegions;
+    uint64_t Ecap = a.nsort[0];
     if (Ecap > a.cap) Ecap = a.cap;
     const uint64_t e0 = (uint64_t)blockIdx.x * kEmitPerBlock;
     if (e0 >= Ecap) return;
@@ -481,11 +532,23 @@ __global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
                 else
                     hi = mid - 1;
             }
-            const GInfo g = a.info[jc + lo];
+            const uint64_t j = jc + lo;
+            const GInfo g = a.info[j];
+            const uint32_t f = a.frame[j];
             const uint32_t k = e - g.off;
-            const uint32_t row = k / g.w, col = k - row * g.w;
-            const uint64_t tile = (uint64_t)(g.tile0 + row * (uint32_t)a.tiles_x + col);
-            a.ents[e] = (tile << 32) | g.idx;
+            if (regions) {
+                const uint32_t gx0 = (g.lo & 0xffffu) / kRegion, gy0 = (g.lo >> 16) / kRegion;
+                const uint32_t w = (g.hi & 0xffffu) / kRegion - gx0 + 1;
+                const uint32_t row = k / w, col = k - row * w;
+                const uint64_t region = (uint64_t)f * a.regions_per_frame + (gy0 + row) * a.regions_x + gx0 + col;
+                a.ents[e] = (region << 32) | (uint32_t)j;
+            } else {
+                const uint32_t x0 = g.lo & 0xffffu, y0 = g.lo >> 16;
+                const uint32_t w = (g.hi & 0xffffu) - x0 + 1;
+                const uint32_t row = k / w, col = k - row * w;
+                const uint64_t tile = (uint64_t)f * a.ntiles + (y0 + row) * (uint32_t)a.tiles_x + x0 + col;
+                a.ents[e] = (tile << 32) | g.idx;
+            }
         }
         if (threadIdx.x == 0) {
             const uint32_t next = (uint32_t)(ec + kBlock);
@@ -707,33 +770,24 @@ __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
     }
 }
 
-// Sorted entries as (tile << 32 | depth bits) keys and Gaussian-index values.
-__global__ void unpack_kernel(const uint64_t* ents, const uint64_t* nent, uint64_t cap, const float* depth,
-                              int64_t N, uint64_t* keys, uint32_t* vals) {
-    uint64_t E = nent[0];
-    if (E > cap) E = cap;
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < E; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint64_t v = ents[i];
-        const uint32_t g = (uint32_t)v;
-        if ((int64_t)g >= N) continue;  // cannot happen for emitted entries
-        keys[i] = (v & 0xffffffff00000000ull) | __float_as_uint(depth[g]);
-        vals[i] = g;
-    }
-}
-
 // ---------------------------------------------------------------- tile ranges
 
 // A tile starts where its key differs from the previous one; the previous
 // key comes from the neighbouring lane.
+// Runs only when mode[0] == want; with vals, also splits off the low words.
 __global__ void __launch_bounds__(kBlock) ranges_kernel(const uint64_t* keys, const uint64_t* nent, uint64_t cap,
-                                                        uint2* ranges, uint32_t ntiles_all) {
+                                                        uint2* ranges, uint32_t ntiles_all, uint32_t* vals,
+                                                        const uint64_t* mode, uint64_t want) {
+    if (mode[0] != want) return;
     uint64_t E = nent[0];
     if (E > cap) E = cap;
     const int lane = threadIdx.x & 63;
     for (uint64_t i0 = (uint64_t)blockIdx.x * kBlock; i0 < E; i0 += (uint64_t)gridDim.x * kBlock) {
         const uint64_t i = i0 + threadIdx.x;
         const bool valid = i < E;
-        const uint32_t t = valid ? (uint32_t)(keys[i] >> 32) : 0xffffffffu;
+        const uint64_t key = valid ? keys[i] : ~0ull;
+        const uint32_t t = (uint32_t)(key >> 32);
+        if (vals && valid) vals[i] = (uint32_t)key;
         uint32_t tp = __shfl_up(t, 1, 64);
         if (lane == 0) tp = (valid && i > 0) ? (uint32_t)(keys[i - 1] >> 32) : 0xffffffffu;
         if (valid && (i == 0 || t != tp)) {
@@ -745,11 +799,239 @@ __global__ void __launch_bounds__(kBlock) ranges_kernel(const uint64_t* keys, co
     }
 }
 
+// ---------------------------------------------------------------- per-tile lists from regions
+
+// Per block of 256 regions: work items (kItemCoarse coarse entries each).
+__global__ void __launch_bounds__(kBlock) region_items_kernel(const uint64_t* mode, const uint2* rranges, uint32_t nreg, uint32_t* bsum) {
+    if (mode[0] != kModeRegions) return;
+    const uint32_t r = blockIdx.x * kBlock + threadIdx.x;
+    uint32_t n = 0;
+    if (r < nreg) {
+        const uint2 rr = rranges[r];
+        n = (rr.y - rr.x + kItemCoarse - 1) / kItemCoarse;
+    }
+    uint32_t total;
+    block_excl_scan<uint32_t>(n, total);
+    if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+// Item table: item -> (region, segment); per region its first item.
+__global__ void __launch_bounds__(kBlock) region_expand_kernel(const uint64_t* mode, const uint2* rranges, uint32_t nreg,
+                                                               const uint64_t* boff, uint64_t max_items,
+                                                               uint2* items, uint32_t* rfirst) {
+    if (mode[0] != kModeRegions) return;
+    const uint32_t r = blockIdx.x * kBlock + threadIdx.x;
+    uint32_t n = 0;
+    if (r < nreg) {
+        const uint2 rr = rranges[r];
+        n = (rr.y - rr.x + kItemCoarse - 1) / kItemCoarse;
+    }
+    uint32_t total;
+    const uint32_t ex = block_excl_scan<uint32_t>(n, total);
+    if (r >= nreg) return;
+    const uint64_t base = boff[blockIdx.x] + ex;
+    rfirst[r] = (uint32_t)base;
+    for (uint32_t s = 0; s < n && base + s < max_items; ++s) items[base + s] = make_uint2(r, s);
+}
+
+struct ExpandArgs {
+    const uint64_t* mode;
+    const uint2* items;
+    const uint64_t* nitems;  // [0] = work items
+    const uint2* rranges;
+    const uint64_t* coarse;  // sorted coarse entries
+    const GInfo* info;
+    uint32_t regions_x;
+    uint32_t regions_per_frame;
+    int tiles_x, tiles_y;
+    uint32_t ntiles;
+    uint32_t* cnt;            // [item][64]: entries per tile, then the item's offset inside the tile
+    const uint32_t* tstart;   // per tile: first entry
+    uint64_t cap;
+    uint32_t* vals;
+};
+
+// One wave per work item.  Its coarse entries are taken 64 at a time; lane l
+// clips Gaussian l's tile rect to the region (w x h tiles), a wave scan
+// flattens the chunk's entries (Gaussian-major, then rows, then columns) and
+// each lane finds the owner of its entry by a binary search over the lanes'
+// offsets (cross-lane reads).  WRITE = false counts entries per region tile;
+// WRITE = true ranks each entry among the item's entries of the same tile
+// (one ballot per bit of the 6-bit tile index) and stores the Gaussian index
+// at its final position.
+constexpr int kStage = 2048;  // entries staged per chunk of a work item (LDS, per wave)
+
+// One work item on one wave.  Coarse entries are taken up to 64 at a time,
+// as many as keep the chunk within kStage entries; lane l clips Gaussian l's
+// tile rect to the region.  For each of the 64 region tiles one ballot over
+// the lanes whose clip covers it gives the tile's count in the chunk and,
+// below each lane, that lane's rank among them (the lanes are in depth
+// order), so no per-entry search is needed.
+// WRITE = false: entries per region tile of the item.
+// WRITE = true: the chunk's per-tile counts give each tile a segment of the
+// stage; every (lane, tile) entry goes to its slot and the stage is written
+// out with consecutive lanes on consecutive positions of a tile's list.
+template <bool WRITE>
+__device__ __forceinline__ void expand_item(const ExpandArgs& a, uint64_t item, int lane, uint32_t* stage,
+                                            uint8_t* tof) {
+    const uint2 it = a.items[item];
+    const uint32_t r = it.x;
+    const uint2 rr = a.rranges[r];
+    const uint32_t cb = rr.x + it.y * kItemCoarse;
+    const uint32_t ce = cb + kItemCoarse < rr.y ? cb + kItemCoarse : rr.y;
+    const uint32_t f = r / a.regions_per_frame, rl = r - f * a.regions_per_frame;
+    const uint32_t ox = (rl % a.regions_x) * kRegion, oy = (rl / a.regions_x) * kRegion;
+    uint32_t basev = 0;  // lane t: next position of this item's entries of region tile t
+    if (WRITE) {
+        const uint32_t tx = ox + (lane % kRegion), ty = oy + (lane / kRegion);
+        if (tx < (uint32_t)a.tiles_x && ty < (uint32_t)a.tiles_y)
+            basev = a.tstart[f * a.ntiles + ty * (uint32_t)a.tiles_x + tx] + a.cnt[item * kRegionTiles + lane];
+    }
+    uint32_t total = 0;  // lane t: entries of region tile t in the item so far (count pass)
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (uint32_t k0 = cb; k0 < ce;) {
+        const uint32_t k = k0 + lane;
+        // clip [cx0, cx1] x [cy0, cy1] in region tile coordinates; empty for lanes past the item
+        uint32_t cx0 = 1, cy0 = 1, cx1 = 0, cy1 = 0, n = 0, gidx = 0;
+        if (k < ce) {
+            const GInfo g = a.info[(uint32_t)a.coarse[k]];
+            const uint32_t x0 = g.lo & 0xffffu, y0 = g.lo >> 16, x1 = g.hi & 0xffffu, y1 = g.hi >> 16;
+            cx0 = (x0 > ox ? x0 : ox) - ox;
+            cy0 = (y0 > oy ? y0 : oy) - oy;
+            cx1 = (x1 < ox + kRegion - 1 ? x1 : ox + kRegion - 1) - ox;
+            cy1 = (y1 < oy + kRegion - 1 ? y1 : oy + kRegion - 1) - oy;
+            n = (cx1 - cx0 + 1) * (cy1 - cy0 + 1);
+            gidx = g.idx;
+        }
+        uint32_t take = 64;
+        if (WRITE) {
+            // lanes [0, take) fit the stage (the inclusive count is non-decreasing; lane 0 always fits)
+            const uint32_t incl = wave_incl_scan(n);
+            take = (uint32_t)__popcll(__ballot(incl <= (uint32_t)kStage));
+            if ((uint32_t)lane >= take) cx0 = 1, cx1 = 0;
+        }
+        uint32_t c = 0;  // lane t: entries of region tile t in this chunk
+#pragma unroll 8
+        for (int t = 0; t < kRegionTiles; ++t) {
+            const uint32_t tx = t % kRegion, ty = t / kRegion;
+            const bool cov = cx0 <= tx && tx <= cx1 && cy0 <= ty && ty <= cy1;
+            const uint32_t nt = (uint32_t)__popcll(__ballot(cov));
+            c = lane == t ? nt : c;
+        }
+        if (!WRITE) {
+            total += c;
+        } else {
+            const uint32_t choff = wave_incl_scan(c) - c;  // tile's segment in the stage
+            const uint32_t m = __shfl(choff + c, 63, 64);
+#pragma unroll 8
+            for (int t = 0; t < kRegionTiles; ++t) {
+                const uint32_t tx = t % kRegion, ty = t / kRegion;
+                const bool cov = cx0 <= tx && tx <= cx1 && cy0 <= ty && ty <= cy1;
+                const uint64_t mk = __ballot(cov);
+                const uint32_t seg = __builtin_amdgcn_readlane(choff, t);
+                if (cov) {
+                    const uint32_t slot = seg + (uint32_t)__popcll(mk & lt_mask);
+                    stage[slot] = gidx;
+                    tof[slot] = (uint8_t)t;
+                }
+            }
+            asm volatile("" ::: "memory");
+            for (uint32_t s0 = 0; s0 < m; s0 += 64) {
+                const uint32_t slot = s0 + lane;
+                const int t = slot < m ? tof[slot] : 0;
+                const uint32_t pos = __shfl(basev, t, 64) + (slot - __shfl(choff, t, 64));
+                if (slot < m && pos < a.cap) a.vals[pos] = stage[slot];
+            }
+            basev += c;
+            asm volatile("" ::: "memory");
+        }
+        k0 += take;
+    }
+    if (!WRITE) a.cnt[item * kRegionTiles + lane] = total;
+}
+
+template <bool WRITE>
+__global__ void __launch_bounds__(kBlock) expand_kernel(ExpandArgs a) {
+    if (a.mode[0] != kModeRegions) return;
+    __shared__ uint32_t s_stage[WRITE ? 4 : 1][WRITE ? kStage : 1];
+    __shared__ uint8_t s_tof[WRITE ? 4 : 1][WRITE ? kStage : 1];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t nitems = a.nitems[0];
+    for (uint64_t item = (uint64_t)blockIdx.x * 4 + w; item < nitems; item += (uint64_t)gridDim.x * 4)
+        expand_item<WRITE>(a, item, lane, s_stage[WRITE ? w : 0], s_tof[WRITE ? w : 0]);
+}
+
+
+// One wave per region: lane t turns the per-item counts of region tile t into
+// the items' offsets inside the tile (exclusive scan over the region's items)
+// and writes the tile's entry count.
+__global__ void __launch_bounds__(kBlock) region_tiles_kernel(const uint64_t* mode, const uint2* rranges, const uint32_t* rfirst,
+                                                              uint32_t nreg, uint32_t regions_x,
+                                                              uint32_t regions_per_frame, int tiles_x, int tiles_y,
+                                                              uint32_t ntiles, uint64_t max_items, uint32_t* cnt,
+                                                              uint32_t* tcount) {
+    if (mode[0] != kModeRegions) return;
+    const int lane = threadIdx.x & 63;
+    const uint32_t r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= nreg) return;
+    const uint2 rr = rranges[r];
+    const uint32_t n = (rr.y - rr.x + kItemCoarse - 1) / kItemCoarse;
+    const uint64_t first = rfirst[r];
+    uint32_t run = 0;
+    for (uint32_t s = 0; s < n && first + s < max_items; ++s) {
+        uint32_t* c = cnt + (first + s) * kRegionTiles + lane;
+        const uint32_t v = *c;
+        *c = run;
+        run += v;
+    }
+    const uint32_t f = r / regions_per_frame, rl = r - f * regions_per_frame;
+    const uint32_t tx = (rl % regions_x) * kRegion + (lane % kRegion);
+    const uint32_t ty = (rl / regions_x) * kRegion + (lane / kRegion);
+    if (tx < (uint32_t)tiles_x && ty < (uint32_t)tiles_y) tcount[f * ntiles + ty * (uint32_t)tiles_x + tx] = run;
+}
+
+// Per block of 256 tiles: entries.
+__global__ void __launch_bounds__(kBlock) tile_sums_kernel(const uint64_t* mode, const uint32_t* tcount, int64_t ntiles_all, uint32_t* bsum) {
+    if (mode[0] != kModeRegions) return;
+    const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    uint32_t total;
+    block_excl_scan<uint32_t>(t < ntiles_all ? tcount[t] : 0u, total);
+    if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+// Tile ranges [start, start + count) (empty tiles [0, 0)) and first entries.
+__global__ void __launch_bounds__(kBlock) tile_ranges_kernel(const uint64_t* mode, const uint32_t* tcount, int64_t ntiles_all,
+                                                             const uint64_t* boff, uint64_t cap, uint32_t* tstart,
+                                                             uint2* ranges) {
+    if (mode[0] != kModeRegions) return;
+    const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const uint32_t c = t < ntiles_all ? tcount[t] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_excl_scan<uint32_t>(c, total);
+    if (t >= ntiles_all) return;
+    uint64_t s = boff[blockIdx.x] + ex, e = s + c;
+    if (s > cap) s = cap;
+    if (e > cap) e = cap;
+    tstart[t] = (uint32_t)s;
+    ranges[t] = c ? make_uint2((uint32_t)s, (uint32_t)e) : make_uint2(0u, 0u);
+}
+
+// Sorted (tile << 32 | depth bits) keys of the entries, one block per tile.
+__global__ void __launch_bounds__(kBlock) unpack_kernel(const uint2* ranges, const uint32_t* vals, const float* depth,
+                                                        int64_t N, uint64_t* keys) {
+    const uint64_t t = blockIdx.x + (uint64_t)gridDim.x * blockIdx.y;
+    const uint2 rg = ranges[t];
+    for (uint32_t i = rg.x + threadIdx.x; i < rg.y; i += kBlock) {
+        const uint32_t g = vals[i];
+        keys[i] = (t << 32) | ((int64_t)g < N ? __float_as_uint(depth[g]) : 0u);
+    }
+}
+
 // ---------------------------------------------------------------- raster
 
 struct RasterArgs {
     const uint2* ranges;
-    const uint64_t* ents;  // sorted entries, Gaussian index in the low word
+    const uint32_t* vals;  // per-tile lists of Gaussian indices
     const float4* pa;
     const float4* pb;
     const float* pc;
@@ -822,7 +1104,7 @@ __global__ void __launch_bounds__(kRasterThreads) raster_kernel(RasterArgs a) {
             const uint32_t slot = threadIdx.x + k * kRasterThreads;
             const uint32_t idx = start + slot;
             if (idx < rg.y) {
-                uint32_t gid = (uint32_t)a.ents[idx];
+                uint32_t gid = a.vals[idx];
                 if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
                 const float4 pa = a.pa[gid], pb = a.pb[gid];
                 s_a[slot] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
@@ -885,16 +1167,25 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     L.tiles_x = (W + 15) / 16;
     L.tiles_y = (H + 15) / 16;
     L.ntiles_all = (int64_t)frames * L.tiles_x * L.tiles_y;
+    L.regions_x = (L.tiles_x + kRegion - 1) / kRegion;
+    L.regions_y = (L.tiles_y + kRegion - 1) / kRegion;
+    L.nreg = (int64_t)frames * L.regions_x * L.regions_y;
     const int64_t n1 = N > 0 ? N : 1;
+    const int64_t cap1 = max_entries > 0 ? max_entries : 1;
     L.nb1 = (int)((n1 + kBlock - 1) / kBlock);
-    L.nb2 = (L.nb1 + kScanChunk - 1) / kScanChunk;
+    L.nbr = (int)((L.nreg + kBlock - 1) / kBlock);
+    L.nbt = (int)((L.ntiles_all + kBlock - 1) / kBlock);
+    int nbmax = L.nb1 > L.nbr ? L.nb1 : L.nbr;
+    nbmax = nbmax > L.nbt ? nbmax : L.nbt;
     auto blocks = [](int64_t items) {
         int64_t b = (items + kSortTile - 1) / kSortTile;
         return (int)(b < 1 ? 1 : (b > 1024 ? 1024 : b));
     };
     L.sort_blocks_g = blocks(n1);
-    L.sort_blocks_e = blocks(max_entries);
-    const int64_t cap1 = max_entries > 0 ? max_entries : 1;
+    L.sort_blocks_e = blocks(cap1);
+    L.nemit = (int)((cap1 + kEmitPerBlock - 1) / kEmitPerBlock);
+    // coarse entries <= tile entries <= capacity, so items <= cap / kItemCoarse + regions
+    L.max_items = (cap1 + kItemCoarse - 1) / kItemCoarse + L.nreg;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -909,24 +1200,30 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     L.depth = take(4 * (size_t)n1);
     L.rect = take(8 * (size_t)n1);
     L.tiles = take(4 * (size_t)n1);
-    L.bsum = take(4 * (size_t)L.nb1);
-    L.bsum2 = take(8 * (size_t)L.nb2);
-    L.boff = take(8 * (size_t)L.nb1);
-    L.nemit = (int)((cap1 + kEmitPerBlock - 1) / kEmitPerBlock);
+    L.bsum = take(4 * (size_t)nbmax);
+    L.bsum_t = take(4 * (size_t)L.nb1);
+    L.bsum2 = take(8 * (size_t)((nbmax + kScanChunk - 1) / kScanChunk));
+    L.boff = take(8 * (size_t)nbmax);
     L.srect = take(8 * (size_t)n1);
     L.ginfo = take(sizeof(GInfo) * (size_t)n1);
+    L.gframe = take(4 * (size_t)n1);
     L.bstart = take(4 * (size_t)L.nemit);
     L.gk0 = take(8 * (size_t)n1);
     L.gk1 = take(8 * (size_t)n1);
     L.ent0 = take(8 * (size_t)cap1);
     L.ent1 = take(8 * (size_t)cap1);
-    L.avals = take(4 * (size_t)cap1);
+    L.vals = take(4 * (size_t)cap1);
     L.counts = take(4 * (size_t)kMaxBuckets *
                     (size_t)(L.sort_blocks_g > L.sort_blocks_e ? L.sort_blocks_g : L.sort_blocks_e));
     L.digit_tot = take(4 * (size_t)kMaxBuckets);
-    L.ranges = take(8 * (size_t)(L.ntiles_all > 0 ? L.ntiles_all : 1));
-    L.nent = take(16);
-    L.nvis = take(16);
+    L.rranges = take(8 * (size_t)L.nreg);
+    L.rfirst = take(4 * (size_t)L.nreg);
+    L.items = take(8 * (size_t)L.max_items);
+    L.icnt = take(4 * (size_t)kRegionTiles * (size_t)L.max_items);
+    L.tcount = take(4 * (size_t)L.ntiles_all);
+    L.tstart = take(4 * (size_t)L.ntiles_all);
+    L.ranges = take(8 * (size_t)L.ntiles_all);
+    L.counters = take(128);
     L.total = off;
     return L;
 }
@@ -948,29 +1245,56 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
     ushort4* rect = reinterpret_cast<ushort4*>(ws + L.rect);
     uint32_t* tiles = reinterpret_cast<uint32_t*>(ws + L.tiles);
     uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + L.bsum);
+    uint32_t* bsum_t = reinterpret_cast<uint32_t*>(ws + L.bsum_t);
     uint64_t* bsum2 = reinterpret_cast<uint64_t*>(ws + L.bsum2);
     uint64_t* boff = reinterpret_cast<uint64_t*>(ws + L.boff);
-    uint64_t* gk[2] = {reinterpret_cast<uint64_t*>(ws + L.gk0), reinterpret_cast<uint64_t*>(ws + L.gk1)};
-    uint64_t* ent[2] = {reinterpret_cast<uint64_t*>(ws + L.ent0), reinterpret_cast<uint64_t*>(ws + L.ent1)};
-    uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
-    uint32_t* digit_tot = reinterpret_cast<uint32_t*>(ws + L.digit_tot);
-    uint2* ranges = reinterpret_cast<uint2*>(ws + L.ranges);
-    uint64_t* nent = reinterpret_cast<uint64_t*>(ws + L.nent);
-    uint64_t* nvis = reinterpret_cast<uint64_t*>(ws + L.nvis);
     ushort4* srect = reinterpret_cast<ushort4*>(ws + L.srect);
     GInfo* ginfo = reinterpret_cast<GInfo*>(ws + L.ginfo);
+    uint32_t* gframe = reinterpret_cast<uint32_t*>(ws + L.gframe);
     uint32_t* bstart = reinterpret_cast<uint32_t*>(ws + L.bstart);
+    uint64_t* gk[2] = {reinterpret_cast<uint64_t*>(ws + L.gk0), reinterpret_cast<uint64_t*>(ws + L.gk1)};
+    uint64_t* ent[2] = {reinterpret_cast<uint64_t*>(ws + L.ent0), reinterpret_cast<uint64_t*>(ws + L.ent1)};
+    uint32_t* vals = reinterpret_cast<uint32_t*>(ws + L.vals);
+    uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
+    uint32_t* digit_tot = reinterpret_cast<uint32_t*>(ws + L.digit_tot);
+    uint2* rranges = reinterpret_cast<uint2*>(ws + L.rranges);
+    uint32_t* rfirst = reinterpret_cast<uint32_t*>(ws + L.rfirst);
+    uint2* items = reinterpret_cast<uint2*>(ws + L.items);
+    uint32_t* icnt = reinterpret_cast<uint32_t*>(ws + L.icnt);
+    uint32_t* tcount = reinterpret_cast<uint32_t*>(ws + L.tcount);
+    uint32_t* tstart = reinterpret_cast<uint32_t*>(ws + L.tstart);
+    uint2* ranges = reinterpret_cast<uint2*>(ws + L.ranges);
+    uint64_t* ctr = reinterpret_cast<uint64_t*>(ws + L.counters);
+    uint64_t* nent = ctr;         // [0] tile entries, [1] overflow
+    uint64_t* nvis = ctr + 2;     // visible Gaussians
+    uint64_t* nsort = ctr + 4;    // entries emitted for sorting (tile or region entries)
+    uint64_t* nitems = ctr + 6;   // work items
+    uint64_t* mode = ctr + 10;    // binning of this call
     const int64_t N = L.N;
+    const uint64_t cap = (uint64_t)L.cap;
     const uint32_t ntiles = (uint32_t)(L.tiles_x * L.tiles_y);
+    const uint32_t rpf = (uint32_t)(L.regions_x * L.regions_y);
+    constexpr uint64_t kNoCap = ~0ull;
 
+    // exclusive scan of per-block sums: per-block offsets (when boff_out) and
+    // the total (with the capacity check when outputs are given)
+    auto scan = [&](const uint32_t* bs, int nb, uint64_t limit, uint64_t* total, uint64_t* total_out,
+                    uint32_t* ovf_out, uint64_t* boff_out) {
+        const int nb2 = (nb + kScanChunk - 1) / kScanChunk;
+        IA_LAUNCH("scan_reduce_kernel", scan_reduce_kernel, dim3(nb2), dim3(kBlock), 0, s, bs, nb, bsum2);
+        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, nb2, limit, total,
+                  total_out, ovf_out);
+        if (boff_out)
+            IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(nb2), dim3(kBlock), 0, s, bs, nb, bsum2, boff_out);
+    };
     // LSD passes over bits [lo, lo + nbits) of 64-bit words, digits of at most
     // kMaxDigitBits bits; returns the buffer index holding the result.
-    auto radix = [&](uint64_t** buf, const uint64_t* count, uint64_t cap, int lo, int nbits, int nblocks) {
+    auto radix = [&](uint64_t** buf, const uint64_t* count, uint64_t rcap, int lo, int nbits, int nblocks) {
         const int passes = (nbits + kMaxDigitBits - 1) / kMaxDigitBits;
         const int bits = (nbits + passes - 1) / passes;
         int cur = 0;
         for (int pass = 0; pass < passes; ++pass) {
-            SortPass sp{buf[cur], buf[cur ^ 1], count, cap, lo + pass * bits, bits, nblocks, counts, digit_tot};
+            SortPass sp{buf[cur], buf[cur ^ 1], count, rcap, lo + pass * bits, bits, nblocks, counts, digit_tot};
             if (bits <= 8) {
                 IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<8>, dim3(nblocks), dim3(kBlock), 0, s, sp);
                 IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
@@ -986,57 +1310,80 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
         }
         return cur;
     };
+    auto bits_for = [](int64_t n) {
+        int b = 1;
+        while (((int64_t)1 << b) < n) ++b;
+        return b;
+    };
 
-    int ecur = 0;
+    IA_LAUNCH("fill_u32_kernel", fill_u32_kernel, dim3(grid_cap(2 * L.ntiles_all, kBlock, 4096)), dim3(kBlock), 0, s,
+              reinterpret_cast<uint32_t*>(ranges), 0u, 2 * L.ntiles_all);
     if (N > 0) {
-        // projection; visible Gaussians per block
+        // projection; per block: visible Gaussians and tiles touched
         PreArgs pre{a.means, a.means_stride, a.scales, a.quats, a.colors, a.sh, a.opacity, a.sh_degree,
-                    cams, fo, a.frames, N, pa, pb, pc, depth, rect, tiles, bsum};
+                    cams, fo, a.frames, N, pa, pb, pc, depth, rect, tiles, bsum, bsum_t};
         IA_LAUNCH("preprocess_kernel", preprocess_kernel, dim3(L.nb1), dim3(kBlock), 0, s, pre);
-        IA_LAUNCH("scan_reduce_kernel", scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
-        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, L.nb2, ~0ull, nvis,
-                  (uint64_t*)nullptr, (uint32_t*)nullptr);
-        IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
+        scan(bsum_t, L.nb1, cap, nent, a.n_entries_out, a.overflow_out, nullptr);
+        scan(bsum, L.nb1, kNoCap, nvis, nullptr, nullptr, boff);
         // visible Gaussians in ascending depth, ties in index order (stable
         // sort of index-ordered input on the 31 depth bits above the index)
         IA_LAUNCH("compact_kernel", compact_kernel, dim3(L.nb1), dim3(kBlock), 0, s, tiles, depth, N, boff, gk[0]);
         const int gcur = radix(gk, nvis, (uint64_t)N, 32, 31, L.sort_blocks_g);
-        // entry offsets in that order
-        IA_LAUNCH("sorted_tiles_kernel", sorted_tiles_kernel, dim3(L.nb1), dim3(kBlock), 0, s, gk[gcur], nvis, rect,
-                  srect, bsum);
-        IA_LAUNCH("scan_reduce_kernel", scan_reduce_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2);
-        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, L.nb2, (uint64_t)L.cap, nent,
-                  a.n_entries_out, a.overflow_out);
-        IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(L.nb2), dim3(kBlock), 0, s, bsum, L.nb1, bsum2, boff);
-        OffsetArgs oa{gk[gcur], nvis, srect, boff, fo, a.frames, L.tiles_x, ntiles, (uint64_t)L.cap,
-                      (uint32_t)L.nemit, ginfo, bstart};
+        IA_LAUNCH("binning_mode_kernel", binning_mode_kernel, dim3(1), dim3(64), 0, s, nent, nvis, a.binning, mode);
+        // entries in depth order: one per (Gaussian, tile) or per (Gaussian, region)
+        IA_LAUNCH("sorted_rects_kernel", sorted_rects_kernel, dim3(L.nb1), dim3(kBlock), 0, s, gk[gcur], nvis, mode,
+                  rect, srect, bsum);
+        scan(bsum, L.nb1, cap, nsort, nullptr, nullptr, boff);
+        OffsetArgs oa{gk[gcur], nvis, mode, srect, boff, cap, (uint32_t)L.nemit, fo, a.frames, ginfo, gframe, bstart};
         IA_LAUNCH("offsets_kernel", offsets_kernel, dim3(L.nb1), dim3(kBlock), 0, s, oa);
-        EmitArgs em{ginfo, nvis, bstart, nent, (uint64_t)L.cap, L.tiles_x, ent[0]};
+        EmitArgs em{ginfo, gframe, nvis, mode, bstart, nsort, cap, L.tiles_x, ntiles, (uint32_t)L.regions_x, rpf,
+                    ent[0]};
         IA_LAUNCH("emit_kernel", emit_kernel, dim3(L.nemit), dim3(kBlock), 0, s, em);
-        // stable sort of the depth-ordered entries on the tile index gives
-        // the (tile, depth, Gaussian index) order
-        int tile_bits = 1;
-        while (((int64_t)1 << tile_bits) < L.ntiles_all) ++tile_bits;
-        ecur = radix(ent, nent, (uint64_t)L.cap, 32, tile_bits, L.sort_blocks_e);
+        // stable sort on the tile (or region) index: per tile (region), its
+        // Gaussians in (depth, index) order.  Region indices are below the
+        // tile count, so the tile bits cover both.
+        const int ecur = radix(ent, nsort, cap, 32, bits_for(L.ntiles_all), L.sort_blocks_e);
+        // tile sort: ranges and values from the sorted entries
+        IA_LAUNCH("ranges_kernel", ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s,
+                  ent[ecur], nsort, cap, ranges, (uint32_t)L.ntiles_all, vals, mode, (uint64_t)kModeTiles);
+        // regions: ranges of the regions, work items, count, scan, write
+        IA_LAUNCH("fill_u32_kernel", fill_u32_kernel, dim3(grid_cap(2 * L.nreg, kBlock, 4096)), dim3(kBlock), 0, s,
+                  reinterpret_cast<uint32_t*>(rranges), 0u, 2 * L.nreg);
+        IA_LAUNCH("ranges_kernel", ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s,
+                  ent[ecur], nsort, cap, rranges, (uint32_t)L.nreg, (uint32_t*)nullptr, mode,
+                  (uint64_t)kModeRegions);
+        IA_LAUNCH("region_items_kernel", region_items_kernel, dim3(L.nbr), dim3(kBlock), 0, s, mode, rranges,
+                  (uint32_t)L.nreg, bsum);
+        scan(bsum, L.nbr, kNoCap, nitems, nullptr, nullptr, boff);
+        IA_LAUNCH("region_expand_kernel", region_expand_kernel, dim3(L.nbr), dim3(kBlock), 0, s, mode, rranges,
+                  (uint32_t)L.nreg, boff, (uint64_t)L.max_items, items, rfirst);
+        ExpandArgs xa{mode, items, nitems, rranges, ent[ecur], ginfo, (uint32_t)L.regions_x, rpf, L.tiles_x,
+                      L.tiles_y, ntiles, icnt, tstart, cap, vals};
+        const int xgrid = grid_cap((L.max_items + 3) / 4, 1, 16384);
+        IA_LAUNCH("expand_count_kernel", expand_kernel<false>, dim3(xgrid), dim3(kBlock), 0, s, xa);
+        IA_LAUNCH("region_tiles_kernel", region_tiles_kernel, dim3(grid_cap((L.nreg + 3) / 4, 1, 1 << 30)),
+                  dim3(kBlock), 0, s, mode, rranges, rfirst, (uint32_t)L.nreg, (uint32_t)L.regions_x, rpf, L.tiles_x,
+                  L.tiles_y, ntiles, (uint64_t)L.max_items, icnt, tcount);
+        IA_LAUNCH("tile_sums_kernel", tile_sums_kernel, dim3(L.nbt), dim3(kBlock), 0, s, mode, tcount, L.ntiles_all,
+                  bsum);
+        scan(bsum, L.nbt, kNoCap, ctr + 8, nullptr, nullptr, boff);
+        IA_LAUNCH("tile_ranges_kernel", tile_ranges_kernel, dim3(L.nbt), dim3(kBlock), 0, s, mode, tcount,
+                  L.ntiles_all, boff, cap, tstart, ranges);
+        IA_LAUNCH("expand_write_kernel", expand_kernel<true>, dim3(xgrid), dim3(kBlock), 0, s, xa);
     } else {
-        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, 0, (uint64_t)L.cap, nent,
+        IA_LAUNCH("scan_top_kernel", scan_top_kernel, dim3(1), dim3(kBlock), 0, s, bsum2, 0, cap, nent,
                   a.n_entries_out, a.overflow_out);
     }
-    const int64_t nr = 2 * L.ntiles_all;
-    IA_LAUNCH("fill_u32_kernel", fill_u32_kernel, dim3(grid_cap(nr, kBlock, 4096)), dim3(kBlock), 0, s,
-              reinterpret_cast<uint32_t*>(ranges), 0u, nr);
-    IA_LAUNCH("ranges_kernel", ranges_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, ent[ecur], nent,
-              (uint64_t)L.cap, ranges, (uint32_t)L.ntiles_all);
-    RasterArgs ra{ranges, ent[ecur], pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, (uint64_t)L.cap, N,
-                  a.image, a.T_final, a.n_contrib};
+    RasterArgs ra{ranges, vals, pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, cap, N, a.image, a.T_final,
+                  a.n_contrib};
     IA_LAUNCH("raster_kernel", raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kRasterThreads), 0, s, ra);
     *keys_out = nullptr;
     *vals_out = nullptr;
     if (a.unpack) {
-        uint64_t* keys = ent[ecur ^ 1];
-        uint32_t* vals = reinterpret_cast<uint32_t*>(ws + L.avals);
-        IA_LAUNCH("unpack_kernel", unpack_kernel, dim3(grid_cap(L.cap, kBlock, 8192)), dim3(kBlock), 0, s, ent[ecur],
-                  nent, (uint64_t)L.cap, depth, N, keys, vals);
+        uint64_t* keys = ent[0];
+        if (N > 0)
+            IA_LAUNCH("unpack_kernel", unpack_kernel, dim3(ntiles, a.frames), dim3(kBlock), 0, s, ranges, vals, depth,
+                      N, keys);
         *keys_out = keys;
         *vals_out = vals;
     }

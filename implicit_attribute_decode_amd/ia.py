@@ -27,8 +27,8 @@ IA_ACT_RELU, IA_ACT_GELU = 0, 1
 # Every entry point include/ia.h declares.
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
            "ia_decoder_destroy", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
-           "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render", "ia_profile_enable",
-           "ia_profile_report", "ia_profile_reset")
+           "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render", "ia_render_set_binning",
+           "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
 
 
 class IAError(RuntimeError):
@@ -99,6 +99,7 @@ def load(path: str = LIB_PATH):
         L.ia_hexplane_destroy.restype = None
         L.ia_render_workspace_size.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int64, P]
         L.ia_render.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P]
+        L.ia_render_set_binning.argtypes = [C.c_int32]
         L.ia_profile_enable.argtypes = [C.c_int32]
         L.ia_profile_report.argtypes = [P, C.c_size_t, P]
         L.ia_profile_reset.argtypes = []
@@ -221,6 +222,14 @@ def ia_render(g: Gaussians, frame_offsets, cams, ws, max_entries: int, image, au
 
 
 # ----------------------------------------------------------------- diagnostics
+
+
+BINNING_AUTO, BINNING_TILE_SORT, BINNING_REGIONS = 0, 1, 2
+
+
+def ia_render_set_binning(mode: int):
+    """0 automatic, 1 tile sort, 2 regions (process-wide)."""
+    _check(load().ia_render_set_binning(int(mode)))
 
 
 def ia_profile_enable(on: bool = True):

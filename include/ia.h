@@ -245,6 +245,19 @@ IA_API ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, 
                     void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux,
                     void* stream);
 
+/* How ia_render turns depth-ordered Gaussians into per-tile lists.  Both give
+ * the same lists; they differ in speed.
+ *   0  automatic (default): regions when visible Gaussians touch 4 or more
+ *      tiles on average, else the tile sort;
+ *   1  tile sort: one entry per (Gaussian, tile), stable radix sort on the
+ *      tile index;
+ *   2  regions: one entry per (Gaussian, 8x8-tile region), stable radix sort
+ *      on the region index, then per region a count pass and a write pass
+ *      that place every (Gaussian, tile) entry at its final position.
+ * Process-wide; applies to ia_render calls issued after it returns.
+ * Errors: INVALID_ARG for other values. */
+IA_API ia_status ia_render_set_binning(int32_t mode);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics: per-kernel timing with HIP events                            */
 /* ------------------------------------------------------------------------ */

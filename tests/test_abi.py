@@ -116,3 +116,11 @@ def test_render_argument_errors_are_synchronous():
     fo4 = (C.c_int64 * 2)(0, 4)
     g2 = ia.Gaussians(1024, 0, 1024, 1024, 1024, 1024, 1024, 2)
     assert L.ia_render(C.byref(g2), fo4, 1, C.byref(cam), img, 1 << 30, 10, img, None, None) == ia.IA_ERR_UNSUPPORTED
+
+
+def test_render_binning_mode_is_validated():
+    for bad in (-1, 3, 100):
+        with pytest.raises(ia.IAError):
+            ia.ia_render_set_binning(bad)
+    for ok in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS, ia.BINNING_AUTO):
+        ia.ia_render_set_binning(ok)

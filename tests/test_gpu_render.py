@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle as O
-from implicit_attribute_decode_amd import scenes as S
+from implicit_attribute_decode_amd import ia, scenes as S
 from implicit_attribute_decode_amd.pipeline import Decoder, Renderer
 
 from gpu_util import (check_bins_bitexact, check_image, check_preprocess_bitexact, cuda, gpu_render, host, say)
@@ -39,19 +39,28 @@ def _oracle_render(cams, fo, h):
 
 
 def _full_check(g: dict, fo, cams, tag, cap=None):
+    """Both binnings (tile sort, regions) against the oracle; returns the
+    results of the automatic choice."""
     h = _host_attrs(g)
     pre, b, r = _oracle_render(cams, fo, h)
     cap = cap or max(b["E"], 1)
-    gr = gpu_render(g, fo, cams, cap)
-    say(f"[{tag}] N={int(fo[-1])} E={gr['E']} frames={len(cams)}")
-    check_preprocess_bitexact(gr, pre)
-    vis = pre["tiles"] > 0
-    np.testing.assert_array_equal(gr["opacity"][vis], h["opacity"][vis])
-    np.testing.assert_array_equal(gr["rgb"][vis], h["colors"][vis])
-    check_bins_bitexact(gr, b)
-    st = check_image(gr, r)
-    say(f"[{tag}] image: {st}")
-    return gr, pre, b, r
+    out = None
+    try:
+        for mode in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS, ia.BINNING_AUTO):
+            ia.ia_render_set_binning(mode)
+            gr = gpu_render(g, fo, cams, cap)
+            say(f"[{tag}] binning {mode}: N={int(fo[-1])} E={gr['E']} frames={len(cams)}")
+            check_preprocess_bitexact(gr, pre)
+            vis = pre["tiles"] > 0
+            np.testing.assert_array_equal(gr["opacity"][vis], h["opacity"][vis])
+            np.testing.assert_array_equal(gr["rgb"][vis], h["colors"][vis])
+            check_bins_bitexact(gr, b)
+            st = check_image(gr, r)
+            say(f"[{tag}] binning {mode}: image {st}")
+            out = gr
+    finally:
+        ia.ia_render_set_binning(ia.BINNING_AUTO)
+    return out, pre, b, r
 
 
 def test_tiny_decode_then_render():
@@ -103,6 +112,29 @@ def test_ragged_image_and_empty_frames():
     assert np.all(gr["image"][1] == 0) and np.all(gr["T"][1] == 1)
 
 
+def test_equal_depths_keep_index_order():
+    """Two planes facing an identity camera: p_z = z exactly, so every
+    Gaussian of a plane has the same depth key.  Within a tile, entries of
+    equal key keep the emission (Gaussian index) order; several frames with
+    different plane pairs share one batch."""
+    rng = np.random.default_rng(23)
+    parts, cams = [], []
+    for f, (z0, z1) in enumerate(((3.0, 4.0), (2.5, 2.5), (5.0, 3.0))):
+        n = 2500 + 300 * f
+        xy = rng.uniform(-1.2, 1.2, size=(n, 2))
+        z = np.where(rng.random(n) < 0.5, z0, z1)
+        parts.append(np.concatenate([xy, z[:, None]], 1).astype(np.float32))
+        cams.append(S.origin_camera(96, 80, 70.0))
+    means = np.concatenate(parts)
+    g = S.render_attributes(rng, means, 0.01, 0.08)
+    fo = np.concatenate([[0], np.cumsum([p.shape[0] for p in parts])])
+    gr, pre, b, r = _full_check(_attrs_from_gaussians(g), fo, cams, "ties")
+    vis = pre["tiles"] > 0
+    assert len(np.unique(pre["depth"][vis])) <= 4  # the planes really tie
+    keys = b["keys"]
+    assert (keys[1:] == keys[:-1]).sum() > 1000  # many equal keys inside tiles
+
+
 def test_nan_and_behind_camera_are_culled():
     rng = np.random.default_rng(22)
     g = S.render_attributes(rng, S.shell_points(rng, 2000, 3.0), 1e-2, 1e-1)
@@ -136,10 +168,15 @@ def test_overflow_reports_needed_capacity_then_retry_matches():
     g, cam, _ = S.single_render_scene(n_shell=8000, n_clus=500)
     attrs = _attrs_from_gaussians(g)
     fo = np.array([0, g.n])
-    small = gpu_render(attrs, fo, [cam], 1000)
-    assert small["overflow"] == 1 and small["E"] > 1000
-    full = gpu_render(attrs, fo, [cam], small["E"])
-    assert full["overflow"] == 0 and full["E"] == small["E"]
+    try:
+        for mode in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS):
+            ia.ia_render_set_binning(mode)
+            small = gpu_render(attrs, fo, [cam], 1000)
+            assert small["overflow"] == 1 and small["E"] > 1000
+            full = gpu_render(attrs, fo, [cam], small["E"])
+            assert full["overflow"] == 0 and full["E"] == small["E"]
+    finally:
+        ia.ia_render_set_binning(ia.BINNING_AUTO)
     _full_check(attrs, fo, [cam], "retry", cap=small["E"])
 
 
