@@ -36,6 +36,12 @@ LEVELS, CORNERS, FEAT_BYTES = 16, 16, 4  # fp16 x 2 features per table entry
 GATHER_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES
 # Whole decode per Gaussian: 16 B position in, 1024 B gathered, 44 B out.
 DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
+# HBM-side bytes per gather launch of this workload (mean launch: 3.75M Gaussians), from two
+# rocprofv3 counter runs over `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra
+# --calibrate-copy`: FETCH_SIZE 899,179.2 KiB x 2 + WRITE_SIZE 246,909.0 KiB x 1, the factors being
+# what the counters read for a 1 GiB device copy (profiles/gather_f16_sequence_hbm_traffic.md).
+# Valid for the gather kernel as it was when counted; null once that kernel changes.
+GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 899_179.2 + 246_909.0) * 1024
 
 
 def log(*a):
@@ -71,24 +77,44 @@ HEX_FLOP_PER_GAUSSIAN = 2 * (192 * 256 + 256 * 256 + 256 * 58)  # 259,072
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
-def secondary(S, Decoder, HexPlane, Renderer, stream, log) -> dict:
+def secondary(S, Decoder, HexPlane, Renderer, stream, log, only: str | None = None) -> dict:
     """The other workloads of the hot-path table, each timed with HIP events:
-    one Single frame, the HexPlane deform + SH render, the Stress batch."""
+    one Single frame, the HexPlane deform + SH render, the Stress batch
+    (only: just that one)."""
     import torch
 
     out = {}
-    # Single: one frame, 100k Gaussians, decode + render
+    R = Renderer()
+    if only in (None, "single"):
+        out["single_frame"] = _single(S, Decoder, R, stream)
+    if only in (None, "hexplane"):
+        out["hexplane"] = _hexplane(S, HexPlane, R, stream)
+    if only in (None, "stress"):
+        out["stress"] = _stress(S, Decoder, Renderer, stream)
+    log(f"secondary: {out}")
+    return out
+
+
+def _single(S, Decoder, R, stream) -> dict:
+    """Single: one frame, 100k Gaussians, decode + render."""
+    import torch
+
     dec = S.single_decoder()
     pos, t = S.single_positions(2)
     x = torch.as_tensor(pos, device="cuda")
-    D, R = Decoder(dec), Renderer()
+    D = Decoder(dec)
     a = D.decode(x, t)
     cam = S.ring_camera(0)
     res = R.render(dict(means=x, **a), [0, x.shape[0]], [cam], 8 * x.shape[0], aux=True)
-    cap = Renderer.count_entries(res) + 4096
+    cap = R.count_entries(res) + 4096
     ms = timed(lambda: (D.decode(x, t, out=a), R.render(dict(means=x, **a), [0, x.shape[0]], [cam], cap)), 20, stream)
-    out["single_frame"] = {"gaussians": int(x.shape[0]), "ms": round(ms, 4), "fps": round(1e3 / ms, 1)}
-    # HexPlane: 300k canonical Gaussians, deform at t = 0.5, SH render at 1352x1014
+    return {"gaussians": int(x.shape[0]), "ms": round(ms, 4), "fps": round(1e3 / ms, 1)}
+
+
+def _hexplane(S, HexPlane, R, stream) -> dict:
+    """HexPlane: 300k canonical Gaussians, deform at t = 0.5, SH render at 1352x1014."""
+    import torch
+
     hp = S.hexplane_params()
     cg = S.hexplane_canonical()
     canon = {k: torch.as_tensor(getattr(cg, k), device="cuda") for k in ("means", "scales", "quats", "sh", "opacity")}
@@ -96,17 +122,20 @@ def secondary(S, Decoder, HexPlane, Renderer, stream, log) -> dict:
     d = H.deform(canon, 0.5)
     hcam = S.hexplane_camera()
     res = R.render(d, [0, cg.n], [hcam], 8 * cg.n, aux=True)
-    hcap = Renderer.count_entries(res) + 4096
+    hcap = R.count_entries(res) + 4096
     ms_def = timed(lambda: H.deform(canon, 0.5, out=d), 10, stream)
     hex_kernels = profiled(lambda: H.deform(canon, 0.5, out=d), 3)
     ms_ren = timed(lambda: R.render(d, [0, cg.n], [hcam], hcap), 10, stream)
     tflops = HEX_FLOP_PER_GAUSSIAN * cg.n / (ms_def / 1e3) / 1e12
-    out["hexplane"] = {"gaussians": cg.n, "deform_ms": round(ms_def, 4), "render_ms": round(ms_ren, 4),
-                       "fps": round(1e3 / (ms_def + ms_ren), 1), "mlp_tflops": round(tflops, 1),
-                       "mlp_frac_of_fp16_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                       "deform_kernels_ms": hex_kernels}
-    del d, res, canon, H
-    # Stress: 8 frames x 1M at 1920x1080 (drawn attributes) + decode of the same 8M positions
+    return {"gaussians": cg.n, "deform_ms": round(ms_def, 4), "render_ms": round(ms_ren, 4),
+            "fps": round(1e3 / (ms_def + ms_ren), 1), "mlp_tflops": round(tflops, 1),
+            "mlp_frac_of_fp16_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "deform_kernels_ms": hex_kernels}
+
+
+def _stress(S, Decoder, Renderer, stream) -> dict:
+    """Stress: 8 frames x 1M at 1920x1080 (drawn attributes) + decode of the same 8M positions."""
+    import torch
+
     g, fo, cams, ts = S.stress_scene()
     attrs = {k: torch.as_tensor(getattr(g, k), device="cuda") for k in ("means", "scales", "quats", "colors",
                                                                          "opacity")}
@@ -119,13 +148,12 @@ def secondary(S, Decoder, HexPlane, Renderer, stream, log) -> dict:
     stress_kernels = profiled(lambda: Rs.render(attrs, fo, cams, E + 4096, out=res), 1)
     xyzt = torch.cat([attrs["means"], torch.as_tensor(np.repeat(np.float32(ts), g.n // len(ts)),
                                                       device="cuda")[:, None]], 1).contiguous()
+    D = Decoder(S.single_decoder())
     da = D.decode_xyzt(xyzt)
     ms_d = timed(lambda: D.decode_xyzt(xyzt, out=da), 3, stream)
-    out["stress"] = {"frames": len(cams), "gaussians": g.n, "tile_entries": E, "render_ms": round(ms_r, 3),
-                     "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3),
-                     "render_kernels_ms": stress_kernels}
-    log(f"secondary: {out}")
-    return out
+    return {"frames": len(cams), "gaussians": g.n, "tile_entries": E, "render_ms": round(ms_r, 3),
+            "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3),
+            "render_kernels_ms": stress_kernels}
 
 
 def profiled(fn, reps):
@@ -168,6 +196,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the per-frame comparison and the other workloads (Single, HexPlane, Stress)")
+    ap.add_argument("--only", choices=("single", "hexplane", "stress"),
+                    help="run just that other workload and print its figures (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (a reference for HBM byte counters)")
     args = ap.parse_args()
@@ -182,6 +212,10 @@ def main():
     from implicit_attribute_decode_amd.pipeline import Decoder, HexPlane, Renderer
 
     ia.load()  # fails loudly when the HIP library is missing
+    if args.only:
+        print(json.dumps(secondary(S, Decoder, HexPlane, Renderer, torch.cuda.current_stream(), log, args.only)),
+              flush=True)
+        return
     dev = "cuda"
     seq = S.Sequence(frames=args.frames)
     F, per = seq.frames, seq.per_frame
@@ -280,7 +314,8 @@ def main():
                    "kernels": kernels, **extra},
         "roofline": {"kernel": "gather_f16_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_unit": GATHER_BYTES_PER_GAUSSIAN,
+                     "traffic": round(GATHER_TRAFFIC_BYTES_PER_LAUNCH) if F == 150 and per == 200_000 else None,
+                     "traffic_unit": "bytes/launch", "bytes_per_unit": GATHER_BYTES_PER_GAUSSIAN,
                      "units_per_launch": round(gaussians_per_launch), "avg_launch_ms": round(gather_avg_ms, 4)},
         "cpu_baseline": None,
     }

@@ -120,7 +120,7 @@ struct RenderLayout {
     size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum_t, bsum2, boff, srect, ginfo, gframe, bstart, gk0, gk1, ent0,
         ent1, vals, counts, digit_tot, rranges, rfirst, items, icnt, tcount, tstart, ranges, counters, total;
     int64_t N, cap, ntiles_all, nreg, max_items;
-    int frames, tiles_x, tiles_y, regions_x, regions_y, nb1, nbr, nbt, nemit;
+    int frames, tiles_x, tiles_y, regions_x, regions_y, nb1, nbr, nbt, nemit, emit_per;
     int sort_blocks_g, sort_blocks_e;  // radix-sort blocks over Gaussians / over coarse entries
 };
 

@@ -440,9 +440,9 @@ __global__ void __launch_bounds__(kBlock) sorted_rects_kernel(const uint64_t* gk
     if (threadIdx.x == 0) bsum[blockIdx.x] = total;
 }
 
-// Entries are emitted kEmitPerBlock per block whatever the Gaussians' sizes
+// Entries are emitted `per` per block whatever the Gaussians' sizes
 // (depth order groups the large near Gaussians).
-constexpr int kEmitPerBlock = 16384;
+constexpr int kEmitMax = 16384;  // entries per emission block, at most (at least kBlock)
 
 struct GInfo {
     uint32_t off;  // first entry (clamped to the capacity)
@@ -459,6 +459,7 @@ struct OffsetArgs {
     const uint64_t* boff;
     uint64_t cap;
     uint32_t nemit;    // emission blocks
+    uint32_t per;      // entries per emission block
     const int64_t* fo;
     int F;
     GInfo* info;
@@ -487,7 +488,7 @@ __global__ void __launch_bounds__(kBlock) offsets_kernel(OffsetArgs a) {
     a.info[j] = g;
     a.frame[j] = (uint32_t)frame_of(a.fo, a.F, g.idx);
     // emission blocks whose first entry lies in [off, stop)
-    for (uint64_t b = (off + kEmitPerBlock - 1) / kEmitPerBlock; b * kEmitPerBlock < stop && b < a.nemit; ++b)
+    for (uint64_t b = (off + a.per - 1) / a.per; b * a.per < stop && b < a.nemit; ++b)
         a.bstart[b] = (uint32_t)j;
 }
 
@@ -499,6 +500,7 @@ struct EmitArgs {
     const uint32_t* bstart;
     const uint64_t* nsort;  // entries to emit
     uint64_t cap;
+    uint32_t per;           // entries per block
     int tiles_x;
     uint32_t ntiles;
     uint32_t regions_x;
@@ -512,9 +514,9 @@ __global__ void __launch_bounds__(kBlock) emit_kernel(EmitArgs a) {
     const bool regions = a.mode[0] == kModeRegions;
     uint64_t Ecap = a.nsort[0];
     if (Ecap > a.cap) Ecap = a.cap;
-    const uint64_t e0 = (uint64_t)blockIdx.x * kEmitPerBlock;
+    const uint64_t e0 = (uint64_t)blockIdx.x * a.per;
     if (e0 >= Ecap) return;
-    const uint64_t e1 = e0 + kEmitPerBlock < Ecap ? e0 + kEmitPerBlock : Ecap;
+    const uint64_t e1 = e0 + a.per < Ecap ? e0 + a.per : Ecap;
     const uint64_t nv = a.nvis[0];
     uint64_t jc = a.bstart[blockIdx.x];  // Gaussian holding entry ec
     for (uint64_t ec = e0; ec < e1; ec += kBlock) {
@@ -1070,20 +1072,23 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
     p.done = p.done || p.T < 1e-4f;
 }
 
-// One 128-thread block per 16x16 tile; thread (col, row) shades pixels
-// (col, 2 row) and (col, 2 row + 1), which share dx and the dx terms of
-// power, so a wave covers a 16 x 8 pixel block.  When no pixel of the wave
-// lies within 3 sigma of a Gaussian the wave skips its compositing step
-// (the step would add alpha = 0 everywhere).
+// One block per 16x16 tile.  PX = 2: 128 threads, thread (col, row) shades
+// pixels (col, 2 row) and (col, 2 row + 1), which share dx and the dx terms
+// of power, so a wave covers a 16 x 8 pixel block; PX = 1: 256 threads, one
+// pixel each (twice the waves, for launches with few tiles).  When no pixel
+// of a wave lies within 3 sigma of a Gaussian the wave skips its compositing
+// step (the step would add alpha = 0 everywhere).
 // Gaussians of the tile's list are staged in LDS 256 at a time with the
 // conic pre-scaled by -1/2, -1, -1/2 (exact), so power = A' dx^2 + C' dy^2 +
 // B' dx dy.  A wave leaves a batch once all its pixels are saturated; the
 // block stops once all 256 are.
-constexpr int kRasterThreads = 128;
 constexpr int kRasterBatch = 256;
+constexpr int64_t kRasterTwoPixelTiles = 8192;  // tiles per launch from which two pixels per thread pay
 
-__global__ void __launch_bounds__(kRasterThreads) raster_kernel(RasterArgs a) {
+template <int PX>
+__global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
 #pragma clang fp contract(fast)
+    constexpr int kThreads = 256 / PX;
     __shared__ float4 s_a[kRasterBatch];
     __shared__ float4 s_b[kRasterBatch];
     __shared__ float s_c[kRasterBatch];
@@ -1093,15 +1098,15 @@ __global__ void __launch_bounds__(kRasterThreads) raster_kernel(RasterArgs a) {
     if (rg.y > a.cap) rg.y = (uint32_t)a.cap;
     if (rg.x > rg.y) rg.x = rg.y;
     const int px = blockIdx.x * 16 + (threadIdx.x & 15);
-    const int py0 = blockIdx.y * 16 + 2 * (threadIdx.x >> 4), py1 = py0 + 1;  // a wave: 16 x 8 pixels
-    const bool in0 = px < a.W && py0 < a.H, in1 = px < a.W && py1 < a.H;
+    const int py0 = blockIdx.y * 16 + PX * (threadIdx.x >> 4), py1 = py0 + 1;
+    const bool in0 = px < a.W && py0 < a.H, in1 = PX == 2 && px < a.W && py1 < a.H;
     const float fx = (float)px + 0.5f, fy0 = (float)py0 + 0.5f, fy1 = (float)py1 + 0.5f;
     Pix p0{1.0f, 0.0f, 0.0f, 0.0f, 0u, !in0}, p1{1.0f, 0.0f, 0.0f, 0.0f, 0u, !in1};
     for (uint32_t start = rg.x; start < rg.y; start += kRasterBatch) {
-        if (__syncthreads_count(p0.done && p1.done) == kRasterThreads) break;
+        if (__syncthreads_count(p0.done && p1.done) == kThreads) break;
 #pragma unroll
-        for (int k = 0; k < kRasterBatch / kRasterThreads; ++k) {
-            const uint32_t slot = threadIdx.x + k * kRasterThreads;
+        for (int k = 0; k < kRasterBatch / kThreads; ++k) {
+            const uint32_t slot = threadIdx.x + k * kThreads;
             const uint32_t idx = start + slot;
             if (idx < rg.y) {
                 uint32_t gid = a.vals[idx];
@@ -1122,21 +1127,26 @@ __global__ void __launch_bounds__(kRasterThreads) raster_kernel(RasterArgs a) {
             const float gcb = s_c[j];
             const float dx = fx - ga.x;
             const float ta = ga.z * dx * dx, tb = ga.w * dx;
-            const float dy0 = fy0 - ga.y, dy1 = fy1 - ga.y;
+            const float dy0 = fy0 - ga.y;
             const float pw0 = (ta + gb.x * dy0 * dy0) + tb * dy0;
-            const float pw1 = (ta + gb.x * dy1 * dy1) + tb * dy1;
+            bool any = pw0 >= -4.5f && pw0 <= 0.0f;
+            float pw1 = 0.0f;
+            if (PX == 2) {
+                const float dy1 = fy1 - ga.y;
+                pw1 = (ta + gb.x * dy1 * dy1) + tb * dy1;
+                any = any || (pw1 >= -4.5f && pw1 <= 0.0f);
+            }
             // no pixel of the wave within 3 sigma: nothing to composite
-            const bool any = (pw0 >= -4.5f && pw0 <= 0.0f) || (pw1 >= -4.5f && pw1 <= 0.0f);
             if (__ballot(any) == 0ull) continue;
             composite_step(p0, pw0, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
-            composite_step(p1, pw1, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
+            if (PX == 2) composite_step(p1, pw1, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
         }
     }
     const DevCamera& cam = a.cams[f];
     const size_t plane = (size_t)a.W * a.H;
     float* img = a.image + (size_t)f * 3 * plane;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < PX; ++k) {
         const Pix& p = k ? p1 : p0;
         if (!(k ? in1 : in0)) continue;
         const size_t pix = (size_t)(k ? py1 : py0) * a.W + px;
@@ -1183,7 +1193,10 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     };
     L.sort_blocks_g = blocks(n1);
     L.sort_blocks_e = blocks(cap1);
-    L.nemit = (int)((cap1 + kEmitPerBlock - 1) / kEmitPerBlock);
+    // about 1024 emission blocks of a power of two entries each, kBlock..kEmitMax
+    L.emit_per = kBlock;
+    while (L.emit_per < kEmitMax && (int64_t)L.emit_per * 1024 < cap1) L.emit_per *= 2;
+    L.nemit = (int)((cap1 + L.emit_per - 1) / L.emit_per);
     // coarse entries <= tile entries <= capacity, so items <= cap / kItemCoarse + regions
     L.max_items = (cap1 + kItemCoarse - 1) / kItemCoarse + L.nreg;
     size_t off = 0;
@@ -1334,10 +1347,11 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
         IA_LAUNCH("sorted_rects_kernel", sorted_rects_kernel, dim3(L.nb1), dim3(kBlock), 0, s, gk[gcur], nvis, mode,
                   rect, srect, bsum);
         scan(bsum, L.nb1, cap, nsort, nullptr, nullptr, boff);
-        OffsetArgs oa{gk[gcur], nvis, mode, srect, boff, cap, (uint32_t)L.nemit, fo, a.frames, ginfo, gframe, bstart};
+        OffsetArgs oa{gk[gcur], nvis, mode, srect, boff, cap, (uint32_t)L.nemit, (uint32_t)L.emit_per, fo, a.frames,
+                      ginfo, gframe, bstart};
         IA_LAUNCH("offsets_kernel", offsets_kernel, dim3(L.nb1), dim3(kBlock), 0, s, oa);
-        EmitArgs em{ginfo, gframe, nvis, mode, bstart, nsort, cap, L.tiles_x, ntiles, (uint32_t)L.regions_x, rpf,
-                    ent[0]};
+        EmitArgs em{ginfo, gframe, nvis, mode, bstart, nsort, cap, (uint32_t)L.emit_per, L.tiles_x, ntiles,
+                    (uint32_t)L.regions_x, rpf, ent[0]};
         IA_LAUNCH("emit_kernel", emit_kernel, dim3(L.nemit), dim3(kBlock), 0, s, em);
         // stable sort on the tile (or region) index: per tile (region), its
         // Gaussians in (depth, index) order.  Region indices are below the
@@ -1376,7 +1390,11 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
     }
     RasterArgs ra{ranges, vals, pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, cap, N, a.image, a.T_final,
                   a.n_contrib};
-    IA_LAUNCH("raster_kernel", raster_kernel, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(kRasterThreads), 0, s, ra);
+    // two pixels per thread when there are enough tiles to fill the chip twice over
+    if (L.ntiles_all >= kRasterTwoPixelTiles)
+        IA_LAUNCH("raster_kernel", raster_kernel<2>, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(128), 0, s, ra);
+    else
+        IA_LAUNCH("raster_kernel", raster_kernel<1>, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(256), 0, s, ra);
     *keys_out = nullptr;
     *vals_out = nullptr;
     if (a.unpack) {

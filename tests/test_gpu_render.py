@@ -99,6 +99,18 @@ def test_sequence_three_frames_decoded_batch():
     _full_check(g, fo, cams, "sequence x3")
 
 
+def test_ten_frames_one_call():
+    """Ten 640x360 frames in one call: 9200 tiles, enough for the raster's
+    two-pixels-per-thread launch shape."""
+    rng = np.random.default_rng(24)
+    n = 4000
+    means = np.concatenate([S.shell_points(rng, n, 3.0) for _ in range(10)])
+    g = S.render_attributes(rng, means, 1e-2, 6e-2)
+    fo = np.arange(11) * n
+    cams = [S.ring_camera(k) for k in range(10)]
+    _full_check(_attrs_from_gaussians(g), fo, cams, "ten frames")
+
+
 def test_ragged_image_and_empty_frames():
     """Image size not a multiple of 16, an empty frame in the middle of the
     batch, and frames of different sizes."""
