@@ -32,7 +32,9 @@ __device__ __forceinline__ half8_t cat8(half4_t lo, half4_t hi) {
     return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-constexpr int kG = 3;         // 16-Gaussian column groups per wave
+constexpr int kG = 3;          // 16-Gaussian column groups per wave
+constexpr int kHexWaves = 4;   // waves per block (two blocks per CU)
+constexpr int kHexThreads = 64 * kHexWaves;
 constexpr int kTileHalf8 = 64;  // one A tile = 64 lanes x 8 fp16 = 1 KiB
 
 // Tiled weight buffer (built once per parameter set): A tiles of the three
@@ -75,23 +77,36 @@ __device__ __forceinline__ void axis_cell(float u, int res, int& i, float& f) {
     f = p - (float)c;
 }
 
-// Copy tiles [first, first + n) of the tiled weights into s[0, n) (all threads).
-__device__ __forceinline__ void stage_tiles(half8_t* s, const half8_t* Wt, int first, int n) {
-    for (int k = threadIdx.x; k < n * kTileHalf8; k += 256) s[k] = Wt[first * kTileHalf8 + k];
+// Copy tiles [first, first + N) of the tiled weights into s[0, N) and, with
+// N2 > 0, tiles [first2, first2 + N2) into s[N, N + N2) (all threads): every
+// load is issued before the first store, so a stage costs one L2 round trip
+// rather than one per 4 KiB.
+template <int N, int N2 = 0>
+__device__ __forceinline__ void stage_tiles(half8_t* s, const half8_t* Wt, int first, int first2 = 0) {
+    constexpr int kPer = N * kTileHalf8 / kHexThreads, kPer2 = N2 * kTileHalf8 / kHexThreads;
+    static_assert(N * kTileHalf8 % kHexThreads == 0 && N2 * kTileHalf8 % kHexThreads == 0, "whole rounds");
+    half8_t v[kPer + kPer2];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) v[k] = Wt[first * kTileHalf8 + k * kHexThreads + threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < kPer2; ++k) v[kPer + k] = Wt[first2 * kTileHalf8 + k * kHexThreads + threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < kPer + kPer2; ++k) s[k * kHexThreads + threadIdx.x] = v[k];
 }
 
-// One block = 4 waves x 64 Gaussians.  The weights pass through LDS in
-// chunks of four row blocks (layer 1: 24 tiles; layer 2: 32 tiles plus the
-// 8 layer-3 tiles that consume those rows), so each 1 KiB A tile read from
-// LDS feeds kG MFMAs.  Features, hidden layers and accumulators stay in
-// registers; two blocks per CU overlap one block's staging with the other's
-// MFMAs.
-__global__ void __launch_bounds__(256, 2) hexplane_kernel(HexArgs a, const half8_t* Wt) {
+// One block = kHexWaves waves x 16 kG Gaussians.  The weights pass through LDS
+// in eight chunks of four row blocks (layer 1: 24 tiles; layer 2: 32 tiles
+// plus the 8 layer-3 tiles that consume those rows); each 1 KiB A tile read
+// from LDS feeds kG MFMAs (one per 16-Gaussian column group), and row blocks
+// go in pairs so that a wave has 2 kG independent accumulation chains.
+// Features, hidden layers and accumulators stay in registers; two blocks per
+// CU overlap one block's staging with the other's MFMAs.
+__global__ void __launch_bounds__(kHexThreads, 2) hexplane_kernel(HexArgs a, const half8_t* Wt) {
 #pragma clang fp contract(fast)
     __shared__ half8_t s_w[40 * kTileHalf8];
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, c = lane & 15;
-    const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 * kG;
+    const int64_t base = ((int64_t)blockIdx.x * kHexWaves + (threadIdx.x >> 6)) * 16 * kG;
     const int C = 32;
     const float t = a.t < 0.0f ? 0.0f : (a.t > 1.0f ? 1.0f : a.t);
 
@@ -136,12 +151,14 @@ __global__ void __launch_bounds__(256, 2) hexplane_kernel(HexArgs a, const half8
                     out[4 * hsel + e] = (_Float16)s;
                 }
             }
-            // materialise the interpolated features here: left to the
-            // compiler, the interpolation sinks to its first use and every
-            // plane's raw corner loads stay live across the staging barriers
-            asm volatile("" : "+v"(out));
             X[p][g] = out;
         }
+        // materialise this column group's features here (its 48 corner loads
+        // are in flight together): left to the compiler, the interpolation
+        // sinks to its first use and the raw corner loads of every group stay
+        // live across the staging barriers
+#pragma unroll
+        for (int p = 0; p < 6; ++p) asm volatile("" : "+v"(X[p][g]));
     }
 
     // ---- layer 1: 192 -> 256, ReLU, fp16; H1[m][g] = k-block m of layer 2's B operand
@@ -149,31 +166,40 @@ __global__ void __launch_bounds__(256, 2) hexplane_kernel(HexArgs a, const half8
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         __syncthreads();
-        stage_tiles(s_w, Wt, 24 * r, 24);
+        stage_tiles<24>(s_w, Wt, 24 * r);
         __syncthreads();
+        const half8_t* sw = s_w;
+        // two row blocks at a time: 2 kG independent accumulation chains,
+        // together one k-block of layer 2's B operand
 #pragma unroll
-        for (int rbl = 0; rbl < 4; ++rbl) {
-            const int rb = 4 * r + rbl;
-            floatx4 acc[kG];
+        for (int i = 0; i < 2; ++i) {
+            const int rb = 4 * r + 2 * i;
+            floatx4 acc0[kG], acc1[kG];
 #pragma unroll
-            for (int g = 0; g < kG; ++g) acc[g] = floatx4{0, 0, 0, 0};
+            for (int g = 0; g < kG; ++g) acc0[g] = acc1[g] = floatx4{0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < 6; ++m) {
-                const half8_t A = s_w[(rbl * 6 + m) * kTileHalf8 + lane];
+                const half8_t A0 = sw[((2 * i) * 6 + m) * kTileHalf8 + lane];
+                const half8_t A1 = sw[((2 * i + 1) * 6 + m) * kTileHalf8 + lane];
 #pragma unroll
-                for (int g = 0; g < kG; ++g) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, X[m][g], acc[g], 0, 0, 0);
+                for (int g = 0; g < kG; ++g) {
+                    acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, X[m][g], acc0[g], 0, 0, 0);
+                    acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, X[m][g], acc1[g], 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int g = 0; g < kG; ++g)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = acc[g][e] + a.b[0][16 * rb + 4 * q + e];
-                    H1[rb >> 1][g][4 * (rb & 1) + e] = (_Float16)(v > 0.0f ? v : 0.0f);
+                    const float v0 = acc0[g][e] + a.b[0][16 * rb + 4 * q + e];
+                    const float v1 = acc1[g][e] + a.b[0][16 * (rb + 1) + 4 * q + e];
+                    H1[2 * r + i][g][e] = (_Float16)(v0 > 0.0f ? v0 : 0.0f);
+                    H1[2 * r + i][g][4 + e] = (_Float16)(v1 > 0.0f ? v1 : 0.0f);
                 }
             // convert now (fp32 accumulators would otherwise stay live until
             // layer 2) and keep later row blocks' loads from being hoisted
 #pragma unroll
-            for (int g = 0; g < kG; ++g) asm volatile("" : "+v"(H1[rb >> 1][g]));
+            for (int g = 0; g < kG; ++g) asm volatile("" : "+v"(H1[2 * r + i][g]));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -187,37 +213,39 @@ __global__ void __launch_bounds__(256, 2) hexplane_kernel(HexArgs a, const half8
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         __syncthreads();
-        stage_tiles(s_w, Wt, kL1Tiles + 32 * r, 32);
-        stage_tiles(s_w + 32 * kTileHalf8, Wt, kL1Tiles + kL2Tiles + 8 * r, 8);
+        stage_tiles<32, 8>(s_w, Wt, kL1Tiles + 32 * r, kL1Tiles + kL2Tiles + 8 * r);
         __syncthreads();
+        const half8_t* sw = s_w;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+            // the two row blocks of this k-block of layer 3 together
+            const int rb = 4 * r + 2 * half;
+            floatx4 acc0[kG], acc1[kG];
+#pragma unroll
+            for (int g = 0; g < kG; ++g) acc0[g] = acc1[g] = floatx4{0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const half8_t A0 = sw[((2 * half) * 8 + m) * kTileHalf8 + lane];
+                const half8_t A1 = sw[((2 * half + 1) * 8 + m) * kTileHalf8 + lane];
+#pragma unroll
+                for (int g = 0; g < kG; ++g) {
+                    acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, H1[m][g], acc0[g], 0, 0, 0);
+                    acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, H1[m][g], acc1[g], 0, 0, 0);
+                }
+            }
             half8_t H2[kG];
 #pragma unroll
-            for (int hsel = 0; hsel < 2; ++hsel) {
-                const int rbl = 2 * half + hsel, rb = 4 * r + rbl;
-                floatx4 acc[kG];
+            for (int g = 0; g < kG; ++g)
 #pragma unroll
-                for (int g = 0; g < kG; ++g) acc[g] = floatx4{0, 0, 0, 0};
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const half8_t A = s_w[(rbl * 8 + m) * kTileHalf8 + lane];
-#pragma unroll
-                    for (int g = 0; g < kG; ++g)
-                        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, H1[m][g], acc[g], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) {
+                    const float v0 = acc0[g][e] + a.b[1][16 * rb + 4 * q + e];
+                    const float v1 = acc1[g][e] + a.b[1][16 * (rb + 1) + 4 * q + e];
+                    H2[g][e] = (_Float16)(v0 > 0.0f ? v0 : 0.0f);
+                    H2[g][4 + e] = (_Float16)(v1 > 0.0f ? v1 : 0.0f);
                 }
 #pragma unroll
-                for (int g = 0; g < kG; ++g)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = acc[g][e] + a.b[1][16 * rb + 4 * q + e];
-                        H2[g][4 * hsel + e] = (_Float16)(v > 0.0f ? v : 0.0f);
-                    }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
             for (int r3 = 0; r3 < 4; ++r3) {
-                const half8_t A = s_w[(32 + 4 * half + r3) * kTileHalf8 + lane];
+                const half8_t A = sw[(32 + 4 * half + r3) * kTileHalf8 + lane];
 #pragma unroll
                 for (int g = 0; g < kG; ++g)
                     acc3[r3][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, H2[g], acc3[r3][g], 0, 0, 0);
@@ -291,10 +319,10 @@ hipError_t launch_hexplane_tiles(const _Float16* const W[3], void* Wt, hipStream
 
 hipError_t launch_hexplane(const HexArgs& a, const void* Wt, hipStream_t s) {
     if (a.N <= 0) return hipSuccess;
-    const int64_t per_block = 4 * 16 * kG;
+    const int64_t per_block = kHexWaves * 16 * kG;
     const int64_t grid = (a.N + per_block - 1) / per_block;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    IA_LAUNCH("hexplane_kernel", hexplane_kernel, dim3((unsigned)grid), dim3(256), 0, s, a,
+    IA_LAUNCH("hexplane_kernel", hexplane_kernel, dim3((unsigned)grid), dim3(kHexThreads), 0, s, a,
               static_cast<const half8_t*>(Wt));
     return hipGetLastError();
 }
