@@ -247,7 +247,7 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // normalize_kernel: Eq. 7-8 once per Gaussian -> x~ (fp32 x4) in the scratch.
 //
 // gather_f16_kernel: level-major.  Block b handles level b / nchunk and
-// Gaussians [1024 (b % nchunk), +1024).  Blocks are dispatched in index order
+// Gaussians [256 (b % nchunk), +256).  Blocks are dispatched in index order
 // and spread round-robin over the XCDs, so at any moment all XCDs work on the
 // same level and that level's 2^log2T x 4-byte table stays resident in every
 // XCD's L2 instead of being fetched line by line from HBM / Infinity Cache.
@@ -264,7 +264,7 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // B column c, each with eight k-slots per lane that A and B share; D holds
 // rows 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows.
 
-constexpr int kGatherPerBlock = 1024;  // Gaussians per gather block (64 per pass x 16 passes)
+constexpr int kGatherPerBlock = 256;  // Gaussians per gather block (64 per pass x 4 passes)
 
 __global__ void __launch_bounds__(256) normalize_kernel(DecodeArgs a, const float* pos, int64_t n, float4* xt) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(256) gather_f16_kernel(const float4* xt, int64
     const int bx = s & 1, by = s >> 1;
     const int sub = threadIdx.x >> 2;        // Gaussian slot within a pass (0..63)
     const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
-#pragma unroll 4
+#pragma unroll 2
     for (int j = 0; j < kGatherPerBlock / 64; ++j) {
         const int64_t i = first + j * 64 + sub;
         if (i >= n) break;  // uniform across each group of four lanes
