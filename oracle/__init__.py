@@ -82,6 +82,8 @@ def _declare(L):
     L.orc_bin.restype = C.c_long
     L.orc_bin.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, C.c_long, P, P, P]
     L.orc_raster_tiles.argtypes = [C.c_int, P, P, P, P, P, P, P, P, P, P, P]
+    L.orc_render_grad.argtypes = [P, C.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    L.orc_render_grad.restype = None
     L.orc_raster_brute.argtypes = [P, C.c_long, C.c_long, P, P, P, P, P, P, P, C.c_int, P, C.c_long,
                                    P, P, P, P]
 
@@ -345,3 +347,31 @@ def render(cams, frame_offsets, means, scales, quats, opacity, colors) -> dict:
     b = bin_and_sort(cams, frame_offsets, pre)
     r = raster_tiles(cams, b, pre, opacity, colors)
     return dict(pre=pre, bins=b, **r)
+
+
+def render_grad(cams, frame_offsets, means, scales, quats, opacity, colors, gimg) -> dict:
+    """fp64 forward + backward of an image-space gradient gimg = dL/dimage
+    [F,3,H,W] (inputs taken as float64): returns image, per-Gaussian gradients (means [N,3], scales
+    [N,3], quats [N,4], opacity [N], colors [N,3], proj [N,9] for (u, v, A,
+    B, C, o, r, g, b)), flags [N] (near a threshold) and the decision
+    signature."""
+    fo = _c(frame_offsets, np.int64)
+    F = len(cams)
+    N = int(fo[-1])
+    W, H = int(cams[0].W), int(cams[0].H)
+    cam_arr = cameras(cams)
+    means, scales, quats = _c(means, np.float64), _c(scales, np.float64), _c(quats, np.float64)
+    opacity, colors, gimg = _c(opacity, np.float64), _c(colors, np.float64), _c(gimg, np.float64)
+    assert gimg.shape == (F, 3, H, W)
+    out = dict(image=np.zeros((F, 3, H, W)), proj=np.zeros((max(N, 1), 9)), means=np.zeros((max(N, 1), 3)),
+               scales=np.zeros((max(N, 1), 3)), quats=np.zeros((max(N, 1), 4)), opacity=np.zeros(max(N, 1)),
+               colors=np.zeros((max(N, 1), 3)), flags=np.zeros(max(N, 1), np.uint8))
+    sig = C.c_uint64(0)
+    lib().orc_render_grad(cam_arr, F, _p(fo), _p(means), _p(scales), _p(quats), _p(opacity), _p(colors), _p(gimg),
+                          _p(out["image"]), _p(out["proj"]), _p(out["means"]), _p(out["scales"]), _p(out["quats"]),
+                          _p(out["opacity"]), _p(out["colors"]), _p(out["flags"]), C.byref(sig))
+    for k in ("proj", "means", "scales", "quats", "opacity", "colors", "flags"):
+        out[k] = out[k][:N]
+    out["flags"] = out["flags"].astype(bool)
+    out["signature"] = int(sig.value)
+    return out

@@ -804,3 +804,312 @@ EXPORT void orc_raster_brute(const orc_camera* cam, long g0, long g1, const floa
     }
     free(ord);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Gradients of an image loss w.r.t. the Gaussians ([SPIN] §3.1 Eq. 1-4 and  */
+/* the EWA projection, differentiated by hand), fp64 throughout               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * fp64 projection of one Gaussian with the intermediates the backward pass
+ * needs.  Same definitions and culling rules as project_one, evaluated in
+ * double: p = R mu + t; qn = q / |q|; Rq(qn); M = Rq diag(s); Sigma = M M^T;
+ * J = [[fx/z, 0, -fx x/z^2], [0, fy/z, -fy y/z^2]]; T = J R; Sigma2D =
+ * T Sigma T^T = [[a, b], [b, c]]; conic (A, B, C) = (c, -b, a) / (a c - b^2);
+ * (u, v) = (fx x / z + cx, fy y / z + cy); r = ceil(3 sqrt(lambda_max)).
+ */
+typedef struct {
+    int vis;
+    double p[3], qn[4], qlen, Rq[9], M[9], S[9], T[6], a, b, c, det;
+    double u, v, A, B, C, depth;
+    int tx0, tx1, ty0, ty1;
+} orc_g64;
+
+static void project64(const orc_camera* cam, const double* mu, const double* s, const double* q, orc_g64* o) {
+    memset(o, 0, sizeof(*o));
+    const float* R = cam->R;
+    for (int k = 0; k < 3; ++k)
+        o->p[k] = (double)R[k * 3] * mu[0] + (double)R[k * 3 + 1] * mu[1] + (double)R[k * 3 + 2] * mu[2] + cam->t[k];
+    if (!(o->p[2] > cam->near_z)) return;
+    double qq = 0.0;
+    for (int k = 0; k < 4; ++k) qq += q[k] * q[k];
+    o->qlen = sqrt(qq);
+    for (int k = 0; k < 4; ++k) o->qn[k] = q[k] / o->qlen;
+    double w = o->qn[0], x = o->qn[1], y = o->qn[2], z = o->qn[3];
+    double* Rq = o->Rq;
+    Rq[0] = 1 - 2 * (y * y + z * z); Rq[1] = 2 * (x * y - w * z); Rq[2] = 2 * (x * z + w * y);
+    Rq[3] = 2 * (x * y + w * z); Rq[4] = 1 - 2 * (x * x + z * z); Rq[5] = 2 * (y * z - w * x);
+    Rq[6] = 2 * (x * z - w * y); Rq[7] = 2 * (y * z + w * x); Rq[8] = 1 - 2 * (x * x + y * y);
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) o->M[i * 3 + j] = Rq[i * 3 + j] * s[j];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < 3; ++k) acc += o->M[i * 3 + k] * o->M[j * 3 + k];
+            o->S[i * 3 + j] = acc;
+        }
+    double pz = o->p[2];
+    double j00 = cam->fx / pz, j02 = -cam->fx * o->p[0] / (pz * pz);
+    double j11 = cam->fy / pz, j12 = -cam->fy * o->p[1] / (pz * pz);
+    for (int k = 0; k < 3; ++k) {
+        o->T[k] = j00 * R[k] + j02 * R[6 + k];
+        o->T[3 + k] = j11 * R[3 + k] + j12 * R[6 + k];
+    }
+    double c2[4];
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < 3; ++k)
+                for (int l = 0; l < 3; ++l) acc += o->T[i * 3 + k] * o->S[k * 3 + l] * o->T[j * 3 + l];
+            c2[i * 2 + j] = acc;
+        }
+    o->a = c2[0]; o->b = c2[1]; o->c = c2[3];
+    o->det = o->a * o->c - o->b * o->b;
+    if (!(o->det > 0.0)) return;
+    o->A = o->c / o->det; o->B = -o->b / o->det; o->C = o->a / o->det;
+    double mid = 0.5 * (o->a + o->c);
+    double disc = mid * mid - o->det;
+    double lam = mid + sqrt(disc > 0.0 ? disc : 0.0);
+    double r = ceil(3.0 * sqrt(lam));
+    o->u = cam->fx * o->p[0] / pz + cam->cx;
+    o->v = cam->fy * o->p[1] / pz + cam->cy;
+    if (!(isfinite(o->u) && isfinite(o->v) && isfinite(o->A) && isfinite(o->B) && isfinite(o->C) && isfinite(r)))
+        return;
+    double x0 = ceil((o->u - r) - 0.5), x1 = floor((o->u + r) - 0.5);
+    double y0 = ceil((o->v - r) - 0.5), y1 = floor((o->v + r) - 0.5);
+    x0 = x0 > 0 ? x0 : 0; y0 = y0 > 0 ? y0 : 0;
+    x1 = x1 < cam->W - 1 ? x1 : cam->W - 1; y1 = y1 < cam->H - 1 ? y1 : cam->H - 1;
+    if (!(x0 <= x1 && y0 <= y1)) return;
+    o->depth = pz;
+    o->tx0 = (int)x0 / 16; o->tx1 = (int)x1 / 16; o->ty0 = (int)y0 / 16; o->ty1 = (int)y1 / 16;
+    o->vis = 1;
+}
+
+/* Chain the gradient of (u, v, A, B, C) back to (mu, s, q) for one projected
+ * Gaussian (see project64 for the definitions). */
+static void project64_backward(const orc_camera* cam, const double* s, const orc_g64* o, const double g2[5],
+                               double gmu[3], double gs[3], double gq[4]) {
+    const float* R = cam->R;
+    double gu = g2[0], gv = g2[1], gA = g2[2], gB = g2[3], gC = g2[4];
+    /* conic = Sigma2D^-1: dL/dSigma2D = -K G K with G the symmetric gradient of K */
+    double K[4] = {o->A, o->B, o->B, o->C};
+    double G[4] = {gA, 0.5 * gB, 0.5 * gB, gC};
+    double KG[4], GS[4];
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) KG[i * 2 + j] = K[i * 2] * G[j] + K[i * 2 + 1] * G[2 + j];
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) GS[i * 2 + j] = -(KG[i * 2] * K[j] + KG[i * 2 + 1] * K[2 + j]);
+    /* Sigma2D = T Sigma T^T: dL/dT = 2 GS T Sigma, dL/dSigma = T^T GS T */
+    double TS[6];
+    for (int i = 0; i < 2; ++i)
+        for (int k = 0; k < 3; ++k) {
+            double acc = 0.0;
+            for (int l = 0; l < 3; ++l) acc += o->T[i * 3 + l] * o->S[l * 3 + k];
+            TS[i * 3 + k] = acc;
+        }
+    double GT[6];
+    for (int i = 0; i < 2; ++i)
+        for (int k = 0; k < 3; ++k) GT[i * 3 + k] = 2.0 * (GS[i * 2] * TS[k] + GS[i * 2 + 1] * TS[3 + k]);
+    double GSig[9];
+    for (int k = 0; k < 3; ++k)
+        for (int l = 0; l < 3; ++l) {
+            double acc = 0.0;
+            for (int i = 0; i < 2; ++i)
+                for (int j = 0; j < 2; ++j) acc += o->T[i * 3 + k] * GS[i * 2 + j] * o->T[j * 3 + l];
+            GSig[k * 3 + l] = acc;
+        }
+    /* T = J R: dL/dJ = GT R^T (J has entries j00, j02, j11, j12) */
+    double gj00 = 0, gj02 = 0, gj11 = 0, gj12 = 0;
+    for (int k = 0; k < 3; ++k) {
+        gj00 += GT[k] * R[0 * 3 + k];
+        gj02 += GT[k] * R[2 * 3 + k];
+        gj11 += GT[3 + k] * R[1 * 3 + k];
+        gj12 += GT[3 + k] * R[2 * 3 + k];
+    }
+    double px = o->p[0], py = o->p[1], pz = o->p[2];
+    double fx = cam->fx, fy = cam->fy;
+    double gp[3];
+    gp[0] = gu * fx / pz + gj02 * (-fx / (pz * pz));
+    gp[1] = gv * fy / pz + gj12 * (-fy / (pz * pz));
+    gp[2] = gu * (-fx * px / (pz * pz)) + gv * (-fy * py / (pz * pz)) + gj00 * (-fx / (pz * pz)) +
+            gj02 * (2.0 * fx * px / (pz * pz * pz)) + gj11 * (-fy / (pz * pz)) + gj12 * (2.0 * fy * py / (pz * pz * pz));
+    for (int k = 0; k < 3; ++k) gmu[k] = R[0 * 3 + k] * gp[0] + R[1 * 3 + k] * gp[1] + R[2 * 3 + k] * gp[2];
+    /* Sigma = M M^T: dL/dM = 2 GSig M;  M = Rq diag(s) */
+    double GM[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < 3; ++k) acc += GSig[i * 3 + k] * o->M[k * 3 + j];
+            GM[i * 3 + j] = 2.0 * acc;
+        }
+    double GR[9];
+    for (int j = 0; j < 3; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < 3; ++i) {
+            acc += GM[i * 3 + j] * o->Rq[i * 3 + j];
+            GR[i * 3 + j] = GM[i * 3 + j] * s[j];
+        }
+        gs[j] = acc;
+    }
+    /* Rq(w, x, y, z) of the unit quaternion, then through q / |q| */
+    double w = o->qn[0], x = o->qn[1], y = o->qn[2], z = o->qn[3];
+    double gn[4];
+    gn[0] = 2.0 * (-z * GR[1] + y * GR[2] + z * GR[3] - x * GR[5] - y * GR[6] + x * GR[7]);
+    gn[1] = 2.0 * (y * GR[1] + z * GR[2] + y * GR[3] - 2.0 * x * GR[4] - w * GR[5] + z * GR[6] + w * GR[7] -
+                   2.0 * x * GR[8]);
+    gn[2] = 2.0 * (-2.0 * y * GR[0] + x * GR[1] + w * GR[2] + x * GR[3] + z * GR[5] - w * GR[6] + z * GR[7] -
+                   2.0 * y * GR[8]);
+    gn[3] = 2.0 * (-2.0 * z * GR[0] - w * GR[1] + x * GR[2] + w * GR[3] - 2.0 * z * GR[4] + y * GR[5] + x * GR[6] +
+                   y * GR[7]);
+    double dot = gn[0] * w + gn[1] * x + gn[2] * y + gn[3] * z;
+    for (int k = 0; k < 4; ++k) gq[k] = (gn[k] - dot * o->qn[k]) / o->qlen;
+}
+
+typedef struct { double depth; uint32_t idx; } orc_dsort;
+
+static int cmp_dsort(const void* a, const void* b) {
+    const orc_dsort* x = (const orc_dsort*)a;
+    const orc_dsort* y = (const orc_dsort*)b;
+    if (x->depth != y->depth) return x->depth < y->depth ? -1 : 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+static uint64_t mix64(uint64_t h, uint64_t v) {
+    h ^= v + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+    return h * 0xff51afd7ed558ccdull;
+}
+
+/*
+ * Forward (fp64 projection, fp64 compositing with the rules of composite())
+ * and backward of a given image-space gradient gimg = dL/dimage [F][3][H][W].
+ * Per pixel, the frame's visible Gaussians whose tile rect holds the pixel's
+ * tile are composited in (depth, index) order; the backward pass walks the
+ * composited ones from the last to the first with
+ *   T_i = T_{i+1} / (1 - alpha_i)  (T after the last = T_final)
+ *   dL/dc_i = g alpha_i T_i,   dL/dalpha_i = g . (c_i T_i - S_i / (1 - alpha_i))
+ *   S_i = sum_{j > i} c_j alpha_j T_j + T_final bg  (what lies behind i)
+ *   alpha = o exp(power) unless clamped at 0.99 (then constant)
+ *   power = -0.5 (A dx^2 + C dy^2) - B dx dy,  d = (px + 0.5 - u, py + 0.5 - v)
+ * and each Gaussian's (u, v, A, B, C) gradient is chained to (mu, s, q) by
+ * project64_backward.  Outputs (all optional but gproj): image [F][3][H][W];
+ * gproj [N][9] = d/d(u, v, A, B, C, o, r, g, b); gmeans [N][3], gscales [N][3],
+ * gquats [N][4], gopacity [N], gcolors [N][3]; gflag [N] = 1 if the Gaussian
+ * took part in a decision within rounding of a threshold (compare only
+ * unflagged ones); *signature = a hash of every discrete decision (which
+ * Gaussians composite each pixel, clamps, stops): equal signatures mean
+ * equal decisions.
+ */
+EXPORT void orc_render_grad(const orc_camera* cams, int F, const long* frame_offsets, const double* means,
+                            const double* scales, const double* quats, const double* opacity, const double* colors,
+                            const double* gimg, double* image, double* gproj, double* gmeans, double* gscales,
+                            double* gquats, double* gopacity, double* gcolors, uint8_t* gflag, uint64_t* signature) {
+    long N = frame_offsets[F];
+    int W = cams[0].W, H = cams[0].H;
+    orc_g64* P = (orc_g64*)malloc(sizeof(orc_g64) * (size_t)(N > 0 ? N : 1));
+    for (long i = 0; i < N; ++i)
+        project64(&cams[frame_of(frame_offsets, F, i)], means + i * 3, scales + i * 3, quats + i * 4, &P[i]);
+    for (long i = 0; i < N * 9; ++i) gproj[i] = 0.0;
+    if (gflag) memset(gflag, 0, (size_t)N);
+    uint64_t sig = 0;
+    const double u32 = 5.9604644775390625e-08;
+    for (int f = 0; f < F; ++f) {
+        long g0 = frame_offsets[f], g1 = frame_offsets[f + 1];
+        const orc_camera* cam = &cams[f];
+        orc_dsort* ord = (orc_dsort*)malloc(sizeof(orc_dsort) * (size_t)(g1 - g0 > 0 ? g1 - g0 : 1));
+        long n = 0;
+        for (long i = g0; i < g1; ++i)
+            if (P[i].vis) { ord[n].depth = P[i].depth; ord[n].idx = (uint32_t)i; ++n; }
+        qsort(ord, (size_t)n, sizeof(orc_dsort), cmp_dsort);
+        uint32_t* taken = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
+        double* talpha = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double* tG = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        int* tclamp = (int*)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+        for (int py = 0; py < H; ++py)
+            for (int px = 0; px < W; ++px) {
+                int tx = px / 16, ty = py / 16;
+                double T = 1.0, Cc[3] = {0, 0, 0}, relT = 0.0;
+                long m = 0;
+                int fl = 0;
+                uint64_t hp = mix64((uint64_t)f, (uint64_t)(py * W + px));
+                for (long k = 0; k < n; ++k) {
+                    uint32_t i = ord[k].idx;
+                    const orc_g64* o = &P[i];
+                    if (!(o->tx0 <= tx && tx <= o->tx1 && o->ty0 <= ty && ty <= o->ty1)) continue;
+                    double dx = px + 0.5 - o->u, dy = py + 0.5 - o->v;
+                    double quad = o->A * dx * dx + o->C * dy * dy, cross = o->B * dx * dy;
+                    double power = -0.5 * quad - cross;
+                    double mag = 0.5 * fabs(quad) + fabs(cross);
+                    double err_p = 2.0 * 6.0 * u32 * mag;
+                    int near = fabs(power + 4.5) <= err_p || (fabs(power) <= err_p && mag > 0.0);
+                    if (power < -4.5 || power > 0.0) { if (near) { fl = 1; if (gflag) gflag[i] = 1; } continue; }
+                    double G = exp(power), ga = opacity[i] * G;
+                    double rel_a = 2.0 * (10.0 * u32 + 6.0 * u32 * mag);
+                    if (fabs(ga - 0.99) <= rel_a * 0.99) near = 1;
+                    int clamp = !(ga < 0.99);
+                    double alpha = clamp ? 0.99 : ga;
+                    if (fabs(alpha - 1.0 / 255.0) <= rel_a / 255.0) near = 1;
+                    if (near) { fl = 1; if (gflag) gflag[i] = 1; }
+                    if (alpha < 1.0 / 255.0) continue;
+                    for (int ch = 0; ch < 3; ++ch) Cc[ch] += colors[i * 3 + ch] * alpha * T;
+                    T = T * (1.0 - alpha);
+                    taken[m] = i; talpha[m] = alpha; tG[m] = G; tclamp[m] = clamp; ++m;
+                    hp = mix64(hp, (uint64_t)i * 2 + (uint64_t)clamp);
+                    relT += 2.0 * (2.0 * u32 + alpha / (1.0 - alpha) * rel_a * 0.5);
+                    if (fabs(T - 1e-4) <= relT * 1e-4) { fl = 1; if (gflag) gflag[i] = 1; }
+                    if (T < 1e-4) break;
+                }
+                sig += hp;
+                long pix = ((long)f * H + py) * W + px;
+                if (image)
+                    for (int ch = 0; ch < 3; ++ch) image[((long)f * 3 + ch) * H * W + (long)py * W + px] = Cc[ch] + T * cam->bg[ch];
+                if (fl)
+                    for (long k = 0; k < m; ++k)
+                        if (gflag) gflag[taken[k]] = 1;
+                double g[3];
+                for (int ch = 0; ch < 3; ++ch) g[ch] = gimg[((long)f * 3 + ch) * H * W + (long)py * W + px];
+                double acc[3];
+                for (int ch = 0; ch < 3; ++ch) acc[ch] = T * cam->bg[ch];
+                double Tn = T;
+                for (long k = m - 1; k >= 0; --k) {
+                    uint32_t i = taken[k];
+                    const orc_g64* o = &P[i];
+                    double alpha = talpha[k];
+                    double Ti = Tn / (1.0 - alpha);
+                    double galpha = 0.0;
+                    for (int ch = 0; ch < 3; ++ch) {
+                        double ci = colors[i * 3 + ch];
+                        gproj[i * 9 + 6 + ch] += g[ch] * alpha * Ti;
+                        galpha += g[ch] * (ci * Ti - acc[ch] / (1.0 - alpha));
+                        acc[ch] += ci * alpha * Ti;
+                    }
+                    Tn = Ti;
+                    if (tclamp[k]) continue;
+                    gproj[i * 9 + 5] += galpha * tG[k];
+                    double gpow = galpha * alpha;
+                    double dx = px + 0.5 - o->u, dy = py + 0.5 - o->v;
+                    gproj[i * 9 + 0] += gpow * (o->A * dx + o->B * dy);
+                    gproj[i * 9 + 1] += gpow * (o->C * dy + o->B * dx);
+                    gproj[i * 9 + 2] += gpow * (-0.5 * dx * dx);
+                    gproj[i * 9 + 3] += gpow * (-dx * dy);
+                    gproj[i * 9 + 4] += gpow * (-0.5 * dy * dy);
+                }
+                (void)pix;
+            }
+        free(ord); free(taken); free(talpha); free(tG); free(tclamp);
+    }
+    for (long i = 0; i < N; ++i) {
+        double gmu[3] = {0, 0, 0}, gs[3] = {0, 0, 0}, gq[4] = {0, 0, 0, 0};
+        if (P[i].vis)
+            project64_backward(&cams[frame_of(frame_offsets, F, i)], scales + i * 3, &P[i], gproj + i * 9, gmu, gs, gq);
+        for (int k = 0; k < 3; ++k) {
+            if (gmeans) gmeans[i * 3 + k] = gmu[k];
+            if (gscales) gscales[i * 3 + k] = gs[k];
+            if (gcolors) gcolors[i * 3 + k] = gproj[i * 9 + 6 + k];
+        }
+        for (int k = 0; k < 4; ++k)
+            if (gquats) gquats[i * 4 + k] = gq[k];
+        if (gopacity) gopacity[i] = gproj[i * 9 + 5];
+    }
+    if (signature) *signature = sig;
+    free(P);
+}
