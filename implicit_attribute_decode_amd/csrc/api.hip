@@ -433,9 +433,15 @@ ia_status ia_render_workspace_size(int64_t N_total, int32_t frames, int32_t W, i
     return IA_OK;
 }
 
-ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames, const ia_camera* cams,
-                    void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux, void* stream) {
-    if (!g || !frame_offsets || !cams || !image) return fail(IA_ERR_INVALID_ARG, "null argument");
+}  // extern "C"
+
+namespace {
+
+// Validates the arguments ia_render and ia_render_backward share; on success
+// *N, *W, *H hold the Gaussian count and the common image size.
+ia_status check_render_args(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames, const ia_camera* cams,
+                            void* ws, size_t ws_bytes, int64_t max_entries, int64_t* N_out, int* W_out, int* H_out) {
+    if (!g || !frame_offsets || !cams) return fail(IA_ERR_INVALID_ARG, "null argument");
     if (frames < 1 || frames > 65535) return fail(IA_ERR_INVALID_ARG, "frames must be in 1..65535");
     if (frame_offsets[0] != 0) return fail(IA_ERR_INVALID_ARG, "frame_offsets[0] must be 0");
     for (int f = 0; f < frames; ++f)
@@ -469,6 +475,23 @@ ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t
     if (!ws || !aligned(ws, 256)) return fail(IA_ERR_INVALID_ARG, "workspace must be non-null and 256-byte aligned");
     if (ws_bytes < need)
         return fail(IA_ERR_WORKSPACE_TOO_SMALL, "workspace too small: need " + std::to_string(need) + " bytes");
+    *N_out = N;
+    *W_out = W;
+    *H_out = H;
+    return IA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames, const ia_camera* cams,
+                    void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux, void* stream) {
+    if (!image) return fail(IA_ERR_INVALID_ARG, "null argument");
+    int64_t N = 0;
+    int W = 0, H = 0;
+    ia_status st = check_render_args(g, frame_offsets, frames, cams, ws, ws_bytes, max_entries, &N, &W, &H);
+    if (st != IA_OK) return st;
 
     // camera table (centre = -R^T t, for SH view directions)
     std::string err;
@@ -533,6 +556,53 @@ ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t
         aux->tiles_touched = reinterpret_cast<const uint32_t*>(w + a.lay.tiles);
         aux->tile_rect = reinterpret_cast<const uint16_t*>(w + a.lay.rect);
     }
+    return IA_OK;
+}
+
+
+ia_status ia_render_backward(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames, const ia_camera* cams,
+                             void* ws, size_t ws_bytes, int64_t max_entries, const float* grad_image,
+                             const float* T_final, const uint32_t* n_contrib, const ia_gaussian_grads* grads,
+                             void* stream) {
+    if (!grads) return fail(IA_ERR_INVALID_ARG, "null argument");
+    int64_t N = 0;
+    int W = 0, H = 0;
+    ia_status st = check_render_args(g, frame_offsets, frames, cams, ws, ws_bytes, max_entries, &N, &W, &H);
+    if (st != IA_OK) return st;
+    if (N > 0 && g->sh_degree != -1)
+        return fail(IA_ERR_UNSUPPORTED, "the render backward takes direct colours (sh_degree = -1)");
+    if (!grad_image || !T_final || !n_contrib) return fail(IA_ERR_INVALID_ARG, "grad_image, T_final, n_contrib must be non-null");
+    if (N > 0 && (!grads->means || !grads->scales || !grads->quats || !grads->opacity || !grads->colors))
+        return fail(IA_ERR_INVALID_ARG, "every gradient buffer must be non-null");
+    ia::RenderBwdArgs a{};
+    a.ws = static_cast<unsigned char*>(ws);
+    a.lay = ia::render_layout(N, frames, W, H, max_entries);
+    a.W = W;
+    a.H = H;
+    a.means = g->means;
+    a.means_stride = g->means_stride == 0 ? 3 : g->means_stride;
+    a.scales = g->scales;
+    a.quats = g->quats;
+    a.grad_image = grad_image;
+    a.T_final = T_final;
+    a.n_contrib = n_contrib;
+    a.g_means = grads->means;
+    a.g_scales = grads->scales;
+    a.g_quats = grads->quats;
+    a.g_opacity = grads->opacity;
+    a.g_colors = grads->colors;
+    hipError_t e = ia::launch_render_backward(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "render backward launch");
+    return IA_OK;
+}
+
+ia_status ia_l1_loss(const float* image, const float* target, int64_t n, double* loss, float* grad_image,
+                     void* stream) {
+    if (n < 0) return fail(IA_ERR_INVALID_ARG, "n must be >= 0");
+    if (!loss) return fail(IA_ERR_INVALID_ARG, "loss is null");
+    if (n > 0 && (!image || !target || !grad_image)) return fail(IA_ERR_INVALID_ARG, "null argument");
+    hipError_t e = ia::launch_l1_loss(image, target, n, loss, grad_image, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "l1 loss launch");
     return IA_OK;
 }
 

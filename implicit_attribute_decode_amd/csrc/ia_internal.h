@@ -118,7 +118,7 @@ struct DevCamera {
 // Byte offsets of every buffer inside the render workspace.
 struct RenderLayout {
     size_t cams, fo, pa, pb, pc, depth, rect, tiles, bsum, bsum_t, bsum2, boff, srect, ginfo, gframe, bstart, gk0, gk1, ent0,
-        ent1, vals, counts, digit_tot, rranges, rfirst, items, icnt, tcount, tstart, ranges, counters, total;
+        ent1, vals, counts, digit_tot, rranges, rfirst, items, icnt, tcount, tstart, ranges, counters, gacc, total;
     int64_t N, cap, ntiles_all, nreg, max_items;
     int frames, tiles_x, tiles_y, regions_x, regions_y, nb1, nbr, nbt, nemit, emit_per;
     int sort_blocks_g, sort_blocks_e;  // radix-sort blocks over Gaussians / over coarse entries
@@ -152,5 +152,33 @@ struct RenderArgs {
 // Enqueue the whole render.  With unpack set, returns the sorted keys and
 // values through keys_out / vals_out (else both are null).
 hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** keys_out, const uint32_t** vals_out);
+
+// Partials per Gaussian the raster backward accumulates in the workspace
+// (gacc): d/d(u, v, A, B, C, opacity, r, g, b).
+constexpr int kGradPerGaussian = 9;
+
+struct RenderBwdArgs {
+    unsigned char* ws;  // workspace of the forward render with the same arguments
+    RenderLayout lay;
+    int W, H;
+    const float* means;
+    int means_stride;
+    const float* scales;
+    const float* quats;
+    const float* grad_image;  // [F,3,H,W]
+    const float* T_final;     // [F,H,W]
+    const uint32_t* n_contrib;
+    float* g_means;  // [N,3]
+    float* g_scales;
+    float* g_quats;  // [N,4]
+    float* g_opacity;
+    float* g_colors;
+};
+
+hipError_t launch_render_backward(const RenderBwdArgs& a, hipStream_t s);
+
+// L = mean |image - target| into *loss (device double); grad = dL/dimage.
+hipError_t launch_l1_loss(const float* image, const float* target, int64_t n, double* loss, float* grad,
+                          hipStream_t s);
 
 }  // namespace ia

@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ia_internal.h"
+#include "raster_common.h"
 
 namespace ia {
 namespace {
@@ -1060,8 +1061,8 @@ struct Pix {
 __device__ __forceinline__ void composite_step(Pix& p, float power, float opacity, float cr, float cg, float cb,
                                                uint32_t pos) {
 #pragma clang fp contract(fast)
-    const float a0 = fminf(0.99f, opacity * __expf(power));
-    const bool take = !p.done && power >= -4.5f && power <= 0.0f && a0 >= (1.0f / 255.0f);
+    const float a0 = splat_alpha(opacity, power);
+    const bool take = !p.done && splat_takes(power, a0);
     const float alpha = take ? a0 : 0.0f;
     const float wgt = alpha * p.T;
     p.r += cr * wgt;
@@ -1126,14 +1127,15 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
             const float4 gb = s_b[j];
             const float gcb = s_c[j];
             const float dx = fx - ga.x;
-            const float ta = ga.z * dx * dx, tb = ga.w * dx;
+            float ta, tb;
+            splat_dx_terms(ga.z, ga.w, dx, ta, tb);
             const float dy0 = fy0 - ga.y;
-            const float pw0 = (ta + gb.x * dy0 * dy0) + tb * dy0;
+            const float pw0 = splat_power(ta, tb, gb.x, dy0);
             bool any = pw0 >= -4.5f && pw0 <= 0.0f;
             float pw1 = 0.0f;
             if (PX == 2) {
                 const float dy1 = fy1 - ga.y;
-                pw1 = (ta + gb.x * dy1 * dy1) + tb * dy1;
+                pw1 = splat_power(ta, tb, gb.x, dy1);
                 any = any || (pw1 >= -4.5f && pw1 <= 0.0f);
             }
             // no pixel of the wave within 3 sigma: nothing to composite
@@ -1237,6 +1239,7 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     L.tstart = take(4 * (size_t)L.ntiles_all);
     L.ranges = take(8 * (size_t)L.ntiles_all);
     L.counters = take(128);
+    L.gacc = take(4 * (size_t)kGradPerGaussian * (size_t)n1);
     L.total = off;
     return L;
 }

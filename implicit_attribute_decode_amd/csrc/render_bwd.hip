@@ -1,0 +1,377 @@
+// Backward pass of the tile rasteriser and of the EWA projection ("SPIN-4DGS"
+// §3.1, Eq. 1-4; Eq. 2-3 differentiated by hand) for an image-space loss
+// gradient dL/dimage, and the L1 image loss itself.
+//
+//   raster_backward_kernel  one 256-thread block per tile, one pixel per
+//       thread.  Each pixel walks its tile's list from the last composited
+//       Gaussian (n_contrib) back to the first, re-deciding every step with
+//       the forward's arithmetic (raster_common.h) and recovering
+//       T_i = T_{i+1} / (1 - alpha_i) from T_final:
+//         dL/dc_i     = g alpha_i T_i
+//         dL/dalpha_i = g . (c_i T_i - S_i / (1 - alpha_i)),
+//                       S_i = sum_{j>i} c_j alpha_j T_j + T_final bg
+//         alpha = o exp(power) (constant where clamped at 0.99), power =
+//         -0.5 (A dx^2 + C dy^2) - B dx dy, d = pixel centre - mean.
+//       The nine partials of a Gaussian (u, v, A, B, C, o, r, g, b) are
+//       summed over a wave with cross-lane adds, over the block in LDS, and
+//       added once per (Gaussian, tile) to its accumulator in global memory.
+//   preprocess_backward_kernel  one thread per Gaussian: (u, v, A, B, C) ->
+//       (mean, scale, quaternion) through the conic inverse, Sigma2D =
+//       T Sigma T^T, T = J W and Sigma = (Rq S)(Rq S)^T; opacity and colour
+//       partials are copied out.
+#include <hip/hip_runtime.h>
+
+#include "ia_internal.h"
+#include "raster_common.h"
+
+namespace ia {
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdBatch = 256;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+struct RasterBwdArgs {
+    const uint2* ranges;
+    const uint32_t* vals;
+    const float4* pa;
+    const float4* pb;
+    const float* pc;
+    const DevCamera* cams;
+    int W, H, tiles_x;
+    uint32_t ntiles;
+    uint64_t cap;
+    int64_t N;
+    const float* gimg;
+    const float* T_final;
+    const uint32_t* n_contrib;
+    float* gacc;  // [N][9]
+};
+
+__global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdArgs a) {
+#pragma clang fp contract(fast)
+    __shared__ float4 s_a[kBwdBatch];  // u, v, -A/2, -B
+    __shared__ float4 s_b[kBwdBatch];  // -C/2, o, r, g
+    __shared__ float s_c[kBwdBatch];   // b
+    __shared__ uint32_t s_id[kBwdBatch];
+    __shared__ float s_g[kBwdBatch][kGradPerGaussian];
+    __shared__ uint32_t s_maxnc;
+    const int f = blockIdx.z;
+    const uint32_t tile = (uint32_t)f * a.ntiles + blockIdx.y * (uint32_t)a.tiles_x + blockIdx.x;
+    uint2 rg = a.ranges[tile];
+    if (rg.y > a.cap) rg.y = (uint32_t)a.cap;
+    if (rg.x > rg.y) rg.x = rg.y;
+    const int lane = threadIdx.x & 63;
+    const int px = blockIdx.x * 16 + (threadIdx.x & 15), py = blockIdx.y * 16 + (threadIdx.x >> 4);
+    const bool in = px < a.W && py < a.H;
+    const size_t plane = (size_t)a.W * a.H;
+    const size_t pix = (size_t)py * a.W + px;
+    const DevCamera& cam = a.cams[f];
+    uint32_t nc = 0;
+    float T = 1.0f, g[3] = {0.0f, 0.0f, 0.0f};
+    if (in) {
+        nc = a.n_contrib[(size_t)f * plane + pix];
+        T = a.T_final[(size_t)f * plane + pix];
+        for (int k = 0; k < 3; ++k) g[k] = a.gimg[((size_t)f * 3 + k) * plane + pix];
+    }
+    float acc[3];
+    for (int k = 0; k < 3; ++k) acc[k] = T * cam.bg[k];
+    if (threadIdx.x == 0) s_maxnc = 0;
+    __syncthreads();
+    if (nc) atomicMax(&s_maxnc, nc);
+    __syncthreads();
+    const uint32_t len = rg.y - rg.x;
+    const int maxnc = (int)(s_maxnc < len ? s_maxnc : len);
+    const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
+    for (int end = maxnc; end > 0; end -= kBwdBatch) {
+        const int start = end - kBwdBatch > 0 ? end - kBwdBatch : 0;
+        const int n = end - start;
+        if ((int)threadIdx.x < n) {
+            uint32_t gid = a.vals[rg.x + start + threadIdx.x];
+            if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
+            const float4 pa = a.pa[gid], pb = a.pb[gid];
+            s_a[threadIdx.x] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
+            s_b[threadIdx.x] = make_float4(-0.5f * pb.x, pb.y, pb.z, pb.w);
+            s_c[threadIdx.x] = a.pc[gid];
+            s_id[threadIdx.x] = gid;
+        }
+        for (int k = threadIdx.x; k < kBwdBatch * kGradPerGaussian; k += kBwdThreads) (&s_g[0][0])[k] = 0.0f;
+        __syncthreads();
+        for (int j = n - 1; j >= 0; --j) {
+            const uint32_t pos1 = (uint32_t)(start + j + 1);  // 1-based list position
+            const float4 ga = s_a[j];
+            const float4 gb = s_b[j];
+            const float dx = fx - ga.x;
+            float ta, tb;
+            splat_dx_terms(ga.z, ga.w, dx, ta, tb);
+            const float dy = fy - ga.y;
+            const float power = splat_power(ta, tb, gb.x, dy);
+            const float a0 = splat_alpha(gb.y, power);
+            const bool take = pos1 <= nc && splat_takes(power, a0);
+            if (__ballot(take) == 0ull) continue;
+            float gv[kGradPerGaussian];
+#pragma unroll
+            for (int k = 0; k < kGradPerGaussian; ++k) gv[k] = 0.0f;
+            if (take) {
+                const float one_m = 1.0f - a0;
+                const float Ti = T / one_m;
+                const float c[3] = {gb.z, gb.w, s_c[j]};
+                float galpha = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    gv[6 + k] = g[k] * a0 * Ti;
+                    galpha += g[k] * (c[k] * Ti - acc[k] / one_m);
+                    acc[k] += c[k] * a0 * Ti;
+                }
+                T = Ti;
+                if (a0 < 0.99f) {  // alpha not clamped
+                    gv[5] = galpha * __expf(power);
+                    const float gp = galpha * a0;
+                    const float A = -2.0f * ga.z, B = -ga.w, C = -2.0f * gb.x;
+                    gv[0] = gp * (A * dx + B * dy);
+                    gv[1] = gp * (C * dy + B * dx);
+                    gv[2] = gp * (-0.5f * dx * dx);
+                    gv[3] = gp * (-dx * dy);
+                    gv[4] = gp * (-0.5f * dy * dy);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kGradPerGaussian; ++k) {
+                const float sum = wave_sum(gv[k]);
+                if (lane == 0 && sum != 0.0f) atomicAdd(&s_g[j][k], sum);
+            }
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < n) {
+            float* dst = a.gacc + (size_t)s_id[threadIdx.x] * kGradPerGaussian;
+#pragma unroll
+            for (int k = 0; k < kGradPerGaussian; ++k) {
+                const float v = s_g[threadIdx.x][k];
+                if (v != 0.0f) atomicAdd(dst + k, v);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+struct PreBwdArgs {
+    const float* means;
+    int stride;
+    const float* scales;
+    const float* quats;
+    const DevCamera* cams;
+    const int64_t* fo;
+    int F;
+    int64_t N;
+    const uint32_t* tiles;
+    const float* gacc;
+    float* g_means;  // [N][3]
+    float* g_scales;
+    float* g_quats;
+    float* g_opacity;
+    float* g_colors;
+};
+
+__device__ __forceinline__ int frame_index(const int64_t* fo, int F, int64_t i) {
+    int lo = 0, hi = F - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (fo[mid] <= i)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ void __launch_bounds__(256) preprocess_backward_kernel(PreBwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.N) return;
+    float gmu[3] = {0, 0, 0}, gs[3] = {0, 0, 0}, gq[4] = {0, 0, 0, 0};
+    const float* gi = a.gacc + i * kGradPerGaussian;
+    const bool vis = a.tiles[i] > 0;
+    if (vis) {
+        const DevCamera& cam = a.cams[frame_index(a.fo, a.F, i)];
+        const float* R = cam.R;
+        const float* mu = a.means + i * a.stride;
+        const float* s = a.scales + i * 3;
+        const float* q = a.quats + i * 4;
+        float p[3];
+        for (int k = 0; k < 3; ++k) p[k] = (R[k * 3] * mu[0] + R[k * 3 + 1] * mu[1]) + R[k * 3 + 2] * mu[2] + cam.t[k];
+        const float qlen = sqrtf(q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3]);
+        const float w = q[0] / qlen, x = q[1] / qlen, y = q[2] / qlen, z = q[3] / qlen;
+        float Rq[9];
+        Rq[0] = 1.0f - 2.0f * (y * y + z * z);
+        Rq[1] = 2.0f * (x * y - w * z);
+        Rq[2] = 2.0f * (x * z + w * y);
+        Rq[3] = 2.0f * (x * y + w * z);
+        Rq[4] = 1.0f - 2.0f * (x * x + z * z);
+        Rq[5] = 2.0f * (y * z - w * x);
+        Rq[6] = 2.0f * (x * z - w * y);
+        Rq[7] = 2.0f * (y * z + w * x);
+        Rq[8] = 1.0f - 2.0f * (x * x + y * y);
+        float M[9], S[9];
+        for (int r = 0; r < 3; ++r)
+            for (int c = 0; c < 3; ++c) M[r * 3 + c] = Rq[r * 3 + c] * s[c];
+        for (int r = 0; r < 3; ++r)
+            for (int c = 0; c < 3; ++c) S[r * 3 + c] = M[r * 3] * M[c * 3] + M[r * 3 + 1] * M[c * 3 + 1] + M[r * 3 + 2] * M[c * 3 + 2];
+        const float pz = p[2], pz2 = pz * pz;
+        const float j00 = cam.fx / pz, j02 = -cam.fx * p[0] / pz2, j11 = cam.fy / pz, j12 = -cam.fy * p[1] / pz2;
+        float T[6];
+        for (int k = 0; k < 3; ++k) {
+            T[k] = j00 * R[k] + j02 * R[6 + k];
+            T[3 + k] = j11 * R[3 + k] + j12 * R[6 + k];
+        }
+        float TS[6];
+        for (int r = 0; r < 2; ++r)
+            for (int k = 0; k < 3; ++k) TS[r * 3 + k] = T[r * 3] * S[k] + T[r * 3 + 1] * S[3 + k] + T[r * 3 + 2] * S[6 + k];
+        float c2[4];
+        for (int r = 0; r < 2; ++r)
+            for (int c = 0; c < 2; ++c) c2[r * 2 + c] = TS[r * 3] * T[c * 3] + TS[r * 3 + 1] * T[c * 3 + 1] + TS[r * 3 + 2] * T[c * 3 + 2];
+        const float det = c2[0] * c2[3] - c2[1] * c2[1];
+        const float Kc[4] = {c2[3] / det, -c2[1] / det, -c2[1] / det, c2[0] / det};
+        // conic = Sigma2D^-1: dL/dSigma2D = -K G K (G: symmetric gradient of the conic matrix)
+        const float G[4] = {gi[2], 0.5f * gi[3], 0.5f * gi[3], gi[4]};
+        float KG[4], GS[4];
+        for (int r = 0; r < 2; ++r)
+            for (int c = 0; c < 2; ++c) KG[r * 2 + c] = Kc[r * 2] * G[c] + Kc[r * 2 + 1] * G[2 + c];
+        for (int r = 0; r < 2; ++r)
+            for (int c = 0; c < 2; ++c) GS[r * 2 + c] = -(KG[r * 2] * Kc[c] + KG[r * 2 + 1] * Kc[2 + c]);
+        // Sigma2D = T Sigma T^T: dL/dT = 2 GS T Sigma, dL/dSigma = T^T GS T
+        float GT[6];
+        for (int r = 0; r < 2; ++r)
+            for (int k = 0; k < 3; ++k) GT[r * 3 + k] = 2.0f * (GS[r * 2] * TS[k] + GS[r * 2 + 1] * TS[3 + k]);
+        float GSig[9];
+        for (int k = 0; k < 3; ++k)
+            for (int l = 0; l < 3; ++l) {
+                float acc = 0.0f;
+                for (int r = 0; r < 2; ++r)
+                    for (int c = 0; c < 2; ++c) acc += T[r * 3 + k] * GS[r * 2 + c] * T[c * 3 + l];
+                GSig[k * 3 + l] = acc;
+            }
+        // T = J W: dL/dJ = GT W^T
+        float gj00 = 0, gj02 = 0, gj11 = 0, gj12 = 0;
+        for (int k = 0; k < 3; ++k) {
+            gj00 += GT[k] * R[k];
+            gj02 += GT[k] * R[6 + k];
+            gj11 += GT[3 + k] * R[3 + k];
+            gj12 += GT[3 + k] * R[6 + k];
+        }
+        const float gu = gi[0], gv = gi[1];
+        const float pz3 = pz2 * pz;
+        float gp[3];
+        gp[0] = gu * cam.fx / pz - gj02 * cam.fx / pz2;
+        gp[1] = gv * cam.fy / pz - gj12 * cam.fy / pz2;
+        gp[2] = -gu * cam.fx * p[0] / pz2 - gv * cam.fy * p[1] / pz2 - gj00 * cam.fx / pz2 +
+                gj02 * 2.0f * cam.fx * p[0] / pz3 - gj11 * cam.fy / pz2 + gj12 * 2.0f * cam.fy * p[1] / pz3;
+        for (int k = 0; k < 3; ++k) gmu[k] = R[k] * gp[0] + R[3 + k] * gp[1] + R[6 + k] * gp[2];
+        // Sigma = M M^T: dL/dM = 2 GSig M; M = Rq diag(s)
+        float GR[9];
+        for (int c = 0; c < 3; ++c) {
+            float acc = 0.0f;
+            for (int r = 0; r < 3; ++r) {
+                const float gm = 2.0f * (GSig[r * 3] * M[c] + GSig[r * 3 + 1] * M[3 + c] + GSig[r * 3 + 2] * M[6 + c]);
+                acc += gm * Rq[r * 3 + c];
+                GR[r * 3 + c] = gm * s[c];
+            }
+            gs[c] = acc;
+        }
+        // Rq of the unit quaternion, then through q / |q|
+        float gn[4];
+        gn[0] = 2.0f * (-z * GR[1] + y * GR[2] + z * GR[3] - x * GR[5] - y * GR[6] + x * GR[7]);
+        gn[1] = 2.0f * (y * GR[1] + z * GR[2] + y * GR[3] - 2.0f * x * GR[4] - w * GR[5] + z * GR[6] + w * GR[7] -
+                        2.0f * x * GR[8]);
+        gn[2] = 2.0f * (-2.0f * y * GR[0] + x * GR[1] + w * GR[2] + x * GR[3] + z * GR[5] - w * GR[6] + z * GR[7] -
+                        2.0f * y * GR[8]);
+        gn[3] = 2.0f * (-2.0f * z * GR[0] - w * GR[1] + x * GR[2] + w * GR[3] - 2.0f * z * GR[4] + y * GR[5] +
+                        x * GR[6] + y * GR[7]);
+        const float dot = gn[0] * w + gn[1] * x + gn[2] * y + gn[3] * z;
+        gq[0] = (gn[0] - dot * w) / qlen;
+        gq[1] = (gn[1] - dot * x) / qlen;
+        gq[2] = (gn[2] - dot * y) / qlen;
+        gq[3] = (gn[3] - dot * z) / qlen;
+    }
+    for (int k = 0; k < 3; ++k) {
+        a.g_means[i * 3 + k] = gmu[k];
+        a.g_scales[i * 3 + k] = gs[k];
+        a.g_colors[i * 3 + k] = vis ? gi[6 + k] : 0.0f;
+    }
+    for (int k = 0; k < 4; ++k) a.g_quats[i * 4 + k] = gq[k];
+    a.g_opacity[i] = vis ? gi[5] : 0.0f;
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
+}
+
+__global__ void zero_f64_kernel(double* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0.0;
+}
+
+// L = mean |image - target|; dL/dimage = sign(image - target) / n (0 where equal).
+__global__ void __launch_bounds__(256) l1_loss_kernel(const float* img, const float* tgt, int64_t n, double* loss,
+                                                      float* grad) {
+    __shared__ double s_sum[4];
+    const float inv = 1.0f / (float)n;
+    double local = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const float x = img[i], y = tgt[i];
+        grad[i] = x > y ? inv : (x < y ? -inv : 0.0f);
+        local += fabs((double)x - (double)y);  // exact in double
+    }
+    for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o, 64);
+    if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = local;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(loss, (s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3]) / (double)n);
+}
+
+int blocks_for(int64_t n, int per, int cap) {
+    int64_t b = (n + per - 1) / per;
+    if (b < 1) b = 1;
+    if (b > cap) b = cap;
+    return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_render_backward(const RenderBwdArgs& a, hipStream_t s) {
+    const RenderLayout& L = a.lay;
+    unsigned char* ws = a.ws;
+    const int64_t N = L.N;
+    float* gacc = reinterpret_cast<float*>(ws + L.gacc);
+    const DevCamera* cams = reinterpret_cast<const DevCamera*>(ws + L.cams);
+    const int64_t* fo = reinterpret_cast<const int64_t*>(ws + L.fo);
+    if (N <= 0) return hipSuccess;
+    IA_LAUNCH("fill_f32_kernel", fill_f32_kernel, dim3(blocks_for(N * kGradPerGaussian, 256, 8192)), dim3(256), 0, s,
+              gacc, N * kGradPerGaussian);
+    RasterBwdArgs rb{reinterpret_cast<const uint2*>(ws + L.ranges), reinterpret_cast<const uint32_t*>(ws + L.vals),
+                     reinterpret_cast<const float4*>(ws + L.pa), reinterpret_cast<const float4*>(ws + L.pb),
+                     reinterpret_cast<const float*>(ws + L.pc), cams, a.W, a.H, L.tiles_x,
+                     (uint32_t)(L.tiles_x * L.tiles_y), (uint64_t)L.cap, N, a.grad_image, a.T_final, a.n_contrib,
+                     gacc};
+    IA_LAUNCH("raster_backward_kernel", raster_backward_kernel, dim3(L.tiles_x, L.tiles_y, L.frames),
+              dim3(kBwdThreads), 0, s, rb);
+    PreBwdArgs pb{a.means, a.means_stride, a.scales, a.quats, cams, fo, L.frames, N,
+                  reinterpret_cast<const uint32_t*>(ws + L.tiles), gacc, a.g_means, a.g_scales, a.g_quats,
+                  a.g_opacity, a.g_colors};
+    IA_LAUNCH("preprocess_backward_kernel", preprocess_backward_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0,
+              s, pb);
+    return hipGetLastError();
+}
+
+hipError_t launch_l1_loss(const float* image, const float* target, int64_t n, double* loss, float* grad,
+                          hipStream_t s) {
+    IA_LAUNCH("zero_f64_kernel", zero_f64_kernel, dim3(1), dim3(64), 0, s, loss);
+    if (n > 0)
+        IA_LAUNCH("l1_loss_kernel", l1_loss_kernel, dim3(blocks_for(n, 256, 4096)), dim3(256), 0, s, image, target, n,
+                  loss, grad);
+    return hipGetLastError();
+}
+
+}  // namespace ia

@@ -28,7 +28,7 @@ IA_ACT_RELU, IA_ACT_GELU = 0, 1
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
            "ia_decoder_destroy", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
            "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render", "ia_render_set_binning",
-           "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
+           "ia_render_backward", "ia_l1_loss", "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
 
 
 class IAError(RuntimeError):
@@ -72,6 +72,11 @@ class RenderAux(C.Structure):
                 ("tile_rect", C.c_void_p)]
 
 
+class GaussianGrads(C.Structure):
+    _fields_ = [("means", C.c_void_p), ("scales", C.c_void_p), ("quats", C.c_void_p), ("opacity", C.c_void_p),
+                ("colors", C.c_void_p)]
+
+
 _lib = None
 P = C.c_void_p
 
@@ -100,6 +105,8 @@ def load(path: str = LIB_PATH):
         L.ia_render_workspace_size.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int64, P]
         L.ia_render.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P]
         L.ia_render_set_binning.argtypes = [C.c_int32]
+        L.ia_render_backward.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P, P, P]
+        L.ia_l1_loss.argtypes = [P, P, C.c_int64, P, P, P]
         L.ia_profile_enable.argtypes = [C.c_int32]
         L.ia_profile_report.argtypes = [P, C.c_size_t, P]
         L.ia_profile_reset.argtypes = []
@@ -219,6 +226,23 @@ def ia_render(g: Gaussians, frame_offsets, cams, ws, max_entries: int, image, au
     _check(load().ia_render(C.byref(g), fo.ctypes.data_as(C.c_void_p), F, arr, _ptr(ws),
                             int(ws.numel() * ws.element_size()), int(max_entries), _ptr(image),
                             None if aux is None else C.byref(aux), _stream(stream)))
+
+
+def ia_render_backward(g: Gaussians, frame_offsets, cams, ws, max_entries: int, grad_image, T_final, n_contrib,
+                       grads: GaussianGrads, stream=None):
+    """Same g / frame_offsets / cams / ws / max_entries as the ia_render it differentiates."""
+    fo = np.ascontiguousarray(frame_offsets, np.int64)
+    F = len(cams)
+    arr = (Camera * F)(*[camera(c) for c in cams])
+    _check(load().ia_render_backward(C.byref(g), fo.ctypes.data_as(C.c_void_p), F, arr, _ptr(ws),
+                                     int(ws.numel() * ws.element_size()), int(max_entries), _ptr(grad_image),
+                                     _ptr(T_final), _ptr(n_contrib), C.byref(grads), _stream(stream)))
+
+
+def ia_l1_loss(image, target, loss, grad_image, stream=None):
+    """loss: device float64 [1]; grad_image like image."""
+    _check(load().ia_l1_loss(_ptr(image), _ptr(target), int(image.numel()), _ptr(loss), _ptr(grad_image),
+                             _stream(stream)))
 
 
 # ----------------------------------------------------------------- diagnostics

@@ -152,6 +152,35 @@ class Renderer:
             res["_ws"] = ws
         return res
 
+    def backward(self, g: dict, frame_offsets, cams, max_entries: int, res: dict, grad_image):
+        """Gradients of the render `res` (made by render(..., aux=True) with
+        the same g, frame_offsets, cams, max_entries and this workspace) for
+        dL/dimage = grad_image.  Returns dict means, scales, quats, opacity,
+        colors (cuda float32, packed rows)."""
+        fo = np.asarray(frame_offsets, np.int64)
+        N = int(fo[-1])
+        F, W, H = len(cams), int(cams[0].W), int(cams[0].H)
+        ws = self.workspace(N, F, W, H, max_entries)
+        means = g["means"]
+        stride = int(means.stride(0)) if means.dim() == 2 else 3
+        G = ia.gaussians(means=means, scales=g["scales"], quats=g["quats"], colors=g.get("colors"), sh=g.get("sh"),
+                         opacity=g["opacity"], means_stride=stride, sh_degree=3 if g.get("sh") is not None else -1)
+        out = {k: torch.empty(shape, device=self.device)
+               for k, shape in (("means", (N, 3)), ("scales", (N, 3)), ("quats", (N, 4)), ("opacity", (N,)),
+                                ("colors", (N, 3)))}
+        GG = ia.GaussianGrads(*[ia._ptr(out[k]) for k in ("means", "scales", "quats", "opacity", "colors")])
+        ia.ia_render_backward(G, fo, cams, ws, max_entries, grad_image.contiguous(), res["T_final"],
+                              res["n_contrib"], GG)
+        return out
+
+    @staticmethod
+    def l1_loss(image, target):
+        """(loss [1] float64 on the device, dL/dimage)."""
+        loss = torch.empty(1, dtype=torch.float64, device=image.device)
+        grad = torch.empty_like(image)
+        ia.ia_l1_loss(image.contiguous(), target.contiguous(), loss, grad)
+        return loss, grad
+
     @staticmethod
     def count_entries(res: dict) -> int:
         return int(res["n_entries"].item())

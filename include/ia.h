@@ -245,6 +245,43 @@ IA_API ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, 
                     void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux,
                     void* stream);
 
+/* Per-Gaussian gradient buffers (device, float32, packed rows). */
+typedef struct {
+    float* means;   /* [N][3] dL/dmean                                   */
+    float* scales;  /* [N][3] dL/dscale                                  */
+    float* quats;   /* [N][4] dL/dquaternion (of the unnormalised input) */
+    float* opacity; /* [N]    dL/dopacity                                */
+    float* colors;  /* [N][3] dL/dcolour                                 */
+} ia_gaussian_grads;
+
+/* Backward of ia_render for an image-space gradient ([SPIN] §3.1 Eq. 1-4,
+ * and the EWA projection of Eq. 2-3 differentiated).  Takes exactly the
+ * arguments of a preceding ia_render call (same g, frame_offsets, cams, ws,
+ * max_entries) whose aux produced T_final and n_contrib, and which reported
+ * no overflow; the workspace must not have been reused in between (the tile
+ * lists and projections are read from it).
+ *   grad_image: device [F,3,H,W] dL/dimage.
+ *   T_final, n_contrib: device [F,H,W], as written by that ia_render.
+ *   grads: device outputs, [N] rows each; overwritten (culled Gaussians get 0).
+ * Per pixel the composited Gaussians are revisited from the last to the
+ * first, recovering T_i = T_{i+1} / (1 - alpha_i); alpha clamped at 0.99
+ * passes no gradient to opacity or position.  Per-Gaussian partials are
+ * summed with float atomics, so results vary in the last bits from run to
+ * run.  The chain to means, scales and quaternions is through the conic
+ * inverse, Sigma2D = J W Sigma W^T J^T and Sigma = R S S^T R^T.
+ * Errors: INVALID_ARG, UNSUPPORTED (sh_degree other than -1),
+ * WORKSPACE_TOO_SMALL, DEVICE. */
+IA_API ia_status ia_render_backward(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames,
+                                    const ia_camera* cams, void* ws, size_t ws_bytes, int64_t max_entries,
+                                    const float* grad_image, const float* T_final, const uint32_t* n_contrib,
+                                    const ia_gaussian_grads* grads, void* stream);
+
+/* L1 image loss: *loss = mean |image - target| (device double, overwritten)
+ * and grad_image = sign(image - target) / n (0 where they are equal), over n
+ * floats of device memory.  Errors: INVALID_ARG, DEVICE. */
+IA_API ia_status ia_l1_loss(const float* image, const float* target, int64_t n, double* loss, float* grad_image,
+                            void* stream);
+
 /* How ia_render turns depth-ordered Gaussians into per-tile lists.  Both give
  * the same lists; they differ in speed.
  *   0  automatic (default): regions when visible Gaussians touch 4 or more
