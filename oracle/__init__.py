@@ -84,6 +84,9 @@ def _declare(L):
     L.orc_raster_tiles.argtypes = [C.c_int, P, P, P, P, P, P, P, P, P, P, P]
     L.orc_render_grad.argtypes = [P, C.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     L.orc_render_grad.restype = None
+    L.orc_decode_grad.argtypes = [P, P, P, P, P, P, P, C.c_long, C.c_int, P, P, P, P, P, P, P, P, P, P, P,
+                                  P, P, P]
+    L.orc_decode_grad.restype = None
     L.orc_raster_brute.argtypes = [P, C.c_long, C.c_long, P, P, P, P, P, P, P, C.c_int, P, C.c_long,
                                    P, P, P, P]
 
@@ -207,6 +210,58 @@ def decode(dec, pos: np.ndarray, t: float | None = None, mode: int = 0) -> dict:
     lib().orc_decode(C.byref(hs), _p(tb), C.byref(mm), keep[2], keep[3], _p(pos), stride,
                      float(t or 0.0), n, int(mode), _p(raw), _p(s), _p(q), _p(c), _p(o))
     return dict(raw=raw, scales=s, quats=q, colors=c, opacity=o)
+
+
+def decode_grad(dec, pos: np.ndarray, t=None, mode: int = 0, grads: dict | None = None,
+                params: dict | None = None) -> dict:
+    """fp64 forward (and, with grads, backward) of the decode; see
+    orc_decode_grad.  pos: [N,3] with scalar or per-point t, or [N,4].
+    Parameters default to the stored values of dec converted exactly to
+    float64; params may override tables / weights / biases (float64), e.g.
+    for finite differences.  grads: upstream dL/d(scales [N,3], quats [N,4],
+    colors [N,3], opacity [N]).  mode bit 0: fp16 rounding of the MLP input
+    and hidden activations; bit 1: fp32 normalisation and cell decision.
+    Returns raw, scales, quats, colors, opacity, flags, signature and, with
+    grads, g_tables [L,T,F], g_weights, g_biases (lists) and g_pos [N,3]."""
+    h, m = dec.hash, dec.mlp
+    pos = np.asarray(pos, np.float64)
+    n = pos.shape[0]
+    if pos.shape[1] == 4:
+        tp = _c(pos[:, 3], np.float64)
+    else:
+        tp = _c(np.broadcast_to(np.float64(t or 0.0), (n,)), np.float64)
+    xyz = _c(pos[:, :3], np.float64)
+    params = params or {}
+    tables = _c(params["tables"] if "tables" in params else np.asarray(dec.tables), np.float64)
+    ws = [_c(w, np.float64) for w in (params["weights"] if "weights" in params else dec.weights)]
+    bs = [_c(b, np.float64) for b in (params["biases"] if "biases" in params else dec.biases)]
+    wp = (C.c_void_p * len(ws))(*[w.ctypes.data for w in ws])
+    bp = (C.c_void_p * len(bs))(*[b.ctypes.data for b in bs])
+    hs = _hash(h)
+    mm = _mlp(m.dims, m.act, m.f16)
+    out = dict(raw=np.zeros((n, 11)), scales=np.zeros((n, 3)), quats=np.zeros((n, 4)), colors=np.zeros((n, 3)),
+               opacity=np.zeros(n), flags=np.zeros(n, np.uint8))
+    sig = C.c_uint64(0)
+    gp = [None] * 4
+    gw, gb = [], []
+    if grads is not None:
+        gp = [_c(grads[k], np.float64) for k in ("scales", "quats", "colors", "opacity")]
+        out["g_tables"] = np.zeros(tables.shape)
+        gw = [np.zeros(w.shape) for w in ws]
+        gb = [np.zeros(b.shape) for b in bs]
+        out["g_pos"] = np.zeros((n, 3))
+    gwp = (C.c_void_p * len(ws))(*[w.ctypes.data for w in gw]) if gw else None
+    gbp = (C.c_void_p * len(bs))(*[b.ctypes.data for b in gb]) if gb else None
+    lib().orc_decode_grad(C.byref(hs), _p(tables), C.byref(mm), wp, bp, _p(xyz), _p(tp), n, int(mode),
+                          *[None if g is None else _p(g) for g in gp], _p(out["raw"]), _p(out["scales"]),
+                          _p(out["quats"]), _p(out["colors"]), _p(out["opacity"]),
+                          None if grads is None else _p(out["g_tables"]), gwp, gbp,
+                          None if grads is None else _p(out["g_pos"]), _p(out["flags"]), C.byref(sig))
+    out["flags"] = out["flags"].astype(bool)
+    out["signature"] = int(sig.value)
+    if grads is not None:
+        out["g_weights"], out["g_biases"] = gw, gb
+    return out
 
 
 def sh_basis(dirs: np.ndarray) -> np.ndarray:

@@ -1113,3 +1113,237 @@ EXPORT void orc_render_grad(const orc_camera* cams, int F, const long* frame_off
     if (signature) *signature = sig;
     free(P);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Decode gradients: backward of [SPIN] §3.3 Eq. 7-11                        */
+/* ------------------------------------------------------------------------ */
+
+static double gelu_grad(double x) {
+    /* d/dx [0.5 x (1 + erf(x / sqrt 2))] = Phi(x) + x phi(x) */
+    return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * exp(-0.5 * x * x) / sqrt(2.0 * acos(-1.0));
+}
+
+/*
+ * Forward and backward of the decode for one batch, with every parameter in
+ * fp64: tables [L][T][F], W[l] row-major [out][in], b[l].  pos [N][3] and
+ * tpos [N] (the time of each point).
+ *
+ * mode bit 0: the MLP input and every hidden activation are rounded to
+ *   binary16 in the forward (as the fp16 device path does); the backward
+ *   treats that rounding as the identity.
+ * mode bit 1: the normalisation and the cell decision are made in fp32 from
+ *   (float) pos and (float) t, as orc_normalize and orc_encode do; otherwise
+ *   they are fp64.  The Jacobian of the normalisation is fp64 either way.
+ *
+ * Outputs of the forward: raw [N][11] (head outputs) and the activations of
+ * Eq. 11 (scales, quats, colors, opacity); all nullable.  With the upstream
+ * gradients gs [N][3], gq [N][4], gc [N][3], go [N] given (else forward
+ * only), the backward accumulates, for L = sum gs.s + gq.q + gc.c + go.o:
+ *   g_tables [L][T][F]   += w_c dL/dz           (scatter-add over the corners)
+ *   g_W[l], g_b[l]       += outer products / sums over the batch
+ *   g_pos [N][3]          = dL/dposition through Eq. 7 and the corner weights
+ * through (in order)
+ *   Eq. 11: s = exp(min(r, 20)) -> dr = ds s (0 above the clip);
+ *           q = r / max(|r|, 1e-12) -> dr = (dq - (dq.q) q) / |r|;
+ *           c = sigmoid(r) -> dr = dc c (1 - c); same for o;
+ *   Eq. 10: the head is linear; a hidden layer y = act(W x + b) passes
+ *           dx = W^T (dy act'(W x + b)) with ReLU' = [a > 0] and
+ *           GELU' = Phi(a) + a phi(a);
+ *   Eq. 9:  z = sum_c w_c table[c], w_c = prod_axis (bit ? f : 1 - f), so
+ *           dz/df_a = sum_c (bit_a ? 1 : -1) prod_{b != a} w_b table[c], and
+ *           df_a / dx~_a = res_a - 1 (the time axis carries no gradient);
+ *   Eq. 7:  x~ = c(mu) / 4 + 1/2 with c = mu for |mu| <= 1, else
+ *           c = g(n) mu, g(n) = 2/n - 1/n^2, whose Jacobian is
+ *           g I + (g'(n) / n) mu mu^T, g'(n) = -2/n^2 + 2/n^3.
+ * flags [N] (nullable) = 1 where a ReLU pre-activation is exactly 0, a scale
+ * output sits at the clip or |r| at its floor (the derivative is one-sided
+ * there).  *signature (nullable) hashes every cell index, ReLU sign and clip,
+ * so that finite differences can check that +-h keeps the same decisions.
+ */
+EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_mlp* m, const double* const* W,
+                            const double* const* b, const double* pos, const double* tpos, long N, int mode,
+                            const double* gs, const double* gq, const double* gc, const double* go, double* raw_out,
+                            double* scales, double* quats, double* colors, double* opacity, double* g_tables,
+                            double* const* g_W, double* const* g_b, double* g_pos, uint8_t* flags,
+                            uint64_t* signature) {
+    int res_s[64], res_t[64], dense[64];
+    orc_level_res(h, res_s, res_t, dense);
+    const uint32_t mask = (uint32_t)((1UL << h->log2T) - 1);
+    const long T = 1L << h->log2T;
+    const int L = h->L, F = h->F, LF = L * F, nl = m->n_layers;
+    const int backward = gs && gq && gc && go;
+    uint64_t sig = 0;
+    for (long i = 0; i < N; ++i) {
+        uint64_t hs = mix64(0x9e3779b97f4a7c15ull, (uint64_t)i);
+        int fl = 0;
+        /* Eq. 7-8 */
+        double xt[4], J[9];
+        const double* mu = pos + i * 3;
+        double n = sqrt(mu[0] * mu[0] + mu[1] * mu[1] + mu[2] * mu[2]);
+        if (mode & 2) {
+            float pf[3] = {(float)mu[0], (float)mu[1], (float)mu[2]}, out[4];
+            orc_normalize(h, pf, 3, (float)tpos[i], 1, out);
+            for (int a = 0; a < 4; ++a) xt[a] = out[a];
+        } else {
+            double c[3] = {mu[0], mu[1], mu[2]};
+            if (!(n <= 1.0)) {
+                double k = (2.0 - 1.0 / n) / n;
+                for (int a = 0; a < 3; ++a) c[a] = mu[a] * k;
+            }
+            double tn = (tpos[i] - h->t_min) / (h->t_max - h->t_min);
+            tn = tn < 0.0 ? 0.0 : (tn > 1.0 ? 1.0 : tn);
+            for (int a = 0; a < 3; ++a) xt[a] = 0.25 * c[a] + 0.5;
+            xt[3] = tn;
+        }
+        hs = mix64(hs, n <= 1.0);
+        for (int r = 0; r < 3; ++r)
+            for (int c = 0; c < 3; ++c) {
+                if (n <= 1.0) {
+                    J[r * 3 + c] = r == c ? 0.25 : 0.0;
+                } else {
+                    double g = 2.0 / n - 1.0 / (n * n), gp = -2.0 / (n * n) + 2.0 / (n * n * n);
+                    J[r * 3 + c] = 0.25 * ((r == c ? g : 0.0) + gp / n * mu[r] * mu[c]);
+                }
+            }
+        /* Eq. 9: per level, the cell, the corner weights and the corner indices */
+        double z[512];
+        long cidx[64][16];
+        double fr[64][4];
+        for (int l = 0; l < L; ++l) {
+            int res[4] = {res_s[l], res_s[l], res_s[l], res_t[l]};
+            int ci[4];
+            for (int a = 0; a < 4; ++a) {
+                int c;
+                double f;
+                if (mode & 2) {
+                    float p = (float)xt[a] * (float)(res[a] - 1);
+                    c = (int)floorf(p);
+                    if (c < 0) c = 0;
+                    if (c > res[a] - 2) c = res[a] - 2;
+                    f = (double)p - (double)c;
+                } else {
+                    double p = xt[a] * (double)(res[a] - 1);
+                    c = (int)floor(p);
+                    if (c < 0) c = 0;
+                    if (c > res[a] - 2) c = res[a] - 2;
+                    f = p - (double)c;
+                }
+                ci[a] = c;
+                fr[l][a] = f;
+                hs = mix64(hs, (uint64_t)(uint32_t)c);
+            }
+            for (int k = 0; k < F; ++k) z[l * F + k] = 0.0;
+            for (int corner = 0; corner < 16; ++corner) {
+                double w = 1.0;
+                uint32_t v[4];
+                for (int a = 0; a < 4; ++a) {
+                    int bit = (corner >> a) & 1;
+                    v[a] = (uint32_t)(ci[a] + bit);
+                    w *= bit ? fr[l][a] : 1.0 - fr[l][a];
+                }
+                long idx = dense[l] ? (long)v[0] + (long)res[0] * ((long)v[1] + (long)res[1] * ((long)v[2] + (long)res[2] * (long)v[3]))
+                                    : (long)hash4(v[0], v[1], v[2], v[3], mask);
+                cidx[l][corner] = idx;
+                for (int k = 0; k < F; ++k) z[l * F + k] += w * tables[((long)l * T + idx) * F + k];
+            }
+        }
+        /* Eq. 10 forward, keeping every layer's input and pre-activation */
+        double xs[8][512], pre[8][512];
+        for (int k = 0; k < LF; ++k) xs[0][k] = (mode & 1) ? round_f16(z[k]) : z[k];
+        for (int l = 0; l < nl; ++l) {
+            int di = m->dims[l], dout = m->dims[l + 1];
+            for (int o = 0; o < dout; ++o) {
+                double s = 0.0;
+                for (int k = 0; k < di; ++k) s += W[l][(long)o * di + k] * xs[l][k];
+                s += b[l][o];
+                pre[l][o] = s;
+                if (l + 1 < nl) {
+                    if (m->act == 0) {
+                        if (s == 0.0) fl = 1;
+                        hs = mix64(hs, s > 0.0);
+                    }
+                    double y = act_fn(m->act, s);
+                    xs[l + 1][o] = (mode & 1) ? round_f16(y) : y;
+                }
+            }
+        }
+        const double* r = pre[nl - 1];
+        /* Eq. 11 */
+        double s3[3], q4[4], c3[3], o1;
+        for (int k = 0; k < 3; ++k) {
+            s3[k] = exp(r[k] < 20.0 ? r[k] : 20.0);
+            if (r[k] == 20.0) fl = 1;
+            hs = mix64(hs, r[k] < 20.0);
+        }
+        double qn = sqrt(r[3] * r[3] + r[4] * r[4] + r[5] * r[5] + r[6] * r[6]);
+        if (qn == 1e-12) fl = 1;
+        hs = mix64(hs, qn < 1e-12);
+        double qd = qn < 1e-12 ? 1e-12 : qn;
+        for (int k = 0; k < 4; ++k) q4[k] = r[3 + k] / qd;
+        for (int k = 0; k < 3; ++k) c3[k] = sigmoid(r[7 + k]);
+        o1 = sigmoid(r[10]);
+        if (raw_out)
+            for (int k = 0; k < 11; ++k) raw_out[i * 11 + k] = r[k];
+        if (scales)
+            for (int k = 0; k < 3; ++k) scales[i * 3 + k] = s3[k];
+        if (quats)
+            for (int k = 0; k < 4; ++k) quats[i * 4 + k] = q4[k];
+        if (colors)
+            for (int k = 0; k < 3; ++k) colors[i * 3 + k] = c3[k];
+        if (opacity) opacity[i] = o1;
+        if (flags) flags[i] = (uint8_t)fl;
+        sig += hs;
+        if (!backward) continue;
+        /* backward of Eq. 11 */
+        double gy[512];
+        for (int k = 0; k < 3; ++k) gy[k] = r[k] < 20.0 ? gs[i * 3 + k] * s3[k] : 0.0;
+        double dot = 0.0;
+        for (int k = 0; k < 4; ++k) dot += gq[i * 4 + k] * q4[k];
+        for (int k = 0; k < 4; ++k)
+            gy[3 + k] = qn < 1e-12 ? gq[i * 4 + k] / 1e-12 : (gq[i * 4 + k] - dot * q4[k]) / qn;
+        for (int k = 0; k < 3; ++k) gy[7 + k] = gc[i * 3 + k] * c3[k] * (1.0 - c3[k]);
+        gy[10] = go[i] * o1 * (1.0 - o1);
+        /* backward of Eq. 10, last layer first */
+        for (int l = nl - 1; l >= 0; --l) {
+            int di = m->dims[l], dout = m->dims[l + 1];
+            if (l + 1 < nl)
+                for (int o = 0; o < dout; ++o)
+                    gy[o] *= m->act == 0 ? (pre[l][o] > 0.0 ? 1.0 : 0.0) : gelu_grad(pre[l][o]);
+            double gx[512];
+            for (int k = 0; k < di; ++k) gx[k] = 0.0;
+            for (int o = 0; o < dout; ++o) {
+                g_b[l][o] += gy[o];
+                for (int k = 0; k < di; ++k) {
+                    g_W[l][(long)o * di + k] += gy[o] * xs[l][k];
+                    gx[k] += W[l][(long)o * di + k] * gy[o];
+                }
+            }
+            for (int k = 0; k < di; ++k) gy[k] = gx[k];
+        }
+        /* backward of Eq. 9 (tables and cell fractions) and Eq. 7 */
+        double gxt[3] = {0.0, 0.0, 0.0};
+        for (int l = 0; l < L; ++l) {
+            int res[4] = {res_s[l], res_s[l], res_s[l], res_t[l]};
+            for (int corner = 0; corner < 16; ++corner) {
+                double wa[4];
+                for (int a = 0; a < 4; ++a) wa[a] = ((corner >> a) & 1) ? fr[l][a] : 1.0 - fr[l][a];
+                double w = ((wa[0] * wa[1]) * wa[2]) * wa[3];
+                long idx = cidx[l][corner];
+                double tg = 0.0;
+                for (int k = 0; k < F; ++k) {
+                    g_tables[((long)l * T + idx) * F + k] += w * gy[l * F + k];
+                    tg += gy[l * F + k] * tables[((long)l * T + idx) * F + k];
+                }
+                for (int a = 0; a < 3; ++a) {
+                    double d = ((corner >> a) & 1) ? 1.0 : -1.0;
+                    for (int e = 0; e < 4; ++e)
+                        if (e != a) d *= wa[e];
+                    gxt[a] += tg * d * (double)(res[a] - 1);
+                }
+            }
+        }
+        for (int c = 0; c < 3; ++c)
+            g_pos[i * 3 + c] = J[0 * 3 + c] * gxt[0] + J[1 * 3 + c] * gxt[1] + J[2 * 3 + c] * gxt[2];
+    }
+    if (signature) *signature = sig;
+}
