@@ -151,9 +151,30 @@ def _stress(S, Decoder, Renderer, stream) -> dict:
     D = Decoder(S.single_decoder())
     da = D.decode_xyzt(xyzt)
     ms_d = timed(lambda: D.decode_xyzt(xyzt, out=da), 3, stream)
+    # backward: L1 loss against a seeded U(0,1) target image, render backward
+    # (per-Gaussian gradients), decode backward of the same 8M positions fed
+    # with those attribute gradients (per-weight, per-table-entry and position
+    # gradients)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    ra = Rs.render(attrs, fo, cams, E + 4096, aux=True, keys=False)
+    target = torch.rand(ra["image"].shape, generator=gen, device="cuda")
+
+    def render_train():
+        r = Rs.render(attrs, fo, cams, E + 4096, aux=True, keys=False, out=ra)
+        loss, gimg = Renderer.l1_loss(r["image"], target)
+        return Rs.backward(attrs, fo, cams, E + 4096, r, gimg)
+
+    ga = render_train()
+    ms_rt = timed(render_train, 2, stream)
+    bwd_kernels = profiled(render_train, 1)
+    ms_db = timed(lambda: D.backward(xyzt, ga, grad_means=ga["means"]), 2, stream)
+    dbwd_kernels = profiled(lambda: D.backward(xyzt, ga, grad_means=ga["means"]), 1)
     return {"frames": len(cams), "gaussians": g.n, "tile_entries": E, "render_ms": round(ms_r, 3),
             "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3),
-            "render_kernels_ms": stress_kernels}
+            "render_fwd_l1_bwd_ms": round(ms_rt, 3), "decode_bwd_8M_ms": round(ms_db, 3),
+            "train_step_ms": round(ms_d + ms_rt + ms_db, 3),
+            "render_kernels_ms": stress_kernels, "render_train_kernels_ms": bwd_kernels,
+            "decode_bwd_kernels_ms": dbwd_kernels}
 
 
 def profiled(fn, reps):

@@ -64,6 +64,7 @@ struct ia_decoder {
     void* W[4] = {nullptr, nullptr, nullptr, nullptr};
     float* b[4] = {nullptr, nullptr, nullptr, nullptr};
     uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [chunk] float4
+    float* bwd_partial = nullptr;  // fp16 path: per-wave weight-gradient partials of the backward
     hipStream_t side = nullptr;  // fp16 path: MLP stream overlapping the next chunk's gather
     hipEvent_t ev_gather[2] = {nullptr, nullptr};
     hipEvent_t ev_mlp[2] = {nullptr, nullptr};
@@ -83,6 +84,8 @@ void free_decoder_params(ia_decoder* d) {
     d->tables = nullptr;
     if (d->zbuf) (void)hipFree(d->zbuf);
     d->zbuf = nullptr;
+    if (d->bwd_partial) (void)hipFree(d->bwd_partial);
+    d->bwd_partial = nullptr;
     for (int k = 0; k < 2; ++k) {
         if (d->ev_gather[k]) (void)hipEventDestroy(d->ev_gather[k]);
         if (d->ev_mlp[k]) (void)hipEventDestroy(d->ev_mlp[k]);
@@ -146,15 +149,8 @@ ia_status check_mlp(const ia_hash_desc* h, const ia_mlp_desc* m) {
 
 bool outputs_ok(const ia_gaussians* o) { return o && o->scales && o->quats && o->colors && o->opacity; }
 
-ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, float t, int64_t N,
-                        const ia_gaussians* out, void* stream) {
-    if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
-    if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
-    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
-    if (N == 0) return IA_OK;
-    if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
-    if (!outputs_ok(out)) return fail(IA_ERR_INVALID_ARG, "output scales/quats/colors/opacity must be non-null");
-    if (N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N too large");
+// Launch arguments of a decode of N Gaussians (outputs left null).
+ia::DecodeArgs decode_args(const ia_decoder* dec, const float* pos, int stride, float t, int64_t N) {
     ia::DecodeArgs a{};
     a.h = dec->lv;
     a.tables = dec->tables;
@@ -170,10 +166,6 @@ ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, flo
     a.stride = stride;
     a.t_scalar = t;
     a.N = N;
-    a.scales = out->scales;
-    a.quats = out->quats;
-    a.colors = out->colors;
-    a.opacity = out->opacity;
     a.zbuf = dec->zbuf;
     a.zcap = ia::kDecodeChunk;
     a.side = dec->side;
@@ -181,6 +173,23 @@ ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, flo
         a.ev_gather[k] = dec->ev_gather[k];
         a.ev_mlp[k] = dec->ev_mlp[k];
     }
+    return a;
+}
+
+ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, float t, int64_t N,
+                        const ia_gaussians* out, void* stream) {
+    if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
+    if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    if (N == 0) return IA_OK;
+    if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
+    if (!outputs_ok(out)) return fail(IA_ERR_INVALID_ARG, "output scales/quats/colors/opacity must be non-null");
+    if (N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N too large");
+    ia::DecodeArgs a = decode_args(dec, pos, stride, t, N);
+    a.scales = out->scales;
+    a.quats = out->quats;
+    a.colors = out->colors;
+    a.opacity = out->opacity;
     hipError_t e = ia::launch_decode(a, dec->mlp.dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return IA_OK;
@@ -237,6 +246,10 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
         // [2][L][chunk] packed feature pairs, then [chunk] normalised positions (float4)
         hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 8 + 16) * ia::kDecodeChunk);
         if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
+        if (st == IA_OK) {
+            e = hipMalloc(&dec->bwd_partial, sizeof(float) * (size_t)ia::kDecodeBwdPartialFloats);
+            if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
+        }
         // a side stream (default priority) and events for the MLP / gather overlap
         if (st == IA_OK) e = hipStreamCreateWithFlags(&dec->side, hipStreamNonBlocking);
         for (int k = 0; st == IA_OK && e == hipSuccess && k < 2; ++k) {
@@ -262,6 +275,45 @@ ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t,
 ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
                          void* stream) {
     return decode_common(dec, xyzt, 4, 0.0f, N, out, stream);
+}
+
+ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
+                             const ia_gaussians* grad_attr, const float* grad_means, float* grad_pos,
+                             const ia_decoder_grads* grads, void* stream) {
+    if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
+    if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
+    if (dec->mlp.dtype != IA_DTYPE_F16)
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the fp16 decoder (32 -> 64 -> 64 -> 11)");
+    if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
+    if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
+    if (N < 0 || N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N must be in [0, 2^40]");
+    if (!grads || !grads->tables) return fail(IA_ERR_INVALID_ARG, "gradient outputs must be non-null");
+    for (int k = 0; k < dec->n_layers; ++k)
+        if (!grads->weights[k] || !grads->biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias gradient");
+    if (N > 0) {
+        if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
+        if (!outputs_ok(grad_attr))
+            return fail(IA_ERR_INVALID_ARG, "grad_attr scales/quats/colors/opacity must be non-null");
+    }
+    ia::DecodeBwdArgs b{};
+    b.fwd = decode_args(dec, pos, pos_stride, t, N);
+    if (N > 0) {
+        b.g_scales = grad_attr->scales;
+        b.g_quats = grad_attr->quats;
+        b.g_colors = grad_attr->colors;
+        b.g_opacity = grad_attr->opacity;
+    }
+    b.g_means = grad_means;
+    b.g_pos = grad_pos;
+    b.g_tables = grads->tables;
+    for (int k = 0; k < 3; ++k) {
+        b.g_W[k] = grads->weights[k];
+        b.g_b[k] = grads->biases[k];
+    }
+    b.partial = dec->bwd_partial;
+    hipError_t e = ia::launch_decode_backward(b, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode backward launch");
+    return IA_OK;
 }
 
 void ia_decoder_destroy(ia_decoder* dec) {
@@ -537,7 +589,7 @@ ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t
     a.n_contrib = aux ? aux->n_contrib : nullptr;
     a.n_entries_out = aux ? aux->n_entries : nullptr;
     a.overflow_out = aux ? aux->overflow : nullptr;
-    a.unpack = aux != nullptr;
+    a.unpack = aux != nullptr && aux->want_keys != 0;
     a.binning = g_binning.load(std::memory_order_relaxed);
     const uint64_t* keys = nullptr;
     const uint32_t* vals = nullptr;

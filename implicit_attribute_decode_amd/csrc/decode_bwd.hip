@@ -1,0 +1,644 @@
+// Backward of the fp16 decode path (SPIN-4DGS §3.3 Eq. 7-11) for upstream
+// gradients of the decoded attributes: gradients of the hash tables, of every
+// decoder weight and bias, and of the positions.
+//
+// Per chunk of at most kBwdChunk Gaussians:
+//   features   the forward's normalise + level-major gather kernels recompute
+//              the encoding z (fp16, as the forward fed the MLP).
+//   mlp_bwd_kernel  one wave per 16 Gaussians at a time (persistent grid):
+//       forward  the decoder on v_mfma_f32_16x16x32_f16 exactly as the decode
+//                runs it (same operands, same fp16 roundings), keeping the
+//                fp32 pre-activations of both hidden layers;
+//       Eq. 11   dr from the upstream gradients: exp' = s below the clip,
+//                (I - q q^T) / |r| for the normalisation, sigma' = c (1 - c);
+//       Eq. 10   data gradients dx = W^T (dy act'(a)) on
+//                v_mfma_f32_16x16x4_f32 with the fp32 weights in LDS (the k
+//                order of each product is permuted so that the gradient a lane
+//                holds in the output tile is its own operand slot for the next
+//                product: no shuffles), and weight gradients
+//                dW += dy x^T over the Gaussians on the same instruction, after
+//                a per-wave LDS transpose that puts the Gaussians on the k
+//                axis.  Each wave accumulates its weight and bias gradients in
+//                registers over all its Gaussians and adds them to its own
+//                slot of a partial buffer;
+//       dz       written to the scratch, fp32, [level][Gaussian] x 2 features.
+//   scatter_kernel  level-major like the gather, four lanes per (Gaussian,
+//       level), each with four of the 16 corners: dtable[corner] += w dz with
+//       float atomics; for positions dz/df_axis = sum_c (+-1) prod_{other
+//       axes} w table[c] (time carries no gradient), times (res - 1), then the
+//       Jacobian of Eq. 7, added to the position gradient with float atomics.
+// After the last chunk a reduction sums the partial buffer in a fixed order
+// (deterministic weight and bias gradients).
+#include <hip/hip_runtime.h>
+
+#include "decode_common.h"
+#include "ia_internal.h"
+
+namespace ia {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kTS = 18;  // row stride (floats) of the per-wave transpose buffers: conflict-free column reads
+// per lane: 4 head tiles + 16 W2 tiles + 8 W1 tiles (4 floats each) + 36 bias partials
+constexpr int kTileSlots = (4 + 16 + 8) * 4;
+constexpr int kBiasSlots = 4 + 16 + 16;
+
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma4(float a, float b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// LDS written by the lanes of one wave is read back by other lanes of the same
+// wave: order the accesses at wavefront scope.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// d/dx GELU(x) = Phi(x) + x phi(x), with erf as in gelu_fp16path.
+__device__ __forceinline__ float gelu_grad_fp16path(float x) {
+    const float u = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    const float e = __expf(-(u * u));
+    const float erf_u = fmaf(-(poly * t), e, 1.0f);
+    const float Phi = 0.5f * (1.0f + copysignf(erf_u, x));
+    return Phi + x * (e * 0.39894228040143268f);  // e = exp(-x^2 / 2)
+}
+
+__device__ __forceinline__ float act_grad(bool gelu, float x) {
+    return gelu ? gelu_grad_fp16path(x) : (x > 0.0f ? 1.0f : 0.0f);
+}
+
+__device__ __forceinline__ float act_fwd(bool gelu, float x) {
+    return gelu ? gelu_fp16path(x) : (x > 0.0f ? x : 0.0f);
+}
+
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+struct MlpBwdArgs {
+    const _Float16* W[3];  // [64][32], [64][64], [11][64]
+    const float* b[3];
+    int gelu;
+    const uint32_t* z;  // [L][zstride] fp16 pairs
+    int64_t zstride;
+    int64_t n;    // Gaussians in this chunk
+    int64_t off;  // index of the chunk's first Gaussian in the upstream gradients
+    const float* gs;
+    const float* gq;
+    const float* gc;
+    const float* go;
+    float2* gz;      // [L][zstride]
+    float* partial;  // [waves][kTileSlots + kBiasSlots][64]
+    int first;       // 1: the partial slots start from zero
+};
+
+__global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
+#pragma clang fp contract(fast)
+    // fp32 operands of the data-gradient products, lane-ordered:
+    //   sWh[rb][e][lane] = Wh[4q+e][16rb+c], sW2[ob][rb][e][lane] = W2[16rb+4q+e][16ob+c],
+    //   sW1[ob][rb][e][lane] = W1[16rb+4q+e][16ob+c]
+    __shared__ float sWh[4 * 4 * 64];
+    __shared__ float sW2[4 * 4 * 4 * 64];
+    __shared__ float sW1[2 * 4 * 4 * 64];
+    __shared__ float sT[kBwdWaves][2][64 * kTS];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int q = lane >> 4, c = lane & 15;
+    const _Float16* W1 = a.W[0];
+    const _Float16* W2 = a.W[1];
+    const _Float16* Wh = a.W[2];
+    for (int k = threadIdx.x; k < 4 * 4 * 64; k += kBwdThreads) {
+        const int l = k & 63, e = (k >> 6) & 3, rb = k >> 8, qq = l >> 4, cc = l & 15;
+        const int row = 4 * qq + e;
+        sWh[k] = row < 11 ? (float)Wh[row * 64 + 16 * rb + cc] : 0.0f;
+    }
+    for (int k = threadIdx.x; k < 4 * 4 * 4 * 64; k += kBwdThreads) {
+        const int l = k & 63, e = (k >> 6) & 3, rb = (k >> 8) & 3, ob = k >> 10, qq = l >> 4, cc = l & 15;
+        sW2[k] = (float)W2[(16 * rb + 4 * qq + e) * 64 + 16 * ob + cc];
+    }
+    for (int k = threadIdx.x; k < 2 * 4 * 4 * 64; k += kBwdThreads) {
+        const int l = k & 63, e = (k >> 6) & 3, rb = (k >> 8) & 3, ob = k >> 10, qq = l >> 4, cc = l & 15;
+        sW1[k] = (float)W1[(16 * rb + 4 * qq + e) * 32 + 16 * ob + cc];
+    }
+    __syncthreads();
+
+    // forward operands, as the decode holds them
+    half8_t A1[4], A2[4][2], A3[2];
+    float B1[4][4], B2[4][4], B3[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        A1[rb] = a_tile32(W1, 32, 64, rb, 0, q, c);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) A2[rb][m] = a_tile32(W2, 64, 64, rb, m, q, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            B1[rb][e] = a.b[0][16 * rb + 4 * q + e];
+            B2[rb][e] = a.b[1][16 * rb + 4 * q + e];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) A3[m] = a_tile32(Wh, 64, 11, 0, m, q, c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) B3[e] = (4 * q + e) < 11 ? a.b[2][4 * q + e] : 0.0f;
+
+    const int64_t wave = (int64_t)blockIdx.x * kBwdWaves + wv;
+    const int64_t nwaves = (int64_t)gridDim.x * kBwdWaves;
+    float* part = a.partial + wave * (int64_t)(kTileSlots + kBiasSlots) * 64 + lane;
+    floatx4_t accH[4], accW2[4][4], accW1[4][2];
+    float gbh[4], gb2[4][4], gb1[4][4];
+    {
+        int j = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accH[t][e] = a.first ? 0.0f : part[64 * j++];
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accW2[t >> 2][t & 3][e] = a.first ? 0.0f : part[64 * j++];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accW1[t >> 1][t & 1][e] = a.first ? 0.0f : part[64 * j++];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gbh[e] = a.first ? 0.0f : part[64 * j++];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gb2[t][e] = a.first ? 0.0f : part[64 * j++];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gb1[t][e] = a.first ? 0.0f : part[64 * j++];
+    }
+
+    const bool gelu = a.gelu != 0;
+    float* sG = sT[wv][0];
+    float* sH = sT[wv][1];
+    for (int64_t base = wave * 16; base < a.n; base += nwaves * 16) {
+        const int64_t gl = base + c;
+        const bool valid = gl < a.n;
+        const int64_t gi = valid ? gl : a.n - 1;
+        // ---------------- forward (as the decode computes it)
+        const int l0 = 2 * q;
+        const half8_t Z = cat8(unpack2(a.z[(size_t)l0 * a.zstride + gi], a.z[(size_t)(l0 + 1) * a.zstride + gi]),
+                               unpack2(a.z[(size_t)(l0 + 8) * a.zstride + gi], a.z[(size_t)(l0 + 9) * a.zstride + gi]));
+        floatx4_t P1[4], P2[4];
+        half8_t H1[2], H2[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const floatx4_t z0 = {0, 0, 0, 0};
+            P1[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z, z0, 0, 0, 0);
+            P1[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z, z0, 0, 0, 0);
+            half8_t h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                P1[2 * m][e] += B1[2 * m][e];
+                P1[2 * m + 1][e] += B1[2 * m + 1][e];
+                h[e] = (_Float16)act_fwd(gelu, P1[2 * m][e]);
+                h[4 + e] = (_Float16)act_fwd(gelu, P1[2 * m + 1][e]);
+            }
+            H1[m] = h;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            floatx4_t lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m][k], H1[k], lo, 0, 0, 0);
+                hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m + 1][k], H1[k], hi, 0, 0, 0);
+            }
+            half8_t h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[e] += B2[2 * m][e];
+                hi[e] += B2[2 * m + 1][e];
+                h[e] = (_Float16)act_fwd(gelu, lo[e]);
+                h[4 + e] = (_Float16)act_fwd(gelu, hi[e]);
+            }
+            P2[2 * m] = lo;
+            P2[2 * m + 1] = hi;
+            H2[m] = h;
+        }
+        floatx4_t accO = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) accO = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[k], H2[k], accO, 0, 0, 0);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = accO[e] + B3[e];
+
+        // ---------------- Eq. 11 backward.  Rows 4q+e of column c:
+        // q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
+        float up[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (valid) {
+            const int64_t u = a.off + gl;
+            if (q == 0) {
+                up[0] = a.gs[u * 3 + 0];
+                up[1] = a.gs[u * 3 + 1];
+                up[2] = a.gs[u * 3 + 2];
+                up[3] = a.gq[u * 4 + 0];
+            } else if (q == 1) {
+                up[0] = a.gq[u * 4 + 1];
+                up[1] = a.gq[u * 4 + 2];
+                up[2] = a.gq[u * 4 + 3];
+                up[3] = a.gc[u * 3 + 0];
+            } else if (q == 2) {
+                up[0] = a.gc[u * 3 + 1];
+                up[1] = a.gc[u * 3 + 2];
+                up[2] = a.go[u];
+            }
+        }
+        const float part_n = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
+        const float rn = sqrtf(part_n + __shfl_xor(part_n, 16));
+        const float nrm = fmaxf(rn, 1e-12f);
+        const float part_d = q == 0 ? up[3] * (o[3] / nrm)
+                                    : (q == 1 ? up[0] * (o[0] / nrm) + up[1] * (o[1] / nrm) + up[2] * (o[2] / nrm) : 0.0f);
+        const float dot = rn >= 1e-12f ? part_d + __shfl_xor(part_d, 16) : 0.0f;
+        float go[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (q == 0) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) go[e] = o[e] < 20.0f ? up[e] * expf(o[e]) : 0.0f;
+            go[3] = (up[3] - dot * (o[3] / nrm)) / nrm;
+        } else if (q == 1) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) go[e] = (up[e] - dot * (o[e] / nrm)) / nrm;
+            const float s = sigmoid_f(o[3]);
+            go[3] = up[3] * s * (1.0f - s);
+        } else if (q == 2) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const float s = sigmoid_f(o[e]);
+                go[e] = up[e] * s * (1.0f - s);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gbh[e] += go[e];
+
+        // ---------------- head: dWh += go H2^T (Gaussians on k through LDS)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sG[(4 * q + e) * kTS + c] = go[e];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sH[(32 * m + 4 * q + e) * kTS + c] = (float)H2[m][e];
+                sH[(32 * m + 16 + 4 * q + e) * kTS + c] = (float)H2[m][4 + e];
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float ag = sG[c * kTS + 4 * s + q];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) accH[hb] = mfma4(ag, sH[(16 * hb + c) * kTS + 4 * s + q], accH[hb]);
+        }
+        wave_lds_sync();
+        // dH2 = Wh^T go; da2 = dH2 act'(a2)
+        floatx4_t D[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            D[rb] = floatx4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) D[rb] = mfma4(sWh[(rb * 4 + e) * 64 + lane], go[e], D[rb]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                D[rb][e] *= act_grad(gelu, P2[rb][e]);
+                gb2[rb][e] += D[rb][e];
+            }
+        // ---------------- layer 2: dW2 += da2 H1^T
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[(16 * rb + 4 * q + e) * kTS + c] = D[rb][e];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sH[(32 * m + 4 * q + e) * kTS + c] = (float)H1[m][e];
+                sH[(32 * m + 16 + 4 * q + e) * kTS + c] = (float)H1[m][4 + e];
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float bh[4];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) bh[hb] = sH[(16 * hb + c) * kTS + 4 * s + q];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const float ag = sG[(16 * rb + c) * kTS + 4 * s + q];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) accW2[rb][hb] = mfma4(ag, bh[hb], accW2[rb][hb]);
+            }
+        }
+        wave_lds_sync();
+        // dH1 = W2^T da2; da1 = dH1 act'(a1)
+        floatx4_t E[4];
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) {
+            E[ob] = floatx4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) E[ob] = mfma4(sW2[((ob * 4 + rb) * 4 + e) * 64 + lane], D[rb][e], E[ob]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                E[rb][e] *= act_grad(gelu, P1[rb][e]);
+                gb1[rb][e] += E[rb][e];
+            }
+        // ---------------- layer 1: dW1 += da1 z^T
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[(16 * rb + 4 * q + e) * kTS + c] = E[rb][e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sH[(4 * q + e) * kTS + c] = (float)Z[e];
+            sH[(16 + 4 * q + e) * kTS + c] = (float)Z[4 + e];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float b0 = sH[c * kTS + 4 * s + q], b1 = sH[(16 + c) * kTS + 4 * s + q];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const float ag = sG[(16 * rb + c) * kTS + 4 * s + q];
+                accW1[rb][0] = mfma4(ag, b0, accW1[rb][0]);
+                accW1[rb][1] = mfma4(ag, b1, accW1[rb][1]);
+            }
+        }
+        wave_lds_sync();
+        // dz = W1^T da1: rows 16 ob + 4 q + e = features (e & 1) of level 8 ob + 2 q + (e >> 1)
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob) {
+            floatx4_t G = {0, 0, 0, 0};
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G = mfma4(sW1[((ob * 4 + rb) * 4 + e) * 64 + lane], E[rb][e], G);
+            if (valid) {
+                const int lv = 8 * ob + 2 * q;
+                a.gz[(size_t)lv * a.zstride + gl] = make_float2(G[0], G[1]);
+                a.gz[(size_t)(lv + 1) * a.zstride + gl] = make_float2(G[2], G[3]);
+            }
+        }
+    }
+    {
+        int j = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = accH[t][e];
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = accW2[t >> 2][t & 3][e];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = accW1[t >> 1][t & 1][e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[64 * j++] = gbh[e];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = gb2[t][e];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = gb1[t][e];
+    }
+}
+
+// Sum the per-wave partials in wave order.  Thread t < kTileSlots * 64 owns
+// one (slot, lane) of the weight tiles; the next 36 * 4 threads own one bias
+// slot of one lane group q (summed over its 16 lanes c).
+__global__ void __launch_bounds__(256) mlp_bwd_reduce_kernel(const float* partial, int nwaves, float* gW1,
+                                                             float* gW2, float* gWh, float* gb1, float* gb2,
+                                                             float* gbh) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int stride = (kTileSlots + kBiasSlots) * 64;
+    if (t < kTileSlots * 64) {
+        const int j = t >> 6, lane = t & 63, q = lane >> 4, c = lane & 15, e = j & 3, tile = j >> 2;
+        float s = 0.0f;
+        for (int w = 0; w < nwaves; ++w) s += partial[(size_t)w * stride + t];
+        if (tile < 4) {
+            const int row = 4 * q + e;
+            if (row < 11) gWh[row * 64 + 16 * tile + c] = s;
+        } else if (tile < 20) {
+            const int rb = (tile - 4) >> 2, hb = (tile - 4) & 3;
+            gW2[(16 * rb + 4 * q + e) * 64 + 16 * hb + c] = s;
+        } else {
+            const int rb = (tile - 20) >> 1, kb = (tile - 20) & 1;
+            gW1[(16 * rb + 4 * q + e) * 32 + 16 * kb + c] = s;
+        }
+        return;
+    }
+    const int u = t - kTileSlots * 64;
+    if (u >= kBiasSlots * 4) return;
+    const int jb = u >> 2, q = u & 3;
+    float s = 0.0f;
+    for (int w = 0; w < nwaves; ++w)
+        for (int c = 0; c < 16; ++c) s += partial[(size_t)w * stride + (kTileSlots + jb) * 64 + 16 * q + c];
+    if (jb < 4) {
+        const int row = 4 * q + jb;
+        if (row < 11) gbh[row] = s;
+    } else if (jb < 20) {
+        const int rb = (jb - 4) >> 2, e = (jb - 4) & 3;
+        gb2[16 * rb + 4 * q + e] = s;
+    } else {
+        const int rb = (jb - 20) >> 2, e = (jb - 20) & 3;
+        gb1[16 * rb + 4 * q + e] = s;
+    }
+}
+
+// Eq. 9 and Eq. 7 backward, level-major as the gather.  Lane s of a group of
+// four takes the x/y corner (s & 1, s >> 1) and its four z/t corners.
+template <bool POS>
+__global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const float* pos, int stride, int64_t n,
+                                                      int nchunk, HashLevels h, const uint32_t* tables,
+                                                      const float2* gz, int64_t zstride, float* gtab, float* gpos) {
+#pragma clang fp contract(fast)
+    const int level = blockIdx.x / nchunk;
+    const int64_t first = (int64_t)(blockIdx.x % nchunk) * 256;
+    const int res = h.res_s[level], res_t = h.res_t[level];
+    const bool dense = h.dense[level] != 0;
+    const uint32_t* tab = tables + (size_t)level * h.T;
+    float* gt = gtab + (size_t)level * h.T * 2;
+    const int s = threadIdx.x & 3;
+    const int bx = s & 1, by = s >> 1;
+    const int sub = threadIdx.x >> 2;
+    const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
+    for (int j = 0; j < 4; ++j) {
+        const int64_t i = first + j * 64 + sub;
+        if (i >= n) break;  // uniform across each group of four lanes
+        const float4 p = xt[i];
+        const float2 g = gz[(size_t)level * zstride + i];
+        int cx, cy, cz, ct;
+        float fx, fy, fz, ft;
+        cell_axis(p.x, res, cx, fx);
+        cell_axis(p.y, res, cy, fy);
+        cell_axis(p.z, res, cz, fz);
+        cell_axis(p.w, res_t, ct, ft);
+        const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
+        uint32_t txy, tz[2], tt[2];
+        if (dense) {
+            txy = ux + uy * r;
+            tz[0] = (uint32_t)cz * r2;
+            tz[1] = tz[0] + r2;
+            tt[0] = (uint32_t)ct * r3;
+            tt[1] = tt[0] + r3;
+        } else {
+            txy = (ux * kP1) ^ (uy * kP2);
+            tz[0] = (uint32_t)cz * kP3;
+            tz[1] = (uint32_t)(cz + 1) * kP3;
+            tt[0] = (uint32_t)ct * kP4;
+            tt[1] = (uint32_t)(ct + 1) * kP4;
+        }
+        const float wx = bx ? fx : 1.0f - fx, wy = by ? fy : 1.0f - fy;
+        const float sx = bx ? 1.0f : -1.0f, sy = by ? 1.0f : -1.0f;
+        const float wxy = wx * wy;
+        const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
+        const bool any = g.x != 0.0f || g.y != 0.0f;
+        float dx = 0.0f, dy = 0.0f, dz = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int bz = k & 1, bt = k >> 1;
+            // a corner of zero time weight has zero weight and zero spatial derivatives
+            if (wt[bt] == 0.0f) continue;
+            const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
+            const float w = (wxy * wz[bz]) * wt[bt];
+            if (any && w != 0.0f) {
+                atomicAdd(gt + 2 * (size_t)idx, w * g.x);
+                atomicAdd(gt + 2 * (size_t)idx + 1, w * g.y);
+            }
+            if (POS) {
+                const uint32_t raw = tab[idx];
+                const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
+                const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+                const float tg = v0 * g.x + v1 * g.y;
+                const float wzt = wz[bz] * wt[bt];
+                dx += tg * (sx * wy) * wzt;
+                dy += tg * (wx * sy) * wzt;
+                dz += tg * wxy * ((bz ? 1.0f : -1.0f) * wt[bt]);
+            }
+        }
+        if (POS) {
+            dx += __shfl_xor(dx, 1, 4);
+            dy += __shfl_xor(dy, 1, 4);
+            dz += __shfl_xor(dz, 1, 4);
+            dx += __shfl_xor(dx, 2, 4);
+            dy += __shfl_xor(dy, 2, 4);
+            dz += __shfl_xor(dz, 2, 4);
+            if (s == 0) {
+                const float sc = (float)(res - 1);
+                const float gx[3] = {dx * sc, dy * sc, dz * sc};
+                const float* mu = pos + i * stride;
+                const float m0 = mu[0], m1 = mu[1], m2 = mu[2];
+                const float nn = sqrtf(m0 * m0 + m1 * m1 + m2 * m2);
+                float out[3];
+                if (nn <= 1.0f) {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) out[k] = 0.25f * gx[k];
+                } else {
+                    // x~ = c(mu)/4 + 1/2, c = gn mu, gn = 2/n - 1/n^2: J = gn I + (gn'/n) mu mu^T
+                    const float inv = 1.0f / nn;
+                    const float gn = (2.0f - inv) * inv;
+                    const float gp_n = (-2.0f + 2.0f * inv) * inv * inv * inv;
+                    const float md = m0 * gx[0] + m1 * gx[1] + m2 * gx[2];
+                    out[0] = 0.25f * (gn * gx[0] + gp_n * m0 * md);
+                    out[1] = 0.25f * (gn * gx[1] + gp_n * m1 * md);
+                    out[2] = 0.25f * (gn * gx[2] + gp_n * m2 * md);
+                }
+                float* dst = gpos + i * 3;
+                atomicAdd(dst + 0, out[0]);
+                atomicAdd(dst + 1, out[1]);
+                atomicAdd(dst + 2, out[2]);
+            }
+        }
+    }
+}
+
+__global__ void fill_kernel(float* p, int64_t n, const float* src) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = src ? src[i] : 0.0f;
+}
+
+int blocks_for(int64_t n, int per, int cap) {
+    int64_t b = (n + per - 1) / per;
+    if (b < 1) b = 1;
+    if (b > cap) b = cap;
+    return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
+    const DecodeArgs& a = b.fwd;
+    const size_t tab_floats = (size_t)a.h.L * a.h.T * 2;
+    IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for((int64_t)tab_floats, 256, 8192)), dim3(256), 0,
+              s, b.g_tables, (int64_t)tab_floats, (const float*)nullptr);
+    if (b.g_pos && a.N > 0)
+        IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(a.N * 3, 256, 8192)), dim3(256), 0, s,
+                  b.g_pos, a.N * 3, b.g_means);
+    const int64_t chunk = kDecodeChunk / 2;
+    const size_t zslot = (size_t)a.h.L * a.zcap;
+    float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
+    uint32_t* z = a.zbuf;
+    float2* gz = reinterpret_cast<float2*>(a.zbuf + (size_t)a.h.L * chunk);
+    MlpBwdArgs m{};
+    for (int k = 0; k < 3; ++k) {
+        m.W[k] = (const _Float16*)a.W[k];
+        m.b[k] = a.b[k];
+    }
+    m.gelu = a.act == IA_ACT_GELU;
+    m.z = z;
+    m.zstride = chunk;
+    m.gs = b.g_scales;
+    m.gq = b.g_quats;
+    m.gc = b.g_colors;
+    m.go = b.g_opacity;
+    m.gz = gz;
+    m.partial = b.partial;
+    int first = 1;
+    for (int64_t off = 0; off < a.N; off += chunk) {
+        const int64_t n = a.N - off < chunk ? a.N - off : chunk;
+        hipError_t e = launch_decode_features(a, off, n, xt, z, chunk, s);
+        if (e != hipSuccess) return e;
+        m.n = n;
+        m.off = off;
+        m.first = first;
+        first = 0;
+        IA_LAUNCH("mlp_bwd_kernel", mlp_bwd_kernel, dim3(kDecodeBwdBlocks), dim3(kBwdThreads), 0, s, m);
+        const int nchunk = (int)((n + 255) / 256);
+        const float* pos = a.pos + off * a.stride;
+        if (b.g_pos)
+            IA_LAUNCH("scatter_kernel", scatter_kernel<true>, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
+                      pos, a.stride, n, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
+                      b.g_pos + off * 3);
+        else
+            IA_LAUNCH("scatter_kernel", scatter_kernel<false>, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
+                      pos, a.stride, n, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
+                      (float*)nullptr);
+    }
+    if (first) {  // N = 0: the weight and bias gradients are zero
+        IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(kDecodeBwdPartialFloats, 256, 8192)),
+                  dim3(256), 0, s, b.partial, (int64_t)kDecodeBwdPartialFloats, (const float*)nullptr);
+    }
+    const int nred = kTileSlots * 64 + kBiasSlots * 4;
+    IA_LAUNCH("mlp_bwd_reduce_kernel", mlp_bwd_reduce_kernel, dim3((nred + 255) / 256), dim3(256), 0, s, b.partial,
+              kDecodeBwdBlocks * kBwdWaves, b.g_W[0], b.g_W[1], b.g_W[2], b.g_b[0], b.g_b[1], b.g_b[2]);
+    return hipGetLastError();
+}
+
+}  // namespace ia

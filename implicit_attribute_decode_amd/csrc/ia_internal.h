@@ -76,6 +76,32 @@ constexpr int64_t kDecodeChunk = int64_t(1) << 22;
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 
+// fp16 path: normalise Gaussians [off, off + n) of a.pos into xt and gather
+// their features into z ([L][zstride] fp16 pairs), as the decode does.
+hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, float4* xt, uint32_t* z,
+                                  int64_t zstride, hipStream_t s);
+
+// Backward of the fp16 decode: one persistent grid of kDecodeBwdBlocks blocks
+// of four waves; each wave owns a slot of 148 x 64 floats in `partial`.
+constexpr int kDecodeBwdBlocks = 256;
+constexpr int64_t kDecodeBwdPartialFloats = (int64_t)kDecodeBwdBlocks * 4 * 148 * 64;
+
+struct DecodeBwdArgs {
+    DecodeArgs fwd;           // the decode being differentiated (parameters, positions, scratch)
+    const float* g_scales;    // [N,3] upstream dL/dscales
+    const float* g_quats;     // [N,4]
+    const float* g_colors;    // [N,3]
+    const float* g_opacity;   // [N]
+    const float* g_means;     // [N,3] added into g_pos, or null
+    float* g_pos;             // [N,3] out, or null (no position gradient)
+    float* g_tables;          // [L][T][2] out
+    float* g_W[3];            // [64][32], [64][64], [11][64] out
+    float* g_b[3];            // [64], [64], [11] out
+    float* partial;           // kDecodeBwdPartialFloats
+};
+
+hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s);
+
 struct HexArgs {
     int res_xyz, res_t, C;
     float aabb;

@@ -26,7 +26,7 @@ IA_ACT_RELU, IA_ACT_GELU = 0, 1
 
 # Every entry point include/ia.h declares.
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
-           "ia_decoder_destroy", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
+           "ia_decoder_destroy", "ia_decode_backward", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
            "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render", "ia_render_set_binning",
            "ia_render_backward", "ia_l1_loss", "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
 
@@ -69,7 +69,11 @@ class RenderAux(C.Structure):
                 ("overflow", C.c_void_p), ("sorted_keys", C.c_void_p), ("sorted_vals", C.c_void_p),
                 ("tile_ranges", C.c_void_p), ("proj_a", C.c_void_p), ("proj_b", C.c_void_p),
                 ("proj_c", C.c_void_p), ("depth", C.c_void_p), ("tiles_touched", C.c_void_p),
-                ("tile_rect", C.c_void_p)]
+                ("tile_rect", C.c_void_p), ("want_keys", C.c_int32)]
+
+
+class DecoderGrads(C.Structure):
+    _fields_ = [("tables", C.c_void_p), ("weights", C.c_void_p * 4), ("biases", C.c_void_p * 4)]
 
 
 class GaussianGrads(C.Structure):
@@ -96,6 +100,7 @@ def load(path: str = LIB_PATH):
         L.ia_decode.argtypes = [P, P, C.c_int64, C.c_float, P, P]
         L.ia_decode_xyzt.argtypes = [P, P, C.c_int64, P, P]
         L.ia_decoder_destroy.argtypes = [P]
+        L.ia_decode_backward.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, P]
         L.ia_decoder_destroy.restype = None
         L.ia_hexplane_create.argtypes = [P, P]
         L.ia_hexplane_set_params.argtypes = [P, P, P, P, C.c_int32, P]
@@ -167,6 +172,12 @@ def ia_decode(dec, xyz, N: int, t: float, out: Gaussians, stream=None):
 
 def ia_decode_xyzt(dec, xyzt, N: int, out: Gaussians, stream=None):
     _check(load().ia_decode_xyzt(dec, _ptr(xyzt), int(N), C.byref(out), _stream(stream)))
+
+
+def ia_decode_backward(dec, pos, pos_stride: int, N: int, t: float, grad_attr: Gaussians, grad_means, grad_pos,
+                       grads: DecoderGrads, stream=None):
+    _check(load().ia_decode_backward(dec, _ptr(pos), int(pos_stride), int(N), float(t), C.byref(grad_attr),
+                                     _ptr(grad_means), _ptr(grad_pos), C.byref(grads), _stream(stream)))
 
 
 def ia_decoder_destroy(dec):

@@ -57,6 +57,25 @@ class Decoder:
         ia.ia_decode_xyzt(self.handle, xyzt, N, g)
         return out
 
+    def backward(self, pos: torch.Tensor, grad_attr: dict, t: float | None = None, grad_means=None,
+                 want_pos: bool = True) -> dict:
+        """Gradients of the decode of pos ([N,3] at time t, or [N,4] xyzt)
+        for upstream dL/d{scales, quats, colors, opacity}.  Returns tables
+        [L,T,F], weights and biases (lists, fp32, shaped like the parameters)
+        and, with want_pos, pos [N,3] = grad_means + the decoder's share."""
+        N = int(pos.shape[0])
+        stride = int(pos.shape[1])
+        out = dict(tables=torch.empty(self._tables.shape, dtype=torch.float32, device=self.device),
+                   weights=[torch.empty(w.shape, dtype=torch.float32, device=self.device) for w in self._W],
+                   biases=[torch.empty(b.shape, dtype=torch.float32, device=self.device) for b in self._b])
+        out["pos"] = torch.empty((N, 3), device=self.device) if want_pos else None
+        G = ia.DecoderGrads(ia._ptr(out["tables"]), (ia.C.c_void_p * 4)(*[ia._ptr(w) for w in out["weights"]]),
+                            (ia.C.c_void_p * 4)(*[ia._ptr(b) for b in out["biases"]]))
+        up = ia.gaussians(scales=grad_attr["scales"], quats=grad_attr["quats"], colors=grad_attr["colors"],
+                          opacity=grad_attr["opacity"])
+        ia.ia_decode_backward(self.handle, pos, stride, N, float(t or 0.0), up, grad_means, out["pos"], G)
+        return out
+
     def __del__(self):
         h = getattr(self, "handle", None)
         if h is not None and h.value:
@@ -117,10 +136,12 @@ class Renderer:
         off = (-self.ws.data_ptr()) % 256
         return self.ws[off:off + need]
 
-    def render(self, g: dict, frame_offsets, cams, max_entries: int, aux: bool = False, out: dict | None = None):
+    def render(self, g: dict, frame_offsets, cams, max_entries: int, aux: bool = False, out: dict | None = None,
+               keys: bool = True):
         """g: means [N,k>=3], scales, quats, colors | sh, opacity (cuda tensors).
         Returns image [F,3,H,W] and, with aux, T_final, n_contrib, n_entries,
-        overflow and workspace views (sorted keys/vals, ranges, projections)."""
+        overflow and workspace views (ranges, projections and, with keys, the
+        sorted keys / values)."""
         fo = np.asarray(frame_offsets, np.int64)
         F, W, H = len(cams), int(cams[0].W), int(cams[0].H)
         N = int(fo[-1])
@@ -143,12 +164,14 @@ class Renderer:
             res["overflow"] = torch.zeros(1, dtype=torch.int32, device=self.device)
             A = ia.RenderAux(ia._ptr(res["T_final"]), ia._ptr(res["n_contrib"]), ia._ptr(res["n_entries"]),
                              ia._ptr(res["overflow"]))
+            A.want_keys = 1 if keys else 0
         ia.ia_render(G, fo, cams, ws, max_entries, image, A)
         if aux:
             base = ws.data_ptr()
             for name, (dt, width) in _VIEW_TYPES.items():
                 p = getattr(A, name)
-                res["_view_" + name] = (int(p) - base, dt, width)
+                if p:  # sorted keys / values only when requested
+                    res["_view_" + name] = (int(p) - base, dt, width)
             res["_ws"] = ws
         return res
 

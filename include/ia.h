@@ -141,6 +141,36 @@ IA_API ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, f
 IA_API ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
                          void* stream);
 
+/* Gradients of the decoder parameters (device, fp32, overwritten). */
+typedef struct {
+    float* tables;     /* [L][2^log2T][F], whatever the table dtype          */
+    float* weights[4]; /* layer k: [out][in] (n_hidden + 1 used)             */
+    float* biases[4];  /* layer k: [out]                                     */
+} ia_decoder_grads;
+
+/* Backward of ia_decode (pos_stride 3, time t) or ia_decode_xyzt (pos_stride
+ * 4) for upstream gradients of the decoded attributes ([SPIN] §3.3 Eq. 7-11
+ * differentiated; positions are trainable, §3.3 Eq. 7).
+ *   grad_attr: device dL/d scales [N,3], quats [N,4], colors [N,3],
+ *              opacity [N] (means and sh are ignored).
+ *   grad_means: device [N,3] or NULL; added into grad_pos (e.g. the render's
+ *              position gradient, the positions being the means).
+ *   grad_pos:  device [N,3] out, grad_means + dL/dposition through Eq. 7 and
+ *              the corner weights of Eq. 9 (time carries none); NULL skips
+ *              the position gradient.
+ *   grads:     all outputs overwritten: table gradient (scatter-add of
+ *              w_c dL/dz over the 16 corners of each level, float atomics,
+ *              so the last bits vary from run to run), weight and bias
+ *              gradients (summed in a fixed order: deterministic).
+ * The forward is recomputed exactly as the decode computes it (fp16 hidden
+ * activations); the backward runs in fp32 (v_mfma_f32_16x16x4_f32), treating
+ * the fp16 roundings as the identity.  Uses the handle's scratch: calls on
+ * one handle must not overlap (same as ia_decode).
+ * Errors: INVALID_ARG, UNSUPPORTED (fp32 decoders), DEVICE. */
+IA_API ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
+                                    const ia_gaussians* grad_attr, const float* grad_means, float* grad_pos,
+                                    const ia_decoder_grads* grads, void* stream);
+
 IA_API void ia_decoder_destroy(ia_decoder* dec);
 
 /* ------------------------------------------------------------------------ */
@@ -206,7 +236,7 @@ typedef struct {
     uint32_t* overflow;  /* device [1] 1 if n_entries > max_entries, or NULL       */
     /* views (written by ia_render) */
     const uint64_t* sorted_keys;  /* [min(E,max_entries)] (tile<<32 | depth bits);
-                                     written only when aux is given             */
+                                     only with want_keys                        */
     const uint32_t* sorted_vals;  /* [min(E,max_entries)] Gaussian index          */
     const uint32_t* tile_ranges;  /* [F*tiles][2] [start,end), empty = [0,0)      */
     const float* proj_a;          /* [N][4] u, v, conic A, conic B                */
@@ -215,6 +245,9 @@ typedef struct {
     const float* depth;           /* [N] camera-space z                           */
     const uint32_t* tiles_touched;/* [N] 0 = culled                               */
     const uint16_t* tile_rect;    /* [N][4] tx0, ty0, tx1, ty1 (inclusive)        */
+    /* input */
+    int32_t want_keys;  /* nonzero: also fill sorted_keys / sorted_vals (one
+                           extra pass over the entries); else both stay NULL */
 } ia_render_aux;
 
 /* Bytes of workspace ia_render needs for N_total Gaussians over `frames`

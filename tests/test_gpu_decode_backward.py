@@ -1,0 +1,185 @@
+"""GPU parity of the decode backward (SPIN-4DGS §3.3 Eq. 7-11 differentiated:
+hash-table, weight, bias and position gradients) against the oracle's fp64
+gradients, which are pinned to central finite differences.
+
+The oracle runs in its fp16-emulating mode with fp32 cell decisions (mode 3):
+the same forward function the GPU differentiates, so what is left is fp32
+against fp64 arithmetic, float-atomic summation order, and the rare one-ulp
+fp16 rounding flip of a hidden activation (2^-11 relative) between the GPU's
+fp32 pre-activation and the oracle's fp64 one.  Bounds (written in each
+check): a gradient array X of the parameters is compared as
+    |X_gpu - X_oracle| <= 1e-3 |X_oracle| + 1e-4 max|X_oracle|,
+the position gradient per point as
+    |g_gpu - g_oracle| <= 2e-3 |g_oracle| + 1e-4 max|g_oracle| (vector norms).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from implicit_attribute_decode_amd import ia, scenes as S
+from implicit_attribute_decode_amd.pipeline import Decoder
+
+from gpu_util import cuda, host, say
+
+pytestmark = pytest.mark.gpu
+
+UP = ("scales", "quats", "colors", "opacity")
+
+
+def _upstream(rng, n):
+    return dict(scales=rng.normal(size=(n, 3)), quats=rng.normal(size=(n, 4)), colors=rng.normal(size=(n, 3)),
+                opacity=rng.normal(size=n))
+
+
+def _edge_xyzt(rng, n):
+    p = np.empty((n, 4), np.float32)
+    p[:, :3] = rng.normal(0, 2.0, (n, 3))
+    p[:, 3] = rng.random(n)
+    d = rng.normal(size=(8, 3))
+    d /= np.linalg.norm(d, axis=1, keepdims=True)
+    special = np.concatenate([np.zeros((1, 3)), d * 0.5, d * 1e4, d * (1 + 1e-6), [[0.999, 0, 0], [1.0, 0, 0]]])
+    k = min(n, len(special))
+    p[:k, :3] = special[:k]
+    p[:k, 3] = np.resize(np.float32([0.0, 1.0, -0.5, 1.5, 0.5, 0.25, 10 / 149]), k)
+    return p
+
+
+def _close(tag, a, b, rtol, afrac):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = np.abs(b).max()
+    lim = rtol * np.abs(b) + afrac * scale
+    ratio = float((np.abs(a - b) / np.maximum(lim, 1e-300)).max())
+    say(f"[{tag}] max|ref| {scale:.3e} worst err/limit {ratio:.3f}")
+    assert ratio <= 1.0, (tag, ratio)
+
+
+def _gpu_backward(D, pos, up, t=None, grad_means=None, want_pos=True):
+    g = {k: cuda(v.astype(np.float32)) for k, v in up.items()}
+    out = D.backward(cuda(pos), g, t, None if grad_means is None else cuda(grad_means), want_pos)
+    torch.cuda.synchronize()
+    return out
+
+
+def _compare(tag, dec, out, ref, pos_ref=None):
+    _close(f"{tag} tables", host(out["tables"]).reshape(-1), ref["g_tables"].reshape(-1), 1e-3, 1e-4)
+    for l in range(len(ref["g_weights"])):
+        _close(f"{tag} W{l}", host(out["weights"][l]), ref["g_weights"][l], 1e-3, 1e-4)
+        _close(f"{tag} b{l}", host(out["biases"][l]), ref["g_biases"][l], 1e-3, 1e-4)
+    if out["pos"] is not None:
+        g = host(out["pos"]).astype(np.float64)
+        o = ref["g_pos"] if pos_ref is None else pos_ref
+        err = np.linalg.norm(g - o, axis=1)
+        nrm = np.linalg.norm(o, axis=1)
+        lim = 2e-3 * nrm + 1e-4 * nrm.max()
+        ratio = float((err / lim).max())
+        say(f"[{tag} pos] max|ref| {nrm.max():.3e} worst err/limit {ratio:.3f}")
+        assert ratio <= 1.0
+
+
+def test_decode_backward_matches_oracle_xyzt():
+    dec = S.single_decoder()
+    rng = np.random.default_rng(60)
+    n = 20000
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare("xyzt", dec, out, ref)
+
+
+def test_decode_backward_sequence_frames_scalar_t():
+    """One frame of the sequence at its own time (scalar t, stride 3), a
+    temporal vertex (half of the 16 corners have zero weight)."""
+    dec = S.single_decoder()
+    seq = S.Sequence()
+    f = 10
+    xyzt = seq.xyzt([f])
+    pos = np.ascontiguousarray(xyzt[:30000, :3])
+    t = float(xyzt[0, 3])
+    rng = np.random.default_rng(61)
+    up = _upstream(rng, pos.shape[0])
+    ref = O.decode_grad(dec, pos.astype(np.float64), t, mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up, t=t)
+    _compare("scalar t", dec, out, ref)
+
+
+@pytest.mark.parametrize("n", [1, 17, 1000])
+def test_decode_backward_small_and_ragged(n):
+    dec = S.single_decoder()
+    rng = np.random.default_rng(62 + n)
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare(f"n={n}", dec, out, ref)
+
+
+def test_decode_backward_adds_render_position_gradient_and_skips_positions():
+    dec = S.single_decoder()
+    rng = np.random.default_rng(63)
+    n = 5000
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    gm = rng.normal(size=(n, 3)).astype(np.float32)
+    D = Decoder(dec)
+    a = _gpu_backward(D, pos, up, grad_means=gm)
+    b = _gpu_backward(D, pos, up, want_pos=False)
+    assert b["pos"] is None
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    _compare("with means", dec, a, ref, pos_ref=ref["g_pos"] + gm.astype(np.float64))
+    for l in range(3):
+        np.testing.assert_array_equal(host(a["weights"][l]), host(b["weights"][l]))  # fixed summation order
+
+
+def test_decode_backward_two_chunks_is_the_sum_of_its_parts():
+    """2^21 + 4097 points (two backward chunks): the parameter gradients are
+    sums over points, so the whole equals the sum of the two halves computed
+    separately; positions are per point.  A sample of points is checked
+    against the oracle one by one."""
+    dec = S.single_decoder()
+    rng = np.random.default_rng(64)
+    n1 = 1 << 21
+    n = n1 + 4097
+    pos = np.empty((n, 4), np.float32)
+    pos[:, :3] = S.shell_points(rng, n, 3.0)
+    pos[:, 3] = rng.random(n)
+    up = _upstream(rng, n)
+    D = Decoder(dec)
+    whole = _gpu_backward(D, pos, up)
+    p1 = _gpu_backward(D, pos[:n1], {k: v[:n1] for k, v in up.items()})
+    p2 = _gpu_backward(D, pos[n1:], {k: v[n1:] for k, v in up.items()})
+    for key in ("tables",):
+        s = host(p1[key]).astype(np.float64) + host(p2[key])
+        _close("chunks tables", host(whole[key]).reshape(-1), s.reshape(-1), 1e-5, 1e-6)
+    # sums of 2M terms of random sign in fp32, in two different orders: the
+    # cancellation leaves differences near 1e-5 of the largest entry
+    for l in range(3):
+        _close(f"chunks W{l}", host(whole["weights"][l]), host(p1["weights"][l]).astype(np.float64)
+               + host(p2["weights"][l]), 1e-4, 1e-4)
+        _close(f"chunks b{l}", host(whole["biases"][l]), host(p1["biases"][l]).astype(np.float64)
+               + host(p2["biases"][l]), 1e-4, 1e-4)
+    wp = host(whole["pos"])
+    np.testing.assert_allclose(wp[:n1], host(p1["pos"]), rtol=1e-5, atol=1e-6 * np.abs(wp).max())
+    np.testing.assert_allclose(wp[n1:], host(p2["pos"]), rtol=1e-5, atol=1e-6 * np.abs(wp).max())
+    idx = np.sort(np.concatenate([rng.choice(n, 300, replace=False), [0, n1 - 1, n1, n - 1]]))
+    ref = O.decode_grad(dec, pos[idx].astype(np.float64), mode=3, grads={k: v[idx] for k, v in up.items()})
+    g = wp[idx].astype(np.float64)
+    err = np.linalg.norm(g - ref["g_pos"], axis=1)
+    nrm = np.linalg.norm(ref["g_pos"], axis=1)
+    assert (err <= 2e-3 * nrm + 1e-4 * nrm.max()).all()
+
+
+def test_decode_backward_zero_points_and_errors():
+    dec = S.single_decoder()
+    D = Decoder(dec)
+    out = D.backward(torch.empty((0, 4), device="cuda"), {k: torch.empty(0, device="cuda") for k in UP})
+    torch.cuda.synchronize()
+    assert float(out["tables"].abs().max()) == 0.0
+    assert all(float(w.abs().max()) == 0.0 for w in out["weights"])
+    assert all(float(b.abs().max()) == 0.0 for b in out["biases"])
+    T = Decoder(S.tiny_decoder())
+    with pytest.raises(ia.IAError) as e:
+        T.backward(torch.zeros((4, 3), device="cuda"), {k: torch.zeros((4, 4), device="cuda") for k in UP}, 0.5)
+    assert e.value.status == ia.IA_ERR_UNSUPPORTED
