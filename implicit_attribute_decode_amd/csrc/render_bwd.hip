@@ -30,10 +30,21 @@ namespace {
 constexpr int kBwdThreads = 256;
 constexpr int kBwdBatch = 256;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+constexpr int kSlots = 7;  // Gaussians buffered per wave before their partials are summed (7 x 9 <= 64 lanes)
+
+// Sum of v over the lane's quad (lanes 4i..4i+3), in every lane of the quad.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
     return v;
+}
+
+// LDS written by the lanes of one wave is read back by other lanes of the same
+// wave: order the accesses at wavefront scope.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 struct RasterBwdArgs {
@@ -60,13 +71,16 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
     __shared__ float s_c[kBwdBatch];   // b
     __shared__ uint32_t s_id[kBwdBatch];
     __shared__ float s_g[kBwdBatch][kGradPerGaussian];
+    // per wave: quad partial sums of the buffered Gaussians [slot][partial][quad]
+    __shared__ __align__(16) float s_q[kBwdThreads / 64][kSlots][kGradPerGaussian][16];
+    __shared__ int s_slot[kBwdThreads / 64][kSlots];
     __shared__ uint32_t s_maxnc;
     const int f = blockIdx.z;
     const uint32_t tile = (uint32_t)f * a.ntiles + blockIdx.y * (uint32_t)a.tiles_x + blockIdx.x;
     uint2 rg = a.ranges[tile];
     if (rg.y > a.cap) rg.y = (uint32_t)a.cap;
     if (rg.x > rg.y) rg.x = rg.y;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int px = blockIdx.x * 16 + (threadIdx.x & 15), py = blockIdx.y * 16 + (threadIdx.x >> 4);
     const bool in = px < a.W && py < a.H;
     const size_t plane = (size_t)a.W * a.H;
@@ -84,10 +98,15 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
     if (threadIdx.x == 0) s_maxnc = 0;
     __syncthreads();
     if (nc) atomicMax(&s_maxnc, nc);
+    // largest n_contrib of this wave: no lane of the wave composites beyond it
+    uint32_t wmax = nc;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wmax = max(wmax, (uint32_t)__shfl_xor((int)wmax, o, 64));
     __syncthreads();
     const uint32_t len = rg.y - rg.x;
     const int maxnc = (int)(s_maxnc < len ? s_maxnc : len);
     const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
+    float* q = &s_q[wv][0][0][0];
     for (int end = maxnc; end > 0; end -= kBwdBatch) {
         const int start = end - kBwdBatch > 0 ? end - kBwdBatch : 0;
         const int n = end - start;
@@ -102,7 +121,23 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
         }
         for (int k = threadIdx.x; k < kBwdBatch * kGradPerGaussian; k += kBwdThreads) (&s_g[0][0])[k] = 0.0f;
         __syncthreads();
-        for (int j = n - 1; j >= 0; --j) {
+        // positions above the wave's largest n_contrib composite nothing here
+        const int top = (int)wmax - start < n ? (int)wmax - start : n;
+        int ns = 0;  // buffered Gaussians (wave-uniform)
+        // sum the buffered quad partials: lane L < 9 ns takes slot L / 9, partial L % 9
+        auto flush = [&](int m) {
+            wave_lds_sync();
+            if (lane < kGradPerGaussian * m) {
+                const int slot = lane / kGradPerGaussian, k = lane - slot * kGradPerGaussian;
+                const float4* r = reinterpret_cast<const float4*>(q + (slot * kGradPerGaussian + k) * 16);
+                const float4 v0 = r[0], v1 = r[1], v2 = r[2], v3 = r[3];
+                const float sum = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) +
+                                  ((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w));
+                if (sum != 0.0f) atomicAdd(&s_g[s_slot[wv][slot]][k], sum);
+            }
+            wave_lds_sync();
+        };
+        for (int j = top - 1; j >= 0; --j) {
             const uint32_t pos1 = (uint32_t)(start + j + 1);  // 1-based list position
             const float4 ga = s_a[j];
             const float4 gb = s_b[j];
@@ -118,14 +153,14 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
 #pragma unroll
             for (int k = 0; k < kGradPerGaussian; ++k) gv[k] = 0.0f;
             if (take) {
-                const float one_m = 1.0f - a0;
-                const float Ti = T / one_m;
+                const float inv = 1.0f / (1.0f - a0);
+                const float Ti = T * inv;
                 const float c[3] = {gb.z, gb.w, s_c[j]};
                 float galpha = 0.0f;
 #pragma unroll
                 for (int k = 0; k < 3; ++k) {
                     gv[6 + k] = g[k] * a0 * Ti;
-                    galpha += g[k] * (c[k] * Ti - acc[k] / one_m);
+                    galpha += g[k] * (c[k] * Ti - acc[k] * inv);
                     acc[k] += c[k] * a0 * Ti;
                 }
                 T = Ti;
@@ -142,10 +177,16 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
             }
 #pragma unroll
             for (int k = 0; k < kGradPerGaussian; ++k) {
-                const float sum = wave_sum(gv[k]);
-                if (lane == 0 && sum != 0.0f) atomicAdd(&s_g[j][k], sum);
+                const float v = quad_sum(gv[k]);
+                if ((lane & 3) == 0) q[(ns * kGradPerGaussian + k) * 16 + (lane >> 2)] = v;
+            }
+            if (lane == 0) s_slot[wv][ns] = j;
+            if (++ns == kSlots) {
+                flush(kSlots);
+                ns = 0;
             }
         }
+        if (ns) flush(ns);
         __syncthreads();
         if ((int)threadIdx.x < n) {
             float* dst = a.gacc + (size_t)s_id[threadIdx.x] * kGradPerGaussian;
