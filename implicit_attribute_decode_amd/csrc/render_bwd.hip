@@ -2,8 +2,8 @@
 // §3.1, Eq. 1-4; Eq. 2-3 differentiated by hand) for an image-space loss
 // gradient dL/dimage, and the L1 image loss itself.
 //
-//   raster_backward_kernel  one 256-thread block per tile, one pixel per
-//       thread.  Each pixel walks its tile's list from the last composited
+//   raster_backward_kernel  one block per tile (one or two pixels per
+//       thread).  Each pixel walks its tile's list from the last composited
 //       Gaussian (n_contrib) back to the first, re-deciding every step with
 //       the forward's arithmetic (raster_common.h) and recovering
 //       T_i = T_{i+1} / (1 - alpha_i) from T_final:
@@ -12,9 +12,12 @@
 //                       S_i = sum_{j>i} c_j alpha_j T_j + T_final bg
 //         alpha = o exp(power) (constant where clamped at 0.99), power =
 //         -0.5 (A dx^2 + C dy^2) - B dx dy, d = pixel centre - mean.
-//       The nine partials of a Gaussian (u, v, A, B, C, o, r, g, b) are
-//       summed over a wave with cross-lane adds, over the block in LDS, and
-//       added once per (Gaussian, tile) to its accumulator in global memory.
+//       Per Gaussian nine partials (power moments gp (dx, dy, dx^2, dx dy,
+//       dy^2), opacity, r, g, b) are summed over each quad of lanes with DPP
+//       adds, buffered per wave in LDS and summed seven Gaussians at a time
+//       (one lane per Gaussian and partial), gathered per block in LDS, turned
+//       into d/d(u, v, A, B, C) and added once per (Gaussian, tile) to its
+//       accumulator in global memory.
 //   preprocess_backward_kernel  one thread per Gaussian: (u, v, A, B, C) ->
 //       (mean, scale, quaternion) through the conic inverse, Sigma2D =
 //       T Sigma T^T, T = J W and Sigma = (Rq S)(Rq S)^T; opacity and colour
@@ -27,15 +30,16 @@
 namespace ia {
 namespace {
 
-constexpr int kBwdThreads = 256;
 constexpr int kBwdBatch = 256;
+constexpr int64_t kBwdTwoPixelTiles = 8192;
 
 constexpr int kSlots = 7;  // Gaussians buffered per wave before their partials are summed (7 x 9 <= 64 lanes)
 
-// Sum of v over the lane's quad (lanes 4i..4i+3), in every lane of the quad.
+// Sum of v over the lane's quad (lanes 4i..4i+3), in every lane of the quad
+// (two adds with a DPP quad permutation on their second operand).
 __device__ __forceinline__ float quad_sum(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
     return v;
 }
 
@@ -64,16 +68,57 @@ struct RasterBwdArgs {
     float* gacc;  // [N][9]
 };
 
-__global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdArgs a) {
+// Backward state of one pixel: transmittance recovered back to front,
+// D = dL/dpixel . S where S is the colour lying behind the current Gaussian
+// (starting at T_final bg), dL/dpixel and the number of Gaussians composited.
+struct BPix {
+    float T, D, g[3];
+    uint32_t nc;
+};
+
+// Adds one pixel's partials for a Gaussian to gv (Eq. 4 and the splat of
+// Eq. 3 differentiated), branch-free: a pixel that does not composite the
+// Gaussian (tk false) adds zeros and keeps its state.
+//   T_i = T_{i+1} / (1 - alpha), w = alpha T_i, dL/dc += g w,
+//   dL/dalpha = T_i (g . c) - D / (1 - alpha), then D += w (g . c);
+//   unless alpha is clamped at 0.99: dL/do += dL/dalpha G and, with
+//   gp = dL/dalpha alpha = dL/dpower, the moments gp (dx, dy, dx^2, dx dy,
+//   dy^2), from which the mean and conic gradients follow once per Gaussian.
+template <bool FIRST>
+__device__ __forceinline__ void pixel_grad(BPix& p, bool tk, float a0, float G, float dx, float dy, float c0,
+                                           float c1, float c2, float gv[kGradPerGaussian]) {
 #pragma clang fp contract(fast)
+    const float ae = tk ? a0 : 0.0f;
+    const float inv = __builtin_amdgcn_rcpf(1.0f - ae);
+    const float Ti = p.T * inv;
+    const float w = ae * Ti;
+    const float gc = p.g[0] * c0 + p.g[1] * c1 + p.g[2] * c2;
+    const float galpha = Ti * gc - inv * p.D;
+    p.D += w * gc;
+    p.T = tk ? Ti : p.T;
+    const float gal = tk && a0 < 0.99f ? galpha : 0.0f;
+    const float gp = gal * a0;
+    const float t = gp * dx, u = gp * dy;
+    const float add[kGradPerGaussian] = {t, u, t * dx, t * dy, u * dy, gal * G, p.g[0] * w, p.g[1] * w, p.g[2] * w};
+#pragma unroll
+    for (int k = 0; k < kGradPerGaussian; ++k) gv[k] = FIRST ? add[k] : gv[k] + add[k];
+}
+
+// One block per 16x16 tile.  PX = 2: 128 threads, thread (col, row) takes
+// pixels (col, 2 row) and (col, 2 row + 1), sharing dx, the dx terms of the
+// power and the per-Gaussian reductions; PX = 1: 256 threads, one pixel each.
+template <int PX>
+__global__ void __launch_bounds__(256 / PX) raster_backward_kernel(RasterBwdArgs a) {
+#pragma clang fp contract(fast)
+    constexpr int kThreads = 256 / PX, kWaves = kThreads / 64;
     __shared__ float4 s_a[kBwdBatch];  // u, v, -A/2, -B
     __shared__ float4 s_b[kBwdBatch];  // -C/2, o, r, g
     __shared__ float s_c[kBwdBatch];   // b
     __shared__ uint32_t s_id[kBwdBatch];
     __shared__ float s_g[kBwdBatch][kGradPerGaussian];
     // per wave: quad partial sums of the buffered Gaussians [slot][partial][quad]
-    __shared__ __align__(16) float s_q[kBwdThreads / 64][kSlots][kGradPerGaussian][16];
-    __shared__ int s_slot[kBwdThreads / 64][kSlots];
+    __shared__ __align__(16) float s_q[kWaves][kSlots][kGradPerGaussian][16];
+    __shared__ int s_slot[kWaves][kSlots];
     __shared__ uint32_t s_maxnc;
     const int f = blockIdx.z;
     const uint32_t tile = (uint32_t)f * a.ntiles + blockIdx.y * (uint32_t)a.tiles_x + blockIdx.x;
@@ -81,50 +126,62 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
     if (rg.y > a.cap) rg.y = (uint32_t)a.cap;
     if (rg.x > rg.y) rg.x = rg.y;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int px = blockIdx.x * 16 + (threadIdx.x & 15), py = blockIdx.y * 16 + (threadIdx.x >> 4);
-    const bool in = px < a.W && py < a.H;
+    const int px = blockIdx.x * 16 + (threadIdx.x & 15);
+    const int py0 = blockIdx.y * 16 + PX * (threadIdx.x >> 4);
     const size_t plane = (size_t)a.W * a.H;
-    const size_t pix = (size_t)py * a.W + px;
     const DevCamera& cam = a.cams[f];
-    uint32_t nc = 0;
-    float T = 1.0f, g[3] = {0.0f, 0.0f, 0.0f};
-    if (in) {
-        nc = a.n_contrib[(size_t)f * plane + pix];
-        T = a.T_final[(size_t)f * plane + pix];
-        for (int k = 0; k < 3; ++k) g[k] = a.gimg[((size_t)f * 3 + k) * plane + pix];
+    BPix P[PX];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < PX; ++k) {
+        const int py = py0 + k;
+        const bool in = px < a.W && py < a.H;
+        const size_t pix = (size_t)py * a.W + px;
+        P[k].nc = 0;
+        P[k].T = 1.0f;
+        for (int c = 0; c < 3; ++c) P[k].g[c] = 0.0f;
+        if (in) {
+            P[k].nc = a.n_contrib[(size_t)f * plane + pix];
+            P[k].T = a.T_final[(size_t)f * plane + pix];
+            for (int c = 0; c < 3; ++c) P[k].g[c] = a.gimg[((size_t)f * 3 + c) * plane + pix];
+        }
+        P[k].D = P[k].T * ((P[k].g[0] * cam.bg[0] + P[k].g[1] * cam.bg[1]) + P[k].g[2] * cam.bg[2]);
+        mine = max(mine, P[k].nc);
     }
-    float acc[3];
-    for (int k = 0; k < 3; ++k) acc[k] = T * cam.bg[k];
     if (threadIdx.x == 0) s_maxnc = 0;
     __syncthreads();
-    if (nc) atomicMax(&s_maxnc, nc);
-    // largest n_contrib of this wave: no lane of the wave composites beyond it
-    uint32_t wmax = nc;
+    if (mine) atomicMax(&s_maxnc, mine);
+    // largest n_contrib of this wave: no pixel of the wave composites beyond it
+    uint32_t wmax = mine;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wmax = max(wmax, (uint32_t)__shfl_xor((int)wmax, o, 64));
     __syncthreads();
     const uint32_t len = rg.y - rg.x;
     const int maxnc = (int)(s_maxnc < len ? s_maxnc : len);
-    const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
+    const float fx = (float)px + 0.5f;
     float* q = &s_q[wv][0][0][0];
     for (int end = maxnc; end > 0; end -= kBwdBatch) {
         const int start = end - kBwdBatch > 0 ? end - kBwdBatch : 0;
         const int n = end - start;
-        if ((int)threadIdx.x < n) {
-            uint32_t gid = a.vals[rg.x + start + threadIdx.x];
-            if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
-            const float4 pa = a.pa[gid], pb = a.pb[gid];
-            s_a[threadIdx.x] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
-            s_b[threadIdx.x] = make_float4(-0.5f * pb.x, pb.y, pb.z, pb.w);
-            s_c[threadIdx.x] = a.pc[gid];
-            s_id[threadIdx.x] = gid;
+#pragma unroll
+        for (int r = 0; r < PX; ++r) {
+            const int slot = threadIdx.x + r * kThreads;
+            if (slot < n) {
+                uint32_t gid = a.vals[rg.x + start + slot];
+                if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
+                const float4 pa = a.pa[gid], pb = a.pb[gid];
+                s_a[slot] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
+                s_b[slot] = make_float4(-0.5f * pb.x, pb.y, pb.z, pb.w);
+                s_c[slot] = a.pc[gid];
+                s_id[slot] = gid;
+            }
         }
-        for (int k = threadIdx.x; k < kBwdBatch * kGradPerGaussian; k += kBwdThreads) (&s_g[0][0])[k] = 0.0f;
+        for (int k = threadIdx.x; k < kBwdBatch * kGradPerGaussian; k += kThreads) (&s_g[0][0])[k] = 0.0f;
         __syncthreads();
         // positions above the wave's largest n_contrib composite nothing here
         const int top = (int)wmax - start < n ? (int)wmax - start : n;
         int ns = 0;  // buffered Gaussians (wave-uniform)
-        // sum the buffered quad partials: lane L < 9 ns takes slot L / 9, partial L % 9
+        // sum the buffered quad partials: lane L < 9 m takes slot L / 9, partial L % 9
         auto flush = [&](int m) {
             wave_lds_sync();
             if (lane < kGradPerGaussian * m) {
@@ -144,41 +201,30 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
             const float dx = fx - ga.x;
             float ta, tb;
             splat_dx_terms(ga.z, ga.w, dx, ta, tb);
-            const float dy = fy - ga.y;
-            const float power = splat_power(ta, tb, gb.x, dy);
-            const float a0 = splat_alpha(gb.y, power);
-            const bool take = pos1 <= nc && splat_takes(power, a0);
-            if (__ballot(take) == 0ull) continue;
-            float gv[kGradPerGaussian];
+            float pw[PX], al[PX], dy[PX];
+            bool tk[PX];
+            bool any = false;
 #pragma unroll
-            for (int k = 0; k < kGradPerGaussian; ++k) gv[k] = 0.0f;
-            if (take) {
-                const float inv = 1.0f / (1.0f - a0);
-                const float Ti = T * inv;
-                const float c[3] = {gb.z, gb.w, s_c[j]};
-                float galpha = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 3; ++k) {
-                    gv[6 + k] = g[k] * a0 * Ti;
-                    galpha += g[k] * (c[k] * Ti - acc[k] * inv);
-                    acc[k] += c[k] * a0 * Ti;
-                }
-                T = Ti;
-                if (a0 < 0.99f) {  // alpha not clamped
-                    gv[5] = galpha * __expf(power);
-                    const float gp = galpha * a0;
-                    const float A = -2.0f * ga.z, B = -ga.w, C = -2.0f * gb.x;
-                    gv[0] = gp * (A * dx + B * dy);
-                    gv[1] = gp * (C * dy + B * dx);
-                    gv[2] = gp * (-0.5f * dx * dx);
-                    gv[3] = gp * (-dx * dy);
-                    gv[4] = gp * (-0.5f * dy * dy);
-                }
+            for (int k = 0; k < PX; ++k) {
+                dy[k] = (float)(py0 + k) + 0.5f - ga.y;
+                pw[k] = splat_power(ta, tb, gb.x, dy[k]);
+                al[k] = splat_alpha(gb.y, pw[k]);
+                tk[k] = pos1 <= P[k].nc && splat_takes(pw[k], al[k]);
+                any = any || tk[k];
             }
+            if (__ballot(any) == 0ull) continue;
+            float gv[kGradPerGaussian];
+            const float cb = s_c[j];
+            pixel_grad<true>(P[0], tk[0], al[0], __expf(pw[0]), dx, dy[0], gb.z, gb.w, cb, gv);
+            // the second pixel row of the wave (PX = 2) is skipped when none of it composites
+            if (PX == 2 && __ballot(tk[PX - 1]) != 0ull)
+                pixel_grad<false>(P[PX - 1], tk[PX - 1], al[PX - 1], __expf(pw[PX - 1]), dx, dy[PX - 1], gb.z, gb.w,
+                                  cb, gv);
 #pragma unroll
-            for (int k = 0; k < kGradPerGaussian; ++k) {
-                const float v = quad_sum(gv[k]);
-                if ((lane & 3) == 0) q[(ns * kGradPerGaussian + k) * 16 + (lane >> 2)] = v;
+            for (int k = 0; k < kGradPerGaussian; ++k) gv[k] = quad_sum(gv[k]);
+            if ((lane & 3) == 0) {
+#pragma unroll
+                for (int k = 0; k < kGradPerGaussian; ++k) q[(ns * kGradPerGaussian + k) * 16 + (lane >> 2)] = gv[k];
             }
             if (lane == 0) s_slot[wv][ns] = j;
             if (++ns == kSlots) {
@@ -188,12 +234,25 @@ __global__ void __launch_bounds__(kBwdThreads) raster_backward_kernel(RasterBwdA
         }
         if (ns) flush(ns);
         __syncthreads();
-        if ((int)threadIdx.x < n) {
-            float* dst = a.gacc + (size_t)s_id[threadIdx.x] * kGradPerGaussian;
 #pragma unroll
-            for (int k = 0; k < kGradPerGaussian; ++k) {
-                const float v = s_g[threadIdx.x][k];
-                if (v != 0.0f) atomicAdd(dst + k, v);
+        for (int r = 0; r < PX; ++r) {
+            const int slot = threadIdx.x + r * kThreads;
+            if (slot < n) {
+                // moments -> d/d(u, v, A, B, C) with power = -(A dx^2 + C dy^2)/2 - B dx dy
+                float v[kGradPerGaussian];
+#pragma unroll
+                for (int k = 0; k < kGradPerGaussian; ++k) v[k] = s_g[slot][k];
+                const float A = -2.0f * s_a[slot].z, B = -s_a[slot].w, C = -2.0f * s_b[slot].x;
+                const float mx = v[0], my = v[1], mxx = v[2], mxy = v[3], myy = v[4];
+                v[0] = A * mx + B * my;
+                v[1] = C * my + B * mx;
+                v[2] = -0.5f * mxx;
+                v[3] = -mxy;
+                v[4] = -0.5f * myy;
+                float* dst = a.gacc + (size_t)s_id[slot] * kGradPerGaussian;
+#pragma unroll
+                for (int k = 0; k < kGradPerGaussian; ++k)
+                    if (v[k] != 0.0f) atomicAdd(dst + k, v[k]);
             }
         }
         __syncthreads();
@@ -396,8 +455,13 @@ hipError_t launch_render_backward(const RenderBwdArgs& a, hipStream_t s) {
                      reinterpret_cast<const float*>(ws + L.pc), cams, a.W, a.H, L.tiles_x,
                      (uint32_t)(L.tiles_x * L.tiles_y), (uint64_t)L.cap, N, a.grad_image, a.T_final, a.n_contrib,
                      gacc};
-    IA_LAUNCH("raster_backward_kernel", raster_backward_kernel, dim3(L.tiles_x, L.tiles_y, L.frames),
-              dim3(kBwdThreads), 0, s, rb);
+    // two pixels per thread when there are enough tiles to fill the chip twice over
+    if (L.ntiles_all >= kBwdTwoPixelTiles)
+        IA_LAUNCH("raster_backward_kernel", raster_backward_kernel<2>, dim3(L.tiles_x, L.tiles_y, L.frames),
+                  dim3(128), 0, s, rb);
+    else
+        IA_LAUNCH("raster_backward_kernel", raster_backward_kernel<1>, dim3(L.tiles_x, L.tiles_y, L.frames),
+                  dim3(256), 0, s, rb);
     PreBwdArgs pb{a.means, a.means_stride, a.scales, a.quats, cams, fo, L.frames, N,
                   reinterpret_cast<const uint32_t*>(ws + L.tiles), gacc, a.g_means, a.g_scales, a.g_quats,
                   a.g_opacity, a.g_colors};
