@@ -8,7 +8,8 @@
 //   mlp_bwd_kernel  one wave per 16 Gaussians at a time (persistent grid):
 //       forward  the decoder on v_mfma_f32_16x16x32_f16 exactly as the decode
 //                runs it (same operands, same fp16 roundings), keeping the
-//                fp32 pre-activations of both hidden layers;
+//                activation derivative at both hidden layers' pre-activations
+//                (GELU' shares the erf polynomial and exponential of GELU);
 //       Eq. 11   dr from the upstream gradients: exp' = s below the clip,
 //                (I - q q^T) / |r| for the normalisation, sigma' = c (1 - c);
 //       Eq. 10   data gradients dx = W^T (dy act'(a)) on
@@ -58,8 +59,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// d/dx GELU(x) = Phi(x) + x phi(x), with erf as in gelu_fp16path.
-__device__ __forceinline__ float gelu_grad_fp16path(float x) {
+// GELU of the fp16 path (the same operations as gelu_fp16path, so the value
+// is bit-identical) and its derivative Phi(x) + x phi(x), which reuses the
+// erf polynomial and exp(-x^2 / 2).  ReLU when gelu is false.
+__device__ __forceinline__ float act_fwd_grad(bool gelu, float x, float& d) {
+    if (!gelu) {
+        d = x > 0.0f ? 1.0f : 0.0f;
+        return x > 0.0f ? x : 0.0f;
+    }
     const float u = fabsf(x) * 0.70710678118654752f;
     const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
     float poly = fmaf(t, 1.061405429f, -1.453152027f);
@@ -68,16 +75,9 @@ __device__ __forceinline__ float gelu_grad_fp16path(float x) {
     poly = fmaf(t, poly, 0.254829592f);
     const float e = __expf(-(u * u));
     const float erf_u = fmaf(-(poly * t), e, 1.0f);
-    const float Phi = 0.5f * (1.0f + copysignf(erf_u, x));
-    return Phi + x * (e * 0.39894228040143268f);  // e = exp(-x^2 / 2)
-}
-
-__device__ __forceinline__ float act_grad(bool gelu, float x) {
-    return gelu ? gelu_grad_fp16path(x) : (x > 0.0f ? 1.0f : 0.0f);
-}
-
-__device__ __forceinline__ float act_fwd(bool gelu, float x) {
-    return gelu ? gelu_fp16path(x) : (x > 0.0f ? x : 0.0f);
+    const float one_erf = 1.0f + copysignf(erf_u, x);
+    d = fmaf(x * e, 0.39894228040143268f, 0.5f * one_erf);  // e = exp(-x^2 / 2)
+    return 0.5f * x * one_erf;
 }
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         const int l0 = 2 * q;
         const half8_t Z = cat8(unpack2(a.z[(size_t)l0 * a.zstride + gi], a.z[(size_t)(l0 + 1) * a.zstride + gi]),
                                unpack2(a.z[(size_t)(l0 + 8) * a.zstride + gi], a.z[(size_t)(l0 + 9) * a.zstride + gi]));
-        floatx4_t P1[4], P2[4];
+        floatx4_t P1[4], P2[4];  // act' of the hidden pre-activations
         half8_t H1[2], H2[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -199,10 +199,11 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
             half8_t h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                P1[2 * m][e] += B1[2 * m][e];
-                P1[2 * m + 1][e] += B1[2 * m + 1][e];
-                h[e] = (_Float16)act_fwd(gelu, P1[2 * m][e]);
-                h[4 + e] = (_Float16)act_fwd(gelu, P1[2 * m + 1][e]);
+                float d0, d1;
+                h[e] = (_Float16)act_fwd_grad(gelu, P1[2 * m][e] + B1[2 * m][e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad(gelu, P1[2 * m + 1][e] + B1[2 * m + 1][e], d1);
+                P1[2 * m][e] = d0;  // from here on: act'(a1)
+                P1[2 * m + 1][e] = d1;
             }
             H1[m] = h;
         }
@@ -217,13 +218,12 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
             half8_t h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                lo[e] += B2[2 * m][e];
-                hi[e] += B2[2 * m + 1][e];
-                h[e] = (_Float16)act_fwd(gelu, lo[e]);
-                h[4 + e] = (_Float16)act_fwd(gelu, hi[e]);
+                float d0, d1;
+                h[e] = (_Float16)act_fwd_grad(gelu, lo[e] + B2[2 * m][e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad(gelu, hi[e] + B2[2 * m + 1][e], d1);
+                P2[2 * m][e] = d0;  // act'(a2)
+                P2[2 * m + 1][e] = d1;
             }
-            P2[2 * m] = lo;
-            P2[2 * m + 1] = hi;
             H2[m] = h;
         }
         floatx4_t accO = {0, 0, 0, 0};
@@ -310,7 +310,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                D[rb][e] *= act_grad(gelu, P2[rb][e]);
+                D[rb][e] *= P2[rb][e];
                 gb2[rb][e] += D[rb][e];
             }
         // ---------------- layer 2: dW2 += da2 H1^T
@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                E[rb][e] *= act_grad(gelu, P1[rb][e]);
+                E[rb][e] *= P1[rb][e];
                 gb1[rb][e] += E[rb][e];
             }
         // ---------------- layer 1: dW1 += da1 z^T
