@@ -28,8 +28,8 @@
 //       float atomics; for positions dz/df_axis = sum_c (+-1) prod_{other
 //       axes} w table[c] (time carries no gradient), times (res - 1), then the
 //       Jacobian of Eq. 7, added to the position gradient with float atomics.
-// After the last chunk a reduction sums the partial buffer in a fixed order
-// (deterministic weight and bias gradients).
+// After the last chunk a two-stage reduction sums the partial buffer in a
+// fixed order (deterministic weight and bias gradients).
 #include <hip/hip_runtime.h>
 
 #include "decode_common.h"
@@ -44,6 +44,7 @@ constexpr int kTS = 18;  // row stride (floats) of the per-wave transpose buffer
 // per lane: 4 head tiles + 16 W2 tiles + 8 W1 tiles (4 floats each) + 36 bias partials
 constexpr int kTileSlots = (4 + 16 + 8) * 4;
 constexpr int kBiasSlots = 4 + 16 + 16;
+static_assert(kDecodeBwdBlocks * kBwdWaves % kDecodeBwdGroups == 0, "groups must split the waves evenly");
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
@@ -420,7 +421,19 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
     }
 }
 
-// Sum the per-wave partials in wave order.  Thread t < kTileSlots * 64 owns
+// First stage of the partial sums: block (slot j, group g) adds the slot of
+// waves [g W, (g + 1) W), W = waves / groups, in wave order, lane by lane.
+__global__ void __launch_bounds__(64) mlp_bwd_group_kernel(const float* partial, int waves_per_group,
+                                                           float* group_sums) {
+    const int stride = (kTileSlots + kBiasSlots) * 64;
+    const int j = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+    const float* src = partial + (size_t)g * waves_per_group * stride + j * 64 + lane;
+    float s = 0.0f;
+    for (int w = 0; w < waves_per_group; ++w) s += src[(size_t)w * stride];
+    group_sums[(size_t)g * stride + j * 64 + lane] = s;
+}
+
+// Sum the per-wave (or per-group) partials in order.  Thread t < kTileSlots * 64 owns
 // one (slot, lane) of the weight tiles; the next 36 * 4 threads own one bias
 // slot of one lane group q (summed over its 16 lanes c).
 __global__ void __launch_bounds__(256) mlp_bwd_reduce_kernel(const float* partial, int nwaves, float* gW1,
@@ -632,12 +645,18 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
                       (float*)nullptr);
     }
     if (first) {  // N = 0: the weight and bias gradients are zero
-        IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(kDecodeBwdPartialFloats, 256, 8192)),
-                  dim3(256), 0, s, b.partial, (int64_t)kDecodeBwdPartialFloats, (const float*)nullptr);
+        const int64_t nf = (int64_t)kDecodeBwdBlocks * kBwdWaves * (kTileSlots + kBiasSlots) * 64;
+        IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(nf, 256, 8192)), dim3(256), 0, s, b.partial,
+                  nf, (const float*)nullptr);
     }
+    // fixed-order two-stage sum of the per-wave partials (deterministic)
+    const int nwaves = kDecodeBwdBlocks * kBwdWaves;
+    float* groups = b.partial + (size_t)nwaves * (kTileSlots + kBiasSlots) * 64;
+    IA_LAUNCH("mlp_bwd_group_kernel", mlp_bwd_group_kernel, dim3(kTileSlots + kBiasSlots, kDecodeBwdGroups), dim3(64),
+              0, s, b.partial, nwaves / kDecodeBwdGroups, groups);
     const int nred = kTileSlots * 64 + kBiasSlots * 4;
-    IA_LAUNCH("mlp_bwd_reduce_kernel", mlp_bwd_reduce_kernel, dim3((nred + 255) / 256), dim3(256), 0, s, b.partial,
-              kDecodeBwdBlocks * kBwdWaves, b.g_W[0], b.g_W[1], b.g_W[2], b.g_b[0], b.g_b[1], b.g_b[2]);
+    IA_LAUNCH("mlp_bwd_reduce_kernel", mlp_bwd_reduce_kernel, dim3((nred + 255) / 256), dim3(256), 0, s, groups,
+              kDecodeBwdGroups, b.g_W[0], b.g_W[1], b.g_W[2], b.g_b[0], b.g_b[1], b.g_b[2]);
     return hipGetLastError();
 }
 

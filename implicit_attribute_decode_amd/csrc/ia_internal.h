@@ -82,9 +82,11 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
                                   int64_t zstride, hipStream_t s);
 
 // Backward of the fp16 decode: one persistent grid of kDecodeBwdBlocks blocks
-// of four waves; each wave owns a slot of 148 x 64 floats in `partial`.
+// of four waves; each wave owns a slot of 148 x 64 floats in `partial`,
+// followed by kDecodeBwdGroups slots of group sums.
 constexpr int kDecodeBwdBlocks = 256;
-constexpr int64_t kDecodeBwdPartialFloats = (int64_t)kDecodeBwdBlocks * 4 * 148 * 64;
+constexpr int kDecodeBwdGroups = 16;
+constexpr int64_t kDecodeBwdPartialFloats = ((int64_t)kDecodeBwdBlocks * 4 + kDecodeBwdGroups) * 148 * 64;
 
 struct DecodeBwdArgs {
     DecodeArgs fwd;           // the decode being differentiated (parameters, positions, scratch)
