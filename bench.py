@@ -96,7 +96,7 @@ def secondary(S, Decoder, HexPlane, Renderer, stream, log, only: str | None = No
 
 
 def _single(S, Decoder, R, stream) -> dict:
-    """Single: one frame, 100k Gaussians, decode + render."""
+    """Single: one frame, 100k Gaussians, decode + render (RGB head, then the SH colour head)."""
     import torch
 
     dec = S.single_decoder()
@@ -108,7 +108,15 @@ def _single(S, Decoder, R, stream) -> dict:
     res = R.render(dict(means=x, **a), [0, x.shape[0]], [cam], 8 * x.shape[0], aux=True)
     cap = R.count_entries(res) + 4096
     ms = timed(lambda: (D.decode(x, t, out=a), R.render(dict(means=x, **a), [0, x.shape[0]], [cam], cap)), 20, stream)
-    return {"gaussians": int(x.shape[0]), "ms": round(ms, 4), "fps": round(1e3 / ms, 1)}
+    # the same frame with the SH colour decoder (48 coefficients) and the degree-3 SH render
+    Dsh = Decoder(S.single_decoder_sh())
+    ash = Dsh.decode(x, t)
+    res = R.render(dict(means=x, **ash), [0, x.shape[0]], [cam], 8 * x.shape[0], aux=True)
+    cap_sh = R.count_entries(res) + 4096
+    ms_sh = timed(lambda: (Dsh.decode(x, t, out=ash), R.render(dict(means=x, **ash), [0, x.shape[0]], [cam], cap_sh)),
+                  20, stream)
+    return {"gaussians": int(x.shape[0]), "ms": round(ms, 4), "fps": round(1e3 / ms, 1),
+            "sh_head_ms": round(ms_sh, 4), "sh_head_fps": round(1e3 / ms_sh, 1)}
 
 
 def _hexplane(S, HexPlane, R, stream) -> dict:

@@ -59,7 +59,7 @@ struct ia_decoder {
     ia_mlp_desc mlp;
     ia::HashLevels lv;
     int n_layers;
-    int dims[6];  // dims[0] = in, dims[k+1] = out of layer k; last = 11
+    int dims[6];  // dims[0] = in, dims[k+1] = out of layer k; last = 11 (RGB) or 56 (SH3)
     void* tables = nullptr;
     void* W[4] = {nullptr, nullptr, nullptr, nullptr};
     float* b[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -131,11 +131,15 @@ ia_status check_mlp(const ia_hash_desc* h, const ia_mlp_desc* m) {
     if (m->n_hidden < 1 || m->n_hidden > 2) return fail(IA_ERR_UNSUPPORTED, "mlp.n_hidden must be 1 or 2");
     if (m->activation != IA_ACT_RELU && m->activation != IA_ACT_GELU)
         return fail(IA_ERR_INVALID_ARG, "mlp.activation must be RELU or GELU");
+    if (m->color != IA_COLOR_RGB && m->color != IA_COLOR_SH3)
+        return fail(IA_ERR_INVALID_ARG, "mlp.color must be RGB or SH3");
+    if (m->color == IA_COLOR_SH3 && m->dtype != IA_DTYPE_F16)
+        return fail(IA_ERR_UNSUPPORTED, "the SH colour head is supported on the fp16 decoder");
     for (int k = 0; k < m->n_hidden; ++k)
         if (m->hidden[k] < 1 || m->hidden[k] > 1024) return fail(IA_ERR_INVALID_ARG, "mlp.hidden width out of range");
     if (m->dtype == IA_DTYPE_F16) {
         if (!(m->in_dim == 32 && m->n_hidden == 2 && m->hidden[0] == 64 && m->hidden[1] == 64))
-            return fail(IA_ERR_UNSUPPORTED, "fp16 decoder supports 32 -> 64 -> 64 -> 11 only");
+            return fail(IA_ERR_UNSUPPORTED, "fp16 decoder supports a 32 -> 64 -> 64 trunk only");
         if (h->table_dtype != IA_DTYPE_F16) return fail(IA_ERR_UNSUPPORTED, "fp16 decoder needs an fp16 hash table");
         return IA_OK;
     }
@@ -147,7 +151,9 @@ ia_status check_mlp(const ia_hash_desc* h, const ia_mlp_desc* m) {
     return IA_OK;
 }
 
-bool outputs_ok(const ia_gaussians* o) { return o && o->scales && o->quats && o->colors && o->opacity; }
+bool outputs_ok(const ia_gaussians* o, bool sh) {
+    return o && o->scales && o->quats && (sh ? o->sh != nullptr : o->colors != nullptr) && o->opacity;
+}
 
 // Launch arguments of a decode of N Gaussians (outputs left null).
 ia::DecodeArgs decode_args(const ia_decoder* dec, const float* pos, int stride, float t, int64_t N) {
@@ -162,6 +168,7 @@ ia::DecodeArgs decode_args(const ia_decoder* dec, const float* pos, int stride, 
     a.n_hidden = dec->mlp.n_hidden;
     for (int k = 0; k < 4; ++k) a.hidden[k] = dec->mlp.hidden[k];
     a.act = dec->mlp.activation;
+    a.sh_head = dec->mlp.color == IA_COLOR_SH3;
     a.pos = pos;
     a.stride = stride;
     a.t_scalar = t;
@@ -183,12 +190,14 @@ ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, flo
     if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
     if (N == 0) return IA_OK;
     if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
-    if (!outputs_ok(out)) return fail(IA_ERR_INVALID_ARG, "output scales/quats/colors/opacity must be non-null");
+    if (!outputs_ok(out, dec->mlp.color == IA_COLOR_SH3))
+        return fail(IA_ERR_INVALID_ARG, "output scales/quats/colors (or sh)/opacity must be non-null");
     if (N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N too large");
     ia::DecodeArgs a = decode_args(dec, pos, stride, t, N);
     a.scales = out->scales;
     a.quats = out->quats;
     a.colors = out->colors;
+    a.sh = out->sh;
     a.opacity = out->opacity;
     hipError_t e = ia::launch_decode(a, dec->mlp.dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -216,7 +225,7 @@ ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* mlp, ia
     d->n_layers = mlp->n_hidden + 1;
     d->dims[0] = mlp->in_dim;
     for (int k = 0; k < mlp->n_hidden; ++k) d->dims[k + 1] = mlp->hidden[k];
-    d->dims[d->n_layers] = 11;
+    d->dims[d->n_layers] = mlp->color == IA_COLOR_SH3 ? 56 : 11;
     *out = d;
     return IA_OK;
 }
@@ -282,8 +291,8 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
                              const ia_decoder_grads* grads, void* stream) {
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
-    if (dec->mlp.dtype != IA_DTYPE_F16)
-        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the fp16 decoder (32 -> 64 -> 64 -> 11)");
+    if (dec->mlp.dtype != IA_DTYPE_F16 || dec->mlp.color != IA_COLOR_RGB)
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the fp16 decoder with the RGB head");
     if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
     if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
     if (N < 0 || N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N must be in [0, 2^40]");
@@ -292,7 +301,7 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
         if (!grads->weights[k] || !grads->biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias gradient");
     if (N > 0) {
         if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
-        if (!outputs_ok(grad_attr))
+        if (!outputs_ok(grad_attr, false))
             return fail(IA_ERR_INVALID_ARG, "grad_attr scales/quats/colors/opacity must be non-null");
     }
     ia::DecodeBwdArgs b{};

@@ -204,7 +204,8 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // shuffles sum the four partial results.  Output z[level][i] = two fp16
 // features packed in 32 bits (RNE).
 //
-// mlp_f16_kernel: the 32 -> 64 -> 64 -> 11 decoder on v_mfma_f32_16x16x32_f16.
+// mlp_f16_kernel: the 32 -> 64 -> 64 -> 11 (or 56, SH colour) decoder on
+// v_mfma_f32_16x16x32_f16.
 // Register layout (wave64, lane l, q = l/16, c = l%16): A supplies row c and
 // B column c, each with eight k-slots per lane that A and B share; D holds
 // rows 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows.
@@ -300,23 +301,65 @@ __device__ __forceinline__ half4_t act_tile(floatx4 acc, const float* bias, bool
     return h;
 }
 
+// Head block of the SH colour decoder for one 16-Gaussian column group, and
+// Eq. 11: rows 0-2 scale, 3-6 rotation (normalised), 7-54 the 48 SH
+// coefficients (no activation), 55 opacity (sigmoid); rows 56-63 are zero.
+// Lane (q, c) holds rows 16 hb + 4 q + e of Gaussian gl.
+__device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (&A3)[4][2], const float (&B3)[4][4],
+                                            half8_t h0, half8_t h1, int64_t gl, int64_t n, int64_t out_off, int q) {
+    float o[4][4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+        floatx4 acc = {0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[hb][0], h0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[hb][1], h1, acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[hb][e] = acc[e] + B3[hb][e];
+    }
+    // rotation rows 3 (q = 0) and 4-6 (q = 1) of the first tile
+    const float part = q == 0 ? o[0][3] * o[0][3] : (q == 1 ? o[0][0] * o[0][0] + o[0][1] * o[0][1] + o[0][2] * o[0][2] : 0.0f);
+    const float other = __shfl_xor(part, 16);
+    const float nrm = fmaxf(sqrtf(part + other), 1e-12f);
+    if (gl >= n) return;
+    const int64_t gi = out_off + gl;
+    float* sh = a.sh + gi * 48;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * hb + 4 * q + e;
+            const float v = o[hb][e];
+            if (row < 3)
+                a.scales[gi * 3 + row] = expf(fminf(v, 20.0f));
+            else if (row < 7)
+                a.quats[gi * 4 + (row - 3)] = v / nrm;
+            else if (row < 55)
+                sh[row - 7] = v;
+            else if (row == 55)
+                a.opacity[gi] = sigmoidf_(v);
+        }
+}
+
 // The decoder on v_mfma_f32_16x16x32_f16: a 32-wide k-block's slots (q, e)
 // map to inputs 32 m + 4 q + e and 32 m + 16 + 4 q + (e - 4), so the rows a
 // lane holds in two consecutive 16-row D tiles are exactly its B slots for
 // the next layer, and the features of levels {2q, 2q+1, 8+2q, 9+2q} the lane
-// loads are exactly its B slots of layer 1.
-__global__ void __launch_bounds__(256, 2) mlp_f16_kernel(DecodeArgs a, const uint32_t* zbuf, int64_t zstride,
-                                                         int64_t n, int64_t out_off) {
+// loads are exactly its B slots of layer 1.  SH: the head block has 56 rows
+// (four 16-row tiles) with the 48 SH coefficients in place of the RGB rows.
+template <bool SH>
+__global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, const uint32_t* zbuf,
+                                                                  int64_t zstride, int64_t n, int64_t out_off) {
+    constexpr int NH = SH ? 4 : 1, kHeadRows = SH ? 56 : 11;
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, c = lane & 15;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     const _Float16* W1 = (const _Float16*)a.W[0];  // [64][32]
     const _Float16* W2 = (const _Float16*)a.W[1];  // [64][64]
-    const _Float16* Wh = (const _Float16*)a.W[2];  // [11][64]
+    const _Float16* Wh = (const _Float16*)a.W[2];  // [kHeadRows][64]
 
-    half8_t A1[4], A2[4][2], A3[2];
-    float B1[4][4], B2[4][4], B3[4];
+    half8_t A1[4], A2[4][2], A3[NH][2];
+    float B1[4][4], B2[4][4], B3[NH][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         A1[rb] = a_tile32(W1, 32, 64, rb, 0, q, c);
@@ -329,9 +372,15 @@ __global__ void __launch_bounds__(256, 2) mlp_f16_kernel(DecodeArgs a, const uin
         }
     }
 #pragma unroll
-    for (int m = 0; m < 2; ++m) A3[m] = a_tile32(Wh, 64, 11, 0, m, q, c);
+    for (int hb = 0; hb < NH; ++hb) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) B3[e] = (4 * q + e) < 11 ? a.b[2][4 * q + e] : 0.0f;
+        for (int m = 0; m < 2; ++m) A3[hb][m] = a_tile32(Wh, 64, kHeadRows, hb, m, q, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * hb + 4 * q + e;
+            B3[hb][e] = row < kHeadRows ? a.b[2][row] : 0.0f;
+        }
+    }
 
     const bool gelu = a.act == IA_ACT_GELU;
     // features of the next 64 Gaussians are loaded while this tile computes
@@ -380,12 +429,16 @@ __global__ void __launch_bounds__(256, 2) mlp_f16_kernel(DecodeArgs a, const uin
         // ---- head block 64 -> 11 (rows 11..15 are zero) and Eq. 11
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+            if constexpr (SH) {
+                sh_head_out(a, A3, B3, H2[0][g], H2[1][g], base + 16 * g + c, n, out_off, q);
+                continue;
+            }
             floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
-            for (int k = 0; k < 2; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[k], H2[k][g], acc, 0, 0, 0);
+            for (int k = 0; k < 2; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[0][k], H2[k][g], acc, 0, 0, 0);
             float o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[e] + B3[e];
+            for (int e = 0; e < 4; ++e) o[e] = acc[e] + B3[0][e];
             // lane q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
             float part = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
             float other = __shfl_xor(part, 16);
@@ -459,10 +512,20 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             if (overlap) {
                 if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;
                 if ((e = hipStreamWaitEvent(a.side, a.ev_gather[k & 1], 0)) != hipSuccess) return e;
-                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel, dim3(grid), dim3(256), 0, a.side, a, zb, a.zcap, n, off);
+                if (a.sh_head)
+                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, a.side, a, zb, a.zcap,
+                              n, off);
+                else
+                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, a.side, a, zb, a.zcap,
+                              n, off);
                 if ((e = hipEventRecord(a.ev_mlp[k & 1], a.side)) != hipSuccess) return e;
             } else {
-                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel, dim3(grid), dim3(256), 0, s, a, zb, a.zcap, n, off);
+                if (a.sh_head)
+                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, s, a, zb, a.zcap, n,
+                              off);
+                else
+                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, s, a, zb, a.zcap, n,
+                              off);
             }
         }
         if (overlap) {

@@ -56,6 +56,7 @@ struct DecodeArgs {
     int n_hidden;
     int hidden[4];
     int act;
+    int sh_head;       // 1: the head block is 56 rows with 48 SH coefficients as the colour
     const float* pos;  // [N, stride]
     int stride;        // 3 (scalar t) or 4 (per-point t)
     float t_scalar;
@@ -63,6 +64,7 @@ struct DecodeArgs {
     float* scales;
     float* quats;
     float* colors;
+    float* sh;  // [N][48] for the SH head
     float* opacity;
     uint32_t* zbuf;  // fp16 path: feature scratch [2][L][zcap] (packed fp16 pairs), then [zcap] float4
     int64_t zcap;    // Gaussians per chunk the scratch holds

@@ -26,9 +26,11 @@ class Decoder:
         hd = ia.HashDesc(int(h.L), int(h.F), int(h.log2T), float(h.base_res), float(h.growth), int(h.temporal_res),
                          ia.IA_DTYPE_F16 if h.table_f16 else ia.IA_DTYPE_F32, float(h.t_min), float(h.t_max))
         hidden = list(m.dims[1:-1])
+        self.sh = int(m.dims[-1]) == 56  # SH colour head (48 coefficients)
         md = ia.MLPDesc(int(m.dims[0]), len(hidden), (ia.C.c_int32 * 4)(*(hidden + [0] * (4 - len(hidden)))),
                         ia.IA_ACT_GELU if m.act == "gelu" else ia.IA_ACT_RELU,
-                        ia.IA_DTYPE_F16 if f16 else ia.IA_DTYPE_F32)
+                        ia.IA_DTYPE_F16 if f16 else ia.IA_DTYPE_F32,
+                        ia.IA_COLOR_SH3 if self.sh else ia.IA_COLOR_RGB)
         self.handle = ia.ia_decoder_create(hd, md)
         self.device = device
         self._tables = _dev(params.tables, device=device)
@@ -40,21 +42,29 @@ class Decoder:
     def _out(self, N, out):
         if out is None:
             out = dict(scales=torch.empty((N, 3), device=self.device), quats=torch.empty((N, 4), device=self.device),
-                       colors=torch.empty((N, 3), device=self.device), opacity=torch.empty((N,), device=self.device))
+                       opacity=torch.empty((N,), device=self.device))
+            if self.sh:
+                out["sh"] = torch.empty((N, 16, 3), device=self.device)
+            else:
+                out["colors"] = torch.empty((N, 3), device=self.device)
         return out
 
+    def _gaussians(self, out):
+        return ia.gaussians(scales=out["scales"], quats=out["quats"], colors=out.get("colors"), sh=out.get("sh"),
+                            opacity=out["opacity"], sh_degree=3 if self.sh else -1)
+
     def decode(self, xyz: torch.Tensor, t: float, out: dict | None = None) -> dict:
+        """Decoded attributes: scales, quats, opacity and colors [N,3] (RGB
+        head) or sh [N,16,3] (SH head)."""
         N = int(xyz.shape[0])
         out = self._out(N, out)
-        g = ia.gaussians(scales=out["scales"], quats=out["quats"], colors=out["colors"], opacity=out["opacity"])
-        ia.ia_decode(self.handle, xyz, N, t, g)
+        ia.ia_decode(self.handle, xyz, N, t, self._gaussians(out))
         return out
 
     def decode_xyzt(self, xyzt: torch.Tensor, out: dict | None = None) -> dict:
         N = int(xyzt.shape[0])
         out = self._out(N, out)
-        g = ia.gaussians(scales=out["scales"], quats=out["quats"], colors=out["colors"], opacity=out["opacity"])
-        ia.ia_decode_xyzt(self.handle, xyzt, N, g)
+        ia.ia_decode_xyzt(self.handle, xyzt, N, self._gaussians(out))
         return out
 
     def backward(self, pos: torch.Tensor, grad_attr: dict, t: float | None = None, grad_means=None,

@@ -161,11 +161,13 @@ def origin_camera(W=64, H=64, f=60.0) -> Camera:
 # --------------------------------------------------------------------------
 
 
-def _head_bias(scale_bias: float) -> np.ndarray:
-    b = np.zeros(11, np.float32)
+def _head_bias(scale_bias: float, rows: int = 11) -> np.ndarray:
+    """Head-block biases: scale, rotation (w,x,y,z) = (1,0,0,0), colour 0 (RGB
+    or SH, no special initialisation), opacity logit(0.1) in the last row."""
+    b = np.zeros(rows, np.float32)
     b[0:3] = scale_bias
-    b[3] = 1.0  # rotation (w,x,y,z) = (1,0,0,0)
-    b[10] = LOGIT_0_1
+    b[3] = 1.0
+    b[rows - 1] = LOGIT_0_1
     return b
 
 
@@ -184,7 +186,7 @@ def make_decoder(rng: np.random.Generator, hcfg: HashConfig, mcfg: MLPConfig,
         b = np.zeros(fan_out, np.float32)
         if i == len(dims) - 2:
             w[0:3] *= scale_row_gain
-            b = _head_bias(scale_bias)
+            b = _head_bias(scale_bias, fan_out)
         weights.append(w.astype(wdt))
         biases.append(b)
     return DecoderParams(hash=hcfg, mlp=mcfg, tables=tables, weights=weights, biases=biases)
@@ -204,6 +206,19 @@ def tiny_decoder(seed: int = 1) -> DecoderParams:
     # image has Gaussians a few pixels wide.
     return make_decoder(rng, tiny_hash(), MLPConfig(dims=[8, 32, 11], act="relu", f16=False),
                         scale_bias=-3.0)
+
+
+def single_decoder_sh(seed: int = 2) -> DecoderParams:
+    """The Single decoder with the SH colour head (56 outputs: 48 degree-3
+    SH coefficients in place of RGB); the SH rows are scaled by 0.5 so that
+    colours stay mostly inside [0, 1]."""
+    rng = np.random.default_rng([seed, 103])
+    d = make_decoder(rng, single_hash(), MLPConfig(dims=[32, 64, 64, 56], act="gelu", f16=True),
+                     scale_bias=0.5 * (math.log(1e-3) + math.log(5e-2)), scale_row_gain=2.0)
+    w = d.weights[-1].astype(np.float32)
+    w[7:55] *= 0.5
+    d.weights[-1] = w.astype(np.float16)
+    return d
 
 
 def single_decoder(seed: int = 2) -> DecoderParams:

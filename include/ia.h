@@ -54,6 +54,11 @@ typedef int32_t ia_status;
 #define IA_ACT_RELU 0
 #define IA_ACT_GELU 1 /* exact: 0.5 x (1 + erf(x / sqrt 2)) */
 
+/* Colour head of the decoder ([SPIN] §3.3 Eq. 10-11) */
+#define IA_COLOR_RGB 0 /* 3 outputs, sigmoid                                   */
+#define IA_COLOR_SH3 1 /* 48 spherical-harmonic coefficients of degree 3, no
+                          activation (the paper's colour decoder)              */
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 IA_API const char* ia_last_error(void);
 
@@ -92,17 +97,21 @@ typedef struct {
 } ia_hash_desc;
 
 /* Decoder MLP ([SPIN] §3.3 Eq. 10): a shared trunk of n_hidden layers
- * act(W x + b) followed by one linear head block of 11 outputs in the order
- * scale(3) | rotation(4: w,x,y,z) | colour(3) | opacity(1).  Supported:
- *   dtype F32: (in_dim, hidden) = (8, {32}), (32, {64}) or (32, {64, 64})
+ * act(W x + b) followed by one linear head block in the order
+ * scale(3) | rotation(4: w,x,y,z) | colour | opacity(1), where colour is 3
+ * RGB outputs (color = IA_COLOR_RGB: 11 outputs) or 48 SH coefficients,
+ * coefficient-major [16][3] (IA_COLOR_SH3: 56 outputs).  Supported:
+ *   dtype F32: (in_dim, hidden) = (8, {32}), (32, {64}) or (32, {64, 64}); RGB
  *   dtype F16: in_dim = 32, n_hidden = 2, hidden = {64, 64}, fp16 MFMA with
- *              fp32 accumulation; hidden activations rounded to fp16. */
+ *              fp32 accumulation; hidden activations rounded to fp16; RGB or
+ *              SH3. */
 typedef struct {
     int32_t in_dim;
     int32_t n_hidden;
     int32_t hidden[4];
     int32_t activation; /* IA_ACT_RELU or IA_ACT_GELU */
     int32_t dtype;      /* IA_DTYPE_F32 or IA_DTYPE_F16 (weights and math) */
+    int32_t color;      /* IA_COLOR_RGB or IA_COLOR_SH3                    */
 } ia_mlp_desc;
 
 typedef struct ia_decoder ia_decoder;
@@ -129,8 +138,10 @@ IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, cons
 /* Decode N Gaussians at one time t ([SPIN] §3.3 Eq. 7-11):
  *   xyz : device [N,3] positions mu
  *   out : device scales[N,3] = exp(min(s_hat,20)), quats[N,4] = r_hat/|r_hat|,
- *         colors[N,3] = sigmoid(c_hat), opacity[N] = sigmoid(o_hat);
- *         out->means is not written (the input positions are the means).
+ *         colors[N,3] = sigmoid(c_hat) (RGB head) or sh[N,16,3] = sh_hat
+ *         (SH3 head; out->colors is then not used), opacity[N] =
+ *         sigmoid(o_hat); out->means is not written (the input positions
+ *         are the means).
  * N = 0 is a no-op.  Errors: INVALID_ARG (null, N < 0, params not set). */
 IA_API ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t, const ia_gaussians* out,
                     void* stream);

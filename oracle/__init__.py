@@ -72,6 +72,7 @@ def _declare(L):
     L.orc_encode.argtypes = [P, P, P, C.c_long, P]
     L.orc_mlp_forward.argtypes = [P, P, P, P, C.c_long, C.c_int, P]
     L.orc_activate.argtypes = [P, C.c_long, P, P, P, P]
+    L.orc_activate_sh.argtypes = [P, C.c_long, P, P, P, P]
     L.orc_decode.argtypes = [P, P, P, P, P, P, C.c_int, C.c_float, C.c_long, C.c_int, P, P, P, P, P]
     L.orc_sh_basis.argtypes = [P, C.c_long, P]
     L.orc_hexplane_features.argtypes = [P, P, P, C.c_float, C.c_long, P]
@@ -196,9 +197,24 @@ def activate(raw: np.ndarray) -> dict:
     return dict(scales=s, quats=q, colors=c, opacity=o)
 
 
+def activate_sh(raw: np.ndarray) -> dict:
+    """Eq. 11 with the SH colour head: raw [N,56] -> scales, quats, sh [N,16,3], opacity."""
+    raw = _c(raw, np.float64)
+    n = raw.shape[0]
+    s, q, sh, o = np.zeros((n, 3)), np.zeros((n, 4)), np.zeros((n, 16, 3)), np.zeros(n)
+    lib().orc_activate_sh(_p(raw), n, _p(s), _p(q), _p(sh), _p(o))
+    return dict(scales=s, quats=q, sh=sh, opacity=o)
+
+
 def decode(dec, pos: np.ndarray, t: float | None = None, mode: int = 0) -> dict:
-    """Full decode of a DecoderParams-like object.  mode 1 = fp16 emulation."""
+    """Full decode of a DecoderParams-like object.  mode 1 = fp16 emulation.
+    A head of 56 outputs is the SH colour decoder (returns sh [N,16,3]
+    instead of colors)."""
     h, m = dec.hash, dec.mlp
+    if int(m.dims[-1]) == 56:
+        z = encode(h, dec.tables, normalize(h, pos, t))
+        raw = mlp_forward(m.dims, m.act, m.f16, dec.weights, dec.biases, z, mode)
+        return dict(raw=raw, **activate_sh(raw))
     pos = _c(pos, np.float32)
     n, stride = pos.shape
     tb = _tables(h, dec.tables)

@@ -282,6 +282,26 @@ EXPORT void orc_activate(const double* raw, long N, double* scales, double* quat
     }
 }
 
+/*
+ * Eq. 11 with the SH colour decoder ([SPIN] §3.3: the colour head regresses
+ * the SH coefficients directly) on the 56 head outputs
+ * [s(3) | r(4) | sh(48, coefficient-major [16][3]) | o]:
+ *   s = exp(min(s_hat, 20)), r = r_hat / max(||r_hat||, 1e-12),
+ *   sh = sh_hat (no activation), o = sigmoid(o_hat).
+ */
+EXPORT void orc_activate_sh(const double* raw, long N, double* scales, double* quats, double* sh,
+                            double* opacity) {
+    for (long i = 0; i < N; ++i) {
+        const double* r = raw + i * 56;
+        for (int k = 0; k < 3; ++k) scales[i * 3 + k] = exp(r[k] < 20.0 ? r[k] : 20.0);
+        double n = sqrt(r[3] * r[3] + r[4] * r[4] + r[5] * r[5] + r[6] * r[6]);
+        if (n < 1e-12) n = 1e-12;
+        for (int k = 0; k < 4; ++k) quats[i * 4 + k] = r[3 + k] / n;
+        for (int k = 0; k < 48; ++k) sh[i * 48 + k] = r[7 + k];
+        opacity[i] = sigmoid(r[55]);
+    }
+}
+
 /* Full decode: normalise -> encode -> MLP -> activations.  raw is [N][11]. */
 EXPORT void orc_decode(const orc_hash* h, const void* tables, const orc_mlp* m, const void* const* W,
                        const float* const* b, const float* pos, int stride, float t_scalar, long N,

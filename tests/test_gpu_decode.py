@@ -121,6 +121,33 @@ def test_single_fp16_ragged_xyzt(n):
     _check_f16(g, o, e, f"xyzt n={n}")
 
 
+def _check_f16_sh(g, o, emu, tag):
+    for k in ("scales", "quats", "sh", "opacity"):
+        err = np.abs(g[k] - o[k]).max()
+        err_e = np.abs(g[k] - emu[k]).max()
+        say(f"[{tag}] {k}: max|gpu-oracle64| {err:.2e}  max|gpu-oracle16emu| {err_e:.2e}")
+        assert err <= 5e-3, (k, err)
+        assert err_e <= 1e-3, (k, err_e)
+
+
+def test_single_fp16_sh_colour_head_full_frame():
+    """The SH colour decoder (56-row head: 48 degree-3 coefficients, no
+    activation) on a full Single frame, same bars as the RGB head."""
+    dec = S.single_decoder_sh()
+    pos, t = S.single_positions(2)
+    g = _gpu_decode(dec, pos, t)
+    assert "colors" not in g and g["sh"].shape == (pos.shape[0], 16, 3)
+    _check_f16_sh(g, O.decode(dec, pos, t, mode=0), O.decode(dec, pos, t, mode=1), "sh head")
+
+
+@pytest.mark.parametrize("n", [1, 17, 4097])
+def test_sh_colour_head_ragged_xyzt(n):
+    dec = S.single_decoder_sh()
+    pos = _edge_positions(np.random.default_rng(300 + n), n)
+    g = _gpu_decode(dec, pos)
+    _check_f16_sh(g, O.decode(dec, pos, mode=0), O.decode(dec, pos, mode=1), f"sh xyzt n={n}")
+
+
 def test_decode_zero_is_noop():
     D = Decoder(S.tiny_decoder())
     out = D.decode(torch.empty((0, 3), device="cuda"), 0.5)

@@ -80,6 +80,34 @@ def test_tiny_decode_then_render():
     assert np.abs(img - bf["rgb"])[ok].max() <= 1e-3
 
 
+def test_sh_colour_decoder_then_sh_render():
+    """SH colour head decoded on the GPU, rendered with degree-3 SH colour in
+    the view direction; the oracle renders the GPU's decoded attributes."""
+    dec = S.single_decoder_sh()
+    pos, t = S.single_positions(2)
+    D = Decoder(dec)
+    x = cuda(pos)
+    a = D.decode(x, t)
+    torch.cuda.synchronize()
+    assert "sh" in a and "colors" not in a
+    g = dict(means=x, **a)
+    cam = S.ring_camera(0)
+    fo = np.array([0, pos.shape[0]])
+    h = _host_attrs(g)
+    pre = O.preprocess([cam], fo, h["means"], h["scales"], h["quats"])
+    rgb = O.sh_colors([cam], fo, h["means"], h["sh"])
+    b = O.bin_and_sort([cam], fo, pre)
+    r = O.raster_tiles([cam], b, pre, h["opacity"], rgb)
+    gr = gpu_render(g, fo, [cam], b["E"])
+    check_preprocess_bitexact(gr, pre)
+    vis = pre["tiles"] > 0
+    err = np.abs(gr["rgb"][vis].astype(np.float64) - rgb[vis]).max()
+    say(f"[sh decode] N={pos.shape[0]} E={gr['E']} SH colour max diff {err:.2e}")
+    assert err <= 1e-5
+    check_bins_bitexact(gr, b)
+    say(f"[sh decode] image: {check_image(gr, r)}")
+
+
 def test_single_render_scene_full_frame():
     g, cam, _ = S.single_render_scene()
     _full_check(_attrs_from_gaussians(g), np.array([0, g.n]), [cam], "single")

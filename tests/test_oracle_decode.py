@@ -270,6 +270,43 @@ def test_activations_closed_forms():
     np.testing.assert_allclose(a["opacity"], sps.expit(raw[:, 10]), rtol=1e-14)
 
 
+def test_sh_head_activations_closed_forms():
+    """SH colour head (Eq. 11 with s_h = s_hat): scale, rotation and opacity
+    as for the RGB head, the 48 coefficients passed through unchanged in
+    coefficient-major [16][3] order."""
+    rng = np.random.default_rng(10)
+    raw = rng.standard_normal((40, 56)) * 3
+    raw[0, 1] = 30.0
+    a = O.activate_sh(raw)
+    assert a["scales"][0, 1] == math.exp(20.0)
+    np.testing.assert_allclose(a["scales"][1:], np.exp(raw[1:, 0:3]), rtol=1e-15)
+    np.testing.assert_allclose(a["quats"], raw[:, 3:7] / np.linalg.norm(raw[:, 3:7], axis=1, keepdims=True),
+                               rtol=1e-14)
+    assert np.array_equal(a["sh"].reshape(40, 48), raw[:, 7:55])
+    assert a["sh"][5, 2, 1] == raw[5, 7 + 2 * 3 + 1]
+    np.testing.assert_allclose(a["opacity"], sps.expit(raw[:, 55]), rtol=1e-14)
+
+
+def test_sh_decoder_shares_the_trunk():
+    """An SH decoder whose head block holds the RGB decoder's scale, rotation
+    and opacity rows decodes the same scales, rotations and opacities."""
+    rgb = S.single_decoder()
+    sh = S.single_decoder_sh()
+    W = [w.copy() for w in sh.weights]
+    B = [b.copy() for b in sh.biases]
+    W[0], W[1], B[0], B[1] = rgb.weights[0], rgb.weights[1], rgb.biases[0], rgb.biases[1]
+    W[2][0:7] = rgb.weights[2][0:7]
+    W[2][55] = rgb.weights[2][10]
+    B[2][0:7] = rgb.biases[2][0:7]
+    B[2][55] = rgb.biases[2][10]
+    mixed = S.DecoderParams(hash=rgb.hash, mlp=sh.mlp, tables=rgb.tables, weights=W, biases=B)
+    pos, t = S.single_positions(2, 0.4, 300, 30)
+    a = O.decode(rgb, pos, t, mode=1)
+    b = O.decode(mixed, pos, t, mode=1)
+    for k in ("scales", "quats", "opacity"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
 def test_rotation_head_scale_invariance():
     """Scaling the rotation head's weights and bias by k > 0 leaves r unchanged."""
     dec = S.tiny_decoder()
