@@ -74,6 +74,8 @@ def cpu_baseline(seq, dec, budget_s: float = 15.0, max_frames: int = 12) -> dict
 
 
 HEX_FLOP_PER_GAUSSIAN = 2 * (192 * 256 + 256 * 256 + 256 * 58)  # 259,072
+# paper-scale decoder: four 64 -> 64 -> 64 -> out branches, outs 3 + 4 + 48 + 1
+PAPER_FLOP_PER_GAUSSIAN = 2 * (4 * (64 * 64 + 64 * 64) + 64 * 56)  # 72,704
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
@@ -89,6 +91,8 @@ def secondary(S, Decoder, HexPlane, Renderer, stream, log, only: str | None = No
         out["single_frame"] = _single(S, Decoder, R, stream)
     if only in (None, "hexplane"):
         out["hexplane"] = _hexplane(S, HexPlane, R, stream)
+    if only in (None, "paper"):
+        out["paper_scale"] = _paper(S, Decoder, R, stream)
     if only in (None, "stress"):
         out["stress"] = _stress(S, Decoder, Renderer, stream)
     log(f"secondary: {out}")
@@ -117,6 +121,31 @@ def _single(S, Decoder, R, stream) -> dict:
                   20, stream)
     return {"gaussians": int(x.shape[0]), "ms": round(ms, 4), "fps": round(1e3 / ms, 1),
             "sh_head_ms": round(ms_sh, 4), "sh_head_fps": round(1e3 / ms_sh, 1)}
+
+
+def _paper(S, Decoder, R, stream) -> dict:
+    """Paper-scale decoder (F = 4, 2^21-entry tables, one GELU MLP per
+    attribute, SH colour): one Single frame decoded and rendered with SH, and
+    the decode alone of 20 sequence frames (4M (x,y,z,t) positions)."""
+    import torch
+
+    D = Decoder(S.paper_decoder())
+    pos, t = S.single_positions(2)
+    x = torch.as_tensor(pos, device="cuda")
+    a = D.decode(x, t)
+    cam = S.ring_camera(0)
+    res = R.render(dict(means=x, **a), [0, x.shape[0]], [cam], 8 * x.shape[0], aux=True)
+    cap = R.count_entries(res) + 4096
+    ms = timed(lambda: (D.decode(x, t, out=a), R.render(dict(means=x, **a), [0, x.shape[0]], [cam], cap)), 20, stream)
+    seq = S.Sequence()
+    xyzt = torch.as_tensor(seq.xyzt(list(range(20))), device="cuda")
+    d = D.decode_xyzt(xyzt)
+    ms_d = timed(lambda: D.decode_xyzt(xyzt, out=d), 5, stream)
+    kern = profiled(lambda: D.decode_xyzt(xyzt, out=d), 1)
+    n = int(xyzt.shape[0])
+    return {"single_frame_ms": round(ms, 4), "single_frame_fps": round(1e3 / ms, 1), "decode_gaussians": n,
+            "decode_ms": round(ms_d, 4), "decode_gaussians_per_s": round(n / (ms_d / 1e3)), "decode_kernels_ms": kern,
+            "mlp_flop_per_gaussian": PAPER_FLOP_PER_GAUSSIAN}
 
 
 def _hexplane(S, HexPlane, R, stream) -> dict:
@@ -225,7 +254,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the per-frame comparison and the other workloads (Single, HexPlane, Stress)")
-    ap.add_argument("--only", choices=("single", "hexplane", "stress"),
+    ap.add_argument("--only", choices=("single", "hexplane", "paper", "stress"),
                     help="run just that other workload and print its figures (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (a reference for HBM byte counters)")

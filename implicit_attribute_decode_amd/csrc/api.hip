@@ -58,11 +58,15 @@ struct ia_decoder {
     ia_hash_desc hash;
     ia_mlp_desc mlp;
     ia::HashLevels lv;
-    int n_layers;
-    int dims[6];  // dims[0] = in, dims[k+1] = out of layer k; last = 11 (RGB) or 56 (SH3)
+    int n_layers;  // layers of one chain (trunk + head, or one attribute branch)
+    int dims[6];   // shared: dims[0] = in, dims[k+1] = out of layer k; last = 11 (RGB) or 56 (SH3)
+    int n_mats;    // weight matrices: n_layers (shared) or 4 n_layers (per attribute)
+    int mat_in[ia::kMaxDecoderMats], mat_out[ia::kMaxDecoderMats];
     void* tables = nullptr;
-    void* W[4] = {nullptr, nullptr, nullptr, nullptr};
-    float* b[4] = {nullptr, nullptr, nullptr, nullptr};
+    void* W[ia::kMaxDecoderMats] = {};
+    float* b[ia::kMaxDecoderMats] = {};
+    void* Wt = nullptr;         // per-attribute fp16 decoder: weights in MFMA A-tile order
+    float* bpack = nullptr;     // per-attribute fp16 decoder: biases packed per branch
     uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [chunk] float4
     float* bwd_partial = nullptr;  // fp16 path: per-wave weight-gradient partials of the backward
     hipStream_t side = nullptr;  // fp16 path: MLP stream overlapping the next chunk's gather
@@ -75,12 +79,16 @@ namespace {
 
 void free_decoder_params(ia_decoder* d) {
     if (d->tables) (void)hipFree(d->tables);
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < ia::kMaxDecoderMats; ++k) {
         if (d->W[k]) (void)hipFree(d->W[k]);
         if (d->b[k]) (void)hipFree(d->b[k]);
         d->W[k] = nullptr;
         d->b[k] = nullptr;
     }
+    if (d->Wt) (void)hipFree(d->Wt);
+    if (d->bpack) (void)hipFree(d->bpack);
+    d->Wt = nullptr;
+    d->bpack = nullptr;
     d->tables = nullptr;
     if (d->zbuf) (void)hipFree(d->zbuf);
     d->zbuf = nullptr;
@@ -98,7 +106,8 @@ void free_decoder_params(ia_decoder* d) {
 
 ia_status check_hash(const ia_hash_desc* h, ia::HashLevels* lv) {
     if (h->L < 1 || h->L > ia::kMaxLevels) return fail(IA_ERR_INVALID_ARG, "hash.L must be in 1..32");
-    if (h->F != 2) return fail(IA_ERR_UNSUPPORTED, "hash.F must be 2");
+    if (h->F != 2 && h->F != 4) return fail(IA_ERR_UNSUPPORTED, "hash.F must be 2 or 4");
+    if (h->F == 4 && h->table_dtype != IA_DTYPE_F16) return fail(IA_ERR_UNSUPPORTED, "hash.F = 4 needs an fp16 table");
     if (h->log2T < 4 || h->log2T > 24) return fail(IA_ERR_INVALID_ARG, "hash.log2T must be in 4..24");
     if (!(std::isfinite(h->base_res) && h->base_res >= 2.0)) return fail(IA_ERR_INVALID_ARG, "hash.base_res must be >= 2");
     if (!(std::isfinite(h->growth) && h->growth >= 1.0)) return fail(IA_ERR_INVALID_ARG, "hash.growth must be >= 1");
@@ -135,6 +144,15 @@ ia_status check_mlp(const ia_hash_desc* h, const ia_mlp_desc* m) {
         return fail(IA_ERR_INVALID_ARG, "mlp.color must be RGB or SH3");
     if (m->color == IA_COLOR_SH3 && m->dtype != IA_DTYPE_F16)
         return fail(IA_ERR_UNSUPPORTED, "the SH colour head is supported on the fp16 decoder");
+    if (m->branches != IA_BRANCHES_SHARED && m->branches != IA_BRANCHES_PER_ATTRIBUTE)
+        return fail(IA_ERR_INVALID_ARG, "mlp.branches must be SHARED or PER_ATTRIBUTE");
+    if (m->branches == IA_BRANCHES_PER_ATTRIBUTE) {
+        if (!(m->dtype == IA_DTYPE_F16 && h->F == 4 && m->in_dim == 64 && m->n_hidden == 2 && m->hidden[0] == 64 &&
+              m->hidden[1] == 64))
+            return fail(IA_ERR_UNSUPPORTED, "per-attribute decoders: fp16, F = 4, 64 -> 64 -> 64 -> out only");
+        return IA_OK;
+    }
+    if (h->F != 2) return fail(IA_ERR_UNSUPPORTED, "shared-trunk decoders need F = 2");
     for (int k = 0; k < m->n_hidden; ++k)
         if (m->hidden[k] < 1 || m->hidden[k] > 1024) return fail(IA_ERR_INVALID_ARG, "mlp.hidden width out of range");
     if (m->dtype == IA_DTYPE_F16) {
@@ -160,10 +178,14 @@ ia::DecodeArgs decode_args(const ia_decoder* dec, const float* pos, int stride, 
     ia::DecodeArgs a{};
     a.h = dec->lv;
     a.tables = dec->tables;
-    for (int k = 0; k < dec->n_layers; ++k) {
-        a.W[k] = dec->W[k];
-        a.b[k] = dec->b[k];
-    }
+    if (dec->mlp.branches == IA_BRANCHES_SHARED)
+        for (int k = 0; k < dec->n_layers; ++k) {
+            a.W[k] = dec->W[k];
+            a.b[k] = dec->b[k];
+        }
+    a.branches = dec->mlp.branches == IA_BRANCHES_PER_ATTRIBUTE;
+    a.Wt = dec->Wt;
+    a.bpack = dec->bpack;
     a.in_dim = dec->mlp.in_dim;
     a.n_hidden = dec->mlp.n_hidden;
     for (int k = 0; k < 4; ++k) a.hidden[k] = dec->mlp.hidden[k];
@@ -226,6 +248,22 @@ ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* mlp, ia
     d->dims[0] = mlp->in_dim;
     for (int k = 0; k < mlp->n_hidden; ++k) d->dims[k + 1] = mlp->hidden[k];
     d->dims[d->n_layers] = mlp->color == IA_COLOR_SH3 ? 56 : 11;
+    if (mlp->branches == IA_BRANCHES_SHARED) {
+        d->n_mats = d->n_layers;
+        for (int k = 0; k < d->n_layers; ++k) {
+            d->mat_in[k] = d->dims[k];
+            d->mat_out[k] = d->dims[k + 1];
+        }
+    } else {
+        // branch a: in -> hidden... -> out_a, out_a = scale 3, rotation 4, colour 3 / 48, opacity 1
+        const int outs[4] = {3, 4, mlp->color == IA_COLOR_SH3 ? 48 : 3, 1};
+        d->n_mats = 4 * d->n_layers;
+        for (int br = 0; br < 4; ++br)
+            for (int k = 0; k < d->n_layers; ++k) {
+                d->mat_in[br * d->n_layers + k] = d->dims[k];
+                d->mat_out[br * d->n_layers + k] = k + 1 < d->n_layers ? d->dims[k + 1] : outs[br];
+            }
+    }
     *out = d;
     return IA_OK;
 }
@@ -233,7 +271,7 @@ ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* mlp, ia
 ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
                                 const float* const* biases, int32_t params_on_device, void* stream) {
     if (!dec || !tables || !weights || !biases) return fail(IA_ERR_INVALID_ARG, "null argument");
-    for (int k = 0; k < dec->n_layers; ++k)
+    for (int k = 0; k < dec->n_mats; ++k)
         if (!weights[k] || !biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias pointer");
     const bool dev = params_on_device != 0;
     hipStream_t s = (hipStream_t)stream;
@@ -246,14 +284,26 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
     const size_t tbytes = (size_t)dec->hash.L * dec->lv.T * dec->hash.F * tsize;
     ia_status st = upload_param(&dec->tables, tables, tbytes, dev, s);
     const size_t wsize = dec->mlp.dtype == IA_DTYPE_F16 ? 2 : 4;
-    for (int k = 0; st == IA_OK && k < dec->n_layers; ++k) {
-        const size_t nw = (size_t)dec->dims[k + 1] * dec->dims[k];
+    for (int k = 0; st == IA_OK && k < dec->n_mats; ++k) {
+        const size_t nw = (size_t)dec->mat_out[k] * dec->mat_in[k];
         st = upload_param(&dec->W[k], weights[k], nw * wsize, dev, s);
-        if (st == IA_OK) st = upload_param(reinterpret_cast<void**>(&dec->b[k]), biases[k], 4 * (size_t)dec->dims[k + 1], dev, s);
+        if (st == IA_OK) st = upload_param(reinterpret_cast<void**>(&dec->b[k]), biases[k], 4 * (size_t)dec->mat_out[k], dev, s);
+    }
+    if (st == IA_OK && dec->mlp.branches == IA_BRANCHES_PER_ATTRIBUTE) {
+        const bool sh = dec->mlp.color == IA_COLOR_SH3;
+        hipError_t e = hipMalloc(&dec->Wt, ia::branch_tile_bytes(sh));
+        if (e == hipSuccess) e = hipMalloc(&dec->bpack, ia::branch_bias_bytes(sh));
+        if (e != hipSuccess) {
+            st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
+        } else {
+            e = ia::launch_branch_pack((const _Float16* const*)dec->W, (const float* const*)dec->b, sh, dec->Wt,
+                                       dec->bpack, s);
+            if (e != hipSuccess) st = hip_fail(e, "decoder weight tiling");
+        }
     }
     if (st == IA_OK && dec->mlp.dtype == IA_DTYPE_F16) {
-        // [2][L][chunk] packed feature pairs, then [chunk] normalised positions (float4)
-        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 8 + 16) * ia::kDecodeChunk);
+        // [2][L][chunk] packed fp16 features (F per entry), then [chunk] normalised positions (float4)
+        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 4 * dec->hash.F + 16) * ia::kDecodeChunk);
         if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
         if (st == IA_OK) {
             e = hipMalloc(&dec->bwd_partial, sizeof(float) * (size_t)ia::kDecodeBwdPartialFloats);
@@ -291,8 +341,8 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
                              const ia_decoder_grads* grads, void* stream) {
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
-    if (dec->mlp.dtype != IA_DTYPE_F16 || dec->mlp.color != IA_COLOR_RGB)
-        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the fp16 decoder with the RGB head");
+    if (dec->mlp.dtype != IA_DTYPE_F16 || dec->mlp.color != IA_COLOR_RGB || dec->mlp.branches != IA_BRANCHES_SHARED)
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoder with the RGB head");
     if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
     if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
     if (N < 0 || N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N must be in [0, 2^40]");

@@ -493,8 +493,19 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         // Chunks of at most zcap Gaussians.  With a side stream, the MLP of
         // chunk k runs there while chunk k+1 is normalised and gathered on s;
         // the feature scratch is double-buffered and events order the hand-offs.
-        const size_t zslot = (size_t)a.h.L * a.zcap;
+        const size_t zslot = (size_t)a.h.L * a.zcap * (a.h.F / 2);  // 32-bit words per scratch slot
         float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
+        auto mlp = [&](hipStream_t st, const uint32_t* zb, int64_t n, int64_t off) -> hipError_t {
+            if (a.branches) return launch_mlp_branch(a, zb, a.zcap, n, off, st);
+            // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
+            const int grid = grid_for(256, n, 256 * 8);
+            if (a.sh_head)
+                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, st, a, zb, a.zcap, n, off);
+            else
+                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, st, a, zb, a.zcap, n,
+                          off);
+            return hipGetLastError();
+        };
         const bool overlap = a.side != nullptr && a.N > a.zcap;
         int k = 0;
         for (int64_t off = 0; off < a.N; off += a.zcap, ++k) {
@@ -505,27 +516,19 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             if (overlap && k >= 2 && (e = hipStreamWaitEvent(s, a.ev_mlp[k & 1], 0)) != hipSuccess) return e;
             IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
                       a.pos + off * a.stride, n, xt);
-            IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n,
-                      nchunk, a.h, (const uint32_t*)a.tables, zb, a.zcap);
-            // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
-            const int grid = grid_for(256, n, 256 * 8);
+            if (a.h.F == 4) {
+                if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, a.zcap, s)) != hipSuccess) return e;
+            } else {
+                IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
+                          n, nchunk, a.h, (const uint32_t*)a.tables, zb, a.zcap);
+            }
             if (overlap) {
                 if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;
                 if ((e = hipStreamWaitEvent(a.side, a.ev_gather[k & 1], 0)) != hipSuccess) return e;
-                if (a.sh_head)
-                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, a.side, a, zb, a.zcap,
-                              n, off);
-                else
-                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, a.side, a, zb, a.zcap,
-                              n, off);
+                if ((e = mlp(a.side, zb, n, off)) != hipSuccess) return e;
                 if ((e = hipEventRecord(a.ev_mlp[k & 1], a.side)) != hipSuccess) return e;
             } else {
-                if (a.sh_head)
-                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, s, a, zb, a.zcap, n,
-                              off);
-                else
-                    IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, s, a, zb, a.zcap, n,
-                              off);
+                if ((e = mlp(s, zb, n, off)) != hipSuccess) return e;
             }
         }
         if (overlap) {

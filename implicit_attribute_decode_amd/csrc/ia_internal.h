@@ -33,6 +33,7 @@ class ProfScope {
     } while (0)
 
 constexpr int kMaxLevels = 32;
+constexpr int kMaxDecoderMats = 12;  // per-attribute decoder: 4 branches x 3 layers
 
 // Per-level geometry of the 4D hash encoder (SPIN-4DGS §3.3, Eq. 9).
 struct HashLevels {
@@ -56,7 +57,10 @@ struct DecodeArgs {
     int n_hidden;
     int hidden[4];
     int act;
-    int sh_head;       // 1: the head block is 56 rows with 48 SH coefficients as the colour
+    int sh_head;       // 1: the colour is 48 SH coefficients (head block of 56 rows, or a 48-row branch)
+    int branches;      // 1: per-attribute fp16 decoder (F = 4), weights in Wt / bpack
+    const void* Wt;    // branch weights in MFMA A-tile order (branch_tile_bytes)
+    const float* bpack;  // branch biases, packed (branch_bias_bytes)
     const float* pos;  // [N, stride]
     int stride;        // 3 (scalar t) or 4 (per-point t)
     float t_scalar;
@@ -77,6 +81,21 @@ struct DecodeArgs {
 constexpr int64_t kDecodeChunk = int64_t(1) << 22;
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
+
+// Per-attribute fp16 decoder (64 -> 64 -> 64 -> out per branch): bytes of the
+// tiled weights and packed biases, and the kernel that builds both from the
+// 12 row-major matrices / bias vectors (branch by branch: scale, rotation,
+// colour, opacity; three layers each).
+size_t branch_tile_bytes(bool sh);
+size_t branch_bias_bytes(bool sh);
+hipError_t launch_branch_pack(const _Float16* const* W, const float* const* b, bool sh, void* Wt, float* bpack,
+                              hipStream_t s);
+// F = 4 level-major gather of n Gaussians (xt) into z ([L][zstride] x 8 bytes).
+hipError_t launch_gather_f4(const float4* xt, int64_t n, const HashLevels& h, const void* tables, uint32_t* z,
+                            int64_t zstride, hipStream_t s);
+// Per-attribute MLPs and Eq. 11 for Gaussians [off, off + n) from z.
+hipError_t launch_mlp_branch(const DecodeArgs& a, const uint32_t* z, int64_t zstride, int64_t n, int64_t off,
+                             hipStream_t s);
 
 // fp16 path: normalise Gaussians [off, off + n) of a.pos into xt and gather
 // their features into z ([L][zstride] fp16 pairs), as the decode does.

@@ -24,6 +24,7 @@ IA_ERR_OUT_OF_MEMORY = -5
 IA_DTYPE_F32, IA_DTYPE_F16 = 0, 1
 IA_ACT_RELU, IA_ACT_GELU = 0, 1
 IA_COLOR_RGB, IA_COLOR_SH3 = 0, 1
+IA_BRANCHES_SHARED, IA_BRANCHES_PER_ATTRIBUTE = 0, 1
 
 # Every entry point include/ia.h declares.
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
@@ -46,7 +47,7 @@ class HashDesc(C.Structure):
 
 class MLPDesc(C.Structure):
     _fields_ = [("in_dim", C.c_int32), ("n_hidden", C.c_int32), ("hidden", C.c_int32 * 4),
-                ("activation", C.c_int32), ("dtype", C.c_int32), ("color", C.c_int32)]
+                ("activation", C.c_int32), ("dtype", C.c_int32), ("color", C.c_int32), ("branches", C.c_int32)]
 
 
 class Gaussians(C.Structure):

@@ -26,11 +26,13 @@ class Decoder:
         hd = ia.HashDesc(int(h.L), int(h.F), int(h.log2T), float(h.base_res), float(h.growth), int(h.temporal_res),
                          ia.IA_DTYPE_F16 if h.table_f16 else ia.IA_DTYPE_F32, float(h.t_min), float(h.t_max))
         hidden = list(m.dims[1:-1])
-        self.sh = int(m.dims[-1]) == 56  # SH colour head (48 coefficients)
+        self.sh = int(m.dims[-1]) == 56  # SH colour (48 coefficients)
+        branches = bool(getattr(m, "branches", False))
         md = ia.MLPDesc(int(m.dims[0]), len(hidden), (ia.C.c_int32 * 4)(*(hidden + [0] * (4 - len(hidden)))),
                         ia.IA_ACT_GELU if m.act == "gelu" else ia.IA_ACT_RELU,
                         ia.IA_DTYPE_F16 if f16 else ia.IA_DTYPE_F32,
-                        ia.IA_COLOR_SH3 if self.sh else ia.IA_COLOR_RGB)
+                        ia.IA_COLOR_SH3 if self.sh else ia.IA_COLOR_RGB,
+                        ia.IA_BRANCHES_PER_ATTRIBUTE if branches else ia.IA_BRANCHES_SHARED)
         self.handle = ia.ia_decoder_create(hd, md)
         self.device = device
         self._tables = _dev(params.tables, device=device)

@@ -42,9 +42,13 @@ class HashConfig:
 
 @dataclass
 class MLPConfig:
-    dims: list  # [in, hidden..., out]; the last layer is the 11-wide head block
+    dims: list  # [in, hidden..., out]; out = 11 (RGB) or 56 (SH colour), all attributes together
     act: str  # "relu" | "gelu"
     f16: bool
+    # False: one trunk and one head block (weights: one matrix per layer);
+    # True: one MLP in -> hidden... -> out_a per attribute (scale 3, rotation 4,
+    # colour 3 or 48, opacity 1), weights listed branch by branch
+    branches: bool = False
 
 
 @dataclass
@@ -190,6 +194,48 @@ def make_decoder(rng: np.random.Generator, hcfg: HashConfig, mcfg: MLPConfig,
         weights.append(w.astype(wdt))
         biases.append(b)
     return DecoderParams(hash=hcfg, mlp=mcfg, tables=tables, weights=weights, biases=biases)
+
+
+BRANCH_OUTS_RGB = (3, 4, 3, 1)
+BRANCH_OUTS_SH = (3, 4, 48, 1)
+
+
+def paper_hash() -> HashConfig:
+    """[SPIN] §4 implementation details: 16 levels of 4 features, 2^21 entries
+    per level (fp16: 256 MiB); resolutions and time axis as single_hash."""
+    return HashConfig(L=16, F=4, log2T=21, base_res=16, growth=1.5, temporal_res=150, table_f16=True)
+
+
+def paper_decoder(seed: int = 4, sh: bool = True) -> DecoderParams:
+    """Paper-scale decoder: one GELU MLP 64 -> 64 -> 64 -> out per attribute
+    ([SPIN] §3.3 Eq. 10, hidden width 64 from §4), reading z of the F = 4
+    encoder.  Last-layer biases per §3.3: scale -5, rotation (1,0,0,0),
+    opacity logit(0.1), colour 0; the SH rows are scaled by 0.5 as in
+    single_decoder_sh."""
+    rng = np.random.default_rng([seed, 104])
+    h = paper_hash()
+    T = 1 << h.log2T
+    tables = rng.uniform(-1.0, 1.0, size=(h.L, T, h.F)).astype(np.float16)
+    outs = BRANCH_OUTS_SH if sh else BRANCH_OUTS_RGB
+    weights, biases = [], []
+    for br, out in enumerate(outs):
+        for fan_in, fan_out in ((64, 64), (64, 64), (64, out)):
+            w = rng.standard_normal((fan_out, fan_in)) * math.sqrt(1.0 / fan_in)
+            b = np.zeros(fan_out, np.float32)
+            if fan_out == out:
+                if br == 0:
+                    w *= 2.0
+                    b[:] = -5.0
+                elif br == 1:
+                    b[0] = 1.0
+                elif br == 2 and sh:
+                    w *= 0.5
+                elif br == 3:
+                    b[0] = LOGIT_0_1
+            weights.append(w.astype(np.float16))
+            biases.append(b)
+    mcfg = MLPConfig(dims=[64, 64, 64, sum(outs)], act="gelu", f16=True, branches=True)
+    return DecoderParams(hash=h, mlp=mcfg, tables=tables, weights=weights, biases=biases)
 
 
 def tiny_hash() -> HashConfig:

@@ -59,6 +59,11 @@ typedef int32_t ia_status;
 #define IA_COLOR_SH3 1 /* 48 spherical-harmonic coefficients of degree 3, no
                           activation (the paper's colour decoder)              */
 
+/* Decoder layout ([SPIN] §3.3 Eq. 10) */
+#define IA_BRANCHES_SHARED 0        /* one trunk, one head block             */
+#define IA_BRANCHES_PER_ATTRIBUTE 1 /* one MLP per attribute (scale, rotation,
+                                       colour, opacity), all reading z       */
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 IA_API const char* ia_last_error(void);
 
@@ -87,7 +92,7 @@ typedef struct {
  * (ix*1 ^ iy*2654435761 ^ iz*805459861 ^ it*3674653429) mod 2^log2T. */
 typedef struct {
     int32_t L;            /* levels: 4 or 16 (in_dim = 2 L)                 */
-    int32_t F;            /* features per level: 2                          */
+    int32_t F;            /* features per level: 2, or 4 (fp16 tables)      */
     int32_t log2T;        /* table entries per level = 2^log2T, 4..24       */
     double base_res;      /* vertices per axis at level 0, >= 2             */
     double growth;        /* per-level growth factor, >= 1                  */
@@ -96,15 +101,24 @@ typedef struct {
     float t_min, t_max;   /* time normalisation of Eq. 8, t_max > t_min     */
 } ia_hash_desc;
 
-/* Decoder MLP ([SPIN] §3.3 Eq. 10): a shared trunk of n_hidden layers
- * act(W x + b) followed by one linear head block in the order
+/* Decoder MLP ([SPIN] §3.3 Eq. 10).  Outputs in the order
  * scale(3) | rotation(4: w,x,y,z) | colour | opacity(1), where colour is 3
  * RGB outputs (color = IA_COLOR_RGB: 11 outputs) or 48 SH coefficients,
- * coefficient-major [16][3] (IA_COLOR_SH3: 56 outputs).  Supported:
- *   dtype F32: (in_dim, hidden) = (8, {32}), (32, {64}) or (32, {64, 64}); RGB
- *   dtype F16: in_dim = 32, n_hidden = 2, hidden = {64, 64}, fp16 MFMA with
- *              fp32 accumulation; hidden activations rounded to fp16; RGB or
- *              SH3. */
+ * coefficient-major [16][3] (IA_COLOR_SH3: 56 outputs).
+ *   branches = IA_BRANCHES_SHARED: a trunk of n_hidden layers act(W x + b)
+ *     and one linear head block of all outputs; weights[k], biases[k] for
+ *     layer k (n_hidden + 1 layers).
+ *   branches = IA_BRANCHES_PER_ATTRIBUTE: four MLPs in -> hidden -> out_a
+ *     (out_a = 3, 4, 3 or 48, 1), each of n_hidden act layers and a linear
+ *     last layer; weights / biases hold 4 (n_hidden + 1) pointers, branch by
+ *     branch in the order scale, rotation, colour, opacity.
+ * Supported:
+ *   dtype F32: shared; (in_dim, hidden) = (8, {32}), (32, {64}) or
+ *              (32, {64, 64}); RGB
+ *   dtype F16: fp16 MFMA with fp32 accumulation, hidden activations rounded
+ *              to fp16; shared with in_dim = 32 (F = 2), hidden = {64, 64},
+ *              or per attribute with in_dim = 64 (F = 4), hidden = {64, 64};
+ *              RGB or SH3. */
 typedef struct {
     int32_t in_dim;
     int32_t n_hidden;
@@ -112,6 +126,7 @@ typedef struct {
     int32_t activation; /* IA_ACT_RELU or IA_ACT_GELU */
     int32_t dtype;      /* IA_DTYPE_F32 or IA_DTYPE_F16 (weights and math) */
     int32_t color;      /* IA_COLOR_RGB or IA_COLOR_SH3                    */
+    int32_t branches;   /* IA_BRANCHES_SHARED or IA_BRANCHES_PER_ATTRIBUTE */
 } ia_mlp_desc;
 
 typedef struct ia_decoder ia_decoder;
@@ -122,15 +137,17 @@ IA_API ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* 
 
 /* Copy the parameters into device memory owned by the handle.
  *   tables : [L][2^log2T][F] of table_dtype
- *   weights: n_hidden + 1 pointers, layer k row-major [out][in] of mlp dtype
- *            (the last one is the [11][hidden] head block)
- *   biases : n_hidden + 1 pointers to fp32 [out]
+ *   weights: layer matrices row-major [out][in] of mlp dtype: n_hidden + 1
+ *            (shared: the last one is the head block) or 4 (n_hidden + 1)
+ *            (per attribute, see ia_mlp_desc)
+ *   biases : fp32 [out], one per weight matrix
  * params_on_device: 1 if all the above are device pointers, 0 if host.
  * The copies are enqueued on `stream`; host sources may be freed on return
  * (host copies are synchronous).  For the fp16 decoder this call also
- * allocates the handle's feature scratch ((8 L + 16) x 2^22 bytes; decode
- * processes at most 2^22 Gaussians per gather/MLP kernel pair).  May be
- * called again to replace parameters (waits for the device first).
+ * allocates the handle's feature scratch ((4 L F + 16) x 2^22 bytes; decode
+ * processes at most 2^22 Gaussians per gather/MLP kernel pair) and 39 MB of
+ * backward partials.  May be called again to replace parameters (waits for
+ * the device first).
  * Errors: INVALID_ARG, OUT_OF_MEMORY, DEVICE. */
 IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
                                 const float* const* biases, int32_t params_on_device, void* stream);

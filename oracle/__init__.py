@@ -211,6 +211,16 @@ def decode(dec, pos: np.ndarray, t: float | None = None, mode: int = 0) -> dict:
     A head of 56 outputs is the SH colour decoder (returns sh [N,16,3]
     instead of colors)."""
     h, m = dec.hash, dec.mlp
+    if getattr(m, "branches", False):
+        # one MLP per attribute (scale, rotation, colour, opacity) on the same z
+        z = encode(h, dec.tables, normalize(h, pos, t))
+        sh = int(m.dims[-1]) == 56
+        outs = (3, 4, 48 if sh else 3, 1)
+        nl = len(m.dims) - 1
+        raw = np.concatenate([
+            mlp_forward(list(m.dims[:-1]) + [o], m.act, m.f16, dec.weights[b * nl:(b + 1) * nl],
+                        dec.biases[b * nl:(b + 1) * nl], z, mode) for b, o in enumerate(outs)], axis=1)
+        return dict(raw=raw, **(activate_sh(raw) if sh else activate(raw)))
     if int(m.dims[-1]) == 56:
         z = encode(h, dec.tables, normalize(h, pos, t))
         raw = mlp_forward(m.dims, m.act, m.f16, dec.weights, dec.biases, z, mode)

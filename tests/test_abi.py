@@ -47,11 +47,26 @@ def test_decoder_create_accepts_the_supported_shapes():
     tiny = ia.HashDesc(4, 2, 12, 8.0, 2.0, 0, ia.IA_DTYPE_F32, 0.0, 1.0)
     h = ia.ia_decoder_create(tiny, ia.MLPDesc(8, 1, (C.c_int32 * 4)(32, 0, 0, 0), ia.IA_ACT_RELU, ia.IA_DTYPE_F32))
     ia.ia_decoder_destroy(h)
+    h = ia.ia_decoder_create(_hash(), _mlp(color=ia.IA_COLOR_SH3))
+    ia.ia_decoder_destroy(h)
+    paper = _hash(F=4, log2T=21)
+    for color in (ia.IA_COLOR_RGB, ia.IA_COLOR_SH3):
+        h = ia.ia_decoder_create(paper, _mlp(in_dim=64, branches=ia.IA_BRANCHES_PER_ATTRIBUTE, color=color))
+        ia.ia_decoder_destroy(h)
+    with pytest.raises(ia.IAError) as e:  # the SH head needs the fp16 decoder
+        ia.ia_decoder_create(tiny, ia.MLPDesc(8, 1, (C.c_int32 * 4)(32, 0, 0, 0), ia.IA_ACT_RELU, ia.IA_DTYPE_F32,
+                                              ia.IA_COLOR_SH3))
+    assert e.value.status == ia.IA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("hkw,mkw,status", [
     (dict(L=0), {}, ia.IA_ERR_INVALID_ARG),
-    (dict(F=4), {}, ia.IA_ERR_UNSUPPORTED),
+    (dict(F=3), {}, ia.IA_ERR_UNSUPPORTED),
+    (dict(F=4), dict(in_dim=64), ia.IA_ERR_UNSUPPORTED),  # a shared trunk needs F = 2
+    (dict(F=4, table_dtype=ia.IA_DTYPE_F32), dict(in_dim=64, branches=1), ia.IA_ERR_UNSUPPORTED),
+    ({}, dict(branches=1), ia.IA_ERR_UNSUPPORTED),  # per-attribute branches need F = 4
+    ({}, dict(branches=2), ia.IA_ERR_INVALID_ARG),
+    ({}, dict(color=5), ia.IA_ERR_INVALID_ARG),
     (dict(log2T=30), {}, ia.IA_ERR_INVALID_ARG),
     (dict(base_res=1.0), {}, ia.IA_ERR_INVALID_ARG),
     (dict(t_max=0.0), {}, ia.IA_ERR_INVALID_ARG),

@@ -148,6 +148,30 @@ def test_sh_colour_head_ragged_xyzt(n):
     _check_f16_sh(g, O.decode(dec, pos, mode=0), O.decode(dec, pos, mode=1), f"sh xyzt n={n}")
 
 
+def test_paper_scale_decoder_full_frame():
+    """Paper-scale decoder (F = 4, 2^21-entry tables, one 64-64-64 GELU MLP
+    per attribute, SH colour) on a full Single frame."""
+    dec = S.paper_decoder()
+    pos, t = S.single_positions(2)
+    g = _gpu_decode(dec, pos, t)
+    _check_f16_sh(g, O.decode(dec, pos, t, mode=0), O.decode(dec, pos, t, mode=1), "paper")
+
+
+@pytest.mark.parametrize("n", [1, 63, 4097, 70001])
+def test_paper_scale_decoder_ragged_xyzt(n):
+    dec = S.paper_decoder()
+    pos = _edge_positions(np.random.default_rng(400 + n), n)
+    g = _gpu_decode(dec, pos)
+    _check_f16_sh(g, O.decode(dec, pos, mode=0), O.decode(dec, pos, mode=1), f"paper xyzt n={n}")
+
+
+def test_paper_scale_decoder_rgb_branches():
+    dec = S.paper_decoder(sh=False)
+    pos = _edge_positions(np.random.default_rng(401), 5000)
+    g = _gpu_decode(dec, pos)
+    _check_f16(g, O.decode(dec, pos, mode=0), O.decode(dec, pos, mode=1), "paper rgb")
+
+
 def test_decode_zero_is_noop():
     D = Decoder(S.tiny_decoder())
     out = D.decode(torch.empty((0, 3), device="cuda"), 0.5)

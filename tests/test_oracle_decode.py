@@ -307,6 +307,47 @@ def test_sh_decoder_shares_the_trunk():
         np.testing.assert_array_equal(a[k], b[k])
 
 
+def test_four_feature_levels_split_into_two_feature_tables():
+    """F = 4 encoding: the entry layout [level][T][F] means the first two
+    features of every entry form an F = 2 table with the same hashing, and so
+    do the last two: z4 = interleave(z2(first half), z2(second half))."""
+    h4 = S.HashConfig(L=6, F=4, log2T=12, base_res=8, growth=1.7, temporal_res=20, table_f16=True)
+    h2 = S.HashConfig(L=6, F=2, log2T=12, base_res=8, growth=1.7, temporal_res=20, table_f16=True)
+    rng = np.random.default_rng(11)
+    tab = rng.uniform(-1, 1, size=(6, 1 << 12, 4)).astype(np.float16)
+    xt = O.normalize(h4, np.concatenate([rng.normal(0, 2, (500, 3)), rng.random((500, 1))], 1).astype(np.float32))
+    z4 = O.encode(h4, tab, xt).reshape(500, 6, 4)
+    za = O.encode(h2, np.ascontiguousarray(tab[:, :, :2]), xt).reshape(500, 6, 2)
+    zb = O.encode(h2, np.ascontiguousarray(tab[:, :, 2:]), xt).reshape(500, 6, 2)
+    assert np.array_equal(z4[:, :, :2], za) and np.array_equal(z4[:, :, 2:], zb)
+
+
+def test_per_attribute_branches_against_numpy():
+    """Paper-scale decoder: each attribute's branch is its own GELU MLP on
+    the shared z (numpy, fp64), outputs concatenated scale | rotation | SH |
+    opacity, then Eq. 11."""
+    dec = S.paper_decoder()
+    pos, t = S.single_positions(2, 0.6, 100, 10)
+    out = O.decode(dec, pos, t, mode=0)
+    z = O.encode(dec.hash, dec.tables, O.normalize(dec.hash, pos, t))
+    gelu = lambda x: 0.5 * x * (1.0 + sps.erf(x / math.sqrt(2.0)))
+    raw = []
+    for br in range(4):
+        x = z
+        for k in range(3):
+            W = dec.weights[3 * br + k].astype(np.float64)
+            b = dec.biases[3 * br + k].astype(np.float64)
+            x = x @ W.T + b
+            if k < 2:
+                x = gelu(x)
+        raw.append(x)
+    raw = np.concatenate(raw, axis=1)
+    assert raw.shape[1] == 56
+    np.testing.assert_allclose(out["raw"], raw, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["sh"].reshape(-1, 48), raw[:, 7:55], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["opacity"], sps.expit(raw[:, 55]), rtol=1e-12)
+
+
 def test_rotation_head_scale_invariance():
     """Scaling the rotation head's weights and bias by k > 0 leaves r unchanged."""
     dec = S.tiny_decoder()
