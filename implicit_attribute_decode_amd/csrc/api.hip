@@ -205,8 +205,22 @@ ia::DecodeArgs decode_args(const ia_decoder* dec, const float* pos, int stride, 
     return a;
 }
 
+size_t feature_bytes(const ia_decoder* dec, int64_t N) {
+    return (size_t)(N > 0 ? N : 0) * (size_t)dec->hash.L * (size_t)dec->hash.F * 2;
+}
+
+// Checks a caller buffer for the decode's features (null allowed).
+ia_status check_features(const ia_decoder* dec, int64_t N, const void* features, size_t bytes) {
+    if (!features) return IA_OK;
+    if (dec->mlp.dtype != IA_DTYPE_F16) return fail(IA_ERR_UNSUPPORTED, "features are kept by the fp16 decoder only");
+    if (!aligned(features, 8)) return fail(IA_ERR_INVALID_ARG, "features must be 8-byte aligned");
+    if (bytes < feature_bytes(dec, N))
+        return fail(IA_ERR_INVALID_ARG, "features buffer too small: need " + std::to_string(feature_bytes(dec, N)) + " bytes");
+    return IA_OK;
+}
+
 ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, float t, int64_t N,
-                        const ia_gaussians* out, void* stream) {
+                        const ia_gaussians* out, void* stream, void* features = nullptr, size_t features_bytes = 0) {
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
     if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
@@ -215,7 +229,10 @@ ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, flo
     if (!outputs_ok(out, dec->mlp.color == IA_COLOR_SH3))
         return fail(IA_ERR_INVALID_ARG, "output scales/quats/colors (or sh)/opacity must be non-null");
     if (N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N too large");
+    ia_status fs = check_features(dec, N, features, features_bytes);
+    if (fs != IA_OK) return fs;
     ia::DecodeArgs a = decode_args(dec, pos, stride, t, N);
+    a.features = static_cast<uint32_t*>(features);
     a.scales = out->scales;
     a.quats = out->quats;
     a.colors = out->colors;
@@ -336,9 +353,25 @@ ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, co
     return decode_common(dec, xyzt, 4, 0.0f, N, out, stream);
 }
 
+ia_status ia_decode_feature_bytes(const ia_decoder* dec, int64_t N, size_t* bytes) {
+    if (!dec || !bytes) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    *bytes = feature_bytes(dec, N);
+    return IA_OK;
+}
+
+ia_status ia_decode_keep(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
+                         const ia_gaussians* out, void* features, size_t features_bytes, void* stream) {
+    if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
+    if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
+    if (!features && N > 0) return fail(IA_ERR_INVALID_ARG, "features is null");
+    return decode_common(dec, pos, pos_stride, t, N, out, stream, features, features_bytes);
+}
+
 ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
                              const ia_gaussians* grad_attr, const float* grad_means, float* grad_pos,
-                             const ia_decoder_grads* grads, void* stream) {
+                             const ia_decoder_grads* grads, const void* features, size_t features_bytes,
+                             void* stream) {
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
     if (dec->mlp.dtype != IA_DTYPE_F16 || dec->mlp.color != IA_COLOR_RGB || dec->mlp.branches != IA_BRANCHES_SHARED)
@@ -354,8 +387,11 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
         if (!outputs_ok(grad_attr, false))
             return fail(IA_ERR_INVALID_ARG, "grad_attr scales/quats/colors/opacity must be non-null");
     }
+    ia_status fs = check_features(dec, N, features, features_bytes);
+    if (fs != IA_OK) return fs;
     ia::DecodeBwdArgs b{};
     b.fwd = decode_args(dec, pos, pos_stride, t, N);
+    b.fwd.features = const_cast<uint32_t*>(static_cast<const uint32_t*>(features));
     if (N > 0) {
         b.g_scales = grad_attr->scales;
         b.g_quats = grad_attr->quats;

@@ -481,6 +481,7 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
     const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
     IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
               a.pos + off * a.stride, n, xt);
+    if (!z) return hipGetLastError();  // features kept by the forward: normalisation only
     IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n, nchunk,
               a.h, (const uint32_t*)a.tables, z, zstride);
     return hipGetLastError();
@@ -495,14 +496,17 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         // the feature scratch is double-buffered and events order the hand-offs.
         const size_t zslot = (size_t)a.h.L * a.zcap * (a.h.F / 2);  // 32-bit words per scratch slot
         float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
+        // features go to the caller's buffer ([L][N], kept for a backward) or to the
+        // double-buffered scratch ([L][zcap] per slot)
+        const int64_t zstride = a.features ? a.N : a.zcap;
         auto mlp = [&](hipStream_t st, const uint32_t* zb, int64_t n, int64_t off) -> hipError_t {
-            if (a.branches) return launch_mlp_branch(a, zb, a.zcap, n, off, st);
+            if (a.branches) return launch_mlp_branch(a, zb, zstride, n, off, st);
             // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
             const int grid = grid_for(256, n, 256 * 8);
             if (a.sh_head)
-                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, st, a, zb, a.zcap, n, off);
+                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, st, a, zb, zstride, n, off);
             else
-                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, st, a, zb, a.zcap, n,
+                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, st, a, zb, zstride, n,
                           off);
             return hipGetLastError();
         };
@@ -511,16 +515,16 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         for (int64_t off = 0; off < a.N; off += a.zcap, ++k) {
             const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
             const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
-            uint32_t* zb = a.zbuf + (size_t)(k & 1) * zslot;
+            uint32_t* zb = a.features ? a.features + (size_t)off * (a.h.F / 2) : a.zbuf + (size_t)(k & 1) * zslot;
             hipError_t e;
             if (overlap && k >= 2 && (e = hipStreamWaitEvent(s, a.ev_mlp[k & 1], 0)) != hipSuccess) return e;
             IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
                       a.pos + off * a.stride, n, xt);
             if (a.h.F == 4) {
-                if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, a.zcap, s)) != hipSuccess) return e;
+                if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, zstride, s)) != hipSuccess) return e;
             } else {
                 IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
-                          n, nchunk, a.h, (const uint32_t*)a.tables, zb, a.zcap);
+                          n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
             }
             if (overlap) {
                 if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;

@@ -95,7 +95,8 @@ struct MlpBwdArgs {
     const float* gq;
     const float* gc;
     const float* go;
-    float2* gz;      // [L][zstride]
+    float2* gz;      // [L][gzstride]
+    int64_t gzstride;
     float* partial;  // [waves][kTileSlots + kBiasSlots][64]
     int first;       // 1: the partial slots start from zero
 };
@@ -389,8 +390,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
                 for (int e = 0; e < 4; ++e) G = mfma4(sW1[((ob * 4 + rb) * 4 + e) * 64 + lane], E[rb][e], G);
             if (valid) {
                 const int lv = 8 * ob + 2 * q;
-                a.gz[(size_t)lv * a.zstride + gl] = make_float2(G[0], G[1]);
-                a.gz[(size_t)(lv + 1) * a.zstride + gl] = make_float2(G[2], G[3]);
+                a.gz[(size_t)lv * a.gzstride + gl] = make_float2(G[0], G[1]);
+                a.gz[(size_t)(lv + 1) * a.gzstride + gl] = make_float2(G[2], G[3]);
             }
         }
     }
@@ -615,8 +616,7 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         m.b[k] = a.b[k];
     }
     m.gelu = a.act == IA_ACT_GELU;
-    m.z = z;
-    m.zstride = chunk;
+    m.gzstride = chunk;
     m.gs = b.g_scales;
     m.gq = b.g_quats;
     m.gc = b.g_colors;
@@ -626,8 +626,11 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     int first = 1;
     for (int64_t off = 0; off < a.N; off += chunk) {
         const int64_t n = a.N - off < chunk ? a.N - off : chunk;
-        hipError_t e = launch_decode_features(a, off, n, xt, z, chunk, s);
+        // features kept by the forward ([L][N]) or recomputed into the scratch ([L][chunk])
+        hipError_t e = launch_decode_features(a, off, n, xt, a.features ? nullptr : z, chunk, s);
         if (e != hipSuccess) return e;
+        m.z = a.features ? a.features + off : z;
+        m.zstride = a.features ? a.N : chunk;
         m.n = n;
         m.off = off;
         m.first = first;

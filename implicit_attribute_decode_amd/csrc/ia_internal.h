@@ -71,6 +71,7 @@ struct DecodeArgs {
     float* sh;  // [N][48] for the SH head
     float* opacity;
     uint32_t* zbuf;  // fp16 path: feature scratch [2][L][zcap] (packed fp16 pairs), then [zcap] float4
+    uint32_t* features;  // fp16 path, or null: caller buffer [L][N] of packed fp16 features (F / 2 words each)
     int64_t zcap;    // Gaussians per chunk the scratch holds
     hipStream_t side;         // fp16 path: stream the MLP of one chunk overlaps the next gather on (or null)
     hipEvent_t ev_gather[2];  // per scratch slot: gather done
@@ -98,7 +99,8 @@ hipError_t launch_mlp_branch(const DecodeArgs& a, const uint32_t* z, int64_t zst
                              hipStream_t s);
 
 // fp16 path: normalise Gaussians [off, off + n) of a.pos into xt and gather
-// their features into z ([L][zstride] fp16 pairs), as the decode does.
+// their features into z ([L][zstride] fp16 pairs), as the decode does; with z
+// null, normalise only.
 hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, float4* xt, uint32_t* z,
                                   int64_t zstride, hipStream_t s);
 

@@ -28,7 +28,7 @@ IA_BRANCHES_SHARED, IA_BRANCHES_PER_ATTRIBUTE = 0, 1
 
 # Every entry point include/ia.h declares.
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
-           "ia_decoder_destroy", "ia_decode_backward", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
+           "ia_decoder_destroy", "ia_decode_backward", "ia_decode_feature_bytes", "ia_decode_keep", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
            "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render", "ia_render_set_binning",
            "ia_render_backward", "ia_l1_loss", "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
 
@@ -102,7 +102,9 @@ def load(path: str = LIB_PATH):
         L.ia_decode.argtypes = [P, P, C.c_int64, C.c_float, P, P]
         L.ia_decode_xyzt.argtypes = [P, P, C.c_int64, P, P]
         L.ia_decoder_destroy.argtypes = [P]
-        L.ia_decode_backward.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, P]
+        L.ia_decode_backward.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, P, C.c_size_t, P]
+        L.ia_decode_feature_bytes.argtypes = [P, C.c_int64, P]
+        L.ia_decode_keep.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, C.c_size_t, P]
         L.ia_decoder_destroy.restype = None
         L.ia_hexplane_create.argtypes = [P, P]
         L.ia_hexplane_set_params.argtypes = [P, P, P, P, C.c_int32, P]
@@ -177,9 +179,22 @@ def ia_decode_xyzt(dec, xyzt, N: int, out: Gaussians, stream=None):
 
 
 def ia_decode_backward(dec, pos, pos_stride: int, N: int, t: float, grad_attr: Gaussians, grad_means, grad_pos,
-                       grads: DecoderGrads, stream=None):
+                       grads: DecoderGrads, features=None, stream=None):
+    fb = 0 if features is None else int(features.numel() * features.element_size())
     _check(load().ia_decode_backward(dec, _ptr(pos), int(pos_stride), int(N), float(t), C.byref(grad_attr),
-                                     _ptr(grad_means), _ptr(grad_pos), C.byref(grads), _stream(stream)))
+                                     _ptr(grad_means), _ptr(grad_pos), C.byref(grads), _ptr(features), fb,
+                                     _stream(stream)))
+
+
+def ia_decode_feature_bytes(dec, N: int) -> int:
+    b = C.c_size_t()
+    _check(load().ia_decode_feature_bytes(dec, int(N), C.byref(b)))
+    return int(b.value)
+
+
+def ia_decode_keep(dec, pos, pos_stride: int, N: int, t: float, out: Gaussians, features, stream=None):
+    _check(load().ia_decode_keep(dec, _ptr(pos), int(pos_stride), int(N), float(t), C.byref(out), _ptr(features),
+                                 int(features.numel() * features.element_size()), _stream(stream)))
 
 
 def ia_decoder_destroy(dec):

@@ -69,8 +69,20 @@ class Decoder:
         ia.ia_decode_xyzt(self.handle, xyzt, N, self._gaussians(out))
         return out
 
+    def decode_keep(self, pos: torch.Tensor, t: float | None = None, out: dict | None = None,
+                    features: torch.Tensor | None = None):
+        """Decode pos ([N,3] at time t, or [N,4] xyzt) and keep the encoding
+        for backward(..., features=...).  Returns (attributes, features)."""
+        N, stride = int(pos.shape[0]), int(pos.shape[1])
+        out = self._out(N, out)
+        nbytes = ia.ia_decode_feature_bytes(self.handle, N)
+        if features is None or features.numel() * features.element_size() < nbytes:
+            features = torch.empty(max(nbytes, 8) // 8, dtype=torch.int64, device=self.device)
+        ia.ia_decode_keep(self.handle, pos, stride, N, float(t or 0.0), self._gaussians(out), features)
+        return out, features
+
     def backward(self, pos: torch.Tensor, grad_attr: dict, t: float | None = None, grad_means=None,
-                 want_pos: bool = True) -> dict:
+                 want_pos: bool = True, features: torch.Tensor | None = None) -> dict:
         """Gradients of the decode of pos ([N,3] at time t, or [N,4] xyzt)
         for upstream dL/d{scales, quats, colors, opacity}.  Returns tables
         [L,T,F], weights and biases (lists, fp32, shaped like the parameters)
@@ -85,7 +97,7 @@ class Decoder:
                             (ia.C.c_void_p * 4)(*[ia._ptr(b) for b in out["biases"]]))
         up = ia.gaussians(scales=grad_attr["scales"], quats=grad_attr["quats"], colors=grad_attr["colors"],
                           opacity=grad_attr["opacity"])
-        ia.ia_decode_backward(self.handle, pos, stride, N, float(t or 0.0), up, grad_means, out["pos"], G)
+        ia.ia_decode_backward(self.handle, pos, stride, N, float(t or 0.0), up, grad_means, out["pos"], G, features)
         return out
 
     def __del__(self):

@@ -169,6 +169,19 @@ IA_API ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, f
 IA_API ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
                          void* stream);
 
+/* Bytes of the encoding z of N Gaussians (N x L x F fp16) that
+ * ia_decode_keep stores and ia_decode_backward can reuse. */
+IA_API ia_status ia_decode_feature_bytes(const ia_decoder* dec, int64_t N, size_t* bytes);
+
+/* As ia_decode (pos_stride 3, time t) or ia_decode_xyzt (pos_stride 4), and
+ * keep the hash encoding z of every Gaussian in `features` (device,
+ * caller-owned, >= ia_decode_feature_bytes, 8-byte aligned; layout
+ * [L][N] x F fp16) for a later ia_decode_backward of the same positions,
+ * which then skips recomputing it.  fp16 decoders only.
+ * Errors: INVALID_ARG, UNSUPPORTED, DEVICE. */
+IA_API ia_status ia_decode_keep(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
+                                const ia_gaussians* out, void* features, size_t features_bytes, void* stream);
+
 /* Gradients of the decoder parameters (device, fp32, overwritten). */
 typedef struct {
     float* tables;     /* [L][2^log2T][F], whatever the table dtype          */
@@ -190,6 +203,8 @@ typedef struct {
  *              w_c dL/dz over the 16 corners of each level, float atomics,
  *              so the last bits vary from run to run), weight and bias
  *              gradients (summed in a fixed order: deterministic).
+ *   features:  the encoding kept by ia_decode_keep for the same positions, or
+ *              NULL (then recomputed).
  * The forward is recomputed exactly as the decode computes it (fp16 hidden
  * activations); the backward runs in fp32 (v_mfma_f32_16x16x4_f32), treating
  * the fp16 roundings as the identity.  Uses the handle's scratch: calls on
@@ -197,7 +212,8 @@ typedef struct {
  * Errors: INVALID_ARG, UNSUPPORTED (fp32 decoders), DEVICE. */
 IA_API ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
                                     const ia_gaussians* grad_attr, const float* grad_means, float* grad_pos,
-                                    const ia_decoder_grads* grads, void* stream);
+                                    const ia_decoder_grads* grads, const void* features, size_t features_bytes,
+                                    void* stream);
 
 IA_API void ia_decoder_destroy(ia_decoder* dec);
 

@@ -171,6 +171,34 @@ def test_decode_backward_two_chunks_is_the_sum_of_its_parts():
     assert (err <= 2e-3 * nrm + 1e-4 * nrm.max()).all()
 
 
+@pytest.mark.parametrize("n", [5000, (1 << 22) + 1000])
+def test_kept_features_match_recomputation(n):
+    """ia_decode_keep gives the same attributes as ia_decode_xyzt (bit for
+    bit) and a backward that reuses the kept encoding gives the same
+    gradients as one that recomputes it (weights and biases bit for bit,
+    the float-atomic table and position sums to rounding); 2^22 + 1000
+    points span two forward chunks and three backward chunks."""
+    dec = S.single_decoder()
+    rng = np.random.default_rng(65)
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    D = Decoder(dec)
+    x = cuda(pos)
+    plain = D.decode_xyzt(x)
+    kept, feats = D.decode_keep(x)
+    torch.cuda.synchronize()
+    for k in plain:
+        assert torch.equal(plain[k], kept[k]), k
+    g = {k: cuda(v.astype(np.float32)) for k, v in up.items()}
+    a = D.backward(x, g)
+    b = D.backward(x, g, features=feats)
+    torch.cuda.synchronize()
+    for l in range(3):
+        assert torch.equal(a["weights"][l], b["weights"][l]) and torch.equal(a["biases"][l], b["biases"][l])
+    _close("kept tables", host(b["tables"]).reshape(-1), host(a["tables"]).reshape(-1), 1e-5, 1e-6)
+    _close("kept pos", host(b["pos"]), host(a["pos"]), 1e-5, 1e-6)
+
+
 def test_decode_backward_zero_points_and_errors():
     dec = S.single_decoder()
     D = Decoder(dec)
