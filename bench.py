@@ -209,10 +209,17 @@ def _stress(S, Decoder, Renderer, stream) -> dict:
     bwd_kernels = profiled(render_train, 1)
     ms_db = timed(lambda: D.backward(xyzt, ga, grad_means=ga["means"], features=feats), 2, stream)
     dbwd_kernels = profiled(lambda: D.backward(xyzt, ga, grad_means=ga["means"], features=feats), 1)
+    # the same decoder backward with a non-zero gradient on every Gaussian (the L1 step above
+    # leaves most of the 8M without one): every corner of every level is a float atomic
+    dense = {k: torch.randn(v.shape, generator=gen, device="cuda") * 1e-6 for k, v in dk.items()}
+    D.backward(xyzt, dense, features=feats)
+    ms_dense = timed(lambda: D.backward(xyzt, dense, features=feats), 1, stream)
+    nz = int((ga["opacity"] != 0).sum().item())
     return {"frames": len(cams), "gaussians": g.n, "tile_entries": E, "render_ms": round(ms_r, 3),
             "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3),
             "decode_keep_8M_ms": round(ms_dk, 3), "render_fwd_l1_bwd_ms": round(ms_rt, 3),
             "decode_bwd_8M_ms": round(ms_db, 3), "train_step_ms": round(ms_dk + ms_rt + ms_db, 3),
+            "gaussians_with_gradient": nz, "decode_bwd_8M_all_nonzero_ms": round(ms_dense, 3),
             "render_kernels_ms": stress_kernels, "render_train_kernels_ms": bwd_kernels,
             "decode_bwd_kernels_ms": dbwd_kernels}
 

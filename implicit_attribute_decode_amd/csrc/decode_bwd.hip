@@ -2,9 +2,13 @@
 // gradients of the decoded attributes: gradients of the hash tables, of every
 // decoder weight and bias, and of the positions.
 //
-// Per chunk of at most kBwdChunk Gaussians:
-//   features   the forward's normalise + level-major gather kernels recompute
-//              the encoding z (fp16, as the forward fed the MLP).
+// Per chunk of at most 2^21 Gaussians:
+//   features   the encoding z kept by the forward decode, or recomputed by the
+//              forward's normalise + level-major gather kernels (fp16, as the
+//              forward fed the MLP); x~ is renormalised either way.
+//   compaction the Gaussians whose upstream gradient is not all zero, in
+//              index order (the others have exactly zero decoder gradients);
+//              the two kernels below work on that list only.
 //   mlp_bwd_kernel  one wave per 16 Gaussians at a time (persistent grid):
 //       forward  the decoder on v_mfma_f32_16x16x32_f16 exactly as the decode
 //                runs it (same operands, same fp16 roundings), keeping the
@@ -89,7 +93,8 @@ struct MlpBwdArgs {
     int gelu;
     const uint32_t* z;  // [L][zstride] fp16 pairs
     int64_t zstride;
-    int64_t n;    // Gaussians in this chunk
+    const uint32_t* list;   // chunk-local indices of the Gaussians with a non-zero upstream gradient
+    const uint32_t* count;  // how many (device)
     int64_t off;  // index of the chunk's first Gaussian in the upstream gradients
     const float* gs;
     const float* gq;
@@ -183,10 +188,11 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
     const bool gelu = a.gelu != 0;
     float* sG = sT[wv][0];
     float* sH = sT[wv][1];
-    for (int64_t base = wave * 16; base < a.n; base += nwaves * 16) {
-        const int64_t gl = base + c;
-        const bool valid = gl < a.n;
-        const int64_t gi = valid ? gl : a.n - 1;
+    const int64_t n = *a.count;
+    for (int64_t base = wave * 16; base < n; base += nwaves * 16) {
+        const int64_t kc = base + c;  // compact index
+        const bool valid = kc < n;
+        const int64_t gi = a.list[valid ? kc : n - 1];  // chunk-local Gaussian
         // ---------------- forward (as the decode computes it)
         const int l0 = 2 * q;
         const half8_t Z = cat8(unpack2(a.z[(size_t)l0 * a.zstride + gi], a.z[(size_t)(l0 + 1) * a.zstride + gi]),
@@ -239,7 +245,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         // q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
         float up[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (valid) {
-            const int64_t u = a.off + gl;
+            const int64_t u = a.off + gi;
             if (q == 0) {
                 up[0] = a.gs[u * 3 + 0];
                 up[1] = a.gs[u * 3 + 1];
@@ -390,8 +396,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
                 for (int e = 0; e < 4; ++e) G = mfma4(sW1[((ob * 4 + rb) * 4 + e) * 64 + lane], E[rb][e], G);
             if (valid) {
                 const int lv = 8 * ob + 2 * q;
-                a.gz[(size_t)lv * a.gzstride + gl] = make_float2(G[0], G[1]);
-                a.gz[(size_t)(lv + 1) * a.gzstride + gl] = make_float2(G[2], G[3]);
+                a.gz[(size_t)lv * a.gzstride + kc] = make_float2(G[0], G[1]);
+                a.gz[(size_t)(lv + 1) * a.gzstride + kc] = make_float2(G[2], G[3]);
             }
         }
     }
@@ -479,12 +485,15 @@ __global__ void __launch_bounds__(256) mlp_bwd_reduce_kernel(const float* partia
 // Eq. 9 and Eq. 7 backward, level-major as the gather.  Lane s of a group of
 // four takes the x/y corner (s & 1, s >> 1) and its four z/t corners.
 template <bool POS>
-__global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const float* pos, int stride, int64_t n,
-                                                      int nchunk, HashLevels h, const uint32_t* tables,
-                                                      const float2* gz, int64_t zstride, float* gtab, float* gpos) {
+__global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const float* pos, int stride,
+                                                      const uint32_t* list, const uint32_t* count, int nchunk,
+                                                      HashLevels h, const uint32_t* tables, const float2* gz,
+                                                      int64_t zstride, float* gtab, float* gpos) {
 #pragma clang fp contract(fast)
     const int level = blockIdx.x / nchunk;
     const int64_t first = (int64_t)(blockIdx.x % nchunk) * 256;
+    const int64_t n = *count;  // Gaussians with a gradient, compacted
+    if (first >= n) return;
     const int res = h.res_s[level], res_t = h.res_t[level];
     const bool dense = h.dense[level] != 0;
     const uint32_t* tab = tables + (size_t)level * h.T;
@@ -494,10 +503,11 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
     const int sub = threadIdx.x >> 2;
     const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
     for (int j = 0; j < 4; ++j) {
-        const int64_t i = first + j * 64 + sub;
-        if (i >= n) break;  // uniform across each group of four lanes
+        const int64_t k = first + j * 64 + sub;  // compact index
+        if (k >= n) break;  // uniform across each group of four lanes
+        const int64_t i = list[k];  // chunk-local Gaussian
         const float4 p = xt[i];
-        const float2 g = gz[(size_t)level * zstride + i];
+        const float2 g = gz[(size_t)level * zstride + k];
         int cx, cy, cz, ct;
         float fx, fy, fz, ft;
         cell_axis(p.x, res, cx, fx);
@@ -523,7 +533,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
         const float sx = bx ? 1.0f : -1.0f, sy = by ? 1.0f : -1.0f;
         const float wxy = wx * wy;
         const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
-        const bool any = g.x != 0.0f || g.y != 0.0f;
+        // no gradient at this level: nothing to add, no position term (uniform over the four lanes)
+        if (g.x == 0.0f && g.y == 0.0f) continue;
         float dx = 0.0f, dy = 0.0f, dz = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -532,7 +543,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
             if (wt[bt] == 0.0f) continue;
             const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
             const float w = (wxy * wz[bz]) * wt[bt];
-            if (any && w != 0.0f) {
+            if (w != 0.0f) {
                 atomicAdd(gt + 2 * (size_t)idx, w * g.x);
                 atomicAdd(gt + 2 * (size_t)idx + 1, w * g.y);
             }
@@ -583,6 +594,88 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
     }
 }
 
+// Compaction of the chunk's Gaussians whose upstream gradient is not all zero
+// (their decoder gradients are exactly zero otherwise), in index order:
+// per-block counts, one exclusive scan, ordered writes.
+constexpr int kCompactItems = 4096;  // per block: 256 threads x 16 rounds
+
+__device__ __forceinline__ bool has_gradient(const float* gs, const float* gq, const float* gc, const float* go,
+                                             int64_t u) {
+    bool nz = go[u] != 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) nz = nz || gs[u * 3 + k] != 0.0f || gc[u * 3 + k] != 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) nz = nz || gq[u * 4 + k] != 0.0f;
+    return nz;
+}
+
+__global__ void __launch_bounds__(256) active_count_kernel(const float* gs, const float* gq, const float* gc,
+                                                           const float* go, int64_t off, int64_t n, uint32_t* bcount) {
+    __shared__ uint32_t s_cnt[4];
+    const int64_t b0 = (int64_t)blockIdx.x * kCompactItems;
+    uint32_t cnt = 0;
+    for (int r = 0; r < kCompactItems / 256; ++r) {
+        const int64_t i = b0 + r * 256 + threadIdx.x;
+        if (i < n && has_gradient(gs, gq, gc, go, off + i)) ++cnt;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) bcount[blockIdx.x] = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+}
+
+// Exclusive scan of nb <= 256 * 8 block counts in place; total into *count.
+__global__ void __launch_bounds__(256) active_scan_kernel(uint32_t* bcount, int nb, uint32_t* count) {
+    __shared__ uint32_t s_sum[256];
+    constexpr int kPer = 8;
+    uint32_t v[kPer], run = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x * kPer + k;
+        v[k] = i < nb ? bcount[i] : 0u;
+        run += v[k];
+    }
+    s_sum[threadIdx.x] = run;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const uint32_t add = threadIdx.x >= (unsigned)o ? s_sum[threadIdx.x - o] : 0u;
+        __syncthreads();
+        s_sum[threadIdx.x] += add;
+        __syncthreads();
+    }
+    uint32_t base = s_sum[threadIdx.x] - run;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x * kPer + k;
+        if (i < nb) bcount[i] = base;
+        base += v[k];
+    }
+    if (threadIdx.x == 255) *count = s_sum[255];
+}
+
+__global__ void __launch_bounds__(256) active_write_kernel(const float* gs, const float* gq, const float* gc,
+                                                           const float* go, int64_t off, int64_t n,
+                                                           const uint32_t* boff, uint32_t* list) {
+    __shared__ uint32_t s_w[4];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t b0 = (int64_t)blockIdx.x * kCompactItems;
+    uint32_t pos = boff[blockIdx.x];
+    for (int r = 0; r < kCompactItems / 256; ++r) {
+        const int64_t i = b0 + r * 256 + threadIdx.x;
+        const bool f = i < n && has_gradient(gs, gq, gc, go, off + i);
+        const uint64_t m = __ballot(f);
+        if (lane == 0) s_w[wv] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t before = 0;
+        for (int w = 0; w < wv; ++w) before += s_w[w];
+        const uint32_t rank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+        if (f) list[pos + before + rank] = (uint32_t)i;
+        pos += s_w[0] + s_w[1] + s_w[2] + s_w[3];
+        __syncthreads();
+    }
+}
+
 __global__ void fill_kernel(float* p, int64_t n, const float* src) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = src ? src[i] : 0.0f;
@@ -610,6 +703,11 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
     uint32_t* z = a.zbuf;
     float2* gz = reinterpret_cast<float2*>(a.zbuf + (size_t)a.h.L * chunk);
+    // after z and dz: the compacted list of a chunk, per-block offsets and the count
+    uint32_t* list = a.zbuf + (size_t)3 * a.h.L * chunk;
+    uint32_t* boff = list + chunk;
+    const int nbc = (int)(chunk / kCompactItems);
+    uint32_t* count = boff + nbc;
     MlpBwdArgs m{};
     for (int k = 0; k < 3; ++k) {
         m.W[k] = (const _Float16*)a.W[k];
@@ -631,7 +729,14 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         if (e != hipSuccess) return e;
         m.z = a.features ? a.features + off : z;
         m.zstride = a.features ? a.N : chunk;
-        m.n = n;
+        const int nb = (int)((n + kCompactItems - 1) / kCompactItems);
+        IA_LAUNCH("active_count_kernel", active_count_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
+                  b.g_colors, b.g_opacity, off, n, boff);
+        IA_LAUNCH("active_scan_kernel", active_scan_kernel, dim3(1), dim3(256), 0, s, boff, nb, count);
+        IA_LAUNCH("active_write_kernel", active_write_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
+                  b.g_colors, b.g_opacity, off, n, boff, list);
+        m.list = list;
+        m.count = count;
         m.off = off;
         m.first = first;
         first = 0;
@@ -640,11 +745,11 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         const float* pos = a.pos + off * a.stride;
         if (b.g_pos)
             IA_LAUNCH("scatter_kernel", scatter_kernel<true>, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
-                      pos, a.stride, n, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
+                      pos, a.stride, list, count, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
                       b.g_pos + off * 3);
         else
             IA_LAUNCH("scatter_kernel", scatter_kernel<false>, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
-                      pos, a.stride, n, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
+                      pos, a.stride, list, count, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
                       (float*)nullptr);
     }
     if (first) {  // N = 0: the weight and bias gradients are zero

@@ -171,6 +171,34 @@ def test_decode_backward_two_chunks_is_the_sum_of_its_parts():
     assert (err <= 2e-3 * nrm + 1e-4 * nrm.max()).all()
 
 
+def test_decode_backward_sparse_upstream_gradients():
+    """Most Gaussians without any upstream gradient (as after a render
+    backward where only the front layers composite), some with a single
+    non-zero component: the decoder backward works on the compacted list of
+    the others and must equal the oracle on the whole set."""
+    dec = S.single_decoder()
+    rng = np.random.default_rng(66)
+    n = 30000
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    idle = rng.random(n) < 0.8
+    for v in up.values():
+        v[idle] = 0.0
+    one = np.flatnonzero(~idle)[:500]  # a single non-zero component each
+    for k, v in up.items():
+        v[one] = 0.0
+    for j, i in enumerate(one):
+        key = ("scales", "quats", "colors", "opacity")[j % 4]
+        if key == "opacity":
+            up[key][i] = 1.5
+        else:
+            up[key][i, j % up[key].shape[1]] = 1.5
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare("sparse", dec, out, ref)
+    assert np.all(host(out["pos"])[idle] == 0.0)
+
+
 @pytest.mark.parametrize("n", [5000, (1 << 22) + 1000])
 def test_kept_features_match_recomputation(n):
     """ia_decode_keep gives the same attributes as ia_decode_xyzt (bit for
