@@ -126,7 +126,8 @@ def _single(S, Decoder, R, stream) -> dict:
 def _paper(S, Decoder, R, stream) -> dict:
     """Paper-scale decoder (F = 4, 2^21-entry tables, one GELU MLP per
     attribute, SH colour): one Single frame decoded and rendered with SH, and
-    the decode alone of 20 sequence frames (4M (x,y,z,t) positions)."""
+    the decode alone of 20 sequence frames (4M (x,y,z,t) positions), also
+    with 2^23-entry tables."""
     import torch
 
     D = Decoder(S.paper_decoder())
@@ -143,8 +144,15 @@ def _paper(S, Decoder, R, stream) -> dict:
     ms_d = timed(lambda: D.decode_xyzt(xyzt, out=d), 5, stream)
     kern = profiled(lambda: D.decode_xyzt(xyzt, out=d), 1)
     n = int(xyzt.shape[0])
+    del D
+    # the 2^23-entry tables (1 GiB of fp16)
+    D23 = Decoder(S.paper_decoder(log2T=23))
+    d23 = D23.decode_xyzt(xyzt)
+    ms_23 = timed(lambda: D23.decode_xyzt(xyzt, out=d23), 5, stream)
+    kern23 = profiled(lambda: D23.decode_xyzt(xyzt, out=d23), 1)
     return {"single_frame_ms": round(ms, 4), "single_frame_fps": round(1e3 / ms, 1), "decode_gaussians": n,
             "decode_ms": round(ms_d, 4), "decode_gaussians_per_s": round(n / (ms_d / 1e3)), "decode_kernels_ms": kern,
+            "decode_2p23_ms": round(ms_23, 4), "decode_2p23_kernels_ms": kern23,
             "mlp_flop_per_gaussian": PAPER_FLOP_PER_GAUSSIAN}
 
 

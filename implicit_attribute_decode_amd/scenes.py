@@ -200,22 +200,25 @@ BRANCH_OUTS_RGB = (3, 4, 3, 1)
 BRANCH_OUTS_SH = (3, 4, 48, 1)
 
 
-def paper_hash() -> HashConfig:
+def paper_hash(log2T: int = 21) -> HashConfig:
     """[SPIN] §4 implementation details: 16 levels of 4 features, 2^21 entries
-    per level (fp16: 256 MiB); resolutions and time axis as single_hash."""
-    return HashConfig(L=16, F=4, log2T=21, base_res=16, growth=1.5, temporal_res=150, table_f16=True)
+    per level (fp16: 256 MiB; 2^23: 1 GiB); resolutions and time axis as
+    single_hash."""
+    return HashConfig(L=16, F=4, log2T=log2T, base_res=16, growth=1.5, temporal_res=150, table_f16=True)
 
 
-def paper_decoder(seed: int = 4, sh: bool = True) -> DecoderParams:
+def paper_decoder(seed: int = 4, sh: bool = True, log2T: int = 21) -> DecoderParams:
     """Paper-scale decoder: one GELU MLP 64 -> 64 -> 64 -> out per attribute
     ([SPIN] §3.3 Eq. 10, hidden width 64 from §4), reading z of the F = 4
     encoder.  Last-layer biases per §3.3: scale -5, rotation (1,0,0,0),
     opacity logit(0.1), colour 0; the SH rows are scaled by 0.5 as in
     single_decoder_sh."""
     rng = np.random.default_rng([seed, 104])
-    h = paper_hash()
+    h = paper_hash(log2T)
     T = 1 << h.log2T
-    tables = rng.uniform(-1.0, 1.0, size=(h.L, T, h.F)).astype(np.float16)
+    tables = np.empty((h.L, T, h.F), np.float16)
+    for l in range(h.L):  # level by level (bounded host memory for 2^23)
+        tables[l] = rng.uniform(-1.0, 1.0, size=(T, h.F)).astype(np.float16)
     outs = BRANCH_OUTS_SH if sh else BRANCH_OUTS_RGB
     weights, biases = [], []
     for br, out in enumerate(outs):

@@ -165,6 +165,14 @@ def test_paper_scale_decoder_ragged_xyzt(n):
     _check_f16_sh(g, O.decode(dec, pos, mode=0), O.decode(dec, pos, mode=1), f"paper xyzt n={n}")
 
 
+def test_paper_scale_decoder_2p23_tables():
+    """The 2^23-entry variant (1 GiB of fp16 tables, beyond the Infinity Cache)."""
+    dec = S.paper_decoder(log2T=23)
+    pos = _edge_positions(np.random.default_rng(402), 20000)
+    g = _gpu_decode(dec, pos)
+    _check_f16_sh(g, O.decode(dec, pos, mode=0), O.decode(dec, pos, mode=1), "paper 2^23")
+
+
 def test_paper_scale_decoder_rgb_branches():
     dec = S.paper_decoder(sh=False)
     pos = _edge_positions(np.random.default_rng(401), 5000)
