@@ -291,13 +291,11 @@ __global__ void __launch_bounds__(256) gather_f16_kernel(const float4* xt, int64
 }
 
 // Bias + activation of one 16x16 D tile (rows 16 rb + 4 q + e), rounded to fp16.
-__device__ __forceinline__ half4_t act_tile(floatx4 acc, const float* bias, bool gelu) {
+template <bool GELU>
+__device__ __forceinline__ half4_t act_tile(floatx4 acc, const float* bias) {
     half4_t h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float v = acc[e] + bias[e];
-        h[e] = (_Float16)(gelu ? gelu_fp16path(v) : (v > 0.0f ? v : 0.0f));
-    }
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)hidden_act<GELU>(acc[e] + bias[e]);
     return h;
 }
 
@@ -346,7 +344,7 @@ __device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (
 // the next layer, and the features of levels {2q, 2q+1, 8+2q, 9+2q} the lane
 // loads are exactly its B slots of layer 1.  SH: the head block has 56 rows
 // (four 16-row tiles) with the 48 SH coefficients in place of the RGB rows.
-template <bool SH>
+template <bool SH, bool GELU>
 __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, const uint32_t* zbuf,
                                                                   int64_t zstride, int64_t n, int64_t out_off) {
     constexpr int NH = SH ? 4 : 1, kHeadRows = SH ? 56 : 11;
@@ -382,7 +380,6 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
         }
     }
 
-    const bool gelu = a.act == IA_ACT_GELU;
     // features of the next 64 Gaussians are loaded while this tile computes
     auto load_z = [&](int64_t b0, half8_t (&Zo)[4]) {
 #pragma unroll
@@ -410,7 +407,7 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
                 floatx4 z0 = {0, 0, 0, 0};
                 const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z[g], z0, 0, 0, 0);
                 const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z[g], z0, 0, 0, 0);
-                H1[m][g] = cat8(act_tile(lo, B1[2 * m], gelu), act_tile(hi, B1[2 * m + 1], gelu));
+                H1[m][g] = cat8(act_tile<GELU>(lo, B1[2 * m]), act_tile<GELU>(hi, B1[2 * m + 1]));
             }
         // ---- trunk layer 2: 64 -> 64
         half8_t H2[2][4];
@@ -424,7 +421,7 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
                     lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m][k], H1[k][g], lo, 0, 0, 0);
                     hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m + 1][k], H1[k][g], hi, 0, 0, 0);
                 }
-                H2[m][g] = cat8(act_tile(lo, B2[2 * m], gelu), act_tile(hi, B2[2 * m + 1], gelu));
+                H2[m][g] = cat8(act_tile<GELU>(lo, B2[2 * m]), act_tile<GELU>(hi, B2[2 * m + 1]));
             }
         // ---- head block 64 -> 11 (rows 11..15 are zero) and Eq. 11
 #pragma unroll
@@ -503,11 +500,10 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             if (a.branches) return launch_mlp_branch(a, zb, zstride, n, off, st);
             // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
             const int grid = grid_for(256, n, 256 * 8);
-            if (a.sh_head)
-                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<true>, dim3(grid), dim3(256), 0, st, a, zb, zstride, n, off);
-            else
-                IA_LAUNCH("mlp_f16_kernel", mlp_f16_kernel<false>, dim3(grid), dim3(256), 0, st, a, zb, zstride, n,
-                          off);
+            const bool gelu = a.act == IA_ACT_GELU;
+            auto k = a.sh_head ? (gelu ? mlp_f16_kernel<true, true> : mlp_f16_kernel<true, false>)
+                               : (gelu ? mlp_f16_kernel<false, true> : mlp_f16_kernel<false, false>);
+            IA_LAUNCH("mlp_f16_kernel", k, dim3(grid), dim3(256), 0, st, a, zb, zstride, n, off);
             return hipGetLastError();
         };
         const bool overlap = a.side != nullptr && a.N > a.zcap;

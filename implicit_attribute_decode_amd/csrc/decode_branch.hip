@@ -107,17 +107,28 @@ __global__ void __launch_bounds__(256) gather_f4_kernel(const float4* xt, int64_
     const int bx = s & 1, by = s >> 1;
     const int sub = threadIdx.x >> 2;
     const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
-#pragma unroll 2
+    // Every corner load of the four passes is issued before any is used; a
+    // skipped corner or a lane past the end reads past the table (zero, no
+    // memory request), as in the F = 2 gather.
+    const __amdgpu_buffer_rsrc_t rt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tab, (short)0, (int)(h.T * 8u), kBufferWord3);
+    float4 P[4];
+#pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t i = first + j * 64 + sub;
-        if (i >= n) break;  // uniform across each group of four lanes
-        const float4 p = xt[i];
+        P[j] = xt[i < n ? i : n - 1];
+    }
+    uint2 raw[4][4];
+    float wc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool valid = first + j * 64 + sub < n;
         int cx, cy, cz, ct;
         float fx, fy, fz, ft;
-        cell_axis(p.x, res, cx, fx);
-        cell_axis(p.y, res, cy, fy);
-        cell_axis(p.z, res, cz, fz);
-        cell_axis(p.w, res_t, ct, ft);
+        cell_axis(P[j].x, res, cx, fx);
+        cell_axis(P[j].y, res, cy, fy);
+        cell_axis(P[j].z, res, cz, fz);
+        cell_axis(P[j].w, res_t, ct, ft);
         const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
         uint32_t txy, tz[2], tt[2];
         if (dense) {
@@ -135,26 +146,38 @@ __global__ void __launch_bounds__(256) gather_f4_kernel(const float4* xt, int64_
         }
         const float wxy = (bx ? fx : 1.0f - fx) * (by ? fy : 1.0f - fy);
         const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int bz = k & 1, bt = k >> 1;
             const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
-            const float w = (wxy * wz[bz]) * wt[bt];
-            if (w != 0.0f) {  // a corner of zero weight adds exactly zero: not fetched
-                const uint2 raw = tab[idx];
-                acc[0] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x & 0xffffu));
-                acc[1] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x >> 16));
-                acc[2] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y & 0xffffu));
-                acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y >> 16));
-            }
+            wc[j][k] = (wxy * wz[bz]) * wt[bt];
+            // a corner of zero weight adds exactly zero: not fetched
+            const uint32_t off = (valid && wc[j][k] != 0.0f) ? idx * 8u : kBufferNone;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rt, off, 0, 0);
+            raw[j][k] = make_uint2(v[0], v[1]);
         }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float w = wc[j][k];
+            acc[0] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][k].x & 0xffffu));
+            acc[1] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][k].x >> 16));
+            acc[2] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][k].y & 0xffffu));
+            acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][k].y >> 16));
+        }
+        // sums over the four lanes of the (Gaussian, level): xor 1, then xor 2
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            acc[f] += __shfl_xor(acc[f], 1, 4);
-            acc[f] += __shfl_xor(acc[f], 2, 4);
+            acc[f] += __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc[f]), 0xB1, 0xF, 0xF, true));
+            acc[f] += __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, acc[f]), 0x4E, 0xF, 0xF, true));
         }
-        if (s == 0) {
+        const int64_t i = first + j * 64 + sub;
+        if (s == 0 && i < n) {
             uint2 o;
             o.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[0]) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[1]) << 16);
@@ -168,13 +191,11 @@ __global__ void __launch_bounds__(256) gather_f4_kernel(const float4* xt, int64_
 __device__ __forceinline__ half4_t unpack4(uint2 v) { return unpack2(v.x, v.y); }
 
 // Bias + activation of one 16-row D tile, rounded to fp16 (rows 16 rb + 4 q + e).
-__device__ __forceinline__ half4_t act4(floatx4 acc, const float* bias, bool gelu) {
+template <bool GELU>
+__device__ __forceinline__ half4_t act4(floatx4 acc, const float* bias) {
     half4_t h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float v = acc[e] + bias[e];
-        h[e] = (_Float16)(gelu ? gelu_fp16path(v) : (v > 0.0f ? v : 0.0f));
-    }
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)hidden_act<GELU>(acc[e] + bias[e]);
     return h;
 }
 
@@ -182,8 +203,9 @@ __device__ __forceinline__ float sigmoid_b(float x) { return 1.0f / (1.0f + expf
 
 // One hidden layer (64 -> 64) of a branch for kBrG column groups: the output
 // k-block mo collects row blocks 2 mo and 2 mo + 1.
+template <bool GELU>
 __device__ __forceinline__ void hidden_layer(const half8_t* W, const float* bias, const half8_t (&X)[2][kBrG],
-                                             half8_t (&Y)[2][kBrG], int lane, int q, bool gelu) {
+                                             half8_t (&Y)[2][kBrG], int lane, int q) {
 #pragma unroll
     for (int mo = 0; mo < 2; ++mo) {
         floatx4 lo[kBrG], hi[kBrG];
@@ -201,24 +223,24 @@ __device__ __forceinline__ void hidden_layer(const half8_t* W, const float* bias
         }
 #pragma unroll
         for (int g = 0; g < kBrG; ++g)
-            Y[mo][g] = cat8(act4(lo[g], bias + 16 * (2 * mo) + 4 * q, gelu), act4(hi[g], bias + 16 * (2 * mo + 1) + 4 * q, gelu));
+            Y[mo][g] = cat8(act4<GELU>(lo[g], bias + 16 * (2 * mo) + 4 * q), act4<GELU>(hi[g], bias + 16 * (2 * mo + 1) + 4 * q));
     }
 }
 
 // One branch for kBrG column groups: two hidden layers, the output layer and
 // its part of Eq. 11.  The scheduling barriers keep the compiler from
 // interleaving branches (their live ranges would not fit the register file).
-template <int BR, bool SH>
+template <int BR, bool SH, bool GELU>
 __device__ __forceinline__ void run_branch(const DecodeArgs& a, const half8_t* s_w, const float* s_b,
                                            const half8_t (&Z)[2][kBrG], int64_t base, int64_t n, int64_t out_off,
-                                           int lane, int q, int c, bool gelu) {
+                                           int lane, int q, int c) {
     __builtin_amdgcn_sched_barrier(0);
     const half8_t* W = s_w + branch_tile_off(BR, SH) * kTile;
     const float* bias = s_b + branch_bias_off(BR, SH);
     half8_t H1[2][kBrG], H2[2][kBrG];
-    hidden_layer(W, bias, Z, H1, lane, q, gelu);
+    hidden_layer<GELU>(W, bias, Z, H1, lane, q);
     __builtin_amdgcn_sched_barrier(0);
-    hidden_layer(W + 8 * kTile, bias + 64, H1, H2, lane, q, gelu);
+    hidden_layer<GELU>(W + 8 * kTile, bias + 64, H1, H2, lane, q);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < branch_rb(BR, SH); ++rb) {
@@ -261,7 +283,7 @@ __device__ __forceinline__ void run_branch(const DecodeArgs& a, const half8_t* s
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool SH>
+template <bool SH, bool GELU>
 __global__ void __launch_bounds__(256, 2) mlp_branch_kernel(DecodeArgs a, const uint2* z, int64_t zstride, int64_t n,
                                                             int64_t out_off) {
     constexpr int kT = total_tiles(SH), kB = total_bias(SH);
@@ -275,7 +297,6 @@ __global__ void __launch_bounds__(256, 2) mlp_branch_kernel(DecodeArgs a, const 
     const int q = lane >> 4, c = lane & 15;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
-    const bool gelu = a.act == IA_ACT_GELU;
     for (int64_t base = wave * 16 * kBrG; base < n; base += nwaves * 16 * kBrG) {
         half8_t Z[2][kBrG];
 #pragma unroll
@@ -287,10 +308,10 @@ __global__ void __launch_bounds__(256, 2) mlp_branch_kernel(DecodeArgs a, const 
                 Z[m][g] = cat8(unpack4(z[(size_t)(8 * m + q) * zstride + gi]),
                                unpack4(z[(size_t)(8 * m + 4 + q) * zstride + gi]));
         }
-        run_branch<0, SH>(a, s_w, s_b, Z, base, n, out_off, lane, q, c, gelu);
-        run_branch<1, SH>(a, s_w, s_b, Z, base, n, out_off, lane, q, c, gelu);
-        run_branch<2, SH>(a, s_w, s_b, Z, base, n, out_off, lane, q, c, gelu);
-        run_branch<3, SH>(a, s_w, s_b, Z, base, n, out_off, lane, q, c, gelu);
+        run_branch<0, SH, GELU>(a, s_w, s_b, Z, base, n, out_off, lane, q, c);
+        run_branch<1, SH, GELU>(a, s_w, s_b, Z, base, n, out_off, lane, q, c);
+        run_branch<2, SH, GELU>(a, s_w, s_b, Z, base, n, out_off, lane, q, c);
+        run_branch<3, SH, GELU>(a, s_w, s_b, Z, base, n, out_off, lane, q, c);
     }
 }
 
@@ -327,12 +348,10 @@ hipError_t launch_mlp_branch(const DecodeArgs& a, const uint32_t* z, int64_t zst
                              hipStream_t s) {
     // 4 waves x 64 Gaussians per block; the weights fill most of the LDS: two blocks per CU
     const int grid = grid_cap(n, 256, 256 * 2);
-    if (a.sh_head)
-        IA_LAUNCH("mlp_branch_kernel", mlp_branch_kernel<true>, dim3(grid), dim3(256), 0, s, a, (const uint2*)z,
-                  zstride, n, off);
-    else
-        IA_LAUNCH("mlp_branch_kernel", mlp_branch_kernel<false>, dim3(grid), dim3(256), 0, s, a, (const uint2*)z,
-                  zstride, n, off);
+    const bool gelu = a.act == IA_ACT_GELU;
+    auto k = a.sh_head ? (gelu ? mlp_branch_kernel<true, true> : mlp_branch_kernel<true, false>)
+                       : (gelu ? mlp_branch_kernel<false, true> : mlp_branch_kernel<false, false>);
+    IA_LAUNCH("mlp_branch_kernel", k, dim3(grid), dim3(256), 0, s, a, (const uint2*)z, zstride, n, off);
     return hipGetLastError();
 }
 

@@ -64,25 +64,21 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// GELU of the fp16 path (the same operations as gelu_fp16path, so the value
-// is bit-identical) and its derivative Phi(x) + x phi(x), which reuses the
-// erf polynomial and exp(-x^2 / 2).  ReLU when gelu is false.
-__device__ __forceinline__ float act_fwd_grad(bool gelu, float x, float& d) {
-    if (!gelu) {
+// The hidden activation of the fp16 path (GELU computed exactly as
+// gelu_fp16path, so the value is bit-identical to the forward's; ReLU
+// otherwise) and its derivative; GELU' = Phi(x) + x phi(x) reuses the tail
+// Q = 1 - Phi(|x|) and exp(-x^2 / 2).
+template <bool GELU>
+__device__ __forceinline__ float act_fwd_grad(float x, float& d) {
+    if constexpr (!GELU) {
         d = x > 0.0f ? 1.0f : 0.0f;
         return x > 0.0f ? x : 0.0f;
+    } else {
+        float e;
+        const float q = gelu_tail(x, e);
+        d = fmaf(x * e, 0.39894228040143268f, x >= 0.0f ? 1.0f - q : q);
+        return fmaf(-fabsf(x), q, fmaxf(x, 0.0f));
     }
-    const float u = fabsf(x) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
-    const float e = __expf(-(u * u));
-    const float erf_u = fmaf(-(poly * t), e, 1.0f);
-    const float one_erf = 1.0f + copysignf(erf_u, x);
-    d = fmaf(x * e, 0.39894228040143268f, 0.5f * one_erf);  // e = exp(-x^2 / 2)
-    return 0.5f * x * one_erf;
 }
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
@@ -106,6 +102,7 @@ struct MlpBwdArgs {
     int first;       // 1: the partial slots start from zero
 };
 
+template <bool GELU>
 __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma clang fp contract(fast)
     // fp32 operands of the data-gradient products, lane-ordered:
@@ -185,7 +182,6 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
             for (int e = 0; e < 4; ++e) gb1[t][e] = a.first ? 0.0f : part[64 * j++];
     }
 
-    const bool gelu = a.gelu != 0;
     float* sG = sT[wv][0];
     float* sH = sT[wv][1];
     const int64_t n = *a.count;
@@ -208,8 +204,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float d0, d1;
-                h[e] = (_Float16)act_fwd_grad(gelu, P1[2 * m][e] + B1[2 * m][e], d0);
-                h[4 + e] = (_Float16)act_fwd_grad(gelu, P1[2 * m + 1][e] + B1[2 * m + 1][e], d1);
+                h[e] = (_Float16)act_fwd_grad<GELU>(P1[2 * m][e] + B1[2 * m][e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad<GELU>(P1[2 * m + 1][e] + B1[2 * m + 1][e], d1);
                 P1[2 * m][e] = d0;  // from here on: act'(a1)
                 P1[2 * m + 1][e] = d1;
             }
@@ -227,8 +223,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float d0, d1;
-                h[e] = (_Float16)act_fwd_grad(gelu, lo[e] + B2[2 * m][e], d0);
-                h[4 + e] = (_Float16)act_fwd_grad(gelu, hi[e] + B2[2 * m + 1][e], d1);
+                h[e] = (_Float16)act_fwd_grad<GELU>(lo[e] + B2[2 * m][e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad<GELU>(hi[e] + B2[2 * m + 1][e], d1);
                 P2[2 * m][e] = d0;  // act'(a2)
                 P2[2 * m + 1][e] = d1;
             }
@@ -601,12 +597,14 @@ constexpr int kCompactItems = 4096;  // per block: 256 threads x 16 rounds
 
 __device__ __forceinline__ bool has_gradient(const float* gs, const float* gq, const float* gc, const float* go,
                                              int64_t u) {
-    bool nz = go[u] != 0.0f;
+    // all eleven values are loaded (no short circuit, so the loads overlap);
+    // a value counts unless it is +0 or -0 (NaN counts)
+    uint32_t bits = __float_as_uint(go[u]);
 #pragma unroll
-    for (int k = 0; k < 3; ++k) nz = nz || gs[u * 3 + k] != 0.0f || gc[u * 3 + k] != 0.0f;
+    for (int k = 0; k < 3; ++k) bits |= __float_as_uint(gs[u * 3 + k]) | __float_as_uint(gc[u * 3 + k]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) nz = nz || gq[u * 4 + k] != 0.0f;
-    return nz;
+    for (int k = 0; k < 4; ++k) bits |= __float_as_uint(gq[u * 4 + k]);
+    return (bits & 0x7fffffffu) != 0u;
 }
 
 __global__ void __launch_bounds__(256) active_count_kernel(const float* gs, const float* gq, const float* gc,
@@ -740,7 +738,8 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         m.off = off;
         m.first = first;
         first = 0;
-        IA_LAUNCH("mlp_bwd_kernel", mlp_bwd_kernel, dim3(kDecodeBwdBlocks), dim3(kBwdThreads), 0, s, m);
+        IA_LAUNCH("mlp_bwd_kernel", m.gelu ? mlp_bwd_kernel<true> : mlp_bwd_kernel<false>, dim3(kDecodeBwdBlocks),
+                  dim3(kBwdThreads), 0, s, m);
         const int nchunk = (int)((n + 255) / 256);
         const float* pos = a.pos + off * a.stride;
         if (b.g_pos)

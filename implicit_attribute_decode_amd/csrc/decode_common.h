@@ -39,6 +39,12 @@ __device__ __forceinline__ void normalize_pos(float x, float y, float z, float t
     xt[3] = tn;
 }
 
+// Buffer resources (raw, stride 0, range-checked in bytes): word 3 of the
+// descriptor for untyped 32-bit loads on this architecture, and an offset past
+// any table, whose loads return zero and touch no memory.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr uint32_t kBufferNone = 0x80000000u;
+
 // Per-axis cell: p = x*(res-1), i = clamp(floor p, 0, res-2), f = p - i.
 __device__ __forceinline__ void cell_axis(float x, int res, int& i, float& f) {
     float p = x * (float)(res - 1);
@@ -51,20 +57,40 @@ __device__ __forceinline__ void cell_axis(float x, int res, int& i, float& f) {
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 // GELU for the fp16 path, whose hidden activations are rounded to fp16
-// (relative step 2^-11) right after: erf from Abramowitz & Stegun, Handbook
-// of Mathematical Functions, formula 7.1.26, |error| <= 1.5e-7:
-//   erf(u) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2),
-//   t = 1 / (1 + p u), u >= 0, erf odd.
+// (relative step 2^-11) right after.  GELU(x) = x Phi(x) = max(x, 0) - |x| Q
+// with Q = 1 - Phi(|x|) = erfc(u) / 2, u = |x| / sqrt 2, and erfc from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (|error of erf| <= 1.5e-7):
+//   erfc(u) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2), t = 1 / (1 + p u).
+// The coefficients below are a_i / 2, so the polynomial gives Q directly.  With
+// w = |x| sqrt(log2(e) / 2), exp(-u^2) = 2^(-w^2) and p u = p' w, p' = p /
+// (sqrt 2 sqrt(log2(e) / 2)).  Writing the negative half as -|x| Q (instead
+// of x (1 - erf)) avoids the cancellation 1 - erf(u) for large |x|.
+// gelu_tail returns Q and sets e = exp(-x^2 / 2).
+__device__ __forceinline__ float gelu_tail(float x, float& e) {
+    const float w = fabsf(x) * 0.84932180028801907f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.27273748087922250f, w, 1.0f));
+    float p = fmaf(t, 0.5307027145f, -0.7265760135f);
+    p = fmaf(t, p, 0.7107068705f);
+    p = fmaf(t, p, -0.142248368f);
+    p = fmaf(t, p, 0.127414796f);
+    e = __builtin_amdgcn_exp2f(-(w * w));
+    return (p * t) * e;
+}
+
 __device__ __forceinline__ float gelu_fp16path(float x) {
-    const float u = fabsf(x) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
-    const float e = __expf(-(u * u));
-    const float erf_u = fmaf(-(poly * t), e, 1.0f);
-    return 0.5f * x * (1.0f + copysignf(erf_u, x));
+    float e;
+    const float q = gelu_tail(x, e);
+    return fmaf(-fabsf(x), q, fmaxf(x, 0.0f));
+}
+
+// The hidden activation of the fp16 path: GELU (erf form) or ReLU.
+template <bool GELU>
+__device__ __forceinline__ float hidden_act(float v) {
+    if constexpr (GELU)
+        return gelu_fp16path(v);
+    else
+        return v > 0.0f ? v : 0.0f;
 }
 
 __device__ __forceinline__ half4_t load_h4(const _Float16* p) {

@@ -31,6 +31,8 @@
 // rounded), which makes tile rects and depth keys reproducible bit for bit.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ia_internal.h"
 #include "raster_common.h"
 
@@ -603,24 +605,34 @@ __device__ __forceinline__ void sort_chunk(const SortPass& p, uint32_t& begin, u
 
 template <int MAXB>
 __global__ void __launch_bounds__(kBlock) sort_upsweep_kernel(SortPass p) {
-    __shared__ uint32_t hist[4 << MAXB];  // per-wave histograms, [4][nb] flat
+    // per-wave histograms, [4][nb] flat, and one spare slot that counts the
+    // lanes past the end of the chunk
+    __shared__ uint32_t hist[(4 << MAXB) + 1];
     const int w = threadIdx.x >> 6;
     const int nb = 1 << p.bits;
     const uint32_t mask = (uint32_t)nb - 1u;
-    for (int k = threadIdx.x; k < 4 * nb; k += kBlock) hist[k] = 0;
+    for (int k = threadIdx.x; k <= 4 * nb; k += kBlock) hist[k] = 0;
     __syncthreads();
     uint32_t begin, end;
     sort_chunk(p, begin, end);
     for (uint32_t tile = begin; tile < end; tile += kSortTile) {
-        uint32_t d[kSortItems];
+        // all 16 loads are issued before the first count: the index is
+        // clamped (tile < end) and every lane counts, the ones past the end
+        // in the spare slot
+        uint32_t slot[kSortItems];
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             const uint32_t idx = tile + j * kBlock + threadIdx.x;
-            d[j] = idx < end ? (uint32_t)(p.in[idx] >> p.shift) & mask : 0xffffffffu;
+            const uint64_t v = p.in[idx < end ? idx : end - 1];
+            const uint32_t d = (uint32_t)(v >> p.shift) & mask;
+            // past the end: pushed to the spare slot by arithmetic, not by a
+            // select on the loaded value (which the compiler would turn into
+            // a branch around the load)
+            const uint32_t past = idx < end ? 0u : 0x7fffffffu;
+            slot[j] = min(w * nb + d + past, (uint32_t)(4 * nb));
         }
 #pragma unroll
-        for (int j = 0; j < kSortItems; ++j)
-            if (d[j] <= mask) atomicAdd(&hist[w * nb + d[j]], 1u);
+        for (int j = 0; j < kSortItems; ++j) atomicAdd(&hist[slot[j]], 1u);
     }
     __syncthreads();
     for (int d = threadIdx.x; d < nb; d += kBlock)
@@ -651,32 +663,37 @@ __global__ void __launch_bounds__(kBlock) sort_scan_kernel(SortPass p) {
 // leave as one contiguous run instead of one scattered word per lane.
 // MAXB: the largest digit width the instance handles (sizes its LDS).  The
 // next tile's keys are loaded while the current one is ranked and written.
+// Thread t owns digits [t kDPT, (t + 1) kDPT): it keeps their global
+// destinations in registers and, per tile, turns the per-wave counts into
+// tile-local starts (s_wc) and destination offsets (s_off = global
+// destination - tile-local start), so placing an item in the tile and
+// writing it out take one LDS lookup each.
 template <int MAXB>
-__global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
+__global__ void __launch_bounds__(kBlock, 3) sort_downsweep_kernel(SortPass p) {
     constexpr int kNB = 1 << MAXB;
-    constexpr int kDigitsPerThread = kNB > kBlock ? kNB / kBlock : 1;
+    constexpr int kDPT = kNB > kBlock ? kNB / kBlock : 1;  // digits per thread
     __shared__ uint64_t s_stage[kSortTile];
-    __shared__ uint32_t s_base[kNB];  // global destination of the digit's next item
-    __shared__ uint32_t s_ts[kNB];    // tile-local start of the digit
-    __shared__ uint4 s_wc4[kNB];      // per-wave counters, [4][nb] flat
+    __shared__ uint32_t s_off[kNB];
+    __shared__ uint4 s_wc4[kNB];  // per-wave counters, [4][nb] flat
     uint32_t* s_wc = reinterpret_cast<uint32_t*>(s_wc4);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int nb = 1 << p.bits;
     const uint32_t mask = (uint32_t)nb - 1u;
-    const int d0 = threadIdx.x * kDigitsPerThread;  // digits [d0, d0 + kDigitsPerThread) of this thread
+    const int d0 = threadIdx.x * kDPT;
+    uint32_t base[kDPT];  // global destination of the next item of each owned digit
     {
-        // digit base = exclusive scan of digit totals + this block's offset
-        uint32_t v[kDigitsPerThread], sum = 0;
+        // exclusive scan of the digit totals + this block's offset within the digit
+        uint32_t v[kDPT], sum = 0;
 #pragma unroll
-        for (int k = 0; k < kDigitsPerThread; ++k) {
+        for (int k = 0; k < kDPT; ++k) {
             v[k] = d0 + k < nb ? p.digit_tot[d0 + k] : 0u;
             sum += v[k];
         }
         uint32_t total;
         uint32_t run = block_excl_scan<uint32_t>(sum, total);
 #pragma unroll
-        for (int k = 0; k < kDigitsPerThread; ++k) {
-            if (d0 + k < nb) s_base[d0 + k] = run + p.counts[(d0 + k) * p.nblocks + blockIdx.x];
+        for (int k = 0; k < kDPT; ++k) {
+            base[k] = d0 + k < nb ? run + p.counts[(d0 + k) * p.nblocks + blockIdx.x] : 0u;
             run += v[k];
         }
     }
@@ -684,33 +701,24 @@ __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
     sort_chunk(p, begin, end);
     const uint64_t end_all = p.count[0] < p.cap ? p.count[0] : p.cap;  // bound on every destination
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint32_t prev_tc[kDigitsPerThread];  // previous tile's count of each of this thread's digits
-#pragma unroll
-    for (int k = 0; k < kDigitsPerThread; ++k) prev_tc[k] = 0;
-    uint64_t key[kSortItems];
-#pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
-        const uint32_t idx = begin + w * (64 * kSortItems) + j * 64 + lane;
-        key[j] = idx < end ? p.in[idx] : 0ull;
-    }
     for (uint32_t tile = begin; tile < end; tile += kSortTile) {
-        // next tile's keys, in flight during this tile
-        uint64_t nkey[kSortItems];
-        const uint32_t ntile = tile + kSortTile;
+        uint64_t key[kSortItems];
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
-            const uint32_t idx = ntile + w * (64 * kSortItems) + j * 64 + lane;
-            nkey[j] = (ntile < end && idx < end) ? p.in[idx] : 0ull;
+            // clamped so that every load is issued unconditionally (tile < end)
+            const uint32_t idx = tile + w * (64 * kSortItems) + j * 64 + lane;
+            key[j] = p.in[idx < end ? idx : end - 1];
         }
         for (int k = threadIdx.x; k < nb; k += kBlock) s_wc4[k] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
-        uint32_t dig[kSortItems], rank[kSortItems];
+        // digit << 16 | rank within the wave's items of that digit (rank < 4096);
+        // digit 0xffff marks an item past the end
+        uint32_t dr[kSortItems];
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
             const uint32_t idx = tile + w * (64 * kSortItems) + j * 64 + lane;
             const bool valid = idx < end;
             const uint32_t d = (uint32_t)(key[j] >> p.shift) & mask;
-            dig[j] = valid ? d : 0xffffffffu;
             uint64_t peers = __ballot(valid);
             for (int bit = 0; bit < p.bits; ++bit) {
                 const uint64_t b = __ballot((d >> bit) & 1u);
@@ -721,41 +729,41 @@ __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
             const uint32_t below = (uint32_t)__popcll(peers & lt_mask);
             // the lowest lane of each peer group advances the wave's counter
             if (valid && below == 0) s_wc[w * nb + d] = prior + (uint32_t)__popcll(peers);
-            rank[j] = prior + below;
+            dr[j] = ((valid ? d : 0xffffu) << 16) | (prior + below);
         }
         __syncthreads();
-        // per digit: advance the global base past the previous tile, offsets
-        // of each wave inside the digit, and the digit's start inside the tile
+        // per owned digit: the tile-local start of each wave's items (tile
+        // start + counts of the waves before), and the destination offset
         {
-            uint32_t tc[kDigitsPerThread], sum = 0;
+            uint32_t c[kDPT][4], tc[kDPT], sum = 0;
 #pragma unroll
-            for (int k = 0; k < kDigitsPerThread; ++k) {
+            for (int k = 0; k < kDPT; ++k) {
                 const int d = d0 + k;
-                tc[k] = 0;
-                if (d < nb) {
-                    const uint32_t c0 = s_wc[d], c1 = s_wc[nb + d], c2 = s_wc[2 * nb + d], c3 = s_wc[3 * nb + d];
-                    s_wc[d] = 0;
-                    s_wc[nb + d] = c0;
-                    s_wc[2 * nb + d] = c0 + c1;
-                    s_wc[3 * nb + d] = c0 + c1 + c2;
-                    s_base[d] += prev_tc[k];
-                    tc[k] = c0 + c1 + c2 + c3;
-                }
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) c[k][ww] = d < nb ? s_wc[ww * nb + d] : 0u;
+                tc[k] = c[k][0] + c[k][1] + c[k][2] + c[k][3];
                 sum += tc[k];
             }
             uint32_t total;
             uint32_t run = block_excl_scan<uint32_t>(sum, total);
 #pragma unroll
-            for (int k = 0; k < kDigitsPerThread; ++k) {
-                if (d0 + k < nb) s_ts[d0 + k] = run;
+            for (int k = 0; k < kDPT; ++k) {
+                const int d = d0 + k;
+                if (d < nb) {
+                    s_wc[d] = run;
+                    s_wc[nb + d] = run + c[k][0];
+                    s_wc[2 * nb + d] = run + c[k][0] + c[k][1];
+                    s_wc[3 * nb + d] = run + c[k][0] + c[k][1] + c[k][2];
+                    s_off[d] = base[k] - run;
+                    base[k] += tc[k];
+                }
                 run += tc[k];
-                prev_tc[k] = tc[k];
             }
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j)
-            if (dig[j] <= mask) s_stage[s_ts[dig[j]] + s_wc[w * nb + dig[j]] + rank[j]] = key[j];
+            if ((dr[j] >> 16) <= mask) s_stage[s_wc[w * nb + (dr[j] >> 16)] + (dr[j] & 0xffffu)] = key[j];
         __syncthreads();
         const uint32_t n = end - tile < (uint32_t)kSortTile ? end - tile : (uint32_t)kSortTile;
 #pragma unroll
@@ -764,12 +772,10 @@ __global__ void __launch_bounds__(kBlock) sort_downsweep_kernel(SortPass p) {
             if (pos < n) {
                 const uint64_t k = s_stage[pos];
                 const uint32_t d = (uint32_t)(k >> p.shift) & mask;
-                const uint32_t dst = s_base[d] + (pos - s_ts[d]);
+                const uint32_t dst = s_off[d] + pos;
                 if (dst < end_all) p.out[dst] = k;
             }
         }
-#pragma unroll
-        for (int j = 0; j < kSortItems; ++j) key[j] = nkey[j];
     }
 }
 
@@ -1162,6 +1168,22 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Blocks of the kBlock-thread kernel K the whole device holds at once (its
+// occupancy times the CU count), cached per kernel; 1024 if the runtime
+// cannot tell.
+template <auto K>
+int resident_blocks() {
+    static int cached = 0;
+    if (cached > 0) return cached;
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, K, kBlock, 0) != hipSuccess || cus <= 0 || per <= 0)
+        return 1024;
+    cached = cus * per;
+    return cached;
+}
+
 int grid_cap(int64_t n, int per, int cap) {
     int64_t g = (n + per - 1) / per;
     if (g < 1) g = 1;
@@ -1305,23 +1327,27 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
     };
     // LSD passes over bits [lo, lo + nbits) of 64-bit words, digits of at most
     // kMaxDigitBits bits; returns the buffer index holding the result.
-    auto radix = [&](uint64_t** buf, const uint64_t* count, uint64_t rcap, int lo, int nbits, int nblocks) {
+    auto radix = [&](uint64_t** buf, const uint64_t* count, uint64_t rcap, int lo, int nbits, int max_blocks) {
         const int passes = (nbits + kMaxDigitBits - 1) / kMaxDigitBits;
         const int bits = (nbits + passes - 1) / passes;
         int cur = 0;
         for (int pass = 0; pass < passes; ++pass) {
-            SortPass sp{buf[cur], buf[cur ^ 1], count, rcap, lo + pass * bits, bits, nblocks, counts, digit_tot};
-            if (bits <= 8) {
-                IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<8>, dim3(nblocks), dim3(kBlock), 0, s, sp);
+            SortPass sp{buf[cur], buf[cur ^ 1], count, rcap, lo + pass * bits, bits, max_blocks, counts, digit_tot};
+            auto run = [&](auto digit_bits) {
+                constexpr int B = decltype(digit_bits)::value;
+                // one round of resident blocks: every block takes an equal chunk
+                const int r = resident_blocks<sort_downsweep_kernel<B>>();
+                sp.nblocks = max_blocks < r ? max_blocks : r;
+                IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<B>, dim3(sp.nblocks), dim3(kBlock), 0, s, sp);
                 IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
-                IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel<8>, dim3(nblocks), dim3(kBlock), 0, s, sp);
-            } else {
-                IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<kMaxDigitBits>, dim3(nblocks), dim3(kBlock), 0,
-                          s, sp);
-                IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
-                IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel<kMaxDigitBits>, dim3(nblocks), dim3(kBlock),
-                          0, s, sp);
-            }
+                IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel<B>, dim3(sp.nblocks), dim3(kBlock), 0, s, sp);
+            };
+            if (bits <= 8)
+                run(std::integral_constant<int, 8>{});
+            else if (bits == 9)
+                run(std::integral_constant<int, 9>{});
+            else
+                run(std::integral_constant<int, kMaxDigitBits>{});
             cur ^= 1;
         }
         return cur;
