@@ -67,11 +67,12 @@ struct ia_decoder {
     float* b[ia::kMaxDecoderMats] = {};
     void* Wt = nullptr;         // per-attribute fp16 decoder: weights in MFMA A-tile order
     float* bpack = nullptr;     // per-attribute fp16 decoder: biases packed per branch
-    uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [chunk] float4
+    uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [2][chunk] float4
     float* bwd_partial = nullptr;  // fp16 path: per-wave weight-gradient partials of the backward
     hipStream_t side = nullptr;  // fp16 path: MLP stream overlapping the next chunk's gather
     hipEvent_t ev_gather[2] = {nullptr, nullptr};
     hipEvent_t ev_mlp[2] = {nullptr, nullptr};
+    hipEvent_t ev_norm[2] = {nullptr, nullptr};
     bool ready = false;
 };
 
@@ -97,7 +98,8 @@ void free_decoder_params(ia_decoder* d) {
     for (int k = 0; k < 2; ++k) {
         if (d->ev_gather[k]) (void)hipEventDestroy(d->ev_gather[k]);
         if (d->ev_mlp[k]) (void)hipEventDestroy(d->ev_mlp[k]);
-        d->ev_gather[k] = d->ev_mlp[k] = nullptr;
+        if (d->ev_norm[k]) (void)hipEventDestroy(d->ev_norm[k]);
+        d->ev_gather[k] = d->ev_mlp[k] = d->ev_norm[k] = nullptr;
     }
     if (d->side) (void)hipStreamDestroy(d->side);
     d->side = nullptr;
@@ -201,6 +203,7 @@ ia::DecodeArgs decode_args(const ia_decoder* dec, const float* pos, int stride, 
     for (int k = 0; k < 2; ++k) {
         a.ev_gather[k] = dec->ev_gather[k];
         a.ev_mlp[k] = dec->ev_mlp[k];
+        a.ev_norm[k] = dec->ev_norm[k];
     }
     return a;
 }
@@ -320,7 +323,7 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
     }
     if (st == IA_OK && dec->mlp.dtype == IA_DTYPE_F16) {
         // [2][L][chunk] packed fp16 features (F per entry), then [chunk] normalised positions (float4)
-        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 4 * dec->hash.F + 16) * ia::kDecodeChunk);
+        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 4 * dec->hash.F + 32) * ia::kDecodeChunk);
         if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
         if (st == IA_OK) {
             e = hipMalloc(&dec->bwd_partial, sizeof(float) * (size_t)ia::kDecodeBwdPartialFloats);
@@ -331,6 +334,7 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
         for (int k = 0; st == IA_OK && e == hipSuccess && k < 2; ++k) {
             e = hipEventCreateWithFlags(&dec->ev_gather[k], hipEventDisableTiming);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&dec->ev_mlp[k], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&dec->ev_norm[k], hipEventDisableTiming);
         }
         if (st == IA_OK && e != hipSuccess) st = hip_fail(e, "stream/event creation");
     }

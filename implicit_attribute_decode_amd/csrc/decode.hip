@@ -489,10 +489,16 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
     if (dtype == IA_DTYPE_F16) {
         if (!a.zbuf || a.zcap <= 0) return hipErrorInvalidValue;
         // Chunks of at most zcap Gaussians.  With a side stream, the MLP of
-        // chunk k runs there while chunk k+1 is normalised and gathered on s;
-        // the feature scratch is double-buffered and events order the hand-offs.
+        // chunk k and the normalisation of chunk k + 1 run there while chunk
+        // k is gathered on s, so s gathers back to back:
+        //   s:    N0 G0 | G1 | G2 ...         (G k+1 waits for N k+1)
+        //   side:    N1 | M0 N2 | M1 N3 ...   (M k waits for G k)
+        // The feature scratch and the normalised positions are
+        // double-buffered; N k+2 follows M k on the side stream, which
+        // follows G k, the last reader of position slot k & 1.
         const size_t zslot = (size_t)a.h.L * a.zcap * (a.h.F / 2);  // 32-bit words per scratch slot
-        float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
+        float4* xtb[2] = {reinterpret_cast<float4*>(a.zbuf + 2 * zslot),
+                          reinterpret_cast<float4*>(a.zbuf + 2 * zslot) + a.zcap};
         // features go to the caller's buffer ([L][N], kept for a backward) or to the
         // double-buffered scratch ([L][zcap] per slot)
         const int64_t zstride = a.features ? a.N : a.zcap;
@@ -506,16 +512,30 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             IA_LAUNCH("mlp_f16_kernel", k, dim3(grid), dim3(256), 0, st, a, zb, zstride, n, off);
             return hipGetLastError();
         };
+        auto normalize = [&](hipStream_t st, int64_t off, float4* xt) -> hipError_t {
+            const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
+            IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a,
+                      a.pos + off * a.stride, n, xt);
+            return hipGetLastError();
+        };
         const bool overlap = a.side != nullptr && a.N > a.zcap;
+        hipError_t e = normalize(s, 0, xtb[0]);
+        if (e != hipSuccess) return e;
+        if (overlap) {
+            // the side stream starts after everything already queued on s
+            // (the caller's writes of the positions, earlier readers of the scratch)
+            if ((e = hipEventRecord(a.ev_norm[0], s)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(a.side, a.ev_norm[0], 0)) != hipSuccess) return e;
+        }
         int k = 0;
         for (int64_t off = 0; off < a.N; off += a.zcap, ++k) {
             const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
             const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
             uint32_t* zb = a.features ? a.features + (size_t)off * (a.h.F / 2) : a.zbuf + (size_t)(k & 1) * zslot;
-            hipError_t e;
+            float4* xt = xtb[overlap ? (k & 1) : 0];
+            if (overlap && k >= 1 && (e = hipStreamWaitEvent(s, a.ev_norm[k & 1], 0)) != hipSuccess) return e;
             if (overlap && k >= 2 && (e = hipStreamWaitEvent(s, a.ev_mlp[k & 1], 0)) != hipSuccess) return e;
-            IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
-                      a.pos + off * a.stride, n, xt);
+            if (!overlap && k >= 1 && (e = normalize(s, off, xt)) != hipSuccess) return e;
             if (a.h.F == 4) {
                 if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, zstride, s)) != hipSuccess) return e;
             } else {
@@ -524,6 +544,11 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             }
             if (overlap) {
                 if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;
+                const int64_t noff = off + a.zcap;
+                if (noff < a.N) {
+                    if ((e = normalize(a.side, noff, xtb[(k + 1) & 1])) != hipSuccess) return e;
+                    if ((e = hipEventRecord(a.ev_norm[(k + 1) & 1], a.side)) != hipSuccess) return e;
+                }
                 if ((e = hipStreamWaitEvent(a.side, a.ev_gather[k & 1], 0)) != hipSuccess) return e;
                 if ((e = mlp(a.side, zb, n, off)) != hipSuccess) return e;
                 if ((e = hipEventRecord(a.ev_mlp[k & 1], a.side)) != hipSuccess) return e;
@@ -534,7 +559,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         if (overlap) {
             // the caller's stream resumes after the last MLPs (the side stream
             // is in order, so the last event covers every earlier chunk)
-            hipError_t e = hipStreamWaitEvent(s, a.ev_mlp[(k - 1) & 1], 0);
+            e = hipStreamWaitEvent(s, a.ev_mlp[(k - 1) & 1], 0);
             if (e != hipSuccess) return e;
         }
         return hipGetLastError();

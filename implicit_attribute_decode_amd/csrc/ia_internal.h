@@ -76,6 +76,7 @@ struct DecodeArgs {
     hipStream_t side;         // fp16 path: stream the MLP of one chunk overlaps the next gather on (or null)
     hipEvent_t ev_gather[2];  // per scratch slot: gather done
     hipEvent_t ev_mlp[2];     // per scratch slot: MLP done
+    hipEvent_t ev_norm[2];    // per position slot: normalisation (side stream) done
 };
 
 // Gaussians per fp16-decode chunk; the handle owns L * kDecodeChunk * 4 bytes.

@@ -1064,6 +1064,8 @@ struct Pix {
     bool done;
 };
 
+// LAST: track the index of the last composited Gaussian (the n_contrib output).
+template <bool LAST>
 __device__ __forceinline__ void composite_step(Pix& p, float power, float opacity, float cr, float cg, float cb,
                                                uint32_t pos) {
 #pragma clang fp contract(fast)
@@ -1075,7 +1077,7 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
     p.g += cg * wgt;
     p.b += cb * wgt;
     p.T = p.T * (1.0f - alpha);
-    p.last = take ? pos : p.last;
+    if (LAST) p.last = take ? pos : p.last;
     p.done = p.done || p.T < 1e-4f;
 }
 
@@ -1090,15 +1092,18 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
 // B' dx dy.  A wave leaves a batch once all its pixels are saturated; the
 // block stops once all 256 are.
 constexpr int kRasterBatch = 256;
+constexpr int kRasterCheck = 8;  // Gaussians between two saturation checks of a wave
 constexpr int64_t kRasterTwoPixelTiles = 8192;  // tiles per launch from which two pixels per thread pay
 
-template <int PX>
+template <int PX, bool LAST>
 __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
 #pragma clang fp contract(fast)
     constexpr int kThreads = 256 / PX;
     __shared__ float4 s_a[kRasterBatch];
     __shared__ float4 s_b[kRasterBatch];
-    __shared__ float s_c[kRasterBatch];
+    // third colour channel, at the same 16-byte stride as s_a and s_b so that one
+    // address serves all three reads of a Gaussian
+    __shared__ float4 s_c[kRasterBatch];
     const int f = blockIdx.z;
     const uint32_t tile = (uint32_t)f * a.ntiles + blockIdx.y * (uint32_t)a.tiles_x + blockIdx.x;
     uint2 rg = a.ranges[tile];
@@ -1121,33 +1126,38 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
                 const float4 pa = a.pa[gid], pb = a.pb[gid];
                 s_a[slot] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
                 s_b[slot] = make_float4(-0.5f * pb.x, pb.y, pb.z, pb.w);
-                s_c[slot] = a.pc[gid];
+                s_c[slot].x = a.pc[gid];
             }
         }
         __syncthreads();
         const int n = (int)min((uint32_t)kRasterBatch, rg.y - start);
         const uint32_t pos0 = start - rg.x + 1u;
-        for (int j = 0; j < n; ++j) {
+        // A wave whose pixels are all saturated leaves the batch; that is
+        // checked every kRasterCheck Gaussians (compositing ignores
+        // saturated pixels, so the check only saves work).
+        for (int j0 = 0; j0 < n; j0 += kRasterCheck) {
             if (__ballot(!(p0.done && p1.done)) == 0ull) break;
-            const float4 ga = s_a[j];
-            const float4 gb = s_b[j];
-            const float gcb = s_c[j];
-            const float dx = fx - ga.x;
-            float ta, tb;
-            splat_dx_terms(ga.z, ga.w, dx, ta, tb);
-            const float dy0 = fy0 - ga.y;
-            const float pw0 = splat_power(ta, tb, gb.x, dy0);
-            bool any = pw0 >= -4.5f && pw0 <= 0.0f;
-            float pw1 = 0.0f;
-            if (PX == 2) {
-                const float dy1 = fy1 - ga.y;
-                pw1 = splat_power(ta, tb, gb.x, dy1);
-                any = any || (pw1 >= -4.5f && pw1 <= 0.0f);
+            const int jn = n - j0 < kRasterCheck ? n : j0 + kRasterCheck;
+            for (int j = j0; j < jn; ++j) {
+                const float4 ga = s_a[j];
+                const float4 gb = s_b[j];
+                const float gcb = s_c[j].x;
+                const float dx = fx - ga.x;
+                float ta, tb;
+                splat_dx_terms(ga.z, ga.w, dx, ta, tb);
+                const float dy0 = fy0 - ga.y;
+                const float pw0 = splat_power(ta, tb, gb.x, dy0);
+                float pw1 = -INFINITY;
+                if (PX == 2) {
+                    const float dy1 = fy1 - ga.y;
+                    pw1 = splat_power(ta, tb, gb.x, dy1);
+                }
+                // no pixel of the wave within 3 sigma: nothing to composite.
+                // (A superset test: the compositing step applies the exact rule.)
+                if (__ballot(fmaxf(pw0, pw1) >= -4.5f) == 0ull) continue;
+                composite_step<LAST>(p0, pw0, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
+                if (PX == 2) composite_step<LAST>(p1, pw1, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
             }
-            // no pixel of the wave within 3 sigma: nothing to composite
-            if (__ballot(any) == 0ull) continue;
-            composite_step(p0, pw0, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
-            if (PX == 2) composite_step(p1, pw1, gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
         }
     }
     const DevCamera& cam = a.cams[f];
@@ -1162,7 +1172,7 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
         img[plane + pix] = p.g + p.T * cam.bg[1];
         img[2 * plane + pix] = p.b + p.T * cam.bg[2];
         if (a.T_final) a.T_final[(size_t)f * plane + pix] = p.T;
-        if (a.n_contrib) a.n_contrib[(size_t)f * plane + pix] = p.last;
+        if (LAST && a.n_contrib) a.n_contrib[(size_t)f * plane + pix] = p.last;
     }
 }
 
@@ -1420,10 +1430,19 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
     RasterArgs ra{ranges, vals, pa, pb, pc, cams, a.W, a.H, L.tiles_x, ntiles, cap, N, a.image, a.T_final,
                   a.n_contrib};
     // two pixels per thread when there are enough tiles to fill the chip twice over
-    if (L.ntiles_all >= kRasterTwoPixelTiles)
-        IA_LAUNCH("raster_kernel", raster_kernel<2>, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(128), 0, s, ra);
-    else
-        IA_LAUNCH("raster_kernel", raster_kernel<1>, dim3(L.tiles_x, L.tiles_y, a.frames), dim3(256), 0, s, ra);
+    // (the index of the last composited Gaussian is tracked only for n_contrib)
+    const dim3 tgrid(L.tiles_x, L.tiles_y, a.frames);
+    if (L.ntiles_all >= kRasterTwoPixelTiles) {
+        if (a.n_contrib)
+            IA_LAUNCH("raster_kernel", (raster_kernel<2, true>), tgrid, dim3(128), 0, s, ra);
+        else
+            IA_LAUNCH("raster_kernel", (raster_kernel<2, false>), tgrid, dim3(128), 0, s, ra);
+    } else {
+        if (a.n_contrib)
+            IA_LAUNCH("raster_kernel", (raster_kernel<1, true>), tgrid, dim3(256), 0, s, ra);
+        else
+            IA_LAUNCH("raster_kernel", (raster_kernel<1, false>), tgrid, dim3(256), 0, s, ra);
+    }
     *keys_out = nullptr;
     *vals_out = nullptr;
     if (a.unpack) {
