@@ -203,11 +203,17 @@ __global__ void __launch_bounds__(256 / PX) raster_backward_kernel(RasterBwdArgs
             splat_dx_terms(ga.z, ga.w, dx, ta, tb);
             float pw[PX], al[PX], dy[PX];
             bool tk[PX];
-            bool any = false;
+            bool near = false;  // a superset of the composited pixels, before any exp
 #pragma unroll
             for (int k = 0; k < PX; ++k) {
                 dy[k] = (float)(py0 + k) + 0.5f - ga.y;
                 pw[k] = splat_power(ta, tb, gb.x, dy[k]);
+                near = near || (pos1 <= P[k].nc && pw[k] >= -4.5f);
+            }
+            if (__ballot(near) == 0ull) continue;
+            bool any = false;
+#pragma unroll
+            for (int k = 0; k < PX; ++k) {
                 al[k] = splat_alpha(gb.y, pw[k]);
                 tk[k] = pos1 <= P[k].nc && splat_takes(pw[k], al[k]);
                 any = any || tk[k];
