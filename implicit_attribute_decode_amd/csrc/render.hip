@@ -919,14 +919,21 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& a, uint64_t item, 
             take = (uint32_t)__popcll(__ballot(incl <= (uint32_t)kStage));
             if ((uint32_t)lane >= take) cx0 = 1, cx1 = 0;
         }
-        uint32_t c = 0;  // lane t: entries of region tile t in this chunk
-#pragma unroll 8
-        for (int t = 0; t < kRegionTiles; ++t) {
-            const uint32_t tx = t % kRegion, ty = t / kRegion;
-            const bool cov = cx0 <= tx && tx <= cx1 && cy0 <= ty && ty <= cy1;
-            const uint32_t nt = (uint32_t)__popcll(__ballot(cov));
-            c = lane == t ? nt : c;
+        // lanes whose clip covers region column x / row y; the lanes covering
+        // tile (x, y) are the intersection of the two masks
+        uint64_t colm[kRegion], rowm[kRegion];
+#pragma unroll
+        for (int x = 0; x < kRegion; ++x) colm[x] = __ballot(cx0 <= (uint32_t)x && (uint32_t)x <= cx1);
+#pragma unroll
+        for (int y = 0; y < kRegion; ++y) rowm[y] = __ballot(cy0 <= (uint32_t)y && (uint32_t)y <= cy1);
+        // lane t: entries of region tile t in this chunk
+        uint64_t cm = 0ull, rm = 0ull;
+#pragma unroll
+        for (int x = 0; x < kRegion; ++x) {
+            cm = lane % kRegion == x ? colm[x] : cm;
+            rm = lane / kRegion == x ? rowm[x] : rm;
         }
+        const uint32_t c = (uint32_t)__popcll(cm & rm);
         if (!WRITE) {
             total += c;
         } else {
@@ -934,14 +941,15 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& a, uint64_t item, 
             const uint32_t m = __shfl(choff + c, 63, 64);
 #pragma unroll 8
             for (int t = 0; t < kRegionTiles; ++t) {
-                const uint32_t tx = t % kRegion, ty = t / kRegion;
-                const bool cov = cx0 <= tx && tx <= cx1 && cy0 <= ty && ty <= cy1;
-                const uint64_t mk = __ballot(cov);
+                const uint64_t mk = colm[t % kRegion] & rowm[t / kRegion];
+                if (mk == 0ull) continue;
                 const uint32_t seg = __builtin_amdgcn_readlane(choff, t);
-                if (cov) {
-                    const uint32_t slot = seg + (uint32_t)__popcll(mk & lt_mask);
-                    stage[slot] = gidx;
-                    tof[slot] = (uint8_t)t;
+                if ((mk >> lane) & 1ull) {
+                    // rank among the covering lanes below this one (depth order)
+                    const uint32_t below =
+                        __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+                    stage[seg + below] = gidx;
+                    tof[seg + below] = (uint8_t)t;
                 }
             }
             asm volatile("" ::: "memory");
