@@ -463,6 +463,19 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
     }
 }
 
+// Compute units of the current device (cached per device; 256 if the
+// runtime cannot tell).
+int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    cached[dev] = cus;
+    return cus;
+}
+
 int grid_for(int64_t items_per_block, int64_t N, int cap_blocks) {
     int64_t b = (N + items_per_block - 1) / items_per_block;
     if (b < 1) b = 1;
@@ -502,23 +515,35 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         // features go to the caller's buffer ([L][N], kept for a backward) or to the
         // double-buffered scratch ([L][zcap] per slot)
         const int64_t zstride = a.features ? a.N : a.zcap;
+        const bool overlap = a.side != nullptr && a.N > a.zcap;
         auto mlp = [&](hipStream_t st, const uint32_t* zb, int64_t n, int64_t off) -> hipError_t {
             if (a.branches) return launch_mlp_branch(a, zb, zstride, n, off, st);
-            // 256 threads = 4 waves x 64 Gaussians; at most 2 resident blocks per CU are useful
-            const int grid = grid_for(256, n, 256 * 8);
+            // 256 threads = 4 waves x 64 Gaussians.  Beside a gather (overlap)
+            // one block per CU: the MLP still finishes well within the next
+            // chunk's gather and takes fewer wave slots from it.
+            const int grid = grid_for(256, n, overlap ? device_cus() : 256 * 8);
             const bool gelu = a.act == IA_ACT_GELU;
             auto k = a.sh_head ? (gelu ? mlp_f16_kernel<true, true> : mlp_f16_kernel<true, false>)
                                : (gelu ? mlp_f16_kernel<false, true> : mlp_f16_kernel<false, false>);
             IA_LAUNCH("mlp_f16_kernel", k, dim3(grid), dim3(256), 0, st, a, zb, zstride, n, off);
             return hipGetLastError();
         };
+        // Chunk length at offset off: zcap, except that with the side stream
+        // the last two chunks split what is left about 2 : 1, so that the
+        // MLP of the second-last chunk hides under the last gather and the
+        // MLP left exposed at the end is short.
+        auto chunk_len = [&](int64_t off) -> int64_t {
+            const int64_t left = a.N - off;
+            if (left <= a.zcap) return left;
+            if (overlap && left < 2 * a.zcap) return (2 * left + 2) / 3 < a.zcap ? (2 * left + 2) / 3 : a.zcap;
+            return a.zcap;
+        };
         auto normalize = [&](hipStream_t st, int64_t off, float4* xt) -> hipError_t {
-            const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
+            const int64_t n = chunk_len(off);
             IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a,
                       a.pos + off * a.stride, n, xt);
             return hipGetLastError();
         };
-        const bool overlap = a.side != nullptr && a.N > a.zcap;
         hipError_t e = normalize(s, 0, xtb[0]);
         if (e != hipSuccess) return e;
         if (overlap) {
@@ -528,8 +553,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             if ((e = hipStreamWaitEvent(a.side, a.ev_norm[0], 0)) != hipSuccess) return e;
         }
         int k = 0;
-        for (int64_t off = 0; off < a.N; off += a.zcap, ++k) {
-            const int64_t n = a.N - off < a.zcap ? a.N - off : a.zcap;
+        for (int64_t off = 0, n = 0; off < a.N; off += n, ++k) {
+            n = chunk_len(off);
             const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
             uint32_t* zb = a.features ? a.features + (size_t)off * (a.h.F / 2) : a.zbuf + (size_t)(k & 1) * zslot;
             float4* xt = xtb[overlap ? (k & 1) : 0];
@@ -544,7 +569,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             }
             if (overlap) {
                 if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;
-                const int64_t noff = off + a.zcap;
+                const int64_t noff = off + n;
                 if (noff < a.N) {
                     if ((e = normalize(a.side, noff, xtb[(k + 1) & 1])) != hipSuccess) return e;
                     if ((e = hipEventRecord(a.ev_norm[(k + 1) & 1], a.side)) != hipSuccess) return e;
