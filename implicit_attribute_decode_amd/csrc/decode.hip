@@ -211,14 +211,16 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // rows 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows.
 
 constexpr int kGatherPerBlock = 256;  // Gaussians per gather block (64 per pass x 4 passes)
+constexpr int kMlpCusPerBlock = 2;    // MLP beside a gather: one block per this many CUs
+constexpr int kNormBlocksPerCu = 2;   // normalisation beside a gather: blocks per CU
 
 __global__ void __launch_bounds__(256) normalize_kernel(DecodeArgs a, const float* pos, int64_t n, float4* xt) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const float* p = pos + i * a.stride;
-    float v[4];
-    normalize_pos(p[0], p[1], p[2], a.stride == 4 ? p[3] : a.t_scalar, a.h.t_min, a.h.t_max, v);
-    xt[i] = make_float4(v[0], v[1], v[2], v[3]);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const float* p = pos + i * a.stride;
+        float v[4];
+        normalize_pos(p[0], p[1], p[2], a.stride == 4 ? p[3] : a.t_scalar, a.h.t_min, a.h.t_max, v);
+        xt[i] = make_float4(v[0], v[1], v[2], v[3]);
+    }
 }
 
 __global__ void __launch_bounds__(256) gather_f16_kernel(const float4* xt, int64_t n, int nchunk, HashLevels h,
@@ -516,12 +518,13 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         // double-buffered scratch ([L][zcap] per slot)
         const int64_t zstride = a.features ? a.N : a.zcap;
         const bool overlap = a.side != nullptr && a.N > a.zcap;
-        auto mlp = [&](hipStream_t st, const uint32_t* zb, int64_t n, int64_t off) -> hipError_t {
+        auto mlp = [&](hipStream_t st, const uint32_t* zb, int64_t n, int64_t off, bool beside) -> hipError_t {
             if (a.branches) return launch_mlp_branch(a, zb, zstride, n, off, st);
-            // 256 threads = 4 waves x 64 Gaussians.  Beside a gather (overlap)
-            // one block per CU: the MLP still finishes well within the next
-            // chunk's gather and takes fewer wave slots from it.
-            const int grid = grid_for(256, n, overlap ? device_cus() : 256 * 8);
+            // 256 threads = 4 waves x 64 Gaussians.  Beside a gather, one block
+            // per kMlpCusPerBlock CUs: the MLP still finishes within the gather
+            // and takes fewer wave slots from it; the last chunk's MLP, which
+            // runs alone, takes the whole chip.
+            const int grid = grid_for(256, n, beside ? device_cus() / kMlpCusPerBlock : 256 * 8);
             const bool gelu = a.act == IA_ACT_GELU;
             auto k = a.sh_head ? (gelu ? mlp_f16_kernel<true, true> : mlp_f16_kernel<true, false>)
                                : (gelu ? mlp_f16_kernel<false, true> : mlp_f16_kernel<false, false>);
@@ -540,8 +543,10 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         };
         auto normalize = [&](hipStream_t st, int64_t off, float4* xt) -> hipError_t {
             const int64_t n = chunk_len(off);
-            IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a,
-                      a.pos + off * a.stride, n, xt);
+            // beside a gather (side stream) a few blocks per CU are enough
+            const int grid = grid_for(256, n, st == s ? 1 << 30 : kNormBlocksPerCu * device_cus());
+            IA_LAUNCH("normalize_kernel", normalize_kernel, dim3(grid), dim3(256), 0, st, a, a.pos + off * a.stride, n,
+                      xt);
             return hipGetLastError();
         };
         hipError_t e = normalize(s, 0, xtb[0]);
@@ -575,10 +580,10 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
                     if ((e = hipEventRecord(a.ev_norm[(k + 1) & 1], a.side)) != hipSuccess) return e;
                 }
                 if ((e = hipStreamWaitEvent(a.side, a.ev_gather[k & 1], 0)) != hipSuccess) return e;
-                if ((e = mlp(a.side, zb, n, off)) != hipSuccess) return e;
+                if ((e = mlp(a.side, zb, n, off, noff < a.N)) != hipSuccess) return e;
                 if ((e = hipEventRecord(a.ev_mlp[k & 1], a.side)) != hipSuccess) return e;
             } else {
-                if ((e = mlp(s, zb, n, off)) != hipSuccess) return e;
+                if ((e = mlp(s, zb, n, off, false)) != hipSuccess) return e;
             }
         }
         if (overlap) {
