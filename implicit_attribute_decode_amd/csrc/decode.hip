@@ -292,6 +292,95 @@ __global__ void __launch_bounds__(256) gather_f16_kernel(const float4* xt, int64
     }
 }
 
+// The same gather for a launch with nothing beside it: all 16 corner loads of
+// a thread's four passes are issued before any is used (46 VGPRs), which a
+// lone launch needs to cover the L2 latency; beside the MLP the kernel above
+// leaves that MLP more room.  The loads are range-checked buffer loads over
+// the level's table: a skipped corner or a lane past the last Gaussian reads
+// past the end (zero, no memory request) instead of branching.
+__global__ void __launch_bounds__(256) gather_f16_batched_kernel(const float4* xt, int64_t n, int nchunk,
+                                                                 HashLevels h, const uint32_t* tables,
+                                                                 uint32_t* zbuf, int64_t zstride) {
+#pragma clang fp contract(fast)
+    const int level = blockIdx.x / nchunk;
+    const int64_t first = (int64_t)(blockIdx.x % nchunk) * kGatherPerBlock;
+    const int res = h.res_s[level], res_t = h.res_t[level];
+    const bool dense = h.dense[level] != 0;
+    const uint32_t* tab = tables + (size_t)level * h.T;
+    uint32_t* zl = zbuf + (size_t)level * zstride;
+    const int s = threadIdx.x & 3;
+    const int bx = s & 1, by = s >> 1;
+    const int sub = threadIdx.x >> 2;
+    const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
+    constexpr int kPasses = kGatherPerBlock / 64;
+    const __amdgpu_buffer_rsrc_t rt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)tab, (short)0, (int)(h.T * 4u), kBufferWord3);
+    float4 P[kPasses];
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+        const int64_t i = first + j * 64 + sub;
+        P[j] = xt[i < n ? i : n - 1];
+    }
+    uint32_t raw[kPasses][4];
+    float wc[kPasses][4];
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+        const bool valid = first + j * 64 + sub < n;
+        int cx, cy, cz, ct;
+        float fx, fy, fz, ft;
+        cell_axis(P[j].x, res, cx, fx);
+        cell_axis(P[j].y, res, cy, fy);
+        cell_axis(P[j].z, res, cz, fz);
+        cell_axis(P[j].w, res_t, ct, ft);
+        const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
+        uint32_t txy, tz[2], tt[2];
+        if (dense) {
+            txy = ux + uy * r;
+            tz[0] = (uint32_t)cz * r2;
+            tz[1] = tz[0] + r2;
+            tt[0] = (uint32_t)ct * r3;
+            tt[1] = tt[0] + r3;
+        } else {
+            txy = (ux * kP1) ^ (uy * kP2);
+            tz[0] = (uint32_t)cz * kP3;
+            tz[1] = (uint32_t)(cz + 1) * kP3;
+            tt[0] = (uint32_t)ct * kP4;
+            tt[1] = (uint32_t)(ct + 1) * kP4;
+        }
+        const float wxy = (bx ? fx : 1.0f - fx) * (by ? fy : 1.0f - fy);
+        const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int bz = c & 1, bt = c >> 1;
+            const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
+            wc[j][c] = (wxy * wz[bz]) * wt[bt];
+            // a corner of zero weight adds exactly zero: not fetched (zero bits stand in)
+            const uint32_t off = (valid && wc[j][c] != 0.0f) ? idx * 4u : kBufferNone;
+            raw[j][c] = __builtin_amdgcn_raw_buffer_load_b32(rt, off, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            a0 += wc[j][c] * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][c] & 0xffffu));
+            a1 += wc[j][c] * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][c] >> 16));
+        }
+        // the same sums over the four lanes as the kernel above: xor 1, then xor 2
+        a0 += __shfl_xor(a0, 1, 4);
+        a1 += __shfl_xor(a1, 1, 4);
+        a0 += __shfl_xor(a0, 2, 4);
+        a1 += __shfl_xor(a1, 2, 4);
+        const int64_t i = first + j * 64 + sub;
+        if (s == 0 && i < n) {
+            const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);
+            const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
+            zl[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        }
+    }
+}
+
 // Bias + activation of one 16x16 D tile (rows 16 rb + 4 q + e), rounded to fp16.
 template <bool GELU>
 __device__ __forceinline__ half4_t act_tile(floatx4 acc, const float* bias) {
@@ -494,8 +583,8 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
     IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
               a.pos + off * a.stride, n, xt);
     if (!z) return hipGetLastError();  // features kept by the forward: normalisation only
-    IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n, nchunk,
-              a.h, (const uint32_t*)a.tables, z, zstride);
+    IA_LAUNCH("gather_f16_kernel", gather_f16_batched_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n,
+              nchunk, a.h, (const uint32_t*)a.tables, z, zstride);
     return hipGetLastError();
 }
 
@@ -569,8 +658,14 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             if (a.h.F == 4) {
                 if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, zstride, s)) != hipSuccess) return e;
             } else {
-                IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
-                          n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
+                // beside an MLP (every chunk but the first of an overlapped decode)
+                // the lean gather, alone the batched one
+                if (overlap && k >= 1)
+                    IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0,
+                              s, xt, n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
+                else
+                    IA_LAUNCH("gather_f16_kernel", gather_f16_batched_kernel, dim3((unsigned)(a.h.L * nchunk)),
+                              dim3(256), 0, s, xt, n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
             }
             if (overlap) {
                 if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;
