@@ -623,11 +623,17 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         // Chunk length at offset off: zcap, except that with the side stream
         // the last two chunks split what is left about 2 : 1, so that the
         // MLP of the second-last chunk hides under the last gather and the
-        // MLP left exposed at the end is short.
+        // MLP left exposed at the end is short.  Every chunk but the last is
+        // a multiple of 256 Gaussians: the MFMA rounding of a Gaussian's
+        // decode depends on the column it occupies (its index mod 64 in the
+        // chunk), so aligned chunks make the result independent of chunking.
         auto chunk_len = [&](int64_t off) -> int64_t {
             const int64_t left = a.N - off;
             if (left <= a.zcap) return left;
-            if (overlap && left < 2 * a.zcap) return (2 * left + 2) / 3 < a.zcap ? (2 * left + 2) / 3 : a.zcap;
+            if (overlap && left < 2 * a.zcap) {
+                const int64_t two_thirds = ((2 * left + 2) / 3 + 255) & ~(int64_t)255;
+                return two_thirds < a.zcap ? two_thirds : a.zcap;
+            }
             return a.zcap;
         };
         auto normalize = [&](hipStream_t st, int64_t off, float4* xt) -> hipError_t {

@@ -187,6 +187,29 @@ def test_decode_zero_is_noop():
     assert out["scales"].shape == (0, 3)
 
 
+def test_chunked_decode_bitwise_equals_slice_decodes():
+    """A decode of more than one chunk (at most 2^22 Gaussians per chunk; the
+    MLP of a chunk runs beside the next chunk's gather, and every chunk after
+    the first uses the lean gather) gives bit for bit what decoding each
+    64-aligned slice on its own gives (one chunk: batched gather, MLP on the
+    whole chip).  The MFMA rounding of a Gaussian depends on its index mod 64
+    (the matrix column it occupies), so slices start at multiples of 64 and
+    the library cuts chunks at multiples of 256."""
+    rng = np.random.default_rng(11)
+    n = (1 << 22) + 5000
+    xyzt = np.concatenate([rng.normal(0.0, 2.0, (n, 3)), rng.uniform(0.0, 1.0, (n, 1))], 1).astype(np.float32)
+    xyzt[::7, 3] = np.round(xyzt[::7, 3] * 149.0) / 149.0  # some times on temporal vertices
+    D = Decoder(S.single_decoder())
+    x = cuda(xyzt)
+    full = {k: v.clone() for k, v in D.decode_xyzt(x).items()}
+    for lo, hi in ((0, 1000), (1 << 21, (1 << 21) + 777), (2_800_000 - 64 * 5, 2_800_000 + 999), (n - 5000 & ~63, n)):
+        part = D.decode_xyzt(x[lo:hi].contiguous())
+        torch.cuda.synchronize()
+        for k in full:
+            assert torch.equal(full[k][lo:hi], part[k]), (k, lo, hi)
+    say(f"chunked decode of {n} = slice decodes bit for bit")
+
+
 def test_sequence_full_size_sampled():
     """All 150 x 200k (x,y,z,t) positions in one launch; 24k sampled rows
     (every frame represented) against the oracle."""
