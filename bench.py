@@ -38,10 +38,11 @@ GATHER_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES
 DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
 # HBM-side bytes per gather launch of this workload (mean launch: 3.75M Gaussians), from two
 # rocprofv3 counter runs over `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra
-# --calibrate-copy`: FETCH_SIZE 616,794.6 KiB x 2 + WRITE_SIZE 235,539.8 KiB x 1, the factors being
-# what the counters read for a 1 GiB device copy (profiles/gather_f16_sequence_hbm_traffic.md).
-# Valid for the gather kernel as it was when counted; null once that kernel changes.
-GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 616_794.6 + 235_539.8) * 1024
+# --calibrate-copy`: FETCH_SIZE 614,388.4 KiB x 2 + WRITE_SIZE 235,684.2 KiB x 1 (mean of the lean
+# and batched gather launches), the factors being what the counters read for a 1 GiB device copy
+# (profiles/gather_f16_sequence_hbm_traffic.md).  Valid for the gather kernels as they were when
+# counted; null once they change.
+GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 614_388.4 + 235_684.2) * 1024
 
 
 def log(*a):
