@@ -33,6 +33,7 @@ class Decoder:
                         ia.IA_DTYPE_F16 if f16 else ia.IA_DTYPE_F32,
                         ia.IA_COLOR_SH3 if self.sh else ia.IA_COLOR_RGB,
                         ia.IA_BRANCHES_PER_ATTRIBUTE if branches else ia.IA_BRANCHES_SHARED)
+        self._destroy = ia.ia_decoder_destroy
         self.handle = ia.ia_decoder_create(hd, md)
         self.device = device
         self._tables = _dev(params.tables, device=device)
@@ -101,9 +102,12 @@ class Decoder:
         return out
 
     def __del__(self):
+        # the destroy function is bound at construction: at interpreter exit
+        # the module globals may already be gone
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
-            ia.ia_decoder_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self.handle = None
 
 
@@ -111,6 +115,7 @@ class HexPlane:
     """HexPlane deformation handle ("4D Gaussian Splatting详解", §3.1-3.2)."""
 
     def __init__(self, params, device="cuda"):
+        self._destroy = ia.ia_hexplane_destroy
         self.handle = ia.ia_hexplane_create(ia.HexPlaneDesc(int(params.res_xyz), int(params.res_t),
                                                             int(params.channels), float(params.aabb)))
         self.device = device
@@ -132,9 +137,12 @@ class HexPlane:
         return out
 
     def __del__(self):
+        # the destroy function is bound at construction: at interpreter exit
+        # the module globals may already be gone
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
-            ia.ia_hexplane_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self.handle = None
 
 

@@ -159,7 +159,14 @@ IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, cons
  *         (SH3 head; out->colors is then not used), opacity[N] =
  *         sigmoid(o_hat); out->means is not written (the input positions
  *         are the means).
- * N = 0 is a no-op.  Errors: INVALID_ARG (null, N < 0, params not set). */
+ * N = 0 is a no-op.  Errors: INVALID_ARG (null, N < 0, params not set).
+ * Asynchronous on stream: all of the call's work, including what it runs on
+ * an internal second stream, starts after everything already queued on
+ * stream, and stream continues only after all of it.  Results are deterministic; with the fp16
+ * decoder the rounding of a Gaussian depends on its index modulo 64 (the
+ * matrix-core column it occupies), so decoding a slice that starts at a
+ * multiple of 64 gives bit for bit the same values as decoding it within a
+ * larger array. */
 IA_API ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t, const ia_gaussians* out,
                     void* stream);
 

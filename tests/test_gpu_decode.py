@@ -200,7 +200,11 @@ def test_chunked_decode_bitwise_equals_slice_decodes():
     xyzt = np.concatenate([rng.normal(0.0, 2.0, (n, 3)), rng.uniform(0.0, 1.0, (n, 1))], 1).astype(np.float32)
     xyzt[::7, 3] = np.round(xyzt[::7, 3] * 149.0) / 149.0  # some times on temporal vertices
     D = Decoder(S.single_decoder())
-    x = cuda(xyzt)
+    x0 = cuda(xyzt)
+    torch.cuda.synchronize()
+    # the positions are produced on the stream right before the call (no host
+    # synchronisation): the decode's internal side stream must wait for them
+    x = x0 * 1.0
     full = {k: v.clone() for k, v in D.decode_xyzt(x).items()}
     for lo, hi in ((0, 1000), (1 << 21, (1 << 21) + 777), (2_800_000 - 64 * 5, 2_800_000 + 999), (n - 5000 & ~63, n)):
         part = D.decode_xyzt(x[lo:hi].contiguous())
