@@ -7,14 +7,14 @@
 //   preprocess  one thread per Gaussian: project, cull, conic, 3-sigma tile
 //               rect, tiles touched; per-block count of visible Gaussians
 //   order       visible Gaussians compacted in index order and radix-sorted
-//               (stable, 8-bit digits) on their 31 depth bits
+//               (stable, four 8-bit digits) on their 31 depth bits
 //   scan        two-level exclusive prefix sum of the tiles touched, in that
 //               depth order; the total entry count stays in device memory
 //   emit        each block spreads its Gaussians' entries over all its
 //               threads: (frame*tiles + tile) << 32 | Gaussian index, in
 //               depth order
 //   sort        stable LSD radix sort of the entries on the tile bits only,
-//               digits of up to 10 bits; per pass: per-block digit
+//               digits of up to 10 bits (two of 9 for 18 tile bits); per pass: per-block digit
 //               histograms, a per-digit scan over blocks, and a stable
 //               scatter ranked by wave ballots.  Because the input is in
 //               (depth, index) order, the result is ordered by the key
@@ -661,8 +661,10 @@ __global__ void __launch_bounds__(kBlock) sort_scan_kernel(SortPass p) {
 // digit.  The tile is then laid out in LDS in digit order and written back
 // with consecutive threads on consecutive destinations, so each digit's items
 // leave as one contiguous run instead of one scattered word per lane.
-// MAXB: the largest digit width the instance handles (sizes its LDS).  The
-// next tile's keys are loaded while the current one is ranked and written.
+// MAXB: the largest digit width the instance handles (sizes its LDS).  All
+// 16 key loads of a thread are issued before the first is used; the grid is
+// one round of resident blocks (three per CU), which the occupancy allows
+// because the next tile's keys are not held in registers.
 // Thread t owns digits [t kDPT, (t + 1) kDPT): it keeps their global
 // destinations in registers and, per tile, turns the per-wave counts into
 // tile-local starts (s_wc) and destination offsets (s_off = global
@@ -872,9 +874,10 @@ constexpr int kStage = 2048;  // entries staged per chunk of a work item (LDS, p
 
 // One work item on one wave.  Coarse entries are taken up to 64 at a time,
 // as many as keep the chunk within kStage entries; lane l clips Gaussian l's
-// tile rect to the region.  For each of the 64 region tiles one ballot over
-// the lanes whose clip covers it gives the tile's count in the chunk and,
-// below each lane, that lane's rank among them (the lanes are in depth
+// tile rect to the region.  Eight ballots over the lanes whose clip covers a
+// region column and eight over those covering a row give, intersected, the
+// lanes covering each of the 64 region tiles: the tile's count in the chunk
+// and, below each lane, that lane's rank among them (the lanes are in depth
 // order), so no per-entry search is needed.
 // WRITE = false: entries per region tile of the item.
 // WRITE = true: the chunk's per-tile counts give each tile a segment of the
