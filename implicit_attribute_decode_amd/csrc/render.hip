@@ -1110,6 +1110,7 @@ template <int PX, bool LAST>
 __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
 #pragma clang fp contract(fast)
     constexpr int kThreads = 256 / PX;
+    static_assert(kRasterBatch % kThreads == 0, "every thread stages the same number of Gaussians");
     __shared__ float4 s_a[kRasterBatch];
     __shared__ float4 s_b[kRasterBatch];
     // third colour channel, at the same 16-byte stride as s_a and s_b so that one
