@@ -78,6 +78,7 @@ HEX_FLOP_PER_GAUSSIAN = 2 * (192 * 256 + 256 * 256 + 256 * 58)  # 259,072
 # paper-scale decoder: four 64 -> 64 -> 64 -> out branches, outs 3 + 4 + 48 + 1
 PAPER_FLOP_PER_GAUSSIAN = 2 * (4 * (64 * 64 + 64 * 64) + 64 * 56)  # 72,704
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MLP_FLOP_PER_GAUSSIAN = 2 * (32 * 64 + 64 * 64 + 64 * 11)  # 13,696: the 32-64-64-11 decoder
 
 
 def secondary(S, Decoder, HexPlane, Renderer, stream, log, only: str | None = None) -> dict:
@@ -351,6 +352,19 @@ def main():
     kernels = {k: {"calls_per_step": round(v[0] / 3, 2), "ms_per_step": round(v[1] / 3, 4)}
                for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
     log("per-kernel (ms/step): " + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
+    # other kernels against their own rooflines, from the same HIP-event times
+    # (algorithmic work per unit as in the design notes; the MLP shares the
+    # chip with the gather it runs beside, and its time goes to GELU's VALU work)
+    per_step_ms = {k: v[1] / 3 for k, v in prof.items()}
+    kernel_rooflines = {}
+    for name, bound, work, peak, unit in (
+            ("preprocess_kernel", "hbm", 108.0 * N / 1e9, HBM_PEAK_GBS, "GB/s"),
+            ("normalize_kernel", "hbm", 32.0 * N / 1e9, HBM_PEAK_GBS, "GB/s"),
+            ("mlp_f16_kernel", "mfma", MLP_FLOP_PER_GAUSSIAN * N / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s")):
+        if per_step_ms.get(name):
+            got = work / (per_step_ms[name] / 1e3)
+            kernel_rooflines[name] = {"bound": bound, "achieved": round(got, 1), "peak": peak, "unit": unit,
+                                      "frac": round(got / peak, 4)}
 
     extra = {}
     if not args.no_extra:
@@ -388,7 +402,7 @@ def main():
         "config": {"workload": f"sequence: {F} frames x {per} Gaussians = {N} (x,y,z,t), 640x360, "
                                "27-camera ring, 16-level fp16 hash (2^19), 32-64-64-11 GELU decoder",
                    "frames": F, "gaussians_per_frame": per, "tile_entries": E,
-                   "kernels": kernels, **extra},
+                   "kernels": kernels, "kernel_rooflines": kernel_rooflines, **extra},
         "roofline": {"kernel": "gather_f16_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": round(GATHER_TRAFFIC_BYTES_PER_LAUNCH) if F == 150 and per == 200_000 else None,
