@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -343,6 +344,30 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
         return st;
     }
     dec->ready = true;
+    return IA_OK;
+}
+
+ia_status ia_decoder_update_params(ia_decoder* dec, const void* tables, const void* const* weights,
+                                   const float* const* biases, void* stream) {
+    if (!dec || !tables || !weights || !biases) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
+    for (int k = 0; k < dec->n_mats; ++k)
+        if (!weights[k] || !biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias pointer");
+    hipStream_t s = (hipStream_t)stream;
+    const size_t tsize = dec->hash.table_dtype == IA_DTYPE_F16 ? 2 : 4;
+    const size_t wsize = dec->mlp.dtype == IA_DTYPE_F16 ? 2 : 4;
+    hipError_t e = hipMemcpyAsync(dec->tables, tables, (size_t)dec->hash.L * dec->lv.T * dec->hash.F * tsize,
+                                  hipMemcpyDeviceToDevice, s);
+    for (int k = 0; e == hipSuccess && k < dec->n_mats; ++k) {
+        e = hipMemcpyAsync(dec->W[k], weights[k], (size_t)dec->mat_out[k] * dec->mat_in[k] * wsize,
+                           hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(dec->b[k], biases[k], 4 * (size_t)dec->mat_out[k], hipMemcpyDeviceToDevice, s);
+    }
+    if (e == hipSuccess && dec->mlp.branches == IA_BRANCHES_PER_ATTRIBUTE)
+        e = ia::launch_branch_pack((const _Float16* const*)dec->W, (const float* const*)dec->b,
+                                   dec->mlp.color == IA_COLOR_SH3, dec->Wt, dec->bpack, s);
+    if (e != hipSuccess) return hip_fail(e, "decoder parameter update");
     return IA_OK;
 }
 
@@ -754,6 +779,58 @@ ia_status ia_l1_loss(const float* image, const float* target, int64_t n, double*
     if (n > 0 && (!image || !target || !grad_image)) return fail(IA_ERR_INVALID_ARG, "null argument");
     hipError_t e = ia::launch_l1_loss(image, target, n, loss, grad_image, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "l1 loss launch");
+    return IA_OK;
+}
+
+ia_status ia_image_loss_workspace_size(int32_t frames, int32_t H, int32_t W, size_t* bytes) {
+    if (!bytes) return fail(IA_ERR_INVALID_ARG, "bytes is null");
+    if (frames <= 0 || H <= 0 || W <= 0) return fail(IA_ERR_INVALID_ARG, "frames, H and W must be > 0");
+    *bytes = ia::image_loss_workspace(frames, H, W);
+    return IA_OK;
+}
+
+ia_status ia_image_loss(const float* image, const float* target, int32_t frames, int32_t H, int32_t W, float lambda,
+                        void* ws, size_t ws_bytes, double* loss, float* grad_image, void* stream) {
+    if (frames <= 0 || H <= 0 || W <= 0) return fail(IA_ERR_INVALID_ARG, "frames, H and W must be > 0");
+    if (!image || !target || !ws || !loss || !grad_image) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (!(lambda >= 0.0f && lambda <= 1.0f)) return fail(IA_ERR_INVALID_ARG, "lambda must be in [0, 1]");
+    if ((int64_t)frames * 3 > 65535) return fail(IA_ERR_INVALID_ARG, "at most 21845 frames per call");
+    if (ws_bytes < ia::image_loss_workspace(frames, H, W))
+        return fail(IA_ERR_WORKSPACE_TOO_SMALL, "image loss workspace too small");
+    if (((uintptr_t)ws & 255) != 0) return fail(IA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    hipError_t e = ia::launch_image_loss(image, target, frames, H, W, lambda, ws, loss, grad_image,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "image loss launch");
+    return IA_OK;
+}
+
+ia_status ia_adam_step(float* param, const float* grad, float* m, float* v, int64_t n, float lr, float beta1,
+                       float beta2, float eps, int32_t step, uint16_t* param_f16, void* stream) {
+    if (n < 0) return fail(IA_ERR_INVALID_ARG, "n must be >= 0");
+    if (n > 0 && (!param || !grad || !m || !v)) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (step < 1) return fail(IA_ERR_INVALID_ARG, "step must be >= 1");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f))
+        return fail(IA_ERR_INVALID_ARG, "betas must be in [0, 1)");
+    if (!(eps >= 0.0f) || !(lr >= 0.0f)) return fail(IA_ERR_INVALID_ARG, "lr and eps must be >= 0");
+    hipError_t e =
+        ia::launch_adam(param, grad, m, v, n, 1, 1, lr, beta1, beta2, eps, step, param_f16, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "adam launch");
+    return IA_OK;
+}
+
+ia_status ia_adam_step_strided(float* param, int32_t param_stride, int32_t dim, const float* grad, float* m, float* v,
+                               int64_t rows, float lr, float beta1, float beta2, float eps, int32_t step,
+                               void* stream) {
+    if (rows < 0 || dim < 1 || param_stride < dim)
+        return fail(IA_ERR_INVALID_ARG, "need rows >= 0 and 1 <= dim <= param_stride");
+    if (rows > 0 && (!param || !grad || !m || !v)) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (step < 1) return fail(IA_ERR_INVALID_ARG, "step must be >= 1");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f))
+        return fail(IA_ERR_INVALID_ARG, "betas must be in [0, 1)");
+    if (!(eps >= 0.0f) || !(lr >= 0.0f)) return fail(IA_ERR_INVALID_ARG, "lr and eps must be >= 0");
+    hipError_t e = ia::launch_adam(param, grad, m, v, rows * dim, dim, param_stride, lr, beta1, beta2, eps, step,
+                                   nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "adam launch");
     return IA_OK;
 }
 

@@ -233,4 +233,15 @@ hipError_t launch_render_backward(const RenderBwdArgs& a, hipStream_t s);
 hipError_t launch_l1_loss(const float* image, const float* target, int64_t n, double* loss, float* grad,
                           hipStream_t s);
 
+// Eq. 12 image loss (L1 + D-SSIM) and its image gradient; workspace bytes for
+// frames x 3 x H x W images.
+size_t image_loss_workspace(int32_t frames, int32_t H, int32_t W);
+hipError_t launch_image_loss(const float* image, const float* target, int32_t frames, int32_t H, int32_t W,
+                             float lambda, void* ws, double* loss, float* grad, hipStream_t s);
+// One bias-corrected Adam step over n fp32 parameters (optional fp16 copy).
+// g, m, v dense [n]; the parameter is rows of `dim` values `stride` floats
+// apart (dim == stride: dense); p16 (dense [n] fp16 copy of the result) or null
+hipError_t launch_adam(float* p, const float* g, float* m, float* v, int64_t n, int32_t dim, int32_t stride,
+                       float lr, float beta1, float beta2, float eps, int32_t step, uint16_t* p16, hipStream_t s);
+
 }  // namespace ia

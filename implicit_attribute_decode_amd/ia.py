@@ -27,10 +27,12 @@ IA_COLOR_RGB, IA_COLOR_SH3 = 0, 1
 IA_BRANCHES_SHARED, IA_BRANCHES_PER_ATTRIBUTE = 0, 1
 
 # Every entry point include/ia.h declares.
-EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decode", "ia_decode_xyzt",
-           "ia_decoder_destroy", "ia_decode_backward", "ia_decode_feature_bytes", "ia_decode_keep", "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform",
-           "ia_hexplane_destroy", "ia_render_workspace_size", "ia_render", "ia_render_set_binning",
-           "ia_render_backward", "ia_l1_loss", "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
+EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decoder_update_params", "ia_decode",
+           "ia_decode_xyzt", "ia_decoder_destroy", "ia_decode_backward", "ia_decode_feature_bytes", "ia_decode_keep",
+           "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform", "ia_hexplane_destroy",
+           "ia_render_workspace_size", "ia_render", "ia_render_set_binning", "ia_render_backward", "ia_l1_loss",
+           "ia_image_loss_workspace_size", "ia_image_loss", "ia_adam_step", "ia_adam_step_strided",
+           "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
 
 
 class IAError(RuntimeError):
@@ -116,6 +118,13 @@ def load(path: str = LIB_PATH):
         L.ia_render_set_binning.argtypes = [C.c_int32]
         L.ia_render_backward.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P, P, P]
         L.ia_l1_loss.argtypes = [P, P, C.c_int64, P, P, P]
+        L.ia_image_loss_workspace_size.argtypes = [C.c_int32, C.c_int32, C.c_int32, P]
+        L.ia_image_loss.argtypes = [P, P, C.c_int32, C.c_int32, C.c_int32, C.c_float, P, C.c_size_t, P, P, P]
+        L.ia_adam_step.argtypes = [P, P, P, P, C.c_int64, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, P,
+                                   P]
+        L.ia_adam_step_strided.argtypes = [P, C.c_int32, C.c_int32, P, P, P, C.c_int64, C.c_float, C.c_float,
+                                           C.c_float, C.c_float, C.c_int32, P]
+        L.ia_decoder_update_params.argtypes = [P, P, P, P, P]
         L.ia_profile_enable.argtypes = [C.c_int32]
         L.ia_profile_report.argtypes = [P, C.c_size_t, P]
         L.ia_profile_reset.argtypes = []
@@ -162,6 +171,13 @@ def ia_decoder_set_params(dec, tables, weights, biases, stream=None):
     W = (C.c_void_p * len(weights))(*[_ptr(w) for w in weights])
     B = (C.c_void_p * len(biases))(*[_ptr(b) for b in biases])
     _check(load().ia_decoder_set_params(dec, _ptr(tables), W, B, 1, _stream(stream)))
+
+
+def ia_decoder_update_params(dec, tables, weights, biases, stream=None):
+    """Stream-ordered device copies of new parameter values into a decoder whose parameters are set."""
+    W = (C.c_void_p * len(weights))(*[_ptr(w) for w in weights])
+    B = (C.c_void_p * len(biases))(*[_ptr(b) for b in biases])
+    _check(load().ia_decoder_update_params(dec, _ptr(tables), W, B, _stream(stream)))
 
 
 def gaussians(means=None, scales=None, quats=None, colors=None, sh=None, opacity=None, means_stride=0,
@@ -271,6 +287,39 @@ def ia_l1_loss(image, target, loss, grad_image, stream=None):
     """loss: device float64 [1]; grad_image like image."""
     _check(load().ia_l1_loss(_ptr(image), _ptr(target), int(image.numel()), _ptr(loss), _ptr(grad_image),
                              _stream(stream)))
+
+
+def ia_image_loss_workspace_size(frames: int, H: int, W: int) -> int:
+    n = C.c_size_t()
+    _check(load().ia_image_loss_workspace_size(int(frames), int(H), int(W), C.byref(n)))
+    return int(n.value)
+
+
+def ia_image_loss(image, target, lam: float, ws, loss, grad_image, stream=None):
+    """image, target: device float [F, 3, H, W]; loss: device float64 [3]."""
+    F, ch, H, W = (int(d) for d in image.shape)
+    if ch != 3:
+        raise ValueError("images must be [frames, 3, H, W]")
+    _check(load().ia_image_loss(_ptr(image), _ptr(target), F, H, W, float(lam), _ptr(ws),
+                                int(ws.numel() * ws.element_size()), _ptr(loss), _ptr(grad_image), _stream(stream)))
+
+
+def ia_adam_step(param, grad, m, v, lr: float, beta1: float, beta2: float, eps: float, step: int, param_f16=None,
+                 stream=None):
+    _check(load().ia_adam_step(_ptr(param), _ptr(grad), _ptr(m), _ptr(v), int(param.numel()), float(lr),
+                               float(beta1), float(beta2), float(eps), int(step), _ptr(param_f16), _stream(stream)))
+
+
+def ia_adam_step_strided(param, grad, m, v, lr: float, beta1: float, beta2: float, eps: float, step: int,
+                         stream=None):
+    """param: a [rows, dim] view whose rows are param.stride(0) floats apart
+    (e.g. xyzt[:, :3]); grad, m, v: dense [rows, dim]."""
+    rows, dim = (int(d) for d in param.shape)
+    if param.stride(1) != 1 or tuple(grad.shape) != (rows, dim) or not grad.is_contiguous():
+        raise ValueError("param must be [rows, dim] with unit column stride; grad, m, v dense [rows, dim]")
+    _check(load().ia_adam_step_strided(_ptr(param), int(param.stride(0)), dim, _ptr(grad), _ptr(m), _ptr(v), rows,
+                                       float(lr), float(beta1), float(beta2), float(eps), int(step),
+                                       _stream(stream)))
 
 
 # ----------------------------------------------------------------- diagnostics

@@ -6,6 +6,8 @@ scenes.py (DecoderParams, HexPlaneParams, Camera).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -101,6 +103,55 @@ class Decoder:
         ia.ia_decode_backward(self.handle, pos, stride, N, float(t or 0.0), up, grad_means, out["pos"], G, features)
         return out
 
+    def update_params(self):
+        """Copy this object's parameter tensors (tables, weights, biases; an
+        optimiser updates them in place) into the handle, stream-ordered."""
+        ia.ia_decoder_update_params(self.handle, self._tables, self._W, self._b)
+
+    # rows of the shared decoder's head block per attribute (RGB head)
+    HEAD_ROWS = {"scale": (0, 3), "rotation": (3, 7), "color": (7, 10), "opacity": (10, 11)}
+
+    def param_groups(self, rates: dict) -> dict:
+        """Adam groups of the shared-trunk RGB decoder ([SPIN] §4 implementation
+        details: the encoder and each attribute's decoder parameters have their
+        own rates).  rates: "encoder", "scale", "rotation", "color", "opacity".
+        The hash tables take the encoder rate, the trunk layers (shared by all
+        attributes) the largest of the attribute rates, and the head's rows and
+        biases of each attribute that attribute's rate.  fp16 tables and
+        weights get fp32 master copies with this object's tensors as their fp16
+        mirrors; fp32 tensors are updated in place."""
+        if self.sh or len(self._W) < 2:
+            raise ValueError("parameter groups are defined for the shared-trunk RGB decoder")
+
+        def master(t):
+            return (t.float(), t.view(torch.int16)) if t.dtype == torch.float16 else (t, None)
+
+        groups = {}
+        p, m = master(self._tables)
+        groups["tables"] = {"param": p, "lr": rates["encoder"], "f16": m}
+        trunk = max(rates[a] for a in self.HEAD_ROWS)
+        for k in range(len(self._W) - 1):
+            p, m = master(self._W[k])
+            groups[f"w{k}"] = {"param": p, "lr": trunk, "f16": m}
+            groups[f"b{k}"] = {"param": self._b[k], "lr": trunk}
+        head, m_head = master(self._W[-1])
+        for a, (r0, r1) in self.HEAD_ROWS.items():
+            groups[f"head_w_{a}"] = {"param": head[r0:r1], "lr": rates[a],
+                                     "f16": None if m_head is None else m_head[r0:r1]}
+            groups[f"head_b_{a}"] = {"param": self._b[-1][r0:r1], "lr": rates[a]}
+        return groups
+
+    def group_grads(self, grads: dict) -> dict:
+        """The gradients of backward() keyed like param_groups()."""
+        out = {"tables": grads["tables"]}
+        for k in range(len(self._W) - 1):
+            out[f"w{k}"] = grads["weights"][k]
+            out[f"b{k}"] = grads["biases"][k]
+        for a, (r0, r1) in self.HEAD_ROWS.items():
+            out[f"head_w_{a}"] = grads["weights"][-1][r0:r1]
+            out[f"head_b_{a}"] = grads["biases"][-1][r0:r1]
+        return out
+
     def __del__(self):
         # the destroy function is bound at construction: at interpreter exit
         # the module globals may already be gone
@@ -159,6 +210,7 @@ class Renderer:
     def __init__(self, device="cuda"):
         self.device = device
         self.ws = None
+        self._loss_ws = None
 
     def workspace(self, N, frames, W, H, max_entries):
         need = ia.ia_render_workspace_size(N, frames, W, H, max_entries)
@@ -236,6 +288,18 @@ class Renderer:
         ia.ia_l1_loss(image.contiguous(), target.contiguous(), loss, grad)
         return loss, grad
 
+    def image_loss(self, image, target, lam: float = 0.2):
+        """Eq. 12 loss of image against target ([F, 3, H, W] device float):
+        (loss [3] float64 on the device = {L, L1, SSIM}, dL/dimage)."""
+        F, _, H, W = (int(d) for d in image.shape)
+        nbytes = ia.ia_image_loss_workspace_size(F, H, W)
+        if self._loss_ws is None or self._loss_ws.numel() < nbytes:
+            self._loss_ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        loss = torch.empty(3, dtype=torch.float64, device=image.device)
+        grad = torch.empty_like(image)
+        ia.ia_image_loss(image.contiguous(), target.contiguous(), lam, self._loss_ws, loss, grad)
+        return loss, grad
+
     @staticmethod
     def count_entries(res: dict) -> int:
         return int(res["n_entries"].item())
@@ -249,3 +313,50 @@ class Renderer:
         t = ws[off:off + nbytes].view(dt)
         return t.view(count, width) if width > 1 else t
 
+
+
+def lr_at(step: int, base: float, warmup: int, total: int, final: float = 1e-7) -> float:
+    """Learning rate at `step` (0-based): linear warm-up over `warmup` steps,
+    then cosine decay from base to `final` at `total` ([SPIN] §4
+    implementation details)."""
+    if warmup > 0 and step < warmup:
+        return base * (step + 1) / warmup
+    span = max(total - warmup, 1)
+    frac = min(max(step - warmup, 0), span) / span
+    return final + 0.5 * (base - final) * (1.0 + math.cos(math.pi * frac))
+
+
+class Adam:
+    """Adam over named parameter groups, each an fp32 device tensor with its
+    own base learning rate ([SPIN] §4 implementation details: per-group rates,
+    linear warm-up then cosine decay to 1e-7).  A group may carry an fp16
+    mirror (e.g. the decoder's hash table) that every step refreshes, and its
+    parameter may be a [rows, dim] view with rows further apart than dim (the
+    x, y, z of xyzt positions).  Every update runs in ia_adam_step or
+    ia_adam_step_strided."""
+
+    def __init__(self, groups: dict, warmup: int, total: int, beta1: float = 0.9, beta2: float = 0.999,
+                 eps: float = 1e-15):
+        self.groups = groups  # name -> {"param": fp32 tensor, "lr": base, optional "f16": tensor}
+        self.state = {k: (torch.zeros(g["param"].shape, device=g["param"].device),
+                          torch.zeros(g["param"].shape, device=g["param"].device)) for k, g in groups.items()}
+        self.warmup, self.total = warmup, total
+        self.beta1, self.beta2, self.eps = beta1, beta2, eps
+        self.t = 0
+
+    def step(self, grads: dict):
+        """One update of every group that has a gradient in `grads` (name -> tensor)."""
+        self.t += 1
+        for name, g in self.groups.items():
+            grad = grads.get(name)
+            if grad is None:
+                continue
+            m, v = self.state[name]
+            lr = lr_at(self.t - 1, g["lr"], self.warmup, self.total)
+            p = g["param"]
+            if p.is_contiguous():
+                ia.ia_adam_step(p, grad.contiguous(), m, v, lr, self.beta1, self.beta2, self.eps, self.t, g.get("f16"))
+            else:
+                if g.get("f16") is not None:
+                    raise ValueError(f"group {name}: an fp16 mirror needs a contiguous parameter")
+                ia.ia_adam_step_strided(p, grad.contiguous(), m, v, lr, self.beta1, self.beta2, self.eps, self.t)

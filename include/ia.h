@@ -152,6 +152,14 @@ IA_API ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* 
 IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
                                 const float* const* biases, int32_t params_on_device, void* stream);
 
+/* Overwrite the parameter values of a decoder whose parameters are set, from
+ * device memory in the layouts of ia_decoder_set_params, with copies enqueued
+ * on `stream` (no allocation, no synchronisation): an optimiser's update
+ * between training steps.  Decodes and backwards enqueued later on `stream`
+ * see the new values.  Errors: INVALID_ARG (null, parameters not set), DEVICE. */
+IA_API ia_status ia_decoder_update_params(ia_decoder* dec, const void* tables, const void* const* weights,
+                                          const float* const* biases, void* stream);
+
 /* Decode N Gaussians at one time t ([SPIN] §3.3 Eq. 7-11):
  *   xyz : device [N,3] positions mu
  *   out : device scales[N,3] = exp(min(s_hat,20)), quats[N,4] = r_hat/|r_hat|,
@@ -365,6 +373,47 @@ IA_API ia_status ia_render_backward(const ia_gaussians* g, const int64_t* frame_
  * floats of device memory.  Errors: INVALID_ARG, DEVICE. */
 IA_API ia_status ia_l1_loss(const float* image, const float* target, int64_t n, double* loss, float* grad_image,
                             void* stream);
+
+/* The training objective of [SPIN] §3.3 Eq. 12 on frames x 3 x H x W images
+ * (device, planar, values nominally in [0, 1]):
+ *   L = (1 - lambda) L1 + lambda (1 - SSIM),
+ * L1 the mean absolute difference and SSIM the structural similarity of
+ * Wang et al. (2004), the metric the pages cite: 11 x 11 Gaussian window of
+ * standard deviation 1.5, C1 = 0.01^2, C2 = 0.03^2, per colour channel,
+ * window taps outside the image counted as zero, averaged over every pixel,
+ * channel and frame.  The pages set lambda = 0.2 (after 3DGS).
+ *   loss       : device double[3], overwritten: {L, L1, SSIM}
+ *   grad_image : device float, like image: dL/dimage (the L1 part 0 where
+ *                image == target)
+ *   ws         : caller-owned device workspace of ia_image_loss_workspace_size
+ *                bytes, 256-byte aligned; contents undefined between calls.
+ * Asynchronous on stream; calls on one workspace must not overlap.
+ * Errors: INVALID_ARG (null, sizes <= 0, lambda outside [0, 1], more than
+ * 21845 frames), WORKSPACE_TOO_SMALL, DEVICE. */
+IA_API ia_status ia_image_loss_workspace_size(int32_t frames, int32_t H, int32_t W, size_t* bytes);
+IA_API ia_status ia_image_loss(const float* image, const float* target, int32_t frames, int32_t H, int32_t W,
+                               float lambda, void* ws, size_t ws_bytes, double* loss, float* grad_image,
+                               void* stream);
+
+/* One Adam step (Kingma & Ba 2015; the optimiser of [SPIN] §4 implementation
+ * details) over n fp32 parameters, in place, step >= 1:
+ *   m = beta1 m + (1 - beta1) g,  v = beta2 v + (1 - beta2) g^2,
+ *   param -= lr (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps).
+ * param, grad, m, v are device float[n] (m and v zero before the first step);
+ * param_f16 (nullable) receives the updated values rounded to fp16 (RNE), e.g.
+ * for an fp16 hash table.  Per-group learning rates and their schedule are
+ * the caller's (one call per group).  Errors: INVALID_ARG, DEVICE. */
+IA_API ia_status ia_adam_step(float* param, const float* grad, float* m, float* v, int64_t n, float lr, float beta1,
+                              float beta2, float eps, int32_t step, uint16_t* param_f16, void* stream);
+
+/* ia_adam_step for a parameter laid out as rows of `dim` values that sit
+ * `param_stride` floats apart (dim <= param_stride), e.g. the x, y, z of
+ * positions stored as [rows][4] (x, y, z, t), leaving the other values of a
+ * row untouched.  grad, m, v are dense device float[rows][dim].
+ * Errors: INVALID_ARG (rows < 0, dim < 1, param_stride < dim, ...), DEVICE. */
+IA_API ia_status ia_adam_step_strided(float* param, int32_t param_stride, int32_t dim, const float* grad, float* m,
+                                      float* v, int64_t rows, float lr, float beta1, float beta2, float eps,
+                                      int32_t step, void* stream);
 
 /* How ia_render turns depth-ordered Gaussians into per-tile lists.  Both give
  * the same lists; they differ in speed.

@@ -1,0 +1,237 @@
+"""GPU parity of the training objective (Eq. 12: L1 + D-SSIM and its image
+gradient) and of the Adam step against the fp64 oracle (oracle/train.py),
+through the C ABI.
+
+Tolerances, from the arithmetic: the kernels form each window moment as an
+fp32 sum of 121 products of values in [0, 1] (relative error of a moment
+~1e-7, a few 1e-8 absolute) and S from differences of moments, so a pixel's
+S carries an absolute error of about 1e-7 / B2 with B2 >= C2 = 9e-4 in flat
+windows (~1e-4) and ~1e-6 in textured ones; the mean over many pixels is far
+tighter.  Bars: SSIM mean 2e-6 absolute on textured images (1e-4 on images
+with flat regions); L1 1e-12 relative (exact differences summed in double);
+the gradient 2e-5 of its largest magnitude on textured images, 2e-3 with flat
+windows, where C2 alone holds the denominators up (its D-SSIM part is the
+window sum of S's derivatives, each carrying S's relative error).  Adam: fp32 moments
+and update against fp64, 1e-5 relative over three steps; the fp16 copy is
+bit-exactly the RNE rounding of the fp32 parameter.  The C ABI takes the
+hyperparameters as fp32, so the oracle is given the same fp32 values (0.999 in
+fp32 moves 1 - beta2 by 1.3e-5 relative, more than the arithmetic's error).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import train as T
+from implicit_attribute_decode_amd import ia, scenes as S
+from implicit_attribute_decode_amd.pipeline import Adam, Decoder, Renderer, lr_at
+
+from gpu_util import cuda, host, say
+
+pytestmark = pytest.mark.gpu
+
+B1, B2, EPS = (float(np.float32(v)) for v in (0.9, 0.999, 1e-15))
+
+
+def f32(v):
+    return float(np.float32(v))
+
+
+def _ulps(p, k):
+    """k fp32 units in the last place of |p|: the parameter is rounded to fp32
+    after every step."""
+    return k * np.spacing(np.abs(p).astype(np.float32)).astype(np.float64)
+
+
+def _loss(x, y, lam=0.2):
+    R = Renderer()
+    loss, grad = R.image_loss(cuda(x), cuda(y), lam)
+    torch.cuda.synchronize()
+    return host(loss), host(grad).astype(np.float64)
+
+
+@pytest.mark.parametrize("shape", [(1, 3, 16, 16), (2, 3, 37, 41), (1, 3, 5, 70), (3, 3, 100, 64)])
+def test_image_loss_matches_oracle_textured(shape):
+    rng = np.random.default_rng(sum(shape))
+    x = rng.uniform(0, 1, shape).astype(np.float32)
+    y = np.clip(x + rng.normal(0, 0.2, shape), 0, 1).astype(np.float32)
+    g_loss, g_grad = _loss(x, y)
+    o = T.image_loss(x, y)
+    assert abs(g_loss[1] - o["l1"]) <= 1e-12 * o["l1"]
+    assert abs(g_loss[2] - o["ssim"]) <= 2e-6
+    assert abs(g_loss[0] - o["loss"]) <= 1e-6
+    err = np.abs(g_grad - o["grad"]).max()
+    say(f"{shape}: ssim {g_loss[2]:.6f} vs {o['ssim']:.6f}, grad err {err:.2e} of {np.abs(o['grad']).max():.2e}")
+    assert err <= 2e-5 * np.abs(o["grad"]).max()
+
+
+def test_image_loss_flat_regions_and_identical_images():
+    """Flat patches (zero variance windows) and an image against itself."""
+    rng = np.random.default_rng(9)
+    x = np.full((1, 3, 48, 48), 0.5, np.float32)
+    x[:, :, 20:, 24:] = rng.uniform(0, 1, (1, 3, 28, 24)).astype(np.float32)
+    y = x.copy()
+    y[:, 1, :10, :10] = 0.25
+    g_loss, g_grad = _loss(x, y)
+    o = T.image_loss(x, y)
+    err = np.abs(g_grad - o["grad"]).max()
+    say(f"flat: ssim {g_loss[2]:.7f} vs {o['ssim']:.7f}, grad err {err:.2e} of {np.abs(o['grad']).max():.2e}")
+    assert abs(g_loss[2] - o["ssim"]) <= 1e-4
+    assert err <= 2e-3 * np.abs(o["grad"]).max()
+    same_loss, same_grad = _loss(x, x)
+    assert same_loss[1] == 0.0 and abs(same_loss[2] - 1.0) <= 1e-5
+    assert np.abs(same_grad).max() <= 1e-6 * (1.0 / x.size)
+
+
+def test_image_loss_lambda_zero_is_l1():
+    rng = np.random.default_rng(4)
+    x = rng.uniform(0, 1, (2, 3, 20, 30)).astype(np.float32)
+    y = rng.uniform(0, 1, (2, 3, 20, 30)).astype(np.float32)
+    g_loss, g_grad = _loss(x, y, lam=0.0)
+    R = Renderer()
+    l1, l1_grad = R.l1_loss(cuda(x), cuda(y))
+    torch.cuda.synchronize()
+    assert abs(g_loss[0] - host(l1)[0]) <= 1e-12
+    assert np.array_equal(np.sign(g_grad), np.sign(host(l1_grad)))
+    assert np.abs(g_grad - host(l1_grad)).max() <= 1e-7 / x.size
+
+
+def test_image_loss_rejects_bad_arguments():
+    x = torch.zeros((1, 3, 8, 8), device="cuda")
+    ws = torch.empty(ia.ia_image_loss_workspace_size(1, 8, 8), dtype=torch.uint8, device="cuda")
+    loss = torch.empty(3, dtype=torch.float64, device="cuda")
+    g = torch.empty_like(x)
+    with pytest.raises(ia.IAError) as e:
+        ia.ia_image_loss(x, x, 1.5, ws, loss, g)
+    assert e.value.status == ia.IA_ERR_INVALID_ARG
+    with pytest.raises(ia.IAError) as e:
+        ia.ia_image_loss(x, x, 0.2, ws[: ws.numel() // 2], loss, g)
+    assert e.value.status == ia.IA_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("n", [1, 1000, 257 * 1021])
+def test_adam_matches_oracle_over_three_steps(n):
+    rng = np.random.default_rng(n)
+    p = rng.normal(0, 1, n).astype(np.float32)
+    P, M, V = cuda(p), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    p16 = torch.empty(n, dtype=torch.int16, device="cuda")
+    op, om, ov = p.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in range(1, 4):
+        g = rng.normal(0, 1e-2, n).astype(np.float32)
+        ia.ia_adam_step(P, cuda(g), M, V, 3e-4, 0.9, 0.999, 1e-15, t, p16)
+        op, om, ov = T.adam_step(op, g, om, ov, f32(3e-4), B1, B2, EPS, t)
+    torch.cuda.synchronize()
+    gp = host(P).astype(np.float64)
+    assert np.all(np.abs(gp - op) <= 1e-5 * 3 * 3e-4 + _ulps(op, 3))
+    # m sums gradients of either sign: its error is relative to their scale, not to m
+    assert np.allclose(host(M), om, rtol=1e-5, atol=1e-6 * np.abs(om).max())
+    assert np.allclose(host(V), ov, rtol=1e-5, atol=1e-6 * np.abs(ov).max())
+    assert np.array_equal(host(p16).view(np.uint16), host(P).astype(np.float16).view(np.uint16))
+
+
+def test_adam_groups_follow_the_schedule():
+    """The pipeline's per-group optimiser applies lr_at(t - 1) to every group."""
+    rng = np.random.default_rng(5)
+    a = rng.normal(0, 1, 500).astype(np.float32)
+    b = rng.normal(0, 1, 300).astype(np.float32)
+    A, B = cuda(a), cuda(b)
+    opt = Adam({"a": {"param": A, "lr": 8e-3}, "b": {"param": B, "lr": 3e-5}}, warmup=2, total=10)
+    oa, ob = a.astype(np.float64), b.astype(np.float64)
+    sa = (np.zeros(500), np.zeros(500))
+    sb = (np.zeros(300), np.zeros(300))
+    for t in range(1, 5):
+        ga = rng.normal(0, 1, 500).astype(np.float32)
+        gb = rng.normal(0, 1, 300).astype(np.float32)
+        opt.step({"a": cuda(ga), "b": cuda(gb)})
+        oa, *sa = T.adam_step(oa, ga, sa[0], sa[1], f32(T.lr_schedule(t - 1, 8e-3, 2, 10)), B1, B2, EPS, t)
+        ob, *sb = T.adam_step(ob, gb, sb[0], sb[1], f32(T.lr_schedule(t - 1, 3e-5, 2, 10)), B1, B2, EPS, t)
+        assert abs(lr_at(t - 1, 8e-3, 2, 10) - T.lr_schedule(t - 1, 8e-3, 2, 10)) <= 1e-18
+    torch.cuda.synchronize()
+    assert np.all(np.abs(host(A) - oa) <= 1e-5 * 4 * 8e-3 + _ulps(oa, 4))
+    assert np.all(np.abs(host(B) - ob) <= 1e-5 * 4 * 3e-5 + _ulps(ob, 4))
+
+
+def test_adam_strided_positions_equal_the_dense_step_and_keep_t():
+    """x, y, z of [N, 4] xyzt rows updated in place: bit-identical to the dense
+    step on a copy of those columns, the t column untouched."""
+    rng = np.random.default_rng(11)
+    n = 100_003
+    xyzt = rng.normal(0, 1, (n, 4)).astype(np.float32)
+    X, Dn = cuda(xyzt), cuda(xyzt[:, :3].copy())
+    m1, v1, m2, v2 = (torch.zeros((n, 3), device="cuda") for _ in range(4))
+    for t in range(1, 4):
+        G = cuda(rng.normal(0, 1e-3, (n, 3)).astype(np.float32))
+        ia.ia_adam_step_strided(X[:, :3], G, m1, v1, 1.6e-4, 0.9, 0.999, 1e-15, t)
+        ia.ia_adam_step(Dn, G, m2, v2, 1.6e-4, 0.9, 0.999, 1e-15, t)
+    torch.cuda.synchronize()
+    hx = host(X)
+    assert np.array_equal(hx[:, 3].view(np.uint32), xyzt[:, 3].view(np.uint32))
+    assert np.array_equal(hx[:, :3], host(Dn)) and not np.array_equal(hx[:, :3], xyzt[:, :3])
+    assert torch.equal(m1, m2) and torch.equal(v1, v2)
+    lib = ia.load()
+    bad = lib.ia_adam_step_strided(ia._ptr(X), 4, 5, ia._ptr(G), ia._ptr(m1), ia._ptr(v1), n, 1e-3, 0.9, 0.999,
+                                   1e-15, 1, None)
+    assert bad == ia.IA_ERR_INVALID_ARG
+
+
+def test_decoder_update_params_equals_a_fresh_decoder():
+    """After update_params the handle decodes exactly as a decoder created
+    with the new values."""
+    D, D1 = Decoder(S.single_decoder()), Decoder(S.single_decoder(seed=3))
+    rng = np.random.default_rng(12)
+    n = 50_000
+    pos = np.concatenate([S.shell_points(rng, n, 1.0), rng.uniform(0, 1, (n, 1))], 1).astype(np.float32)
+    P = cuda(pos)
+    before = D.decode_xyzt(P)
+    D._tables.copy_(D1._tables)
+    for k in range(len(D._W)):
+        D._W[k].copy_(D1._W[k])
+        D._b[k].copy_(D1._b[k])
+    D.update_params()
+    got, want = D.decode_xyzt(P), D1.decode_xyzt(P)
+    torch.cuda.synchronize()
+    for k in want:
+        assert torch.equal(got[k], want[k]), k
+    assert not torch.equal(before["colors"], want["colors"])
+
+
+RATES = {"encoder": 8e-3, "color": 1e-3, "scale": 3e-4, "rotation": 3e-5, "opacity": 8e-4}
+
+
+def test_training_steps_lower_the_loss_and_keep_the_mirrors():
+    """Decode (kept encoding) -> render -> Eq. 12 loss -> render backward ->
+    decode backward -> Adam over the decoder groups and the positions ->
+    update_params, ten times: the loss falls, t stays, the fp16 tables are
+    the rounding of their fp32 masters."""
+    rng = np.random.default_rng(13)
+    n = 40_000
+    D = Decoder(S.single_decoder())
+    pos = np.concatenate([S.shell_points(rng, n, 1.0), np.full((n, 1), 0.4)], 1).astype(np.float32)
+    xyzt = cuda(pos)
+    groups = D.param_groups(RATES)
+    groups["positions"] = {"param": xyzt[:, :3], "lr": 1.6e-4}
+    opt = Adam(groups, warmup=1, total=1000)
+    R = Renderer()
+    cams = [S.ring_camera(0, W=200, H=150, fx=180.0, fy=180.0)]
+    target = torch.full((1, 3, 150, 200), 0.5, device="cuda")
+    cap = 64 * n
+    losses = []
+    for it in range(10):
+        attrs, feats = D.decode_keep(xyzt)
+        g = dict(attrs, means=xyzt[:, :3])
+        r = R.render(g, [0, n], cams, cap, aux=True, keys=False)
+        loss, gimg = R.image_loss(r["image"], target)
+        ga = R.backward(g, [0, n], cams, cap, r, gimg)
+        dg = D.backward(xyzt, ga, grad_means=ga["means"], features=feats)
+        grads = D.group_grads(dg)
+        grads["positions"] = dg["pos"]
+        opt.step(grads)
+        D.update_params()
+        losses.append(float(host(loss)[0]))
+        assert int(host(r["overflow"])[0]) == 0
+    torch.cuda.synchronize()
+    say("losses", [round(v, 6) for v in losses])
+    assert np.all(np.isfinite(losses)) and losses[-1] < losses[0]
+    assert np.array_equal(host(xyzt)[:, 3], pos[:, 3])
+    tab = groups["tables"]
+    assert torch.equal(tab["f16"].view(torch.float16), tab["param"].half())
+    assert not np.array_equal(host(xyzt)[:, :3], pos[:, :3])
