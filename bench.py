@@ -225,13 +225,66 @@ def _stress(S, Decoder, Renderer, stream) -> dict:
     D.backward(xyzt, dense, features=feats)
     ms_dense = timed(lambda: D.backward(xyzt, dense, features=feats), 1, stream)
     nz = int((ga["opacity"] != 0).sum().item())
+    full = _train_full(S, Decoder, Renderer, stream, xyzt, fo, cams, target)
     return {"frames": len(cams), "gaussians": g.n, "tile_entries": E, "render_ms": round(ms_r, 3),
             "render_fps": round(len(cams) / (ms_r / 1e3), 2), "decode_8M_ms": round(ms_d, 3),
             "decode_keep_8M_ms": round(ms_dk, 3), "render_fwd_l1_bwd_ms": round(ms_rt, 3),
             "decode_bwd_8M_ms": round(ms_db, 3), "train_step_ms": round(ms_dk + ms_rt + ms_db, 3),
             "gaussians_with_gradient": nz, "decode_bwd_8M_all_nonzero_ms": round(ms_dense, 3),
             "render_kernels_ms": stress_kernels, "render_train_kernels_ms": bwd_kernels,
-            "decode_bwd_kernels_ms": dbwd_kernels}
+            "decode_bwd_kernels_ms": dbwd_kernels, "train_full": full}
+
+
+# [SPIN] §4 implementation details: encoder and per-attribute decoder rates;
+# positions at the 3DGS position rate; 40K iterations
+TRAIN_RATES = {"encoder": 8e-3, "color": 1e-3, "scale": 3e-4, "rotation": 3e-5, "opacity": 8e-4}
+TRAIN_POSITION_LR = 1.6e-4
+TRAIN_ITERS = 40_000
+TRAIN_WARMUP = 1_000
+
+
+def _train_full(S, Decoder, Renderer, stream, xyzt, fo, cams, target) -> dict:
+    """One whole training step on the Stress batch, everything the step
+    does inside the timed region: decode of the 8M positions (keeping the
+    encoding), render of the decoded Gaussians, the Eq. 12 loss (L1 + D-SSIM)
+    and its image gradient, render backward, decode backward, Adam over the
+    decoder's groups and the positions, and the decoder parameter update."""
+    from implicit_attribute_decode_amd.pipeline import Adam
+
+    D = Decoder(S.single_decoder())
+    xt = xyzt.clone()
+    groups = D.param_groups(TRAIN_RATES)
+    groups["positions"] = {"param": xt[:, :3], "lr": TRAIN_POSITION_LR}
+    opt = Adam(groups, warmup=TRAIN_WARMUP, total=TRAIN_ITERS)
+    R = Renderer()
+    attrs, feats = D.decode_keep(xt)
+    g = dict(attrs, means=xt[:, :3])
+    n = int(xt.shape[0])
+    E = Renderer.count_entries(R.render(g, fo, cams, 4 * n, aux=True, keys=False))
+    cap = E + E // 4 + 4096  # the positions move between steps
+    res = R.render(g, fo, cams, cap, aux=True, keys=False)
+
+    def step():
+        D.decode_keep(xt, out=attrs, features=feats)
+        r = R.render(g, fo, cams, cap, aux=True, keys=False, out=res)
+        loss, gimg = R.image_loss(r["image"], target)
+        ga = R.backward(g, fo, cams, cap, r, gimg)
+        dg = D.backward(xt, ga, grad_means=ga["means"], features=feats)
+        grads = D.group_grads(dg)
+        grads["positions"] = dg["pos"]
+        opt.step(grads)
+        D.update_params()
+        return loss
+
+    first = step()
+    l0 = [float(v) for v in first.cpu()]
+    ms = timed(step, 3, stream)
+    kernels = profiled(step, 1)
+    last = [float(v) for v in step().cpu()]
+    overflow = int(res["overflow"].item())
+    return {"tile_entries": E, "step_ms": round(ms, 3), "overflow": overflow,
+            "loss_first": [round(v, 6) for v in l0], "loss_after": [round(v, 6) for v in last],
+            "steps_taken": opt.t, "kernels_ms": kernels}
 
 
 def profiled(fn, reps):

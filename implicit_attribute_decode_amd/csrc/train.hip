@@ -13,8 +13,9 @@
 // sums of the five moments (x, y, x^2, y^2, xy) over the 26 rows are formed
 // in LDS, and each thread sums 11 of them vertically: mu_x, mu_y, E[x^2],
 // E[y^2], E[xy] of its pixel.  It writes S's derivatives with respect to
-// mu_x, E[x^2] and E[xy] (the only moments that depend on x) and adds the
-// block's sums of S and |x - y| to the loss.
+// mu_x, E[x^2] and E[xy] (the only moments that depend on x) and the block's
+// sums of S and |x - y| (one pair per block; loss_finish_kernel adds them in
+// a fixed order, so the loss is the same on every run).
 // ssim_bwd_kernel: the same tiling applied to the three derivative maps (the
 // window is symmetric, so its adjoint is the same zero-padded window sum),
 // combined into dL/dx = (1 - lambda) sign(x - y) / n
@@ -47,7 +48,7 @@ struct LossArgs {
     double inv_n;
     float* d;       // [3][planes][H][W]: dS/dmu_x, dS/dE[x^2], dS/dE[xy]
     size_t plane_stride;  // floats between the three derivative maps
-    double* sums;   // [0] sum S, [1] sum |x - y|
+    double2* part;  // per block: sum S, sum |x - y|
     float* grad;
 };
 
@@ -123,8 +124,9 @@ __global__ void __launch_bounds__(256) ssim_fwd_kernel(LossArgs a) {
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        atomicAdd(&a.sums[0], (s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]));
-        atomicAdd(&a.sums[1], (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]));
+        const size_t b = ((size_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+        a.part[b] = make_double2((s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]),
+                                 (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]));
     }
 }
 
@@ -168,16 +170,34 @@ __global__ void __launch_bounds__(256) ssim_bwd_kernel(LossArgs a) {
     a.grad[i] = (1.0f - a.lambda) * sgn * inv_n - a.lambda * dssim;
 }
 
+// One block of kFinish threads: the per-block sums added in a fixed order;
 // loss[0] = (1 - lambda) L1 + lambda (1 - SSIM), loss[1] = L1, loss[2] = SSIM
-__global__ void loss_finish_kernel(const double* sums, double inv_n, double lambda, double* loss) {
-    const double ssim = sums[0] * inv_n, l1 = sums[1] * inv_n;
-    loss[0] = (1.0 - lambda) * l1 + lambda * (1.0 - ssim);
-    loss[1] = l1;
-    loss[2] = ssim;
-}
-
-__global__ void zero2_kernel(double* p) {
-    if (threadIdx.x < 2) p[threadIdx.x] = 0.0;
+constexpr int kFinish = 1024;
+__global__ void __launch_bounds__(kFinish) loss_finish_kernel(const double2* part, int64_t nblocks, double inv_n,
+                                                              double lambda, double* loss) {
+    __shared__ double s_s[kFinish], s_l[kFinish];
+    double ss = 0.0, sl = 0.0;
+    for (int64_t b = threadIdx.x; b < nblocks; b += kFinish) {
+        const double2 v = part[b];
+        ss += v.x;
+        sl += v.y;
+    }
+    s_s[threadIdx.x] = ss;
+    s_l[threadIdx.x] = sl;
+    __syncthreads();
+    for (int w = kFinish / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            s_s[threadIdx.x] += s_s[threadIdx.x + w];
+            s_l[threadIdx.x] += s_l[threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double ssim = s_s[0] * inv_n, l1 = s_l[0] * inv_n;
+        loss[0] = (1.0 - lambda) * l1 + lambda * (1.0 - ssim);
+        loss[1] = l1;
+        loss[2] = ssim;
+    }
 }
 
 // p -= step_size * m / (sqrt(v * v_scale) + eps) after the moment updates;
@@ -207,23 +227,26 @@ __global__ void __launch_bounds__(256) adam_kernel(float* p, const float* g, flo
 
 }  // namespace
 
+// [3][planes][H][W] float derivative maps, then one double2 per SSIM block
 size_t image_loss_workspace(int32_t frames, int32_t H, int32_t W) {
-    return (size_t)3 * frames * 3 * (size_t)H * W * sizeof(float) + 256;
+    const size_t maps = (size_t)3 * frames * 3 * (size_t)H * W * sizeof(float);
+    const size_t blocks = (size_t)((W + kT - 1) / kT) * ((H + kT - 1) / kT) * frames * 3;
+    return ((maps + 255) & ~(size_t)255) + blocks * sizeof(double2);
 }
 
 hipError_t launch_image_loss(const float* image, const float* target, int32_t frames, int32_t H, int32_t W,
                              float lambda, void* ws, double* loss, float* grad, hipStream_t s) {
     const int planes = frames * 3;
     const size_t n = (size_t)planes * H * W;
-    double* sums = reinterpret_cast<double*>(ws);
-    LossArgs a{image, target, H, W, lambda, 1.0 / (double)n, reinterpret_cast<float*>((char*)ws + 256), n, sums,
-               grad};
+    const size_t maps = ((3 * n * sizeof(float)) + 255) & ~(size_t)255;
+    double2* part = reinterpret_cast<double2*>((char*)ws + maps);
+    LossArgs a{image, target, H, W, lambda, 1.0 / (double)n, reinterpret_cast<float*>(ws), n, part, grad};
     const dim3 grid((W + kT - 1) / kT, (H + kT - 1) / kT, planes);
-    IA_LAUNCH("loss_zero_kernel", zero2_kernel, dim3(1), dim3(64), 0, s, sums);
+    const int64_t nblocks = (int64_t)grid.x * grid.y * grid.z;
     IA_LAUNCH("ssim_fwd_kernel", ssim_fwd_kernel, grid, dim3(256), 0, s, a);
     IA_LAUNCH("ssim_bwd_kernel", ssim_bwd_kernel, grid, dim3(256), 0, s, a);
-    IA_LAUNCH("loss_finish_kernel", loss_finish_kernel, dim3(1), dim3(1), 0, s, sums, 1.0 / (double)n,
-              (double)lambda, loss);
+    IA_LAUNCH("loss_finish_kernel", loss_finish_kernel, dim3(1), dim3(kFinish), 0, s, part, nblocks,
+              1.0 / (double)n, (double)lambda, loss);
     return hipGetLastError();
 }
 

@@ -382,7 +382,8 @@ IA_API ia_status ia_l1_loss(const float* image, const float* target, int64_t n, 
  * standard deviation 1.5, C1 = 0.01^2, C2 = 0.03^2, per colour channel,
  * window taps outside the image counted as zero, averaged over every pixel,
  * channel and frame.  The pages set lambda = 0.2 (after 3DGS).
- *   loss       : device double[3], overwritten: {L, L1, SSIM}
+ *   loss       : device double[3], overwritten: {L, L1, SSIM}; the per-pixel
+ *                terms are summed in a fixed order (the same on every run)
  *   grad_image : device float, like image: dL/dimage (the L1 part 0 where
  *                image == target)
  *   ws         : caller-owned device workspace of ia_image_loss_workspace_size

@@ -82,6 +82,18 @@ def test_image_loss_flat_regions_and_identical_images():
     assert np.abs(same_grad).max() <= 1e-6 * (1.0 / x.size)
 
 
+def test_image_loss_is_the_same_on_every_run():
+    """The per-pixel terms are summed in a fixed order: repeated calls agree bit for bit."""
+    rng = np.random.default_rng(21)
+    x = cuda(rng.uniform(0, 1, (2, 3, 130, 170)).astype(np.float32))
+    y = cuda(rng.uniform(0, 1, (2, 3, 130, 170)).astype(np.float32))
+    R = Renderer()
+    runs = [R.image_loss(x, y) for _ in range(3)]
+    torch.cuda.synchronize()
+    for loss, grad in runs[1:]:
+        assert torch.equal(loss, runs[0][0]) and torch.equal(grad, runs[0][1])
+
+
 def test_image_loss_lambda_zero_is_l1():
     rng = np.random.default_rng(4)
     x = rng.uniform(0, 1, (2, 3, 20, 30)).astype(np.float32)
