@@ -70,6 +70,7 @@ struct ia_decoder {
     float* bpack = nullptr;     // per-attribute fp16 decoder: biases packed per branch
     uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [2][chunk] float4
     float* bwd_partial = nullptr;  // fp16 path: per-wave weight-gradient partials of the backward
+    void* bwd_sort = nullptr;      // fp16 path: the backward's spatial ordering of its active list
     hipStream_t side = nullptr;  // fp16 path: MLP stream overlapping the next chunk's gather
     hipEvent_t ev_gather[2] = {nullptr, nullptr};
     hipEvent_t ev_mlp[2] = {nullptr, nullptr};
@@ -96,6 +97,8 @@ void free_decoder_params(ia_decoder* d) {
     d->zbuf = nullptr;
     if (d->bwd_partial) (void)hipFree(d->bwd_partial);
     d->bwd_partial = nullptr;
+    if (d->bwd_sort) (void)hipFree(d->bwd_sort);
+    d->bwd_sort = nullptr;
     for (int k = 0; k < 2; ++k) {
         if (d->ev_gather[k]) (void)hipEventDestroy(d->ev_gather[k]);
         if (d->ev_mlp[k]) (void)hipEventDestroy(d->ev_mlp[k]);
@@ -328,6 +331,7 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
         if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
         if (st == IA_OK) {
             e = hipMalloc(&dec->bwd_partial, sizeof(float) * (size_t)ia::kDecodeBwdPartialFloats);
+            if (e == hipSuccess) e = hipMalloc(&dec->bwd_sort, ia::decode_bwd_sort_bytes());
             if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
         }
         // a side stream (default priority) and events for the MLP / gather overlap
@@ -435,6 +439,7 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
         b.g_b[k] = grads->biases[k];
     }
     b.partial = dec->bwd_partial;
+    b.sort = dec->bwd_sort;
     hipError_t e = ia::launch_decode_backward(b, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode backward launch");
     return IA_OK;

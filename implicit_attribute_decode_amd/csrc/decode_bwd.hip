@@ -6,9 +6,13 @@
 //   features   the encoding z kept by the forward decode, or recomputed by the
 //              forward's normalise + level-major gather kernels (fp16, as the
 //              forward fed the MLP); x~ is renormalised either way.
-//   compaction the Gaussians whose upstream gradient is not all zero, in
-//              index order (the others have exactly zero decoder gradients);
-//              the two kernels below work on that list only.
+//   compaction the Gaussians whose upstream gradient is not all zero (the
+//              others have exactly zero decoder gradients), then ordered by a
+//              key of 8 bits of time over a 24-bit Morton code of the
+//              normalised position (stable radix sort: index order within a
+//              key), so that the Gaussians of one block lie close together
+//              and share the corners of the coarser levels; the two kernels
+//              below work on that list only.
 //   mlp_bwd_kernel  one wave per 16 Gaussians at a time (persistent grid):
 //       forward  the decoder on v_mfma_f32_16x16x32_f16 exactly as the decode
 //                runs it (same operands, same fp16 roundings), keeping the
@@ -32,9 +36,17 @@
 //       float atomics; for positions dz/df_axis = sum_c (+-1) prod_{other
 //       axes} w table[c] (time carries no gradient), times (res - 1), then the
 //       Jacobian of Eq. 7, added to the position gradient with float atomics.
+//       On levels of at most kAggMaxRes vertices per axis, where the block's
+//       Gaussians share corners, each block first adds its contributions per
+//       table entry in an LDS hash table (open addressing, LDS atomics) and
+//       then issues one pair of global atomics per distinct entry: global
+//       float atomics are served far below L2 speed on this chip, LDS ones
+//       are not.
 // After the last chunk a two-stage reduction sums the partial buffer in a
 // fixed order (deterministic weight and bias gradients).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "decode_common.h"
 #include "ia_internal.h"
@@ -478,18 +490,55 @@ __global__ void __launch_bounds__(256) mlp_bwd_reduce_kernel(const float* partia
     }
 }
 
-// Eq. 9 and Eq. 7 backward, level-major as the gather.  Lane s of a group of
-// four takes the x/y corner (s & 1, s >> 1) and its four z/t corners.
-template <bool POS>
+// Per-block combining of table-gradient contributions (see the file header):
+// kAggSlots entries of LDS, at most kAggProbes linear probes, then a direct
+// global atomic.
+constexpr int kAggBits = 12;
+constexpr int kAggSlots = 1 << kAggBits;
+constexpr int kAggProbes = 8;
+constexpr uint32_t kAggEmpty = 0xffffffffu;  // table indices are < 2^24
+constexpr int kAggMaxRes = 640;
+
+__device__ __forceinline__ void agg_add(uint32_t* key, float* v0, float* v1, uint32_t idx, float a, float b,
+                                        float* gt) {
+    uint32_t slot = (idx * 2654435761u) >> (32 - kAggBits);
+    for (int p = 0; p < kAggProbes; ++p) {
+        const uint32_t old = atomicCAS(&key[slot], kAggEmpty, idx);
+        if (old == kAggEmpty || old == idx) {
+            atomicAdd(&v0[slot], a);
+            atomicAdd(&v1[slot], b);
+            return;
+        }
+        slot = (slot + 1) & (kAggSlots - 1);
+    }
+    atomicAdd(gt + 2 * (size_t)idx, a);
+    atomicAdd(gt + 2 * (size_t)idx + 1, b);
+}
+
+// Eq. 9 and Eq. 7 backward, level-major as the gather, levels level0 + 0, 1,
+// ...  Lane s of a group of four takes the x/y corner (s & 1, s >> 1) and its
+// four z/t corners.  AGG: combine per entry in LDS first (every thread of a
+// block reaches the final barrier: the only early exit is block-uniform).
+template <bool POS, bool AGG>
 __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const float* pos, int stride,
                                                       const uint32_t* list, const uint32_t* count, int nchunk,
-                                                      HashLevels h, const uint32_t* tables, const float2* gz,
-                                                      int64_t zstride, float* gtab, float* gpos) {
+                                                      int level0, HashLevels h, const uint32_t* tables,
+                                                      const float2* gz, int64_t zstride, float* gtab, float* gpos) {
 #pragma clang fp contract(fast)
-    const int level = blockIdx.x / nchunk;
+    __shared__ uint32_t s_key[AGG ? kAggSlots : 1];
+    __shared__ float s_v0[AGG ? kAggSlots : 1], s_v1[AGG ? kAggSlots : 1];
+    const int level = level0 + (int)(blockIdx.x / nchunk);
     const int64_t first = (int64_t)(blockIdx.x % nchunk) * 256;
     const int64_t n = *count;  // Gaussians with a gradient, compacted
     if (first >= n) return;
+    if constexpr (AGG) {
+        for (int k = threadIdx.x; k < kAggSlots; k += 256) {
+            s_key[k] = kAggEmpty;
+            s_v0[k] = 0.0f;
+            s_v1[k] = 0.0f;
+        }
+        __syncthreads();
+    }
     const int res = h.res_s[level], res_t = h.res_t[level];
     const bool dense = h.dense[level] != 0;
     const uint32_t* tab = tables + (size_t)level * h.T;
@@ -540,8 +589,12 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
             const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
             const float w = (wxy * wz[bz]) * wt[bt];
             if (w != 0.0f) {
-                atomicAdd(gt + 2 * (size_t)idx, w * g.x);
-                atomicAdd(gt + 2 * (size_t)idx + 1, w * g.y);
+                if constexpr (AGG) {
+                    agg_add(s_key, s_v0, s_v1, idx, w * g.x, w * g.y, gt);
+                } else {
+                    atomicAdd(gt + 2 * (size_t)idx, w * g.x);
+                    atomicAdd(gt + 2 * (size_t)idx + 1, w * g.y);
+                }
             }
             if (POS) {
                 const uint32_t raw = tab[idx];
@@ -588,6 +641,16 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
             }
         }
     }
+    if constexpr (AGG) {
+        __syncthreads();
+        for (int k = threadIdx.x; k < kAggSlots; k += 256) {
+            const uint32_t idx = s_key[k];
+            if (idx != kAggEmpty) {
+                atomicAdd(gt + 2 * (size_t)idx, s_v0[k]);
+                atomicAdd(gt + 2 * (size_t)idx + 1, s_v1[k]);
+            }
+        }
+    }
 }
 
 // Compaction of the chunk's Gaussians whose upstream gradient is not all zero
@@ -624,7 +687,8 @@ __global__ void __launch_bounds__(256) active_count_kernel(const float* gs, cons
 }
 
 // Exclusive scan of nb <= 256 * 8 block counts in place; total into *count.
-__global__ void __launch_bounds__(256) active_scan_kernel(uint32_t* bcount, int nb, uint32_t* count) {
+__global__ void __launch_bounds__(256) active_scan_kernel(uint32_t* bcount, int nb, uint32_t* count,
+                                                          uint64_t* count64) {
     __shared__ uint32_t s_sum[256];
     constexpr int kPer = 8;
     uint32_t v[kPer], run = 0;
@@ -649,12 +713,31 @@ __global__ void __launch_bounds__(256) active_scan_kernel(uint32_t* bcount, int 
         if (i < nb) bcount[i] = base;
         base += v[k];
     }
-    if (threadIdx.x == 255) *count = s_sum[255];
+    if (threadIdx.x == 255) {
+        *count = s_sum[255];
+        *count64 = s_sum[255];
+    }
+}
+
+// 8 bits of v in [0, 1] spread to every third bit (bits 0, 3, ..., 21)
+__device__ __forceinline__ uint32_t spread3(float v) {
+    uint32_t q = (uint32_t)(fminf(fmaxf(v, 0.0f), 1.0f) * 255.0f);
+    q = (q | (q << 8)) & 0x0000f00fu;
+    q = (q | (q << 4)) & 0x000c30c3u;
+    q = (q | (q << 2)) & 0x00249249u;
+    return q;
+}
+
+// sort key of a normalised position: 8 bits of time above the 24-bit Morton
+// code of x, y, z
+__device__ __forceinline__ uint32_t spatial_key(float4 p) {
+    return (spread3(p.w) << 24) | spread3(p.x) | (spread3(p.y) << 1) | (spread3(p.z) << 2);
 }
 
 __global__ void __launch_bounds__(256) active_write_kernel(const float* gs, const float* gq, const float* gc,
                                                            const float* go, int64_t off, int64_t n,
-                                                           const uint32_t* boff, uint32_t* list) {
+                                                           const uint32_t* boff, const float4* xt,
+                                                           uint64_t* items) {
     __shared__ uint32_t s_w[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t b0 = (int64_t)blockIdx.x * kCompactItems;
@@ -668,10 +751,18 @@ __global__ void __launch_bounds__(256) active_write_kernel(const float* gs, cons
         uint32_t before = 0;
         for (int w = 0; w < wv; ++w) before += s_w[w];
         const uint32_t rank = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        if (f) list[pos + before + rank] = (uint32_t)i;
+        if (f) items[pos + before + rank] = ((uint64_t)spatial_key(xt[i]) << 32) | (uint64_t)i;
         pos += s_w[0] + s_w[1] + s_w[2] + s_w[3];
         __syncthreads();
     }
+}
+
+// the chunk-local indices of the sorted (key, index) words
+__global__ void __launch_bounds__(256) unpack_list_kernel(const uint64_t* items, const uint32_t* count,
+                                                          uint32_t* list) {
+    const int64_t n = *count;
+    for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += (int64_t)gridDim.x * 256)
+        list[k] = (uint32_t)items[k];
 }
 
 __global__ void fill_kernel(float* p, int64_t n, const float* src) {
@@ -686,7 +777,42 @@ int blocks_for(int64_t n, int per, int cap) {
     return (int)b;
 }
 
+constexpr int64_t kBwdChunk = kDecodeChunk / 2;
+
+// the sort scratch: two buffers of kBwdChunk words, the radix counts, the
+// digit totals and the item count
+struct SortScratch {
+    uint64_t* items[2];
+    uint32_t* counts;
+    uint32_t* digit_tot;
+    uint64_t* count;
+    int max_blocks;
+};
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+SortScratch sort_scratch(void* base) {
+    SortScratch t{};
+    char* p = static_cast<char*>(base);
+    t.max_blocks = radix_sort_blocks(kBwdChunk);
+    t.items[0] = reinterpret_cast<uint64_t*>(p);
+    p += align256(kBwdChunk * sizeof(uint64_t));
+    t.items[1] = reinterpret_cast<uint64_t*>(p);
+    p += align256(kBwdChunk * sizeof(uint64_t));
+    t.counts = reinterpret_cast<uint32_t*>(p);
+    p += align256(radix_sort_counts_bytes(t.max_blocks));
+    t.digit_tot = reinterpret_cast<uint32_t*>(p);
+    p += align256(4 * 1024);
+    t.count = reinterpret_cast<uint64_t*>(p);
+    return t;
+}
+
 }  // namespace
+
+size_t decode_bwd_sort_bytes() {
+    return 2 * align256(kBwdChunk * sizeof(uint64_t)) + align256(radix_sort_counts_bytes(radix_sort_blocks(kBwdChunk))) +
+           align256(4 * 1024) + 256;
+}
 
 hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     const DecodeArgs& a = b.fwd;
@@ -696,7 +822,8 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     if (b.g_pos && a.N > 0)
         IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(a.N * 3, 256, 8192)), dim3(256), 0, s,
                   b.g_pos, a.N * 3, b.g_means);
-    const int64_t chunk = kDecodeChunk / 2;
+    const int64_t chunk = kBwdChunk;
+    const SortScratch srt = sort_scratch(b.sort);
     const size_t zslot = (size_t)a.h.L * a.zcap;
     float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
     uint32_t* z = a.zbuf;
@@ -730,9 +857,14 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         const int nb = (int)((n + kCompactItems - 1) / kCompactItems);
         IA_LAUNCH("active_count_kernel", active_count_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
                   b.g_colors, b.g_opacity, off, n, boff);
-        IA_LAUNCH("active_scan_kernel", active_scan_kernel, dim3(1), dim3(256), 0, s, boff, nb, count);
+        IA_LAUNCH("active_scan_kernel", active_scan_kernel, dim3(1), dim3(256), 0, s, boff, nb, count, srt.count);
         IA_LAUNCH("active_write_kernel", active_write_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
-                  b.g_colors, b.g_opacity, off, n, boff, list);
+                  b.g_colors, b.g_opacity, off, n, boff, xt, srt.items[0]);
+        // stable sort on the 32 key bits above the index
+        const int cur = radix_sort_u64(srt.items, srt.count, (uint64_t)chunk, 32, 32, srt.max_blocks, srt.counts,
+                                       srt.digit_tot, s);
+        IA_LAUNCH("unpack_list_kernel", unpack_list_kernel, dim3(blocks_for(n, 256, 2048)), dim3(256), 0, s,
+                  srt.items[cur], count, list);
         m.list = list;
         m.count = count;
         m.off = off;
@@ -742,14 +874,25 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
                   dim3(kBwdThreads), 0, s, m);
         const int nchunk = (int)((n + 255) / 256);
         const float* pos = a.pos + off * a.stride;
-        if (b.g_pos)
-            IA_LAUNCH("scatter_kernel", scatter_kernel<true>, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
-                      pos, a.stride, list, count, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
-                      b.g_pos + off * 3);
-        else
-            IA_LAUNCH("scatter_kernel", scatter_kernel<false>, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt,
-                      pos, a.stride, list, count, nchunk, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables,
-                      (float*)nullptr);
+        float* gpos = b.g_pos ? b.g_pos + off * 3 : nullptr;
+        // levels [0, nagg) combine in LDS first (resolution grows with the level)
+        int nagg = 0;
+        while (nagg < a.h.L && a.h.res_s[nagg] <= kAggMaxRes) ++nagg;
+        auto scatter = [&](auto pos_t, auto agg_t, int level0, int levels) {
+            constexpr bool P = decltype(pos_t)::value, G = decltype(agg_t)::value;
+            if (levels > 0)
+                IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<P, G>),
+                          dim3((unsigned)(levels * nchunk)), dim3(256), 0,
+                          s, xt, pos, a.stride, list, count, nchunk, level0, a.h, (const uint32_t*)a.tables, gz,
+                          chunk, b.g_tables, gpos);
+        };
+        if (b.g_pos) {
+            scatter(std::true_type{}, std::true_type{}, 0, nagg);
+            scatter(std::true_type{}, std::false_type{}, nagg, a.h.L - nagg);
+        } else {
+            scatter(std::false_type{}, std::true_type{}, 0, nagg);
+            scatter(std::false_type{}, std::false_type{}, nagg, a.h.L - nagg);
+        }
     }
     if (first) {  // N = 0: the weight and bias gradients are zero
         const int64_t nf = (int64_t)kDecodeBwdBlocks * kBwdWaves * (kTileSlots + kBiasSlots) * 64;

@@ -124,8 +124,10 @@ struct DecodeBwdArgs {
     float* g_W[3];            // [64][32], [64][64], [11][64] out
     float* g_b[3];            // [64], [64], [11] out
     float* partial;           // kDecodeBwdPartialFloats
+    void* sort;               // decode_bwd_sort_bytes(): the spatial ordering of the active list
 };
 
+size_t decode_bwd_sort_bytes();
 hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s);
 
 struct HexArgs {
@@ -239,6 +241,15 @@ size_t image_loss_workspace(int32_t frames, int32_t H, int32_t W);
 hipError_t launch_image_loss(const float* image, const float* target, int32_t frames, int32_t H, int32_t W,
                              float lambda, void* ws, double* loss, float* grad, hipStream_t s);
 // One bias-corrected Adam step over n fp32 parameters (optional fp16 copy).
+// Stable LSD radix sort of the first min(*count, cap) 64-bit words of buf[0]
+// on bits [lo, lo + nbits) (render.hip); returns the index (0 or 1) of the
+// buffer of buf that holds the result.  max_blocks <= radix_sort_blocks(cap);
+// counts: radix_sort_counts_bytes(max_blocks) bytes; digit_tot: 4 KiB.
+int radix_sort_u64(uint64_t* const* buf, const uint64_t* count, uint64_t cap, int lo, int nbits, int max_blocks,
+                   uint32_t* counts, uint32_t* digit_tot, hipStream_t s);
+int radix_sort_blocks(int64_t items);
+size_t radix_sort_counts_bytes(int max_blocks);
+
 // g, m, v dense [n]; the parameter is rows of `dim` values `stride` floats
 // apart (dim == stride: dense); p16 (dense [n] fp16 copy of the result) or null
 hipError_t launch_adam(float* p, const float* g, float* m, float* v, int64_t n, int32_t dim, int32_t stride,

@@ -1225,6 +1225,45 @@ int grid_cap(int64_t n, int per, int cap) {
 
 }  // namespace
 
+// LSD passes over bits [lo, lo + nbits) of the first min(*count, cap) 64-bit
+// words of buf[0], digits of at most kMaxDigitBits bits, ping-ponging between
+// buf[0] and buf[1]; returns the index of the buffer holding the result.
+// counts: 4 * kMaxBuckets * max_blocks bytes, digit_tot: 4 * kMaxBuckets.
+int radix_sort_u64(uint64_t* const* buf, const uint64_t* count, uint64_t cap, int lo, int nbits, int max_blocks,
+                   uint32_t* counts, uint32_t* digit_tot, hipStream_t s) {
+    const int passes = (nbits + kMaxDigitBits - 1) / kMaxDigitBits;
+    const int bits = (nbits + passes - 1) / passes;
+    int cur = 0;
+    for (int pass = 0; pass < passes; ++pass) {
+        SortPass sp{buf[cur], buf[cur ^ 1], count, cap, lo + pass * bits, bits, max_blocks, counts, digit_tot};
+        auto run = [&](auto digit_bits) {
+            constexpr int B = decltype(digit_bits)::value;
+            // one round of resident blocks: every block takes an equal chunk
+            const int r = resident_blocks<sort_downsweep_kernel<B>>();
+            sp.nblocks = max_blocks < r ? max_blocks : r;
+            IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<B>, dim3(sp.nblocks), dim3(kBlock), 0, s, sp);
+            IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
+            IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel<B>, dim3(sp.nblocks), dim3(kBlock), 0, s, sp);
+        };
+        if (bits <= 8)
+            run(std::integral_constant<int, 8>{});
+        else if (bits == 9)
+            run(std::integral_constant<int, 9>{});
+        else
+            run(std::integral_constant<int, kMaxDigitBits>{});
+        cur ^= 1;
+    }
+    return cur;
+}
+
+int radix_sort_blocks(int64_t items) {
+    const int64_t b = (items + kSortTile - 1) / kSortTile;
+    return (int)(b < 1 ? 1 : (b > 1024 ? 1024 : b));
+}
+
+size_t radix_sort_counts_bytes(int max_blocks) { return 4 * (size_t)kMaxBuckets * (size_t)max_blocks; }
+
+
 RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entries) {
     RenderLayout L{};
     L.N = N;
@@ -1357,32 +1396,8 @@ hipError_t launch_render(const RenderArgs& a, hipStream_t s, const uint64_t** ke
         if (boff_out)
             IA_LAUNCH("scan_down_kernel", scan_down_kernel, dim3(nb2), dim3(kBlock), 0, s, bs, nb, bsum2, boff_out);
     };
-    // LSD passes over bits [lo, lo + nbits) of 64-bit words, digits of at most
-    // kMaxDigitBits bits; returns the buffer index holding the result.
     auto radix = [&](uint64_t** buf, const uint64_t* count, uint64_t rcap, int lo, int nbits, int max_blocks) {
-        const int passes = (nbits + kMaxDigitBits - 1) / kMaxDigitBits;
-        const int bits = (nbits + passes - 1) / passes;
-        int cur = 0;
-        for (int pass = 0; pass < passes; ++pass) {
-            SortPass sp{buf[cur], buf[cur ^ 1], count, rcap, lo + pass * bits, bits, max_blocks, counts, digit_tot};
-            auto run = [&](auto digit_bits) {
-                constexpr int B = decltype(digit_bits)::value;
-                // one round of resident blocks: every block takes an equal chunk
-                const int r = resident_blocks<sort_downsweep_kernel<B>>();
-                sp.nblocks = max_blocks < r ? max_blocks : r;
-                IA_LAUNCH("sort_upsweep_kernel", sort_upsweep_kernel<B>, dim3(sp.nblocks), dim3(kBlock), 0, s, sp);
-                IA_LAUNCH("sort_scan_kernel", sort_scan_kernel, dim3(1 << bits), dim3(kBlock), 0, s, sp);
-                IA_LAUNCH("sort_downsweep_kernel", sort_downsweep_kernel<B>, dim3(sp.nblocks), dim3(kBlock), 0, s, sp);
-            };
-            if (bits <= 8)
-                run(std::integral_constant<int, 8>{});
-            else if (bits == 9)
-                run(std::integral_constant<int, 9>{});
-            else
-                run(std::integral_constant<int, kMaxDigitBits>{});
-            cur ^= 1;
-        }
-        return cur;
+        return radix_sort_u64(buf, count, rcap, lo, nbits, max_blocks, counts, digit_tot, s);
     };
     auto bits_for = [](int64_t n) {
         int b = 1;

@@ -145,8 +145,9 @@ IA_API ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* 
  * The copies are enqueued on `stream`; host sources may be freed on return
  * (host copies are synchronous).  For the fp16 decoder this call also
  * allocates the handle's feature scratch ((4 L F + 16) x 2^22 bytes; decode
- * processes at most 2^22 Gaussians per gather/MLP kernel pair) and 39 MB of
- * backward partials.  May be called again to replace parameters (waits for
+ * processes at most 2^22 Gaussians per gather/MLP kernel pair), 39 MB of
+ * backward partials and 34 MiB for the backward's spatial ordering of the
+ * Gaussians it differentiates.  May be called again to replace parameters (waits for
  * the device first).
  * Errors: INVALID_ARG, OUT_OF_MEMORY, DEVICE. */
 IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
