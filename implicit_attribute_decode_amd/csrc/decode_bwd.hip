@@ -498,6 +498,9 @@ constexpr int kAggSlots = 1 << kAggBits;
 constexpr int kAggProbes = 8;
 constexpr uint32_t kAggEmpty = 0xffffffffu;  // table indices are < 2^24
 constexpr int kAggMaxRes = 640;
+// rounds of 64 Gaussians per combining block (768 Gaussians share one LDS table;
+// 256, 384, 512 measured slower)
+constexpr int kAggRounds = 12;
 
 __device__ __forceinline__ void agg_add(uint32_t* key, float* v0, float* v1, uint32_t idx, float a, float b,
                                         float* gt) {
@@ -528,7 +531,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
     __shared__ uint32_t s_key[AGG ? kAggSlots : 1];
     __shared__ float s_v0[AGG ? kAggSlots : 1], s_v1[AGG ? kAggSlots : 1];
     const int level = level0 + (int)(blockIdx.x / nchunk);
-    const int64_t first = (int64_t)(blockIdx.x % nchunk) * 256;
+    constexpr int kRounds = AGG ? kAggRounds : 4;
+    const int64_t first = (int64_t)(blockIdx.x % nchunk) * (64 * kRounds);
     const int64_t n = *count;  // Gaussians with a gradient, compacted
     if (first >= n) return;
     if constexpr (AGG) {
@@ -547,7 +551,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
     const int bx = s & 1, by = s >> 1;
     const int sub = threadIdx.x >> 2;
     const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kRounds; ++j) {
         const int64_t k = first + j * 64 + sub;  // compact index
         if (k >= n) break;  // uniform across each group of four lanes
         const int64_t i = list[k];  // chunk-local Gaussian
@@ -872,7 +876,7 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         first = 0;
         IA_LAUNCH("mlp_bwd_kernel", m.gelu ? mlp_bwd_kernel<true> : mlp_bwd_kernel<false>, dim3(kDecodeBwdBlocks),
                   dim3(kBwdThreads), 0, s, m);
-        const int nchunk = (int)((n + 255) / 256);
+        const int nchunk = (int)((n + 255) / 256), nchunk_agg = (int)((n + 64 * kAggRounds - 1) / (64 * kAggRounds));
         const float* pos = a.pos + off * a.stride;
         float* gpos = b.g_pos ? b.g_pos + off * 3 : nullptr;
         // levels [0, nagg) combine in LDS first (resolution grows with the level)
@@ -880,10 +884,11 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         while (nagg < a.h.L && a.h.res_s[nagg] <= kAggMaxRes) ++nagg;
         auto scatter = [&](auto pos_t, auto agg_t, int level0, int levels) {
             constexpr bool P = decltype(pos_t)::value, G = decltype(agg_t)::value;
+            const int nc = G ? nchunk_agg : nchunk;
             if (levels > 0)
                 IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<P, G>),
-                          dim3((unsigned)(levels * nchunk)), dim3(256), 0,
-                          s, xt, pos, a.stride, list, count, nchunk, level0, a.h, (const uint32_t*)a.tables, gz,
+                          dim3((unsigned)(levels * nc)), dim3(256), 0,
+                          s, xt, pos, a.stride, list, count, nc, level0, a.h, (const uint32_t*)a.tables, gz,
                           chunk, b.g_tables, gpos);
         };
         if (b.g_pos) {
