@@ -8,17 +8,20 @@
 //   Adam (Kingma & Ba, 2015), the optimiser named in §4 implementation
 //     details, one bias-corrected step over a parameter array.
 //
-// ssim_fwd_kernel: one 256-thread block per 16 x 16 output tile of one image
-// plane.  The 26 x 26 halo of x and y is staged in LDS, the horizontal window
-// sums of the five moments (x, y, x^2, y^2, xy) over the 26 rows are formed
-// in LDS, and each thread sums 11 of them vertically: mu_x, mu_y, E[x^2],
-// E[y^2], E[xy] of its pixel.  It writes S's derivatives with respect to
-// mu_x, E[x^2] and E[xy] (the only moments that depend on x) and the block's
-// sums of S and |x - y| (one pair per block; loss_finish_kernel adds them in
-// a fixed order, so the loss is the same on every run).
-// ssim_bwd_kernel: the same tiling applied to the three derivative maps (the
-// window is symmetric, so its adjoint is the same zero-padded window sum),
-// combined into dL/dx = (1 - lambda) sign(x - y) / n
+// ssim_fwd_kernel: one 256-thread block per strip of 256 columns x 64 output
+// rows of one image plane, one column per thread.  The block walks the 74
+// input rows the strip's windows cover: each row of x and y (with a 5-column
+// margin, zero outside the image) is staged in LDS, every thread forms the
+// horizontal window sums of the five moments (x, y, x^2, y^2, xy) for its
+// column and keeps the last 11 rows of them in registers; once 11 rows are
+// in, the vertical window sum gives mu_x, mu_y, E[x^2], E[y^2], E[xy] of one
+// output pixel.  It writes S's derivatives with respect to mu_x, E[x^2] and
+// E[xy] (the only moments that depend on x) and the block's sums of S and
+// |x - y| (one pair per block; loss_finish_kernel adds them in a fixed order,
+// so the loss is the same on every run).
+// ssim_bwd_kernel: the same sliding window over the three derivative maps
+// (the window is symmetric, so its adjoint is the same zero-padded window
+// sum), combined into dL/dx = (1 - lambda) sign(x - y) / n
 //   - lambda (blur(dS/dmu_x) + 2 x blur(dS/dE[x^2]) + y blur(dS/dE[xy])) / n.
 #include <hip/hip_runtime.h>
 
@@ -27,9 +30,12 @@
 namespace ia {
 namespace {
 
-constexpr int kT = 16;                // output tile edge
-constexpr int kR = 5;                 // window radius
-constexpr int kHalo = kT + 2 * kR;    // 26
+constexpr int kR = 5;                  // window radius
+constexpr int kWin = 2 * kR + 1;       // 11 taps
+constexpr int kSW = 256;               // strip width: one column per thread
+constexpr int kSH = 64;                // output rows per block
+constexpr int kRowsIn = kSH + 2 * kR;  // input rows a block reads
+constexpr int kRowW = kSW + 2 * kR;    // staged row width
 constexpr float kC1 = 0.01f * 0.01f;
 constexpr float kC2 = 0.03f * 0.03f;
 
@@ -52,67 +58,102 @@ struct LossArgs {
     float* grad;
 };
 
-// Stage the 26 x 26 halo of `src` (one plane) around tile (tx, ty); zero outside.
-__device__ __forceinline__ void stage_halo(const float* src, int H, int W, int x0, int y0, float* dst) {
-    for (int k = threadIdx.x; k < kHalo * kHalo; k += 256) {
-        const int r = k / kHalo, c = k - r * kHalo;
-        const int yy = y0 + r - kR, xx = x0 + c - kR;
-        dst[k] = (yy >= 0 && yy < H && xx >= 0 && xx < W) ? src[(size_t)yy * W + xx] : 0.0f;
-    }
+// A thread's share of image row yy (columns x0 - kR .. x0 + kSW + kR - 1,
+// zero outside the image) of plane `src`: staged column c, and c + kSW for
+// the first 2 kR threads.  Loaded one row ahead of its use (registers), so
+// the loads overlap the previous row's arithmetic.
+struct RowVals {
+    float v0, v1;
+};
+
+// Both loads are unconditional, from clamped (in-image) addresses, and the
+// values outside the image are replaced by zero afterwards: a load under a
+// branch would wait for its data inside the branch.
+__device__ __forceinline__ RowVals load_row(const float* src, int H, int W, int x0, int yy) {
+    const int xa = x0 - kR + (int)threadIdx.x, xb = xa + kSW;
+    const float* row = src + (size_t)min(max(yy, 0), H - 1) * W;
+    const float va = row[min(max(xa, 0), W - 1)];
+    const float vb = row[min(max(xb, 0), W - 1)];
+    const bool rin = yy >= 0 && yy < H;
+    return RowVals{(rin && xa >= 0 && xa < W) ? va : 0.0f, (rin && xb < W && threadIdx.x < 2 * kR) ? vb : 0.0f};
 }
 
-__global__ void __launch_bounds__(256) ssim_fwd_kernel(LossArgs a) {
-    __shared__ float s_x[kHalo * kHalo], s_y[kHalo * kHalo];
-    __shared__ float s_h[5][kHalo][kT];  // horizontal window sums of the moments
-    __shared__ double s_red[2][4];
-    const int plane = blockIdx.z;
-    const int x0 = blockIdx.x * kT, y0 = blockIdx.y * kT;
-    const size_t poff = (size_t)plane * a.H * a.W;
-    stage_halo(a.x + poff, a.H, a.W, x0, y0, s_x);
-    stage_halo(a.y + poff, a.H, a.W, x0, y0, s_y);
-    __syncthreads();
-    for (int k = threadIdx.x; k < kHalo * kT; k += 256) {
-        const int r = k / kT, c = k - r * kT;
-        float m[5] = {0, 0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t <= 2 * kR; ++t) {
-            const float xv = s_x[r * kHalo + c + t], yv = s_y[r * kHalo + c + t], w = c_win[t];
-            m[0] += w * xv;
-            m[1] += w * yv;
-            m[2] += w * (xv * xv);
-            m[3] += w * (yv * yv);
-            m[4] += w * (xv * yv);
-        }
-#pragma unroll
-        for (int q = 0; q < 5; ++q) s_h[q][r][c] = m[q];
-    }
-    __syncthreads();
-    const int c = threadIdx.x & (kT - 1), r = threadIdx.x / kT;
-    const int px = x0 + c, py = y0 + r;
-    const bool in = px < a.W && py < a.H;
-    float m[5] = {0, 0, 0, 0, 0};
-#pragma unroll
-    for (int t = 0; t <= 2 * kR; ++t) {
-        const float w = c_win[t];
-#pragma unroll
-        for (int q = 0; q < 5; ++q) m[q] += w * s_h[q][r + t][c];
-    }
+__device__ __forceinline__ void store_row(float* dst, RowVals r) {
+    dst[threadIdx.x] = r.v0;
+    if (threadIdx.x < 2 * kR) dst[threadIdx.x + kSW] = r.v1;
+}
+
+__device__ __forceinline__ size_t block_index() {
+    return ((size_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+}
+
+__global__ void __launch_bounds__(kSW) ssim_fwd_kernel(LossArgs a) {
+    __shared__ float s_x[2][kRowW], s_y[2][kRowW];
+    __shared__ double s_red[2][kSW / 64];
+    const int x0 = blockIdx.x * kSW, y0 = blockIdx.y * kSH;
+    const size_t poff = (size_t)blockIdx.z * a.H * a.W;
+    const int c = threadIdx.x, px = x0 + c;
+    float ring[kWin][5];  // horizontal sums of the last 11 input rows, slot = row % 11
     double s_sum = 0.0, l1_sum = 0.0;
-    if (in) {
-        const float mx = m[0], my = m[1];
-        const float sxx = m[2] - mx * mx, syy = m[3] - my * my, sxy = m[4] - mx * my;
-        const float a1 = 2.0f * mx * my + kC1, a2 = 2.0f * sxy + kC2;
-        const float b1 = mx * mx + my * my + kC1, b2 = sxx + syy + kC2;
-        const float S = (a1 * a2) / (b1 * b2);
-        const size_t i = poff + (size_t)py * a.W + px;
-        // terms paired by the moments that approach each other as x -> y, so
-        // identical windows give exactly zero
-        a.d[i] = S * ((2.0f * my / a1 - 2.0f * mx / b1) + (2.0f * mx / b2 - 2.0f * my / a2));
-        a.d[a.plane_stride + i] = -S / b2;
-        a.d[2 * a.plane_stride + i] = 2.0f * S / a2;
-        s_sum = (double)S;
-        const float xv = s_x[(r + kR) * kHalo + c + kR], yv = s_y[(r + kR) * kHalo + c + kR];
-        l1_sum = fabs((double)xv - (double)yv);
+    const float* xs = a.x + poff;
+    const float* ys = a.y + poff;
+    RowVals nx = load_row(xs, a.H, a.W, x0, y0 - kR), ny = load_row(ys, a.H, a.W, x0, y0 - kR);
+    for (int base = 0; base < kRowsIn; base += kWin) {
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+            const int ri = base + u;  // input row of the block's window (uniform)
+            if (ri < kRowsIn) {
+                float* bx = s_x[ri & 1];
+                float* by = s_y[ri & 1];
+                store_row(bx, nx);
+                store_row(by, ny);
+                // one barrier per row: a buffer is rewritten two rows later,
+                // after every thread has passed this barrier of the row between
+                __syncthreads();
+                if (ri + 1 < kRowsIn) {
+                    nx = load_row(xs, a.H, a.W, x0, y0 - kR + ri + 1);
+                    ny = load_row(ys, a.H, a.W, x0, y0 - kR + ri + 1);
+                }
+                float m[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < kWin; ++t) {
+                    const float xv = bx[c + t], yv = by[c + t], w = c_win[t];
+                    m[0] += w * xv;
+                    m[1] += w * yv;
+                    m[2] += w * (xv * xv);
+                    m[3] += w * (yv * yv);
+                    m[4] += w * (xv * yv);
+                }
+#pragma unroll
+                for (int q = 0; q < 5; ++q) ring[u][q] = m[q];
+                const int ro = ri - 2 * kR;  // output row whose window ends at this input row
+                const int py = y0 + ro;
+                if (ro >= 0 && px < a.W && py < a.H) {
+                    float v[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int t = 0; t < kWin; ++t) {
+                        // input row ro + t = ri - 10 + t sits in slot (u + 1 + t) % 11
+                        const float w = c_win[t];
+#pragma unroll
+                        for (int q = 0; q < 5; ++q) v[q] += w * ring[(u + 1 + t) % kWin][q];
+                    }
+                    const float mx = v[0], my = v[1];
+                    const float sxx = v[2] - mx * mx, syy = v[3] - my * my, sxy = v[4] - mx * my;
+                    const float a1 = 2.0f * mx * my + kC1, a2 = 2.0f * sxy + kC2;
+                    const float b1 = mx * mx + my * my + kC1, b2 = sxx + syy + kC2;
+                    const float S = (a1 * a2) / (b1 * b2);
+                    const size_t i = poff + (size_t)py * a.W + px;
+                    // terms paired by the moments that approach each other as x -> y,
+                    // so identical windows give exactly zero
+                    a.d[i] = S * ((2.0f * my / a1 - 2.0f * mx / b1) + (2.0f * mx / b2 - 2.0f * my / a2));
+                    a.d[a.plane_stride + i] = -S / b2;
+                    a.d[2 * a.plane_stride + i] = 2.0f * S / a2;
+                    const float xv = a.x[i], yv = a.y[i];  // staged kR rows ago: an L2 hit
+                    s_sum += (double)S;
+                    l1_sum += fabs((double)xv - (double)yv);
+                }
+            }
+        }
     }
     for (int o = 32; o > 0; o >>= 1) {
         s_sum += __shfl_xor(s_sum, o, 64);
@@ -123,51 +164,63 @@ __global__ void __launch_bounds__(256) ssim_fwd_kernel(LossArgs a) {
         s_red[1][threadIdx.x >> 6] = l1_sum;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const size_t b = ((size_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-        a.part[b] = make_double2((s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]),
-                                 (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]));
-    }
+    if (threadIdx.x == 0)
+        a.part[block_index()] = make_double2((s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]),
+                                             (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]));
 }
 
-__global__ void __launch_bounds__(256) ssim_bwd_kernel(LossArgs a) {
-    __shared__ float s_d[3][kHalo * kHalo];
-    __shared__ float s_h[3][kHalo][kT];
-    const int plane = blockIdx.z;
-    const int x0 = blockIdx.x * kT, y0 = blockIdx.y * kT;
-    const size_t poff = (size_t)plane * a.H * a.W;
-#pragma unroll
-    for (int q = 0; q < 3; ++q) stage_halo(a.d + q * a.plane_stride + poff, a.H, a.W, x0, y0, s_d[q]);
-    __syncthreads();
-    for (int k = threadIdx.x; k < kHalo * kT; k += 256) {
-        const int r = k / kT, c = k - r * kT;
-        float m[3] = {0, 0, 0};
-#pragma unroll
-        for (int t = 0; t <= 2 * kR; ++t) {
-            const float w = c_win[t];
-#pragma unroll
-            for (int q = 0; q < 3; ++q) m[q] += w * s_d[q][r * kHalo + c + t];
-        }
-#pragma unroll
-        for (int q = 0; q < 3; ++q) s_h[q][r][c] = m[q];
-    }
-    __syncthreads();
-    const int c = threadIdx.x & (kT - 1), r = threadIdx.x / kT;
-    const int px = x0 + c, py = y0 + r;
-    if (px >= a.W || py >= a.H) return;
-    float m[3] = {0, 0, 0};
-#pragma unroll
-    for (int t = 0; t <= 2 * kR; ++t) {
-        const float w = c_win[t];
-#pragma unroll
-        for (int q = 0; q < 3; ++q) m[q] += w * s_h[q][r + t][c];
-    }
-    const size_t i = poff + (size_t)py * a.W + px;
-    const float xv = a.x[i], yv = a.y[i];
+__global__ void __launch_bounds__(kSW) ssim_bwd_kernel(LossArgs a) {
+    __shared__ float s_d[2][3][kRowW];
+    const int x0 = blockIdx.x * kSW, y0 = blockIdx.y * kSH;
+    const size_t poff = (size_t)blockIdx.z * a.H * a.W;
+    const int c = threadIdx.x, px = x0 + c;
     const float inv_n = (float)a.inv_n;
-    const float dssim = (m[0] + 2.0f * xv * m[1] + yv * m[2]) * inv_n;
-    const float sgn = xv > yv ? 1.0f : (xv < yv ? -1.0f : 0.0f);
-    a.grad[i] = (1.0f - a.lambda) * sgn * inv_n - a.lambda * dssim;
+    float ring[kWin][3];
+    const float* ds[3] = {a.d + poff, a.d + a.plane_stride + poff, a.d + 2 * a.plane_stride + poff};
+    RowVals nd[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) nd[q] = load_row(ds[q], a.H, a.W, x0, y0 - kR);
+    for (int base = 0; base < kRowsIn; base += kWin) {
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+            const int ri = base + u;
+            if (ri < kRowsIn) {
+                float(*bd)[kRowW] = s_d[ri & 1];
+#pragma unroll
+                for (int q = 0; q < 3; ++q) store_row(bd[q], nd[q]);
+                __syncthreads();
+                if (ri + 1 < kRowsIn) {
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) nd[q] = load_row(ds[q], a.H, a.W, x0, y0 - kR + ri + 1);
+                }
+                float m[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < kWin; ++t) {
+                    const float w = c_win[t];
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) m[q] += w * bd[q][c + t];
+                }
+#pragma unroll
+                for (int q = 0; q < 3; ++q) ring[u][q] = m[q];
+                const int ro = ri - 2 * kR;
+                const int py = y0 + ro;
+                if (ro >= 0 && px < a.W && py < a.H) {
+                    float v[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int t = 0; t < kWin; ++t) {
+                        const float w = c_win[t];
+#pragma unroll
+                        for (int q = 0; q < 3; ++q) v[q] += w * ring[(u + 1 + t) % kWin][q];
+                    }
+                    const size_t i = poff + (size_t)py * a.W + px;
+                    const float xv = a.x[i], yv = a.y[i];
+                    const float dssim = (v[0] + 2.0f * xv * v[1] + yv * v[2]) * inv_n;
+                    const float sgn = xv > yv ? 1.0f : (xv < yv ? -1.0f : 0.0f);
+                    a.grad[i] = (1.0f - a.lambda) * sgn * inv_n - a.lambda * dssim;
+                }
+            }
+        }
+    }
 }
 
 // One block of kFinish threads: the per-block sums added in a fixed order;
@@ -230,7 +283,7 @@ __global__ void __launch_bounds__(256) adam_kernel(float* p, const float* g, flo
 // [3][planes][H][W] float derivative maps, then one double2 per SSIM block
 size_t image_loss_workspace(int32_t frames, int32_t H, int32_t W) {
     const size_t maps = (size_t)3 * frames * 3 * (size_t)H * W * sizeof(float);
-    const size_t blocks = (size_t)((W + kT - 1) / kT) * ((H + kT - 1) / kT) * frames * 3;
+    const size_t blocks = (size_t)((W + kSW - 1) / kSW) * ((H + kSH - 1) / kSH) * frames * 3;
     return ((maps + 255) & ~(size_t)255) + blocks * sizeof(double2);
 }
 
@@ -241,10 +294,10 @@ hipError_t launch_image_loss(const float* image, const float* target, int32_t fr
     const size_t maps = ((3 * n * sizeof(float)) + 255) & ~(size_t)255;
     double2* part = reinterpret_cast<double2*>((char*)ws + maps);
     LossArgs a{image, target, H, W, lambda, 1.0 / (double)n, reinterpret_cast<float*>(ws), n, part, grad};
-    const dim3 grid((W + kT - 1) / kT, (H + kT - 1) / kT, planes);
+    const dim3 grid((W + kSW - 1) / kSW, (H + kSH - 1) / kSH, planes);
     const int64_t nblocks = (int64_t)grid.x * grid.y * grid.z;
-    IA_LAUNCH("ssim_fwd_kernel", ssim_fwd_kernel, grid, dim3(256), 0, s, a);
-    IA_LAUNCH("ssim_bwd_kernel", ssim_bwd_kernel, grid, dim3(256), 0, s, a);
+    IA_LAUNCH("ssim_fwd_kernel", ssim_fwd_kernel, grid, dim3(kSW), 0, s, a);
+    IA_LAUNCH("ssim_bwd_kernel", ssim_bwd_kernel, grid, dim3(kSW), 0, s, a);
     IA_LAUNCH("loss_finish_kernel", loss_finish_kernel, dim3(1), dim3(kFinish), 0, s, part, nblocks,
               1.0 / (double)n, (double)lambda, loss);
     return hipGetLastError();
