@@ -247,8 +247,13 @@ def _train_full(S, Decoder, Renderer, stream, xyzt, fo, cams, target) -> dict:
     """One whole training step on the Stress batch, everything the step
     does inside the timed region: decode of the 8M positions (keeping the
     encoding), render of the decoded Gaussians, the Eq. 12 loss (L1 + D-SSIM)
-    and its image gradient, render backward, decode backward, Adam over the
-    decoder's groups and the positions, and the decoder parameter update."""
+    and its image gradient, render backward, decode backward, the position
+    gradients' norms accumulated for densification, Adam over the decoder's
+    groups and the positions, and the decoder parameter update.  Then one
+    densify / prune of the 8M positions (Eq. 6), timed on its own."""
+    import torch
+
+    from implicit_attribute_decode_amd import ia
     from implicit_attribute_decode_amd.pipeline import Adam
 
     D = Decoder(S.single_decoder())
@@ -263,6 +268,8 @@ def _train_full(S, Decoder, Renderer, stream, xyzt, fo, cams, target) -> dict:
     E = Renderer.count_entries(R.render(g, fo, cams, 4 * n, aux=True, keys=False))
     cap = E + E // 4 + 4096  # the positions move between steps
     res = R.render(g, fo, cams, cap, aux=True, keys=False)
+    acc = torch.zeros(n, device="cuda")
+    cnt = torch.zeros(n, dtype=torch.int32, device="cuda")
 
     def step():
         D.decode_keep(xt, out=attrs, features=feats)
@@ -272,6 +279,7 @@ def _train_full(S, Decoder, Renderer, stream, xyzt, fo, cams, target) -> dict:
         dg = D.backward(xt, ga, grad_means=ga["means"], features=feats)
         grads = D.group_grads(dg)
         grads["positions"] = dg["pos"]
+        ia.ia_densify_accumulate(dg["pos"], acc, cnt)
         opt.step(grads)
         D.update_params()
         return loss
@@ -282,7 +290,27 @@ def _train_full(S, Decoder, Renderer, stream, xyzt, fo, cams, target) -> dict:
     kernels = profiled(step, 1)
     last = [float(v) for v in step().cpu()]
     overflow = int(res["overflow"].item())
+    # one densify / prune of the 8M positions on the gradients accumulated above
+    # (3DGS's thresholds: mean gradient 2e-4, scale 1 % of the scene extent, opacity 0.005)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    noise = torch.randn((n, 2, 3), generator=gen, device="cuda")
+    m_pos, v_pos = opt.state["positions"]
+    out_x = torch.empty((2 * n, 4), device="cuda")
+    out_m = torch.empty((2 * n, 3), device="cuda")
+    out_v = torch.empty((2 * n, 3), device="cuda")
+    out_n = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dws = torch.empty(ia.ia_densify_workspace_size(n), dtype=torch.uint8, device="cuda")
+    prm = ia.DensifyParams(2e-4, 0.01 * 3.0, 0.005)
+
+    def densify():
+        ia.ia_densify(xt, acc, cnt, attrs["scales"], attrs["quats"], attrs["opacity"], noise, m_pos, v_pos, prm,
+                      out_x, out_m, out_v, out_n, dws)
+
+    densify()
+    ms_dn = timed(densify, 3, stream)
+    rows = int(out_n.item())
     return {"tile_entries": E, "step_ms": round(ms, 3), "overflow": overflow,
+            "densify_ms": round(ms_dn, 3), "densify_rows_out": rows,
             "loss_first": [round(v, 6) for v in l0], "loss_after": [round(v, 6) for v in last],
             "steps_taken": opt.t, "kernels_ms": kernels}
 

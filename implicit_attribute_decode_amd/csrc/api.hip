@@ -839,4 +839,42 @@ ia_status ia_adam_step_strided(float* param, int32_t param_stride, int32_t dim, 
     return IA_OK;
 }
 
+ia_status ia_densify_accumulate(const float* grad_pos, int64_t N, float* grad_acc, int32_t* grad_count,
+                                void* stream) {
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    if (N > 0 && (!grad_pos || !grad_acc || !grad_count)) return fail(IA_ERR_INVALID_ARG, "null argument");
+    hipError_t e = ia::launch_densify_accumulate(grad_pos, N, grad_acc, grad_count, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "densify accumulate launch");
+    return IA_OK;
+}
+
+ia_status ia_densify_workspace_size(int64_t N, size_t* bytes) {
+    if (N < 0 || !bytes) return fail(IA_ERR_INVALID_ARG, "N must be >= 0 and bytes non-null");
+    *bytes = ia::densify_workspace(N);
+    return IA_OK;
+}
+
+ia_status ia_densify(const float* xyzt, const float* grad_acc, const int32_t* grad_count, const float* scales,
+                     const float* quats, const float* opacity, const float* noise, const float* m, const float* v,
+                     int64_t N, const ia_densify_params* params, float* out_xyzt, float* out_m, float* out_v,
+                     int64_t out_capacity, int64_t* out_n, void* ws, size_t ws_bytes, void* stream) {
+    if (N < 0 || !params || !out_n) return fail(IA_ERR_INVALID_ARG, "N must be >= 0; params, out_n non-null");
+    if (N > 0 && (!xyzt || !grad_acc || !grad_count || !scales || !quats || !opacity || !noise || !m || !v ||
+                  !out_xyzt || !out_m || !out_v))
+        return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N too large");
+    if (out_capacity < 2 * N) return fail(IA_ERR_INVALID_ARG, "out_capacity must be >= 2 N");
+    if (N > 0 && (!aligned(xyzt, 16) || !aligned(out_xyzt, 16)))
+        return fail(IA_ERR_INVALID_ARG, "xyzt and out_xyzt must be 16-byte aligned");
+    if (N > 0 && (!ws || ws_bytes < ia::densify_workspace(N)))
+        return fail(IA_ERR_WORKSPACE_TOO_SMALL, "densify workspace too small");
+    if (!(params->grad_threshold >= 0.0f) || !(params->scale_threshold >= 0.0f) || !(params->min_opacity >= 0.0f))
+        return fail(IA_ERR_INVALID_ARG, "thresholds must be >= 0");
+    ia::DensifyIn in{xyzt, grad_acc, grad_count, scales, quats, opacity, noise, m, v, N, params->grad_threshold,
+                     params->scale_threshold, params->min_opacity, out_xyzt, out_m, out_v, out_n};
+    hipError_t e = ia::launch_densify(in, ws, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "densify launch");
+    return IA_OK;
+}
+
 }  // extern "C"

@@ -241,6 +241,28 @@ size_t image_loss_workspace(int32_t frames, int32_t H, int32_t W);
 hipError_t launch_image_loss(const float* image, const float* target, int32_t frames, int32_t H, int32_t W,
                              float lambda, void* ws, double* loss, float* grad, hipStream_t s);
 // One bias-corrected Adam step over n fp32 parameters (optional fp16 copy).
+// Densify / prune of the positions (densify.hip)
+struct DensifyIn {
+    const float* xyzt;        // [N][4]
+    const float* grad_acc;    // [N]
+    const int32_t* grad_count;
+    const float* scales;      // [N][3] decoded
+    const float* quats;       // [N][4] decoded
+    const float* opacity;     // [N] decoded
+    const float* noise;       // [N][2][3] standard normal draws
+    const float* m;           // [N][3] Adam moments of the positions
+    const float* v;
+    int64_t N;
+    float grad_threshold, scale_threshold, min_opacity;
+    float* out_xyzt;          // [2N][4]
+    float* out_m;             // [2N][3]
+    float* out_v;
+    int64_t* out_n;           // device: rows written
+};
+size_t densify_workspace(int64_t N);
+hipError_t launch_densify(const DensifyIn& in, void* ws, hipStream_t s);
+hipError_t launch_densify_accumulate(const float* g, int64_t N, float* acc, int32_t* cnt, hipStream_t s);
+
 // Stable LSD radix sort of the first min(*count, cap) 64-bit words of buf[0]
 // on bits [lo, lo + nbits) (render.hip); returns the index (0 or 1) of the
 // buffer of buf that holds the result.  max_blocks <= radix_sort_blocks(cap);

@@ -32,6 +32,7 @@ EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_de
            "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform", "ia_hexplane_destroy",
            "ia_render_workspace_size", "ia_render", "ia_render_set_binning", "ia_render_backward", "ia_l1_loss",
            "ia_image_loss_workspace_size", "ia_image_loss", "ia_adam_step", "ia_adam_step_strided",
+           "ia_densify_accumulate", "ia_densify_workspace_size", "ia_densify",
            "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
 
 
@@ -125,6 +126,9 @@ def load(path: str = LIB_PATH):
         L.ia_adam_step_strided.argtypes = [P, C.c_int32, C.c_int32, P, P, P, C.c_int64, C.c_float, C.c_float,
                                            C.c_float, C.c_float, C.c_int32, P]
         L.ia_decoder_update_params.argtypes = [P, P, P, P, P]
+        L.ia_densify_accumulate.argtypes = [P, C.c_int64, P, P, P]
+        L.ia_densify_workspace_size.argtypes = [C.c_int64, P]
+        L.ia_densify.argtypes = [P, P, P, P, P, P, P, P, P, C.c_int64, P, P, P, P, C.c_int64, P, P, C.c_size_t, P]
         L.ia_profile_enable.argtypes = [C.c_int32]
         L.ia_profile_report.argtypes = [P, C.c_size_t, P]
         L.ia_profile_reset.argtypes = []
@@ -320,6 +324,30 @@ def ia_adam_step_strided(param, grad, m, v, lr: float, beta1: float, beta2: floa
     _check(load().ia_adam_step_strided(_ptr(param), int(param.stride(0)), dim, _ptr(grad), _ptr(m), _ptr(v), rows,
                                        float(lr), float(beta1), float(beta2), float(eps), int(step),
                                        _stream(stream)))
+
+
+class DensifyParams(C.Structure):
+    _fields_ = [("grad_threshold", C.c_float), ("scale_threshold", C.c_float), ("min_opacity", C.c_float)]
+
+
+def ia_densify_accumulate(grad_pos, grad_acc, grad_count, stream=None):
+    _check(load().ia_densify_accumulate(_ptr(grad_pos), int(grad_pos.shape[0]), _ptr(grad_acc), _ptr(grad_count),
+                                        _stream(stream)))
+
+
+def ia_densify_workspace_size(N: int) -> int:
+    n = C.c_size_t()
+    _check(load().ia_densify_workspace_size(int(N), C.byref(n)))
+    return int(n.value)
+
+
+def ia_densify(xyzt, grad_acc, grad_count, scales, quats, opacity, noise, m, v, params: DensifyParams, out_xyzt,
+               out_m, out_v, out_n, ws, stream=None):
+    """All device tensors; out_* of >= 2 N rows; out_n: int64 [1]."""
+    _check(load().ia_densify(_ptr(xyzt), _ptr(grad_acc), _ptr(grad_count), _ptr(scales), _ptr(quats),
+                             _ptr(opacity), _ptr(noise), _ptr(m), _ptr(v), int(xyzt.shape[0]), C.byref(params),
+                             _ptr(out_xyzt), _ptr(out_m), _ptr(out_v), int(out_xyzt.shape[0]), _ptr(out_n),
+                             _ptr(ws), 0 if ws is None else int(ws.numel() * ws.element_size()), _stream(stream)))
 
 
 # ----------------------------------------------------------------- diagnostics

@@ -360,3 +360,23 @@ class Adam:
                 if g.get("f16") is not None:
                     raise ValueError(f"group {name}: an fp16 mirror needs a contiguous parameter")
                 ia.ia_adam_step_strided(p, grad.contiguous(), m, v, lr, self.beta1, self.beta2, self.eps, self.t)
+
+
+def densify_positions(xyzt, grad_acc, grad_count, attrs: dict, m, v, noise, grad_threshold: float,
+                      scale_threshold: float, min_opacity: float):
+    """Refine the positions ([SPIN] §3.2 Eq. 6; clone / split / prune, see
+    ia_densify) from the decoded attributes `attrs` (scales, quats, opacity).
+    Returns (xyzt', m', v') of the rows written; reading their count is the
+    one host synchronisation."""
+    N = int(xyzt.shape[0])
+    dev = xyzt.device
+    out_x = torch.empty((2 * N, 4), device=dev)
+    out_m = torch.empty((2 * N, 3), device=dev)
+    out_v = torch.empty((2 * N, 3), device=dev)
+    out_n = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(ia.ia_densify_workspace_size(N), 256), dtype=torch.uint8, device=dev)
+    p = ia.DensifyParams(grad_threshold, scale_threshold, min_opacity)
+    ia.ia_densify(xyzt.contiguous(), grad_acc, grad_count, attrs["scales"], attrs["quats"], attrs["opacity"],
+                  noise.contiguous(), m.contiguous(), v.contiguous(), p, out_x, out_m, out_v, out_n, ws)
+    n = int(out_n.item())
+    return out_x[:n], out_m[:n], out_v[:n]

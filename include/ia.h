@@ -417,6 +417,50 @@ IA_API ia_status ia_adam_step_strided(float* param, int32_t param_stride, int32_
                                       float* v, int64_t rows, float lr, float beta1, float beta2, float eps,
                                       int32_t step, void* stream);
 
+/* Refinement of the positions ([SPIN] §3.2 Eq. 6: the rendering loss
+ * densifies salient points and prunes unnecessary ones; the rule is read as
+ * 3D Gaussian Splatting's adaptive density control on the trainable
+ * positions, the other attributes being decoded):
+ *   prune  decoded opacity < min_opacity (first);
+ *   salient  grad_count > 0 and grad_acc / grad_count >= grad_threshold
+ *          (one fp32 division);
+ *   clone  salient and max(scale) <= scale_threshold: the Gaussian (with its
+ *          moments) and a copy at the same position (moments 0);
+ *   split  salient and larger: two Gaussians at mu + R(q) (s * n_j), j = 0, 1,
+ *          n = noise[i][j][0..2] (standard normal draws the caller supplies),
+ *          time carried over, moments 0;
+ *   keep   otherwise, with its moments.
+ * Outputs keep the input order (a Gaussian's rows follow its predecessors').
+ * All arrays are device memory:
+ *   xyzt [N][4] (16-byte aligned), grad_acc [N], grad_count [N] (as left by
+ *   ia_densify_accumulate), scales [N][3], quats [N][4] (w,x,y,z, any
+ *   non-zero norm), opacity [N] (decoded), noise [N][2][3], m, v [N][3] (the
+ *   positions' Adam moments);
+ *   out_xyzt [out_capacity][4] (16-byte aligned), out_m, out_v
+ *   [out_capacity][3], out_capacity >= 2 N; out_n: device int64, the rows
+ *   written (no host synchronisation);
+ *   ws: ia_densify_workspace_size bytes, contents undefined between calls.
+ * The accumulators are not reset here (zero them after a densification).
+ * Errors: INVALID_ARG (null, N < 0, out_capacity < 2 N, misalignment,
+ * negative thresholds), WORKSPACE_TOO_SMALL, DEVICE. */
+typedef struct {
+    float grad_threshold;  /* mean position-gradient norm that makes a Gaussian salient */
+    float scale_threshold; /* largest decoded scale up to which a salient one is cloned */
+    float min_opacity;     /* decoded opacity below which a Gaussian is pruned        */
+} ia_densify_params;
+
+/* grad_acc[i] += |grad_pos[i]| and grad_count[i] += 1 for every Gaussian whose
+ * position gradient (device [N][3]) is not zero; |.| is sqrtf((x^2 + y^2) + z^2).
+ * Errors: INVALID_ARG, DEVICE. */
+IA_API ia_status ia_densify_accumulate(const float* grad_pos, int64_t N, float* grad_acc, int32_t* grad_count,
+                                       void* stream);
+IA_API ia_status ia_densify_workspace_size(int64_t N, size_t* bytes);
+IA_API ia_status ia_densify(const float* xyzt, const float* grad_acc, const int32_t* grad_count, const float* scales,
+                            const float* quats, const float* opacity, const float* noise, const float* m,
+                            const float* v, int64_t N, const ia_densify_params* params, float* out_xyzt,
+                            float* out_m, float* out_v, int64_t out_capacity, int64_t* out_n, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* How ia_render turns depth-ordered Gaussians into per-tile lists.  Both give
  * the same lists; they differ in speed.
  *   0  automatic (default): regions when visible Gaussians touch 4 or more
