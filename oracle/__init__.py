@@ -371,6 +371,18 @@ def sh_colors(cams, frame_offsets, means, sh) -> np.ndarray:
     return rgb
 
 
+def sh_colors_grad(cams, frame_offsets, means, sh, gcol):
+    """Backward of sh_colors for dL/drgb = gcol [N,3]: (dL/dsh [N,16,3],
+    dL/dmeans [N,3] through the view direction)."""
+    fo = _c(frame_offsets, np.int64)
+    means, sh, gcol = _c(means, np.float32), _c(sh, np.float32), _c(gcol, np.float64)
+    N = means.shape[0]
+    gsh = np.zeros((max(N, 1), 48))
+    gm = np.zeros((max(N, 1), 3))
+    lib().orc_sh_colors_grad(cameras(cams), len(cams), _p(fo), _p(means), _p(sh), _p(gcol), _p(gsh), _p(gm))
+    return gsh[:N].reshape(N, 16, 3), gm[:N]
+
+
 def bin_and_sort(cams, frame_offsets, pre: dict, cap: int | None = None) -> dict:
     fo = _c(frame_offsets, np.int64)
     F, W, H = len(cams), int(cams[0].W), int(cams[0].H)

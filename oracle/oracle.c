@@ -622,6 +622,70 @@ EXPORT void orc_sh_colors(const orc_camera* cams, int F, const long* frame_offse
     }
 }
 
+/*
+ * Backward of orc_sh_colors for a colour gradient gcol = dL/drgb [N][3]:
+ *   dL/dsh_k,ch = gcol_ch Y_k(dir) where sum_k sh_k,ch Y_k + 0.5 > 0, else 0
+ *   dL/dmean    = (I - dir dir^T) / |mu - centre| . sum_ch,k gcol_ch [>0] sh_k,ch grad Y_k
+ * with grad Y_k the derivative of the basis polynomials of orc_sh_basis in
+ * (x, y, z), projected onto the sphere by the normalisation's Jacobian.
+ * Outputs gsh [N][48] (k-major like sh) and gmeans [N][3] (overwritten).
+ */
+EXPORT void orc_sh_colors_grad(const orc_camera* cams, int F, const long* frame_offsets, const float* means,
+                               const float* sh, const double* gcol, double* gsh, double* gmeans) {
+    const double pi = 3.14159265358979323846;
+    const double k1 = sqrt(3.0 / (4.0 * pi));
+    const double k2a = 0.5 * sqrt(15.0 / pi), k2b = 0.25 * sqrt(5.0 / pi), k2c = 0.25 * sqrt(15.0 / pi);
+    const double k3a = 0.25 * sqrt(35.0 / (2.0 * pi)), k3b = 0.5 * sqrt(105.0 / pi);
+    const double k3c = 0.25 * sqrt(21.0 / (2.0 * pi)), k3d = 0.25 * sqrt(7.0 / pi);
+    const double k3e = 0.25 * sqrt(105.0 / pi);
+    long N = frame_offsets[F];
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < N; ++i) {
+        const orc_camera* c = &cams[frame_of(frame_offsets, F, i)];
+        double ctr[3];
+        for (int k = 0; k < 3; ++k)
+            ctr[k] = -((double)c->R[0 * 3 + k] * c->t[0] + (double)c->R[1 * 3 + k] * c->t[1] +
+                       (double)c->R[2 * 3 + k] * c->t[2]);
+        double d[3], n = 0.0;
+        for (int k = 0; k < 3; ++k) { d[k] = (double)means[i * 3 + k] - ctr[k]; n += d[k] * d[k]; }
+        n = sqrt(n);
+        for (int k = 0; k < 3; ++k) d[k] /= n;
+        double Y[16];
+        orc_sh_basis(d, 1, Y);
+        const double x = d[0], y = d[1], z = d[2], xx = x * x, yy = y * y, zz = z * z;
+        /* dY_k / d(x, y, z) */
+        const double dY[16][3] = {
+            {0, 0, 0},
+            {0, -k1, 0},
+            {0, 0, k1},
+            {-k1, 0, 0},
+            {k2a * y, k2a * x, 0},
+            {0, -k2a * z, -k2a * y},
+            {-2 * k2b * x, -2 * k2b * y, 4 * k2b * z},
+            {-k2a * z, 0, -k2a * x},
+            {2 * k2c * x, -2 * k2c * y, 0},
+            {-6 * k3a * x * y, -k3a * (3 * xx - 3 * yy), 0},
+            {k3b * y * z, k3b * x * z, k3b * x * y},
+            {2 * k3c * x * y, -k3c * (4 * zz - xx - 3 * yy), -8 * k3c * y * z},
+            {-6 * k3d * x * z, -6 * k3d * y * z, k3d * (6 * zz - 3 * xx - 3 * yy)},
+            {-k3c * (4 * zz - 3 * xx - yy), 2 * k3c * x * y, -8 * k3c * x * z},
+            {2 * k3e * x * z, -2 * k3e * y * z, k3e * (xx - yy)},
+            {-k3a * (3 * xx - 3 * yy), 6 * k3a * x * y, 0}};
+        double gd[3] = {0, 0, 0};
+        for (int ch = 0; ch < 3; ++ch) {
+            double s = 0.5;
+            for (int k = 0; k < 16; ++k) s += (double)sh[i * 48 + k * 3 + ch] * Y[k];
+            const double g = s > 0.0 ? gcol[i * 3 + ch] : 0.0;
+            for (int k = 0; k < 16; ++k) {
+                gsh[i * 48 + k * 3 + ch] = g * Y[k];
+                for (int a = 0; a < 3; ++a) gd[a] += g * (double)sh[i * 48 + k * 3 + ch] * dY[k][a];
+            }
+        }
+        const double dot = d[0] * gd[0] + d[1] * gd[1] + d[2] * gd[2];
+        for (int a = 0; a < 3; ++a) gmeans[i * 3 + a] = (gd[a] - d[a] * dot) / n;
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Binning and sort (16x16 tiles)                                             */
 /* ------------------------------------------------------------------------ */
