@@ -750,8 +750,8 @@ ia_status ia_render_backward(const ia_gaussians* g, const int64_t* frame_offsets
     int W = 0, H = 0;
     ia_status st = check_render_args(g, frame_offsets, frames, cams, ws, ws_bytes, max_entries, &N, &W, &H);
     if (st != IA_OK) return st;
-    if (N > 0 && g->sh_degree != -1)
-        return fail(IA_ERR_UNSUPPORTED, "the render backward takes direct colours (sh_degree = -1)");
+    if (N > 0 && g->sh_degree == 3 && !grads->sh)
+        return fail(IA_ERR_INVALID_ARG, "grads->sh must be non-null when sh_degree = 3");
     if (!grad_image || !T_final || !n_contrib) return fail(IA_ERR_INVALID_ARG, "grad_image, T_final, n_contrib must be non-null");
     if (N > 0 && (!grads->means || !grads->scales || !grads->quats || !grads->opacity || !grads->colors))
         return fail(IA_ERR_INVALID_ARG, "every gradient buffer must be non-null");
@@ -772,6 +772,8 @@ ia_status ia_render_backward(const ia_gaussians* g, const int64_t* frame_offsets
     a.g_quats = grads->quats;
     a.g_opacity = grads->opacity;
     a.g_colors = grads->colors;
+    a.sh = g->sh_degree == 3 ? g->sh : nullptr;
+    a.g_sh = g->sh_degree == 3 ? grads->sh : nullptr;
     hipError_t e = ia::launch_render_backward(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "render backward launch");
     return IA_OK;

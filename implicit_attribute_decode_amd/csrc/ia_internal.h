@@ -227,6 +227,8 @@ struct RenderBwdArgs {
     float* g_quats;  // [N,4]
     float* g_opacity;
     float* g_colors;
+    const float* sh;  // [N,16,3] when the colours are degree-3 SH, else null
+    float* g_sh;      // [N,16,3] out with sh
 };
 
 hipError_t launch_render_backward(const RenderBwdArgs& a, hipStream_t s);

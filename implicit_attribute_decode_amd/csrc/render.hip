@@ -143,28 +143,6 @@ struct PreArgs {
     uint32_t* bsum_t;  // per block: tiles touched
 };
 
-// Degree-3 real spherical harmonics (orthonormal, l-major, m = -l..l, the
-// Condon-Shortley sign convention) at unit direction (x, y, z).
-__device__ __forceinline__ void sh_basis16(float x, float y, float z, float Y[16]) {
-    const float xx = x * x, yy = y * y, zz = z * z;
-    Y[0] = 0.28209479177387814f;
-    Y[1] = -0.48860251190291992f * y;
-    Y[2] = 0.48860251190291992f * z;
-    Y[3] = -0.48860251190291992f * x;
-    Y[4] = 1.0925484305920792f * x * y;
-    Y[5] = -1.0925484305920792f * y * z;
-    Y[6] = 0.31539156525252005f * (2.0f * zz - xx - yy);
-    Y[7] = -1.0925484305920792f * x * z;
-    Y[8] = 0.54627421529603959f * (xx - yy);
-    Y[9] = -0.59004358992664352f * y * (3.0f * xx - yy);
-    Y[10] = 2.8906114426405538f * x * y * z;
-    Y[11] = -0.45704579946446572f * y * (4.0f * zz - xx - yy);
-    Y[12] = 0.37317633259011546f * z * (2.0f * zz - 3.0f * xx - 3.0f * yy);
-    Y[13] = -0.45704579946446572f * x * (4.0f * zz - xx - yy);
-    Y[14] = 1.4453057213202769f * z * (xx - yy);
-    Y[15] = -0.59004358992664352f * x * (xx - 3.0f * yy);
-}
-
 __global__ void __launch_bounds__(kBlock) preprocess_kernel(PreArgs a) {
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     uint32_t ntouch = 0;

@@ -282,6 +282,8 @@ struct PreBwdArgs {
     float* g_quats;
     float* g_opacity;
     float* g_colors;
+    const float* sh;  // degree-3 SH colours, or null
+    float* g_sh;
 };
 
 __device__ __forceinline__ int frame_index(const int64_t* fo, int F, int64_t i) {
@@ -403,6 +405,48 @@ __global__ void __launch_bounds__(256) preprocess_backward_kernel(PreBwdArgs a) 
         gq[2] = (gn[2] - dot * y) / qlen;
         gq[3] = (gn[3] - dot * z) / qlen;
     }
+    if (a.sh) {
+        // colour = max(0, sum_k sh_k Y_k(dir) + 1/2), dir = normalize(mu - centre)
+        // (as the forward evaluates it): dL/dsh_k = dL/dc Y_k where the sum is
+        // positive, and the view direction's share of dL/dmu
+        float* gsh = a.g_sh + i * 48;
+        if (vis) {
+            const DevCamera& cam = a.cams[frame_index(a.fo, a.F, i)];
+            const float* mu = a.means + i * a.stride;
+            const float d0 = mu[0] - cam.centre[0], d1 = mu[1] - cam.centre[1], d2 = mu[2] - cam.centre[2];
+            const float inv = 1.0f / sqrtf(d0 * d0 + d1 * d1 + d2 * d2);
+            const float x = d0 * inv, y = d1 * inv, z = d2 * inv;
+            float Y[16];
+            sh_basis16(x, y, z, Y);
+            const float* shc = a.sh + i * 48;
+            float acc[3] = {0.5f, 0.5f, 0.5f};
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                acc[0] += shc[k * 3 + 0] * Y[k];
+                acc[1] += shc[k * 3 + 1] * Y[k];
+                acc[2] += shc[k * 3 + 2] * Y[k];
+            }
+            float gc[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) gc[c] = acc[c] > 0.0f ? gi[6 + c] : 0.0f;
+            float wk[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                gsh[k * 3 + 0] = gc[0] * Y[k];
+                gsh[k * 3 + 1] = gc[1] * Y[k];
+                gsh[k * 3 + 2] = gc[2] * Y[k];
+                wk[k] = (gc[0] * shc[k * 3 + 0] + gc[1] * shc[k * 3 + 1]) + gc[2] * shc[k * 3 + 2];
+            }
+            float gd[3];
+            sh_basis16_grad(x, y, z, wk, gd);
+            const float dot = (x * gd[0] + y * gd[1]) + z * gd[2];
+            gmu[0] += (gd[0] - x * dot) * inv;
+            gmu[1] += (gd[1] - y * dot) * inv;
+            gmu[2] += (gd[2] - z * dot) * inv;
+        } else {
+            for (int k = 0; k < 48; ++k) gsh[k] = 0.0f;
+        }
+    }
     for (int k = 0; k < 3; ++k) {
         a.g_means[i * 3 + k] = gmu[k];
         a.g_scales[i * 3 + k] = gs[k];
@@ -473,7 +517,7 @@ hipError_t launch_render_backward(const RenderBwdArgs& a, hipStream_t s) {
                   dim3(256), 0, s, rb);
     PreBwdArgs pb{a.means, a.means_stride, a.scales, a.quats, cams, fo, L.frames, N,
                   reinterpret_cast<const uint32_t*>(ws + L.tiles), gacc, a.g_means, a.g_scales, a.g_quats,
-                  a.g_opacity, a.g_colors};
+                  a.g_opacity, a.g_colors, a.sh, a.g_sh};
     IA_LAUNCH("preprocess_backward_kernel", preprocess_backward_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0,
               s, pb);
     return hipGetLastError();

@@ -83,7 +83,7 @@ class DecoderGrads(C.Structure):
 
 class GaussianGrads(C.Structure):
     _fields_ = [("means", C.c_void_p), ("scales", C.c_void_p), ("quats", C.c_void_p), ("opacity", C.c_void_p),
-                ("colors", C.c_void_p)]
+                ("colors", C.c_void_p), ("sh", C.c_void_p)]
 
 
 _lib = None

@@ -263,7 +263,8 @@ class Renderer:
         """Gradients of the render `res` (made by render(..., aux=True) with
         the same g, frame_offsets, cams, max_entries and this workspace) for
         dL/dimage = grad_image.  Returns dict means, scales, quats, opacity,
-        colors (cuda float32, packed rows)."""
+        colors and, for SH colours, sh [N,16,3] (cuda float32, packed rows;
+        the means include the view direction's share)."""
         fo = np.asarray(frame_offsets, np.int64)
         N = int(fo[-1])
         F, W, H = len(cams), int(cams[0].W), int(cams[0].H)
@@ -275,7 +276,9 @@ class Renderer:
         out = {k: torch.empty(shape, device=self.device)
                for k, shape in (("means", (N, 3)), ("scales", (N, 3)), ("quats", (N, 4)), ("opacity", (N,)),
                                 ("colors", (N, 3)))}
-        GG = ia.GaussianGrads(*[ia._ptr(out[k]) for k in ("means", "scales", "quats", "opacity", "colors")])
+        if g.get("sh") is not None:
+            out["sh"] = torch.empty((N, 16, 3), device=self.device)
+        GG = ia.GaussianGrads(*[ia._ptr(out.get(k)) for k in ("means", "scales", "quats", "opacity", "colors", "sh")])
         ia.ia_render_backward(G, fo, cams, ws, max_entries, grad_image.contiguous(), res["T_final"],
                               res["n_contrib"], GG)
         return out

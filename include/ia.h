@@ -344,7 +344,10 @@ typedef struct {
     float* scales;  /* [N][3] dL/dscale                                  */
     float* quats;   /* [N][4] dL/dquaternion (of the unnormalised input) */
     float* opacity; /* [N]    dL/dopacity                                */
-    float* colors;  /* [N][3] dL/dcolour                                 */
+    float* colors;  /* [N][3] dL/dcolour (the rendered colour)           */
+    float* sh;      /* [N][16][3] dL/dsh when the render used sh_degree 3
+                     * (then also added into means: the view direction's
+                     * share); unused otherwise                           */
 } ia_gaussian_grads;
 
 /* Backward of ia_render for an image-space gradient ([SPIN] §3.1 Eq. 1-4,
@@ -361,9 +364,12 @@ typedef struct {
  * passes no gradient to opacity or position.  Per-Gaussian partials are
  * summed with float atomics, so results vary in the last bits from run to
  * run.  The chain to means, scales and quaternions is through the conic
- * inverse, Sigma2D = J W Sigma W^T J^T and Sigma = R S S^T R^T.
- * Errors: INVALID_ARG, UNSUPPORTED (sh_degree other than -1),
- * WORKSPACE_TOO_SMALL, DEVICE. */
+ * inverse, Sigma2D = J W Sigma W^T J^T and Sigma = R S S^T R^T.  With
+ * degree-3 SH colours (sh_degree 3, grads->sh required) the colour gradient
+ * is chained through colour = max(0, sum_k sh_k Y_k(dir) + 1/2) to
+ * grads->sh, and through dir = normalize(mu - camera centre) into
+ * grads->means.
+ * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, DEVICE. */
 IA_API ia_status ia_render_backward(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames,
                                     const ia_camera* cams, void* ws, size_t ws_bytes, int64_t max_entries,
                                     const float* grad_image, const float* T_final, const uint32_t* n_contrib,

@@ -184,15 +184,75 @@ def test_backward_culled_and_empty():
     assert all(grads[k].numel() == 0 for k in GROUPS)
 
 
-def test_backward_rejects_sh_and_missing_buffers():
+def _sh_attrs(rng, g, scale):
+    attrs = _attrs(g)
+    attrs.pop("colors")
+    sh = (scale * rng.normal(0, 1, (len(g.means), 16, 3))).astype(np.float32)
+    attrs["sh"] = cuda(sh)
+    return attrs, sh
+
+
+def test_backward_with_sh_colours_matches_oracle():
+    """Render with degree-3 SH colours, backward of a random dL/dimage: the
+    oracle differentiates the render with its fp64 SH colours, then chains
+    dL/dcolour through the SH colour (sh_colors_grad) to dL/dsh and the view
+    direction's share of dL/dmean."""
+    rng = np.random.default_rng(47)
+    n = 3000
+    g = S.render_attributes(rng, S.shell_points(rng, n, 1.0), 0.01, 0.05)
+    attrs, sh = _sh_attrs(rng, g, 0.05)  # every channel stays far above the clamp at 0
+    fo = np.array([0, n // 2, n])
+    cams = [S.ring_camera(0, W=160, H=120, fx=150.0, fy=150.0), S.ring_camera(4, W=160, H=120, fx=150.0, fy=150.0)]
+    R = Renderer()
+    res = R.render(attrs, fo, cams, 1 << 20, aux=True)
+    torch.cuda.synchronize()
+    assert int(res["overflow"].item()) == 0
+    gimg = _normal_grad(48)(res["image"])
+    grads = R.backward(attrs, fo, cams, 1 << 20, res, gimg)
+    torch.cuda.synchronize()
+    col = O.sh_colors(cams, fo, g.means, sh)
+    ref = O.render_grad(cams, fo, g.means.astype(np.float64), g.scales.astype(np.float64),
+                        g.quats.astype(np.float64), g.opacity.astype(np.float64), col, host(gimg).astype(np.float64))
+    gsh, gdir = O.sh_colors_grad(cams, fo, g.means, sh, ref["colors"])
+    ref = dict(ref, means=ref["means"] + gdir)
+    _compare("sh", grads, ref)
+    keep = ~ref["flags"]
+    a = host(grads["sh"]).astype(np.float64).reshape(n, 48)[keep]
+    b = gsh.reshape(n, 48)[keep]
+    err = np.abs(a - b)
+    assert np.all(err <= 2e-4 * np.abs(b) + 2e-5 * np.abs(b).max()), float(err.max())
+    assert np.abs(gdir[keep]).max() > 1e-3 * np.abs(ref["means"][keep]).max()  # the direction term matters
+
+
+def test_backward_sh_clamped_channel_has_no_gradient():
+    rng = np.random.default_rng(49)
+    n = 500
+    g = S.render_attributes(rng, S.shell_points(rng, n, 1.0), 0.01, 0.05)
+    attrs, sh = _sh_attrs(rng, g, 0.05)
+    sh[:, 0, 1] = -5.0  # green below zero for every Gaussian
+    attrs["sh"] = cuda(sh)
+    cams = [S.ring_camera(0, W=96, H=64, fx=90.0, fy=90.0)]
+    R = Renderer()
+    res = R.render(attrs, [0, n], cams, 1 << 18, aux=True)
+    grads = R.backward(attrs, [0, n], cams, 1 << 18, res, _normal_grad(50)(res["image"]))
+    torch.cuda.synchronize()
+    gs = host(grads["sh"])
+    assert not gs[:, :, 1].any() and np.abs(gs[:, :, 0]).max() > 0
+
+
+def test_backward_rejects_missing_sh_buffer():
     rng = np.random.default_rng(46)
     g = S.render_attributes(rng, S.shell_points(rng, 10, 3.0), 0.02, 0.1)
-    attrs = _attrs(g)
+    attrs, _ = _sh_attrs(rng, g, 0.05)
     cam = S.origin_camera(32, 32, 40.0)
     R = Renderer()
     res = R.render(attrs, np.array([0, 10]), [cam], 256, aux=True)
-    sh_attrs = dict(attrs, sh=torch.zeros((10, 48), device="cuda"))
-    sh_attrs.pop("colors")
+    G = ia.gaussians(means=attrs["means"], scales=attrs["scales"], quats=attrs["quats"], sh=attrs["sh"],
+                     opacity=attrs["opacity"], means_stride=3, sh_degree=3)
+    out = [torch.empty(sh, device="cuda") for sh in ((10, 3), (10, 3), (10, 4), (10,), (10, 3))]
+    GG = ia.GaussianGrads(*[ia._ptr(t) for t in out], None)
+    ws = R.workspace(10, 1, 32, 32, 256)
     with pytest.raises(ia.IAError) as e:
-        R.backward(sh_attrs, np.array([0, 10]), [cam], 256, res, torch.ones_like(res["image"]))
-    assert e.value.status == ia.IA_ERR_UNSUPPORTED
+        ia.ia_render_backward(G, np.array([0, 10]), [cam], ws, 256, torch.ones_like(res["image"]), res["T_final"],
+                              res["n_contrib"], GG)
+    assert e.value.status == ia.IA_ERR_INVALID_ARG
