@@ -42,7 +42,7 @@ DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
 # and batched gather launches), the factors being what the counters read for a 1 GiB device copy
 # (profiles/gather_f16_sequence_hbm_traffic.md).  Valid for the gather kernels as they were when
 # counted; null once they change.
-GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 614_388.4 + 235_684.2) * 1024
+GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 614_520.0 + 235_675.0) * 1024
 
 
 def log(*a):
