@@ -8,7 +8,7 @@
 //              forward fed the MLP); x~ is renormalised either way.
 //   compaction the Gaussians whose upstream gradient is not all zero (the
 //              others have exactly zero decoder gradients), then ordered by a
-//              key of 8 bits of time over a 24-bit Morton code of the
+//              key of 6 bits of time over a 24-bit Morton code of the
 //              normalised position (stable radix sort: index order within a
 //              key), so that the Gaussians of one block lie close together
 //              and share the corners of the coarser levels; the two kernels
@@ -732,10 +732,11 @@ __device__ __forceinline__ uint32_t spread3(float v) {
     return q;
 }
 
-// sort key of a normalised position: 8 bits of time above the 24-bit Morton
-// code of x, y, z
+// sort key of a normalised position: 6 bits of time above the 24-bit Morton
+// code of x, y, z (30 bits: three 10-bit radix passes)
 __device__ __forceinline__ uint32_t spatial_key(float4 p) {
-    return (spread3(p.w) << 24) | spread3(p.x) | (spread3(p.y) << 1) | (spread3(p.z) << 2);
+    const uint32_t tq = (uint32_t)(fminf(fmaxf(p.w, 0.0f), 1.0f) * 63.0f);
+    return (tq << 24) | spread3(p.x) | (spread3(p.y) << 1) | (spread3(p.z) << 2);
 }
 
 __global__ void __launch_bounds__(256) active_write_kernel(const float* gs, const float* gq, const float* gc,
@@ -864,8 +865,8 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         IA_LAUNCH("active_scan_kernel", active_scan_kernel, dim3(1), dim3(256), 0, s, boff, nb, count, srt.count);
         IA_LAUNCH("active_write_kernel", active_write_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
                   b.g_colors, b.g_opacity, off, n, boff, xt, srt.items[0]);
-        // stable sort on the 32 key bits above the index
-        const int cur = radix_sort_u64(srt.items, srt.count, (uint64_t)chunk, 32, 32, srt.max_blocks, srt.counts,
+        // stable sort on the 30 key bits above the index
+        const int cur = radix_sort_u64(srt.items, srt.count, (uint64_t)chunk, 32, 30, srt.max_blocks, srt.counts,
                                        srt.digit_tot, s);
         IA_LAUNCH("unpack_list_kernel", unpack_list_kernel, dim3(blocks_for(n, 256, 2048)), dim3(256), 0, s,
                   srt.items[cur], count, list);
