@@ -350,6 +350,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--parts", type=int, default=1,
+                    help="groups of frames; each group's render overlaps the next group's decode")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--frames", type=int, default=150)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -368,7 +370,7 @@ def main():
     import torch
 
     from implicit_attribute_decode_amd import ia, scenes as S
-    from implicit_attribute_decode_amd.pipeline import Decoder, HexPlane, Renderer
+    from implicit_attribute_decode_amd.pipeline import Decoder, HexPlane, PipelinedDecodeRender, Renderer
 
     ia.load()  # fails loudly when the HIP library is missing
     if args.only:
@@ -397,18 +399,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     D = Decoder(dec)
-    R = Renderer()
-    g = dict(means=xyzt[:, :3], **attrs)
-    D.decode_xyzt(xyzt, out=attrs)
-    probe = R.render(g, fo, cams, 4 * N, aux=True, out={"image": image})
-    E = Renderer.count_entries(probe)
-    cap = int(E * 1.02) + 4096
-    del probe
-    log(f"tile entries: {E}, capacity {cap}")
-
-    def step():
-        D.decode_xyzt(xyzt, out=attrs)
-        R.render(g, fo, cams, cap, out={"image": image})
+    # frames in `parts` groups: group k renders on a second stream beside the
+    # decode of group k + 1
+    step = PipelinedDecodeRender(D, xyzt, fo, cams, attrs, image, args.parts)
+    E = step.probe()
+    log(f"tile entries: {E}, {args.parts} groups")
 
     for _ in range(args.warmup):
         step()
@@ -482,7 +477,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"sequence: {F} frames x {per} Gaussians = {N} (x,y,z,t), 640x360, "
                                "27-camera ring, 16-level fp16 hash (2^19), 32-64-64-11 GELU decoder",
-                   "frames": F, "gaussians_per_frame": per, "tile_entries": E,
+                   "frames": F, "gaussians_per_frame": per, "tile_entries": E, "frame_groups": args.parts,
                    "kernels": kernels, "kernel_rooflines": kernel_rooflines, **extra},
         "roofline": {"kernel": "gather_f16_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -383,3 +383,59 @@ def densify_positions(xyzt, grad_acc, grad_count, attrs: dict, m, v, noise, grad
                   noise.contiguous(), m.contiguous(), v.contiguous(), p, out_x, out_m, out_v, out_n, ws)
     n = int(out_n.item())
     return out_x[:n], out_m[:n], out_v[:n]
+
+
+class PipelinedDecodeRender:
+    """Decode + render of a batch of frames whose Gaussians are stored frame
+    after frame, in `parts` consecutive groups of frames: the render of group k
+    runs on a second stream (default priority) beside the decode of group
+    k + 1.  The decode's gather is bound by L2 requests and the raster by VALU
+    issue, so the two share the chip well.  Every group has its own render
+    workspace; images and decoded attributes land in the caller's tensors.
+    Results equal one decode and one render of the whole batch, bit for bit
+    when every group starts at a multiple of 64 Gaussians (a decoded value's
+    MFMA rounding depends on its index mod 64 within a decode call), else to
+    the decoder's tolerance."""
+
+    def __init__(self, decoder: Decoder, xyzt: torch.Tensor, frame_offsets, cams, attrs: dict,
+                 image: torch.Tensor, parts: int):
+        fo = np.asarray(frame_offsets, np.int64)
+        F = len(cams)
+        if not 1 <= parts <= F:
+            raise ValueError("parts must be in 1..frames")
+        self.decoder, self.xyzt = decoder, xyzt
+        self.side = torch.cuda.Stream(device=xyzt.device)
+        bounds = [(F * k) // parts for k in range(parts + 1)]
+        self.groups = []
+        for k in range(parts):
+            f0, f1 = bounds[k], bounds[k + 1]
+            lo, hi = int(fo[f0]), int(fo[f1])
+            out = {n: v[lo:hi] for n, v in attrs.items()}
+            self.groups.append(dict(lo=lo, hi=hi, fo=fo[f0:f1 + 1] - lo, cams=list(cams[f0:f1]), out=out,
+                                    g=dict(means=xyzt[lo:hi, :3], **out), R=Renderer(str(xyzt.device)),
+                                    image=image[f0:f1], cap=None))
+
+    def probe(self, slack: float = 1.02) -> int:
+        """Decode and render once, counting each group's tile entries (host
+        synchronisation); sets the capacities.  Returns the total count."""
+        total = 0
+        for grp in self.groups:
+            self.decoder.decode_xyzt(self.xyzt[grp["lo"]:grp["hi"]], out=grp["out"])
+            n = grp["hi"] - grp["lo"]
+            res = grp["R"].render(grp["g"], grp["fo"], grp["cams"], 4 * max(n, 1), aux=True,
+                                  out={"image": grp["image"]})
+            e = Renderer.count_entries(res)
+            grp["cap"] = int(e * slack) + 4096
+            total += e
+        return total
+
+    def __call__(self):
+        if any(grp["cap"] is None for grp in self.groups):
+            raise RuntimeError("call probe() first")
+        main = torch.cuda.current_stream(self.xyzt.device)
+        for grp in self.groups:
+            self.decoder.decode_xyzt(self.xyzt[grp["lo"]:grp["hi"]], out=grp["out"])
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                grp["R"].render(grp["g"], grp["fo"], grp["cams"], grp["cap"], out={"image": grp["image"]})
+        main.wait_stream(self.side)

@@ -244,3 +244,39 @@ def test_stop_rule_and_clamp_on_gpu():
     sig = 40 * 2.0 / np.array([2.0, 2.5, 3.0, 3.5])
     exp = 1 - np.prod(1 - 0.95 * np.exp(-0.5 * 0.5 / sig ** 2))
     assert abs(gr["image"][0, 0, 16, 16] - exp) < 1e-5
+
+
+def test_pipelined_decode_render_equals_one_batch():
+    """Frames in groups, each group's render on a second stream beside the
+    next group's decode: the same attributes and images, bit for bit, as one
+    decode and one render of the whole batch (frames of a multiple of 64
+    Gaussians, so every group starts where the whole-batch decode has the
+    same MFMA column)."""
+    from implicit_attribute_decode_amd.pipeline import Decoder, PipelinedDecodeRender
+
+    rng = np.random.default_rng(60)
+    F, per = 12, 19_200
+    cams = [S.ring_camera(k, W=160, H=96, fx=120.0, fy=120.0) for k in range(F)]
+    pos = np.concatenate([S.shell_points(rng, F * per, 3.0), np.repeat(np.arange(F) / (F - 1), per)[:, None]], 1)
+    xyzt = torch.as_tensor(pos.astype(np.float32), device="cuda")
+    fo = np.arange(F + 1) * per
+    D = Decoder(S.single_decoder())
+    mk = lambda: ({k: torch.empty((F * per, w), device="cuda") for k, w in (("scales", 3), ("quats", 4), ("colors", 3))}
+                  | {"opacity": torch.empty((F * per,), device="cuda")})
+    a1, img1 = mk(), torch.empty((F, 3, 96, 160), device="cuda")
+    D.decode_xyzt(xyzt, out=a1)
+    R = Renderer()
+    r = R.render(dict(means=xyzt[:, :3], **a1), fo, cams, 64 * F * per, aux=True, out={"image": img1})
+    torch.cuda.synchronize()
+    assert int(r["overflow"].item()) == 0
+    for parts in (2, 5):
+        a2, img2 = mk(), torch.empty_like(img1)
+        run = PipelinedDecodeRender(D, xyzt, fo, cams, a2, img2, parts)
+        run.probe()
+        img2.zero_()
+        run()
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(img1, img2), parts
+        for k in a1:
+            assert torch.equal(a1[k], a2[k]), (parts, k)
