@@ -433,6 +433,11 @@ class PipelinedDecodeRender:
         if any(grp["cap"] is None for grp in self.groups):
             raise RuntimeError("call probe() first")
         main = torch.cuda.current_stream(self.xyzt.device)
+        if len(self.groups) == 1:  # nothing to overlap: one decode, one render, one stream
+            grp = self.groups[0]
+            self.decoder.decode_xyzt(self.xyzt[grp["lo"]:grp["hi"]], out=grp["out"])
+            grp["R"].render(grp["g"], grp["fo"], grp["cams"], grp["cap"], out={"image": grp["image"]})
+            return
         for grp in self.groups:
             self.decoder.decode_xyzt(self.xyzt[grp["lo"]:grp["hi"]], out=grp["out"])
             self.side.wait_stream(main)

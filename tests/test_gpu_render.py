@@ -269,7 +269,7 @@ def test_pipelined_decode_render_equals_one_batch():
     r = R.render(dict(means=xyzt[:, :3], **a1), fo, cams, 64 * F * per, aux=True, out={"image": img1})
     torch.cuda.synchronize()
     assert int(r["overflow"].item()) == 0
-    for parts in (2, 5):
+    for parts in (1, 2, 5):
         a2, img2 = mk(), torch.empty_like(img1)
         run = PipelinedDecodeRender(D, xyzt, fo, cams, a2, img2, parts)
         run.probe()
