@@ -173,8 +173,15 @@ def _hexplane(S, HexPlane, R, stream) -> dict:
     ms_def = timed(lambda: H.deform(canon, 0.5, out=d), 10, stream)
     hex_kernels = profiled(lambda: H.deform(canon, 0.5, out=d), 3)
     ms_ren = timed(lambda: R.render(d, [0, cg.n], [hcam], hcap), 10, stream)
+    # render backward with the SH colours (dL/dsh and the view direction's
+    # share of dL/dmean) for a seeded N(0, 1) image gradient
+    ra = R.render(d, [0, cg.n], [hcam], hcap, aux=True)
+    gimg = torch.randn(ra["image"].shape, generator=torch.Generator(device="cuda").manual_seed(3), device="cuda")
+    R.backward(d, [0, cg.n], [hcam], hcap, ra, gimg)
+    ms_bwd = timed(lambda: R.backward(d, [0, cg.n], [hcam], hcap, ra, gimg), 5, stream)
     tflops = HEX_FLOP_PER_GAUSSIAN * cg.n / (ms_def / 1e3) / 1e12
     return {"gaussians": cg.n, "deform_ms": round(ms_def, 4), "render_ms": round(ms_ren, 4),
+            "render_backward_sh_ms": round(ms_bwd, 4),
             "fps": round(1e3 / (ms_def + ms_ren), 1), "mlp_tflops": round(tflops, 1),
             "mlp_frac_of_fp16_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "deform_kernels_ms": hex_kernels}
 
