@@ -121,3 +121,29 @@ def test_accumulate_matches_fp32_formula():
         want = np.where(nrm > 0, (want + nrm).astype(np.float32), want)
     assert np.array_equal(host(A), want)
     assert np.array_equal(host(Cn), cnt0 + 2 * (nrm > 0))
+
+
+def test_densify_stress_size_sampled():
+    """8M positions (the Stress batch): every decision, the row count and the
+    offsets from the oracle's vectorised rule; 3000 sampled Gaussians' rows
+    against the oracle one by one."""
+    n = 8_000_000
+    case = _case(n, 12)
+    th = (1e-4, 0.05, 0.005)
+    P, M, V = _gpu(*case, th)
+    xyzt, acc, cnt, scales, quats, opac, noise, m, v = case
+    dec = Dn.decide(acc, cnt, scales.max(axis=1), opac, *th)
+    k = np.choose(dec, [0, 1, 2, 2])
+    off = np.concatenate([[0], np.cumsum(k)[:-1]])
+    assert len(P) == int(k.sum())
+    rng = np.random.default_rng(13)
+    for i in rng.choice(n, 3000, replace=False):
+        oP, oM, oV, d1 = Dn.densify(*[a[i:i + 1] for a in case], *th)
+        assert d1[0] == dec[i]
+        rows = slice(off[i], off[i] + k[i])
+        assert np.array_equal(M[rows], oM.astype(np.float32)) and np.array_equal(V[rows], oV.astype(np.float32))
+        if dec[i] == Dn.SPLIT:
+            mag = np.abs(xyzt[i, :3]).max() + 3 * (np.abs(scales[i]) * np.abs(noise[i]).max()).sum()
+            assert np.abs(P[rows, :3] - oP[:, :3]).max() <= 1e-6 * mag
+        else:
+            assert np.array_equal(P[rows], oP.astype(np.float32))

@@ -247,3 +247,18 @@ def test_training_steps_lower_the_loss_and_keep_the_mirrors():
     tab = groups["tables"]
     assert torch.equal(tab["f16"].view(torch.float16), tab["param"].half())
     assert not np.array_equal(host(xyzt)[:, :3], pos[:, :3])
+
+
+def test_image_loss_full_hd_frame():
+    """One 1920 x 1080 frame (the Stress resolution: ragged strips in both
+    directions) against the oracle, every pixel."""
+    rng = np.random.default_rng(31)
+    x = rng.uniform(0, 1, (1, 3, 1080, 1920)).astype(np.float32)
+    y = np.clip(x + rng.normal(0, 0.1, x.shape), 0, 1).astype(np.float32)
+    g_loss, g_grad = _loss(x, y)
+    o = T.image_loss(x, y)
+    err = np.abs(g_grad - o["grad"]).max()
+    say(f"1080p: ssim {g_loss[2]:.7f} vs {o['ssim']:.7f}, grad err {err:.2e} of {np.abs(o['grad']).max():.2e}")
+    assert abs(g_loss[1] - o["l1"]) <= 1e-12 * o["l1"]
+    assert abs(g_loss[2] - o["ssim"]) <= 2e-6
+    assert err <= 2e-5 * np.abs(o["grad"]).max()
