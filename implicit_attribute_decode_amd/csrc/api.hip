@@ -71,6 +71,9 @@ struct ia_decoder {
     uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [2][chunk] float4
     float* bwd_partial = nullptr;  // fp16 path: per-wave weight-gradient partials of the backward
     void* bwd_sort = nullptr;      // fp16 path: the backward's spatial ordering of its active list
+    // per-level position-gradient shares of a backward chunk; allocated by the
+    // first backward that asks for position gradients
+    mutable float4* bwd_pos = nullptr;
     hipStream_t side = nullptr;  // fp16 path: MLP stream overlapping the next chunk's gather
     hipEvent_t ev_gather[2] = {nullptr, nullptr};
     hipEvent_t ev_mlp[2] = {nullptr, nullptr};
@@ -99,6 +102,8 @@ void free_decoder_params(ia_decoder* d) {
     d->bwd_partial = nullptr;
     if (d->bwd_sort) (void)hipFree(d->bwd_sort);
     d->bwd_sort = nullptr;
+    if (d->bwd_pos) (void)hipFree(d->bwd_pos);
+    d->bwd_pos = nullptr;
     for (int k = 0; k < 2; ++k) {
         if (d->ev_gather[k]) (void)hipEventDestroy(d->ev_gather[k]);
         if (d->ev_mlp[k]) (void)hipEventDestroy(d->ev_mlp[k]);
@@ -440,6 +445,14 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
     }
     b.partial = dec->bwd_partial;
     b.sort = dec->bwd_sort;
+    if (grad_pos && N > 0 && !dec->bwd_pos) {
+        hipError_t ea = hipMalloc(reinterpret_cast<void**>(&dec->bwd_pos), ia::decode_bwd_pos_bytes(dec->hash.L));
+        if (ea != hipSuccess) {
+            dec->bwd_pos = nullptr;
+            return fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(ea));
+        }
+    }
+    b.pos_partial = dec->bwd_pos;
     hipError_t e = ia::launch_decode_backward(b, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode backward launch");
     return IA_OK;

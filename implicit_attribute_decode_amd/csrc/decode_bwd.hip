@@ -35,7 +35,9 @@
 //       level), each with four of the 16 corners: dtable[corner] += w dz with
 //       float atomics; for positions dz/df_axis = sum_c (+-1) prod_{other
 //       axes} w table[c] (time carries no gradient), times (res - 1), then the
-//       Jacobian of Eq. 7, added to the position gradient with float atomics.
+//       Jacobian of Eq. 7: each level's share is stored (one 16-byte store per
+//       Gaussian and level, in list order) and pos_reduce_kernel adds the
+//       levels in a fixed order to the position gradient (no atomics).
 //       On levels of at most kAggMaxRes vertices per axis, where the block's
 //       Gaussians share corners, each block first adds its contributions per
 //       table entry in an LDS hash table (open addressing, LDS atomics) and
@@ -526,7 +528,8 @@ template <bool POS, bool AGG>
 __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const float* pos, int stride,
                                                       const uint32_t* list, const uint32_t* count, int nchunk,
                                                       int level0, HashLevels h, const uint32_t* tables,
-                                                      const float2* gz, int64_t zstride, float* gtab, float* gpos) {
+                                                      const float2* gz, int64_t zstride, float* gtab,
+                                                      float4* gpos_part) {
 #pragma clang fp contract(fast)
     __shared__ uint32_t s_key[AGG ? kAggSlots : 1];
     __shared__ float s_v0[AGG ? kAggSlots : 1], s_v1[AGG ? kAggSlots : 1];
@@ -583,7 +586,10 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
         const float wxy = wx * wy;
         const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
         // no gradient at this level: nothing to add, no position term (uniform over the four lanes)
-        if (g.x == 0.0f && g.y == 0.0f) continue;
+        if (g.x == 0.0f && g.y == 0.0f) {
+            if (POS && s == 0) gpos_part[(size_t)level * zstride + k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            continue;
+        }
         float dx = 0.0f, dy = 0.0f, dz = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -638,10 +644,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
                     out[1] = 0.25f * (gn * gx[1] + gp_n * m1 * md);
                     out[2] = 0.25f * (gn * gx[2] + gp_n * m2 * md);
                 }
-                float* dst = gpos + i * 3;
-                atomicAdd(dst + 0, out[0]);
-                atomicAdd(dst + 1, out[1]);
-                atomicAdd(dst + 2, out[2]);
+                // this level's share, summed over the levels by pos_reduce_kernel
+                gpos_part[(size_t)level * zstride + k] = make_float4(out[0], out[1], out[2], 0.0f);
             }
         }
     }
@@ -654,6 +658,26 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
                 atomicAdd(gt + 2 * (size_t)idx + 1, s_v1[k]);
             }
         }
+    }
+}
+
+// Position gradient of the active Gaussians: the levels' shares added in level
+// order (deterministic) to what the position gradient already holds.
+__global__ void __launch_bounds__(256) pos_reduce_kernel(const uint32_t* list, const uint32_t* count, int L,
+                                                         const float4* part, int64_t zstride, float* gpos) {
+    const int64_t n = *count;
+    for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < n; k += (int64_t)gridDim.x * 256) {
+        float sx = 0.0f, sy = 0.0f, sz = 0.0f;
+        for (int l = 0; l < L; ++l) {
+            const float4 p = part[(size_t)l * zstride + k];
+            sx += p.x;
+            sy += p.y;
+            sz += p.z;
+        }
+        float* dst = gpos + (size_t)list[k] * 3;
+        dst[0] += sx;
+        dst[1] += sy;
+        dst[2] += sz;
     }
 }
 
@@ -814,6 +838,8 @@ SortScratch sort_scratch(void* base) {
 
 }  // namespace
 
+size_t decode_bwd_pos_bytes(int L) { return (size_t)L * kBwdChunk * sizeof(float4); }
+
 size_t decode_bwd_sort_bytes() {
     return 2 * align256(kBwdChunk * sizeof(uint64_t)) + align256(radix_sort_counts_bytes(radix_sort_blocks(kBwdChunk))) +
            align256(4 * 1024) + 256;
@@ -890,11 +916,13 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
                 IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<P, G>),
                           dim3((unsigned)(levels * nc)), dim3(256), 0,
                           s, xt, pos, a.stride, list, count, nc, level0, a.h, (const uint32_t*)a.tables, gz,
-                          chunk, b.g_tables, gpos);
+                          chunk, b.g_tables, b.pos_partial);
         };
         if (b.g_pos) {
             scatter(std::true_type{}, std::true_type{}, 0, nagg);
             scatter(std::true_type{}, std::false_type{}, nagg, a.h.L - nagg);
+            IA_LAUNCH("pos_reduce_kernel", pos_reduce_kernel, dim3(blocks_for(n, 256, 4096)), dim3(256), 0, s, list,
+                      count, a.h.L, (const float4*)b.pos_partial, chunk, gpos);
         } else {
             scatter(std::false_type{}, std::true_type{}, 0, nagg);
             scatter(std::false_type{}, std::false_type{}, nagg, a.h.L - nagg);

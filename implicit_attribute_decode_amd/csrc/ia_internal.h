@@ -125,9 +125,11 @@ struct DecodeBwdArgs {
     float* g_b[3];            // [64], [64], [11] out
     float* partial;           // kDecodeBwdPartialFloats
     void* sort;               // decode_bwd_sort_bytes(): the spatial ordering of the active list
+    float4* pos_partial;      // decode_bwd_pos_bytes(L), when g_pos is set: per level position shares
 };
 
 size_t decode_bwd_sort_bytes();
+size_t decode_bwd_pos_bytes(int L);
 hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s);
 
 struct HexArgs {

@@ -213,8 +213,11 @@ typedef struct {
  *   grad_means: device [N,3] or NULL; added into grad_pos (e.g. the render's
  *              position gradient, the positions being the means).
  *   grad_pos:  device [N,3] out, grad_means + dL/dposition through Eq. 7 and
- *              the corner weights of Eq. 9 (time carries none); NULL skips
- *              the position gradient.
+ *              the corner weights of Eq. 9 (time carries none), the levels'
+ *              shares added in a fixed order (the same on every run); NULL
+ *              skips the position gradient.  The first call with grad_pos
+ *              allocates L x 2^21 x 16 bytes of handle scratch (512 MiB at
+ *              L = 16) for those shares.
  *   grads:     all outputs overwritten: table gradient (scatter-add of
  *              w_c dL/dz over the 16 corners of each level, float atomics,
  *              so the last bits vary from run to run), weight and bias
