@@ -239,3 +239,19 @@ def test_decode_backward_zero_points_and_errors():
     with pytest.raises(ia.IAError) as e:
         T.backward(torch.zeros((4, 3), device="cuda"), {k: torch.zeros((4, 4), device="cuda") for k in UP}, 0.5)
     assert e.value.status == ia.IA_ERR_UNSUPPORTED
+
+
+def test_decode_backward_weight_bias_and_position_gradients_are_deterministic():
+    """Weights, biases and positions are summed in fixed orders: repeated
+    calls agree bit for bit (the table gradient uses float atomics)."""
+    dec = S.single_decoder()
+    rng = np.random.default_rng(66)
+    n = 300_000  # more than one block per level and several LDS-combining blocks
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    D = Decoder(dec)
+    a = _gpu_backward(D, pos, up)
+    b = _gpu_backward(D, pos, up)
+    assert torch.equal(a["pos"], b["pos"])
+    for k in range(len(a["weights"])):
+        assert torch.equal(a["weights"][k], b["weights"][k]) and torch.equal(a["biases"][k], b["biases"][k])
