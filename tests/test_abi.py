@@ -139,3 +139,36 @@ def test_render_binning_mode_is_validated():
             ia.ia_render_set_binning(bad)
     for ok in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS, ia.BINNING_AUTO):
         ia.ia_render_set_binning(ok)
+
+
+def test_training_entry_points_validate_before_any_gpu_work():
+    """Loss, optimiser and densify argument errors return before anything is
+    enqueued (fake aligned addresses: nothing is dereferenced)."""
+    L = ia.load()
+    p = C.c_void_p(1 << 20)
+    # image loss: workspace size, lambda outside [0, 1], too small a workspace, too many frames
+    n = ia.ia_image_loss_workspace_size(2, 1080, 1920)
+    assert n >= 3 * 2 * 3 * 1080 * 1920 * 4
+    with pytest.raises(ia.IAError):
+        ia.ia_image_loss_workspace_size(0, 10, 10)
+    assert L.ia_image_loss(p, p, 1, 8, 8, C.c_float(1.5), p, 1 << 30, p, p, None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_image_loss(p, p, 1, 8, 8, C.c_float(0.2), p, 16, p, p, None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
+    assert L.ia_image_loss(p, p, 30000, 8, 8, C.c_float(0.2), p, 1 << 40, p, p, None) == ia.IA_ERR_INVALID_ARG
+    # Adam: step 0, beta1 = 1, negative lr; strided with stride < dim
+    f = C.c_float
+    assert L.ia_adam_step(p, p, p, p, 10, f(1e-3), f(0.9), f(0.999), f(1e-15), 0, None, None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_adam_step(p, p, p, p, 10, f(1e-3), f(1.0), f(0.999), f(1e-15), 1, None, None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_adam_step(p, p, p, p, 10, f(-1.0), f(0.9), f(0.999), f(1e-15), 1, None, None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_adam_step_strided(p, 3, 4, p, p, p, 10, f(1e-3), f(0.9), f(0.999), f(1e-15), 1,
+                                  None) == ia.IA_ERR_INVALID_ARG
+    # densify: workspace size, capacity below 2 N, negative threshold, null params
+    assert ia.ia_densify_workspace_size(8_000_000) >= 8 * (8_000_000 // 4096)
+    prm = ia.DensifyParams(1e-4, 0.05, 0.005)
+    args = [p] * 9
+    assert L.ia_densify(*args, 100, C.byref(prm), p, p, p, 150, p, p, 1 << 20, None) == ia.IA_ERR_INVALID_ARG
+    bad = ia.DensifyParams(-1.0, 0.05, 0.005)
+    assert L.ia_densify(*args, 100, C.byref(bad), p, p, p, 200, p, p, 1 << 20, None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_densify(*args, 100, None, p, p, p, 200, p, p, 1 << 20, None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_densify(*args, 100, C.byref(prm), p, p, p, 200, p, p, 0, None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
+    # accumulate: negative N
+    assert L.ia_densify_accumulate(p, -1, p, p, None) == ia.IA_ERR_INVALID_ARG
