@@ -5,8 +5,10 @@
  * The operations follow two pages:
  *   [SPIN] "Implicit 4D Gaussian Splatting for Fast Motion with Large
  *          Inter-Frame Displacements" (SPIN-4DGS): §3.1 Eq. 1-4 (Gaussians,
- *          covariance, EWA projection, alpha compositing), §3.3 Eq. 7-11
- *          (normalisation, 4D hash encoder, multibranch decoder, activations).
+ *          covariance, EWA projection, alpha compositing), §3.2 Eq. 6
+ *          (refinement of the positions), §3.3 Eq. 7-12 (normalisation, 4D
+ *          hash encoder, multibranch decoder, activations, training loss),
+ *          §4 implementation details (Adam, per-group rates).
  *   [HEX]  "4D Gaussian Splatting详解：动态场景实时渲染的范式突破":
  *          §3.1 (HexPlane six-plane encoder), §3.2 (deformation MLP), §6.1
  *          (opacity is not deformed).
@@ -22,7 +24,8 @@
  *     errors are detected before anything is enqueued; the message is
  *     available from ia_last_error() on the calling thread.  No C++
  *     exception crosses this boundary.
- *   - Handles are immutable after their set_params call.  HexPlane deform
+ *   - Handles change only through their set_params call and, for decoders,
+ *     ia_decoder_update_params (stream-ordered).  HexPlane deform
  *     calls on different streams may overlap.  An fp16 decoder handle owns a
  *     feature scratch buffer ((8 L + 16) x 2^22 bytes) and a side stream, so decode calls on one
  *     such handle must be stream-ordered (use one handle per concurrent
