@@ -508,7 +508,10 @@ __device__ __forceinline__ void agg_add(uint32_t* key, float* v0, float* v1, uin
                                         float* gt) {
     uint32_t slot = (idx * 2654435761u) >> (32 - kAggBits);
     for (int p = 0; p < kAggProbes; ++p) {
-        const uint32_t old = atomicCAS(&key[slot], kAggEmpty, idx);
+        // a set key never changes: a plain read settles most probes, the
+        // compare-and-swap only claims an empty slot
+        uint32_t old = key[slot];
+        if (old == kAggEmpty) old = atomicCAS(&key[slot], kAggEmpty, idx);
         if (old == kAggEmpty || old == idx) {
             atomicAdd(&v0[slot], a);
             atomicAdd(&v1[slot], b);
