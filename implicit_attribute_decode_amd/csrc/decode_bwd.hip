@@ -495,14 +495,15 @@ __global__ void __launch_bounds__(256) mlp_bwd_reduce_kernel(const float* partia
 // Per-block combining of table-gradient contributions (see the file header):
 // kAggSlots entries of LDS, at most kAggProbes linear probes, then a direct
 // global atomic.
-constexpr int kAggBits = 12;
+constexpr int kAggBits = 11;
 constexpr int kAggSlots = 1 << kAggBits;
 constexpr int kAggProbes = 8;
 constexpr uint32_t kAggEmpty = 0xffffffffu;  // table indices are < 2^24
 constexpr int kAggMaxRes = 640;
-// rounds of 64 Gaussians per combining block (768 Gaussians share one LDS table;
-// 256, 384, 512 measured slower)
-constexpr int kAggRounds = 12;
+// rounds of 64 Gaussians per combining block: 384 Gaussians share one
+// 2048-slot LDS table (24 KiB, six blocks per CU); 768 Gaussians on 4096
+// slots, 512 or 768 on 2048, and 192 on 1024 measured slower
+constexpr int kAggRounds = 6;
 
 __device__ __forceinline__ void agg_add(uint32_t* key, float* v0, float* v1, uint32_t idx, float a, float b,
                                         float* gt) {
