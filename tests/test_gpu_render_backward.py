@@ -256,3 +256,26 @@ def test_backward_rejects_missing_sh_buffer():
         ia.ia_render_backward(G, np.array([0, 10]), [cam], ws, 256, torch.ones_like(res["image"]), res["T_final"],
                               res["n_contrib"], GG)
     assert e.value.status == ia.IA_ERR_INVALID_ARG
+
+
+def test_backward_sh_with_an_empty_frame():
+    """A frame without Gaussians between two with: zero rows stay consistent."""
+    rng = np.random.default_rng(51)
+    n = 400
+    g = S.render_attributes(rng, S.shell_points(rng, n, 1.0), 0.01, 0.05)
+    attrs, sh = _sh_attrs(rng, g, 0.05)
+    fo = np.array([0, n // 2, n // 2, n])
+    cams = [S.ring_camera(k, W=96, H=64, fx=90.0, fy=90.0) for k in (0, 3, 6)]
+    R = Renderer()
+    res = R.render(attrs, fo, cams, 1 << 18, aux=True)
+    gimg = _normal_grad(52)(res["image"])
+    grads = R.backward(attrs, fo, cams, 1 << 18, res, gimg)
+    torch.cuda.synchronize()
+    col = O.sh_colors(cams, fo, g.means, sh)
+    ref = O.render_grad(cams, fo, g.means.astype(np.float64), g.scales.astype(np.float64),
+                        g.quats.astype(np.float64), g.opacity.astype(np.float64), col, host(gimg).astype(np.float64))
+    gsh, gdir = O.sh_colors_grad(cams, fo, g.means, sh, ref["colors"])
+    keep = ~ref["flags"]
+    a = host(grads["sh"]).astype(np.float64).reshape(n, 48)[keep]
+    b = gsh.reshape(n, 48)[keep]
+    assert np.all(np.abs(a - b) <= 2e-4 * np.abs(b) + 2e-5 * np.abs(b).max())

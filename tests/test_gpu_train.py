@@ -262,3 +262,31 @@ def test_image_loss_full_hd_frame():
     assert abs(g_loss[1] - o["l1"]) <= 1e-12 * o["l1"]
     assert abs(g_loss[2] - o["ssim"]) <= 2e-6
     assert err <= 2e-5 * np.abs(o["grad"]).max()
+
+
+def test_image_loss_lambda_one_is_pure_dssim():
+    rng = np.random.default_rng(41)
+    x = rng.uniform(0, 1, (2, 3, 70, 300)).astype(np.float32)  # two strips wide, ragged
+    y = np.clip(x + rng.normal(0, 0.15, x.shape), 0, 1).astype(np.float32)
+    g_loss, g_grad = _loss(x, y, lam=1.0)
+    o = T.image_loss(x, y, lam=1.0)
+    assert abs(g_loss[0] - (1.0 - o["ssim"])) <= 2e-6
+    assert np.abs(g_grad - o["grad"]).max() <= 2e-5 * np.abs(o["grad"]).max()
+
+
+def test_adam_empty_and_late_steps():
+    """n = 0 is a no-op; at step 10000 the bias corrections are ~1."""
+    e = torch.empty(0, device="cuda")
+    ia.ia_adam_step(e, e, e, e, 1e-3, 0.9, 0.999, 1e-15, 1)
+    rng = np.random.default_rng(42)
+    n = 5000
+    p = rng.normal(0, 1, n).astype(np.float32)
+    m = rng.normal(0, 1e-3, n).astype(np.float32)
+    v = rng.uniform(1e-8, 1e-6, n).astype(np.float32)
+    g = rng.normal(0, 1e-3, n).astype(np.float32)
+    P, M, V = cuda(p), cuda(m), cuda(v)
+    ia.ia_adam_step(P, cuda(g), M, V, 1e-3, 0.9, 0.999, 1e-15, 10_000)
+    torch.cuda.synchronize()
+    op, om, ov = T.adam_step(p, g, m, v, f32(1e-3), B1, B2, EPS, 10_000)
+    assert np.all(np.abs(host(P) - op) <= 1e-5 * 1e-3 + _ulps(op, 1))
+    assert np.allclose(host(M), om, rtol=1e-5, atol=1e-6 * np.abs(om).max())
