@@ -3,7 +3,6 @@
 // HIP call of an entry point, so invalid arguments never enqueue work.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdint>
 #include <cmath>
 #include <cstdio>
@@ -12,11 +11,6 @@
 #include <string>
 
 #include "ia_internal.h"
-
-namespace {
-// Binning of ia_render: 0 automatic, 1 tile sort, 2 regions (process-wide).
-std::atomic<int> g_binning{0};
-}  // namespace
 
 namespace {
 
@@ -68,16 +62,6 @@ struct ia_decoder {
     float* b[ia::kMaxDecoderMats] = {};
     void* Wt = nullptr;         // per-attribute fp16 decoder: weights in MFMA A-tile order
     float* bpack = nullptr;     // per-attribute fp16 decoder: biases packed per branch
-    uint32_t* zbuf = nullptr;  // fp16 path feature scratch, [2][L][chunk] + [2][chunk] float4
-    float* bwd_partial = nullptr;  // fp16 path: per-wave weight-gradient partials of the backward
-    void* bwd_sort = nullptr;      // fp16 path: the backward's spatial ordering of its active list
-    // per-level position-gradient shares of a backward chunk; allocated by the
-    // first backward that asks for position gradients
-    mutable float4* bwd_pos = nullptr;
-    hipStream_t side = nullptr;  // fp16 path: MLP stream overlapping the next chunk's gather
-    hipEvent_t ev_gather[2] = {nullptr, nullptr};
-    hipEvent_t ev_mlp[2] = {nullptr, nullptr};
-    hipEvent_t ev_norm[2] = {nullptr, nullptr};
     bool ready = false;
 };
 
@@ -96,22 +80,6 @@ void free_decoder_params(ia_decoder* d) {
     d->Wt = nullptr;
     d->bpack = nullptr;
     d->tables = nullptr;
-    if (d->zbuf) (void)hipFree(d->zbuf);
-    d->zbuf = nullptr;
-    if (d->bwd_partial) (void)hipFree(d->bwd_partial);
-    d->bwd_partial = nullptr;
-    if (d->bwd_sort) (void)hipFree(d->bwd_sort);
-    d->bwd_sort = nullptr;
-    if (d->bwd_pos) (void)hipFree(d->bwd_pos);
-    d->bwd_pos = nullptr;
-    for (int k = 0; k < 2; ++k) {
-        if (d->ev_gather[k]) (void)hipEventDestroy(d->ev_gather[k]);
-        if (d->ev_mlp[k]) (void)hipEventDestroy(d->ev_mlp[k]);
-        if (d->ev_norm[k]) (void)hipEventDestroy(d->ev_norm[k]);
-        d->ev_gather[k] = d->ev_mlp[k] = d->ev_norm[k] = nullptr;
-    }
-    if (d->side) (void)hipStreamDestroy(d->side);
-    d->side = nullptr;
     d->ready = false;
 }
 
@@ -206,14 +174,6 @@ ia::DecodeArgs decode_args(const ia_decoder* dec, const float* pos, int stride, 
     a.stride = stride;
     a.t_scalar = t;
     a.N = N;
-    a.zbuf = dec->zbuf;
-    a.zcap = ia::kDecodeChunk;
-    a.side = dec->side;
-    for (int k = 0; k < 2; ++k) {
-        a.ev_gather[k] = dec->ev_gather[k];
-        a.ev_mlp[k] = dec->ev_mlp[k];
-        a.ev_norm[k] = dec->ev_norm[k];
-    }
     return a;
 }
 
@@ -231,8 +191,31 @@ ia_status check_features(const ia_decoder* dec, int64_t N, const void* features,
     return IA_OK;
 }
 
+size_t decode_ws_bytes(const ia_decoder* dec, int64_t N) {
+    if (dec->mlp.dtype != IA_DTYPE_F16 || N <= 0) return 0;
+    return ia::decode_layout(dec->lv, N).total;
+}
+
+// Points the decode's scratch slots into a workspace laid out by decode_layout.
+void set_scratch(ia::DecodeArgs& a, unsigned char* ws, const ia::DecodeLayout& lay) {
+    for (int k = 0; k < 2; ++k) {
+        a.zslot[k] = reinterpret_cast<uint32_t*>(ws + lay.z[k]);
+        a.xt[k] = reinterpret_cast<float4*>(ws + lay.xt[k]);
+    }
+    a.zcap = lay.zcap;
+}
+
+ia_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return IA_OK;
+    if (!ws || !aligned(ws, 256)) return fail(IA_ERR_INVALID_ARG, "workspace must be non-null and 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(IA_ERR_WORKSPACE_TOO_SMALL, "workspace too small: need " + std::to_string(need) + " bytes");
+    return IA_OK;
+}
+
 ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, float t, int64_t N,
-                        const ia_gaussians* out, void* stream, void* features = nullptr, size_t features_bytes = 0) {
+                        const ia_gaussians* out, void* features, size_t features_bytes, void* ws, size_t ws_bytes,
+                        void* side_stream, void* stream) {
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
     if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
@@ -243,7 +226,11 @@ ia_status decode_common(const ia_decoder* dec, const float* pos, int stride, flo
     if (N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N too large");
     ia_status fs = check_features(dec, N, features, features_bytes);
     if (fs != IA_OK) return fs;
+    fs = check_ws(ws, ws_bytes, decode_ws_bytes(dec, N));
+    if (fs != IA_OK) return fs;
     ia::DecodeArgs a = decode_args(dec, pos, stride, t, N);
+    if (dec->mlp.dtype == IA_DTYPE_F16) set_scratch(a, static_cast<unsigned char*>(ws), ia::decode_layout(dec->lv, N));
+    a.side = (hipStream_t)side_stream;
     a.features = static_cast<uint32_t*>(features);
     a.scales = out->scales;
     a.quats = out->quats;
@@ -330,24 +317,6 @@ ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void*
             if (e != hipSuccess) st = hip_fail(e, "decoder weight tiling");
         }
     }
-    if (st == IA_OK && dec->mlp.dtype == IA_DTYPE_F16) {
-        // [2][L][chunk] packed fp16 features (F per entry), then [chunk] normalised positions (float4)
-        hipError_t e = hipMalloc(&dec->zbuf, ((size_t)dec->hash.L * 4 * dec->hash.F + 32) * ia::kDecodeChunk);
-        if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
-        if (st == IA_OK) {
-            e = hipMalloc(&dec->bwd_partial, sizeof(float) * (size_t)ia::kDecodeBwdPartialFloats);
-            if (e == hipSuccess) e = hipMalloc(&dec->bwd_sort, ia::decode_bwd_sort_bytes());
-            if (e != hipSuccess) st = fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(e));
-        }
-        // a side stream (default priority) and events for the MLP / gather overlap
-        if (st == IA_OK) e = hipStreamCreateWithFlags(&dec->side, hipStreamNonBlocking);
-        for (int k = 0; st == IA_OK && e == hipSuccess && k < 2; ++k) {
-            e = hipEventCreateWithFlags(&dec->ev_gather[k], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&dec->ev_mlp[k], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&dec->ev_norm[k], hipEventDisableTiming);
-        }
-        if (st == IA_OK && e != hipSuccess) st = hip_fail(e, "stream/event creation");
-    }
     if (st != IA_OK) {
         free_decoder_params(dec);
         return st;
@@ -380,15 +349,22 @@ ia_status ia_decoder_update_params(ia_decoder* dec, const void* tables, const vo
     return IA_OK;
 }
 
-ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t, const ia_gaussians* out,
-                    void* stream) {
-    if (!std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
-    return decode_common(dec, xyz, 3, t, N, out, stream);
+ia_status ia_decode_workspace_size(const ia_decoder* dec, int64_t N, size_t* bytes) {
+    if (!dec || !bytes) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    *bytes = decode_ws_bytes(dec, N);
+    return IA_OK;
 }
 
-ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
-                         void* stream) {
-    return decode_common(dec, xyzt, 4, 0.0f, N, out, stream);
+ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t, const ia_gaussians* out, void* ws,
+                    size_t ws_bytes, void* side_stream, void* stream) {
+    if (!std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
+    return decode_common(dec, xyz, 3, t, N, out, nullptr, 0, ws, ws_bytes, side_stream, stream);
+}
+
+ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out, void* ws,
+                         size_t ws_bytes, void* side_stream, void* stream) {
+    return decode_common(dec, xyzt, 4, 0.0f, N, out, nullptr, 0, ws, ws_bytes, side_stream, stream);
 }
 
 ia_status ia_decode_feature_bytes(const ia_decoder* dec, int64_t N, size_t* bytes) {
@@ -399,20 +375,36 @@ ia_status ia_decode_feature_bytes(const ia_decoder* dec, int64_t N, size_t* byte
 }
 
 ia_status ia_decode_keep(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
-                         const ia_gaussians* out, void* features, size_t features_bytes, void* stream) {
+                         const ia_gaussians* out, void* features, size_t features_bytes, void* ws, size_t ws_bytes,
+                         void* side_stream, void* stream) {
     if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
     if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
     if (!features && N > 0) return fail(IA_ERR_INVALID_ARG, "features is null");
-    return decode_common(dec, pos, pos_stride, t, N, out, stream, features, features_bytes);
+    return decode_common(dec, pos, pos_stride, t, N, out, features, features_bytes, ws, ws_bytes, side_stream, stream);
+}
+
+namespace {
+bool backward_supported(const ia_decoder* dec) {
+    return dec->mlp.dtype == IA_DTYPE_F16 && dec->mlp.color == IA_COLOR_RGB && dec->mlp.branches == IA_BRANCHES_SHARED;
+}
+}  // namespace
+
+ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_t N, size_t* bytes) {
+    if (!dec || !bytes) return fail(IA_ERR_INVALID_ARG, "null argument");
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    if (!backward_supported(dec))
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoder with the RGB head");
+    *bytes = ia::decode_bwd_layout(dec->lv, N).total;
+    return IA_OK;
 }
 
 ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
                              const ia_gaussians* grad_attr, const float* grad_means, float* grad_pos,
-                             const ia_decoder_grads* grads, const void* features, size_t features_bytes,
-                             void* stream) {
+                             const ia_decoder_grads* grads, const void* features, size_t features_bytes, void* ws,
+                             size_t ws_bytes, void* stream) {
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
-    if (dec->mlp.dtype != IA_DTYPE_F16 || dec->mlp.color != IA_COLOR_RGB || dec->mlp.branches != IA_BRANCHES_SHARED)
+    if (!backward_supported(dec))
         return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoder with the RGB head");
     if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
     if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
@@ -426,6 +418,8 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
             return fail(IA_ERR_INVALID_ARG, "grad_attr scales/quats/colors/opacity must be non-null");
     }
     ia_status fs = check_features(dec, N, features, features_bytes);
+    if (fs != IA_OK) return fs;
+    fs = check_ws(ws, ws_bytes, ia::decode_bwd_layout(dec->lv, N).total);
     if (fs != IA_OK) return fs;
     ia::DecodeBwdArgs b{};
     b.fwd = decode_args(dec, pos, pos_stride, t, N);
@@ -443,16 +437,7 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
         b.g_W[k] = grads->weights[k];
         b.g_b[k] = grads->biases[k];
     }
-    b.partial = dec->bwd_partial;
-    b.sort = dec->bwd_sort;
-    if (grad_pos && N > 0 && !dec->bwd_pos) {
-        hipError_t ea = hipMalloc(reinterpret_cast<void**>(&dec->bwd_pos), ia::decode_bwd_pos_bytes(dec->hash.L));
-        if (ea != hipSuccess) {
-            dec->bwd_pos = nullptr;
-            return fail(IA_ERR_OUT_OF_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(ea));
-        }
-    }
-    b.pos_partial = dec->bwd_pos;
+    b.ws = static_cast<unsigned char*>(ws);
     hipError_t e = ia::launch_decode_backward(b, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode backward launch");
     return IA_OK;
@@ -607,12 +592,6 @@ void ia_hexplane_destroy(ia_hexplane* hp) {
 
 // ============================================================== render
 
-ia_status ia_render_set_binning(int32_t mode) {
-    if (mode < 0 || mode > 2) return fail(IA_ERR_INVALID_ARG, "binning mode must be 0, 1 or 2");
-    g_binning.store(mode, std::memory_order_relaxed);
-    return IA_OK;
-}
-
 ia_status ia_render_workspace_size(int64_t N_total, int32_t frames, int32_t W, int32_t H, int64_t max_entries,
                                    size_t* bytes) {
     if (!bytes) return fail(IA_ERR_INVALID_ARG, "bytes is null");
@@ -686,6 +665,9 @@ ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t
     int W = 0, H = 0;
     ia_status st = check_render_args(g, frame_offsets, frames, cams, ws, ws_bytes, max_entries, &N, &W, &H);
     if (st != IA_OK) return st;
+    const int binning = aux ? aux->binning : IA_BINNING_AUTO;
+    if (binning != IA_BINNING_AUTO && binning != IA_BINNING_TILE_SORT && binning != IA_BINNING_REGIONS)
+        return fail(IA_ERR_INVALID_ARG, "aux->binning must be IA_BINNING_AUTO, _TILE_SORT or _REGIONS");
 
     // camera table (centre = -R^T t, for SH view directions)
     std::string err;
@@ -732,7 +714,7 @@ ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t
     a.n_entries_out = aux ? aux->n_entries : nullptr;
     a.overflow_out = aux ? aux->overflow : nullptr;
     a.unpack = aux != nullptr && aux->want_keys != 0;
-    a.binning = g_binning.load(std::memory_order_relaxed);
+    a.binning = binning;
     const uint64_t* keys = nullptr;
     const uint32_t* vals = nullptr;
     hipError_t e = ia::launch_render(a, (hipStream_t)stream, &keys, &vals);
@@ -835,6 +817,25 @@ ia_status ia_adam_step(float* param, const float* grad, float* m, float* v, int6
     hipError_t e =
         ia::launch_adam(param, grad, m, v, n, 1, 1, lr, beta1, beta2, eps, step, param_f16, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "adam launch");
+    return IA_OK;
+}
+
+ia_status ia_lr_at(float base_lr, int32_t step, int32_t warmup, int32_t total, float final_lr, float* lr) {
+    if (!lr) return fail(IA_ERR_INVALID_ARG, "lr is null");
+    if (step < 0 || warmup < 0 || total < warmup)
+        return fail(IA_ERR_INVALID_ARG, "need step >= 0, warmup >= 0 and total >= warmup");
+    if (!(std::isfinite(base_lr) && base_lr >= 0.0f && std::isfinite(final_lr) && final_lr >= 0.0f))
+        return fail(IA_ERR_INVALID_ARG, "rates must be finite and >= 0");
+    const double base = base_lr, fin = final_lr;
+    if (warmup > 0 && step < warmup) {
+        *lr = (float)(base * (double)(step + 1) / (double)warmup);
+        return IA_OK;
+    }
+    const int64_t span = total - warmup > 1 ? (int64_t)total - warmup : 1;
+    int64_t k = (int64_t)step - warmup;
+    if (k > span) k = span;
+    const double frac = (double)k / (double)span;
+    *lr = (float)(fin + 0.5 * (base - fin) * (1.0 + std::cos(M_PI * frac)));
     return IA_OK;
 }
 

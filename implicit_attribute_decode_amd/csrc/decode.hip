@@ -588,25 +588,90 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
     return hipGetLastError();
 }
 
+namespace {
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Events of the side-stream overlap, one set per host thread and device.
+// A stream wait takes the event's latest record at the time the wait is
+// enqueued, so reusing a set across the calls of one thread is safe, and
+// threads never share one.  Created on a thread's first overlapped decode on
+// a device (no device memory) and kept until the process ends.
+struct OverlapEvents {
+    hipEvent_t gather[2], mlp[2], norm[2];
+};
+
+hipError_t overlap_events(OverlapEvents** out) {
+    constexpr int kMaxDevices = 64;
+    thread_local OverlapEvents* per_device[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (!per_device[dev]) {
+        OverlapEvents ev{};
+        hipEvent_t* all[6] = {&ev.gather[0], &ev.gather[1], &ev.mlp[0], &ev.mlp[1], &ev.norm[0], &ev.norm[1]};
+        for (int k = 0; k < 6; ++k) {
+            e = hipEventCreateWithFlags(all[k], hipEventDisableTiming);
+            if (e != hipSuccess) {
+                for (int j = 0; j < k; ++j) (void)hipEventDestroy(*all[j]);
+                return e;
+            }
+        }
+        per_device[dev] = new OverlapEvents(ev);
+    }
+    *out = per_device[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+DecodeLayout decode_layout(const HashLevels& h, int64_t N, int64_t max_chunk) {
+    DecodeLayout L{};
+    const int64_t n = N > 0 ? N : 1;
+    int64_t zcap = (n + 255) / 256 * 256;
+    if (zcap > max_chunk) zcap = max_chunk;
+    L.zcap = zcap;
+    L.slots = n > zcap ? 2 : 1;
+    size_t off = 0;
+    for (int k = 0; k < L.slots; ++k) {
+        L.z[k] = off;
+        off = align256(off + (size_t)h.L * (size_t)zcap * (size_t)(h.F / 2) * 4);
+    }
+    for (int k = 0; k < L.slots; ++k) {
+        L.xt[k] = off;
+        off = align256(off + (size_t)zcap * sizeof(float4));
+    }
+    if (L.slots == 1) {
+        L.z[1] = L.z[0];
+        L.xt[1] = L.xt[0];
+    }
+    L.total = off;
+    return L;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
     if (a.N <= 0) return hipSuccess;
     if (dtype == IA_DTYPE_F16) {
-        if (!a.zbuf || a.zcap <= 0) return hipErrorInvalidValue;
+        if (!a.zslot[0] || !a.xt[0] || a.zcap <= 0) return hipErrorInvalidValue;
         // Chunks of at most zcap Gaussians.  With a side stream, the MLP of
         // chunk k and the normalisation of chunk k + 1 run there while chunk
         // k is gathered on s, so s gathers back to back:
         //   s:    N0 G0 | G1 | G2 ...         (G k+1 waits for N k+1)
         //   side:    N1 | M0 N2 | M1 N3 ...   (M k waits for G k)
-        // The feature scratch and the normalised positions are
-        // double-buffered; N k+2 follows M k on the side stream, which
-        // follows G k, the last reader of position slot k & 1.
-        const size_t zslot = (size_t)a.h.L * a.zcap * (a.h.F / 2);  // 32-bit words per scratch slot
-        float4* xtb[2] = {reinterpret_cast<float4*>(a.zbuf + 2 * zslot),
-                          reinterpret_cast<float4*>(a.zbuf + 2 * zslot) + a.zcap};
+        // The feature scratch and the normalised positions alternate between
+        // two slots; N k+2 follows M k on the side stream, which follows G k,
+        // the last reader of position slot k & 1.
         // features go to the caller's buffer ([L][N], kept for a backward) or to the
-        // double-buffered scratch ([L][zcap] per slot)
+        // scratch slots ([L][zcap] each)
         const int64_t zstride = a.features ? a.N : a.zcap;
-        const bool overlap = a.side != nullptr && a.N > a.zcap;
+        const bool overlap = a.side != nullptr && a.side != s && a.N > a.zcap && a.zslot[1] != a.zslot[0] &&
+                             a.xt[1] != a.xt[0];
+        OverlapEvents* ev = nullptr;
+        if (overlap) {
+            hipError_t e = overlap_events(&ev);
+            if (e != hipSuccess) return e;
+        }
         auto mlp = [&](hipStream_t st, const uint32_t* zb, int64_t n, int64_t off, bool beside) -> hipError_t {
             if (a.branches) return launch_mlp_branch(a, zb, zstride, n, off, st);
             // 256 threads = 4 waves x 64 Gaussians.  Beside a gather, one block
@@ -644,22 +709,23 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
                       xt);
             return hipGetLastError();
         };
-        hipError_t e = normalize(s, 0, xtb[0]);
+        hipError_t e = normalize(s, 0, a.xt[0]);
         if (e != hipSuccess) return e;
         if (overlap) {
             // the side stream starts after everything already queued on s
             // (the caller's writes of the positions, earlier readers of the scratch)
-            if ((e = hipEventRecord(a.ev_norm[0], s)) != hipSuccess) return e;
-            if ((e = hipStreamWaitEvent(a.side, a.ev_norm[0], 0)) != hipSuccess) return e;
+            if ((e = hipEventRecord(ev->norm[0], s)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(a.side, ev->norm[0], 0)) != hipSuccess) return e;
         }
         int k = 0;
         for (int64_t off = 0, n = 0; off < a.N; off += n, ++k) {
             n = chunk_len(off);
             const int nchunk = (int)((n + kGatherPerBlock - 1) / kGatherPerBlock);
-            uint32_t* zb = a.features ? a.features + (size_t)off * (a.h.F / 2) : a.zbuf + (size_t)(k & 1) * zslot;
-            float4* xt = xtb[overlap ? (k & 1) : 0];
-            if (overlap && k >= 1 && (e = hipStreamWaitEvent(s, a.ev_norm[k & 1], 0)) != hipSuccess) return e;
-            if (overlap && k >= 2 && (e = hipStreamWaitEvent(s, a.ev_mlp[k & 1], 0)) != hipSuccess) return e;
+            const int slot = overlap ? (k & 1) : 0;
+            uint32_t* zb = a.features ? a.features + (size_t)off * (a.h.F / 2) : a.zslot[slot];
+            float4* xt = a.xt[slot];
+            if (overlap && k >= 1 && (e = hipStreamWaitEvent(s, ev->norm[k & 1], 0)) != hipSuccess) return e;
+            if (overlap && k >= 2 && (e = hipStreamWaitEvent(s, ev->mlp[k & 1], 0)) != hipSuccess) return e;
             if (!overlap && k >= 1 && (e = normalize(s, off, xt)) != hipSuccess) return e;
             if (a.h.F == 4) {
                 if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, zstride, s)) != hipSuccess) return e;
@@ -674,15 +740,15 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
                               dim3(256), 0, s, xt, n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
             }
             if (overlap) {
-                if ((e = hipEventRecord(a.ev_gather[k & 1], s)) != hipSuccess) return e;
+                if ((e = hipEventRecord(ev->gather[k & 1], s)) != hipSuccess) return e;
                 const int64_t noff = off + n;
                 if (noff < a.N) {
-                    if ((e = normalize(a.side, noff, xtb[(k + 1) & 1])) != hipSuccess) return e;
-                    if ((e = hipEventRecord(a.ev_norm[(k + 1) & 1], a.side)) != hipSuccess) return e;
+                    if ((e = normalize(a.side, noff, a.xt[(k + 1) & 1])) != hipSuccess) return e;
+                    if ((e = hipEventRecord(ev->norm[(k + 1) & 1], a.side)) != hipSuccess) return e;
                 }
-                if ((e = hipStreamWaitEvent(a.side, a.ev_gather[k & 1], 0)) != hipSuccess) return e;
+                if ((e = hipStreamWaitEvent(a.side, ev->gather[k & 1], 0)) != hipSuccess) return e;
                 if ((e = mlp(a.side, zb, n, off, noff < a.N)) != hipSuccess) return e;
-                if ((e = hipEventRecord(a.ev_mlp[k & 1], a.side)) != hipSuccess) return e;
+                if ((e = hipEventRecord(ev->mlp[k & 1], a.side)) != hipSuccess) return e;
             } else {
                 if ((e = mlp(s, zb, n, off, false)) != hipSuccess) return e;
             }
@@ -690,7 +756,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         if (overlap) {
             // the caller's stream resumes after the last MLPs (the side stream
             // is in order, so the last event covers every earlier chunk)
-            e = hipStreamWaitEvent(s, a.ev_mlp[(k - 1) & 1], 0);
+            e = hipStreamWaitEvent(s, ev->mlp[(k - 1) & 1], 0);
             if (e != hipSuccess) return e;
         }
         return hipGetLastError();

@@ -812,7 +812,7 @@ int blocks_for(int64_t n, int per, int cap) {
 
 constexpr int64_t kBwdChunk = kDecodeChunk / 2;
 
-// the sort scratch: two buffers of kBwdChunk words, the radix counts, the
+// the sort scratch: two buffers of `chunk` words, the radix counts, the
 // digit totals and the item count
 struct SortScratch {
     uint64_t* items[2];
@@ -824,14 +824,19 @@ struct SortScratch {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-SortScratch sort_scratch(void* base) {
+size_t sort_scratch_bytes(int64_t chunk) {
+    return 2 * align256(chunk * sizeof(uint64_t)) + align256(radix_sort_counts_bytes(radix_sort_blocks(chunk))) +
+           align256(4 * 1024) + 256;
+}
+
+SortScratch sort_scratch(void* base, int64_t chunk) {
     SortScratch t{};
     char* p = static_cast<char*>(base);
-    t.max_blocks = radix_sort_blocks(kBwdChunk);
+    t.max_blocks = radix_sort_blocks(chunk);
     t.items[0] = reinterpret_cast<uint64_t*>(p);
-    p += align256(kBwdChunk * sizeof(uint64_t));
+    p += align256(chunk * sizeof(uint64_t));
     t.items[1] = reinterpret_cast<uint64_t*>(p);
-    p += align256(kBwdChunk * sizeof(uint64_t));
+    p += align256(chunk * sizeof(uint64_t));
     t.counts = reinterpret_cast<uint32_t*>(p);
     p += align256(radix_sort_counts_bytes(t.max_blocks));
     t.digit_tot = reinterpret_cast<uint32_t*>(p);
@@ -842,11 +847,30 @@ SortScratch sort_scratch(void* base) {
 
 }  // namespace
 
-size_t decode_bwd_pos_bytes(int L) { return (size_t)L * kBwdChunk * sizeof(float4); }
-
-size_t decode_bwd_sort_bytes() {
-    return 2 * align256(kBwdChunk * sizeof(uint64_t)) + align256(radix_sort_counts_bytes(radix_sort_blocks(kBwdChunk))) +
-           align256(4 * 1024) + 256;
+DecodeBwdLayout decode_bwd_layout(const HashLevels& h, int64_t N) {
+    DecodeBwdLayout L{};
+    const int64_t n = N > 0 ? N : 1;
+    // a multiple of the compaction's block size, at most kBwdChunk
+    int64_t chunk = (n + kCompactItems - 1) / kCompactItems * kCompactItems;
+    if (chunk > kBwdChunk) chunk = kBwdChunk;
+    L.chunk = chunk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    L.z = take((size_t)h.L * chunk * 4);
+    L.gz = take((size_t)h.L * chunk * sizeof(float2));
+    L.list = take((size_t)chunk * 4);
+    L.boff = take((size_t)(chunk / kCompactItems) * 4);
+    L.count = take(16);
+    L.xt = take((size_t)chunk * sizeof(float4));
+    L.partial = take((size_t)kDecodeBwdPartialFloats * sizeof(float));
+    L.sort = take(sort_scratch_bytes(chunk));
+    L.pos = take((size_t)h.L * chunk * sizeof(float4));
+    L.total = off;
+    return L;
 }
 
 hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
@@ -857,17 +881,18 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     if (b.g_pos && a.N > 0)
         IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(a.N * 3, 256, 8192)), dim3(256), 0, s,
                   b.g_pos, a.N * 3, b.g_means);
-    const int64_t chunk = kBwdChunk;
-    const SortScratch srt = sort_scratch(b.sort);
-    const size_t zslot = (size_t)a.h.L * a.zcap;
-    float4* xt = reinterpret_cast<float4*>(a.zbuf + 2 * zslot);
-    uint32_t* z = a.zbuf;
-    float2* gz = reinterpret_cast<float2*>(a.zbuf + (size_t)a.h.L * chunk);
-    // after z and dz: the compacted list of a chunk, per-block offsets and the count
-    uint32_t* list = a.zbuf + (size_t)3 * a.h.L * chunk;
-    uint32_t* boff = list + chunk;
-    const int nbc = (int)(chunk / kCompactItems);
-    uint32_t* count = boff + nbc;
+    const DecodeBwdLayout lay = decode_bwd_layout(a.h, a.N);
+    const int64_t chunk = lay.chunk;
+    const SortScratch srt = sort_scratch(b.ws + lay.sort, chunk);
+    float4* xt = reinterpret_cast<float4*>(b.ws + lay.xt);
+    uint32_t* z = reinterpret_cast<uint32_t*>(b.ws + lay.z);
+    float2* gz = reinterpret_cast<float2*>(b.ws + lay.gz);
+    // the compacted list of a chunk, per-block offsets and the count
+    uint32_t* list = reinterpret_cast<uint32_t*>(b.ws + lay.list);
+    uint32_t* boff = reinterpret_cast<uint32_t*>(b.ws + lay.boff);
+    uint32_t* count = reinterpret_cast<uint32_t*>(b.ws + lay.count);
+    float* partial = reinterpret_cast<float*>(b.ws + lay.partial);
+    float4* pos_partial = reinterpret_cast<float4*>(b.ws + lay.pos);
     MlpBwdArgs m{};
     for (int k = 0; k < 3; ++k) {
         m.W[k] = (const _Float16*)a.W[k];
@@ -880,7 +905,7 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     m.gc = b.g_colors;
     m.go = b.g_opacity;
     m.gz = gz;
-    m.partial = b.partial;
+    m.partial = partial;
     int first = 1;
     for (int64_t off = 0; off < a.N; off += chunk) {
         const int64_t n = a.N - off < chunk ? a.N - off : chunk;
@@ -920,13 +945,13 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
                 IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<P, G>),
                           dim3((unsigned)(levels * nc)), dim3(256), 0,
                           s, xt, pos, a.stride, list, count, nc, level0, a.h, (const uint32_t*)a.tables, gz,
-                          chunk, b.g_tables, b.pos_partial);
+                          chunk, b.g_tables, pos_partial);
         };
         if (b.g_pos) {
             scatter(std::true_type{}, std::true_type{}, 0, nagg);
             scatter(std::true_type{}, std::false_type{}, nagg, a.h.L - nagg);
             IA_LAUNCH("pos_reduce_kernel", pos_reduce_kernel, dim3(blocks_for(n, 256, 4096)), dim3(256), 0, s, list,
-                      count, a.h.L, (const float4*)b.pos_partial, chunk, gpos);
+                      count, a.h.L, (const float4*)pos_partial, chunk, gpos);
         } else {
             scatter(std::false_type{}, std::true_type{}, 0, nagg);
             scatter(std::false_type{}, std::false_type{}, nagg, a.h.L - nagg);
@@ -934,14 +959,14 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     }
     if (first) {  // N = 0: the weight and bias gradients are zero
         const int64_t nf = (int64_t)kDecodeBwdBlocks * kBwdWaves * (kTileSlots + kBiasSlots) * 64;
-        IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(nf, 256, 8192)), dim3(256), 0, s, b.partial,
+        IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(nf, 256, 8192)), dim3(256), 0, s, partial,
                   nf, (const float*)nullptr);
     }
     // fixed-order two-stage sum of the per-wave partials (deterministic)
     const int nwaves = kDecodeBwdBlocks * kBwdWaves;
-    float* groups = b.partial + (size_t)nwaves * (kTileSlots + kBiasSlots) * 64;
+    float* groups = partial + (size_t)nwaves * (kTileSlots + kBiasSlots) * 64;
     IA_LAUNCH("mlp_bwd_group_kernel", mlp_bwd_group_kernel, dim3(kTileSlots + kBiasSlots, kDecodeBwdGroups), dim3(64),
-              0, s, b.partial, nwaves / kDecodeBwdGroups, groups);
+              0, s, partial, nwaves / kDecodeBwdGroups, groups);
     const int nred = kTileSlots * 64 + kBiasSlots * 4;
     IA_LAUNCH("mlp_bwd_reduce_kernel", mlp_bwd_reduce_kernel, dim3((nred + 255) / 256), dim3(256), 0, s, groups,
               kDecodeBwdGroups, b.g_W[0], b.g_W[1], b.g_W[2], b.g_b[0], b.g_b[1], b.g_b[2]);

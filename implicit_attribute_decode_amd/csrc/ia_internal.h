@@ -70,17 +70,27 @@ struct DecodeArgs {
     float* colors;
     float* sh;  // [N][48] for the SH head
     float* opacity;
-    uint32_t* zbuf;  // fp16 path: feature scratch [2][L][zcap] (packed fp16 pairs), then [zcap] float4
     uint32_t* features;  // fp16 path, or null: caller buffer [L][N] of packed fp16 features (F / 2 words each)
-    int64_t zcap;    // Gaussians per chunk the scratch holds
-    hipStream_t side;         // fp16 path: stream the MLP of one chunk overlaps the next gather on (or null)
-    hipEvent_t ev_gather[2];  // per scratch slot: gather done
-    hipEvent_t ev_mlp[2];     // per scratch slot: MLP done
-    hipEvent_t ev_norm[2];    // per position slot: normalisation (side stream) done
+    // fp16 path scratch, carved from the caller's workspace (decode_layout)
+    uint32_t* zslot[2];  // per slot: [L][zcap] packed fp16 features (F / 2 words each)
+    float4* xt[2];       // per slot: [zcap] normalised positions
+    int64_t zcap;        // Gaussians per chunk a slot holds
+    hipStream_t side;    // caller's second stream for the MLP beside the next gather, or null
 };
 
-// Gaussians per fp16-decode chunk; the handle owns L * kDecodeChunk * 4 bytes.
+// Gaussians per fp16-decode chunk (one normalise / gather / MLP triple).
 constexpr int64_t kDecodeChunk = int64_t(1) << 22;
+
+// Byte offsets of the fp16 decode's scratch inside a workspace: chunks of
+// zcap Gaussians (N rounded up to a multiple of 256, at most max_chunk), one
+// slot, or two when N needs more than one chunk (consecutive chunks
+// alternate, so the MLP of one can run beside the gather of the next).
+struct DecodeLayout {
+    size_t z[2], xt[2], total;
+    int64_t zcap;
+    int slots;
+};
+DecodeLayout decode_layout(const HashLevels& h, int64_t N, int64_t max_chunk = kDecodeChunk);
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 
@@ -106,14 +116,25 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
                                   int64_t zstride, hipStream_t s);
 
 // Backward of the fp16 decode: one persistent grid of kDecodeBwdBlocks blocks
-// of four waves; each wave owns a slot of 148 x 64 floats in `partial`,
-// followed by kDecodeBwdGroups slots of group sums.
+// of four waves; each wave owns a slot of 148 x 64 floats in the workspace's
+// partials, followed by kDecodeBwdGroups slots of group sums.
 constexpr int kDecodeBwdBlocks = 256;
 constexpr int kDecodeBwdGroups = 16;
 constexpr int64_t kDecodeBwdPartialFloats = ((int64_t)kDecodeBwdBlocks * 4 + kDecodeBwdGroups) * 148 * 64;
 
+// Byte offsets of the backward's scratch inside a workspace (chunks of at
+// most 2^21 Gaussians): recomputed features z [L][chunk], their gradient
+// [L][chunk] float2, the chunk's active list, block offsets and count,
+// normalised positions, the weight-gradient partials, the spatial sort's
+// buffers and the per-level position shares [L][chunk] float4.
+struct DecodeBwdLayout {
+    size_t z, gz, list, boff, count, xt, partial, sort, pos, total;
+    int64_t chunk;
+};
+DecodeBwdLayout decode_bwd_layout(const HashLevels& h, int64_t N);
+
 struct DecodeBwdArgs {
-    DecodeArgs fwd;           // the decode being differentiated (parameters, positions, scratch)
+    DecodeArgs fwd;           // the decode being differentiated (parameters, positions)
     const float* g_scales;    // [N,3] upstream dL/dscales
     const float* g_quats;     // [N,4]
     const float* g_colors;    // [N,3]
@@ -123,13 +144,9 @@ struct DecodeBwdArgs {
     float* g_tables;          // [L][T][2] out
     float* g_W[3];            // [64][32], [64][64], [11][64] out
     float* g_b[3];            // [64], [64], [11] out
-    float* partial;           // kDecodeBwdPartialFloats
-    void* sort;               // decode_bwd_sort_bytes(): the spatial ordering of the active list
-    float4* pos_partial;      // decode_bwd_pos_bytes(L), when g_pos is set: per level position shares
+    unsigned char* ws;        // caller's workspace, decode_bwd_layout(h, N).total bytes
 };
 
-size_t decode_bwd_sort_bytes();
-size_t decode_bwd_pos_bytes(int L);
 hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s);
 
 struct HexArgs {

@@ -366,7 +366,7 @@ __global__ void __launch_bounds__(kBlock) compact_kernel(const uint32_t* tiles, 
 //
 // Two ways to turn the depth-ordered Gaussians into per-tile lists, chosen on
 // the device from the mean number of tiles a visible Gaussian touches (or
-// forced through ia_render_set_binning):
+// forced per call through ia_render_aux.binning):
 //
 // Tile sort (small footprints): one entry (frame*tiles + tile) << 32 | index
 // per (Gaussian, tile), emitted in depth order, then a stable radix sort on

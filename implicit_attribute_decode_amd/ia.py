@@ -25,12 +25,15 @@ IA_DTYPE_F32, IA_DTYPE_F16 = 0, 1
 IA_ACT_RELU, IA_ACT_GELU = 0, 1
 IA_COLOR_RGB, IA_COLOR_SH3 = 0, 1
 IA_BRANCHES_SHARED, IA_BRANCHES_PER_ATTRIBUTE = 0, 1
+# ia_render_aux.binning
+BINNING_AUTO, BINNING_TILE_SORT, BINNING_REGIONS = 0, 1, 2
 
 # Every entry point include/ia.h declares.
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decoder_update_params", "ia_decode",
            "ia_decode_xyzt", "ia_decoder_destroy", "ia_decode_backward", "ia_decode_feature_bytes", "ia_decode_keep",
+           "ia_decode_workspace_size", "ia_decode_backward_workspace_size", "ia_lr_at",
            "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform", "ia_hexplane_destroy",
-           "ia_render_workspace_size", "ia_render", "ia_render_set_binning", "ia_render_backward", "ia_l1_loss",
+           "ia_render_workspace_size", "ia_render", "ia_render_backward", "ia_l1_loss",
            "ia_image_loss_workspace_size", "ia_image_loss", "ia_adam_step", "ia_adam_step_strided",
            "ia_densify_accumulate", "ia_densify_workspace_size", "ia_densify",
            "ia_profile_enable", "ia_profile_report", "ia_profile_reset")
@@ -74,7 +77,7 @@ class RenderAux(C.Structure):
                 ("overflow", C.c_void_p), ("sorted_keys", C.c_void_p), ("sorted_vals", C.c_void_p),
                 ("tile_ranges", C.c_void_p), ("proj_a", C.c_void_p), ("proj_b", C.c_void_p),
                 ("proj_c", C.c_void_p), ("depth", C.c_void_p), ("tiles_touched", C.c_void_p),
-                ("tile_rect", C.c_void_p), ("want_keys", C.c_int32)]
+                ("tile_rect", C.c_void_p), ("want_keys", C.c_int32), ("binning", C.c_int32)]
 
 
 class DecoderGrads(C.Structure):
@@ -102,12 +105,16 @@ def load(path: str = LIB_PATH):
         L.ia_last_error.argtypes = []
         L.ia_decoder_create.argtypes = [P, P, P]
         L.ia_decoder_set_params.argtypes = [P, P, P, P, C.c_int32, P]
-        L.ia_decode.argtypes = [P, P, C.c_int64, C.c_float, P, P]
-        L.ia_decode_xyzt.argtypes = [P, P, C.c_int64, P, P]
+        L.ia_decode_workspace_size.argtypes = [P, C.c_int64, P]
+        L.ia_decode_backward_workspace_size.argtypes = [P, C.c_int64, P]
+        L.ia_decode.argtypes = [P, P, C.c_int64, C.c_float, P, P, C.c_size_t, P, P]
+        L.ia_decode_xyzt.argtypes = [P, P, C.c_int64, P, P, C.c_size_t, P, P]
         L.ia_decoder_destroy.argtypes = [P]
-        L.ia_decode_backward.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, P, C.c_size_t, P]
+        L.ia_decode_backward.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, P, C.c_size_t, P,
+                                         C.c_size_t, P]
         L.ia_decode_feature_bytes.argtypes = [P, C.c_int64, P]
-        L.ia_decode_keep.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, C.c_size_t, P]
+        L.ia_decode_keep.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, C.c_size_t, P, C.c_size_t, P, P]
+        L.ia_lr_at.argtypes = [C.c_float, C.c_int32, C.c_int32, C.c_int32, C.c_float, P]
         L.ia_decoder_destroy.restype = None
         L.ia_hexplane_create.argtypes = [P, P]
         L.ia_hexplane_set_params.argtypes = [P, P, P, P, C.c_int32, P]
@@ -116,7 +123,6 @@ def load(path: str = LIB_PATH):
         L.ia_hexplane_destroy.restype = None
         L.ia_render_workspace_size.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int64, P]
         L.ia_render.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P]
-        L.ia_render_set_binning.argtypes = [C.c_int32]
         L.ia_render_backward.argtypes = [P, P, C.c_int32, P, P, C.c_size_t, C.c_int64, P, P, P, P, P]
         L.ia_l1_loss.argtypes = [P, P, C.c_int64, P, P, P]
         L.ia_image_loss_workspace_size.argtypes = [C.c_int32, C.c_int32, C.c_int32, P]
@@ -190,20 +196,43 @@ def gaussians(means=None, scales=None, quats=None, colors=None, sh=None, opacity
                      sh_degree)
 
 
-def ia_decode(dec, xyz, N: int, t: float, out: Gaussians, stream=None):
-    _check(load().ia_decode(dec, _ptr(xyz), int(N), float(t), C.byref(out), _stream(stream)))
+def _nbytes(t) -> int:
+    return 0 if t is None else int(t.numel() * t.element_size())
 
 
-def ia_decode_xyzt(dec, xyzt, N: int, out: Gaussians, stream=None):
-    _check(load().ia_decode_xyzt(dec, _ptr(xyzt), int(N), C.byref(out), _stream(stream)))
+def _side(side) -> int | None:
+    return None if side is None else int(side.cuda_stream)
+
+
+def ia_decode_workspace_size(dec, N: int) -> int:
+    b = C.c_size_t()
+    _check(load().ia_decode_workspace_size(dec, int(N), C.byref(b)))
+    return int(b.value)
+
+
+def ia_decode_backward_workspace_size(dec, N: int) -> int:
+    b = C.c_size_t()
+    _check(load().ia_decode_backward_workspace_size(dec, int(N), C.byref(b)))
+    return int(b.value)
+
+
+def ia_decode(dec, xyz, N: int, t: float, out: Gaussians, ws=None, side=None, stream=None):
+    """ws: device uint8 tensor (256-byte aligned) of ia_decode_workspace_size
+    bytes or more; side: an optional second torch stream."""
+    _check(load().ia_decode(dec, _ptr(xyz), int(N), float(t), C.byref(out), _ptr(ws), _nbytes(ws), _side(side),
+                            _stream(stream)))
+
+
+def ia_decode_xyzt(dec, xyzt, N: int, out: Gaussians, ws=None, side=None, stream=None):
+    _check(load().ia_decode_xyzt(dec, _ptr(xyzt), int(N), C.byref(out), _ptr(ws), _nbytes(ws), _side(side),
+                                 _stream(stream)))
 
 
 def ia_decode_backward(dec, pos, pos_stride: int, N: int, t: float, grad_attr: Gaussians, grad_means, grad_pos,
-                       grads: DecoderGrads, features=None, stream=None):
-    fb = 0 if features is None else int(features.numel() * features.element_size())
+                       grads: DecoderGrads, features=None, ws=None, stream=None):
     _check(load().ia_decode_backward(dec, _ptr(pos), int(pos_stride), int(N), float(t), C.byref(grad_attr),
-                                     _ptr(grad_means), _ptr(grad_pos), C.byref(grads), _ptr(features), fb,
-                                     _stream(stream)))
+                                     _ptr(grad_means), _ptr(grad_pos), C.byref(grads), _ptr(features),
+                                     _nbytes(features), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def ia_decode_feature_bytes(dec, N: int) -> int:
@@ -212,9 +241,17 @@ def ia_decode_feature_bytes(dec, N: int) -> int:
     return int(b.value)
 
 
-def ia_decode_keep(dec, pos, pos_stride: int, N: int, t: float, out: Gaussians, features, stream=None):
+def ia_decode_keep(dec, pos, pos_stride: int, N: int, t: float, out: Gaussians, features, ws=None, side=None,
+                   stream=None):
     _check(load().ia_decode_keep(dec, _ptr(pos), int(pos_stride), int(N), float(t), C.byref(out), _ptr(features),
-                                 int(features.numel() * features.element_size()), _stream(stream)))
+                                 _nbytes(features), _ptr(ws), _nbytes(ws), _side(side), _stream(stream)))
+
+
+def ia_lr_at(base_lr: float, step: int, warmup: int, total: int, final_lr: float = 1e-7) -> float:
+    """Learning rate at iteration `step` (0-based) of the warm-up + cosine schedule."""
+    lr = C.c_float()
+    _check(load().ia_lr_at(float(base_lr), int(step), int(warmup), int(total), float(final_lr), C.byref(lr)))
+    return float(lr.value)
 
 
 def ia_decoder_destroy(dec):
@@ -351,14 +388,6 @@ def ia_densify(xyzt, grad_acc, grad_count, scales, quats, opacity, noise, m, v, 
 
 
 # ----------------------------------------------------------------- diagnostics
-
-
-BINNING_AUTO, BINNING_TILE_SORT, BINNING_REGIONS = 0, 1, 2
-
-
-def ia_render_set_binning(mode: int):
-    """0 automatic, 1 tile sort, 2 regions (process-wide)."""
-    _check(load().ia_render_set_binning(int(mode)))
 
 
 def ia_profile_enable(on: bool = True):

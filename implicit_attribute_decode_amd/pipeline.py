@@ -19,6 +19,24 @@ def _dev(a, dtype=None, device="cuda"):
     return t if dtype is None else t.to(dtype)
 
 
+class _Workspace:
+    """A device byte buffer that grows on demand and hands out 256-byte
+    aligned views of the requested size (None for zero bytes)."""
+
+    def __init__(self, device):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes <= 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes + 256:
+            self.buf = None
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.buf.data_ptr()) % 256
+        return self.buf[off:off + nbytes]
+
+
 class Decoder:
     """Hash encoder + decoder MLP handle (SPIN-4DGS §3.3)."""
 
@@ -43,6 +61,15 @@ class Decoder:
         self._b = [_dev(b, torch.float32, device=device) for b in params.biases]
         ia.ia_decoder_set_params(self.handle, self._tables, self._W, self._b)
         torch.cuda.current_stream().synchronize()
+        # this object's scratch (the handle holds only parameters) and a second
+        # stream (default priority) for the MLP of one chunk beside the next gather
+        self._ws = _Workspace(device)
+        self._bwd_ws = _Workspace(device)
+        self.side = torch.cuda.Stream(device=device)
+
+    def workspace(self, N: int):
+        """Aligned scratch view for a decode of N Gaussians (None if none is needed)."""
+        return self._ws.get(ia.ia_decode_workspace_size(self.handle, N))
 
     def _out(self, N, out):
         if out is None:
@@ -63,13 +90,13 @@ class Decoder:
         head) or sh [N,16,3] (SH head)."""
         N = int(xyz.shape[0])
         out = self._out(N, out)
-        ia.ia_decode(self.handle, xyz, N, t, self._gaussians(out))
+        ia.ia_decode(self.handle, xyz, N, t, self._gaussians(out), self.workspace(N), self.side)
         return out
 
     def decode_xyzt(self, xyzt: torch.Tensor, out: dict | None = None) -> dict:
         N = int(xyzt.shape[0])
         out = self._out(N, out)
-        ia.ia_decode_xyzt(self.handle, xyzt, N, self._gaussians(out))
+        ia.ia_decode_xyzt(self.handle, xyzt, N, self._gaussians(out), self.workspace(N), self.side)
         return out
 
     def decode_keep(self, pos: torch.Tensor, t: float | None = None, out: dict | None = None,
@@ -81,7 +108,8 @@ class Decoder:
         nbytes = ia.ia_decode_feature_bytes(self.handle, N)
         if features is None or features.numel() * features.element_size() < nbytes:
             features = torch.empty(max(nbytes, 8) // 8, dtype=torch.int64, device=self.device)
-        ia.ia_decode_keep(self.handle, pos, stride, N, float(t or 0.0), self._gaussians(out), features)
+        ia.ia_decode_keep(self.handle, pos, stride, N, float(t or 0.0), self._gaussians(out), features,
+                          self.workspace(N), self.side)
         return out, features
 
     def backward(self, pos: torch.Tensor, grad_attr: dict, t: float | None = None, grad_means=None,
@@ -100,7 +128,9 @@ class Decoder:
                             (ia.C.c_void_p * 4)(*[ia._ptr(b) for b in out["biases"]]))
         up = ia.gaussians(scales=grad_attr["scales"], quats=grad_attr["quats"], colors=grad_attr["colors"],
                           opacity=grad_attr["opacity"])
-        ia.ia_decode_backward(self.handle, pos, stride, N, float(t or 0.0), up, grad_means, out["pos"], G, features)
+        ws = self._bwd_ws.get(ia.ia_decode_backward_workspace_size(self.handle, N))
+        ia.ia_decode_backward(self.handle, pos, stride, N, float(t or 0.0), up, grad_means, out["pos"], G, features,
+                              ws)
         return out
 
     def update_params(self):
@@ -209,23 +239,20 @@ class Renderer:
 
     def __init__(self, device="cuda"):
         self.device = device
-        self.ws = None
-        self._loss_ws = None
+        self._ws = _Workspace(device)
+        self._loss_ws = _Workspace(device)
 
     def workspace(self, N, frames, W, H, max_entries):
-        need = ia.ia_render_workspace_size(N, frames, W, H, max_entries)
-        if self.ws is None or self.ws.numel() < need:
-            self.ws = None
-            self.ws = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
-        off = (-self.ws.data_ptr()) % 256
-        return self.ws[off:off + need]
+        """Aligned view of this object's render workspace for these sizes."""
+        return self._ws.get(ia.ia_render_workspace_size(N, frames, W, H, max_entries))
 
     def render(self, g: dict, frame_offsets, cams, max_entries: int, aux: bool = False, out: dict | None = None,
-               keys: bool = True):
+               keys: bool = True, binning: int = ia.BINNING_AUTO):
         """g: means [N,k>=3], scales, quats, colors | sh, opacity (cuda tensors).
         Returns image [F,3,H,W] and, with aux, T_final, n_contrib, n_entries,
         overflow and workspace views (ranges, projections and, with keys, the
-        sorted keys / values)."""
+        sorted keys / values).  binning: ia.BINNING_AUTO, _TILE_SORT or
+        _REGIONS (the same lists either way)."""
         fo = np.asarray(frame_offsets, np.int64)
         F, W, H = len(cams), int(cams[0].W), int(cams[0].H)
         N = int(fo[-1])
@@ -241,6 +268,9 @@ class Renderer:
                          opacity=g["opacity"], means_stride=stride, sh_degree=3 if sh is not None else -1)
         res = {"image": image}
         A = None
+        if not aux and binning != ia.BINNING_AUTO:
+            A = ia.RenderAux()
+            A.binning = int(binning)
         if aux:
             res["T_final"] = torch.empty((F, H, W), device=self.device)
             res["n_contrib"] = torch.empty((F, H, W), dtype=torch.int32, device=self.device)
@@ -249,6 +279,7 @@ class Renderer:
             A = ia.RenderAux(ia._ptr(res["T_final"]), ia._ptr(res["n_contrib"]), ia._ptr(res["n_entries"]),
                              ia._ptr(res["overflow"]))
             A.want_keys = 1 if keys else 0
+            A.binning = int(binning)
         ia.ia_render(G, fo, cams, ws, max_entries, image, A)
         if aux:
             base = ws.data_ptr()
@@ -295,12 +326,10 @@ class Renderer:
         """Eq. 12 loss of image against target ([F, 3, H, W] device float):
         (loss [3] float64 on the device = {L, L1, SSIM}, dL/dimage)."""
         F, _, H, W = (int(d) for d in image.shape)
-        nbytes = ia.ia_image_loss_workspace_size(F, H, W)
-        if self._loss_ws is None or self._loss_ws.numel() < nbytes:
-            self._loss_ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        ws = self._loss_ws.get(ia.ia_image_loss_workspace_size(F, H, W))  # 256-byte aligned
         loss = torch.empty(3, dtype=torch.float64, device=image.device)
         grad = torch.empty_like(image)
-        ia.ia_image_loss(image.contiguous(), target.contiguous(), lam, self._loss_ws, loss, grad)
+        ia.ia_image_loss(image.contiguous(), target.contiguous(), lam, ws, loss, grad)
         return loss, grad
 
     @staticmethod
@@ -321,12 +350,8 @@ class Renderer:
 def lr_at(step: int, base: float, warmup: int, total: int, final: float = 1e-7) -> float:
     """Learning rate at `step` (0-based): linear warm-up over `warmup` steps,
     then cosine decay from base to `final` at `total` ([SPIN] §4
-    implementation details)."""
-    if warmup > 0 and step < warmup:
-        return base * (step + 1) / warmup
-    span = max(total - warmup, 1)
-    frac = min(max(step - warmup, 0), span) / span
-    return final + 0.5 * (base - final) * (1.0 + math.cos(math.pi * frac))
+    implementation details); evaluated by ia_lr_at."""
+    return ia.ia_lr_at(base, step, warmup, total, final)
 
 
 class Adam:

@@ -24,12 +24,15 @@
  *     errors are detected before anything is enqueued; the message is
  *     available from ia_last_error() on the calling thread.  No C++
  *     exception crosses this boundary.
- *   - Handles change only through their set_params call and, for decoders,
- *     ia_decoder_update_params (stream-ordered).  HexPlane deform
- *     calls on different streams may overlap.  An fp16 decoder handle owns a
- *     feature scratch buffer ((8 L + 16) x 2^22 bytes) and a side stream, so decode calls on one
- *     such handle must be stream-ordered (use one handle per concurrent
- *     stream).  Calls that share a render workspace must not overlap.
+ *   - Handles own only their parameters (device memory allocated by
+ *     set_params, freed by destroy) and change only through set_params and,
+ *     for decoders, ia_decoder_update_params (stream-ordered).  Every other
+ *     call reads a handle without modifying it, so calls on one handle from
+ *     several streams or threads may overlap, each with its own workspace.
+ *   - Scratch memory is the caller's: a workspace of the size the matching
+ *     *_workspace_size call reports, 256-byte aligned, contents undefined
+ *     between calls.  Calls that share a workspace must not overlap.  No entry
+ *     point allocates device memory except set_params / create.
  */
 #ifndef IA_H_
 #define IA_H_
@@ -146,12 +149,8 @@ IA_API ia_status ia_decoder_create(const ia_hash_desc* hash, const ia_mlp_desc* 
  *   biases : fp32 [out], one per weight matrix
  * params_on_device: 1 if all the above are device pointers, 0 if host.
  * The copies are enqueued on `stream`; host sources may be freed on return
- * (host copies are synchronous).  For the fp16 decoder this call also
- * allocates the handle's feature scratch ((4 L F + 16) x 2^22 bytes; decode
- * processes at most 2^22 Gaussians per gather/MLP kernel pair), 39 MB of
- * backward partials and 34 MiB for the backward's spatial ordering of the
- * Gaussians it differentiates.  May be called again to replace parameters (waits for
- * the device first).
+ * (host copies are synchronous).  May be called again to replace parameters
+ * (waits for the device first).
  * Errors: INVALID_ARG, OUT_OF_MEMORY, DEVICE. */
 IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, const void* const* weights,
                                 const float* const* biases, int32_t params_on_device, void* stream);
@@ -160,9 +159,17 @@ IA_API ia_status ia_decoder_set_params(ia_decoder* dec, const void* tables, cons
  * device memory in the layouts of ia_decoder_set_params, with copies enqueued
  * on `stream` (no allocation, no synchronisation): an optimiser's update
  * between training steps.  Decodes and backwards enqueued later on `stream`
- * see the new values.  Errors: INVALID_ARG (null, parameters not set), DEVICE. */
+ * see the new values; the caller orders other streams after it.
+ * Errors: INVALID_ARG (null, parameters not set), DEVICE. */
 IA_API ia_status ia_decoder_update_params(ia_decoder* dec, const void* tables, const void* const* weights,
                                           const float* const* biases, void* stream);
+
+/* Bytes of workspace a decode of N Gaussians needs (ia_decode,
+ * ia_decode_xyzt, ia_decode_keep): 0 for fp32 decoders; for fp16 decoders
+ * (2 L F + 16) bytes per Gaussian of a chunk of min(N, 2^22) Gaussians
+ * (rounded up to a multiple of 256), twice that when N > 2^22 (consecutive
+ * chunks alternate between two halves).  Errors: INVALID_ARG. */
+IA_API ia_status ia_decode_workspace_size(const ia_decoder* dec, int64_t N, size_t* bytes);
 
 /* Decode N Gaussians at one time t ([SPIN] §3.3 Eq. 7-11):
  *   xyz : device [N,3] positions mu
@@ -171,22 +178,28 @@ IA_API ia_status ia_decoder_update_params(ia_decoder* dec, const void* tables, c
  *         (SH3 head; out->colors is then not used), opacity[N] =
  *         sigmoid(o_hat); out->means is not written (the input positions
  *         are the means).
- * N = 0 is a no-op.  Errors: INVALID_ARG (null, N < 0, params not set).
+ *   ws, ws_bytes: device workspace of ia_decode_workspace_size(dec, N) bytes
+ *         (may be NULL when that is 0), 256-byte aligned.
+ *   side_stream: a second hipStream_t of the caller, or NULL.  When N needs
+ *         more than one chunk, the MLP of each chunk runs on it beside the
+ *         gather of the next; otherwise it is not used.
+ * N = 0 is a no-op.  Errors: INVALID_ARG (null, N < 0, params not set,
+ * misaligned workspace), WORKSPACE_TOO_SMALL.
  * Asynchronous on stream: all of the call's work, including what it runs on
- * an internal second stream, starts after everything already queued on
- * stream, and stream continues only after all of it.  Results are deterministic; with the fp16
- * decoder the rounding of a Gaussian depends on its index modulo 64 (the
- * matrix-core column it occupies), so decoding a slice that starts at a
- * multiple of 64 gives bit for bit the same values as decoding it within a
- * larger array. */
+ * side_stream, starts after everything already queued on stream, and stream
+ * continues only after all of it.  Results are deterministic and do not
+ * depend on side_stream; with the fp16 decoder the rounding of a Gaussian
+ * depends on its index modulo 64 (the matrix-core column it occupies), so
+ * decoding a slice that starts at a multiple of 64 gives bit for bit the same
+ * values as decoding it within a larger array. */
 IA_API ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, float t, const ia_gaussians* out,
-                    void* stream);
+                           void* ws, size_t ws_bytes, void* side_stream, void* stream);
 
 /* As ia_decode with a per-Gaussian time: xyzt is device [N,4] (x, y, z, t).
  * One launch decodes any mix of frames (spatiotemporal slicing: every frame
  * is its own set of positions, [SPIN] §3.2). */
 IA_API ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
-                         void* stream);
+                                void* ws, size_t ws_bytes, void* side_stream, void* stream);
 
 /* Bytes of the encoding z of N Gaussians (N x L x F fp16) that
  * ia_decode_keep stores and ia_decode_backward can reuse. */
@@ -196,10 +209,11 @@ IA_API ia_status ia_decode_feature_bytes(const ia_decoder* dec, int64_t N, size_
  * keep the hash encoding z of every Gaussian in `features` (device,
  * caller-owned, >= ia_decode_feature_bytes, 8-byte aligned; layout
  * [L][N] x F fp16) for a later ia_decode_backward of the same positions,
- * which then skips recomputing it.  fp16 decoders only.
- * Errors: INVALID_ARG, UNSUPPORTED, DEVICE. */
+ * which then skips recomputing it.  fp16 decoders only; ws, side_stream as
+ * ia_decode.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, DEVICE. */
 IA_API ia_status ia_decode_keep(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
-                                const ia_gaussians* out, void* features, size_t features_bytes, void* stream);
+                                const ia_gaussians* out, void* features, size_t features_bytes, void* ws,
+                                size_t ws_bytes, void* side_stream, void* stream);
 
 /* Gradients of the decoder parameters (device, fp32, overwritten). */
 typedef struct {
@@ -207,6 +221,14 @@ typedef struct {
     float* weights[4]; /* layer k: [out][in] (n_hidden + 1 used)             */
     float* biases[4];  /* layer k: [out]                                     */
 } ia_decoder_grads;
+
+/* Bytes of workspace ia_decode_backward needs for N Gaussians: per chunk of
+ * min(N, 2^21) Gaussians (rounded up to a multiple of 4096) the recomputed
+ * encoding, its gradient, the chunk's active list and spatial sort, the
+ * normalised positions and the per-level position shares (484 bytes per
+ * Gaussian at L = 16), plus 39 MB of weight-gradient partials.
+ * Errors: INVALID_ARG, UNSUPPORTED (decoders without a backward). */
+IA_API ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_t N, size_t* bytes);
 
 /* Backward of ia_decode (pos_stride 3, time t) or ia_decode_xyzt (pos_stride
  * 4) for upstream gradients of the decoded attributes ([SPIN] §3.3 Eq. 7-11
@@ -218,24 +240,25 @@ typedef struct {
  *   grad_pos:  device [N,3] out, grad_means + dL/dposition through Eq. 7 and
  *              the corner weights of Eq. 9 (time carries none), the levels'
  *              shares added in a fixed order (the same on every run); NULL
- *              skips the position gradient.  The first call with grad_pos
- *              allocates L x 2^21 x 16 bytes of handle scratch (512 MiB at
- *              L = 16) for those shares.
+ *              skips the position gradient.
  *   grads:     all outputs overwritten: table gradient (scatter-add of
  *              w_c dL/dz over the 16 corners of each level, float atomics,
  *              so the last bits vary from run to run), weight and bias
  *              gradients (summed in a fixed order: deterministic).
  *   features:  the encoding kept by ia_decode_keep for the same positions, or
  *              NULL (then recomputed).
+ *   ws, ws_bytes: device workspace of ia_decode_backward_workspace_size(dec,
+ *              N) bytes, 256-byte aligned.
  * The forward is recomputed exactly as the decode computes it (fp16 hidden
  * activations); the backward runs in fp32 (v_mfma_f32_16x16x4_f32), treating
- * the fp16 roundings as the identity.  Uses the handle's scratch: calls on
- * one handle must not overlap (same as ia_decode).
- * Errors: INVALID_ARG, UNSUPPORTED (fp32 decoders), DEVICE. */
+ * the fp16 roundings as the identity.  Supported: the shared-trunk fp16
+ * decoder with the RGB head.
+ * Errors: INVALID_ARG, UNSUPPORTED (other decoders), WORKSPACE_TOO_SMALL,
+ * DEVICE. */
 IA_API ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,
                                     const ia_gaussians* grad_attr, const float* grad_means, float* grad_pos,
                                     const ia_decoder_grads* grads, const void* features, size_t features_bytes,
-                                    void* stream);
+                                    void* ws, size_t ws_bytes, void* stream);
 
 IA_API void ia_decoder_destroy(ia_decoder* dec);
 
@@ -311,10 +334,26 @@ typedef struct {
     const float* depth;           /* [N] camera-space z                           */
     const uint32_t* tiles_touched;/* [N] 0 = culled                               */
     const uint16_t* tile_rect;    /* [N][4] tx0, ty0, tx1, ty1 (inclusive)        */
-    /* input */
+    /* inputs */
     int32_t want_keys;  /* nonzero: also fill sorted_keys / sorted_vals (one
                            extra pass over the entries); else both stay NULL */
+    int32_t binning;    /* how depth-ordered Gaussians become per-tile lists;
+                           both methods give the same lists, they differ in
+                           speed (a NULL aux means IA_BINNING_AUTO):
+      IA_BINNING_AUTO       regions when visible Gaussians touch 4 or more
+                            tiles on average, else the tile sort;
+      IA_BINNING_TILE_SORT  one entry per (Gaussian, tile), stable radix sort
+                            on the tile index;
+      IA_BINNING_REGIONS    one entry per (Gaussian, 8x8-tile region), stable
+                            radix sort on the region index, then per region a
+                            count pass and a write pass that place every
+                            (Gaussian, tile) entry at its final position.
+                            Other values: IA_ERR_INVALID_ARG. */
 } ia_render_aux;
+
+#define IA_BINNING_AUTO 0
+#define IA_BINNING_TILE_SORT 1
+#define IA_BINNING_REGIONS 2
 
 /* Bytes of workspace ia_render needs for N_total Gaussians over `frames`
  * frames of W x H with room for max_entries tile entries.
@@ -338,8 +377,8 @@ IA_API ia_status ia_render_workspace_size(int64_t N_total, int32_t frames, int32
  * needed, the surplus is dropped, aux->overflow is set to 1 and
  * aux->n_entries holds the needed count; the image is then incomplete and
  * the caller retries with a larger max_entries.
- * Errors: INVALID_ARG, UNSUPPORTED (sh_degree not -1/3),
- * WORKSPACE_TOO_SMALL, DEVICE. */
+ * Errors: INVALID_ARG (also an unknown aux->binning), UNSUPPORTED (sh_degree
+ * not -1/3), WORKSPACE_TOO_SMALL, DEVICE. */
 IA_API ia_status ia_render(const ia_gaussians* g, const int64_t* frame_offsets, int32_t frames, const ia_camera* cams,
                     void* ws, size_t ws_bytes, int64_t max_entries, float* image, ia_render_aux* aux,
                     void* stream);
@@ -415,10 +454,20 @@ IA_API ia_status ia_image_loss(const float* image, const float* target, int32_t 
  *   param -= lr (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps).
  * param, grad, m, v are device float[n] (m and v zero before the first step);
  * param_f16 (nullable) receives the updated values rounded to fp16 (RNE), e.g.
- * for an fp16 hash table.  Per-group learning rates and their schedule are
- * the caller's (one call per group).  Errors: INVALID_ARG, DEVICE. */
+ * for an fp16 hash table.  Per-group learning rates are the caller's (one
+ * call per group, the rate from ia_lr_at).  Errors: INVALID_ARG, DEVICE. */
 IA_API ia_status ia_adam_step(float* param, const float* grad, float* m, float* v, int64_t n, float lr, float beta1,
                               float beta2, float eps, int32_t step, uint16_t* param_f16, void* stream);
+
+/* The learning-rate schedule of [SPIN] §4 implementation details: at
+ * iteration `step` (0-based), a linear warm-up base (step + 1) / warmup over
+ * the first `warmup` iterations, then a cosine decay from base_lr at
+ * iteration warmup to final_lr at iteration total (and final_lr after it):
+ *   lr = final + (base - final) (1 + cos(pi min(step - warmup, span) / span)) / 2,
+ * span = max(total - warmup, 1), evaluated in double and rounded to float.
+ * Host-only, no device work.  Errors: INVALID_ARG (null lr, step < 0,
+ * warmup < 0, total < warmup, non-finite or negative rates). */
+IA_API ia_status ia_lr_at(float base_lr, int32_t step, int32_t warmup, int32_t total, float final_lr, float* lr);
 
 /* ia_adam_step for a parameter laid out as rows of `dim` values that sit
  * `param_stride` floats apart (dim <= param_stride), e.g. the x, y, z of
@@ -473,18 +522,6 @@ IA_API ia_status ia_densify(const float* xyzt, const float* grad_acc, const int3
                             float* out_m, float* out_v, int64_t out_capacity, int64_t* out_n, void* ws,
                             size_t ws_bytes, void* stream);
 
-/* How ia_render turns depth-ordered Gaussians into per-tile lists.  Both give
- * the same lists; they differ in speed.
- *   0  automatic (default): regions when visible Gaussians touch 4 or more
- *      tiles on average, else the tile sort;
- *   1  tile sort: one entry per (Gaussian, tile), stable radix sort on the
- *      tile index;
- *   2  regions: one entry per (Gaussian, 8x8-tile region), stable radix sort
- *      on the region index, then per region a count pass and a write pass
- *      that place every (Gaussian, tile) entry at its final position.
- * Process-wide; applies to ia_render calls issued after it returns.
- * Errors: INVALID_ARG for other values. */
-IA_API ia_status ia_render_set_binning(int32_t mode);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics: per-kernel timing with HIP events                            */

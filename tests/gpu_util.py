@@ -30,9 +30,9 @@ def rel_ok(a, b, rtol=1e-5, atol=1e-7):
     return np.abs(a - b) <= rtol * np.abs(b) + atol
 
 
-def gpu_render(g: dict, fo, cams, cap: int, renderer: Renderer | None = None):
+def gpu_render(g: dict, fo, cams, cap: int, renderer: Renderer | None = None, binning: int = 0):
     r = renderer or Renderer()
-    res = r.render(g, fo, cams, cap, aux=True)
+    res = r.render(g, fo, cams, cap, aux=True, binning=binning)
     torch.cuda.synchronize()
     E = int(res["n_entries"].item())
     n = min(E, cap)

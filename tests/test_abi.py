@@ -88,10 +88,10 @@ def test_decode_without_params_is_rejected_before_any_gpu_work():
     L = ia.load()
     h = ia.ia_decoder_create(_hash(), _mlp())
     g = ia.Gaussians()
-    assert L.ia_decode(h, None, 10, C.c_float(0.5), C.byref(g), None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_decode(h, None, 10, C.c_float(0.5), C.byref(g), None, 0, None, None) == ia.IA_ERR_INVALID_ARG
     assert "not set" in ia.ia_last_error()
     ia.ia_decoder_destroy(h)
-    assert L.ia_decode(None, None, 10, C.c_float(0.5), C.byref(g), None) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_decode(None, None, 10, C.c_float(0.5), C.byref(g), None, 0, None, None) == ia.IA_ERR_INVALID_ARG
 
 
 def test_workspace_size_validation_and_growth():
@@ -133,12 +133,21 @@ def test_render_argument_errors_are_synchronous():
     assert L.ia_render(C.byref(g2), fo4, 1, C.byref(cam), img, 1 << 30, 10, img, None, None) == ia.IA_ERR_UNSUPPORTED
 
 
-def test_render_binning_mode_is_validated():
+def test_render_binning_mode_is_validated_per_call():
+    """An unknown ia_render_aux.binning is an argument error, returned before
+    anything is enqueued (fake aligned addresses: nothing is dereferenced)."""
+    L = ia.load()
+    cam = ia.Camera()
+    cam.W, cam.H, cam.fx, cam.fy = 64, 64, 60.0, 60.0
+    fo = (C.c_int64 * 2)(0, 0)
+    g = ia.Gaussians()
+    img = C.c_void_p(256)
     for bad in (-1, 3, 100):
-        with pytest.raises(ia.IAError):
-            ia.ia_render_set_binning(bad)
-    for ok in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS, ia.BINNING_AUTO):
-        ia.ia_render_set_binning(ok)
+        aux = ia.RenderAux()
+        aux.binning = bad
+        assert L.ia_render(C.byref(g), fo, 1, C.byref(cam), img, 1 << 30, 10, img, C.byref(aux),
+                           None) == ia.IA_ERR_INVALID_ARG
+        assert "binning" in ia.ia_last_error()
 
 
 def test_training_entry_points_validate_before_any_gpu_work():
@@ -172,3 +181,46 @@ def test_training_entry_points_validate_before_any_gpu_work():
     assert L.ia_densify(*args, 100, C.byref(prm), p, p, p, 200, p, p, 0, None) == ia.IA_ERR_WORKSPACE_TOO_SMALL
     # accumulate: negative N
     assert L.ia_densify_accumulate(p, -1, p, p, None) == ia.IA_ERR_INVALID_ARG
+
+
+def test_lr_schedule_matches_the_oracle_and_validates():
+    """ia_lr_at (host-only) against the oracle's warm-up + cosine schedule
+    ([SPIN] §4 implementation details): equal within one fp32 ulp of the
+    base rate over warm-up, decay and the floor after the last iteration."""
+    from oracle import train as T
+
+    for base, warm, total in ((8e-3, 1000, 40000), (3e-5, 2, 10), (1.6e-4, 0, 100)):
+        for step in sorted({0, 1, max(warm - 1, 0), warm, warm + 1, (warm + total) // 2, total - 1, total,
+                            total + 5}):
+            got = ia.ia_lr_at(base, step, warm, total, 1e-7)
+            want = T.lr_schedule(step, base, warm, total, 1e-7)
+            assert abs(got - want) <= 2.0 ** -23 * base, (base, warm, total, step, got, want)
+    assert ia.ia_lr_at(8e-3, 40000, 1000, 40000, 1e-7) == pytest.approx(1e-7, rel=1e-6)
+    L = ia.load()
+    out = C.c_float()
+    for args in ((1e-3, -1, 0, 10), (1e-3, 0, -1, 10), (1e-3, 0, 20, 10), (float("nan"), 0, 0, 10), (-1.0, 0, 0, 10)):
+        assert L.ia_lr_at(C.c_float(args[0]), args[1], args[2], args[3], C.c_float(1e-7),
+                          C.byref(out)) == ia.IA_ERR_INVALID_ARG
+    assert L.ia_lr_at(C.c_float(1e-3), 0, 0, 10, C.c_float(1e-7), None) == ia.IA_ERR_INVALID_ARG
+
+
+def test_device_memory_is_allocated_only_when_parameters_are_set():
+    """Handles own only their parameters: hipMalloc appears only in the
+    parameter uploads of the set_params calls; every other entry point takes
+    its scratch from a caller workspace."""
+    import glob
+
+    allowed = {"upload_param", "ia_decoder_set_params", "ia_hexplane_set_params"}
+    defn = re.compile(r"^(?!\s)(?!#)(?!//)[\w:<>\*&, ]*?\b(\w+)\s*\(")
+    seen = set()
+    for path in sorted(glob.glob(os.path.join(ROOT, "implicit_attribute_decode_amd", "csrc", "*"))):
+        fn = None
+        for line in open(path).read().splitlines():
+            m = defn.match(line)
+            if m:
+                fn = m.group(1)
+            code = line.split("//")[0]
+            if re.search(r"\bhipMalloc\w*\s*\(", code):
+                assert fn in allowed, (os.path.basename(path), fn, line.strip())
+                seen.add(fn)
+    assert seen == allowed

@@ -214,6 +214,98 @@ def test_chunked_decode_bitwise_equals_slice_decodes():
     say(f"chunked decode of {n} = slice decodes bit for bit")
 
 
+def test_concurrent_decodes_on_one_handle_match_serial():
+    """A decoder handle holds only its parameters (SPIN-4DGS page, §3.3
+    Eq. 10-11: decoding is a function of position and time): two host threads
+    decode different position sets on one handle at the same time, each on
+    its own stream with its own workspace and second stream (both sets span
+    two chunks, so each overlaps its MLPs with its gathers).  Every result
+    equals, bit for bit, a serial decode of the same set on one stream with no
+    second stream."""
+    import threading
+
+    from implicit_attribute_decode_amd import ia
+
+    rng = np.random.default_rng(12)
+    n = (1 << 22) + 300_000
+    D = Decoder(S.single_decoder())
+    xs = [cuda(np.concatenate([rng.normal(0.0, 2.0, (n, 3)), rng.uniform(0.0, 1.0, (n, 1))], 1).astype(np.float32))
+          for _ in range(2)]
+    nbytes = ia.ia_decode_workspace_size(D.handle, n)
+    assert nbytes >= 2 * (1 << 22) * (16 * 2 * 2 + 16)  # two slots of a full chunk
+
+    def aligned(nb):
+        buf = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+        off = (-buf.data_ptr()) % 256
+        return buf[off:off + nb]
+
+    ref = []
+    for x in xs:
+        out = D._out(n, None)
+        ia.ia_decode_xyzt(D.handle, x, n, D._gaussians(out), aligned(nbytes), None)
+        ref.append(out)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    sides = [torch.cuda.Stream() for _ in range(2)]
+    wss = [aligned(nbytes) for _ in range(2)]
+    for rep in range(3):
+        outs = [D._out(n, None) for _ in range(2)]
+        for o in outs:
+            for v in o.values():
+                v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        barrier = threading.Barrier(2)
+        errors = []
+
+        def run(k):
+            try:
+                barrier.wait()
+                ia.ia_decode_xyzt(D.handle, xs[k], n, D._gaussians(outs[k]), wss[k], sides[k], stream=streams[k])
+            except Exception as exc:  # reported on the main thread
+                errors.append(exc)
+
+        th = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+        assert not errors, errors
+        torch.cuda.synchronize()
+        for k in range(2):
+            for key in ref[k]:
+                assert torch.equal(outs[k][key], ref[k][key]), (rep, k, key)
+    say(f"two concurrent decodes of {n} on one handle = serial decodes, bit for bit")
+
+
+def test_decode_workspace_errors():
+    """A missing, misaligned or too small workspace is an argument error,
+    returned before anything is enqueued."""
+    from implicit_attribute_decode_amd import ia
+
+    D = Decoder(S.single_decoder())
+    n = 5000
+    x = cuda(np.zeros((n, 4), np.float32))
+    out = D._out(n, None)
+    need = ia.ia_decode_workspace_size(D.handle, n)
+    assert need == (n + 255) // 256 * 256 * (16 * 2 * 2 + 16)
+    buf = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    off = (-buf.data_ptr()) % 256
+    with pytest.raises(ia.IAError) as e:
+        ia.ia_decode_xyzt(D.handle, x, n, D._gaussians(out), None)
+    assert e.value.status == ia.IA_ERR_INVALID_ARG
+    with pytest.raises(ia.IAError) as e:
+        ia.ia_decode_xyzt(D.handle, x, n, D._gaussians(out), buf[off + 4:off + 4 + need])
+    assert e.value.status == ia.IA_ERR_INVALID_ARG
+    with pytest.raises(ia.IAError) as e:
+        ia.ia_decode_xyzt(D.handle, x, n, D._gaussians(out), buf[off:off + need - 1])
+    assert e.value.status == ia.IA_ERR_WORKSPACE_TOO_SMALL
+    # an fp32 decoder needs none
+    T = Decoder(S.tiny_decoder())
+    assert ia.ia_decode_workspace_size(T.handle, n) == 0
+    ia.ia_decode_xyzt(T.handle, x, n, T._gaussians(T._out(n, None)), None)
+    torch.cuda.synchronize()
+
+
 def test_sequence_full_size_sampled():
     """All 150 x 200k (x,y,z,t) positions in one launch; 24k sampled rows
     (every frame represented) against the oracle."""

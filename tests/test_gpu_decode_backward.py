@@ -255,3 +255,14 @@ def test_decode_backward_weight_bias_and_position_gradients_are_deterministic():
     assert torch.equal(a["pos"], b["pos"])
     for k in range(len(a["weights"])):
         assert torch.equal(a["weights"][k], b["weights"][k]) and torch.equal(a["biases"][k], b["biases"][k])
+    # the table gradient adds each entry's contributions with float atomics in
+    # whatever order the waves arrive: its last bits may vary between runs,
+    # within the rounding of an fp32 sum of that entry's terms
+    ta, tb = a["tables"], b["tables"]
+    diff = (ta - tb).abs()
+    scale = float(ta.abs().max())
+    frac = float((diff > 0).float().mean())
+    say(f"table gradient run-to-run: max |diff| {float(diff.max()):.2e} of max |g| {scale:.2e}, "
+        f"{frac:.2e} of entries differ")
+    assert float(diff.max()) <= 1e-5 * scale
+    assert bool((diff <= 1e-5 * ta.abs() + 1e-7 * scale).all())

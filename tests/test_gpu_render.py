@@ -45,21 +45,17 @@ def _full_check(g: dict, fo, cams, tag, cap=None):
     pre, b, r = _oracle_render(cams, fo, h)
     cap = cap or max(b["E"], 1)
     out = None
-    try:
-        for mode in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS, ia.BINNING_AUTO):
-            ia.ia_render_set_binning(mode)
-            gr = gpu_render(g, fo, cams, cap)
-            say(f"[{tag}] binning {mode}: N={int(fo[-1])} E={gr['E']} frames={len(cams)}")
-            check_preprocess_bitexact(gr, pre)
-            vis = pre["tiles"] > 0
-            np.testing.assert_array_equal(gr["opacity"][vis], h["opacity"][vis])
-            np.testing.assert_array_equal(gr["rgb"][vis], h["colors"][vis])
-            check_bins_bitexact(gr, b)
-            st = check_image(gr, r)
-            say(f"[{tag}] binning {mode}: image {st}")
-            out = gr
-    finally:
-        ia.ia_render_set_binning(ia.BINNING_AUTO)
+    for mode in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS, ia.BINNING_AUTO):
+        gr = gpu_render(g, fo, cams, cap, binning=mode)
+        say(f"[{tag}] binning {mode}: N={int(fo[-1])} E={gr['E']} frames={len(cams)}")
+        check_preprocess_bitexact(gr, pre)
+        vis = pre["tiles"] > 0
+        np.testing.assert_array_equal(gr["opacity"][vis], h["opacity"][vis])
+        np.testing.assert_array_equal(gr["rgb"][vis], h["colors"][vis])
+        check_bins_bitexact(gr, b)
+        st = check_image(gr, r)
+        say(f"[{tag}] binning {mode}: image {st}")
+        out = gr
     return out, pre, b, r
 
 
@@ -208,15 +204,11 @@ def test_overflow_reports_needed_capacity_then_retry_matches():
     g, cam, _ = S.single_render_scene(n_shell=8000, n_clus=500)
     attrs = _attrs_from_gaussians(g)
     fo = np.array([0, g.n])
-    try:
-        for mode in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS):
-            ia.ia_render_set_binning(mode)
-            small = gpu_render(attrs, fo, [cam], 1000)
-            assert small["overflow"] == 1 and small["E"] > 1000
-            full = gpu_render(attrs, fo, [cam], small["E"])
-            assert full["overflow"] == 0 and full["E"] == small["E"]
-    finally:
-        ia.ia_render_set_binning(ia.BINNING_AUTO)
+    for mode in (ia.BINNING_TILE_SORT, ia.BINNING_REGIONS):
+        small = gpu_render(attrs, fo, [cam], 1000, binning=mode)
+        assert small["overflow"] == 1 and small["E"] > 1000
+        full = gpu_render(attrs, fo, [cam], small["E"], binning=mode)
+        assert full["overflow"] == 0 and full["E"] == small["E"]
     _full_check(attrs, fo, [cam], "retry", cap=small["E"])
 
 
