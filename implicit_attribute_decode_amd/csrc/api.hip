@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -441,6 +442,77 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
     hipError_t e = ia::launch_decode_backward(b, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode backward launch");
     return IA_OK;
+}
+
+}  // extern "C"
+
+// ============================================================== decode without allocation
+
+namespace {
+
+// Scratch of ia_decode_xyzt_noalloc: a file-scope device array, so the call
+// allocates nothing.  Every GPU the library runs on holds its own copy until
+// the process ends, and every call on that GPU shares it.
+constexpr size_t kNoAllocScratchBytes = size_t(20) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kNoAllocMaxDevices] = {};
+
+// The device address of the current device's copy of `scratch`, looked up on
+// the first call on that device (with it current) and kept.  In host code the
+// array's name is a host-side stand-in, never a device address: only this
+// pointer reaches the kernels.
+ia_status noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kNoAllocMaxDevices) return fail(IA_ERR_DEVICE, "device index out of range");
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(IA_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned null");
+        g_noalloc_ptr[dev] = p;
+    }
+    *out = g_noalloc_ptr[dev];
+    return IA_OK;
+}
+
+// Largest N whose decode scratch (one slot: 2 L F + 16 bytes per Gaussian,
+// a multiple of 256 Gaussians) fits the array.
+int64_t noalloc_max_n(const ia_decoder* dec) {
+    const int64_t per = 2 * (int64_t)dec->hash.L * dec->hash.F + 16;
+    return ((int64_t)kNoAllocScratchBytes / per) & ~(int64_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+ia_status ia_decode_xyzt_noalloc(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
+                                 void* stream) {
+    if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
+    if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
+    if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
+    if (N == 0) return IA_OK;
+    const bool f16 = dec->mlp.dtype == IA_DTYPE_F16;  // the fp32 decoder uses no scratch
+    if (f16 && N > noalloc_max_n(dec))
+        return fail(IA_ERR_INVALID_ARG, "N = " + std::to_string(N) + " exceeds the " +
+                                            std::to_string(noalloc_max_n(dec)) +
+                                            " Gaussians the 20 MiB static scratch holds for this decoder");
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (f16) {
+        if (ia::decode_layout(dec->lv, N).total > kNoAllocScratchBytes)
+            return fail(IA_ERR_INVALID_ARG, "decode scratch exceeds the static array");
+        ia_status st = noalloc_scratch(&ws);
+        if (st != IA_OK) return st;
+        ws_bytes = kNoAllocScratchBytes;
+    }
+    return decode_common(dec, xyzt, 4, 0.0f, N, out, nullptr, 0, ws, ws_bytes, nullptr, stream);
 }
 
 void ia_decoder_destroy(ia_decoder* dec) {

@@ -31,7 +31,7 @@ BINNING_AUTO, BINNING_TILE_SORT, BINNING_REGIONS = 0, 1, 2
 # Every entry point include/ia.h declares.
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decoder_update_params", "ia_decode",
            "ia_decode_xyzt", "ia_decoder_destroy", "ia_decode_backward", "ia_decode_feature_bytes", "ia_decode_keep",
-           "ia_decode_workspace_size", "ia_decode_backward_workspace_size", "ia_lr_at",
+           "ia_decode_workspace_size", "ia_decode_backward_workspace_size", "ia_lr_at", "ia_decode_xyzt_noalloc",
            "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform", "ia_hexplane_destroy",
            "ia_render_workspace_size", "ia_render", "ia_render_backward", "ia_l1_loss",
            "ia_image_loss_workspace_size", "ia_image_loss", "ia_adam_step", "ia_adam_step_strided",
@@ -109,6 +109,7 @@ def load(path: str = LIB_PATH):
         L.ia_decode_backward_workspace_size.argtypes = [P, C.c_int64, P]
         L.ia_decode.argtypes = [P, P, C.c_int64, C.c_float, P, P, C.c_size_t, P, P]
         L.ia_decode_xyzt.argtypes = [P, P, C.c_int64, P, P, C.c_size_t, P, P]
+        L.ia_decode_xyzt_noalloc.argtypes = [P, P, C.c_int64, P, P]
         L.ia_decoder_destroy.argtypes = [P]
         L.ia_decode_backward.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, P, C.c_size_t, P,
                                          C.c_size_t, P]
@@ -226,6 +227,11 @@ def ia_decode(dec, xyz, N: int, t: float, out: Gaussians, ws=None, side=None, st
 def ia_decode_xyzt(dec, xyzt, N: int, out: Gaussians, ws=None, side=None, stream=None):
     _check(load().ia_decode_xyzt(dec, _ptr(xyzt), int(N), C.byref(out), _ptr(ws), _nbytes(ws), _side(side),
                                  _stream(stream)))
+
+
+def ia_decode_xyzt_noalloc(dec, xyzt, N: int, out: Gaussians, stream=None):
+    """ia_decode_xyzt with the library's static scratch (allocates nothing)."""
+    _check(load().ia_decode_xyzt_noalloc(dec, _ptr(xyzt), int(N), C.byref(out), _stream(stream)))
 
 
 def ia_decode_backward(dec, pos, pos_stride: int, N: int, t: float, grad_attr: Gaussians, grad_means, grad_pos,

@@ -201,6 +201,24 @@ IA_API ia_status ia_decode(const ia_decoder* dec, const float* xyz, int64_t N, f
 IA_API ia_status ia_decode_xyzt(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
                                 void* ws, size_t ws_bytes, void* side_stream, void* stream);
 
+/* For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): ia_decode_xyzt (no second stream) with its scratch in a
+ * file-scope device array of 20 MiB instead of a workspace.  Allocates
+ * nothing; each GPU the library runs on holds its own copy of the array from
+ * the first call on it until the process ends.
+ *   N: at most floor(20 MiB / (2 L F + 16 bytes)) rounded down to a multiple
+ *      of 256 for fp16 decoders (262,144 Gaussians for L = 16, F = 2;
+ *      145,408 for L = 16, F = 4), else INVALID_ARG before anything is
+ *      enqueued; any N for fp32 decoders, which use no scratch.
+ * Results equal those of ia_decode_xyzt for the same N bit for bit.  Every
+ * call on one GPU uses the same array: calls that overlap on one GPU (other
+ * streams, other threads) race and must not be made; the array needs no
+ * clearing between calls (each call overwrites what it reads).
+ * Errors: INVALID_ARG, DEVICE. */
+IA_API ia_status ia_decode_xyzt_noalloc(const ia_decoder* dec, const float* xyzt, int64_t N, const ia_gaussians* out,
+                                        void* stream);
+
 /* Bytes of the encoding z of N Gaussians (N x L x F fp16) that
  * ia_decode_keep stores and ia_decode_backward can reuse. */
 IA_API ia_status ia_decode_feature_bytes(const ia_decoder* dec, int64_t N, size_t* bytes);
