@@ -927,6 +927,42 @@ ia_status ia_adam_step_strided(float* param, int32_t param_stride, int32_t dim, 
     return IA_OK;
 }
 
+ia_status ia_spatial_order_workspace_size(int64_t N, int32_t frames, size_t* bytes) {
+    if (!bytes) return fail(IA_ERR_INVALID_ARG, "bytes is null");
+    if (N < 0 || N >= ((int64_t)1 << 32)) return fail(IA_ERR_INVALID_ARG, "N must be in [0, 2^32)");
+    if (frames < 1 || frames > 65535) return fail(IA_ERR_INVALID_ARG, "frames must be in 1..65535");
+    *bytes = ia::spatial_order_workspace(N, frames);
+    return IA_OK;
+}
+
+ia_status ia_spatial_order(const float* pos, int32_t pos_stride, int64_t N, const int64_t* frame_offsets,
+                           int32_t frames, uint32_t* perm, float* pos_out, void* ws, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    ia_status st = ia_spatial_order_workspace_size(N, frames, &need);
+    if (st != IA_OK) return st;
+    if (pos_stride < 3 || pos_stride > 64) return fail(IA_ERR_INVALID_ARG, "pos_stride must be in 3..64");
+    if (!frame_offsets) return fail(IA_ERR_INVALID_ARG, "frame_offsets is null");
+    if (frame_offsets[0] != 0) return fail(IA_ERR_INVALID_ARG, "frame_offsets[0] must be 0");
+    for (int f = 0; f < frames; ++f)
+        if (frame_offsets[f + 1] < frame_offsets[f]) return fail(IA_ERR_INVALID_ARG, "frame_offsets must be non-decreasing");
+    if (frame_offsets[frames] != N) return fail(IA_ERR_INVALID_ARG, "frame_offsets[frames] must equal N");
+    if (N == 0) return IA_OK;
+    if (!pos || !perm || !aligned(pos, 4) || !aligned(perm, 4)) return fail(IA_ERR_INVALID_ARG, "null or misaligned pos / perm");
+    if (pos_out) {
+        const char* a = reinterpret_cast<const char*>(pos);
+        const char* b = reinterpret_cast<const char*>(pos_out);
+        const size_t bytes = (size_t)N * pos_stride * sizeof(float);
+        if (!aligned(pos_out, 4)) return fail(IA_ERR_INVALID_ARG, "pos_out misaligned");
+        if (a < b + bytes && b < a + bytes) return fail(IA_ERR_INVALID_ARG, "pos_out must not overlap pos");
+    }
+    st = check_ws(ws, ws_bytes, need);
+    if (st != IA_OK) return st;
+    hipError_t e = ia::launch_spatial_order(pos, pos_stride, N, frame_offsets, frames, perm, pos_out, ws,
+                                            (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "spatial order launch");
+    return IA_OK;
+}
+
 ia_status ia_densify_accumulate(const float* grad_pos, int64_t N, float* grad_acc, int32_t* grad_count,
                                 void* stream) {
     if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");

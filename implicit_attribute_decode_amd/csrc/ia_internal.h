@@ -284,6 +284,16 @@ size_t densify_workspace(int64_t N);
 hipError_t launch_densify(const DensifyIn& in, void* ws, hipStream_t s);
 hipError_t launch_densify_accumulate(const float* g, int64_t N, float* acc, int32_t* cnt, hipStream_t s);
 
+// Copy `bytes` of host memory to device memory through kernel arguments
+// (stream-ordered, no host staging buffer that could outlive the call; the
+// host source may be freed on return).
+hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// Per-frame spatial order of positions (order.hip).
+size_t spatial_order_workspace(int64_t N, int frames);
+hipError_t launch_spatial_order(const float* pos, int stride, int64_t N, const int64_t* frame_offsets_host, int frames,
+                                uint32_t* perm, float* pos_out, void* ws, hipStream_t s);
+
 // Stable LSD radix sort of the first min(*count, cap) 64-bit words of buf[0]
 // on bits [lo, lo + nbits) (render.hip); returns the index (0 or 1) of the
 // buffer of buf that holds the result.  max_blocks <= radix_sort_blocks(cap);

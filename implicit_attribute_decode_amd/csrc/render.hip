@@ -54,6 +54,8 @@ __global__ void upload_kernel(uint32_t* dst, Payload p, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = p.w[i];
 }
 
+}  // namespace
+
 hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(src);
     size_t words = (bytes + 3) / 4;
@@ -68,6 +70,8 @@ hipError_t upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
     }
     return hipSuccess;
 }
+
+namespace {
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)

@@ -32,6 +32,7 @@ BINNING_AUTO, BINNING_TILE_SORT, BINNING_REGIONS = 0, 1, 2
 EXPORTS = ("ia_last_error", "ia_decoder_create", "ia_decoder_set_params", "ia_decoder_update_params", "ia_decode",
            "ia_decode_xyzt", "ia_decoder_destroy", "ia_decode_backward", "ia_decode_feature_bytes", "ia_decode_keep",
            "ia_decode_workspace_size", "ia_decode_backward_workspace_size", "ia_lr_at", "ia_decode_xyzt_noalloc",
+           "ia_spatial_order_workspace_size", "ia_spatial_order",
            "ia_hexplane_create", "ia_hexplane_set_params", "ia_hexplane_deform", "ia_hexplane_destroy",
            "ia_render_workspace_size", "ia_render", "ia_render_backward", "ia_l1_loss",
            "ia_image_loss_workspace_size", "ia_image_loss", "ia_adam_step", "ia_adam_step_strided",
@@ -110,6 +111,8 @@ def load(path: str = LIB_PATH):
         L.ia_decode.argtypes = [P, P, C.c_int64, C.c_float, P, P, C.c_size_t, P, P]
         L.ia_decode_xyzt.argtypes = [P, P, C.c_int64, P, P, C.c_size_t, P, P]
         L.ia_decode_xyzt_noalloc.argtypes = [P, P, C.c_int64, P, P]
+        L.ia_spatial_order_workspace_size.argtypes = [C.c_int64, C.c_int32, P]
+        L.ia_spatial_order.argtypes = [P, C.c_int32, C.c_int64, P, C.c_int32, P, P, P, C.c_size_t, P]
         L.ia_decoder_destroy.argtypes = [P]
         L.ia_decode_backward.argtypes = [P, P, C.c_int32, C.c_int64, C.c_float, P, P, P, P, P, C.c_size_t, P,
                                          C.c_size_t, P]
@@ -262,6 +265,22 @@ def ia_lr_at(base_lr: float, step: int, warmup: int, total: int, final_lr: float
 
 def ia_decoder_destroy(dec):
     load().ia_decoder_destroy(dec)
+
+
+def ia_spatial_order_workspace_size(N: int, frames: int) -> int:
+    b = C.c_size_t()
+    _check(load().ia_spatial_order_workspace_size(int(N), int(frames), C.byref(b)))
+    return int(b.value)
+
+
+def ia_spatial_order(pos, frame_offsets, perm, pos_out, ws, stream=None):
+    """pos: device [N, k>=3] float32 (contiguous rows); frame_offsets: host
+    int64 [frames+1]; perm: device int32 [N] out; pos_out: device like pos,
+    or None; ws: device uint8 workspace (256-byte aligned)."""
+    fo = np.ascontiguousarray(frame_offsets, np.int64)
+    N, stride = int(pos.shape[0]), int(pos.stride(0))
+    _check(load().ia_spatial_order(_ptr(pos), stride, N, fo.ctypes.data_as(C.c_void_p), len(fo) - 1, _ptr(perm),
+                                   _ptr(pos_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 # ----------------------------------------------------------------- HexPlane

@@ -347,6 +347,20 @@ class Renderer:
 
 
 
+def spatial_order(pos: torch.Tensor, frame_offsets):
+    """(perm, reordered positions): every frame's Gaussians along a Morton
+    curve of their normalised positions (ia_spatial_order); a one-time
+    storage layout for fixed per-frame position sets."""
+    fo = np.asarray(frame_offsets, np.int64)
+    pos = pos.contiguous()
+    N = int(pos.shape[0])
+    perm = torch.empty(N, dtype=torch.int32, device=pos.device)
+    out = torch.empty_like(pos)
+    ws = _Workspace(pos.device).get(ia.ia_spatial_order_workspace_size(N, len(fo) - 1))
+    ia.ia_spatial_order(pos, fo, perm, out, ws)
+    return perm, out
+
+
 def lr_at(step: int, base: float, warmup: int, total: int, final: float = 1e-7) -> float:
     """Learning rate at `step` (0-based): linear warm-up over `warmup` steps,
     then cosine decay from base to `final` at `total` ([SPIN] §4

@@ -321,6 +321,32 @@ IA_API void ia_hexplane_destroy(ia_hexplane* hp);
 /* Render: [SPIN] §3.1 Eq. 1-4, 16x16 tiles                                  */
 /* ------------------------------------------------------------------------ */
 
+/* Spatial order of the Gaussians of each frame (a storage layout, not a step
+ * of the method).  Every frame is a fixed set of positions ([SPIN] §3.2), and
+ * the order of a frame's Gaussians changes neither a decoded attribute nor a
+ * composited pixel (compositing follows depth, ties in index order), but it
+ * does change the hash gather's traffic: Gaussians close in space share the
+ * coarse levels' grid cells, and cache lines when they sit in one wave.
+ *   pos: device [N, pos_stride] (x, y, z first; e.g. xyzt rows, stride 4);
+ *   frame_offsets: host [frames + 1], 0 = first, N = last, non-decreasing;
+ *   perm: device uint32 [N] out: new position i holds old index perm[i];
+ *         every frame's range maps onto itself, its Gaussians in the order of
+ *         a Morton curve over the normalised positions of Eq. 7 (10 bits per
+ *         axis; fewer only when frame, cell and index do not fit 64 bits),
+ *         equal cells in index order;
+ *   pos_out: device [N, pos_stride] or NULL: pos_out[i] = pos[perm[i]] (must
+ *         not overlap pos);
+ *   ws: ia_spatial_order_workspace_size bytes (16 per Gaussian + 8 per
+ *         frame + radix counts), 256-byte aligned.
+ * One-time data preparation: decode, render and their backwards take the
+ * reordered positions as they are.
+ * Errors: INVALID_ARG (N outside [0, 2^32), frames outside 1..65535, bad
+ * offsets, null or overlapping buffers), WORKSPACE_TOO_SMALL, DEVICE. */
+IA_API ia_status ia_spatial_order_workspace_size(int64_t N, int32_t frames, size_t* bytes);
+IA_API ia_status ia_spatial_order(const float* pos, int32_t pos_stride, int64_t N, const int64_t* frame_offsets,
+                                  int32_t frames, uint32_t* perm, float* pos_out, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Pinhole camera, OpenCV axes (x right, y down, z forward).
  * p_cam = R p_world + t; u = fx x/z + cx; v = fy y/z + cy; pixel (i, j) has
  * its centre at (i + 0.5, j + 0.5).  Gaussians with z <= near_z are culled. */
