@@ -36,42 +36,68 @@ LEVELS, CORNERS, FEAT_BYTES = 16, 16, 4  # fp16 x 2 features per table entry
 GATHER_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES
 # Whole decode per Gaussian: 16 B position in, 1024 B gathered, 44 B out.
 DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
-# HBM-side bytes per gather launch of this workload (mean launch: 3.75M Gaussians), from two
-# rocprofv3 counter runs over `bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-extra
-# --calibrate-copy`: FETCH_SIZE 614,388.4 KiB x 2 + WRITE_SIZE 235,684.2 KiB x 1 (mean of the lean
-# and batched gather launches), the factors being what the counters read for a 1 GiB device copy
-# (profiles/gather_f16_sequence_hbm_traffic.md).  Valid for the gather kernels as they were when
-# counted; null once they change.
-GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 614_520.0 + 235_675.0) * 1024
+# HBM-side bytes per gather launch of this workload (positions in per-frame Morton order), from two
+# rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, each scaled by what the counter
+# reads for a plain device copy of known size); None until counted for the kernel as it stands.
+GATHER_TRAFFIC_BYTES_PER_LAUNCH = None
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(seq, dec, budget_s: float = 15.0, max_frames: int = 12) -> dict:
-    """The oracle (plain C, OpenMP) decoding and rendering whole frames of the
-    same sequence on this host's cores; frames/s over a bounded sample."""
+def cpu_baseline(seq, dec, frame: int = 1, one_core_decode: int = 20_000) -> dict:
+    """The oracle (plain C, OpenMP, fp64 decode) on the same workload, stage by
+    stage, on this host: one whole frame of the sequence (200k Gaussians,
+    640x360), median of 5 on all cores; on one core the median of 3, with the
+    decode timed on the frame's first `one_core_decode` Gaussians and scaled
+    to the frame (it is linear in N).  Value: frames/s on all cores."""
     import oracle as O
 
-    def one(f):
-        x = seq.xyzt([f])
-        d = O.decode(dec, x, mode=0)
-        fo = np.array([0, x.shape[0]])
-        O.render([seq.camera(f)], fo, x[:, :3], d["scales"].astype(np.float32), d["quats"].astype(np.float32),
-                 d["opacity"].astype(np.float32), d["colors"])
+    x = seq.xyzt([frame])
+    cam = seq.camera(frame)
+    fo = np.array([0, x.shape[0]])
 
-    t0 = time.perf_counter()
-    one(0)
-    t1 = time.perf_counter() - t0
-    k = int(max(1, min(max_frames, budget_s // max(t1, 1e-3))))
-    t0 = time.perf_counter()
-    for f in range(1, 1 + k):
-        one(f)
-    dt = time.perf_counter() - t0
-    return {"value": round(k / dt, 4), "unit": "frames/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"frames 1..{k} of the 150-frame sequence (200k Gaussians each, 640x360), "
-                      f"decode (fp64) + render, {dt:.1f} s"}
+    def run(xs, reps, stages=("decode", "preprocess", "bin_sort", "raster"), attrs=None):
+        t = {k: [] for k in stages}
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            d = O.decode(dec, xs, mode=0) if "decode" in stages else attrs
+            t1 = time.perf_counter()
+            if "decode" in stages:
+                t["decode"].append(t1 - t0)
+            if "preprocess" in stages:
+                f = np.array([0, xs.shape[0]])
+                pre = O.preprocess([cam], f, xs[:, :3], d["scales"].astype(np.float32),
+                                   d["quats"].astype(np.float32))
+                t2 = time.perf_counter()
+                b = O.bin_and_sort([cam], f, pre)
+                t3 = time.perf_counter()
+                O.raster_tiles([cam], b, pre, d["opacity"].astype(np.float32), d["colors"])
+                t4 = time.perf_counter()
+                t["preprocess"].append(t2 - t1)
+                t["bin_sort"].append(t3 - t2)
+                t["raster"].append(t4 - t3)
+        return {k: float(np.median(v)) for k, v in t.items()}, d
+
+    cores = O.num_threads()
+    run(x[:2000], 1)  # warm-up (page-in, thread pool)
+    all_med, attrs = run(x, 5)
+    O.set_num_threads(1)
+    try:
+        one_dec, _ = run(x[:one_core_decode], 3, stages=("decode",))
+        one_rest, _ = run(x, 3, stages=("preprocess", "bin_sort", "raster"), attrs=attrs)
+    finally:
+        O.set_num_threads(cores)
+    one_med = {"decode": one_dec["decode"] * x.shape[0] / one_core_decode, **one_rest}
+    all_s, one_s = sum(all_med.values()), sum(one_med.values())
+    return {"value": round(1.0 / all_s, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
+            "sample": f"frame {frame} of the 150-frame sequence (200k Gaussians, 640x360): decode (fp64) + "
+                      f"preprocess + bin/sort + raster, median of 5 per stage on {cores} cores; one core: "
+                      f"median of 3, decode timed on {one_core_decode} Gaussians and scaled to the frame",
+            "per_stage_ms": {"all_cores": {k: round(1e3 * v, 2) for k, v in all_med.items()},
+                             "one_core": {k: round(1e3 * v, 2) for k, v in one_med.items()}},
+            "one_core_value": round(1.0 / one_s, 4)}
 
 
 HEX_FLOP_PER_GAUSSIAN = 2 * (192 * 256 + 256 * 256 + 256 * 58)  # 259,072
@@ -322,6 +348,152 @@ def _train_full(S, Decoder, Renderer, stream, xyzt, fo, cams, target) -> dict:
             "steps_taken": opt.t, "kernels_ms": kernels}
 
 
+def median_step(fn, n, warm, stream) -> dict:
+    """`warm` untimed calls, then `n` calls each bracketed by HIP events on
+    the stream: median, min and max milliseconds."""
+    import torch
+
+    for _ in range(warm):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(n):
+        fn()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(n)])
+    return {"steps": n, "warmup": warm, "median_ms": round(float(np.median(ms)), 4),
+            "min_ms": round(float(ms.min()), 4), "max_ms": round(float(ms.max()), 4)}
+
+
+def render_counts(step, xyzt, fo, cams, attrs, E) -> dict:
+    """From one render of the step's decoded attributes with T_final and
+    n_contrib: visible Gaussians, tile entries and the pixel x Gaussian
+    evaluations the compositing rule requires (per pixel, the entries of its
+    tile up to the one after which T < 1e-4, else the whole list)."""
+    import torch
+
+    from implicit_attribute_decode_amd.pipeline import Renderer
+
+    R = Renderer()
+    g = dict(means=xyzt[:, :3], **attrs)
+    res = R.render(g, fo, cams, E + E // 50 + 4096, aux=True, keys=False)
+    F, W, H = len(cams), cams[0].W, cams[0].H
+    tx, ty = (W + 15) // 16, (H + 15) // 16
+    rg = Renderer.view(res, "tile_ranges", F * tx * ty).long()
+    cnt = (rg[:, 1] - rg[:, 0]).view(F, ty * tx)
+    tile = (torch.arange(H, device=xyzt.device)[:, None] // 16) * tx + torch.arange(W, device=xyzt.device)[None, :] // 16
+    per_px = cnt[:, tile.view(-1)].view(F, H, W)
+    stopped = res["T_final"] < 1e-4
+    evals = torch.where(stopped, res["n_contrib"].long(), per_px).sum()
+    vis = (Renderer.view(res, "tiles_touched", int(xyzt.shape[0])) > 0).sum()
+    out = {"visible": int(vis.item()), "entries": int(res["n_entries"].item()), "evaluations": int(evals.item()),
+           "stopped_pixels": int(stopped.sum().item())}
+    del res, R
+    return out
+
+
+def fetched_gather_bytes(xyzt, h) -> float:
+    """Bytes the hash gather fetches per Gaussian: the 16-byte position and 4
+    bytes per corner of non-zero weight (a corner's weight is zero when the
+    position sits exactly on a grid vertex of that axis), evaluated with the
+    fp32 operations of the normalisation and cell decision of Eq. 7-9."""
+    import torch
+
+    x, y, z, t = (xyzt[:, k].float() for k in range(4))
+    n2 = x * x + y * y
+    n2 = n2 + z * z
+    n = torch.sqrt(n2)
+    k = (2.0 - 1.0 / n) / n
+    inside = n <= 1.0
+    axes = [torch.where(inside, v, v * k) * 0.25 + 0.5 for v in (x, y, z)]
+    tn = ((t - h.t_min) / (h.t_max - h.t_min)).clamp(0.0, 1.0)
+    total = torch.zeros_like(x)
+    for l in range(h.L):
+        res = int(np.floor(h.base_res * h.growth ** l))
+        res_t = h.temporal_res if h.temporal_res > 0 else res
+        c = torch.ones_like(x)
+        for v, r in ((axes[0], res), (axes[1], res), (axes[2], res), (tn, res_t)):
+            p = v * float(r - 1)
+            i = torch.floor(p).clamp(0, r - 2)
+            f = p - i
+            c = c * torch.where((f == 0.0) | (f == 1.0), 1.0, 2.0)
+        total += c
+    return 16.0 + 4.0 * float(total.mean().item())
+
+
+def general_t_gather(D, xyzt, seq, stream) -> dict:
+    """The gather at a general time: the same positions with t moved half a
+    frame off the temporal vertices (all 16 corners weighted), decoded as in
+    the step; achieved algorithmic bytes against HBM."""
+    import torch
+
+    from implicit_attribute_decode_amd import ia
+
+    xg = xyzt.clone()
+    half = 0.5 / (seq.frames - 1)
+    xg[:, 3] = torch.where(xg[:, 3] + half <= 1.0, xg[:, 3] + half, xg[:, 3] - half)
+    out = D.decode_xyzt(xg)
+    D.decode_xyzt(xg, out=out)
+    torch.cuda.synchronize()
+    ia.ia_profile_reset()
+    ia.ia_profile_enable(True)
+    for _ in range(2):
+        D.decode_xyzt(xg, out=out)
+    torch.cuda.synchronize()
+    prof = ia.ia_profile_report()
+    ia.ia_profile_enable(False)
+    calls, ms = prof["gather_f16_kernel"]
+    n = xyzt.shape[0] * 2 / calls
+    got = GATHER_BYTES_PER_GAUSSIAN * n / (ms / calls / 1e3) / 1e9
+    del out, xg
+    return {"achieved": round(got, 1), "frac": round(got / HBM_PEAK_GBS, 4), "avg_launch_ms": round(ms / calls, 4),
+            "positions": "sequence, t + half a frame"}
+
+
+# per pixel x Gaussian evaluation of the compositing rule: offset, power (five
+# products and sums), the 3-sigma and alpha tests, alpha, the colour update and
+# the transmittance update; the exponential is not counted
+RASTER_FLOP_PER_EVAL = 24
+FP32_VALU_PEAK_TFLOPS = 78.6  # non-packed (packed fp32 instructions are not used)
+
+
+def other_rooflines(ms: dict, N: int, E: int, c: dict) -> dict:
+    """The step's other kernels against their own rooflines, from the same
+    HIP-event times; algorithmic work per unit as in the design notes."""
+    nvis = c["visible"]
+
+    def row(names, work, peak, unit, bound, per):
+        t = sum(ms.get(k, 0.0) for k in names)
+        if t <= 0:
+            return None
+        got = work / (t / 1e3)
+        return {"kernels": names, "bound": bound, "achieved": round(got, 1), "peak": peak, "unit": unit,
+                "frac": round(got / peak, 4), "ms_per_step": round(t, 4), "work_per_unit": per}
+
+    sort = ["sort_upsweep_kernel", "sort_scan_kernel", "sort_downsweep_kernel"]
+    emit = ["compact_kernel", "sorted_rects_kernel", "offsets_kernel", "emit_kernel", "scan_reduce_kernel",
+            "scan_top_kernel", "scan_down_kernel"]
+    out = {
+        "raster": row(["raster_kernel"], RASTER_FLOP_PER_EVAL * c["evaluations"] / 1e12, FP32_VALU_PEAK_TFLOPS,
+                      "TFLOP/s", "valu", f"{RASTER_FLOP_PER_EVAL} flop per pixel x Gaussian evaluation "
+                      f"({c['evaluations']} evaluations, measured)"),
+        "preprocess": row(["preprocess_kernel"], 108.0 * N / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                          "56 B in + 52 B out per Gaussian"),
+        "radix_sort": row(sort, 24.0 * (4 * nvis + 2 * E) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                          f"24 B per item and pass: 4 passes over {nvis} visible Gaussians, 2 over {E} entries"),
+        "key_emit": row(emit, (8.0 * N + 12.0 * E) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                        "8 B per Gaussian + 12 B per entry"),
+        "ranges": row(["ranges_kernel"], 8.0 * E / 1e9, HBM_PEAK_GBS, "GB/s", "hbm", "8 B per entry"),
+        "normalize": row(["normalize_kernel"], 32.0 * N / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                         "16 B in + 16 B out per Gaussian"),
+        "mlp": row(["mlp_f16_kernel"], MLP_FLOP_PER_GAUSSIAN * N / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma",
+                   "13,696 flop per Gaussian (beside the gather, one block per two compute units)"),
+    }
+    return {k: v for k, v in out.items() if v is not None}
+
+
 def profiled(fn, reps):
     """Milliseconds per call of each library kernel over `reps` calls of fn
     (HIP events around every launch), largest first."""
@@ -432,8 +604,12 @@ def main():
     ms_step = timed(step, args.steps, stream)
     wall = (time.perf_counter() - wall0) / args.steps
     log(f"step: {ms_step:.3f} ms (wall {1e3 * wall:.3f} ms)")
+    # the timing protocol of the measurement plan: 10 warm-ups, then the
+    # median of 50 steps, each bracketed by HIP events on the stream
+    med = median_step(step, 50, 10, stream)
+    log(f"median of 50 steps: {med['median_ms']:.3f} ms")
 
-    # dominant kernel: HIP events around every library launch, same streams
+    # per kernel: HIP events around every library launch, on its launch stream
     ia.ia_profile_reset()
     ia.ia_profile_enable(True)
     for _ in range(3):
@@ -441,26 +617,21 @@ def main():
     torch.cuda.synchronize()
     prof = ia.ia_profile_report()
     ia.ia_profile_enable(False)
+    kernels = {k: {"calls_per_step": round(v[0] / 3, 2), "ms_per_step": round(v[1] / 3, 4)}
+               for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
+    log("per-kernel (ms/step): " + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
+    per_step_ms = {k: v[1] / 3 for k, v in prof.items()}
     calls, gather_ms = prof["gather_f16_kernel"]
     gather_avg_ms = gather_ms / calls
     gaussians_per_launch = N * 3 / calls
     achieved = GATHER_BYTES_PER_GAUSSIAN * gaussians_per_launch / (gather_avg_ms / 1e3) / 1e9
-    kernels = {k: {"calls_per_step": round(v[0] / 3, 2), "ms_per_step": round(v[1] / 3, 4)}
-               for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
-    log("per-kernel (ms/step): " + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
-    # other kernels against their own rooflines, from the same HIP-event times
-    # (algorithmic work per unit as in the design notes; the MLP shares the
-    # chip with the gather it runs beside, and its time goes to GELU's VALU work)
-    per_step_ms = {k: v[1] / 3 for k, v in prof.items()}
-    kernel_rooflines = {}
-    for name, bound, work, peak, unit in (
-            ("preprocess_kernel", "hbm", 108.0 * N / 1e9, HBM_PEAK_GBS, "GB/s"),
-            ("normalize_kernel", "hbm", 32.0 * N / 1e9, HBM_PEAK_GBS, "GB/s"),
-            ("mlp_f16_kernel", "mfma", MLP_FLOP_PER_GAUSSIAN * N / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s")):
-        if per_step_ms.get(name):
-            got = work / (per_step_ms[name] / 1e3)
-            kernel_rooflines[name] = {"bound": bound, "achieved": round(got, 1), "peak": peak, "unit": unit,
-                                      "frac": round(got / peak, 4)}
+
+    # the counts the other rooflines need, from one render of this step's attributes
+    counts = render_counts(step, xyzt, fo, cams, attrs, E)
+    fetched = fetched_gather_bytes(xyzt, dec.hash)
+    general = general_t_gather(D, xyzt, seq, stream)
+    kernel_rooflines = other_rooflines(per_step_ms, N, E, counts)
+    log(f"rooflines: {kernel_rooflines}")
 
     extra = {}
     if not args.no_extra:
@@ -490,6 +661,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "median_of_50": med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -499,12 +671,19 @@ def main():
                                "27-camera ring, 16-level fp16 hash (2^19), 32-64-64-11 GELU decoder",
                    "frames": F, "gaussians_per_frame": per, "tile_entries": E, "frame_groups": args.parts,
                    "layout": layout,
-                   "kernels": kernels, "kernel_rooflines": kernel_rooflines, **extra},
+                   "kernels": kernels, "kernel_rooflines": kernel_rooflines, "render_counts": counts, **extra},
         "roofline": {"kernel": "gather_f16_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": round(GATHER_TRAFFIC_BYTES_PER_LAUNCH) if F == 150 and per == 200_000 else None,
+                     "traffic": (round(GATHER_TRAFFIC_BYTES_PER_LAUNCH) if GATHER_TRAFFIC_BYTES_PER_LAUNCH
+                                 and F == 150 and per == 200_000 and not args.stored_order else None),
                      "traffic_unit": "bytes/launch", "bytes_per_unit": GATHER_BYTES_PER_GAUSSIAN,
-                     "units_per_launch": round(gaussians_per_launch), "avg_launch_ms": round(gather_avg_ms, 4)},
+                     "units_per_launch": round(gaussians_per_launch), "avg_launch_ms": round(gather_avg_ms, 4),
+                     # the corners the kernel actually fetches (zero-weight corners are skipped)
+                     "fetched_bytes_per_unit": round(fetched, 1),
+                     "achieved_fetched": round(achieved * fetched / GATHER_BYTES_PER_GAUSSIAN, 1),
+                     "frac_fetched": round(achieved * fetched / GATHER_BYTES_PER_GAUSSIAN / HBM_PEAK_GBS, 4),
+                     # the same positions half a frame off the temporal vertices: all 16 corners weighted
+                     "general_t": general},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

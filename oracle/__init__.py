@@ -63,6 +63,8 @@ P = C.c_void_p
 def _declare(L):
     L.orc_num_threads.restype = C.c_int
     L.orc_num_threads.argtypes = []
+    L.orc_set_num_threads.restype = None
+    L.orc_set_num_threads.argtypes = [C.c_int]
     L.orc_half_to_double.restype = C.c_double
     L.orc_half_to_double.argtypes = [C.c_uint16]
     L.orc_double_to_half.restype = C.c_uint16
@@ -94,6 +96,11 @@ def _declare(L):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later parallel loops."""
+    lib().orc_set_num_threads(int(n))
 
 
 def _p(a: np.ndarray):

@@ -44,6 +44,15 @@ EXPORT int orc_num_threads(void) {
 #endif
 }
 
+/* Sets the threads later parallel loops use (n >= 1; no-op without OpenMP). */
+EXPORT void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* IEEE binary16 <-> double, from the format definition                      */
 /* ------------------------------------------------------------------------ */
