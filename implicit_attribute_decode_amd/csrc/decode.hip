@@ -192,17 +192,17 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // normalize_kernel: Eq. 7-8 once per Gaussian -> x~ (fp32 x4) in the scratch.
 //
 // gather_f16_kernel: level-major.  Block b handles level b / nchunk and
-// Gaussians [256 (b % nchunk), +256).  Blocks are dispatched in index order
-// and spread round-robin over the XCDs, so at any moment all XCDs work on the
-// same level and that level's 2^log2T x 4-byte table stays resident in every
-// XCD's L2 instead of being fetched line by line from HBM / Infinity Cache.
-// Four lanes share one (Gaussian, level): lane s takes the x-corner s & 1 and
-// the y-corner s >> 1 and loops over the four (z, t) corners.  Under the hash
-// (first prime 1) the two x-corners differ only in their low index bits, so
-// neighbouring lanes usually hit the same cache line inside one load
-// instruction, halving the distinct lines each gather touches.  Two quad
-// shuffles sum the four partial results.  Output z[level][i] = two fp16
-// features packed in 32 bits (RNE).
+// Gaussians [256 (b % nchunk), +256), one lane per Gaussian.  Blocks are
+// dispatched in index order and spread round-robin over the XCDs, so at any
+// moment all XCDs work on the same level and that level's 2^log2T x 4-byte
+// table stays resident in every XCD's L2 instead of being fetched line by
+// line from HBM / Infinity Cache.  A lane computes its Gaussian's cell once
+// and issues all its corner loads before using any (range-checked buffer
+// loads: a corner of zero weight, or a lane past the last Gaussian, reads
+// past the table, which returns zero without a memory request).  Consecutive
+// lanes hold consecutive Gaussians, so when the positions of a frame are
+// stored in spatial order the lanes of a wave share the coarse levels' cache
+// lines.  Output z[level][i] = two fp16 features packed in 32 bits (RNE).
 //
 // mlp_f16_kernel: the 32 -> 64 -> 64 -> 11 (or 56, SH colour) decoder on
 // v_mfma_f32_16x16x32_f16.
@@ -210,8 +210,8 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // B column c, each with eight k-slots per lane that A and B share; D holds
 // rows 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows.
 
-constexpr int kGatherPerBlock = 256;  // Gaussians per gather block (64 per pass x 4 passes)
-constexpr int kMlpCusPerBlock = 2;    // MLP beside a gather: one block per this many CUs
+constexpr int kGatherPerBlock = 256;  // Gaussians per gather block, one lane each
+constexpr int kMlpCusPerBlock = 1;    // MLP beside a gather: one block per this many CUs
 constexpr int kNormBlocksPerCu = 2;   // normalisation beside a gather: blocks per CU
 
 __global__ void __launch_bounds__(256) normalize_kernel(DecodeArgs a, const float* pos, int64_t n, float4* xt) {
@@ -223,170 +223,119 @@ __global__ void __launch_bounds__(256) normalize_kernel(DecodeArgs a, const floa
     }
 }
 
-__global__ void __launch_bounds__(256) gather_f16_kernel(const float4* xt, int64_t n, int nchunk, HashLevels h,
-                                                         const uint32_t* tables, uint32_t* zbuf, int64_t zstride) {
+// One lane's gather of one level (see gather_f16_kernel).  DENSE: corner
+// index = sum of the per-axis terms (row-major, x fastest); else their XOR
+// (the hash), modulo T.
+template <bool DENSE>
+__device__ __forceinline__ void gather_lane(const float4 p, bool valid, int res, int res_t, uint32_t mask,
+                                            const __amdgpu_buffer_rsrc_t rt, float& a0, float& a1) {
 #pragma clang fp contract(fast)
-    const int level = blockIdx.x / nchunk;
-    const int64_t first = (int64_t)(blockIdx.x % nchunk) * kGatherPerBlock;
-    const int res = h.res_s[level], res_t = h.res_t[level];
-    const bool dense = h.dense[level] != 0;
-    const uint32_t* tab = tables + (size_t)level * h.T;
-    uint32_t* zl = zbuf + (size_t)level * zstride;
-    const int s = threadIdx.x & 3;           // corner pair this lane takes
-    const int bx = s & 1, by = s >> 1;
-    const int sub = threadIdx.x >> 2;        // Gaussian slot within a pass (0..63)
-    const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
-#pragma unroll 2
-    for (int j = 0; j < kGatherPerBlock / 64; ++j) {
-        const int64_t i = first + j * 64 + sub;
-        if (i >= n) break;  // uniform across each group of four lanes
-        const float4 p = xt[i];
-        int cx, cy, cz, ct;
-        float fx, fy, fz, ft;
-        cell_axis(p.x, res, cx, fx);
-        cell_axis(p.y, res, cy, fy);
-        cell_axis(p.z, res, cz, fz);
-        cell_axis(p.w, res_t, ct, ft);
-        const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
-        uint32_t txy, tz0, tz1, tt0, tt1;
-        if (dense) {
-            txy = ux + uy * r;
-            tz0 = (uint32_t)cz * r2;
-            tz1 = tz0 + r2;
-            tt0 = (uint32_t)ct * r3;
-            tt1 = tt0 + r3;
-        } else {
-            txy = (ux * kP1) ^ (uy * kP2);
-            tz0 = (uint32_t)cz * kP3;
-            tz1 = (uint32_t)(cz + 1) * kP3;
-            tt0 = (uint32_t)ct * kP4;
-            tt1 = (uint32_t)(ct + 1) * kP4;
-        }
-        const float wxy = (bx ? fx : 1.0f - fx) * (by ? fy : 1.0f - fy);
-        const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
-        const uint32_t tz[2] = {tz0, tz1}, tt[2] = {tt0, tt1};
-        float a0 = 0.0f, a1 = 0.0f;
+    int cx, cy, cz, ct;
+    float fx, fy, fz, ft;
+    cell_axis(p.x, res, cx, fx);
+    cell_axis(p.y, res, cy, fy);
+    cell_axis(p.z, res, cz, fz);
+    cell_axis(p.w, res_t, ct, ft);
+    uint32_t tx[2], ty[2], tz[2], tt[2];
+    if (DENSE) {
+        const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
+        tx[0] = (uint32_t)cx;
+        tx[1] = tx[0] + 1u;
+        ty[0] = (uint32_t)cy * r;
+        ty[1] = ty[0] + r;
+        tz[0] = (uint32_t)cz * r2;
+        tz[1] = tz[0] + r2;
+        tt[0] = (uint32_t)ct * r3;
+        tt[1] = tt[0] + r3;
+    } else {
+        tx[0] = (uint32_t)cx * kP1;
+        tx[1] = (uint32_t)(cx + 1) * kP1;
+        ty[0] = (uint32_t)cy * kP2;
+        ty[1] = (uint32_t)(cy + 1) * kP2;
+        tz[0] = (uint32_t)cz * kP3;
+        tz[1] = (uint32_t)(cz + 1) * kP3;
+        tt[0] = (uint32_t)ct * kP4;
+        tt[1] = (uint32_t)(ct + 1) * kP4;
+    }
+    auto comb = [](uint32_t u, uint32_t v) { return DENSE ? u + v : u ^ v; };
+    const float wx[2] = {1.0f - fx, fx}, wy[2] = {1.0f - fy, fy}, wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
+    // partial products over x, y, z shared by the two temporal vertices; the
+    // weight is ((w_x w_y) w_z) w_t as defined
+    float wxyz[8];
+    uint32_t txyz[8];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int bz = c & 1, bt = c >> 1;
-            const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
-            const float w = (wxy * wz[bz]) * wt[bt];
-            // A corner of exactly zero weight adds exactly zero (finite table
-            // entries): it is not fetched.  This happens whenever a coordinate
-            // sits on a grid vertex, e.g. frames whose time is a temporal vertex.
-            if (w != 0.0f) {
-                const uint32_t raw = tab[idx];
-                a0 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
-                a1 += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+    for (int c = 0; c < 8; ++c) {
+        const int bx = c & 1, by = (c >> 1) & 1, bz = (c >> 2) & 1;
+        wxyz[c] = (wx[bx] * wy[by]) * wz[bz];
+        txyz[c] = comb(comb(tx[bx], ty[by]), tz[bz]);
+    }
+    // The corners of one temporal vertex are fetched only when some lane of
+    // the wave gives them a non-zero weight: a frame's Gaussians share one
+    // time, and on a temporal vertex half the corners weigh exactly zero.
+    // Corners of zero weight add exactly zero (finite table entries), so
+    // skipping them, for a lane or for the wave, changes no sum.
+    const bool need_t[2] = {__ballot(valid && wt[0] != 0.0f) != 0ull, __ballot(valid && wt[1] != 0.0f) != 0ull};
+    uint32_t raw[16];
+    float w[16];
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt) {
+        if (need_t[bt]) {
+            // all loads of this temporal vertex are issued before any is used;
+            // one not needed reads past the end of the table (zero, no request)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                w[8 * bt + c] = wxyz[c] * wt[bt];
+                const uint32_t idx = comb(txyz[c], tt[bt]) & mask;
+                raw[8 * bt + c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rt, (valid && w[8 * bt + c] != 0.0f) ? idx * 4u : kBufferNone, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                w[8 * bt + c] = 0.0f;
+                raw[8 * bt + c] = 0u;
             }
         }
-        a0 += __shfl_xor(a0, 1, 4);
-        a1 += __shfl_xor(a1, 1, 4);
-        a0 += __shfl_xor(a0, 2, 4);
-        a1 += __shfl_xor(a1, 2, 4);
-        if (s == 0) {
-            const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);
-            const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
-            zl[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        }
+    }
+    // sum over the 16 corners in corner order of w_c * table entry
+    a0 = 0.0f;
+    a1 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        a0 += w[c] * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[c] & 0xffffu));
+        a1 += w[c] * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[c] >> 16));
     }
 }
 
-// The same gather for a launch with nothing beside it: all 16 corner loads of
-// a thread's four passes are issued before any is used (46 VGPRs), which a
-// lone launch needs to cover the L2 latency; beside the MLP the kernel above
-// leaves that MLP more room.  The loads are range-checked buffer loads over
-// the level's table: a skipped corner or a lane past the last Gaussian reads
-// past the end (zero, no memory request) instead of branching.
-__global__ void __launch_bounds__(256) gather_f16_batched_kernel(const float4* xt, int64_t n, int nchunk,
-                                                                 HashLevels h, const uint32_t* tables,
-                                                                 uint32_t* zbuf, int64_t zstride) {
-#pragma clang fp contract(fast)
+__global__ void __launch_bounds__(kGatherPerBlock) gather_f16_kernel(const float4* xt, int64_t n, int nchunk,
+                                                                     HashLevels h, const uint32_t* tables,
+                                                                     uint32_t* zbuf, int64_t zstride) {
     const int level = blockIdx.x / nchunk;
-    const int64_t first = (int64_t)(blockIdx.x % nchunk) * kGatherPerBlock;
-    const int res = h.res_s[level], res_t = h.res_t[level];
-    const bool dense = h.dense[level] != 0;
-    const uint32_t* tab = tables + (size_t)level * h.T;
-    uint32_t* zl = zbuf + (size_t)level * zstride;
-    const int s = threadIdx.x & 3;
-    const int bx = s & 1, by = s >> 1;
-    const int sub = threadIdx.x >> 2;
-    const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
-    constexpr int kPasses = kGatherPerBlock / 64;
+    const int64_t i = (int64_t)(blockIdx.x % nchunk) * kGatherPerBlock + threadIdx.x;
+    const bool valid = i < n;
+    const float4 p = xt[valid ? i : n - 1];
     const __amdgpu_buffer_rsrc_t rt =
-        __builtin_amdgcn_make_buffer_rsrc((void*)tab, (short)0, (int)(h.T * 4u), kBufferWord3);
-    float4 P[kPasses];
-#pragma unroll
-    for (int j = 0; j < kPasses; ++j) {
-        const int64_t i = first + j * 64 + sub;
-        P[j] = xt[i < n ? i : n - 1];
-    }
-    uint32_t raw[kPasses][4];
-    float wc[kPasses][4];
-#pragma unroll
-    for (int j = 0; j < kPasses; ++j) {
-        const bool valid = first + j * 64 + sub < n;
-        int cx, cy, cz, ct;
-        float fx, fy, fz, ft;
-        cell_axis(P[j].x, res, cx, fx);
-        cell_axis(P[j].y, res, cy, fy);
-        cell_axis(P[j].z, res, cz, fz);
-        cell_axis(P[j].w, res_t, ct, ft);
-        const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
-        uint32_t txy, tz[2], tt[2];
-        if (dense) {
-            txy = ux + uy * r;
-            tz[0] = (uint32_t)cz * r2;
-            tz[1] = tz[0] + r2;
-            tt[0] = (uint32_t)ct * r3;
-            tt[1] = tt[0] + r3;
-        } else {
-            txy = (ux * kP1) ^ (uy * kP2);
-            tz[0] = (uint32_t)cz * kP3;
-            tz[1] = (uint32_t)(cz + 1) * kP3;
-            tt[0] = (uint32_t)ct * kP4;
-            tt[1] = (uint32_t)(ct + 1) * kP4;
-        }
-        const float wxy = (bx ? fx : 1.0f - fx) * (by ? fy : 1.0f - fy);
-        const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int bz = c & 1, bt = c >> 1;
-            const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
-            wc[j][c] = (wxy * wz[bz]) * wt[bt];
-            // a corner of zero weight adds exactly zero: not fetched (zero bits stand in)
-            const uint32_t off = (valid && wc[j][c] != 0.0f) ? idx * 4u : kBufferNone;
-            raw[j][c] = __builtin_amdgcn_raw_buffer_load_b32(rt, off, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kPasses; ++j) {
-        float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            a0 += wc[j][c] * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][c] & 0xffffu));
-            a1 += wc[j][c] * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j][c] >> 16));
-        }
-        // the same sums over the four lanes as the kernel above: xor 1, then xor 2
-        a0 += __shfl_xor(a0, 1, 4);
-        a1 += __shfl_xor(a1, 1, 4);
-        a0 += __shfl_xor(a0, 2, 4);
-        a1 += __shfl_xor(a1, 2, 4);
-        const int64_t i = first + j * 64 + sub;
-        if (s == 0 && i < n) {
-            const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);
-            const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
-            zl[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        }
+        __builtin_amdgcn_make_buffer_rsrc((void*)(tables + (size_t)level * h.T), (short)0, (int)(h.T * 4u),
+                                          kBufferWord3);
+    float a0, a1;
+    if (h.dense[level])
+        gather_lane<true>(p, valid, h.res_s[level], h.res_t[level], h.mask, rt, a0, a1);
+    else
+        gather_lane<false>(p, valid, h.res_s[level], h.res_t[level], h.mask, rt, a0, a1);
+    if (valid) {
+        const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);
+        const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
+        zbuf[(size_t)level * zstride + i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
     }
 }
 
-// Bias + activation of one 16x16 D tile (rows 16 rb + 4 q + e), rounded to fp16.
+// Activation of one 16x16 D tile (rows 16 rb + 4 q + e; the MFMA started
+// from the bias, so acc = W x + b), rounded to fp16.
 template <bool GELU>
-__device__ __forceinline__ half4_t act_tile(floatx4 acc, const float* bias) {
+__device__ __forceinline__ half4_t act_tile(floatx4 acc) {
     half4_t h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = (_Float16)hidden_act<GELU>(acc[e] + bias[e]);
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)hidden_act<GELU>(acc[e]);
     return h;
 }
 
@@ -394,16 +343,15 @@ __device__ __forceinline__ half4_t act_tile(floatx4 acc, const float* bias) {
 // Eq. 11: rows 0-2 scale, 3-6 rotation (normalised), 7-54 the 48 SH
 // coefficients (no activation), 55 opacity (sigmoid); rows 56-63 are zero.
 // Lane (q, c) holds rows 16 hb + 4 q + e of Gaussian gl.
-__device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (&A3)[4][2], const float (&B3)[4][4],
+__device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (&A3)[4][2], const floatx4 (&B3)[4],
                                             half8_t h0, half8_t h1, int64_t gl, int64_t n, int64_t out_off, int q) {
     float o[4][4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-        floatx4 acc = {0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[hb][0], h0, acc, 0, 0, 0);
+        floatx4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[hb][0], h0, B3[hb], 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[hb][1], h1, acc, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[hb][e] = acc[e] + B3[hb][e];
+        for (int e = 0; e < 4; ++e) o[hb][e] = acc[e];
     }
     // rotation rows 3 (q = 0) and 4-6 (q = 1) of the first tile
     const float part = q == 0 ? o[0][3] * o[0][3] : (q == 1 ? o[0][0] * o[0][0] + o[0][1] * o[0][1] + o[0][2] * o[0][2] : 0.0f);
@@ -448,7 +396,8 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
     const _Float16* Wh = (const _Float16*)a.W[2];  // [kHeadRows][64]
 
     half8_t A1[4], A2[4][2], A3[NH][2];
-    float B1[4][4], B2[4][4], B3[NH][4];
+    // biases as the MFMAs' initial accumulators: rows 16 rb + 4 q + e
+    floatx4 B1[4], B2[4], B3[NH];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         A1[rb] = a_tile32(W1, 32, 64, rb, 0, q, c);
@@ -495,10 +444,9 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
         for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                floatx4 z0 = {0, 0, 0, 0};
-                const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z[g], z0, 0, 0, 0);
-                const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z[g], z0, 0, 0, 0);
-                H1[m][g] = cat8(act_tile<GELU>(lo, B1[2 * m]), act_tile<GELU>(hi, B1[2 * m + 1]));
+                const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z[g], B1[2 * m], 0, 0, 0);
+                const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z[g], B1[2 * m + 1], 0, 0, 0);
+                H1[m][g] = cat8(act_tile<GELU>(lo), act_tile<GELU>(hi));
             }
         // ---- trunk layer 2: 64 -> 64
         half8_t H2[2][4];
@@ -506,13 +454,13 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
         for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                floatx4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+                floatx4 lo = B2[2 * m], hi = B2[2 * m + 1];
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
                     lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m][k], H1[k][g], lo, 0, 0, 0);
                     hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m + 1][k], H1[k][g], hi, 0, 0, 0);
                 }
-                H2[m][g] = cat8(act_tile<GELU>(lo, B2[2 * m]), act_tile<GELU>(hi, B2[2 * m + 1]));
+                H2[m][g] = cat8(act_tile<GELU>(lo), act_tile<GELU>(hi));
             }
         // ---- head block 64 -> 11 (rows 11..15 are zero) and Eq. 11
 #pragma unroll
@@ -521,12 +469,12 @@ __global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, 
                 sh_head_out(a, A3, B3, H2[0][g], H2[1][g], base + 16 * g + c, n, out_off, q);
                 continue;
             }
-            floatx4 acc = {0, 0, 0, 0};
+            floatx4 acc = B3[0];
 #pragma unroll
             for (int k = 0; k < 2; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[0][k], H2[k][g], acc, 0, 0, 0);
             float o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[e] + B3[0][e];
+            for (int e = 0; e < 4; ++e) o[e] = acc[e];
             // lane q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
             float part = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
             float other = __shfl_xor(part, 16);
@@ -583,8 +531,8 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
     IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
               a.pos + off * a.stride, n, xt);
     if (!z) return hipGetLastError();  // features kept by the forward: normalisation only
-    IA_LAUNCH("gather_f16_kernel", gather_f16_batched_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0, s, xt, n,
-              nchunk, a.h, (const uint32_t*)a.tables, z, zstride);
+    IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(kGatherPerBlock), 0, s,
+              xt, n, nchunk, a.h, (const uint32_t*)a.tables, z, zstride);
     return hipGetLastError();
 }
 
@@ -730,14 +678,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             if (a.h.F == 4) {
                 if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, zstride, s)) != hipSuccess) return e;
             } else {
-                // beside an MLP (every chunk but the first of an overlapped decode)
-                // the lean gather, alone the batched one
-                if (overlap && k >= 1)
-                    IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(256), 0,
-                              s, xt, n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
-                else
-                    IA_LAUNCH("gather_f16_kernel", gather_f16_batched_kernel, dim3((unsigned)(a.h.L * nchunk)),
-                              dim3(256), 0, s, xt, n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
+                IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)),
+                          dim3(kGatherPerBlock), 0, s, xt, n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
             }
             if (overlap) {
                 if ((e = hipEventRecord(ev->gather[k & 1], s)) != hipSuccess) return e;

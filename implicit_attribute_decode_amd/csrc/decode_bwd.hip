@@ -148,7 +148,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 
     // forward operands, as the decode holds them
     half8_t A1[4], A2[4][2], A3[2];
-    float B1[4][4], B2[4][4], B3[4];
+    // biases as the recomputed forward's initial MFMA accumulators, as the decode does
+    floatx4_t B1[4], B2[4], B3;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         A1[rb] = a_tile32(W1, 32, 64, rb, 0, q, c);
@@ -211,15 +212,14 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         half8_t H1[2], H2[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const floatx4_t z0 = {0, 0, 0, 0};
-            P1[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z, z0, 0, 0, 0);
-            P1[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z, z0, 0, 0, 0);
+            P1[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z, B1[2 * m], 0, 0, 0);
+            P1[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z, B1[2 * m + 1], 0, 0, 0);
             half8_t h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float d0, d1;
-                h[e] = (_Float16)act_fwd_grad<GELU>(P1[2 * m][e] + B1[2 * m][e], d0);
-                h[4 + e] = (_Float16)act_fwd_grad<GELU>(P1[2 * m + 1][e] + B1[2 * m + 1][e], d1);
+                h[e] = (_Float16)act_fwd_grad<GELU>(P1[2 * m][e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad<GELU>(P1[2 * m + 1][e], d1);
                 P1[2 * m][e] = d0;  // from here on: act'(a1)
                 P1[2 * m + 1][e] = d1;
             }
@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            floatx4_t lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            floatx4_t lo = B2[2 * m], hi = B2[2 * m + 1];
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m][k], H1[k], lo, 0, 0, 0);
@@ -237,19 +237,19 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float d0, d1;
-                h[e] = (_Float16)act_fwd_grad<GELU>(lo[e] + B2[2 * m][e], d0);
-                h[4 + e] = (_Float16)act_fwd_grad<GELU>(hi[e] + B2[2 * m + 1][e], d1);
+                h[e] = (_Float16)act_fwd_grad<GELU>(lo[e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad<GELU>(hi[e], d1);
                 P2[2 * m][e] = d0;  // act'(a2)
                 P2[2 * m + 1][e] = d1;
             }
             H2[m] = h;
         }
-        floatx4_t accO = {0, 0, 0, 0};
+        floatx4_t accO = B3;
 #pragma unroll
         for (int k = 0; k < 2; ++k) accO = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[k], H2[k], accO, 0, 0, 0);
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = accO[e] + B3[e];
+        for (int e = 0; e < 4; ++e) o[e] = accO[e];
 
         // ---------------- Eq. 11 backward.  Rows 4q+e of column c:
         // q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
