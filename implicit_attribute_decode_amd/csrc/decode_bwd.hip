@@ -17,7 +17,7 @@
 //       forward  the decoder on v_mfma_f32_16x16x32_f16 exactly as the decode
 //                runs it (same operands, same fp16 roundings), keeping the
 //                activation derivative at both hidden layers' pre-activations
-//                (GELU' shares the erf polynomial and exponential of GELU);
+//                (GELU' reuses GELU's normal tail Q);
 //       Eq. 11   dr from the upstream gradients: exp' = s below the clip,
 //                (I - q q^T) / |r| for the normalisation, sigma' = c (1 - c);
 //       Eq. 10   data gradients dx = W^T (dy act'(a)) on
