@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // rows 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows.
 
 constexpr int kGatherPerBlock = 256;  // Gaussians per gather block, one lane each
-constexpr int kMlpCusPerBlock = 1;    // MLP beside a gather: one block per this many CUs
+constexpr int kMlpBlocksPerCu = 1;    // MLP beside a gather: blocks per CU
 constexpr int kNormBlocksPerCu = 2;   // normalisation beside a gather: blocks per CU
 
 __global__ void __launch_bounds__(256) normalize_kernel(DecodeArgs a, const float* pos, int64_t n, float4* xt) {
@@ -343,13 +343,14 @@ __device__ __forceinline__ half4_t act_tile(floatx4 acc) {
 // Eq. 11: rows 0-2 scale, 3-6 rotation (normalised), 7-54 the 48 SH
 // coefficients (no activation), 55 opacity (sigmoid); rows 56-63 are zero.
 // Lane (q, c) holds rows 16 hb + 4 q + e of Gaussian gl.
-__device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (&A3)[4][2], const floatx4 (&B3)[4],
-                                            half8_t h0, half8_t h1, int64_t gl, int64_t n, int64_t out_off, int q) {
+__device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (*sA3)[64], const floatx4 (*sB3)[64],
+                                            half8_t h0, half8_t h1, int64_t gl, int64_t n, int64_t out_off, int lane,
+                                            int q) {
     float o[4][4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-        floatx4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[hb][0], h0, B3[hb], 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[hb][1], h1, acc, 0, 0, 0);
+        floatx4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sA3[2 * hb][lane], h0, sB3[hb][lane], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sA3[2 * hb + 1][lane], h1, acc, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[hb][e] = acc[e];
     }
@@ -383,120 +384,125 @@ __device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (
 // the next layer, and the features of levels {2q, 2q+1, 8+2q, 9+2q} the lane
 // loads are exactly its B slots of layer 1.  SH: the head block has 56 rows
 // (four 16-row tiles) with the 48 SH coefficients in place of the RGB rows.
+// Each lane's A operands (the weights) and initial accumulators (the biases)
+// are staged once per block in LDS, indexed by lane, and every 16-Gaussian
+// column group goes through all layers before the next, so a wave holds few
+// registers and more waves (of this kernel, or of the gather beside it) fit.
 template <bool SH, bool GELU>
-__global__ void __launch_bounds__(256, SH ? 1 : 2) mlp_f16_kernel(DecodeArgs a, const uint32_t* zbuf,
-                                                                  int64_t zstride, int64_t n, int64_t out_off) {
+__global__ void __launch_bounds__(256) mlp_f16_kernel(DecodeArgs a, const uint32_t* zbuf, int64_t zstride, int64_t n,
+                                                      int64_t out_off) {
     constexpr int NH = SH ? 4 : 1, kHeadRows = SH ? 56 : 11;
+    // A tiles: layer 1 [rb] (4), layer 2 [rb][m] (8), head [hb][m] (2 NH);
+    // bias tiles: layer 1 [rb], layer 2 [rb], head [hb]
+    constexpr int kA2 = 4, kA3 = 12, kTilesA = 12 + 2 * NH;
+    constexpr int kB2 = 4, kB3 = 8, kTilesB = 8 + NH;
+    __shared__ half8_t sA[kTilesA][64];
+    __shared__ floatx4 sB[kTilesB][64];
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, c = lane & 15;
+    {
+        const _Float16* W1 = (const _Float16*)a.W[0];  // [64][32]
+        const _Float16* W2 = (const _Float16*)a.W[1];  // [64][64]
+        const _Float16* Wh = (const _Float16*)a.W[2];  // [kHeadRows][64]
+        for (int j = threadIdx.x >> 6; j < kTilesA; j += 4) {
+            if (j < kA2)
+                sA[j][lane] = a_tile32(W1, 32, 64, j, 0, q, c);
+            else if (j < kA3)
+                sA[j][lane] = a_tile32(W2, 64, 64, (j - kA2) >> 1, (j - kA2) & 1, q, c);
+            else
+                sA[j][lane] = a_tile32(Wh, 64, kHeadRows, (j - kA3) >> 1, (j - kA3) & 1, q, c);
+        }
+        for (int j = threadIdx.x >> 6; j < kTilesB; j += 4) {
+            floatx4 b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (j < kB2)
+                    b[e] = a.b[0][16 * j + 4 * q + e];
+                else if (j < kB3)
+                    b[e] = a.b[1][16 * (j - kB2) + 4 * q + e];
+                else {
+                    const int row = 16 * (j - kB3) + 4 * q + e;
+                    b[e] = row < kHeadRows ? a.b[2][row] : 0.0f;
+                }
+            }
+            sB[j][lane] = b;
+        }
+    }
+    __syncthreads();
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
-    const _Float16* W1 = (const _Float16*)a.W[0];  // [64][32]
-    const _Float16* W2 = (const _Float16*)a.W[1];  // [64][64]
-    const _Float16* Wh = (const _Float16*)a.W[2];  // [kHeadRows][64]
 
-    half8_t A1[4], A2[4][2], A3[NH][2];
-    // biases as the MFMAs' initial accumulators: rows 16 rb + 4 q + e
-    floatx4 B1[4], B2[4], B3[NH];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        A1[rb] = a_tile32(W1, 32, 64, rb, 0, q, c);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) A2[rb][m] = a_tile32(W2, 64, 64, rb, m, q, c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            B1[rb][e] = a.b[0][16 * rb + 4 * q + e];
-            B2[rb][e] = a.b[1][16 * rb + 4 * q + e];
-        }
-    }
-#pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) A3[hb][m] = a_tile32(Wh, 64, kHeadRows, hb, m, q, c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * hb + 4 * q + e;
-            B3[hb][e] = row < kHeadRows ? a.b[2][row] : 0.0f;
-        }
-    }
-
-    // features of the next 64 Gaussians are loaded while this tile computes
-    auto load_z = [&](int64_t b0, half8_t (&Zo)[4]) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            int64_t gi = b0 + 16 * g + c;
-            if (gi >= n) gi = n - 1;
-            const int l = 2 * q;
-            Zo[g] = cat8(unpack2(zbuf[(size_t)l * zstride + gi], zbuf[(size_t)(l + 1) * zstride + gi]),
-                         unpack2(zbuf[(size_t)(l + 8) * zstride + gi], zbuf[(size_t)(l + 9) * zstride + gi]));
-        }
+    // the features of one 16-Gaussian group (rows of the columns' B operand)
+    auto load_z = [&](int64_t g0) {
+        int64_t gi = g0 + c;
+        if (gi >= n) gi = n - 1;
+        const int l = 2 * q;
+        return cat8(unpack2(zbuf[(size_t)l * zstride + gi], zbuf[(size_t)(l + 1) * zstride + gi]),
+                    unpack2(zbuf[(size_t)(l + 8) * zstride + gi], zbuf[(size_t)(l + 9) * zstride + gi]));
     };
-    half8_t Zn[4];
-    if (wave * 64 < n) load_z(wave * 64, Zn);
-    for (int64_t base = wave * 64; base < n; base += nwaves * 64) {
-        half8_t Z[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) Z[g] = Zn[g];
-        if (base + nwaves * 64 < n) load_z(base + nwaves * 64, Zn);
+    // groups of this wave: 64 consecutive Gaussians per turn (four groups), turns nwaves apart
+    auto group_at = [&](int64_t k) { return ((k >> 2) * nwaves + wave) * 64 + 16 * (k & 3); };
+    half8_t Zn = wave * 64 < n ? load_z(wave * 64) : half8_t{};
+    for (int64_t k = 0;; ++k) {
+        const int64_t g0 = group_at(k);
+        if (g0 >= n) break;
+        const half8_t Z = Zn;
+        const int64_t g1 = group_at(k + 1);
+        if (g1 < n) Zn = load_z(g1);  // the next group's features load while this one computes
         // ---- trunk layer 1: 32 -> 64
-        half8_t H1[2][4];
+        half8_t H1[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m], Z[g], B1[2 * m], 0, 0, 0);
-                const floatx4 hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * m + 1], Z[g], B1[2 * m + 1], 0, 0, 0);
-                H1[m][g] = cat8(act_tile<GELU>(lo), act_tile<GELU>(hi));
-            }
+        for (int m = 0; m < 2; ++m) {
+            const floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(sA[2 * m][lane], Z, sB[2 * m][lane], 0, 0, 0);
+            const floatx4 hi =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(sA[2 * m + 1][lane], Z, sB[2 * m + 1][lane], 0, 0, 0);
+            H1[m] = cat8(act_tile<GELU>(lo), act_tile<GELU>(hi));
+        }
         // ---- trunk layer 2: 64 -> 64
-        half8_t H2[2][4];
+        half8_t H2[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int m = 0; m < 2; ++m) {
+            floatx4 lo = sB[kB2 + 2 * m][lane], hi = sB[kB2 + 2 * m + 1][lane];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                floatx4 lo = B2[2 * m], hi = B2[2 * m + 1];
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m][k], H1[k][g], lo, 0, 0, 0);
-                    hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * m + 1][k], H1[k][g], hi, 0, 0, 0);
-                }
-                H2[m][g] = cat8(act_tile<GELU>(lo), act_tile<GELU>(hi));
+            for (int kk = 0; kk < 2; ++kk) {
+                lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(sA[kA2 + 2 * (2 * m) + kk][lane], H1[kk], lo, 0, 0, 0);
+                hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(sA[kA2 + 2 * (2 * m + 1) + kk][lane], H1[kk], hi, 0, 0, 0);
             }
-        // ---- head block 64 -> 11 (rows 11..15 are zero) and Eq. 11
+            H2[m] = cat8(act_tile<GELU>(lo), act_tile<GELU>(hi));
+        }
+        // ---- head block and Eq. 11
+        const int64_t gl = g0 + c;
+        if constexpr (SH) {
+            sh_head_out(a, sA + kA3, sB + kB3, H2[0], H2[1], gl, n, out_off, lane, q);
+            continue;
+        }
+        floatx4 acc = sB[kB3][lane];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            if constexpr (SH) {
-                sh_head_out(a, A3, B3, H2[0][g], H2[1][g], base + 16 * g + c, n, out_off, q);
-                continue;
-            }
-            floatx4 acc = B3[0];
+        for (int kk = 0; kk < 2; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(sA[kA3 + kk][lane], H2[kk], acc, 0, 0, 0);
+        float o[4];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[0][k], H2[k][g], acc, 0, 0, 0);
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[e];
-            // lane q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
-            float part = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
-            float other = __shfl_xor(part, 16);
-            float nrm = fmaxf(sqrtf(part + other), 1e-12f);
-            const int64_t gl = base + 16 * g + c;
-            if (gl < n) {
-                const int64_t gi = out_off + gl;
-                if (q == 0) {
-                    a.scales[gi * 3 + 0] = expf(fminf(o[0], 20.0f));
-                    a.scales[gi * 3 + 1] = expf(fminf(o[1], 20.0f));
-                    a.scales[gi * 3 + 2] = expf(fminf(o[2], 20.0f));
-                    a.quats[gi * 4 + 0] = o[3] / nrm;
-                } else if (q == 1) {
-                    a.quats[gi * 4 + 1] = o[0] / nrm;
-                    a.quats[gi * 4 + 2] = o[1] / nrm;
-                    a.quats[gi * 4 + 3] = o[2] / nrm;
-                    a.colors[gi * 3 + 0] = sigmoidf_(o[3]);
-                } else if (q == 2) {
-                    a.colors[gi * 3 + 1] = sigmoidf_(o[0]);
-                    a.colors[gi * 3 + 2] = sigmoidf_(o[1]);
-                    a.opacity[gi] = sigmoidf_(o[2]);
-                }
+        for (int e = 0; e < 4; ++e) o[e] = acc[e];
+        // lane q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
+        float part = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
+        float other = __shfl_xor(part, 16);
+        float nrm = fmaxf(sqrtf(part + other), 1e-12f);
+        if (gl < n) {
+            const int64_t gi = out_off + gl;
+            if (q == 0) {
+                a.scales[gi * 3 + 0] = expf(fminf(o[0], 20.0f));
+                a.scales[gi * 3 + 1] = expf(fminf(o[1], 20.0f));
+                a.scales[gi * 3 + 2] = expf(fminf(o[2], 20.0f));
+                a.quats[gi * 4 + 0] = o[3] / nrm;
+            } else if (q == 1) {
+                a.quats[gi * 4 + 1] = o[0] / nrm;
+                a.quats[gi * 4 + 2] = o[1] / nrm;
+                a.quats[gi * 4 + 3] = o[2] / nrm;
+                a.colors[gi * 3 + 0] = sigmoidf_(o[3]);
+            } else if (q == 2) {
+                a.colors[gi * 3 + 1] = sigmoidf_(o[0]);
+                a.colors[gi * 3 + 2] = sigmoidf_(o[1]);
+                a.opacity[gi] = sigmoidf_(o[2]);
             }
         }
     }
@@ -622,11 +628,11 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
         }
         auto mlp = [&](hipStream_t st, const uint32_t* zb, int64_t n, int64_t off, bool beside) -> hipError_t {
             if (a.branches) return launch_mlp_branch(a, zb, zstride, n, off, st);
-            // 256 threads = 4 waves x 64 Gaussians.  Beside a gather, one block
-            // per kMlpCusPerBlock CUs: the MLP still finishes within the gather
-            // and takes fewer wave slots from it; the last chunk's MLP, which
-            // runs alone, takes the whole chip.
-            const int grid = grid_for(256, n, beside ? device_cus() / kMlpCusPerBlock : 256 * 8);
+            // 256 threads = 4 waves.  Beside a gather, kMlpBlocksPerCu blocks
+            // per CU: the MLP finishes within the gather and leaves it most
+            // wave slots; the last chunk's MLP, which runs alone, takes the
+            // whole chip.
+            const int grid = grid_for(256, n, beside ? device_cus() * kMlpBlocksPerCu : 256 * 8);
             const bool gelu = a.act == IA_ACT_GELU;
             auto k = a.sh_head ? (gelu ? mlp_f16_kernel<true, true> : mlp_f16_kernel<true, false>)
                                : (gelu ? mlp_f16_kernel<false, true> : mlp_f16_kernel<false, false>);
