@@ -107,7 +107,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 MLP_FLOP_PER_GAUSSIAN = 2 * (32 * 64 + 64 * 64 + 64 * 11)  # 13,696: the 32-64-64-11 decoder
 
 
-def secondary(S, Decoder, HexPlane, Renderer, stream, log, only: str | None = None) -> dict:
+def secondary(S, Decoder, HexPlane, Renderer, stream, log, only: str | None = None,
+              stored_order: bool = False) -> dict:
     """The other workloads of the hot-path table, each timed with HIP events:
     one Single frame, the HexPlane deform + SH render, the Stress batch
     (only: just that one)."""
@@ -118,7 +119,7 @@ def secondary(S, Decoder, HexPlane, Renderer, stream, log, only: str | None = No
     if only in (None, "single"):
         out["single_frame"] = _single(S, Decoder, R, stream)
     if only in (None, "hexplane"):
-        out["hexplane"] = _hexplane(S, HexPlane, R, stream)
+        out["hexplane"] = _hexplane(S, HexPlane, R, stream, stored_order)
     if only in (None, "paper"):
         out["paper_scale"] = _paper(S, Decoder, R, stream)
     if only in (None, "stress"):
@@ -184,15 +185,29 @@ def _paper(S, Decoder, R, stream) -> dict:
             "mlp_flop_per_gaussian": PAPER_FLOP_PER_GAUSSIAN}
 
 
-def _hexplane(S, HexPlane, R, stream) -> dict:
-    """HexPlane: 300k canonical Gaussians, deform at t = 0.5, SH render at 1352x1014."""
+def _hexplane(S, HexPlane, R, stream, stored_order: bool = False) -> dict:
+    """HexPlane: 300k canonical Gaussians, deform at t = 0.5, SH render at 1352x1014.
+
+    The canonical set is fixed model data; by default it is stored along a
+    Morton curve of the positions once (ia_spatial_order, not part of a step),
+    so that Gaussians of one wave share plane texels.  The deform of the stored
+    order is timed beside it."""
     import torch
+
+    from implicit_attribute_decode_amd.pipeline import spatial_order
 
     hp = S.hexplane_params()
     cg = S.hexplane_canonical()
     canon = {k: torch.as_tensor(getattr(cg, k), device="cuda") for k in ("means", "scales", "quats", "sh", "opacity")}
     H = HexPlane(hp)
     d = H.deform(canon, 0.5)
+    ms_stored = timed(lambda: H.deform(canon, 0.5, out=d), 10, stream)
+    order = "stored"
+    if not stored_order:
+        perm, _ = spatial_order(canon["means"], np.array([0, cg.n], np.int64))
+        perm = perm.long()
+        canon = {k: v[perm].contiguous() for k, v in canon.items()}
+        order = "Morton (ia_spatial_order, once)"
     hcam = S.hexplane_camera()
     res = R.render(d, [0, cg.n], [hcam], 8 * cg.n, aux=True)
     hcap = R.count_entries(res) + 4096
@@ -206,7 +221,8 @@ def _hexplane(S, HexPlane, R, stream) -> dict:
     R.backward(d, [0, cg.n], [hcam], hcap, ra, gimg)
     ms_bwd = timed(lambda: R.backward(d, [0, cg.n], [hcam], hcap, ra, gimg), 5, stream)
     tflops = HEX_FLOP_PER_GAUSSIAN * cg.n / (ms_def / 1e3) / 1e12
-    return {"gaussians": cg.n, "deform_ms": round(ms_def, 4), "render_ms": round(ms_ren, 4),
+    return {"gaussians": cg.n, "order": order, "deform_ms": round(ms_def, 4),
+            "deform_stored_order_ms": round(ms_stored, 4), "render_ms": round(ms_ren, 4),
             "render_backward_sh_ms": round(ms_bwd, 4),
             "fps": round(1e3 / (ms_def + ms_ren), 1), "mlp_tflops": round(tflops, 1),
             "mlp_frac_of_fp16_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "deform_kernels_ms": hex_kernels}
@@ -539,7 +555,7 @@ def main():
     ap.add_argument("--only", choices=("single", "hexplane", "paper", "stress"),
                     help="run just that other workload and print its figures (for profiling)")
     ap.add_argument("--stored-order", action="store_true",
-                    help="keep each frame's Gaussians in their stored order (default: per-frame Morton order, "
+                    help="keep each frame's Gaussians (and the HexPlane canonical set) in their stored order (default: Morton order, "
                          "a one-time ia_spatial_order of the fixed position sets, timed on its own)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (a reference for HBM byte counters)")
@@ -557,7 +573,8 @@ def main():
 
     ia.load()  # fails loudly when the HIP library is missing
     if args.only:
-        print(json.dumps(secondary(S, Decoder, HexPlane, Renderer, torch.cuda.current_stream(), log, args.only)),
+        print(json.dumps(secondary(S, Decoder, HexPlane, Renderer, torch.cuda.current_stream(), log, args.only,
+                                   args.stored_order)),
               flush=True)
         return
     dev = "cuda"
@@ -649,7 +666,7 @@ def main():
         extra["per_frame_mode_fps"] = round(F / (timed(frame_pass, 1, stream) / 1e3), 2)
         log(f"per-frame mode {extra['per_frame_mode_fps']} fps")
         del Rf
-        extra["secondary"] = secondary(S, Decoder, HexPlane, Renderer, stream, log)
+        extra["secondary"] = secondary(S, Decoder, HexPlane, Renderer, stream, log, stored_order=args.stored_order)
 
     fps = F / (ms_step / 1e3)
     result = {
