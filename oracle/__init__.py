@@ -23,11 +23,16 @@ _lib = None
 
 
 def lib():
+    """The compiled oracle.  With ORACLE_SANITIZED=1 in the environment, the
+    AddressSanitizer + UndefinedBehaviorSanitizer build (the process must have
+    preloaded the sanitizer runtimes, see build.sanitizer_runtimes)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        _lib = C.CDLL(_build.LIB)
+        san = os.environ.get("ORACLE_SANITIZED") == "1"
+        path = _build.SAN_LIB if san else _build.LIB
+        if not os.path.exists(path):
+            _build.build(sanitize=san)
+        _lib = C.CDLL(path)
         _declare(_lib)
     return _lib
 
