@@ -8,7 +8,8 @@ ia_render call renders the 150 frames at 640x360 from a 27-camera ring
 level-major hash gather needs the L2 to itself, so decode and render are not
 overlapped across streams.  Prints one JSON line.
 
-Also reported: the per-frame mode (150 separate decode + render calls), the
+Also reported: the per-frame mode (150 separate decode + render calls, issued
+one by one and replayed from one HIP graph per frame), the
 roofline of the dominant kernel (the level-major hash gather) from HIP events
 recorded around its launches, and the CPU oracle's rate on a bounded sample
 of the same workload.
@@ -568,8 +569,8 @@ def main():
     import torch
 
     from implicit_attribute_decode_amd import ia, scenes as S
-    from implicit_attribute_decode_amd.pipeline import (Decoder, HexPlane, PipelinedDecodeRender, Renderer,
-                                                        spatial_order)
+    from implicit_attribute_decode_amd.pipeline import (Decoder, FrameGraphs, HexPlane, PipelinedDecodeRender,
+                                                        Renderer, spatial_order)
 
     ia.load()  # fails loudly when the HIP library is missing
     if args.only:
@@ -665,7 +666,14 @@ def main():
         frame_pass()
         extra["per_frame_mode_fps"] = round(F / (timed(frame_pass, 1, stream) / 1e3), 2)
         log(f"per-frame mode {extra['per_frame_mode_fps']} fps")
-        del Rf
+        # the same per-frame work replayed from one HIP graph per frame
+        FG = FrameGraphs(D, Rf, xyzt, fo, cams, capf, attrs, image)
+        ms_graph = timed(FG.replay, 3, stream)
+        extra["per_frame_graph_fps"] = round(F / (ms_graph / 1e3), 2)
+        one = timed(lambda: FG.replay([0]), 20, stream)
+        extra["per_frame_graph_one_frame_ms"] = round(one, 4)
+        log(f"per-frame graphs {extra['per_frame_graph_fps']} fps ({one:.4f} ms for one frame)")
+        del FG, Rf
         extra["secondary"] = secondary(S, Decoder, HexPlane, Renderer, stream, log, stored_order=args.stored_order)
 
     fps = F / (ms_step / 1e3)

@@ -483,3 +483,60 @@ class PipelinedDecodeRender:
             with torch.cuda.stream(self.side):
                 grp["R"].render(grp["g"], grp["fo"], grp["cams"], grp["cap"], out={"image": grp["image"]})
         main.wait_stream(self.side)
+
+
+class FrameGraphs:
+    """Per-frame decode + render replayed from HIP graphs (SPIN-4DGS page §4:
+    every frame is decoded from its own position set at its own time and
+    rendered on its own).
+
+    Frame f's graph holds its ia_decode_xyzt call (normalisation, hash gather,
+    decoder MLP) and its ia_render call (projection, depth sort, key emission,
+    tile sort, ranges, raster; the camera and frame offsets travel as kernel
+    arguments of upload kernels, clears are fill kernels: no memset or memcpy
+    node).  A replay submits the frame's ~45 kernels in one call instead of
+    one launch each.  The graphs keep the addresses they were captured with:
+    positions, attribute and image buffers, and the decoder's and renderer's
+    workspaces must stay allocated and in place while they are used, and the
+    decoder's parameters may be updated in place (set_params) but not
+    reallocated.
+
+    xyzt: [N, 4] device positions of all frames, frame f at
+    frame_offsets[f]:frame_offsets[f+1]; attrs: decoder output buffers [N, ...];
+    image: [F, 3, H, W]; max_entries: the tile-entry capacity of one frame."""
+
+    def __init__(self, decoder: "Decoder", renderer: "Renderer", xyzt: torch.Tensor, frame_offsets, cams,
+                 max_entries: int, attrs: dict, image: torch.Tensor):
+        self.D, self.R = decoder, renderer
+        self.xyzt, self.cams, self.cap = xyzt, list(cams), int(max_entries)
+        self.fo = np.asarray(frame_offsets, np.int64)
+        self.attrs, self.image = attrs, image
+        F = len(self.cams)
+        # one eager pass: sizes both workspaces (no allocation happens while
+        # capturing) and fills the one-time caches of the launch code
+        for f in range(F):
+            self.frame(f)
+        torch.cuda.synchronize()
+        self.graphs = []
+        pool = None
+        for f in range(F):
+            g = torch.cuda.CUDAGraph(keep_graph=True)
+            with torch.cuda.graph(g, pool=pool):
+                self.frame(f)
+            g.instantiate()
+            pool = g.pool()
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def frame(self, f: int):
+        """Frame f eagerly: one decode and one single-frame render."""
+        lo, hi = int(self.fo[f]), int(self.fo[f + 1])
+        x = self.xyzt[lo:hi]
+        a = self.D.decode_xyzt(x, out={k: v[lo:hi] for k, v in self.attrs.items()})
+        self.R.render(dict(means=x[:, :3], **a), [0, hi - lo], [self.cams[f]], self.cap,
+                      out={"image": self.image[f:f + 1]})
+
+    def replay(self, frames=None):
+        """Replay the graphs of `frames` (default: all) in order on the current stream."""
+        for f in (range(len(self.graphs)) if frames is None else frames):
+            self.graphs[f].replay()
