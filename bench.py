@@ -39,8 +39,11 @@ GATHER_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES
 DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
 # HBM-side bytes per gather launch of this workload (positions in per-frame Morton order), from two
 # rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, each scaled by what the counter
-# reads for a plain device copy of known size); None until counted for the kernel as it stands.
-GATHER_TRAFFIC_BYTES_PER_LAUNCH = None
+# reads for a plain device copy of known size).  Per Gaussian the gather's FETCH_SIZE counts 164.3 B and
+# its WRITE_SIZE 64.0 B; a 1 GiB copy counts 524,315 KiB of FETCH_SIZE for the 1 GiB it reads (x 2) and
+# 1,048,576 KiB of WRITE_SIZE for the 1 GiB it writes (x 1): 2 x 164.3 + 64.0 B per Gaussian, times the
+# 3.75M Gaussians of a mean launch.
+GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 164.3 + 64.0) * 3_750_000
 
 
 def log(*a):
@@ -506,7 +509,7 @@ def other_rooflines(ms: dict, N: int, E: int, c: dict) -> dict:
         "normalize": row(["normalize_kernel"], 32.0 * N / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
                          "16 B in + 16 B out per Gaussian"),
         "mlp": row(["mlp_f16_kernel"], MLP_FLOP_PER_GAUSSIAN * N / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma",
-                   "13,696 flop per Gaussian (beside the gather, one block per two compute units)"),
+                   "13,696 flop per Gaussian (beside the gather, one block per compute unit)"),
     }
     return {k: v for k, v in out.items() if v is not None}
 

@@ -41,8 +41,23 @@ def _check_f32(g, o):
         ok = rel_ok(g[k], o[k], 1e-5, 1e-7)
         assert ok.all(), (k, int((~ok).sum()), np.abs(g[k] - o[k]).max())
     qn = np.linalg.norm(o["quats"], axis=1, keepdims=True)
-    ok = np.abs(g["quats"] - o["quats"]) <= 1e-5 * qn + 1e-7
-    assert ok.all(), ("quats", int((~ok).sum()), np.abs(g["quats"] - o["quats"]).max())
+    dq = np.abs(g["quats"] - o["quats"])
+    ok = dq <= 1e-5 * qn + 1e-7
+    assert ok.all(), ("quats", int((~ok).sum()), dq.max())
+    # the same errors per component, by the component's share of the norm:
+    # components of at least a tenth of the norm also meet 1e-5 of their own
+    # magnitude; smaller ones are reported
+    share = np.abs(o["quats"]) / np.maximum(qn, 1e-30)
+    rel = dq / np.maximum(np.abs(o["quats"]), 1e-30)
+    figs = []
+    for lo, hi in ((0.1, 2.0), (0.01, 0.1), (0.0, 0.01)):
+        m = (share >= lo) & (share < hi)
+        if m.any():
+            figs.append(f"|q_i|/|q| in [{lo}, {hi}): {int(m.sum())} comps, max rel {rel[m].max():.2e}, "
+                        f"max err/|q| {(dq / qn)[m].max():.2e}")
+    say("[quats per component] " + "; ".join(figs))
+    big = share >= 0.1
+    assert (rel[big] <= 1e-5).all(), ("quats per component", float(rel[big].max()))
 
 
 def _check_f16(g, o, emu, tag):
