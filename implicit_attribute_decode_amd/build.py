@@ -24,6 +24,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 
+# Per-source flags.  The decoder MLP kernels (forward, branches, backward) need
+# far fewer than 256 registers per lane, so their MFMA accumulators stay in
+# ordinary VGPRs: with accumulation registers the compiler moves every result
+# out with one v_accvgpr_read before its activation (about a tenth of the
+# backward's VALU instructions).
+EXTRA_FLAGS = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+               for name in ("decode.hip", "decode_branch.hip", "decode_bwd.hip")}
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -40,7 +49,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = common + ["-c", src, "-o", obj]
+        cmd = common + EXTRA_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -339,6 +339,23 @@ __device__ __forceinline__ half4_t act_tile(floatx4 acc) {
     return h;
 }
 
+// Eq. 11 activations of the fp16 path from the hardware's one-ulp exp2, rcp
+// and rsq (the full-precision expf and the IEEE division take several times
+// the instructions, and every lane of a wave runs each lane's branch):
+//   scale     exp(min(x, 20)) = 2^(min(x, 20) log2 e)
+//   colour    1 / (1 + 2^(-x log2 e))      (0 and 1 at the extremes)
+//   rotation  r / max(|r|, 1e-12) = r min(rsq(|r|^2), 1e12)
+// The clamps are v_med3_f32 (fminf adds a NaN-quieting instruction).
+__device__ __forceinline__ float exp_clip20(float x) {
+    return __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(x, -3.402823466e+38f, 20.0f) * 1.44269504088896341f);
+}
+__device__ __forceinline__ float sigmoid_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+__device__ __forceinline__ float inv_norm(float sq) {
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_rsqf(sq), 0.0f, 1e12f);
+}
+
 // Head block of the SH colour decoder for one 16-Gaussian column group, and
 // Eq. 11: rows 0-2 scale, 3-6 rotation (normalised), 7-54 the 48 SH
 // coefficients (no activation), 55 opacity (sigmoid); rows 56-63 are zero.
@@ -357,7 +374,7 @@ __device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (
     // rotation rows 3 (q = 0) and 4-6 (q = 1) of the first tile
     const float part = q == 0 ? o[0][3] * o[0][3] : (q == 1 ? o[0][0] * o[0][0] + o[0][1] * o[0][1] + o[0][2] * o[0][2] : 0.0f);
     const float other = __shfl_xor(part, 16);
-    const float nrm = fmaxf(sqrtf(part + other), 1e-12f);
+    const float inv = inv_norm(part + other);
     if (gl >= n) return;
     const int64_t gi = out_off + gl;
     float* sh = a.sh + gi * 48;
@@ -368,13 +385,13 @@ __device__ __forceinline__ void sh_head_out(const DecodeArgs& a, const half8_t (
             const int row = 16 * hb + 4 * q + e;
             const float v = o[hb][e];
             if (row < 3)
-                a.scales[gi * 3 + row] = expf(fminf(v, 20.0f));
+                a.scales[gi * 3 + row] = exp_clip20(v);
             else if (row < 7)
-                a.quats[gi * 4 + (row - 3)] = v / nrm;
+                a.quats[gi * 4 + (row - 3)] = v * inv;
             else if (row < 55)
                 sh[row - 7] = v;
             else if (row == 55)
-                a.opacity[gi] = sigmoidf_(v);
+                a.opacity[gi] = sigmoid_fast(v);
         }
 }
 
@@ -486,23 +503,23 @@ __global__ void __launch_bounds__(256) mlp_f16_kernel(DecodeArgs a, const uint32
         // lane q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
         float part = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
         float other = __shfl_xor(part, 16);
-        float nrm = fmaxf(sqrtf(part + other), 1e-12f);
+        const float inv = inv_norm(part + other);
         if (gl < n) {
             const int64_t gi = out_off + gl;
             if (q == 0) {
-                a.scales[gi * 3 + 0] = expf(fminf(o[0], 20.0f));
-                a.scales[gi * 3 + 1] = expf(fminf(o[1], 20.0f));
-                a.scales[gi * 3 + 2] = expf(fminf(o[2], 20.0f));
-                a.quats[gi * 4 + 0] = o[3] / nrm;
+                a.scales[gi * 3 + 0] = exp_clip20(o[0]);
+                a.scales[gi * 3 + 1] = exp_clip20(o[1]);
+                a.scales[gi * 3 + 2] = exp_clip20(o[2]);
+                a.quats[gi * 4 + 0] = o[3] * inv;
             } else if (q == 1) {
-                a.quats[gi * 4 + 1] = o[0] / nrm;
-                a.quats[gi * 4 + 2] = o[1] / nrm;
-                a.quats[gi * 4 + 3] = o[2] / nrm;
-                a.colors[gi * 3 + 0] = sigmoidf_(o[3]);
+                a.quats[gi * 4 + 1] = o[0] * inv;
+                a.quats[gi * 4 + 2] = o[1] * inv;
+                a.quats[gi * 4 + 3] = o[2] * inv;
+                a.colors[gi * 3 + 0] = sigmoid_fast(o[3]);
             } else if (q == 2) {
-                a.colors[gi * 3 + 1] = sigmoidf_(o[0]);
-                a.colors[gi * 3 + 2] = sigmoidf_(o[1]);
-                a.opacity[gi] = sigmoidf_(o[2]);
+                a.colors[gi * 3 + 1] = sigmoid_fast(o[0]);
+                a.colors[gi * 3 + 2] = sigmoid_fast(o[1]);
+                a.opacity[gi] = sigmoid_fast(o[2]);
             }
         }
     }

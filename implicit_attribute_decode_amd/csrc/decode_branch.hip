@@ -192,14 +192,25 @@ __device__ __forceinline__ half4_t unpack4(uint2 v) { return unpack2(v.x, v.y); 
 
 // Bias + activation of one 16-row D tile, rounded to fp16 (rows 16 rb + 4 q + e).
 template <bool GELU>
-__device__ __forceinline__ half4_t act4(floatx4 acc, const float* bias) {
+__device__ __forceinline__ half4_t act4(floatx4 acc) {
     half4_t h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[e] = (_Float16)hidden_act<GELU>(acc[e] + bias[e]);
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)hidden_act<GELU>(acc[e]);
     return h;
 }
 
-__device__ __forceinline__ float sigmoid_b(float x) { return 1.0f / (1.0f + expf(-x)); }
+// Four biases of a lane (rows 4 q .. 4 q + 3 of a tile) as an initial MFMA
+// accumulator: the products then start from the bias, one add fewer per value.
+__device__ __forceinline__ floatx4 bias4(const float* b) { return *reinterpret_cast<const floatx4*>(b); }
+
+// Eq. 11 activations from the hardware's one-ulp exp2, rcp and rsq (see the
+// shared-trunk decoder); the clamps are v_med3_f32.
+__device__ __forceinline__ float exp_clip20_b(float x) {
+    return __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(x, -3.402823466e+38f, 20.0f) * 1.44269504088896341f);
+}
+__device__ __forceinline__ float sigmoid_b(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
 
 // One hidden layer (64 -> 64) of a branch for kBrG column groups: the output
 // k-block mo collects row blocks 2 mo and 2 mo + 1.
@@ -209,8 +220,12 @@ __device__ __forceinline__ void hidden_layer(const half8_t* W, const float* bias
 #pragma unroll
     for (int mo = 0; mo < 2; ++mo) {
         floatx4 lo[kBrG], hi[kBrG];
+        const floatx4 b_lo = bias4(bias + 16 * (2 * mo) + 4 * q), b_hi = bias4(bias + 16 * (2 * mo + 1) + 4 * q);
 #pragma unroll
-        for (int g = 0; g < kBrG; ++g) lo[g] = hi[g] = floatx4{0, 0, 0, 0};
+        for (int g = 0; g < kBrG; ++g) {
+            lo[g] = b_lo;
+            hi[g] = b_hi;
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const half8_t a_lo = W[(2 * (2 * mo) + m) * kTile + lane];
@@ -223,7 +238,7 @@ __device__ __forceinline__ void hidden_layer(const half8_t* W, const float* bias
         }
 #pragma unroll
         for (int g = 0; g < kBrG; ++g)
-            Y[mo][g] = cat8(act4<GELU>(lo[g], bias + 16 * (2 * mo) + 4 * q), act4<GELU>(hi[g], bias + 16 * (2 * mo + 1) + 4 * q));
+            Y[mo][g] = cat8(act4<GELU>(lo[g]), act4<GELU>(hi[g]));
     }
 }
 
@@ -247,12 +262,12 @@ __device__ __forceinline__ void run_branch(const DecodeArgs& a, const half8_t* s
         const half8_t a0 = W[(16 + 2 * rb) * kTile + lane], a1 = W[(16 + 2 * rb + 1) * kTile + lane];
 #pragma unroll
         for (int g = 0; g < kBrG; ++g) {
-            floatx4 acc = {0, 0, 0, 0};
+            floatx4 acc = bias4(bias + 128 + 16 * rb + 4 * q);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, H2[0][g], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, H2[1][g], acc, 0, 0, 0);
             float o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[e] + bias[128 + 16 * rb + 4 * q + e];
+            for (int e = 0; e < 4; ++e) o[e] = acc[e];
             const int64_t gl = base + 16 * g + c;
             if (gl >= n) continue;
             const int64_t gi = out_off + gl;
@@ -260,12 +275,13 @@ __device__ __forceinline__ void run_branch(const DecodeArgs& a, const half8_t* s
             if (BR == 0) {
                 if (q == 0)
 #pragma unroll
-                    for (int e = 0; e < 3; ++e) a.scales[gi * 3 + e] = expf(fminf(o[e], 20.0f));
+                    for (int e = 0; e < 3; ++e) a.scales[gi * 3 + e] = exp_clip20_b(o[e]);
             } else if (BR == 1) {
                 if (q == 0) {
-                    const float nrm = fmaxf(sqrtf(o[0] * o[0] + (o[1] * o[1] + o[2] * o[2] + o[3] * o[3])), 1e-12f);
+                    const float sq = o[0] * o[0] + (o[1] * o[1] + o[2] * o[2] + o[3] * o[3]);
+                    const float inv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_rsqf(sq), 0.0f, 1e12f);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a.quats[gi * 4 + e] = o[e] / nrm;
+                    for (int e = 0; e < 4; ++e) a.quats[gi * 4 + e] = o[e] * inv;
                 }
             } else if (BR == 2) {
                 if (SH) {
@@ -288,7 +304,7 @@ __global__ void __launch_bounds__(256, 2) mlp_branch_kernel(DecodeArgs a, const 
                                                             int64_t out_off) {
     constexpr int kT = total_tiles(SH), kB = total_bias(SH);
     __shared__ half8_t s_w[kT * kTile];
-    __shared__ float s_b[kB];
+    __shared__ __attribute__((aligned(16))) float s_b[kB];
     const half8_t* Wt = (const half8_t*)a.Wt;
     for (int i = threadIdx.x; i < kT * kTile; i += 256) s_w[i] = Wt[i];
     for (int i = threadIdx.x; i < kB; i += 256) s_b[i] = a.bpack[i];

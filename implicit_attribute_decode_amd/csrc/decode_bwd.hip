@@ -91,7 +91,7 @@ __device__ __forceinline__ float act_fwd_grad(float x, float& d) {
         float e;
         const float q = gelu_tail(x, e);
         d = fmaf(x * e, 0.39894228040143268f, x >= 0.0f ? 1.0f - q : q);
-        return fmaf(-fabsf(x), q, fmaxf(x, 0.0f));
+        return fmaf(-fabsf(x), q, relu_med3(x));
     }
 }
 

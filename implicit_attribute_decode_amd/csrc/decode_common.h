@@ -61,31 +61,34 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf
 // with Q = 1 - Phi(|x|) the upper tail of the standard normal distribution.
 // Writing the negative half as -|x| Q (instead of x (1 - erf)) avoids the
 // cancellation 1 - erf(u) for large |x|.  Q(w) is evaluated as 2^P(min(w, 6))
-// with P a degree-9 polynomial fitted to log2 Q on [0, 6] (gen_gelu_tail.py,
+// with P a degree-7 polynomial fitted to log2 Q on [0, 6] (gen_gelu_tail.py,
 // least squares refined towards the minimax error): relative error of Q at
-// most 2.1e-6 for w < 4.3 (where |x| Q is above fp16's smallest normal) and
-// 3.8e-6 on [0, 6], in fp32 with fused multiply-adds; beyond 6, |x| Q(6) <
-// 1e-9 |x| is far below what the fp16 result can hold.  One exponential per
-// value and no reciprocal.
+// most 3.9e-6 for w < 4.3 (where |x| Q is above fp16's smallest normal) and
+// 4.6e-6 on [0, 6], in fp32 with fused multiply-adds, under a hundredth of an
+// fp16 step of the result; beyond 6, |x| Q(6) < 1e-9 |x| is far below what
+// the fp16 result can hold.  One exponential per value and no reciprocal.
+// The clamps are v_med3_f32 (for finite inputs: min(|x|, 6) and max(x, 0))
+// rather than fminf / fmaxf, which add a NaN-quieting instruction each.
 __device__ __forceinline__ float normal_tail(float w) {
 #pragma clang fp contract(fast)
-    const float v = fminf(w, 6.0f);
-    float p = 5.266901226e-08f;
-    p = fmaf(p, v, -1.428938162e-06f);
-    p = fmaf(p, v, 1.427341613e-05f);
-    p = fmaf(p, v, -3.597961040e-05f);
-    p = fmaf(p, v, -5.875685019e-04f);
-    p = fmaf(p, v, 7.803893648e-03f);
-    p = fmaf(p, v, -5.315436423e-02f);
-    p = fmaf(p, v, -4.589217603e-01f);
-    p = fmaf(p, v, -1.151152372e+00f);
-    p = fmaf(p, v, -9.999987483e-01f);
+    const float v = __builtin_amdgcn_fmed3f(w, 0.0f, 6.0f);
+    float p = -1.845025508e-06f;
+    p = fmaf(p, v, 6.177832256e-05f);
+    p = fmaf(p, v, -9.317235090e-04f);
+    p = fmaf(p, v, 8.511628956e-03f);
+    p = fmaf(p, v, -5.396552756e-02f);
+    p = fmaf(p, v, -4.584611952e-01f);
+    p = fmaf(p, v, -1.151251435e+00f);
+    p = fmaf(p, v, -9.999952912e-01f);
     return __builtin_amdgcn_exp2f(p);
 }
 
+// max(x, 0) for finite x in one instruction.
+__device__ __forceinline__ float relu_med3(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e+38f); }
+
 __device__ __forceinline__ float gelu_fp16path(float x) {
     const float q = normal_tail(fabsf(x));
-    return fmaf(-fabsf(x), q, fmaxf(x, 0.0f));
+    return fmaf(-fabsf(x), q, relu_med3(x));
 }
 
 // Q = 1 - Phi(|x|) as gelu_fp16path computes it, and e = exp(-x^2 / 2) (for

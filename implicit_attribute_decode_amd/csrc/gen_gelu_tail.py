@@ -17,7 +17,7 @@ import numpy as np
 from scipy.special import log_ndtr
 
 W = 6.0
-DEG = 9
+DEG = 7
 
 
 def log2_tail(w):

@@ -1,5 +1,5 @@
 """The fp16 decoder's GELU tail (decode_common.h): Q(w) = 1 - Phi(w) as
-2^P(min(w, 6)), P the degree-9 polynomial whose coefficients the header
+2^P(min(w, 6)), P the degree-7 polynomial whose coefficients the header
 holds.  Evaluated here as the kernels evaluate it (Horner in fp32 with fused
 multiply-adds, then exp2) and compared with scipy's normal tail: the relative
 error bounds the header states, and GELU = max(x, 0) - |x| Q against the erf
@@ -17,7 +17,7 @@ def _coefficients():
     text = open(os.path.join(ROOT, "implicit_attribute_decode_amd", "csrc", "decode_common.h")).read()
     body = text[text.index("normal_tail(float w)"):text.index("__builtin_amdgcn_exp2f(p);")]
     vals = [float(v) for v in re.findall(r"([-+]?\d\.\d+e[-+]\d+)f", body)]
-    assert len(vals) == 10
+    assert len(vals) == 8
     return np.float32(vals[::-1])  # lowest order first
 
 
@@ -34,8 +34,8 @@ def test_tail_relative_error_bounds():
     w = np.linspace(0.0, 6.0, 300001).astype(np.float32)
     exact = np.exp(log_ndtr(-w.astype(np.float64)))
     rel = np.abs(_q(w) / exact - 1.0)
-    assert rel[w < 4.3].max() <= 2.5e-6, rel[w < 4.3].max()
-    assert rel.max() <= 4.5e-6, rel.max()
+    assert rel[w < 4.3].max() <= 3.9e-6, rel[w < 4.3].max()
+    assert rel.max() <= 4.6e-6, rel.max()
 
 
 def test_gelu_against_the_erf_form():
