@@ -214,6 +214,8 @@ def test_device_memory_is_allocated_only_when_parameters_are_set():
     defn = re.compile(r"^(?!\s)(?!#)(?!//)[\w:<>\*&, ]*?\b(\w+)\s*\(")
     seen = set()
     for path in sorted(glob.glob(os.path.join(ROOT, "implicit_attribute_decode_amd", "csrc", "*"))):
+        if not path.endswith((".hip", ".h", ".cpp", ".c")):
+            continue
         fn = None
         for line in open(path).read().splitlines():
             m = defn.match(line)
