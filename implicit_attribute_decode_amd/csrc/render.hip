@@ -1051,11 +1051,15 @@ struct RasterArgs {
 // Gaussian that is skipped (power outside [-4.5, 0] i.e. beyond 3 sigma,
 // alpha below 1/255, or the pixel already saturated) contributes alpha = 0,
 // which leaves C and T exactly unchanged, so the step has no branches.
+// A pixel's compositing state.  It is saturated ("done") exactly when
+// T < 1e-4: T only decreases, the step that takes T below the threshold is
+// the last one composited, and a pixel outside the image starts at T = 0.
 struct Pix {
     float T, r, g, b;
     uint32_t last;
-    bool done;
 };
+
+__device__ __forceinline__ bool pix_done(const Pix& p) { return p.T < 1e-4f; }
 
 // LAST: track the index of the last composited Gaussian (the n_contrib output).
 template <bool LAST>
@@ -1063,7 +1067,7 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
                                                uint32_t pos) {
 #pragma clang fp contract(fast)
     const float a0 = splat_alpha(opacity, power);
-    const bool take = !p.done && splat_takes(power, a0);
+    const bool take = !pix_done(p) && splat_takes(power, a0);
     const float alpha = take ? a0 : 0.0f;
     const float wgt = alpha * p.T;
     p.r += cr * wgt;
@@ -1071,7 +1075,6 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
     p.b += cb * wgt;
     p.T = p.T * (1.0f - alpha);
     if (LAST) p.last = take ? pos : p.last;
-    p.done = p.done || p.T < 1e-4f;
 }
 
 // One block per 16x16 tile.  PX = 2: 128 threads, thread (col, row) shades
@@ -1111,12 +1114,12 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
 #pragma unroll
     for (int k = 0; k < PX; ++k) {
         in[k] = px < a.W && py0 + k < a.H;
-        p[k] = Pix{1.0f, 0.0f, 0.0f, 0.0f, 0u, !in[k]};
+        p[k] = Pix{in[k] ? 1.0f : 0.0f, 0.0f, 0.0f, 0.0f, 0u};
     }
     auto all_done = [&]() {
         bool d = true;
 #pragma unroll
-        for (int k = 0; k < PX; ++k) d = d && p[k].done;
+        for (int k = 0; k < PX; ++k) d = d && pix_done(p[k]);
         return d;
     };
     for (uint32_t start = rg.x; start < rg.y; start += kRasterBatch) {
