@@ -499,8 +499,10 @@ def other_rooflines(ms: dict, N: int, E: int, c: dict) -> dict:
         "raster": row(["raster_kernel"], RASTER_FLOP_PER_EVAL * c["evaluations"] / 1e12, FP32_VALU_PEAK_TFLOPS,
                       "TFLOP/s", "valu", f"{RASTER_FLOP_PER_EVAL} flop per pixel x Gaussian evaluation "
                       f"({c['evaluations']} evaluations, measured)"),
-        "preprocess": row(["preprocess_kernel"], 108.0 * N / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
-                          "56 B in + 52 B out per Gaussian"),
+        "preprocess": row(["preprocess_kernel"], (16.0 * N + 92.0 * nvis) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                          "12 B mean in + 4 B tile count out per Gaussian, + 44 B attributes in and 48 B "
+                          "projection out per visible Gaussian (culled Gaussians in front of the camera also "
+                          "read 28 B of scale and rotation, not counted)"),
         "radix_sort": row(sort, 24.0 * (4 * nvis + 2 * E) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
                           f"24 B per item and pass: 4 passes over {nvis} visible Gaussians, 2 over {E} entries"),
         "key_emit": row(emit, (8.0 * N + 12.0 * E) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",

@@ -286,12 +286,16 @@ __global__ void __launch_bounds__(kBlock) preprocess_kernel(PreArgs a) {
             }
             ntouch = (uint32_t)((x1 - x0 + 1) * (y1 - y0 + 1));
         }
-        a.pa[i] = make_float4(u, v, A, B);
-        a.pb[i] = make_float4(C, o, r, g);
-        a.pc[i] = b;
-        a.depth[i] = vis ? pz : 0.0f;
-        a.rect[i] = vis ? make_ushort4((unsigned short)x0, (unsigned short)y0, (unsigned short)x1, (unsigned short)y1)
-                        : make_ushort4(0, 0, 0, 0);
+        // the projection of a culled Gaussian is never read (every reader
+        // starts from tiles > 0 or from a tile list): only its zero tile
+        // count is written, which saves most of the stores of a frame
+        if (vis) {
+            a.pa[i] = make_float4(u, v, A, B);
+            a.pb[i] = make_float4(C, o, r, g);
+            a.pc[i] = b;
+            a.depth[i] = pz;
+            a.rect[i] = make_ushort4((unsigned short)x0, (unsigned short)y0, (unsigned short)x1, (unsigned short)y1);
+        }
         a.tiles[i] = ntouch;
     }
     uint32_t total, total_t;

@@ -372,6 +372,8 @@ typedef struct {
                                      only with want_keys                        */
     const uint32_t* sorted_vals;  /* [min(E,max_entries)] Gaussian index          */
     const uint32_t* tile_ranges;  /* [F*tiles][2] [start,end), empty = [0,0)      */
+    /* projections: defined where tiles_touched > 0 (a culled Gaussian's
+       entries are not written)                                               */
     const float* proj_a;          /* [N][4] u, v, conic A, conic B                */
     const float* proj_b;          /* [N][4] conic C, opacity, red, green          */
     const float* proj_c;          /* [N] blue                                     */

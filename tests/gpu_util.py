@@ -56,7 +56,9 @@ def gpu_render(g: dict, fo, cams, cap: int, renderer: Renderer | None = None, bi
 
 
 def check_preprocess_bitexact(gp: dict, op: dict):
-    """GPU projection == oracle projection, bit for bit, on every Gaussian."""
+    """GPU projection == oracle projection, bit for bit: the tile counts of
+    every Gaussian, the other fields of every visible one (a culled
+    Gaussian's projection is not written)."""
     np.testing.assert_array_equal(gp["tiles"], op["tiles"])
     vis = op["tiles"] > 0
     for k in ("mean2d", "conic", "depth"):
