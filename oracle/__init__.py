@@ -257,7 +257,8 @@ def decode_grad(dec, pos: np.ndarray, t=None, mode: int = 0, grads: dict | None 
     Parameters default to the stored values of dec converted exactly to
     float64; params may override tables / weights / biases (float64), e.g.
     for finite differences.  grads: upstream dL/d(scales [N,3], quats [N,4],
-    colors [N,3], opacity [N]).  mode bit 0: fp16 rounding of the MLP input
+    colors [N,3] -- or sh [N,48] for a 56-output SH colour head, which is then
+    returned as sh [N,48] --, opacity [N]).  mode bit 0: fp16 rounding of the MLP input
     and hidden activations; bit 1: fp32 normalisation and cell decision.
     Returns raw, scales, quats, colors, opacity, flags, signature and, with
     grads, g_tables [L,T,F], g_weights, g_biases (lists) and g_pos [N,3]."""
@@ -277,13 +278,17 @@ def decode_grad(dec, pos: np.ndarray, t=None, mode: int = 0, grads: dict | None 
     bp = (C.c_void_p * len(bs))(*[b.ctypes.data for b in bs])
     hs = _hash(h)
     mm = _mlp(m.dims, m.act, m.f16)
-    out = dict(raw=np.zeros((n, 11)), scales=np.zeros((n, 3)), quats=np.zeros((n, 4)), colors=np.zeros((n, 3)),
-               opacity=np.zeros(n), flags=np.zeros(n, np.uint8))
+    head = int(m.dims[-1])
+    cname, ncol = ("sh", 48) if head == 56 else ("colors", 3)
+    out = dict(raw=np.zeros((n, head)), scales=np.zeros((n, 3)), quats=np.zeros((n, 4)), opacity=np.zeros(n),
+               flags=np.zeros(n, np.uint8))
+    out[cname] = np.zeros((n, ncol))
     sig = C.c_uint64(0)
     gp = [None] * 4
     gw, gb = [], []
     if grads is not None:
-        gp = [_c(grads[k], np.float64) for k in ("scales", "quats", "colors", "opacity")]
+        gp = [_c(np.asarray(grads[k], np.float64).reshape(n, -1) if k == cname else grads[k], np.float64)
+              for k in ("scales", "quats", cname, "opacity")]
         out["g_tables"] = np.zeros(tables.shape)
         gw = [np.zeros(w.shape) for w in ws]
         gb = [np.zeros(b.shape) for b in bs]
@@ -292,7 +297,7 @@ def decode_grad(dec, pos: np.ndarray, t=None, mode: int = 0, grads: dict | None 
     gbp = (C.c_void_p * len(bs))(*[b.ctypes.data for b in gb]) if gb else None
     lib().orc_decode_grad(C.byref(hs), _p(tables), C.byref(mm), wp, bp, _p(xyz), _p(tp), n, int(mode),
                           *[None if g is None else _p(g) for g in gp], _p(out["raw"]), _p(out["scales"]),
-                          _p(out["quats"]), _p(out["colors"]), _p(out["opacity"]),
+                          _p(out["quats"]), _p(out[cname]), _p(out["opacity"]),
                           None if grads is None else _p(out["g_tables"]), gwp, gbp,
                           None if grads is None else _p(out["g_pos"]), _p(out["flags"]), C.byref(sig))
     out["flags"] = out["flags"].astype(bool)

@@ -1229,7 +1229,10 @@ static double gelu_grad(double x) {
  *   they are fp64.  The Jacobian of the normalisation is fp64 either way.
  *
  * Outputs of the forward: raw [N][11] (head outputs) and the activations of
- * Eq. 11 (scales, quats, colors, opacity); all nullable.  With the upstream
+ * Eq. 11 (scales, quats, colors, opacity); all nullable.  A head of 56
+ * outputs is the SH colour decoder ([SPIN] §3.3: s | r | 48 SH coefficients
+ * | o): then raw is [N][56], `colors` receives the 48 coefficients per
+ * Gaussian (no activation, so dr = dsh) and gc is [N][48].  With the upstream
  * gradients gs [N][3], gq [N][4], gc [N][3], go [N] given (else forward
  * only), the backward accumulates, for L = sum gs.s + gq.q + gc.c + go.o:
  *   g_tables [L][T][F]   += w_c dL/dz           (scatter-add over the corners)
@@ -1265,6 +1268,9 @@ EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_m
     const long T = 1L << h->log2T;
     const int L = h->L, F = h->F, LF = L * F, nl = m->n_layers;
     const int backward = gs && gq && gc && go;
+    /* head of 56 outputs: the SH colour decoder (s | r | 48 SH | o), whose
+       colour slots are the coefficients themselves; else 11 (s | r | c | o) */
+    const int sh = m->dims[nl] == 56, head = sh ? 56 : 11, ncol = sh ? 48 : 3;
     uint64_t sig = 0;
     for (long i = 0; i < N; ++i) {
         uint64_t hs = mix64(0x9e3779b97f4a7c15ull, (uint64_t)i);
@@ -1374,15 +1380,15 @@ EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_m
         double qd = qn < 1e-12 ? 1e-12 : qn;
         for (int k = 0; k < 4; ++k) q4[k] = r[3 + k] / qd;
         for (int k = 0; k < 3; ++k) c3[k] = sigmoid(r[7 + k]);
-        o1 = sigmoid(r[10]);
+        o1 = sigmoid(r[head - 1]);
         if (raw_out)
-            for (int k = 0; k < 11; ++k) raw_out[i * 11 + k] = r[k];
+            for (int k = 0; k < head; ++k) raw_out[i * head + k] = r[k];
         if (scales)
             for (int k = 0; k < 3; ++k) scales[i * 3 + k] = s3[k];
         if (quats)
             for (int k = 0; k < 4; ++k) quats[i * 4 + k] = q4[k];
-        if (colors)
-            for (int k = 0; k < 3; ++k) colors[i * 3 + k] = c3[k];
+        if (colors)  /* the RGB colour, or the SH coefficients (no activation) */
+            for (int k = 0; k < ncol; ++k) colors[i * ncol + k] = sh ? r[7 + k] : c3[k];
         if (opacity) opacity[i] = o1;
         if (flags) flags[i] = (uint8_t)fl;
         sig += hs;
@@ -1394,8 +1400,8 @@ EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_m
         for (int k = 0; k < 4; ++k) dot += gq[i * 4 + k] * q4[k];
         for (int k = 0; k < 4; ++k)
             gy[3 + k] = qn < 1e-12 ? gq[i * 4 + k] / 1e-12 : (gq[i * 4 + k] - dot * q4[k]) / qn;
-        for (int k = 0; k < 3; ++k) gy[7 + k] = gc[i * 3 + k] * c3[k] * (1.0 - c3[k]);
-        gy[10] = go[i] * o1 * (1.0 - o1);
+        for (int k = 0; k < ncol; ++k) gy[7 + k] = sh ? gc[i * ncol + k] : gc[i * 3 + k] * c3[k] * (1.0 - c3[k]);
+        gy[head - 1] = go[i] * o1 * (1.0 - o1);
         /* backward of Eq. 10, last layer first */
         for (int l = nl - 1; l >= 0; --l) {
             int di = m->dims[l], dout = m->dims[l + 1];

@@ -15,22 +15,28 @@ import oracle as O
 from implicit_attribute_decode_amd import scenes as S
 
 
-def _batch(seed, n=64):
+def _colour_key(dec):
+    """The colour output of a decoder: RGB, or the 48 SH coefficients of a
+    56-output head."""
+    return ("sh", 48) if int(dec.mlp.dims[-1]) == 56 else ("colors", 3)
+
+
+def _batch(seed, n=64, colour=("colors", 3)):
     rng = np.random.default_rng(seed)
     pos = np.concatenate([S.shell_points(rng, n // 2, 3.0), rng.uniform(-0.9, 0.9, (n - n // 2, 3))])
     t = rng.uniform(0.0, 1.0, n)
     xyzt = np.concatenate([pos, t[:, None]], 1).astype(np.float64)
-    grads = dict(scales=rng.normal(size=(n, 3)), quats=rng.normal(size=(n, 4)), colors=rng.normal(size=(n, 3)),
-                 opacity=rng.normal(size=n))
+    grads = dict(scales=rng.normal(size=(n, 3)), quats=rng.normal(size=(n, 4)), opacity=rng.normal(size=n))
+    grads[colour[0]] = rng.normal(size=(n, colour[1]))
     return xyzt, grads
 
 
 def _loss(out, g):
-    return sum(float(np.sum(out[k] * g[k])) for k in ("scales", "quats", "colors", "opacity"))
+    return sum(float(np.sum(out[k] * g[k])) for k in g)
 
 
 def _check_fd(dec, seed, n_weights=40, n_tables=80):
-    xyzt, g = _batch(seed)
+    xyzt, g = _batch(seed, colour=_colour_key(dec))
     params = dict(tables=np.asarray(dec.tables).astype(np.float64),
                   weights=[np.asarray(w).astype(np.float64) for w in dec.weights],
                   biases=[np.asarray(b).astype(np.float64) for b in dec.biases])
@@ -87,6 +93,27 @@ def test_single_decoder_gradients_match_central_differences():
     dec = S.single_decoder()
     checked, skipped = _check_fd(dec, 51)
     assert checked >= 500 and skipped <= 0.1 * checked
+
+
+def test_sh_head_decoder_gradients_match_central_differences():
+    """The Single decoder with the SH colour head (56 outputs, [SPIN] §3.3:
+    the colour decoder regresses the 48 coefficients, no activation)."""
+    dec = S.single_decoder_sh()
+    checked, skipped = _check_fd(dec, 54)
+    assert checked >= 500 and skipped <= 0.1 * checked
+
+
+def test_sh_head_gradient_of_a_coefficient_is_its_weight_row():
+    """The SH coefficients are linear in the last hidden layer: dL/dW_head
+    for an SH row is sum_points g_sh * h2, and dL/db of that row is
+    sum_points g_sh, exactly (a closed form, not a difference)."""
+    dec = S.single_decoder_sh()
+    xyzt, g = _batch(55, n=100, colour=("sh", 48))
+    out = O.decode_grad(dec, xyzt, mode=0, grads=g)
+    gb = out["g_biases"][-1]
+    np.testing.assert_allclose(gb[7:55], g["sh"].sum(axis=0), rtol=1e-12, atol=1e-12)
+    # the SH rows of the head are the raw outputs themselves
+    np.testing.assert_array_equal(out["raw"][:, 7:55], out["sh"])
 
 
 def test_tiny_decoder_gradients_match_central_differences():
