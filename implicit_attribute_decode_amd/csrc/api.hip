@@ -386,7 +386,7 @@ ia_status ia_decode_keep(const ia_decoder* dec, const float* pos, int32_t pos_st
 
 namespace {
 bool backward_supported(const ia_decoder* dec) {
-    return dec->mlp.dtype == IA_DTYPE_F16 && dec->mlp.color == IA_COLOR_RGB && dec->mlp.branches == IA_BRANCHES_SHARED;
+    return dec->mlp.dtype == IA_DTYPE_F16 && dec->mlp.branches == IA_BRANCHES_SHARED;
 }
 }  // namespace
 
@@ -394,7 +394,7 @@ ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_t N, si
     if (!dec || !bytes) return fail(IA_ERR_INVALID_ARG, "null argument");
     if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
     if (!backward_supported(dec))
-        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoder with the RGB head");
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoders (RGB or SH head)");
     *bytes = ia::decode_bwd_layout(dec->lv, N).total;
     return IA_OK;
 }
@@ -406,7 +406,7 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
     if (!backward_supported(dec))
-        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoder with the RGB head");
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoders (RGB or SH head)");
     if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
     if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
     if (N < 0 || N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N must be in [0, 2^40]");
@@ -415,8 +415,8 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
         if (!grads->weights[k] || !grads->biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias gradient");
     if (N > 0) {
         if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
-        if (!outputs_ok(grad_attr, false))
-            return fail(IA_ERR_INVALID_ARG, "grad_attr scales/quats/colors/opacity must be non-null");
+        if (!outputs_ok(grad_attr, dec->mlp.color == IA_COLOR_SH3))
+            return fail(IA_ERR_INVALID_ARG, "grad_attr scales/quats/colors (sh for the SH head)/opacity must be non-null");
     }
     ia_status fs = check_features(dec, N, features, features_bytes);
     if (fs != IA_OK) return fs;
@@ -428,7 +428,7 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
     if (N > 0) {
         b.g_scales = grad_attr->scales;
         b.g_quats = grad_attr->quats;
-        b.g_colors = grad_attr->colors;
+        b.g_colors = dec->mlp.color == IA_COLOR_SH3 ? grad_attr->sh : grad_attr->colors;
         b.g_opacity = grad_attr->opacity;
     }
     b.g_means = grad_means;

@@ -59,9 +59,17 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kTS = 18;  // row stride (floats) of the per-wave transpose buffers: conflict-free column reads
-// per lane: 4 head tiles + 16 W2 tiles + 8 W1 tiles (4 floats each) + 36 bias partials
-constexpr int kTileSlots = (4 + 16 + 8) * 4;
-constexpr int kBiasSlots = 4 + 16 + 16;
+// The head block has HT row tiles of 16: 1 for the RGB head (11 rows), 4 for
+// the SH colour head (56 rows: s | r | 48 SH | o).  Per lane of a wave's
+// partial slot: 4 HT head tiles + 16 W2 tiles + 8 W1 tiles (4 floats each),
+// then 4 HT + 16 + 16 bias partials.
+template <int HT>
+constexpr int tile_slots() { return (4 * HT + 16 + 8) * 4; }
+template <int HT>
+constexpr int bias_slots() { return 4 * HT + 16 + 16; }
+template <int HT>
+constexpr int head_rows() { return HT == 1 ? 11 : 56; }
+static_assert(tile_slots<4>() + bias_slots<4>() <= kDecodeBwdSlotFloats / 64, "partial slots hold the SH head");
 static_assert(kDecodeBwdBlocks * kBwdWaves % kDecodeBwdGroups == 0, "groups must split the waves evenly");
 
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
@@ -108,21 +116,23 @@ struct MlpBwdArgs {
     int64_t off;  // index of the chunk's first Gaussian in the upstream gradients
     const float* gs;
     const float* gq;
-    const float* gc;
+    const float* gc;  // [N,3] colours, or [N,48] SH coefficients (HT = 4)
     const float* go;
     float2* gz;      // [L][gzstride]
     int64_t gzstride;
-    float* partial;  // [waves][kTileSlots + kBiasSlots][64]
+    float* partial;  // [waves][kDecodeBwdSlotFloats]: tile_slots<HT>() + bias_slots<HT>() rows of 64
     int first;       // 1: the partial slots start from zero
 };
 
-template <bool GELU>
+template <bool GELU, int HT>
 __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma clang fp contract(fast)
+    constexpr int HEAD = head_rows<HT>();
+    constexpr bool SH = HT == 4;
     // fp32 operands of the data-gradient products, lane-ordered:
-    //   sWh[rb][e][lane] = Wh[4q+e][16rb+c], sW2[ob][rb][e][lane] = W2[16rb+4q+e][16ob+c],
+    //   sWh[ht][rb][e][lane] = Wh[16ht+4q+e][16rb+c], sW2[ob][rb][e][lane] = W2[16rb+4q+e][16ob+c],
     //   sW1[ob][rb][e][lane] = W1[16rb+4q+e][16ob+c]
-    __shared__ float sWh[4 * 4 * 64];
+    __shared__ float sWh[HT * 4 * 4 * 64];
     __shared__ float sW2[4 * 4 * 4 * 64];
     __shared__ float sW1[2 * 4 * 4 * 64];
     __shared__ float sT[kBwdWaves][2][64 * kTS];
@@ -131,10 +141,10 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
     const _Float16* W1 = a.W[0];
     const _Float16* W2 = a.W[1];
     const _Float16* Wh = a.W[2];
-    for (int k = threadIdx.x; k < 4 * 4 * 64; k += kBwdThreads) {
-        const int l = k & 63, e = (k >> 6) & 3, rb = k >> 8, qq = l >> 4, cc = l & 15;
-        const int row = 4 * qq + e;
-        sWh[k] = row < 11 ? (float)Wh[row * 64 + 16 * rb + cc] : 0.0f;
+    for (int k = threadIdx.x; k < HT * 4 * 4 * 64; k += kBwdThreads) {
+        const int l = k & 63, e = (k >> 6) & 3, rb = (k >> 8) & 3, ht = k >> 10, qq = l >> 4, cc = l & 15;
+        const int row = 16 * ht + 4 * qq + e;
+        sWh[k] = row < HEAD ? (float)Wh[row * 64 + 16 * rb + cc] : 0.0f;
     }
     for (int k = threadIdx.x; k < 4 * 4 * 4 * 64; k += kBwdThreads) {
         const int l = k & 63, e = (k >> 6) & 3, rb = (k >> 8) & 3, ob = k >> 10, qq = l >> 4, cc = l & 15;
@@ -147,9 +157,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
     __syncthreads();
 
     // forward operands, as the decode holds them
-    half8_t A1[4], A2[4][2], A3[2];
+    half8_t A1[4], A2[4][2], A3[HT][2];
     // biases as the recomputed forward's initial MFMA accumulators, as the decode does
-    floatx4_t B1[4], B2[4], B3;
+    floatx4_t B1[4], B2[4], B3[HT];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
         A1[rb] = a_tile32(W1, 32, 64, rb, 0, q, c);
@@ -162,21 +172,24 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         }
     }
 #pragma unroll
-    for (int m = 0; m < 2; ++m) A3[m] = a_tile32(Wh, 64, 11, 0, m, q, c);
+    for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) B3[e] = (4 * q + e) < 11 ? a.b[2][4 * q + e] : 0.0f;
+        for (int m = 0; m < 2; ++m) A3[ht][m] = a_tile32(Wh, 64, HEAD, ht, m, q, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) B3[ht][e] = (16 * ht + 4 * q + e) < HEAD ? a.b[2][16 * ht + 4 * q + e] : 0.0f;
+    }
 
     const int64_t wave = (int64_t)blockIdx.x * kBwdWaves + wv;
     const int64_t nwaves = (int64_t)gridDim.x * kBwdWaves;
-    float* part = a.partial + wave * (int64_t)(kTileSlots + kBiasSlots) * 64 + lane;
-    floatx4_t accH[4], accW2[4][4], accW1[4][2];
-    float gbh[4], gb2[4][4], gb1[4][4];
+    float* part = a.partial + wave * (int64_t)kDecodeBwdSlotFloats + lane;
+    floatx4_t accH[HT][4], accW2[4][4], accW1[4][2];
+    float gbh[HT][4], gb2[4][4], gb1[4][4];
     {
         int j = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4 * HT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) accH[t][e] = a.first ? 0.0f : part[64 * j++];
+            for (int e = 0; e < 4; ++e) accH[t >> 2][t & 3][e] = a.first ? 0.0f : part[64 * j++];
 #pragma unroll
         for (int t = 0; t < 16; ++t)
 #pragma unroll
@@ -186,7 +199,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) accW1[t >> 1][t & 1][e] = a.first ? 0.0f : part[64 * j++];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gbh[e] = a.first ? 0.0f : part[64 * j++];
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gbh[ht][e] = a.first ? 0.0f : part[64 * j++];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -244,63 +259,80 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
             }
             H2[m] = h;
         }
-        floatx4_t accO = B3;
+        float o[HT][4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) accO = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[k], H2[k], accO, 0, 0, 0);
-        float o[4];
+        for (int ht = 0; ht < HT; ++ht) {
+            floatx4_t accO = B3[ht];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = accO[e];
-
-        // ---------------- Eq. 11 backward.  Rows 4q+e of column c:
-        // q = 0: s0 s1 s2 rw | q = 1: rx ry rz c0 | q = 2: c1 c2 op - | q = 3: -
-        float up[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (valid) {
-            const int64_t u = a.off + gi;
-            if (q == 0) {
-                up[0] = a.gs[u * 3 + 0];
-                up[1] = a.gs[u * 3 + 1];
-                up[2] = a.gs[u * 3 + 2];
-                up[3] = a.gq[u * 4 + 0];
-            } else if (q == 1) {
-                up[0] = a.gq[u * 4 + 1];
-                up[1] = a.gq[u * 4 + 2];
-                up[2] = a.gq[u * 4 + 3];
-                up[3] = a.gc[u * 3 + 0];
-            } else if (q == 2) {
-                up[0] = a.gc[u * 3 + 1];
-                up[1] = a.gc[u * 3 + 2];
-                up[2] = a.go[u];
-            }
+            for (int k = 0; k < 2; ++k) accO = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[ht][k], H2[k], accO, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[ht][e] = accO[e];
         }
-        const float part_n = q == 0 ? o[3] * o[3] : (q == 1 ? o[0] * o[0] + o[1] * o[1] + o[2] * o[2] : 0.0f);
+
+        // ---------------- Eq. 11 backward.  Head row r = 16 ht + 4 q + e of
+        // column c.  Tile 0: q = 0: s0 s1 s2 rw | q = 1: rx ry rz, then row 7
+        // (RGB: c0 c1 c2 op; SH: the 48 coefficients up to row 54, opacity 55)
+        float up[HT][4];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * ht + 4 * q + e;
+                float v = 0.0f;
+                if (valid) {
+                    const int64_t u = a.off + gi;
+                    if (r < 3)
+                        v = a.gs[u * 3 + r];
+                    else if (r < 7)
+                        v = a.gq[u * 4 + (r - 3)];
+                    else if (r < HEAD - 1)
+                        v = a.gc[u * (HEAD - 8) + (r - 7)];
+                    else if (r == HEAD - 1)
+                        v = a.go[u];
+                }
+                up[ht][e] = v;
+            }
+        const float part_n =
+            q == 0 ? o[0][3] * o[0][3] : (q == 1 ? o[0][0] * o[0][0] + o[0][1] * o[0][1] + o[0][2] * o[0][2] : 0.0f);
         const float rn = sqrtf(part_n + __shfl_xor(part_n, 16));
         const float nrm = fmaxf(rn, 1e-12f);
-        const float part_d = q == 0 ? up[3] * (o[3] / nrm)
-                                    : (q == 1 ? up[0] * (o[0] / nrm) + up[1] * (o[1] / nrm) + up[2] * (o[2] / nrm) : 0.0f);
+        const float part_d = q == 0 ? up[0][3] * (o[0][3] / nrm)
+                                    : (q == 1 ? up[0][0] * (o[0][0] / nrm) + up[0][1] * (o[0][1] / nrm) +
+                                                    up[0][2] * (o[0][2] / nrm)
+                                              : 0.0f);
         const float dot = rn >= 1e-12f ? part_d + __shfl_xor(part_d, 16) : 0.0f;
-        float go[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (q == 0) {
+        float go[HT][4];
 #pragma unroll
-            for (int e = 0; e < 3; ++e) go[e] = o[e] < 20.0f ? up[e] * expf(o[e]) : 0.0f;
-            go[3] = (up[3] - dot * (o[3] / nrm)) / nrm;
-        } else if (q == 1) {
+        for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int e = 0; e < 3; ++e) go[e] = (up[e] - dot * (o[e] / nrm)) / nrm;
-            const float s = sigmoid_f(o[3]);
-            go[3] = up[3] * s * (1.0f - s);
-        } else if (q == 2) {
-#pragma unroll
-            for (int e = 0; e < 3; ++e) {
-                const float s = sigmoid_f(o[e]);
-                go[e] = up[e] * s * (1.0f - s);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * ht + 4 * q + e;
+                const float x = o[ht][e], g = up[ht][e];
+                float d = 0.0f;
+                if (r < 3) {
+                    d = x < 20.0f ? g * expf(x) : 0.0f;
+                } else if (r < 7) {
+                    d = (g - dot * (x / nrm)) / nrm;
+                } else if (r < HEAD) {
+                    if (SH && r < HEAD - 1) {
+                        d = g;  // an SH coefficient is its head output
+                    } else {
+                        const float sg = sigmoid_f(x);
+                        d = g * sg * (1.0f - sg);
+                    }
+                }
+                go[ht][e] = d;
             }
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gbh[e] += go[e];
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gbh[ht][e] += go[ht][e];
 
         // ---------------- head: dWh += go H2^T (Gaussians on k through LDS)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sG[(4 * q + e) * kTS + c] = go[e];
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[(16 * ht + 4 * q + e) * kTS + c] = go[ht][e];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -311,9 +343,15 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const float ag = sG[c * kTS + 4 * s + q];
+            float bh[4];
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) accH[hb] = mfma4(ag, sH[(16 * hb + c) * kTS + 4 * s + q], accH[hb]);
+            for (int hb = 0; hb < 4; ++hb) bh[hb] = sH[(16 * hb + c) * kTS + 4 * s + q];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const float ag = sG[(16 * ht + c) * kTS + 4 * s + q];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) accH[ht][hb] = mfma4(ag, bh[hb], accH[ht][hb]);
+            }
         }
         wave_lds_sync();
         // dH2 = Wh^T go; da2 = dH2 act'(a2)
@@ -322,7 +360,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
         for (int rb = 0; rb < 4; ++rb) {
             D[rb] = floatx4_t{0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) D[rb] = mfma4(sWh[(rb * 4 + e) * 64 + lane], go[e], D[rb]);
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) D[rb] = mfma4(sWh[((ht * 4 + rb) * 4 + e) * 64 + lane], go[ht][e], D[rb]);
         }
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
@@ -414,9 +454,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
     {
         int j = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4 * HT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) part[64 * j++] = accH[t][e];
+            for (int e = 0; e < 4; ++e) part[64 * j++] = accH[t >> 2][t & 3][e];
 #pragma unroll
         for (int t = 0; t < 16; ++t)
 #pragma unroll
@@ -426,7 +466,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) part[64 * j++] = accW1[t >> 1][t & 1][e];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part[64 * j++] = gbh[e];
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = gbh[ht][e];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -442,7 +484,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
 // waves [g W, (g + 1) W), W = waves / groups, in wave order, lane by lane.
 __global__ void __launch_bounds__(64) mlp_bwd_group_kernel(const float* partial, int waves_per_group,
                                                            float* group_sums) {
-    const int stride = (kTileSlots + kBiasSlots) * 64;
+    const int stride = kDecodeBwdSlotFloats;
     const int j = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
     const float* src = partial + (size_t)g * waves_per_group * stride + j * 64 + lane;
     float s = 0.0f;
@@ -450,44 +492,47 @@ __global__ void __launch_bounds__(64) mlp_bwd_group_kernel(const float* partial,
     group_sums[(size_t)g * stride + j * 64 + lane] = s;
 }
 
-// Sum the per-wave (or per-group) partials in order.  Thread t < kTileSlots * 64 owns
-// one (slot, lane) of the weight tiles; the next 36 * 4 threads own one bias
-// slot of one lane group q (summed over its 16 lanes c).
+// Sum the per-wave (or per-group) partials in order.  Thread t < tile_slots * 64
+// owns one (slot, lane) of the weight tiles; the next bias_slots * 4 threads own
+// one bias slot of one lane group q (summed over its 16 lanes c).
+template <int HT>
 __global__ void __launch_bounds__(256) mlp_bwd_reduce_kernel(const float* partial, int nwaves, float* gW1,
                                                              float* gW2, float* gWh, float* gb1, float* gb2,
                                                              float* gbh) {
+    constexpr int kT = tile_slots<HT>(), kB = bias_slots<HT>(), HEAD = head_rows<HT>();
     const int t = blockIdx.x * 256 + threadIdx.x;
-    const int stride = (kTileSlots + kBiasSlots) * 64;
-    if (t < kTileSlots * 64) {
+    const int stride = kDecodeBwdSlotFloats;
+    if (t < kT * 64) {
         const int j = t >> 6, lane = t & 63, q = lane >> 4, c = lane & 15, e = j & 3, tile = j >> 2;
         float s = 0.0f;
         for (int w = 0; w < nwaves; ++w) s += partial[(size_t)w * stride + t];
-        if (tile < 4) {
-            const int row = 4 * q + e;
-            if (row < 11) gWh[row * 64 + 16 * tile + c] = s;
-        } else if (tile < 20) {
-            const int rb = (tile - 4) >> 2, hb = (tile - 4) & 3;
+        if (tile < 4 * HT) {
+            const int ht = tile >> 2, hb = tile & 3;
+            const int row = 16 * ht + 4 * q + e;
+            if (row < HEAD) gWh[row * 64 + 16 * hb + c] = s;
+        } else if (tile < 4 * HT + 16) {
+            const int rb = (tile - 4 * HT) >> 2, hb = (tile - 4 * HT) & 3;
             gW2[(16 * rb + 4 * q + e) * 64 + 16 * hb + c] = s;
         } else {
-            const int rb = (tile - 20) >> 1, kb = (tile - 20) & 1;
+            const int rb = (tile - 4 * HT - 16) >> 1, kb = (tile - 4 * HT - 16) & 1;
             gW1[(16 * rb + 4 * q + e) * 32 + 16 * kb + c] = s;
         }
         return;
     }
-    const int u = t - kTileSlots * 64;
-    if (u >= kBiasSlots * 4) return;
+    const int u = t - kT * 64;
+    if (u >= kB * 4) return;
     const int jb = u >> 2, q = u & 3;
     float s = 0.0f;
     for (int w = 0; w < nwaves; ++w)
-        for (int c = 0; c < 16; ++c) s += partial[(size_t)w * stride + (kTileSlots + jb) * 64 + 16 * q + c];
-    if (jb < 4) {
-        const int row = 4 * q + jb;
-        if (row < 11) gbh[row] = s;
-    } else if (jb < 20) {
-        const int rb = (jb - 4) >> 2, e = (jb - 4) & 3;
+        for (int c = 0; c < 16; ++c) s += partial[(size_t)w * stride + (kT + jb) * 64 + 16 * q + c];
+    if (jb < 4 * HT) {
+        const int row = 16 * (jb >> 2) + 4 * q + (jb & 3);
+        if (row < HEAD) gbh[row] = s;
+    } else if (jb < 4 * HT + 16) {
+        const int rb = (jb - 4 * HT) >> 2, e = (jb - 4 * HT) & 3;
         gb2[16 * rb + 4 * q + e] = s;
     } else {
-        const int rb = (jb - 20) >> 2, e = (jb - 20) & 3;
+        const int rb = (jb - 4 * HT - 16) >> 2, e = (jb - 4 * HT - 16) & 3;
         gb1[16 * rb + 4 * q + e] = s;
     }
 }
@@ -690,26 +735,29 @@ __global__ void __launch_bounds__(256) pos_reduce_kernel(const uint32_t* list, c
 // per-block counts, one exclusive scan, ordered writes.
 constexpr int kCompactItems = 4096;  // per block: 256 threads x 16 rounds
 
+// ncol: colour values per Gaussian (3 RGB, or the 48 SH coefficients)
 __device__ __forceinline__ bool has_gradient(const float* gs, const float* gq, const float* gc, const float* go,
-                                             int64_t u) {
-    // all eleven values are loaded (no short circuit, so the loads overlap);
-    // a value counts unless it is +0 or -0 (NaN counts)
+                                             int ncol, int64_t u) {
+    // every value is loaded (no short circuit, so the loads overlap); a
+    // value counts unless it is +0 or -0 (NaN counts)
     uint32_t bits = __float_as_uint(go[u]);
 #pragma unroll
-    for (int k = 0; k < 3; ++k) bits |= __float_as_uint(gs[u * 3 + k]) | __float_as_uint(gc[u * 3 + k]);
+    for (int k = 0; k < 3; ++k) bits |= __float_as_uint(gs[u * 3 + k]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) bits |= __float_as_uint(gq[u * 4 + k]);
+    for (int k = 0; k < ncol; ++k) bits |= __float_as_uint(gc[u * ncol + k]);
     return (bits & 0x7fffffffu) != 0u;
 }
 
 __global__ void __launch_bounds__(256) active_count_kernel(const float* gs, const float* gq, const float* gc,
-                                                           const float* go, int64_t off, int64_t n, uint32_t* bcount) {
+                                                           const float* go, int ncol, int64_t off, int64_t n,
+                                                           uint32_t* bcount) {
     __shared__ uint32_t s_cnt[4];
     const int64_t b0 = (int64_t)blockIdx.x * kCompactItems;
     uint32_t cnt = 0;
     for (int r = 0; r < kCompactItems / 256; ++r) {
         const int64_t i = b0 + r * 256 + threadIdx.x;
-        if (i < n && has_gradient(gs, gq, gc, go, off + i)) ++cnt;
+        if (i < n && has_gradient(gs, gq, gc, go, ncol, off + i)) ++cnt;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
@@ -768,7 +816,7 @@ __device__ __forceinline__ uint32_t spatial_key(float4 p) {
 }
 
 __global__ void __launch_bounds__(256) active_write_kernel(const float* gs, const float* gq, const float* gc,
-                                                           const float* go, int64_t off, int64_t n,
+                                                           const float* go, int ncol, int64_t off, int64_t n,
                                                            const uint32_t* boff, const float4* xt,
                                                            uint64_t* items) {
     __shared__ uint32_t s_w[4];
@@ -777,7 +825,7 @@ __global__ void __launch_bounds__(256) active_write_kernel(const float* gs, cons
     uint32_t pos = boff[blockIdx.x];
     for (int r = 0; r < kCompactItems / 256; ++r) {
         const int64_t i = b0 + r * 256 + threadIdx.x;
-        const bool f = i < n && has_gradient(gs, gq, gc, go, off + i);
+        const bool f = i < n && has_gradient(gs, gq, gc, go, ncol, off + i);
         const uint64_t m = __ballot(f);
         if (lane == 0) s_w[wv] = (uint32_t)__popcll(m);
         __syncthreads();
@@ -906,6 +954,7 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     m.go = b.g_opacity;
     m.gz = gz;
     m.partial = partial;
+    const int ncol = a.sh_head ? 48 : 3;
     int first = 1;
     for (int64_t off = 0; off < a.N; off += chunk) {
         const int64_t n = a.N - off < chunk ? a.N - off : chunk;
@@ -916,10 +965,10 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         m.zstride = a.features ? a.N : chunk;
         const int nb = (int)((n + kCompactItems - 1) / kCompactItems);
         IA_LAUNCH("active_count_kernel", active_count_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
-                  b.g_colors, b.g_opacity, off, n, boff);
+                  b.g_colors, b.g_opacity, ncol, off, n, boff);
         IA_LAUNCH("active_scan_kernel", active_scan_kernel, dim3(1), dim3(256), 0, s, boff, nb, count, srt.count);
         IA_LAUNCH("active_write_kernel", active_write_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
-                  b.g_colors, b.g_opacity, off, n, boff, xt, srt.items[0]);
+                  b.g_colors, b.g_opacity, ncol, off, n, boff, xt, srt.items[0]);
         // stable sort on the 30 key bits above the index
         const int cur = radix_sort_u64(srt.items, srt.count, (uint64_t)chunk, 32, 30, srt.max_blocks, srt.counts,
                                        srt.digit_tot, s);
@@ -930,8 +979,9 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         m.off = off;
         m.first = first;
         first = 0;
-        IA_LAUNCH("mlp_bwd_kernel", m.gelu ? mlp_bwd_kernel<true> : mlp_bwd_kernel<false>, dim3(kDecodeBwdBlocks),
-                  dim3(kBwdThreads), 0, s, m);
+        auto kernel = a.sh_head ? (m.gelu ? mlp_bwd_kernel<true, 4> : mlp_bwd_kernel<false, 4>)
+                                : (m.gelu ? mlp_bwd_kernel<true, 1> : mlp_bwd_kernel<false, 1>);
+        IA_LAUNCH("mlp_bwd_kernel", kernel, dim3(kDecodeBwdBlocks), dim3(kBwdThreads), 0, s, m);
         const int nchunk = (int)((n + 255) / 256), nchunk_agg = (int)((n + 64 * kAggRounds - 1) / (64 * kAggRounds));
         const float* pos = a.pos + off * a.stride;
         float* gpos = b.g_pos ? b.g_pos + off * 3 : nullptr;
@@ -958,18 +1008,25 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         }
     }
     if (first) {  // N = 0: the weight and bias gradients are zero
-        const int64_t nf = (int64_t)kDecodeBwdBlocks * kBwdWaves * (kTileSlots + kBiasSlots) * 64;
+        const int64_t nf = (int64_t)kDecodeBwdBlocks * kBwdWaves * kDecodeBwdSlotFloats;
         IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(nf, 256, 8192)), dim3(256), 0, s, partial,
                   nf, (const float*)nullptr);
     }
     // fixed-order two-stage sum of the per-wave partials (deterministic)
     const int nwaves = kDecodeBwdBlocks * kBwdWaves;
-    float* groups = partial + (size_t)nwaves * (kTileSlots + kBiasSlots) * 64;
-    IA_LAUNCH("mlp_bwd_group_kernel", mlp_bwd_group_kernel, dim3(kTileSlots + kBiasSlots, kDecodeBwdGroups), dim3(64),
-              0, s, partial, nwaves / kDecodeBwdGroups, groups);
-    const int nred = kTileSlots * 64 + kBiasSlots * 4;
-    IA_LAUNCH("mlp_bwd_reduce_kernel", mlp_bwd_reduce_kernel, dim3((nred + 255) / 256), dim3(256), 0, s, groups,
-              kDecodeBwdGroups, b.g_W[0], b.g_W[1], b.g_W[2], b.g_b[0], b.g_b[1], b.g_b[2]);
+    float* groups = partial + (size_t)nwaves * kDecodeBwdSlotFloats;
+    const int slots = a.sh_head ? tile_slots<4>() + bias_slots<4>() : tile_slots<1>() + bias_slots<1>();
+    IA_LAUNCH("mlp_bwd_group_kernel", mlp_bwd_group_kernel, dim3(slots, kDecodeBwdGroups), dim3(64), 0, s, partial,
+              nwaves / kDecodeBwdGroups, groups);
+    if (a.sh_head) {
+        const int nred = tile_slots<4>() * 64 + bias_slots<4>() * 4;
+        IA_LAUNCH("mlp_bwd_reduce_kernel", mlp_bwd_reduce_kernel<4>, dim3((nred + 255) / 256), dim3(256), 0, s,
+                  groups, kDecodeBwdGroups, b.g_W[0], b.g_W[1], b.g_W[2], b.g_b[0], b.g_b[1], b.g_b[2]);
+    } else {
+        const int nred = tile_slots<1>() * 64 + bias_slots<1>() * 4;
+        IA_LAUNCH("mlp_bwd_reduce_kernel", mlp_bwd_reduce_kernel<1>, dim3((nred + 255) / 256), dim3(256), 0, s,
+                  groups, kDecodeBwdGroups, b.g_W[0], b.g_W[1], b.g_W[2], b.g_b[0], b.g_b[1], b.g_b[2]);
+    }
     return hipGetLastError();
 }
 

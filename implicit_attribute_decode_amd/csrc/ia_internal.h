@@ -116,11 +116,13 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
                                   int64_t zstride, hipStream_t s);
 
 // Backward of the fp16 decode: one persistent grid of kDecodeBwdBlocks blocks
-// of four waves; each wave owns a slot of 148 x 64 floats in the workspace's
-// partials, followed by kDecodeBwdGroups slots of group sums.
+// of four waves; each wave owns a slot of kDecodeBwdSlotFloats floats in the
+// workspace's partials (148 x 64 used by the RGB head, 208 x 64 by the SH
+// colour head), followed by kDecodeBwdGroups slots of group sums.
 constexpr int kDecodeBwdBlocks = 256;
 constexpr int kDecodeBwdGroups = 16;
-constexpr int64_t kDecodeBwdPartialFloats = ((int64_t)kDecodeBwdBlocks * 4 + kDecodeBwdGroups) * 148 * 64;
+constexpr int kDecodeBwdSlotFloats = 208 * 64;
+constexpr int64_t kDecodeBwdPartialFloats = ((int64_t)kDecodeBwdBlocks * 4 + kDecodeBwdGroups) * kDecodeBwdSlotFloats;
 
 // Byte offsets of the backward's scratch inside a workspace (chunks of at
 // most 2^21 Gaussians): recomputed features z [L][chunk], their gradient
@@ -137,13 +139,13 @@ struct DecodeBwdArgs {
     DecodeArgs fwd;           // the decode being differentiated (parameters, positions)
     const float* g_scales;    // [N,3] upstream dL/dscales
     const float* g_quats;     // [N,4]
-    const float* g_colors;    // [N,3]
+    const float* g_colors;    // [N,3], or the SH coefficients [N,48] (SH colour head)
     const float* g_opacity;   // [N]
     const float* g_means;     // [N,3] added into g_pos, or null
     float* g_pos;             // [N,3] out, or null (no position gradient)
     float* g_tables;          // [L][T][2] out
-    float* g_W[3];            // [64][32], [64][64], [11][64] out
-    float* g_b[3];            // [64], [64], [11] out
+    float* g_W[3];            // [64][32], [64][64], [11 or 56][64] out
+    float* g_b[3];            // [64], [64], [11 or 56] out
     unsigned char* ws;        // caller's workspace, decode_bwd_layout(h, N).total bytes
 };
 

@@ -244,15 +244,16 @@ typedef struct {
  * min(N, 2^21) Gaussians (rounded up to a multiple of 4096) the recomputed
  * encoding, its gradient, the chunk's active list and spatial sort, the
  * normalised positions and the per-level position shares (484 bytes per
- * Gaussian at L = 16), plus 39 MB of weight-gradient partials.
+ * Gaussian at L = 16), plus 55 MB of weight-gradient partials.
  * Errors: INVALID_ARG, UNSUPPORTED (decoders without a backward). */
 IA_API ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_t N, size_t* bytes);
 
 /* Backward of ia_decode (pos_stride 3, time t) or ia_decode_xyzt (pos_stride
  * 4) for upstream gradients of the decoded attributes ([SPIN] §3.3 Eq. 7-11
  * differentiated; positions are trainable, §3.3 Eq. 7).
- *   grad_attr: device dL/d scales [N,3], quats [N,4], colors [N,3],
- *              opacity [N] (means and sh are ignored).
+ *   grad_attr: device dL/d scales [N,3], quats [N,4], colors [N,3] (RGB
+ *              head) or sh [N,16,3] (SH colour head), opacity [N] (means
+ *              and the other colour field are ignored).
  *   grad_means: device [N,3] or NULL; added into grad_pos (e.g. the render's
  *              position gradient, the positions being the means).
  *   grad_pos:  device [N,3] out, grad_means + dL/dposition through Eq. 7 and
@@ -270,7 +271,9 @@ IA_API ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_
  * The forward is recomputed exactly as the decode computes it (fp16 hidden
  * activations); the backward runs in fp32 (v_mfma_f32_16x16x4_f32), treating
  * the fp16 roundings as the identity.  Supported: the shared-trunk fp16
- * decoder with the RGB head.
+ * decoders with the RGB head or the SH colour head ([SPIN] §3.3: the colour
+ * decoder regresses the 48 coefficients, so their gradient passes unchanged
+ * to the head outputs).
  * Errors: INVALID_ARG, UNSUPPORTED (other decoders), WORKSPACE_TOO_SMALL,
  * DEVICE. */
 IA_API ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,

@@ -266,3 +266,68 @@ def test_decode_backward_weight_bias_and_position_gradients_are_deterministic():
         f"{frac:.2e} of entries differ")
     assert float(diff.max()) <= 1e-5 * scale
     assert bool((diff <= 1e-5 * ta.abs() + 1e-7 * scale).all())
+
+
+# ---------------------------------------------------------------- SH colour head
+
+def _upstream_sh(rng, n):
+    return dict(scales=rng.normal(size=(n, 3)), quats=rng.normal(size=(n, 4)), sh=rng.normal(size=(n, 48)),
+                opacity=rng.normal(size=n))
+
+
+@pytest.mark.parametrize("n", [1, 17, 1000, 20000])
+def test_sh_head_backward_matches_oracle(n):
+    """The Single decoder with the SH colour head (SPIN-4DGS §3.3: the colour
+    decoder regresses the 48 coefficients, whose gradients reach the head
+    unchanged), on edge positions and ragged sizes."""
+    dec = S.single_decoder_sh()
+    rng = np.random.default_rng(70 + n)
+    pos = _edge_xyzt(rng, n)
+    up = _upstream_sh(rng, n)
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare(f"sh {n}", dec, out, ref)
+
+
+def test_sh_head_backward_only_sh_gradients_count():
+    """Gaussians whose only non-zero upstream gradient is one SH coefficient
+    take part (the active list reads all 48); those with none are skipped
+    without changing any gradient.  Three quarters of the Gaussians carry one
+    coefficient each, about 300 terms per head row, so that, as in the dense
+    cases, a one-ulp fp16 flip of a hidden activation stays inside the
+    module's bound."""
+    dec = S.single_decoder_sh()
+    rng = np.random.default_rng(75)
+    n = 20000
+    pos = _edge_xyzt(rng, n)
+    up = {k: np.zeros_like(v) for k, v in _upstream_sh(rng, n).items()}
+    idx = rng.choice(n, size=3 * n // 4, replace=False)
+    coef = rng.integers(48, size=idx.size)
+    up["sh"][idx, coef] = rng.normal(size=idx.size)
+    up["sh"][idx[:5], 47] = 1.0  # the last coefficient too
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare("sh only", dec, out, ref)
+    # Gaussians without any upstream gradient have no position gradient
+    rest = np.setdiff1d(np.arange(n), idx)
+    assert float(np.abs(host(out["pos"])[rest]).max()) == 0.0
+
+
+def test_sh_head_backward_is_deterministic_and_paper_decoder_unsupported():
+    dec = S.single_decoder_sh()
+    rng = np.random.default_rng(76)
+    n = 5000
+    pos = _edge_xyzt(rng, n)
+    up = _upstream_sh(rng, n)
+    D = Decoder(dec)
+    a = _gpu_backward(D, pos, up)
+    a = {k: ([x.clone() for x in v] if isinstance(v, list) else v.clone()) for k, v in a.items()}
+    b = _gpu_backward(D, pos, up)
+    for l in range(3):
+        assert torch.equal(a["weights"][l], b["weights"][l]) and torch.equal(a["biases"][l], b["biases"][l])
+    assert torch.equal(a["pos"], b["pos"])
+    P = Decoder(S.paper_decoder(log2T=12))
+    with pytest.raises(ia.IAError) as e:
+        P.backward(torch.zeros((4, 4), device="cuda"),
+                   {k: torch.zeros((4, 48 if k == "sh" else 4), device="cuda") for k in ("scales", "quats", "sh", "opacity")})
+    assert e.value.status == ia.IA_ERR_UNSUPPORTED
