@@ -49,7 +49,8 @@ class _Hash(C.Structure):
 
 
 class _MLP(C.Structure):
-    _fields_ = [("n_layers", C.c_int), ("dims", C.c_int * 8), ("act", C.c_int), ("w_f16", C.c_int)]
+    _fields_ = [("n_layers", C.c_int), ("dims", C.c_int * 8), ("act", C.c_int), ("w_f16", C.c_int),
+                ("branches", C.c_int)]
 
 
 class _HexPlane(C.Structure):
@@ -278,6 +279,7 @@ def decode_grad(dec, pos: np.ndarray, t=None, mode: int = 0, grads: dict | None 
     bp = (C.c_void_p * len(bs))(*[b.ctypes.data for b in bs])
     hs = _hash(h)
     mm = _mlp(m.dims, m.act, m.f16)
+    mm.branches = int(bool(getattr(m, "branches", False)))
     head = int(m.dims[-1])
     cname, ncol = ("sh", 48) if head == 56 else ("colors", 3)
     out = dict(raw=np.zeros((n, head)), scales=np.zeros((n, 3)), quats=np.zeros((n, 4)), opacity=np.zeros(n),

@@ -225,6 +225,10 @@ typedef struct {
     int dims[8];   /* dims[0] = input width, dims[l+1] = output width of layer l */
     int act;       /* hidden activation: 0 = ReLU, 1 = GELU (exact erf) */
     int w_f16;     /* weights stored as binary16 (else fp32) */
+    int branches;  /* orc_decode_grad only: 1 = one MLP per attribute on the
+                      same z ([SPIN] §3.3 Eq. 10, the per-head reading), dims
+                      [in, hidden..., head] with each branch's last width
+                      3, 4, head - 8, 1; weights and biases branch-major */
 } orc_mlp;
 
 static double act_fn(int act, double x) {
@@ -1271,6 +1275,9 @@ EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_m
     /* head of 56 outputs: the SH colour decoder (s | r | 48 SH | o), whose
        colour slots are the coefficients themselves; else 11 (s | r | c | o) */
     const int sh = m->dims[nl] == 56, head = sh ? 56 : 11, ncol = sh ? 48 : 3;
+    /* every branch's layer inputs and pre-activations of the current point */
+    double(*xs)[8][512] = (double(*)[8][512])malloc(sizeof(double) * 4 * 8 * 512);
+    double(*pre)[8][512] = (double(*)[8][512])malloc(sizeof(double) * 4 * 8 * 512);
     uint64_t sig = 0;
     for (long i = 0; i < N; ++i) {
         uint64_t hs = mix64(0x9e3779b97f4a7c15ull, (uint64_t)i);
@@ -1346,27 +1353,38 @@ EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_m
                 for (int k = 0; k < F; ++k) z[l * F + k] += w * tables[((long)l * T + idx) * F + k];
             }
         }
-        /* Eq. 10 forward, keeping every layer's input and pre-activation */
-        double xs[8][512], pre[8][512];
-        for (int k = 0; k < LF; ++k) xs[0][k] = (mode & 1) ? round_f16(z[k]) : z[k];
-        for (int l = 0; l < nl; ++l) {
-            int di = m->dims[l], dout = m->dims[l + 1];
-            for (int o = 0; o < dout; ++o) {
-                double s = 0.0;
-                for (int k = 0; k < di; ++k) s += W[l][(long)o * di + k] * xs[l][k];
-                s += b[l][o];
-                pre[l][o] = s;
-                if (l + 1 < nl) {
-                    if (m->act == 0) {
-                        if (s == 0.0) fl = 1;
-                        hs = mix64(hs, s > 0.0);
+        /* Eq. 10 forward, keeping every layer's input and pre-activation: one
+           MLP, or one per attribute whose outputs fill head rows
+           [row0[br], row0[br] + width[br]) (scale, rotation, colour, opacity) */
+        const int nbr = m->branches ? 4 : 1;
+        const int row0[4] = {0, 3, 7, head - 1}, width[4] = {3, 4, ncol, 1};
+        double r[512];
+        for (int br = 0; br < nbr; ++br) {
+            const double* const* Wb = W + br * nl;
+            const double* const* bb = b + br * nl;
+            for (int k = 0; k < LF; ++k) xs[br][0][k] = (mode & 1) ? round_f16(z[k]) : z[k];
+            for (int l = 0; l < nl; ++l) {
+                int di = m->dims[l], dout = l + 1 < nl || !m->branches ? m->dims[l + 1] : width[br];
+                for (int o = 0; o < dout; ++o) {
+                    double s = 0.0;
+                    for (int k = 0; k < di; ++k) s += Wb[l][(long)o * di + k] * xs[br][l][k];
+                    s += bb[l][o];
+                    pre[br][l][o] = s;
+                    if (l + 1 < nl) {
+                        if (m->act == 0) {
+                            if (s == 0.0) fl = 1;
+                            hs = mix64(hs, s > 0.0);
+                        }
+                        double y = act_fn(m->act, s);
+                        xs[br][l + 1][o] = (mode & 1) ? round_f16(y) : y;
                     }
-                    double y = act_fn(m->act, s);
-                    xs[l + 1][o] = (mode & 1) ? round_f16(y) : y;
                 }
             }
+            if (m->branches)
+                for (int k = 0; k < width[br]; ++k) r[row0[br] + k] = pre[br][nl - 1][k];
+            else
+                for (int k = 0; k < head; ++k) r[k] = pre[0][nl - 1][k];
         }
-        const double* r = pre[nl - 1];
         /* Eq. 11 */
         double s3[3], q4[4], c3[3], o1;
         for (int k = 0; k < 3; ++k) {
@@ -1402,23 +1420,37 @@ EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_m
             gy[3 + k] = qn < 1e-12 ? gq[i * 4 + k] / 1e-12 : (gq[i * 4 + k] - dot * q4[k]) / qn;
         for (int k = 0; k < ncol; ++k) gy[7 + k] = sh ? gc[i * ncol + k] : gc[i * 3 + k] * c3[k] * (1.0 - c3[k]);
         gy[head - 1] = go[i] * o1 * (1.0 - o1);
-        /* backward of Eq. 10, last layer first */
-        for (int l = nl - 1; l >= 0; --l) {
-            int di = m->dims[l], dout = m->dims[l + 1];
-            if (l + 1 < nl)
-                for (int o = 0; o < dout; ++o)
-                    gy[o] *= m->act == 0 ? (pre[l][o] > 0.0 ? 1.0 : 0.0) : gelu_grad(pre[l][o]);
-            double gx[512];
-            for (int k = 0; k < di; ++k) gx[k] = 0.0;
-            for (int o = 0; o < dout; ++o) {
-                g_b[l][o] += gy[o];
-                for (int k = 0; k < di; ++k) {
-                    g_W[l][(long)o * di + k] += gy[o] * xs[l][k];
-                    gx[k] += W[l][(long)o * di + k] * gy[o];
+        /* backward of Eq. 10, last layer first; with branches each branch
+           starts from its head rows and the branches' input gradients add up
+           in dz */
+        double dz[512];
+        for (int k = 0; k < LF; ++k) dz[k] = 0.0;
+        for (int br = 0; br < nbr; ++br) {
+            const double* const* Wb = W + br * nl;
+            double* const* gWb = g_W + br * nl;
+            double* const* gbb = g_b + br * nl;
+            double g[512];
+            const int outw = m->branches ? width[br] : head;
+            for (int k = 0; k < outw; ++k) g[k] = gy[(m->branches ? row0[br] : 0) + k];
+            for (int l = nl - 1; l >= 0; --l) {
+                int di = m->dims[l], dout = l + 1 < nl || !m->branches ? m->dims[l + 1] : width[br];
+                if (l + 1 < nl)
+                    for (int o = 0; o < dout; ++o)
+                        g[o] *= m->act == 0 ? (pre[br][l][o] > 0.0 ? 1.0 : 0.0) : gelu_grad(pre[br][l][o]);
+                double gx[512];
+                for (int k = 0; k < di; ++k) gx[k] = 0.0;
+                for (int o = 0; o < dout; ++o) {
+                    gbb[l][o] += g[o];
+                    for (int k = 0; k < di; ++k) {
+                        gWb[l][(long)o * di + k] += g[o] * xs[br][l][k];
+                        gx[k] += Wb[l][(long)o * di + k] * g[o];
+                    }
                 }
+                for (int k = 0; k < di; ++k) g[k] = gx[k];
             }
-            for (int k = 0; k < di; ++k) gy[k] = gx[k];
+            for (int k = 0; k < LF; ++k) dz[k] += g[k];
         }
+        for (int k = 0; k < LF; ++k) gy[k] = dz[k];
         /* backward of Eq. 9 (tables and cell fractions) and Eq. 7 */
         double gxt[3] = {0.0, 0.0, 0.0};
         for (int l = 0; l < L; ++l) {
@@ -1444,5 +1476,7 @@ EXPORT void orc_decode_grad(const orc_hash* h, const double* tables, const orc_m
         for (int c = 0; c < 3; ++c)
             g_pos[i * 3 + c] = J[0 * 3 + c] * gxt[0] + J[1 * 3 + c] * gxt[1] + J[2 * 3 + c] * gxt[2];
     }
+    free(xs);
+    free(pre);
     if (signature) *signature = sig;
 }

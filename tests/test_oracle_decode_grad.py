@@ -152,3 +152,40 @@ def test_table_gradient_partition_of_unity():
     L, F = dec.hash.L, dec.hash.F
     got = out["g_tables"].reshape(L, -1, F).sum(axis=1).reshape(-1)
     np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12 * np.abs(want).max())
+
+
+def test_paper_branch_decoder_gradients_match_central_differences():
+    """The paper-scale decoder read as one 64-64-64 GELU MLP per attribute on
+    the F = 4 encoding (SPIN-4DGS §3.3 Eq. 10, §4 hidden width 64), SH colour
+    head; a 2^12-entry table keeps the differences cheap."""
+    dec = S.paper_decoder(log2T=12, sh=True)
+    checked, skipped = _check_fd(dec, 56, n_weights=12)
+    assert checked >= 500 and skipped <= 0.1 * checked
+
+
+def test_paper_branch_decoder_rgb_gradients_match_central_differences():
+    dec = S.paper_decoder(log2T=12, sh=False)
+    checked, skipped = _check_fd(dec, 57, n_weights=8, n_tables=40)
+    assert checked >= 350 and skipped <= 0.1 * checked
+
+
+def test_paper_branch_table_gradient_partition_of_unity():
+    """As for the shared decoder, with the four branches reading the same z:
+    the sum of a level's table gradient over its entries is
+    sum_branches g_b1[branch] @ W1[branch]."""
+    dec = S.paper_decoder(log2T=12, sh=True)
+    xyzt, g = _batch(58, n=200, colour=("sh", 48))
+    out = O.decode_grad(dec, xyzt, mode=0, grads=g)
+    nl = len(dec.mlp.dims) - 1
+    want = sum(out["g_biases"][b * nl] @ np.asarray(dec.weights[b * nl]).astype(np.float64) for b in range(4))
+    L, F = dec.hash.L, dec.hash.F
+    got = out["g_tables"].reshape(L, -1, F).sum(axis=1).reshape(-1)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12 * np.abs(want).max())
+    # a branch's weight gradients see only its own attribute's upstream gradient
+    g2 = dict(g, sh=np.zeros_like(g["sh"]))
+    out2 = O.decode_grad(dec, xyzt, mode=0, grads=g2)
+    for b in (0, 1, 3):
+        for l in range(nl):
+            np.testing.assert_array_equal(out2["g_weights"][b * nl + l], out["g_weights"][b * nl + l])
+    assert all(not out2["g_weights"][2 * nl + l].any() for l in range(nl))
+
