@@ -158,9 +158,9 @@ def _single(S, Decoder, R, stream) -> dict:
 
 def _paper(S, Decoder, R, stream) -> dict:
     """Paper-scale decoder (F = 4, 2^21-entry tables, one GELU MLP per
-    attribute, SH colour): one Single frame decoded and rendered with SH, and
-    the decode alone of 20 sequence frames (4M (x,y,z,t) positions), also
-    with 2^23-entry tables."""
+    attribute, SH colour): one Single frame decoded and rendered with SH, the
+    decoder backward of that frame, and the decode alone of 20 sequence
+    frames (4M (x,y,z,t) positions), also with 2^23-entry tables."""
     import torch
 
     D = Decoder(S.paper_decoder())
@@ -171,6 +171,17 @@ def _paper(S, Decoder, R, stream) -> dict:
     res = R.render(dict(means=x, **a), [0, x.shape[0]], [cam], 8 * x.shape[0], aux=True)
     cap = R.count_entries(res) + 4096
     ms = timed(lambda: (D.decode(x, t, out=a), R.render(dict(means=x, **a), [0, x.shape[0]], [cam], cap)), 20, stream)
+    # the decoder backward of the frame from the kept encoding, every Gaussian
+    # with a seeded N(0, 1) upstream gradient on all 56 outputs
+    g = torch.Generator(device="cuda").manual_seed(9)
+    nf = int(x.shape[0])
+    up = {k: torch.randn(shape, generator=g, device="cuda") for k, shape in
+          (("scales", (nf, 3)), ("quats", (nf, 4)), ("sh", (nf, 48)), ("opacity", (nf,)))}
+    _, feats = D.decode_keep(x, t)
+    D.backward(x, up, t, features=feats)
+    ms_b = timed(lambda: D.backward(x, up, t, features=feats), 5, stream)
+    kern_b = profiled(lambda: D.backward(x, up, t, features=feats), 1)
+    del feats
     seq = S.Sequence()
     xyzt = torch.as_tensor(seq.xyzt(list(range(20))), device="cuda")
     d = D.decode_xyzt(xyzt)
@@ -186,7 +197,8 @@ def _paper(S, Decoder, R, stream) -> dict:
     return {"single_frame_ms": round(ms, 4), "single_frame_fps": round(1e3 / ms, 1), "decode_gaussians": n,
             "decode_ms": round(ms_d, 4), "decode_gaussians_per_s": round(n / (ms_d / 1e3)), "decode_kernels_ms": kern,
             "decode_2p23_ms": round(ms_23, 4), "decode_2p23_kernels_ms": kern23,
-            "mlp_flop_per_gaussian": PAPER_FLOP_PER_GAUSSIAN}
+            "mlp_flop_per_gaussian": PAPER_FLOP_PER_GAUSSIAN,
+            "decode_backward_frame_ms": round(ms_b, 4), "decode_backward_frame_kernels_ms": kern_b}
 
 
 def _hexplane(S, HexPlane, R, stream, stored_order: bool = False) -> dict:

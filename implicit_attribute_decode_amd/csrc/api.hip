@@ -385,16 +385,15 @@ ia_status ia_decode_keep(const ia_decoder* dec, const float* pos, int32_t pos_st
 }
 
 namespace {
-bool backward_supported(const ia_decoder* dec) {
-    return dec->mlp.dtype == IA_DTYPE_F16 && dec->mlp.branches == IA_BRANCHES_SHARED;
-}
+// every fp16 decoder: the shared trunk (RGB or SH head) and the per-attribute branches
+bool backward_supported(const ia_decoder* dec) { return dec->mlp.dtype == IA_DTYPE_F16; }
 }  // namespace
 
 ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_t N, size_t* bytes) {
     if (!dec || !bytes) return fail(IA_ERR_INVALID_ARG, "null argument");
     if (N < 0) return fail(IA_ERR_INVALID_ARG, "N must be >= 0");
     if (!backward_supported(dec))
-        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoders (RGB or SH head)");
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the fp16 decoders");
     *bytes = ia::decode_bwd_layout(dec->lv, N).total;
     return IA_OK;
 }
@@ -406,12 +405,12 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
     if (!dec) return fail(IA_ERR_INVALID_ARG, "decoder is null");
     if (!dec->ready) return fail(IA_ERR_INVALID_ARG, "decoder parameters not set");
     if (!backward_supported(dec))
-        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the shared-trunk fp16 decoders (RGB or SH head)");
+        return fail(IA_ERR_UNSUPPORTED, "the decode backward supports the fp16 decoders");
     if (pos_stride != 3 && pos_stride != 4) return fail(IA_ERR_INVALID_ARG, "pos_stride must be 3 or 4");
     if (pos_stride == 3 && !std::isfinite(t)) return fail(IA_ERR_INVALID_ARG, "t must be finite");
     if (N < 0 || N > ((int64_t)1 << 40)) return fail(IA_ERR_INVALID_ARG, "N must be in [0, 2^40]");
     if (!grads || !grads->tables) return fail(IA_ERR_INVALID_ARG, "gradient outputs must be non-null");
-    for (int k = 0; k < dec->n_layers; ++k)
+    for (int k = 0; k < dec->n_mats; ++k)
         if (!grads->weights[k] || !grads->biases[k]) return fail(IA_ERR_INVALID_ARG, "null weight or bias gradient");
     if (N > 0) {
         if (!pos || !aligned(pos, 4)) return fail(IA_ERR_INVALID_ARG, "positions must be a non-null fp32 array");
@@ -434,10 +433,15 @@ ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t po
     b.g_means = grad_means;
     b.g_pos = grad_pos;
     b.g_tables = grads->tables;
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < dec->n_mats; ++k) {
         b.g_W[k] = grads->weights[k];
         b.g_b[k] = grads->biases[k];
     }
+    if (dec->mlp.branches == IA_BRANCHES_PER_ATTRIBUTE)
+        for (int k = 0; k < dec->n_mats; ++k) {
+            b.Wbr[k] = static_cast<const _Float16*>(dec->W[k]);
+            b.bbr[k] = dec->b[k];
+        }
     b.ws = static_cast<unsigned char*>(ws);
     hipError_t e = ia::launch_decode_backward(b, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode backward launch");

@@ -554,6 +554,7 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
     IA_LAUNCH("normalize_kernel", normalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a,
               a.pos + off * a.stride, n, xt);
     if (!z) return hipGetLastError();  // features kept by the forward: normalisation only
+    if (a.h.F == 4) return launch_gather_f4(xt, n, a.h, a.tables, z, zstride, s);
     IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(kGatherPerBlock), 0, s,
               xt, n, nchunk, a.h, (const uint32_t*)a.tables, z, zstride);
     return hipGetLastError();

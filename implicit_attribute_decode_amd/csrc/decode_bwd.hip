@@ -30,7 +30,11 @@
 //                axis.  Each wave accumulates its weight and bias gradients in
 //                registers over all its Gaussians and adds them to its own
 //                slot of a partial buffer;
-//       dz       written to the scratch, fp32, [level][Gaussian] x 2 features.
+//       dz       written to the scratch, fp32, [level][Gaussian] x F features.
+//   mlp_bwd_branch_kernel  the same for one branch of the per-attribute
+//       decoder (F = 4, 64 -> 64 -> 64 -> out), one launch per branch: the
+//       branches' encoding gradients add up in dz, each branch's weight
+//       gradients are reduced after its launch.
 //   scatter_kernel  level-major like the gather, four lanes per (Gaussian,
 //       level), each with four of the 16 corners: dtable[corner] += w dz with
 //       float atomics; for positions dz/df_axis = sum_c (+-1) prod_{other
@@ -480,6 +484,410 @@ __global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_kernel(MlpBwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- per-attribute branches
+//
+// The paper-scale decoder (F = 4 encoding of 64 features, one GELU MLP
+// 64 -> 64 -> 64 -> out per attribute) differentiated one branch per launch:
+// the forward of branch BR recomputed exactly as mlp_branch_kernel runs it
+// (same A tiles, biases as the initial accumulators, fp16 hidden
+// activations), Eq. 11 of its own rows, the data and weight gradients as in
+// mlp_bwd_kernel, and its input gradient added into dz (branch 0 writes it).
+// Lane (q, c): Z[m] slots e < 4 are the four features of level 8 m + q, e >= 4
+// those of level 8 m + 4 + q; the dz tile ob holds inputs 16 ob + 4 q + e, the
+// four features of level 4 ob + q.
+__host__ __device__ constexpr int branch_out(int br, bool sh) { return br == 0 ? 3 : (br == 1 ? 4 : (br == 2 ? (sh ? 48 : 3) : 1)); }
+__host__ __device__ constexpr int branch_head_tiles(int br, bool sh) { return br == 2 && sh ? 3 : 1; }
+template <int HT>
+constexpr int branch_tile_slots() { return (4 * HT + 16 + 16) * 4; }
+template <int HT>
+constexpr int branch_bias_slots() { return 4 * HT + 16 + 16; }
+static_assert(branch_tile_slots<3>() + branch_bias_slots<3>() <= kDecodeBwdSlotFloats / 64, "partial slots hold a branch");
+
+struct BranchBwdArgs {
+    const _Float16* W[3];  // the branch's [64][64], [64][64], [out][64]
+    const float* b[3];
+    const uint2* z;        // [L][zstride] four fp16 per level
+    int64_t zstride;
+    const uint32_t* list;
+    const uint32_t* count;
+    int64_t off;
+    const float* gup;      // the branch's upstream gradient, [N][out] (or opacity [N])
+    float4* gz;            // [L][gzstride]
+    int64_t gzstride;
+    float* partial;        // [waves][kDecodeBwdSlotFloats]
+};
+
+__device__ __forceinline__ half4_t unpack4(uint2 v) { return unpack2(v.x, v.y); }
+
+template <bool GELU, int BR, bool SH>
+__global__ void __launch_bounds__(kBwdThreads, 1) mlp_bwd_branch_kernel(BranchBwdArgs a) {
+#pragma clang fp contract(fast)
+    constexpr int HT = branch_head_tiles(BR, SH), OUT = branch_out(BR, SH);
+    __shared__ float sWh[HT * 4 * 4 * 64];
+    __shared__ float sW2[4 * 4 * 4 * 64];
+    __shared__ float sW1[4 * 4 * 4 * 64];
+    __shared__ float sT[kBwdWaves][2][64 * kTS];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int q = lane >> 4, c = lane & 15;
+    const _Float16* W1 = a.W[0];
+    const _Float16* W2 = a.W[1];
+    const _Float16* Wh = a.W[2];
+    for (int k = threadIdx.x; k < HT * 4 * 4 * 64; k += kBwdThreads) {
+        const int l = k & 63, e = (k >> 6) & 3, rb = (k >> 8) & 3, ht = k >> 10, qq = l >> 4, cc = l & 15;
+        const int row = 16 * ht + 4 * qq + e;
+        sWh[k] = row < OUT ? (float)Wh[row * 64 + 16 * rb + cc] : 0.0f;
+    }
+    for (int k = threadIdx.x; k < 4 * 4 * 4 * 64; k += kBwdThreads) {
+        const int l = k & 63, e = (k >> 6) & 3, rb = (k >> 8) & 3, ob = k >> 10, qq = l >> 4, cc = l & 15;
+        sW2[k] = (float)W2[(16 * rb + 4 * qq + e) * 64 + 16 * ob + cc];
+        sW1[k] = (float)W1[(16 * rb + 4 * qq + e) * 64 + 16 * ob + cc];
+    }
+    __syncthreads();
+
+    half8_t A1[4][2], A2[4][2], A3[HT][2];
+    floatx4_t B1[4], B2[4], B3[HT];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            A1[rb][m] = a_tile32(W1, 64, 64, rb, m, q, c);
+            A2[rb][m] = a_tile32(W2, 64, 64, rb, m, q, c);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            B1[rb][e] = a.b[0][16 * rb + 4 * q + e];
+            B2[rb][e] = a.b[1][16 * rb + 4 * q + e];
+        }
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) A3[ht][m] = a_tile32(Wh, 64, OUT, ht, m, q, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) B3[ht][e] = (16 * ht + 4 * q + e) < OUT ? a.b[2][16 * ht + 4 * q + e] : 0.0f;
+    }
+
+    const int64_t wave = (int64_t)blockIdx.x * kBwdWaves + wv;
+    const int64_t nwaves = (int64_t)gridDim.x * kBwdWaves;
+    float* part = a.partial + wave * (int64_t)kDecodeBwdSlotFloats + lane;
+    floatx4_t accH[HT][4], accW2[4][4], accW1[4][4];
+    float gbh[HT][4], gb2[4][4], gb1[4][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            accH[ht][t] = floatx4_t{0, 0, 0, 0};
+            gbh[ht][t] = 0.0f;
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            accW2[r][t] = accW1[r][t] = floatx4_t{0, 0, 0, 0};
+            gb2[r][t] = gb1[r][t] = 0.0f;
+        }
+
+    float* sG = sT[wv][0];
+    float* sH = sT[wv][1];
+    const int64_t n = *a.count;
+    for (int64_t base = wave * 16; base < n; base += nwaves * 16) {
+        const int64_t kc = base + c;
+        const bool valid = kc < n;
+        const int64_t gi = a.list[valid ? kc : n - 1];
+        // ---------------- forward (as mlp_branch_kernel computes it)
+        half8_t Z[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            Z[m] = cat8(unpack4(a.z[(size_t)(8 * m + q) * a.zstride + gi]),
+                        unpack4(a.z[(size_t)(8 * m + 4 + q) * a.zstride + gi]));
+        floatx4_t P1[4], P2[4];
+        half8_t H1[2], H2[2];
+#pragma unroll
+        for (int mo = 0; mo < 2; ++mo) {
+            floatx4_t lo = B1[2 * mo], hi = B1[2 * mo + 1];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * mo][m], Z[m], lo, 0, 0, 0);
+                hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[2 * mo + 1][m], Z[m], hi, 0, 0, 0);
+            }
+            half8_t h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float d0, d1;
+                h[e] = (_Float16)act_fwd_grad<GELU>(lo[e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad<GELU>(hi[e], d1);
+                P1[2 * mo][e] = d0;
+                P1[2 * mo + 1][e] = d1;
+            }
+            H1[mo] = h;
+        }
+#pragma unroll
+        for (int mo = 0; mo < 2; ++mo) {
+            floatx4_t lo = B2[2 * mo], hi = B2[2 * mo + 1];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * mo][m], H1[m], lo, 0, 0, 0);
+                hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2[2 * mo + 1][m], H1[m], hi, 0, 0, 0);
+            }
+            half8_t h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float d0, d1;
+                h[e] = (_Float16)act_fwd_grad<GELU>(lo[e], d0);
+                h[4 + e] = (_Float16)act_fwd_grad<GELU>(hi[e], d1);
+                P2[2 * mo][e] = d0;
+                P2[2 * mo + 1][e] = d1;
+            }
+            H2[mo] = h;
+        }
+        float o[HT][4];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            floatx4_t acc = B3[ht];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[ht][0], H2[0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3[ht][1], H2[1], acc, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[ht][e] = acc[e];
+        }
+        // ---------------- Eq. 11 backward of this branch's rows r = 16 ht + 4 q + e
+        float go[HT][4];
+        const int64_t u = a.off + gi;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * ht + 4 * q + e;
+                go[ht][e] = valid && r < OUT ? a.gup[u * OUT + r] : 0.0f;
+            }
+        if constexpr (BR == 0) {  // scale: exp below the clip
+#pragma unroll
+            for (int e = 0; e < 4; ++e) go[0][e] = o[0][e] < 20.0f ? go[0][e] * expf(o[0][e]) : 0.0f;
+        } else if constexpr (BR == 1) {  // rotation: rows 0-3 all in lane group q = 0
+            const float rn = sqrtf(o[0][0] * o[0][0] + (o[0][1] * o[0][1] + o[0][2] * o[0][2] + o[0][3] * o[0][3]));
+            const float nrm = fmaxf(rn, 1e-12f);
+            float dot = 0.0f;
+            if (rn >= 1e-12f)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dot += go[0][e] * (o[0][e] / nrm);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) go[0][e] = (go[0][e] - dot * (o[0][e] / nrm)) / nrm;
+        } else if constexpr (BR == 3 || (BR == 2 && !SH)) {  // sigmoid
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sg = sigmoid_f(o[0][e]);
+                go[0][e] = go[0][e] * sg * (1.0f - sg);
+            }
+        }  // SH coefficients: the head outputs themselves
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (16 * ht + 4 * q + e >= OUT) go[ht][e] = 0.0f;
+                gbh[ht][e] += go[ht][e];
+            }
+        // ---------------- head: dWh += go H2^T
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[(16 * ht + 4 * q + e) * kTS + c] = go[ht][e];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sH[(32 * m + 4 * q + e) * kTS + c] = (float)H2[m][e];
+                sH[(32 * m + 16 + 4 * q + e) * kTS + c] = (float)H2[m][4 + e];
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float bh[4];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) bh[hb] = sH[(16 * hb + c) * kTS + 4 * s + q];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const float ag = sG[(16 * ht + c) * kTS + 4 * s + q];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) accH[ht][hb] = mfma4(ag, bh[hb], accH[ht][hb]);
+            }
+        }
+        wave_lds_sync();
+        floatx4_t D[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            D[rb] = floatx4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) D[rb] = mfma4(sWh[((ht * 4 + rb) * 4 + e) * 64 + lane], go[ht][e], D[rb]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                D[rb][e] *= P2[rb][e];
+                gb2[rb][e] += D[rb][e];
+            }
+        // ---------------- layer 2: dW2 += da2 H1^T
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[(16 * rb + 4 * q + e) * kTS + c] = D[rb][e];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sH[(32 * m + 4 * q + e) * kTS + c] = (float)H1[m][e];
+                sH[(32 * m + 16 + 4 * q + e) * kTS + c] = (float)H1[m][4 + e];
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float bh[4];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) bh[hb] = sH[(16 * hb + c) * kTS + 4 * s + q];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const float ag = sG[(16 * rb + c) * kTS + 4 * s + q];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) accW2[rb][hb] = mfma4(ag, bh[hb], accW2[rb][hb]);
+            }
+        }
+        wave_lds_sync();
+        floatx4_t E[4];
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) {
+            E[ob] = floatx4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) E[ob] = mfma4(sW2[((ob * 4 + rb) * 4 + e) * 64 + lane], D[rb][e], E[ob]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                E[rb][e] *= P1[rb][e];
+                gb1[rb][e] += E[rb][e];
+            }
+        // ---------------- layer 1: dW1 += da1 z^T (64 inputs: four 16-wide k tiles)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sG[(16 * rb + 4 * q + e) * kTS + c] = E[rb][e];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sH[(32 * m + 4 * q + e) * kTS + c] = (float)Z[m][e];
+                sH[(32 * m + 16 + 4 * q + e) * kTS + c] = (float)Z[m][4 + e];
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float bz[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) bz[kb] = sH[(16 * kb + c) * kTS + 4 * s + q];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const float ag = sG[(16 * rb + c) * kTS + 4 * s + q];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) accW1[rb][kb] = mfma4(ag, bz[kb], accW1[rb][kb]);
+            }
+        }
+        wave_lds_sync();
+        // dz = W1^T da1, added into this level's four features
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) {
+            floatx4_t G = {0, 0, 0, 0};
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G = mfma4(sW1[((ob * 4 + rb) * 4 + e) * 64 + lane], E[rb][e], G);
+            if (valid) {
+                float4* dst = a.gz + (size_t)(4 * ob + q) * a.gzstride + kc;
+                float4 v = make_float4(G[0], G[1], G[2], G[3]);
+                if (BR > 0) {
+                    const float4 w = *dst;
+                    v = make_float4(w.x + v.x, w.y + v.y, w.z + v.z, w.w + v.w);
+                }
+                *dst = v;
+            }
+        }
+    }
+    {
+        int j = 0;
+#pragma unroll
+        for (int t = 0; t < 4 * HT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = accH[t >> 2][t & 3][e];
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = accW2[t >> 2][t & 3][e];
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = accW1[t >> 2][t & 3][e];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = gbh[ht][e];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = gb2[t][e];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[64 * j++] = gb1[t][e];
+    }
+}
+
+// As mlp_bwd_reduce_kernel for one branch (64 inputs, HT head tiles of which
+// OUT rows are real); add != 0 adds into the outputs (later chunks) instead of
+// overwriting them.
+template <int HT, int OUT>
+__global__ void __launch_bounds__(256) branch_bwd_reduce_kernel(const float* partial, int nwaves, float* gW1,
+                                                                float* gW2, float* gWh, float* gb1, float* gb2,
+                                                                float* gbh, int add) {
+    constexpr int kT = branch_tile_slots<HT>(), kB = branch_bias_slots<HT>();
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const int stride = kDecodeBwdSlotFloats;
+    float* dst = nullptr;
+    float s = 0.0f;
+    if (t < kT * 64) {
+        const int j = t >> 6, lane = t & 63, q = lane >> 4, c = lane & 15, e = j & 3, tile = j >> 2;
+        for (int w = 0; w < nwaves; ++w) s += partial[(size_t)w * stride + t];
+        if (tile < 4 * HT) {
+            const int row = 16 * (tile >> 2) + 4 * q + e;
+            if (row < OUT) dst = gWh + row * 64 + 16 * (tile & 3) + c;
+        } else if (tile < 4 * HT + 16) {
+            const int rb = (tile - 4 * HT) >> 2, hb = (tile - 4 * HT) & 3;
+            dst = gW2 + (16 * rb + 4 * q + e) * 64 + 16 * hb + c;
+        } else {
+            const int rb = (tile - 4 * HT - 16) >> 2, kb = (tile - 4 * HT - 16) & 3;
+            dst = gW1 + (16 * rb + 4 * q + e) * 64 + 16 * kb + c;
+        }
+    } else {
+        const int u = t - kT * 64;
+        if (u >= kB * 4) return;
+        const int jb = u >> 2, q = u & 3;
+        for (int w = 0; w < nwaves; ++w)
+            for (int c = 0; c < 16; ++c) s += partial[(size_t)w * stride + (kT + jb) * 64 + 16 * q + c];
+        if (jb < 4 * HT) {
+            const int row = 16 * (jb >> 2) + 4 * q + (jb & 3);
+            if (row < OUT) dst = gbh + row;
+        } else if (jb < 4 * HT + 16) {
+            const int rb = (jb - 4 * HT) >> 2, e = (jb - 4 * HT) & 3;
+            dst = gb2 + 16 * rb + 4 * q + e;
+        } else {
+            const int rb = (jb - 4 * HT - 16) >> 2, e = (jb - 4 * HT - 16) & 3;
+            dst = gb1 + 16 * rb + 4 * q + e;
+        }
+    }
+    if (dst) *dst = add ? *dst + s : s;
+}
+
 // First stage of the partial sums: block (slot j, group g) adds the slot of
 // waves [g W, (g + 1) W), W = waves / groups, in wave order, lane by lane.
 __global__ void __launch_bounds__(64) mlp_bwd_group_kernel(const float* partial, int waves_per_group,
@@ -550,8 +958,9 @@ constexpr int kAggMaxRes = 640;
 // slots, 512 or 768 on 2048, and 192 on 1024 measured slower
 constexpr int kAggRounds = 6;
 
-__device__ __forceinline__ void agg_add(uint32_t* key, float* v0, float* v1, uint32_t idx, float a, float b,
-                                        float* gt) {
+// F features per entry: feature f of slot k at v[f * kAggSlots + k].
+template <int F>
+__device__ __forceinline__ void agg_add(uint32_t* key, float* v, uint32_t idx, const float (&a)[F], float* gt) {
     uint32_t slot = (idx * 2654435761u) >> (32 - kAggBits);
     for (int p = 0; p < kAggProbes; ++p) {
         // a set key never changes: a plain read settles most probes, the
@@ -559,46 +968,46 @@ __device__ __forceinline__ void agg_add(uint32_t* key, float* v0, float* v1, uin
         uint32_t old = key[slot];
         if (old == kAggEmpty) old = atomicCAS(&key[slot], kAggEmpty, idx);
         if (old == kAggEmpty || old == idx) {
-            atomicAdd(&v0[slot], a);
-            atomicAdd(&v1[slot], b);
+#pragma unroll
+            for (int f = 0; f < F; ++f) atomicAdd(&v[f * kAggSlots + slot], a[f]);
             return;
         }
         slot = (slot + 1) & (kAggSlots - 1);
     }
-    atomicAdd(gt + 2 * (size_t)idx, a);
-    atomicAdd(gt + 2 * (size_t)idx + 1, b);
+#pragma unroll
+    for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, a[f]);
 }
 
 // Eq. 9 and Eq. 7 backward, level-major as the gather, levels level0 + 0, 1,
 // ...  Lane s of a group of four takes the x/y corner (s & 1, s >> 1) and its
-// four z/t corners.  AGG: combine per entry in LDS first (every thread of a
-// block reaches the final barrier: the only early exit is block-uniform).
-template <bool POS, bool AGG>
+// four z/t corners.  F features per table entry (2, or 4 for the paper-scale
+// encoder; gz holds F floats per level and Gaussian).  AGG: combine per entry
+// in LDS first (every thread of a block reaches the final barrier: the only
+// early exit is block-uniform).
+template <int F, bool POS, bool AGG>
 __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const float* pos, int stride,
                                                       const uint32_t* list, const uint32_t* count, int nchunk,
                                                       int level0, HashLevels h, const uint32_t* tables,
-                                                      const float2* gz, int64_t zstride, float* gtab,
+                                                      const float* gz, int64_t zstride, float* gtab,
                                                       float4* gpos_part) {
 #pragma clang fp contract(fast)
+    static_assert(F == 2 || F == 4, "two or four features per entry");
     __shared__ uint32_t s_key[AGG ? kAggSlots : 1];
-    __shared__ float s_v0[AGG ? kAggSlots : 1], s_v1[AGG ? kAggSlots : 1];
+    __shared__ float s_v[AGG ? F * kAggSlots : 1];
     const int level = level0 + (int)(blockIdx.x / nchunk);
     constexpr int kRounds = AGG ? kAggRounds : 4;
     const int64_t first = (int64_t)(blockIdx.x % nchunk) * (64 * kRounds);
     const int64_t n = *count;  // Gaussians with a gradient, compacted
     if (first >= n) return;
     if constexpr (AGG) {
-        for (int k = threadIdx.x; k < kAggSlots; k += 256) {
-            s_key[k] = kAggEmpty;
-            s_v0[k] = 0.0f;
-            s_v1[k] = 0.0f;
-        }
+        for (int k = threadIdx.x; k < kAggSlots; k += 256) s_key[k] = kAggEmpty;
+        for (int k = threadIdx.x; k < F * kAggSlots; k += 256) s_v[k] = 0.0f;
         __syncthreads();
     }
     const int res = h.res_s[level], res_t = h.res_t[level];
     const bool dense = h.dense[level] != 0;
-    const uint32_t* tab = tables + (size_t)level * h.T;
-    float* gt = gtab + (size_t)level * h.T * 2;
+    const uint32_t* tab = tables + (size_t)level * h.T * (F / 2);
+    float* gt = gtab + (size_t)level * h.T * F;
     const int s = threadIdx.x & 3;
     const int bx = s & 1, by = s >> 1;
     const int sub = threadIdx.x >> 2;
@@ -608,7 +1017,18 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
         if (k >= n) break;  // uniform across each group of four lanes
         const int64_t i = list[k];  // chunk-local Gaussian
         const float4 p = xt[i];
-        const float2 g = gz[(size_t)level * zstride + k];
+        float g[F];
+        if constexpr (F == 2) {
+            const float2 v = reinterpret_cast<const float2*>(gz)[(size_t)level * zstride + k];
+            g[0] = v.x;
+            g[1] = v.y;
+        } else {
+            const float4 v = reinterpret_cast<const float4*>(gz)[(size_t)level * zstride + k];
+            g[0] = v.x;
+            g[1] = v.y;
+            g[2] = v.z;
+            g[3] = v.w;
+        }
         int cx, cy, cz, ct;
         float fx, fy, fz, ft;
         cell_axis(p.x, res, cx, fx);
@@ -635,7 +1055,10 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
         const float wxy = wx * wy;
         const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
         // no gradient at this level: nothing to add, no position term (uniform over the four lanes)
-        if (g.x == 0.0f && g.y == 0.0f) {
+        bool none = true;
+#pragma unroll
+        for (int f = 0; f < F; ++f) none = none && g[f] == 0.0f;
+        if (none) {
             if (POS && s == 0) gpos_part[(size_t)level * zstride + k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             continue;
         }
@@ -649,17 +1072,25 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
             const float w = (wxy * wz[bz]) * wt[bt];
             if (w != 0.0f) {
                 if constexpr (AGG) {
-                    agg_add(s_key, s_v0, s_v1, idx, w * g.x, w * g.y, gt);
+                    float wg[F];
+#pragma unroll
+                    for (int f = 0; f < F; ++f) wg[f] = w * g[f];
+                    agg_add<F>(s_key, s_v, idx, wg, gt);
                 } else {
-                    atomicAdd(gt + 2 * (size_t)idx, w * g.x);
-                    atomicAdd(gt + 2 * (size_t)idx + 1, w * g.y);
+#pragma unroll
+                    for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, w * g[f]);
                 }
             }
             if (POS) {
-                const uint32_t raw = tab[idx];
-                const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
-                const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
-                const float tg = v0 * g.x + v1 * g.y;
+                // the entry's features times the level's gradient
+                float tg = 0.0f;
+#pragma unroll
+                for (int f = 0; f < F; f += 2) {
+                    const uint32_t raw = tab[(F / 2) * (size_t)idx + f / 2];
+                    const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
+                    const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+                    tg += v0 * g[f] + v1 * g[f + 1];
+                }
                 const float wzt = wz[bz] * wt[bt];
                 dx += tg * (sx * wy) * wzt;
                 dy += tg * (wx * sy) * wzt;
@@ -702,10 +1133,9 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
         __syncthreads();
         for (int k = threadIdx.x; k < kAggSlots; k += 256) {
             const uint32_t idx = s_key[k];
-            if (idx != kAggEmpty) {
-                atomicAdd(gt + 2 * (size_t)idx, s_v0[k]);
-                atomicAdd(gt + 2 * (size_t)idx + 1, s_v1[k]);
-            }
+            if (idx != kAggEmpty)
+#pragma unroll
+                for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, s_v[f * kAggSlots + k]);
         }
     }
 }
@@ -893,6 +1323,79 @@ SortScratch sort_scratch(void* base, int64_t chunk) {
     return t;
 }
 
+// One branch: the fixed-order sum of its partials into its weight and bias
+// gradients (added after the first chunk).
+template <int BR, bool SH>
+hipError_t reduce_branch(const DecodeBwdArgs& b, const float* partial, bool add, hipStream_t s) {
+    constexpr int HT = branch_head_tiles(BR, SH), OUT = branch_out(BR, SH);
+    constexpr int kSlots = branch_tile_slots<HT>() + branch_bias_slots<HT>();
+    const int nwaves = kDecodeBwdBlocks * kBwdWaves;
+    float* groups = const_cast<float*>(partial) + (size_t)nwaves * kDecodeBwdSlotFloats;
+    IA_LAUNCH("mlp_bwd_group_kernel", mlp_bwd_group_kernel, dim3(kSlots, kDecodeBwdGroups), dim3(64), 0, s, partial,
+              nwaves / kDecodeBwdGroups, groups);
+    const int nred = branch_tile_slots<HT>() * 64 + branch_bias_slots<HT>() * 4;
+    const int k = 3 * BR;
+    IA_LAUNCH("branch_bwd_reduce_kernel", (branch_bwd_reduce_kernel<HT, OUT>), dim3((nred + 255) / 256), dim3(256),
+              0, s, groups, kDecodeBwdGroups, b.g_W[k], b.g_W[k + 1], b.g_W[k + 2], b.g_b[k], b.g_b[k + 1],
+              b.g_b[k + 2], add ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <bool SH>
+hipError_t reduce_branches_t(const DecodeBwdArgs& b, const float* partial, bool add, hipStream_t s) {
+    hipError_t e = reduce_branch<0, SH>(b, partial, add, s);
+    if (e == hipSuccess) e = reduce_branch<1, SH>(b, partial, add, s);
+    if (e == hipSuccess) e = reduce_branch<2, SH>(b, partial, add, s);
+    if (e == hipSuccess) e = reduce_branch<3, SH>(b, partial, add, s);
+    return e;
+}
+
+hipError_t reduce_branches(const DecodeBwdArgs& b, const float* partial, bool add, hipStream_t s) {
+    return b.fwd.sh_head ? reduce_branches_t<true>(b, partial, add, s) : reduce_branches_t<false>(b, partial, add, s);
+}
+
+// Branch BR over a chunk's active list, then its reduction (each branch
+// starts from zeroed partials: the kernel overwrites every slot).
+template <int BR, bool SH>
+hipError_t branch_bwd(const DecodeBwdArgs& b, BranchBwdArgs ba, float* partial, bool add, hipStream_t s) {
+    const int k = 3 * BR;
+    for (int l = 0; l < 3; ++l) {
+        ba.W[l] = b.Wbr[k + l];
+        ba.b[l] = b.bbr[k + l];
+    }
+    ba.gup = BR == 0 ? b.g_scales : (BR == 1 ? b.g_quats : (BR == 2 ? b.g_colors : b.g_opacity));
+    ba.partial = partial;
+    const bool gelu = b.fwd.act == IA_ACT_GELU;
+    auto kernel = gelu ? mlp_bwd_branch_kernel<true, BR, SH> : mlp_bwd_branch_kernel<false, BR, SH>;
+    IA_LAUNCH("mlp_bwd_branch_kernel", kernel, dim3(kDecodeBwdBlocks), dim3(kBwdThreads), 0, s, ba);
+    return reduce_branch<BR, SH>(b, partial, add, s);
+}
+
+template <bool SH>
+hipError_t branches_bwd_t(const DecodeBwdArgs& b, const BranchBwdArgs& ba, float* partial, bool add, hipStream_t s) {
+    hipError_t e = branch_bwd<0, SH>(b, ba, partial, add, s);
+    if (e == hipSuccess) e = branch_bwd<1, SH>(b, ba, partial, add, s);
+    if (e == hipSuccess) e = branch_bwd<2, SH>(b, ba, partial, add, s);
+    if (e == hipSuccess) e = branch_bwd<3, SH>(b, ba, partial, add, s);
+    return e;
+}
+
+// The four branches of one chunk: their input gradients accumulate in gz
+// (branch 0 first), their weight gradients are reduced per branch.
+hipError_t launch_branches_bwd(const DecodeBwdArgs& b, const uint2* z, int64_t zstride, const uint32_t* list,
+                               const uint32_t* count, int64_t off, float4* gz, int64_t gzstride, float* partial,
+                               bool add, hipStream_t s) {
+    BranchBwdArgs ba{};
+    ba.z = z;
+    ba.zstride = zstride;
+    ba.list = list;
+    ba.count = count;
+    ba.off = off;
+    ba.gz = gz;
+    ba.gzstride = gzstride;
+    return b.fwd.sh_head ? branches_bwd_t<true>(b, ba, partial, add, s) : branches_bwd_t<false>(b, ba, partial, add, s);
+}
+
 }  // namespace
 
 DecodeBwdLayout decode_bwd_layout(const HashLevels& h, int64_t N) {
@@ -908,8 +1411,8 @@ DecodeBwdLayout decode_bwd_layout(const HashLevels& h, int64_t N) {
         off = align256(off + bytes);
         return o;
     };
-    L.z = take((size_t)h.L * chunk * 4);
-    L.gz = take((size_t)h.L * chunk * sizeof(float2));
+    L.z = take((size_t)h.L * chunk * 2 * h.F);              // F fp16 per level
+    L.gz = take((size_t)h.L * chunk * sizeof(float) * h.F);  // F fp32 per level
     L.list = take((size_t)chunk * 4);
     L.boff = take((size_t)(chunk / kCompactItems) * 4);
     L.count = take(16);
@@ -923,7 +1426,8 @@ DecodeBwdLayout decode_bwd_layout(const HashLevels& h, int64_t N) {
 
 hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     const DecodeArgs& a = b.fwd;
-    const size_t tab_floats = (size_t)a.h.L * a.h.T * 2;
+    const int F = a.h.F;
+    const size_t tab_floats = (size_t)a.h.L * a.h.T * F;
     IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for((int64_t)tab_floats, 256, 8192)), dim3(256), 0,
               s, b.g_tables, (int64_t)tab_floats, (const float*)nullptr);
     if (b.g_pos && a.N > 0)
@@ -934,7 +1438,7 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     const SortScratch srt = sort_scratch(b.ws + lay.sort, chunk);
     float4* xt = reinterpret_cast<float4*>(b.ws + lay.xt);
     uint32_t* z = reinterpret_cast<uint32_t*>(b.ws + lay.z);
-    float2* gz = reinterpret_cast<float2*>(b.ws + lay.gz);
+    float* gz = reinterpret_cast<float*>(b.ws + lay.gz);
     // the compacted list of a chunk, per-block offsets and the count
     uint32_t* list = reinterpret_cast<uint32_t*>(b.ws + lay.list);
     uint32_t* boff = reinterpret_cast<uint32_t*>(b.ws + lay.boff);
@@ -952,7 +1456,7 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     m.gq = b.g_quats;
     m.gc = b.g_colors;
     m.go = b.g_opacity;
-    m.gz = gz;
+    m.gz = reinterpret_cast<float2*>(gz);
     m.partial = partial;
     const int ncol = a.sh_head ? 48 : 3;
     int first = 1;
@@ -961,8 +1465,11 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         // features kept by the forward ([L][N]) or recomputed into the scratch ([L][chunk])
         hipError_t e = launch_decode_features(a, off, n, xt, a.features ? nullptr : z, chunk, s);
         if (e != hipSuccess) return e;
-        m.z = a.features ? a.features + off : z;
-        m.zstride = a.features ? a.N : chunk;
+        // F = 2: one word per (level, Gaussian); F = 4: two
+        const uint32_t* zc = a.features ? a.features + off * (F / 2) : z;
+        const int64_t zstride = a.features ? a.N : chunk;
+        m.z = zc;
+        m.zstride = zstride;
         const int nb = (int)((n + kCompactItems - 1) / kCompactItems);
         IA_LAUNCH("active_count_kernel", active_count_kernel, dim3(nb), dim3(256), 0, s, b.g_scales, b.g_quats,
                   b.g_colors, b.g_opacity, ncol, off, n, boff);
@@ -979,9 +1486,15 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         m.off = off;
         m.first = first;
         first = 0;
-        auto kernel = a.sh_head ? (m.gelu ? mlp_bwd_kernel<true, 4> : mlp_bwd_kernel<false, 4>)
-                                : (m.gelu ? mlp_bwd_kernel<true, 1> : mlp_bwd_kernel<false, 1>);
-        IA_LAUNCH("mlp_bwd_kernel", kernel, dim3(kDecodeBwdBlocks), dim3(kBwdThreads), 0, s, m);
+        if (a.branches) {
+            hipError_t be = launch_branches_bwd(b, reinterpret_cast<const uint2*>(zc), zstride, list, count, off,
+                                                reinterpret_cast<float4*>(gz), chunk, partial, off > 0, s);
+            if (be != hipSuccess) return be;
+        } else {
+            auto kernel = a.sh_head ? (m.gelu ? mlp_bwd_kernel<true, 4> : mlp_bwd_kernel<false, 4>)
+                                    : (m.gelu ? mlp_bwd_kernel<true, 1> : mlp_bwd_kernel<false, 1>);
+            IA_LAUNCH("mlp_bwd_kernel", kernel, dim3(kDecodeBwdBlocks), dim3(kBwdThreads), 0, s, m);
+        }
         const int nchunk = (int)((n + 255) / 256), nchunk_agg = (int)((n + 64 * kAggRounds - 1) / (64 * kAggRounds));
         const float* pos = a.pos + off * a.stride;
         float* gpos = b.g_pos ? b.g_pos + off * 3 : nullptr;
@@ -991,11 +1504,16 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         auto scatter = [&](auto pos_t, auto agg_t, int level0, int levels) {
             constexpr bool P = decltype(pos_t)::value, G = decltype(agg_t)::value;
             const int nc = G ? nchunk_agg : nchunk;
-            if (levels > 0)
-                IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<P, G>),
-                          dim3((unsigned)(levels * nc)), dim3(256), 0,
-                          s, xt, pos, a.stride, list, count, nc, level0, a.h, (const uint32_t*)a.tables, gz,
-                          chunk, b.g_tables, pos_partial);
+            if (levels <= 0) return;
+            if (F == 4) {
+                IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<4, P, G>),
+                          dim3((unsigned)(levels * nc)), dim3(256), 0, s, xt, pos, a.stride, list, count, nc,
+                          level0, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial);
+            } else {
+                IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<2, P, G>),
+                          dim3((unsigned)(levels * nc)), dim3(256), 0, s, xt, pos, a.stride, list, count, nc,
+                          level0, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial);
+            }
         };
         if (b.g_pos) {
             scatter(std::true_type{}, std::true_type{}, 0, nagg);
@@ -1011,7 +1529,9 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
         const int64_t nf = (int64_t)kDecodeBwdBlocks * kBwdWaves * kDecodeBwdSlotFloats;
         IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for(nf, 256, 8192)), dim3(256), 0, s, partial,
                   nf, (const float*)nullptr);
+        if (a.branches) return reduce_branches(b, partial, false, s);
     }
+    if (a.branches) return hipGetLastError();  // reduced after every chunk
     // fixed-order two-stage sum of the per-wave partials (deterministic)
     const int nwaves = kDecodeBwdBlocks * kBwdWaves;
     float* groups = partial + (size_t)nwaves * kDecodeBwdSlotFloats;

@@ -118,10 +118,11 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
 // Backward of the fp16 decode: one persistent grid of kDecodeBwdBlocks blocks
 // of four waves; each wave owns a slot of kDecodeBwdSlotFloats floats in the
 // workspace's partials (148 x 64 used by the RGB head, 208 x 64 by the SH
-// colour head), followed by kDecodeBwdGroups slots of group sums.
+// colour head, up to 220 x 64 by one branch of the per-attribute decoder),
+// followed by kDecodeBwdGroups slots of group sums.
 constexpr int kDecodeBwdBlocks = 256;
 constexpr int kDecodeBwdGroups = 16;
-constexpr int kDecodeBwdSlotFloats = 208 * 64;
+constexpr int kDecodeBwdSlotFloats = 224 * 64;
 constexpr int64_t kDecodeBwdPartialFloats = ((int64_t)kDecodeBwdBlocks * 4 + kDecodeBwdGroups) * kDecodeBwdSlotFloats;
 
 // Byte offsets of the backward's scratch inside a workspace (chunks of at
@@ -143,9 +144,13 @@ struct DecodeBwdArgs {
     const float* g_opacity;   // [N]
     const float* g_means;     // [N,3] added into g_pos, or null
     float* g_pos;             // [N,3] out, or null (no position gradient)
-    float* g_tables;          // [L][T][2] out
-    float* g_W[3];            // [64][32], [64][64], [11 or 56][64] out
-    float* g_b[3];            // [64], [64], [11 or 56] out
+    float* g_tables;          // [L][T][F] out
+    // shared trunk: g_W[0..2] = [64][32], [64][64], [11 or 56][64]; per-attribute
+    // branches: g_W[3 br + l] = [64][64], [64][64], [out_br][64]; the same for g_b
+    float* g_W[kMaxDecoderMats];
+    float* g_b[kMaxDecoderMats];
+    const _Float16* Wbr[kMaxDecoderMats];  // per-attribute branches: the fp16 weights, branch-major
+    const float* bbr[kMaxDecoderMats];
     unsigned char* ws;        // caller's workspace, decode_bwd_layout(h, N).total bytes
 };
 

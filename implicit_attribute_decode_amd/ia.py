@@ -82,7 +82,7 @@ class RenderAux(C.Structure):
 
 
 class DecoderGrads(C.Structure):
-    _fields_ = [("tables", C.c_void_p), ("weights", C.c_void_p * 4), ("biases", C.c_void_p * 4)]
+    _fields_ = [("tables", C.c_void_p), ("weights", C.c_void_p * 12), ("biases", C.c_void_p * 12)]
 
 
 class GaussianGrads(C.Structure):

@@ -115,9 +115,10 @@ class Decoder:
     def backward(self, pos: torch.Tensor, grad_attr: dict, t: float | None = None, grad_means=None,
                  want_pos: bool = True, features: torch.Tensor | None = None) -> dict:
         """Gradients of the decode of pos ([N,3] at time t, or [N,4] xyzt)
-        for upstream dL/d{scales, quats, colors (RGB head) or sh [N,16,3] (SH
-        colour head), opacity}.  Returns tables
-        [L,T,F], weights and biases (lists, fp32, shaped like the parameters)
+        for upstream dL/d{scales, quats, colors (RGB) or sh [N,16,3] (SH
+        colour), opacity}.  Every fp16 decoder: the shared trunk and the
+        per-attribute branches.  Returns tables [L,T,F], weights and biases
+        (lists in the order of the parameters, fp32, shaped like them)
         and, with want_pos, pos [N,3] = grad_means + the decoder's share."""
         N = int(pos.shape[0])
         stride = int(pos.shape[1])
@@ -127,8 +128,9 @@ class Decoder:
                    weights=[torch.empty(w.shape, dtype=torch.float32, device=self.device) for w in self._W],
                    biases=[torch.empty(b.shape, dtype=torch.float32, device=self.device) for b in self._b])
         out["pos"] = torch.empty((N, 3), device=self.device) if want_pos else None
-        G = ia.DecoderGrads(ia._ptr(out["tables"]), (ia.C.c_void_p * 4)(*[ia._ptr(w) for w in out["weights"]]),
-                            (ia.C.c_void_p * 4)(*[ia._ptr(b) for b in out["biases"]]))
+        wp = [ia._ptr(w) for w in out["weights"]] + [None] * (12 - len(out["weights"]))
+        bp = [ia._ptr(b) for b in out["biases"]] + [None] * (12 - len(out["biases"]))
+        G = ia.DecoderGrads(ia._ptr(out["tables"]), (ia.C.c_void_p * 12)(*wp), (ia.C.c_void_p * 12)(*bp))
         up = ia.gaussians(scales=grad_attr["scales"], quats=grad_attr["quats"], colors=grad_attr.get("colors"),
                           sh=grad_attr.get("sh"), opacity=grad_attr["opacity"])
         ia.ia_decode_backward(self.handle, pos, stride, N, float(t or 0.0), up, grad_means, out["pos"], G, features,

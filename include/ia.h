@@ -233,18 +233,22 @@ IA_API ia_status ia_decode_keep(const ia_decoder* dec, const float* pos, int32_t
                                 const ia_gaussians* out, void* features, size_t features_bytes, void* ws,
                                 size_t ws_bytes, void* side_stream, void* stream);
 
-/* Gradients of the decoder parameters (device, fp32, overwritten). */
+/* Gradients of the decoder parameters (device, fp32, overwritten), one per
+ * weight matrix in the order ia_decoder_set_params takes them: the shared
+ * trunk's n_hidden + 1 layers, or the per-attribute decoder's 12 (branch by
+ * branch: scale, rotation, colour, opacity; three layers each). */
 typedef struct {
-    float* tables;     /* [L][2^log2T][F], whatever the table dtype          */
-    float* weights[4]; /* layer k: [out][in] (n_hidden + 1 used)             */
-    float* biases[4];  /* layer k: [out]                                     */
+    float* tables;      /* [L][2^log2T][F], whatever the table dtype         */
+    float* weights[12]; /* matrix k: [out][in]                               */
+    float* biases[12];  /* matrix k: [out]                                   */
 } ia_decoder_grads;
 
 /* Bytes of workspace ia_decode_backward needs for N Gaussians: per chunk of
  * min(N, 2^21) Gaussians (rounded up to a multiple of 4096) the recomputed
  * encoding, its gradient, the chunk's active list and spatial sort, the
  * normalised positions and the per-level position shares (484 bytes per
- * Gaussian at L = 16), plus 55 MB of weight-gradient partials.
+ * Gaussian at L = 16, F = 2; 676 at F = 4), plus 60 MB of weight-gradient
+ * partials.
  * Errors: INVALID_ARG, UNSUPPORTED (decoders without a backward). */
 IA_API ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_t N, size_t* bytes);
 
@@ -270,10 +274,12 @@ IA_API ia_status ia_decode_backward_workspace_size(const ia_decoder* dec, int64_
  *              N) bytes, 256-byte aligned.
  * The forward is recomputed exactly as the decode computes it (fp16 hidden
  * activations); the backward runs in fp32 (v_mfma_f32_16x16x4_f32), treating
- * the fp16 roundings as the identity.  Supported: the shared-trunk fp16
- * decoders with the RGB head or the SH colour head ([SPIN] §3.3: the colour
- * decoder regresses the 48 coefficients, so their gradient passes unchanged
- * to the head outputs).
+ * the fp16 roundings as the identity.  Supported: every fp16 decoder -- the
+ * shared trunk with the RGB head or the SH colour head ([SPIN] §3.3: the
+ * colour decoder regresses the 48 coefficients, so their gradient passes
+ * unchanged to the head outputs), and the per-attribute decoder of §3.3 (one
+ * MLP per attribute over the F = 4 encoding; the encoding's gradient is the
+ * sum of the four branches').
  * Errors: INVALID_ARG, UNSUPPORTED (other decoders), WORKSPACE_TOO_SMALL,
  * DEVICE. */
 IA_API ia_status ia_decode_backward(const ia_decoder* dec, const float* pos, int32_t pos_stride, int64_t N, float t,

@@ -11,6 +11,11 @@ check): a gradient array X of the parameters is compared as
     |X_gpu - X_oracle| <= 1e-3 |X_oracle| + 1e-4 max|X_oracle|,
 the position gradient per point as
     |g_gpu - g_oracle| <= 2e-3 |g_oracle| + 1e-4 max|g_oracle| (vector norms).
+A flipped fp16 activation errs by 2^-11 of its own term, not of the entry's
+sum: where few Gaussians contribute (the per-attribute decoder at n <= 1000)
+and their terms cancel, |X_oracle| in the relative part is replaced by the
+sum over Gaussians of each Gaussian's |X_oracle| (the oracle run one Gaussian
+at a time), which bounds every term.
 """
 import numpy as np
 import pytest
@@ -62,11 +67,49 @@ def _gpu_backward(D, pos, up, t=None, grad_means=None, want_pos=True):
     return out
 
 
-def _compare(tag, dec, out, ref, pos_ref=None):
-    _close(f"{tag} tables", host(out["tables"]).reshape(-1), ref["g_tables"].reshape(-1), 1e-3, 1e-4)
-    for l in range(len(ref["g_weights"])):
-        _close(f"{tag} W{l}", host(out["weights"][l]), ref["g_weights"][l], 1e-3, 1e-4)
-        _close(f"{tag} b{l}", host(out["biases"][l]), ref["g_biases"][l], 1e-3, 1e-4)
+def _close_terms(tag, a, b, terms, rtol, afrac):
+    """As _close with the relative part taken of `terms` (>= |b|)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = np.abs(b).max()
+    lim = rtol * terms + afrac * scale
+    ratio = float((np.abs(a - b) / np.maximum(lim, 1e-300)).max())
+    say(f"[{tag}] max|ref| {scale:.3e} worst err/limit {ratio:.3f} (term sums)")
+    assert ratio <= 1.0, (tag, ratio)
+
+
+def _term_sums(dec, pos, up):
+    """Per parameter entry, the sum over Gaussians of |the oracle's gradient
+    of that Gaussian alone|."""
+    acc = None
+    for g in range(pos.shape[0]):
+        r = O.decode_grad(dec, pos[g:g + 1].astype(np.float64), mode=3, grads={k: v[g:g + 1] for k, v in up.items()})
+        one = dict(g_tables=np.abs(r["g_tables"]), g_weights=[np.abs(w) for w in r["g_weights"]],
+                   g_biases=[np.abs(b) for b in r["g_biases"]])
+        if acc is None:
+            acc = one
+        else:
+            acc["g_tables"] += one["g_tables"]
+            for l in range(len(acc["g_weights"])):
+                acc["g_weights"][l] += one["g_weights"][l]
+                acc["g_biases"][l] += one["g_biases"][l]
+    return acc
+
+
+def _compare(tag, dec, out, ref, pos_ref=None, terms=None):
+    if terms is None:
+        _close(f"{tag} tables", host(out["tables"]).reshape(-1), ref["g_tables"].reshape(-1), 1e-3, 1e-4)
+        for l in range(len(ref["g_weights"])):
+            _close(f"{tag} W{l}", host(out["weights"][l]), ref["g_weights"][l], 1e-3, 1e-4)
+            _close(f"{tag} b{l}", host(out["biases"][l]), ref["g_biases"][l], 1e-3, 1e-4)
+    else:
+        _close_terms(f"{tag} tables", host(out["tables"]).reshape(-1), ref["g_tables"].reshape(-1),
+                     terms["g_tables"].reshape(-1), 1e-3, 1e-4)
+        for l in range(len(ref["g_weights"])):
+            _close_terms(f"{tag} W{l}", host(out["weights"][l]), ref["g_weights"][l], terms["g_weights"][l],
+                         1e-3, 1e-4)
+            _close_terms(f"{tag} b{l}", host(out["biases"][l]), ref["g_biases"][l], terms["g_biases"][l],
+                         1e-3, 1e-4)
     if out["pos"] is not None:
         g = host(out["pos"]).astype(np.float64)
         o = ref["g_pos"] if pos_ref is None else pos_ref
@@ -313,7 +356,7 @@ def test_sh_head_backward_only_sh_gradients_count():
     assert float(np.abs(host(out["pos"])[rest]).max()) == 0.0
 
 
-def test_sh_head_backward_is_deterministic_and_paper_decoder_unsupported():
+def test_sh_head_backward_is_deterministic():
     dec = S.single_decoder_sh()
     rng = np.random.default_rng(76)
     n = 5000
@@ -326,8 +369,115 @@ def test_sh_head_backward_is_deterministic_and_paper_decoder_unsupported():
     for l in range(3):
         assert torch.equal(a["weights"][l], b["weights"][l]) and torch.equal(a["biases"][l], b["biases"][l])
     assert torch.equal(a["pos"], b["pos"])
-    P = Decoder(S.paper_decoder(log2T=12))
-    with pytest.raises(ia.IAError) as e:
-        P.backward(torch.zeros((4, 4), device="cuda"),
-                   {k: torch.zeros((4, 48 if k == "sh" else 4), device="cuda") for k in ("scales", "quats", "sh", "opacity")})
-    assert e.value.status == ia.IA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- per-attribute decoder
+
+def _upstream_paper(rng, n, sh):
+    return _upstream_sh(rng, n) if sh else _upstream(rng, n)
+
+
+@pytest.mark.parametrize("sh,n", [(True, 1), (True, 17), (True, 1000), (True, 20000), (False, 17), (False, 20000)])
+def test_paper_decoder_backward_matches_oracle(sh, n):
+    """The per-attribute decoder of SPIN-4DGS §3.3 (one GELU MLP 64 -> 64 ->
+    64 -> out per attribute over the F = 4 encoding, hidden width from §4):
+    twelve weight and bias gradients, the table gradient (the four branches'
+    encoding gradients summed) and the position gradient."""
+    dec = S.paper_decoder(log2T=12, sh=sh)
+    rng = np.random.default_rng(80 + n + (1000 if sh else 0))
+    pos = _edge_xyzt(rng, n)
+    up = _upstream_paper(rng, n, sh)
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    assert len(out["weights"]) == 12
+    terms = _term_sums(dec, pos, up) if n <= 1000 else None
+    _compare(f"paper {'sh' if sh else 'rgb'} {n}", dec, out, ref, terms=terms)
+
+
+def test_paper_decoder_backward_one_attribute_at_a_time():
+    """Upstream gradients on one attribute only: the other branches' weight
+    and bias gradients are exactly zero, and the encoding's gradient is that
+    branch's alone (checked against the oracle)."""
+    dec = S.paper_decoder(log2T=12, sh=True)
+    rng = np.random.default_rng(85)
+    n = 8000
+    pos = _edge_xyzt(rng, n)
+    full = _upstream_sh(rng, n)
+    D = Decoder(dec)
+    for br, key in enumerate(("scales", "quats", "sh", "opacity")):
+        up = {k: (v if k == key else np.zeros_like(v)) for k, v in full.items()}
+        ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+        out = _gpu_backward(D, pos, up)
+        for k in range(12):
+            if k // 3 != br:
+                assert float(out["weights"][k].abs().max()) == 0.0 and float(out["biases"][k].abs().max()) == 0.0
+        _compare(f"paper only {key}", dec, out, ref)
+
+
+def test_paper_decoder_backward_chunks_kept_features_and_determinism():
+    """2^21 + 4097 points (two backward chunks, the branch gradients reduced
+    after each): the parameter gradients equal the sum of the two halves
+    computed separately; a backward from the encoding kept by the forward
+    equals one that recomputes it (weights and biases bit for bit); repeated
+    calls agree bit for bit except for the float-atomic table gradient."""
+    dec = S.paper_decoder(log2T=14, sh=True)
+    rng = np.random.default_rng(86)
+    n1 = 1 << 21
+    n = n1 + 4097
+    pos = np.empty((n, 4), np.float32)
+    pos[:, :3] = S.shell_points(rng, n, 3.0)
+    pos[:, 3] = rng.random(n)
+    up = _upstream_sh(rng, n)
+    D = Decoder(dec)
+    whole = _gpu_backward(D, pos, up)
+    whole = {k: ([x.clone() for x in v] if isinstance(v, list) else v.clone()) for k, v in whole.items()}
+    p1 = _gpu_backward(D, pos[:n1], {k: v[:n1] for k, v in up.items()})
+    p1 = {k: ([x.clone() for x in v] if isinstance(v, list) else v.clone()) for k, v in p1.items()}
+    p2 = _gpu_backward(D, pos[n1:], {k: v[n1:] for k, v in up.items()})
+    s = host(p1["tables"]).astype(np.float64) + host(p2["tables"])
+    _close("paper chunks tables", host(whole["tables"]).reshape(-1), s.reshape(-1), 1e-5, 1e-6)
+    for l in range(12):
+        _close(f"paper chunks W{l}", host(whole["weights"][l]), host(p1["weights"][l]).astype(np.float64)
+               + host(p2["weights"][l]), 1e-4, 1e-4)
+        _close(f"paper chunks b{l}", host(whole["biases"][l]), host(p1["biases"][l]).astype(np.float64)
+               + host(p2["biases"][l]), 1e-4, 1e-4)
+    wp = host(whole["pos"])
+    np.testing.assert_allclose(wp[:n1], host(p1["pos"]), rtol=1e-5, atol=1e-6 * np.abs(wp).max())
+    np.testing.assert_allclose(wp[n1:], host(p2["pos"]), rtol=1e-5, atol=1e-6 * np.abs(wp).max())
+    idx = np.sort(np.concatenate([rng.choice(n, 200, replace=False), [0, n1 - 1, n1, n - 1]]))
+    ref = O.decode_grad(dec, pos[idx].astype(np.float64), mode=3, grads={k: v[idx] for k, v in up.items()})
+    err = np.linalg.norm(wp[idx].astype(np.float64) - ref["g_pos"], axis=1)
+    nrm = np.linalg.norm(ref["g_pos"], axis=1)
+    assert (err <= 2e-3 * nrm + 1e-4 * nrm.max()).all()
+    # kept encoding and repeat
+    x = cuda(pos)
+    _, feats = D.decode_keep(x)
+    g = {k: cuda(v.astype(np.float32)) for k, v in up.items()}
+    kept = D.backward(x, g, features=feats)
+    torch.cuda.synchronize()
+    for l in range(12):
+        assert torch.equal(kept["weights"][l], whole["weights"][l]) and torch.equal(kept["biases"][l], whole["biases"][l])
+    assert torch.equal(kept["pos"], whole["pos"])
+    _close("paper kept tables", host(kept["tables"]).reshape(-1), host(whole["tables"]).reshape(-1), 1e-5, 1e-6)
+
+
+def test_paper_decoder_backward_zero_points_and_sparse():
+    dec = S.paper_decoder(log2T=12, sh=False)
+    D = Decoder(dec)
+    out = D.backward(torch.empty((0, 4), device="cuda"), {k: torch.empty(0, device="cuda") for k in UP})
+    torch.cuda.synchronize()
+    assert float(out["tables"].abs().max()) == 0.0
+    assert len(out["weights"]) == 12
+    assert all(float(w.abs().max()) == 0.0 for w in out["weights"])
+    assert all(float(b.abs().max()) == 0.0 for b in out["biases"])
+    rng = np.random.default_rng(87)
+    n = 20000
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    idle = rng.random(n) < 0.8
+    for v in up.values():
+        v[idle] = 0.0
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(D, pos, up)
+    _compare("paper sparse", dec, out, ref)
+    assert np.all(host(out["pos"])[idle] == 0.0)
