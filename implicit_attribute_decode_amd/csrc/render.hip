@@ -1081,6 +1081,37 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
     if (LAST) p.last = take ? pos : p.last;
 }
 
+// Whether a staged Gaussian (ga = mean, A', B'; gbx = C'; power = A' dx^2 +
+// C' dy^2 + B' dx dy) can pass the per-pixel 3-sigma test at some pixel centre
+// of a wave, whose centres lie in [X0, X1] x [Y0, Y1].  q = -power is convex:
+// its minimum over the box is 0 when the box holds the mean, else it lies on
+// an edge, where q is a parabola in the free coordinate, minimised at its
+// vertex clamped to the edge.  The offsets a pixel computes lie in the box
+// the offsets of its corners span (rounding is monotonic), so a pixel whose
+// computed power is >= -4.5 has q <= 4.5 + e there, and the computed minimum
+// exceeds the exact one by at most e', with e, e' a few units of fp32
+// rounding of M = |A'| dx^2 + |C'| dy^2 + |B' dx dy| over the box (about 15 u
+// M in all, u = 2^-24).  The test allows 4e-6 M + 1e-4: it never rejects a
+// Gaussian the per-pixel test would take, only spares the wave the Gaussians
+// that cannot reach it.  Degenerate or non-finite values pass.
+__device__ __forceinline__ bool may_reach(float4 ga, float gbx, float X0, float X1, float Y0, float Y1) {
+#pragma clang fp contract(fast)
+    const float x0 = X0 - ga.x, x1 = X1 - ga.x, y0 = Y0 - ga.y, y1 = Y1 - ga.y;
+    if (x0 <= 0.0f && x1 >= 0.0f && y0 <= 0.0f && y1 >= 0.0f) return true;
+    const float a = -ga.z, b = -ga.w, c = -gbx;
+    if (!(a > 1e-30f && c > 1e-30f)) return true;
+    const float ia = 0.5f / a, ic = 0.5f / c;
+    auto q = [&](float dx, float dy) { return (a * dx * dx + c * dy * dy) + b * dx * dy; };
+    auto clampf = [](float v, float lo, float hi) { return fminf(fmaxf(v, lo), hi); };
+    float m = q(x0, clampf(-b * x0 * ic, y0, y1));
+    m = fminf(m, q(x1, clampf(-b * x1 * ic, y0, y1)));
+    m = fminf(m, q(clampf(-b * y0 * ia, x0, x1), y0));
+    m = fminf(m, q(clampf(-b * y1 * ia, x0, x1), y1));
+    const float xm = fmaxf(fabsf(x0), fabsf(x1)), ym = fmaxf(fabsf(y0), fabsf(y1));
+    const float M = (a * xm * xm + c * ym * ym) + fabsf(b) * xm * ym;
+    return !(m > 4.5f + 4e-6f * M + 1e-4f);
+}
+
 // One block per 16x16 tile.  PX = 2: 128 threads, thread (col, row) shades
 // pixels (col, 2 row) and (col, 2 row + 1), which share dx and the dx terms
 // of power, so a wave covers a 16 x 8 pixel block; PX = 1: 256 threads, one
@@ -1089,8 +1120,10 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
 // step (the step would add alpha = 0 everywhere).
 // Gaussians of the tile's list are staged in LDS 256 at a time with the
 // conic pre-scaled by -1/2, -1, -1/2 (exact), so power = A' dx^2 + C' dy^2 +
-// B' dx dy.  A wave leaves a batch once all its pixels are saturated; the
-// block stops once all 256 are.
+// B' dx dy.  After staging, each wave marks with may_reach the batch's
+// Gaussians that can reach one of its pixels (four per lane, one ballot per
+// 64) and visits only those, in list order.  A wave leaves a batch once all
+// its pixels are saturated; the block stops once all 256 are.
 constexpr int kRasterBatch = 256;
 constexpr int kRasterCheck = 8;  // Gaussians between two saturation checks of a wave
 constexpr int64_t kRasterTwoPixelTiles = 8192;  // tiles per launch from which two pixels per thread pay
@@ -1113,6 +1146,10 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
     const int px = blockIdx.x * 16 + (threadIdx.x & 15);
     const int py0 = blockIdx.y * 16 + PX * (threadIdx.x >> 4);
     const float fx = (float)px + 0.5f;
+    // this wave's pixel centres: 16 columns, 4 PX rows
+    const int lane = threadIdx.x & 63;
+    const float wx0 = (float)(blockIdx.x * 16) + 0.5f, wx1 = wx0 + 15.0f;
+    const float wy0 = (float)(blockIdx.y * 16 + 4 * PX * (int)(threadIdx.x >> 6)) + 0.5f, wy1 = wy0 + (float)(4 * PX - 1);
     Pix p[PX];
     bool in[PX];
 #pragma unroll
@@ -1144,13 +1181,28 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
         __syncthreads();
         const int n = (int)min((uint32_t)kRasterBatch, rg.y - start);
         const uint32_t pos0 = start - rg.x + 1u;
+        uint64_t hit[kRasterBatch / 64];
+#pragma unroll
+        for (int r = 0; r < kRasterBatch / 64; ++r) {
+            const int j = r * 64 + lane;
+            hit[r] = r * 64 < n ? __ballot(j < n && may_reach(s_a[j], s_b[j].x, wx0, wx1, wy0, wy1)) : 0ull;
+        }
         // A wave whose pixels are all saturated leaves the batch; that is
-        // checked every kRasterCheck Gaussians (compositing ignores
-        // saturated pixels, so the check only saves work).
-        for (int j0 = 0; j0 < n; j0 += kRasterCheck) {
-            if (__ballot(!all_done()) == 0ull) break;
-            const int jn = n - j0 < kRasterCheck ? n : j0 + kRasterCheck;
-            for (int j = j0; j < jn; ++j) {
+        // checked before every kRasterCheck-th Gaussian it visits
+        // (compositing ignores saturated pixels, so the check only saves work).
+        bool live = true;
+        int since = 0;
+#pragma unroll
+        for (int r = 0; r < kRasterBatch / 64; ++r) {
+            uint64_t mm = hit[r];
+            while (live && mm != 0ull) {
+                if (since == 0 && __ballot(!all_done()) == 0ull) {
+                    live = false;
+                    break;
+                }
+                since = since + 1 == kRasterCheck ? 0 : since + 1;
+                const int j = r * 64 + (int)__builtin_ctzll(mm);
+                mm &= mm - 1ull;
                 const float4 ga = s_a[j];
                 const float4 gb = s_b[j];
                 const float gcb = s_c[j].x;
