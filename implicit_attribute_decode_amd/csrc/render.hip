@@ -456,7 +456,29 @@ struct OffsetArgs {
     uint32_t* bstart;  // per emission block: the Gaussian holding its first entry
 };
 
+// Frame offsets searched in LDS (the depth-ordered Gaussians of a block come
+// from any frame, so every lane searches on its own): up to this many frames,
+// with offsets below 2^32; beyond, the search reads global memory.
+constexpr int kLdsFrames = 2047;
+
+__device__ __forceinline__ int frame_of_lds(const uint32_t* fo, int F, uint32_t i) {
+    int lo = 0, hi = F - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (fo[mid] <= i)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
 __global__ void __launch_bounds__(kBlock) offsets_kernel(OffsetArgs a) {
+    __shared__ uint32_t s_fo[kLdsFrames + 1];
+    const bool lds_fo = a.F <= kLdsFrames && a.fo[a.F] <= (int64_t)0xffffffffu;
+    if (lds_fo)
+        for (int k = threadIdx.x; k <= a.F; k += kBlock) s_fo[k] = (uint32_t)a.fo[k];
+    __syncthreads();
     const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
     const bool live = j < a.nvis[0];
     ushort4 r = make_ushort4(0, 0, 0, 0);
@@ -475,7 +497,7 @@ __global__ void __launch_bounds__(kBlock) offsets_kernel(OffsetArgs a) {
     g.lo = (uint32_t)r.x | ((uint32_t)r.y << 16);
     g.hi = (uint32_t)r.z | ((uint32_t)r.w << 16);
     a.info[j] = g;
-    a.frame[j] = (uint32_t)frame_of(a.fo, a.F, g.idx);
+    a.frame[j] = (uint32_t)(lds_fo ? frame_of_lds(s_fo, a.F, g.idx) : frame_of(a.fo, a.F, g.idx));
     // emission blocks whose first entry lies in [off, stop)
     for (uint64_t b = (off + a.per - 1) / a.per; b * a.per < stop && b < a.nemit; ++b)
         a.bstart[b] = (uint32_t)j;
