@@ -1351,9 +1351,13 @@ RenderLayout render_layout(int64_t N, int frames, int W, int H, int64_t max_entr
     };
     L.sort_blocks_g = blocks(n1);
     L.sort_blocks_e = blocks(cap1);
-    // about 1024 emission blocks of a power of two entries each, kBlock..kEmitMax
+    // about 65536 emission blocks of a power of two entries each, kBlock..kEmitMax:
+    // a block's chunks of kBlock entries run one after another (each starts
+    // with a global read of Gaussian offsets), so short blocks keep that
+    // chain short (22.7M entries: 512 per block 0.157 ms, 2048 0.164 ms,
+    // 16384 0.209 ms; 256 per block 0.173 ms)
     L.emit_per = kBlock;
-    while (L.emit_per < kEmitMax && (int64_t)L.emit_per * 1024 < cap1) L.emit_per *= 2;
+    while (L.emit_per < kEmitMax && (int64_t)L.emit_per * 65536 < cap1) L.emit_per *= 2;
     L.nemit = (int)((cap1 + L.emit_per - 1) / L.emit_per);
     // coarse entries <= tile entries <= capacity, so items <= cap / kItemCoarse + regions
     L.max_items = (cap1 + kItemCoarse - 1) / kItemCoarse + L.nreg;
