@@ -39,11 +39,11 @@ GATHER_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES
 DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
 # HBM-side bytes per gather launch of this workload (positions in per-frame Morton order), from two
 # rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, each scaled by what the counter
-# reads for a plain device copy of known size).  Per Gaussian the gather's FETCH_SIZE counts 164.3 B and
-# its WRITE_SIZE 64.0 B; a 1 GiB copy counts 524,315 KiB of FETCH_SIZE for the 1 GiB it reads (x 2) and
-# 1,048,576 KiB of WRITE_SIZE for the 1 GiB it writes (x 1): 2 x 164.3 + 64.0 B per Gaussian, times the
+# reads for a plain device copy of known size).  Per Gaussian the gather's FETCH_SIZE counts 152.55 B and
+# its WRITE_SIZE 64.0 B; a 1 GiB copy counts 524,314 KiB of FETCH_SIZE for the 1 GiB it reads (x 2) and
+# 1,048,576 KiB of WRITE_SIZE for the 1 GiB it writes (x 1): 2 x 152.55 + 64.0 B per Gaussian, times the
 # 3.75M Gaussians of a mean launch.
-GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 164.3 + 64.0) * 3_750_000
+GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 152.55 + 64.0) * 3_750_000
 
 
 def log(*a):

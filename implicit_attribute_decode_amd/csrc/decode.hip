@@ -191,12 +191,15 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 //
 // normalize_kernel: Eq. 7-8 once per Gaussian -> x~ (fp32 x4) in the scratch.
 //
-// gather_f16_kernel: level-major.  Block b handles level b / nchunk and
+// gather_f16_kernel: level-major.  Block b handles level group b / nchunk and
 // Gaussians [256 (b % nchunk), +256), one lane per Gaussian.  Blocks are
 // dispatched in index order and spread round-robin over the XCDs, so at any
 // moment all XCDs work on the same level and that level's 2^log2T x 4-byte
 // table stays resident in every XCD's L2 instead of being fetched line by
-// line from HBM / Infinity Cache.  A lane computes its Gaussian's cell once
+// line from HBM / Infinity Cache.  The eight coarsest levels go four to a
+// block: their Gaussians touch few table lines (the four levels' working
+// sets share L2), and one load of the normalised position (a 16-byte read,
+// mostly from the Infinity Cache) then serves four levels instead of one.  A lane computes its Gaussian's cell once
 // and issues all its corner loads before using any (range-checked buffer
 // loads: a corner of zero weight, or a lane past the last Gaussian, reads
 // past the table, which returns zero without a memory request).  Consecutive
@@ -211,6 +214,16 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // rows 4q..4q+3 of column c.  Gaussians are the columns and neurons the rows.
 
 constexpr int kGatherPerBlock = 256;  // Gaussians per gather block, one lane each
+// Levels [0, kGroupedLevels) go kLevelGroup to a block (one position load for
+// all of them); the finer levels one to a block.
+constexpr int kGroupedLevels = 8;
+constexpr int kLevelGroup = 4;
+
+// Gather blocks per chunk of kGatherPerBlock Gaussians for L levels.
+int gather_groups(int L) {
+    const int gl = L < kGroupedLevels ? L : kGroupedLevels;
+    return (gl + kLevelGroup - 1) / kLevelGroup + (L - gl);
+}
 constexpr int kMlpBlocksPerCu = 1;    // MLP beside a gather: blocks per CU
 constexpr int kNormBlocksPerCu = 2;   // normalisation beside a gather: blocks per CU
 
@@ -307,13 +320,9 @@ __device__ __forceinline__ void gather_lane(const float4 p, bool valid, int res,
     }
 }
 
-__global__ void __launch_bounds__(kGatherPerBlock) gather_f16_kernel(const float4* xt, int64_t n, int nchunk,
-                                                                     HashLevels h, const uint32_t* tables,
-                                                                     uint32_t* zbuf, int64_t zstride) {
-    const int level = blockIdx.x / nchunk;
-    const int64_t i = (int64_t)(blockIdx.x % nchunk) * kGatherPerBlock + threadIdx.x;
-    const bool valid = i < n;
-    const float4 p = xt[valid ? i : n - 1];
+// One lane's gather of one level, stored as two packed fp16 features.
+__device__ __forceinline__ void gather_store(const float4 p, bool valid, int64_t i, int level, const HashLevels& h,
+                                             const uint32_t* tables, uint32_t* zbuf, int64_t zstride) {
     const __amdgpu_buffer_rsrc_t rt =
         __builtin_amdgcn_make_buffer_rsrc((void*)(tables + (size_t)level * h.T), (short)0, (int)(h.T * 4u),
                                           kBufferWord3);
@@ -326,6 +335,41 @@ __global__ void __launch_bounds__(kGatherPerBlock) gather_f16_kernel(const float
         const uint16_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);
         const uint16_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
         zbuf[(size_t)level * zstride + i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    }
+}
+
+// A full group of coarse levels L0 .. L0 + kLevelGroup - 1, compiled with its
+// level indices: all of its loads can be in flight together.
+template <int L0>
+__device__ __forceinline__ void gather_group(const float4 p, bool valid, int64_t i, const HashLevels& h,
+                                             const uint32_t* tables, uint32_t* zbuf, int64_t zstride) {
+#pragma unroll
+    for (int k = 0; k < kLevelGroup; ++k) gather_store(p, valid, i, L0 + k, h, tables, zbuf, zstride);
+}
+static_assert(kGroupedLevels == 2 * kLevelGroup, "two groups of coarse levels");
+
+__global__ void __launch_bounds__(kGatherPerBlock) gather_f16_kernel(const float4* xt, int64_t n, int nchunk,
+                                                                     HashLevels h, const uint32_t* tables,
+                                                                     uint32_t* zbuf, int64_t zstride) {
+    const int gl = h.L < kGroupedLevels ? h.L : kGroupedLevels;
+    const int ng = (gl + kLevelGroup - 1) / kLevelGroup;
+    const int grp = blockIdx.x / nchunk;
+    const int64_t i = (int64_t)(blockIdx.x % nchunk) * kGatherPerBlock + threadIdx.x;
+    const bool valid = i < n;
+    const float4 p = xt[valid ? i : n - 1];
+    if (grp < ng) {
+        // kLevelGroup coarse levels from one position load
+        if (gl == kGroupedLevels) {
+            if (grp == 0)
+                gather_group<0>(p, valid, i, h, tables, zbuf, zstride);
+            else
+                gather_group<kLevelGroup>(p, valid, i, h, tables, zbuf, zstride);
+        } else {  // fewer levels than two full groups
+            const int l1 = grp * kLevelGroup + kLevelGroup < gl ? grp * kLevelGroup + kLevelGroup : gl;
+            for (int l = grp * kLevelGroup; l < l1; ++l) gather_store(p, valid, i, l, h, tables, zbuf, zstride);
+        }
+    } else {
+        gather_store(p, valid, i, grp - ng + gl, h, tables, zbuf, zstride);
     }
 }
 
@@ -555,7 +599,7 @@ hipError_t launch_decode_features(const DecodeArgs& a, int64_t off, int64_t n, f
               a.pos + off * a.stride, n, xt);
     if (!z) return hipGetLastError();  // features kept by the forward: normalisation only
     if (a.h.F == 4) return launch_gather_f4(xt, n, a.h, a.tables, z, zstride, s);
-    IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)), dim3(kGatherPerBlock), 0, s,
+    IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(gather_groups(a.h.L) * nchunk)), dim3(kGatherPerBlock), 0, s,
               xt, n, nchunk, a.h, (const uint32_t*)a.tables, z, zstride);
     return hipGetLastError();
 }
@@ -702,7 +746,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
             if (a.h.F == 4) {
                 if ((e = launch_gather_f4(xt, n, a.h, a.tables, zb, zstride, s)) != hipSuccess) return e;
             } else {
-                IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(a.h.L * nchunk)),
+                IA_LAUNCH("gather_f16_kernel", gather_f16_kernel, dim3((unsigned)(gather_groups(a.h.L) * nchunk)),
                           dim3(kGatherPerBlock), 0, s, xt, n, nchunk, a.h, (const uint32_t*)a.tables, zb, zstride);
             }
             if (overlap) {
