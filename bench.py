@@ -39,11 +39,11 @@ GATHER_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES
 DECODE_BYTES_PER_GAUSSIAN = 16 + LEVELS * CORNERS * FEAT_BYTES + 44
 # HBM-side bytes per gather launch of this workload (positions in per-frame Morton order), from two
 # rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, each scaled by what the counter
-# reads for a plain device copy of known size).  Per Gaussian the gather's FETCH_SIZE counts 152.55 B and
+# reads for a plain device copy of known size).  Per Gaussian the gather's FETCH_SIZE counts 152.49 B and
 # its WRITE_SIZE 64.0 B; a 1 GiB copy counts 524,314 KiB of FETCH_SIZE for the 1 GiB it reads (x 2) and
-# 1,048,576 KiB of WRITE_SIZE for the 1 GiB it writes (x 1): 2 x 152.55 + 64.0 B per Gaussian, times the
+# 1,048,576 KiB of WRITE_SIZE for the 1 GiB it writes (x 1): 2 x 152.49 + 64.0 B per Gaussian, times the
 # 3.75M Gaussians of a mean launch.
-GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 152.55 + 64.0) * 3_750_000
+GATHER_TRAFFIC_BYTES_PER_LAUNCH = (2 * 152.49 + 64.0) * 3_750_000
 
 
 def log(*a):
@@ -427,31 +427,24 @@ def render_counts(step, xyzt, fo, cams, attrs, E) -> dict:
 
 
 def fetched_gather_bytes(xyzt, h) -> float:
-    """Bytes the hash gather fetches per Gaussian: the 16-byte position and 4
-    bytes per corner of non-zero weight (a corner's weight is zero when the
-    position sits exactly on a grid vertex of that axis), evaluated with the
-    fp32 operations of the normalisation and cell decision of Eq. 7-9."""
+    """Bytes the hash gather fetches per Gaussian: the 16-byte position and,
+    per level, the 8 corners (4 bytes each) of every temporal vertex with a
+    non-zero weight (one vertex when t sits exactly on it, else two),
+    evaluated with the fp32 operations of the time normalisation and cell
+    decision of Eq. 8-9.  (A wave loads a vertex for all its lanes when any
+    of them weights it; the Gaussians of a wave share one frame's time.)"""
     import torch
 
-    x, y, z, t = (xyzt[:, k].float() for k in range(4))
-    n2 = x * x + y * y
-    n2 = n2 + z * z
-    n = torch.sqrt(n2)
-    k = (2.0 - 1.0 / n) / n
-    inside = n <= 1.0
-    axes = [torch.where(inside, v, v * k) * 0.25 + 0.5 for v in (x, y, z)]
+    t = xyzt[:, 3].float()
     tn = ((t - h.t_min) / (h.t_max - h.t_min)).clamp(0.0, 1.0)
-    total = torch.zeros_like(x)
+    total = torch.zeros_like(t)
     for l in range(h.L):
         res = int(np.floor(h.base_res * h.growth ** l))
         res_t = h.temporal_res if h.temporal_res > 0 else res
-        c = torch.ones_like(x)
-        for v, r in ((axes[0], res), (axes[1], res), (axes[2], res), (tn, res_t)):
-            p = v * float(r - 1)
-            i = torch.floor(p).clamp(0, r - 2)
-            f = p - i
-            c = c * torch.where((f == 0.0) | (f == 1.0), 1.0, 2.0)
-        total += c
+        p = tn * float(res_t - 1)
+        i = torch.floor(p).clamp(0, res_t - 2)
+        f = p - i
+        total += 8.0 * torch.where((f == 0.0) | (f == 1.0), 1.0, 2.0)
     return 16.0 + 4.0 * float(total.mean().item())
 
 

@@ -199,10 +199,10 @@ __global__ void __launch_bounds__(256, 2) decode_f32_kernel(DecodeArgs a) {
 // line from HBM / Infinity Cache.  The eight coarsest levels go four to a
 // block: their Gaussians touch few table lines (the four levels' working
 // sets share L2), and one load of the normalised position (a 16-byte read,
-// mostly from the Infinity Cache) then serves four levels instead of one.  A lane computes its Gaussian's cell once
-// and issues all its corner loads before using any (range-checked buffer
-// loads: a corner of zero weight, or a lane past the last Gaussian, reads
-// past the table, which returns zero without a memory request).  Consecutive
+// mostly from the Infinity Cache) then serves four levels instead of one.
+// A lane computes its Gaussian's cell once and issues all its corner loads
+// before using any (range-checked buffer loads; the corners of a temporal
+// vertex no lane of the wave weights are not loaded).  Consecutive
 // lanes hold consecutive Gaussians, so when the positions of a frame are
 // stored in spatial order the lanes of a wave share the coarse levels' cache
 // lines.  Output z[level][i] = two fp16 features packed in 32 bits (RNE).
@@ -249,31 +249,32 @@ __device__ __forceinline__ void gather_lane(const float4 p, bool valid, int res,
     cell_axis(p.y, res, cy, fy);
     cell_axis(p.z, res, cz, fz);
     cell_axis(p.w, res_t, ct, ft);
+    // per-axis index terms in bytes (4 per entry): the factor distributes over
+    // the sum and, before the mask, over the XOR of the hash
     uint32_t tx[2], ty[2], tz[2], tt[2];
     if (DENSE) {
         const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
-        tx[0] = (uint32_t)cx;
-        tx[1] = tx[0] + 1u;
-        ty[0] = (uint32_t)cy * r;
-        ty[1] = ty[0] + r;
-        tz[0] = (uint32_t)cz * r2;
-        tz[1] = tz[0] + r2;
-        tt[0] = (uint32_t)ct * r3;
-        tt[1] = tt[0] + r3;
+        tx[0] = (uint32_t)cx * 4u;
+        tx[1] = tx[0] + 4u;
+        ty[0] = (uint32_t)cy * (r * 4u);
+        ty[1] = ty[0] + r * 4u;
+        tz[0] = (uint32_t)cz * (r2 * 4u);
+        tz[1] = tz[0] + r2 * 4u;
+        tt[0] = (uint32_t)ct * (r3 * 4u);
+        tt[1] = tt[0] + r3 * 4u;
     } else {
-        tx[0] = (uint32_t)cx * kP1;
-        tx[1] = (uint32_t)(cx + 1) * kP1;
-        ty[0] = (uint32_t)cy * kP2;
-        ty[1] = (uint32_t)(cy + 1) * kP2;
-        tz[0] = (uint32_t)cz * kP3;
-        tz[1] = (uint32_t)(cz + 1) * kP3;
-        tt[0] = (uint32_t)ct * kP4;
-        tt[1] = (uint32_t)(ct + 1) * kP4;
+        tx[0] = (uint32_t)cx * (kP1 * 4u);
+        tx[1] = (uint32_t)(cx + 1) * (kP1 * 4u);
+        ty[0] = (uint32_t)cy * (kP2 * 4u);
+        ty[1] = (uint32_t)(cy + 1) * (kP2 * 4u);
+        tz[0] = (uint32_t)cz * (kP3 * 4u);
+        tz[1] = (uint32_t)(cz + 1) * (kP3 * 4u);
+        tt[0] = (uint32_t)ct * (kP4 * 4u);
+        tt[1] = (uint32_t)(ct + 1) * (kP4 * 4u);
     }
+    const uint32_t mask4 = mask * 4u;
     auto comb = [](uint32_t u, uint32_t v) { return DENSE ? u + v : u ^ v; };
     const float wx[2] = {1.0f - fx, fx}, wy[2] = {1.0f - fy, fy}, wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
-    // partial products over x, y, z shared by the two temporal vertices; the
-    // weight is ((w_x w_y) w_z) w_t as defined
     float wxyz[8];
     uint32_t txyz[8];
 #pragma unroll
@@ -283,24 +284,19 @@ __device__ __forceinline__ void gather_lane(const float4 p, bool valid, int res,
         txyz[c] = comb(comb(tx[bx], ty[by]), tz[bz]);
     }
     // The corners of one temporal vertex are fetched only when some lane of
-    // the wave gives them a non-zero weight: a frame's Gaussians share one
-    // time, and on a temporal vertex half the corners weigh exactly zero.
-    // Corners of zero weight add exactly zero (finite table entries), so
-    // skipping them, for a lane or for the wave, changes no sum.
+    // the wave gives them a non-zero weight (a frame's Gaussians share one
+    // time, and on a temporal vertex half the corners weigh exactly zero).
+    // A lane past the last Gaussian gathers the last one's corners, unused.
     const bool need_t[2] = {__ballot(valid && wt[0] != 0.0f) != 0ull, __ballot(valid && wt[1] != 0.0f) != 0ull};
     uint32_t raw[16];
     float w[16];
 #pragma unroll
     for (int bt = 0; bt < 2; ++bt) {
         if (need_t[bt]) {
-            // all loads of this temporal vertex are issued before any is used;
-            // one not needed reads past the end of the table (zero, no request)
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 w[8 * bt + c] = wxyz[c] * wt[bt];
-                const uint32_t idx = comb(txyz[c], tt[bt]) & mask;
-                raw[8 * bt + c] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rt, (valid && w[8 * bt + c] != 0.0f) ? idx * 4u : kBufferNone, 0, 0);
+                raw[8 * bt + c] = __builtin_amdgcn_raw_buffer_load_b32(rt, comb(txyz[c], tt[bt]) & mask4, 0, 0);
             }
         } else {
 #pragma unroll
