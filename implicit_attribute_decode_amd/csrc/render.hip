@@ -640,7 +640,17 @@ __global__ void __launch_bounds__(kBlock) sort_upsweep_kernel(SortPass p) {
             slot[j] = min(w * nb + d + past, (uint32_t)(4 * nb));
         }
 #pragma unroll
-        for (int j = 0; j < kSortItems; ++j) atomicAdd(&hist[slot[j]], 1u);
+        for (int j = 0; j < kSortItems; ++j) {
+            // a wave whose lanes all count the same slot (common for the top
+            // digit of depth keys) adds its 64 with one atomic instead of 64
+            // conflicting ones
+            const uint32_t s0 = __builtin_amdgcn_readfirstlane(slot[j]);
+            if (__ballot(slot[j] != s0) == 0ull) {
+                if ((threadIdx.x & 63) == 0) atomicAdd(&hist[s0], 64u);
+            } else {
+                atomicAdd(&hist[slot[j]], 1u);
+            }
+        }
     }
     __syncthreads();
     for (int d = threadIdx.x; d < nb; d += kBlock)
@@ -730,7 +740,10 @@ __global__ void __launch_bounds__(kBlock, 3) sort_downsweep_kernel(SortPass p) {
             const bool valid = idx < end;
             const uint32_t d = (uint32_t)(key[j] >> p.shift) & mask;
             uint64_t peers = __ballot(valid);
-            for (int bit = 0; bit < p.bits; ++bit) {
+            // bits at and above p.bits are zero in every lane's digit and
+            // leave peers unchanged
+#pragma unroll
+            for (int bit = 0; bit < MAXB; ++bit) {
                 const uint64_t b = __ballot((d >> bit) & 1u);
                 peers &= ((d >> bit) & 1u) ? b : ~b;
             }
