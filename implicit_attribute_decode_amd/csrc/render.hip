@@ -1150,9 +1150,7 @@ __device__ __forceinline__ bool may_reach(float4 ga, float gbx, float X0, float 
 // One block per 16x16 tile.  PX = 2: 128 threads, thread (col, row) shades
 // pixels (col, 2 row) and (col, 2 row + 1), which share dx and the dx terms
 // of power, so a wave covers a 16 x 8 pixel block; PX = 1: 256 threads, one
-// pixel each (twice the waves, for launches with few tiles).  When no pixel
-// of a wave lies within 3 sigma of a Gaussian the wave skips its compositing
-// step (the step would add alpha = 0 everywhere).
+// pixel each (twice the waves, for launches with few tiles).
 // Gaussians of the tile's list are staged in LDS 256 at a time with the
 // conic pre-scaled by -1/2, -1, -1/2 (exact), so power = A' dx^2 + C' dy^2 +
 // B' dx dy.  After staging, each wave marks with may_reach the batch's
@@ -1244,16 +1242,15 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
                 const float dx = fx - ga.x;
                 float ta, tb;
                 splat_dx_terms(ga.z, ga.w, dx, ta, tb);
-                float pw[PX], pmax = -INFINITY;
+                float pw[PX];
 #pragma unroll
                 for (int k = 0; k < PX; ++k) {
                     const float dy = ((float)(py0 + k) + 0.5f) - ga.y;
                     pw[k] = splat_power(ta, tb, gb.x, dy);
-                    pmax = fmaxf(pmax, pw[k]);
                 }
-                // no pixel of the wave within 3 sigma: nothing to composite.
-                // (A superset test: the compositing step applies the exact rule.)
-                if (__ballot(pmax >= -4.5f) == 0ull) continue;
+                // (no wave-wide test that some pixel is within 3 sigma before
+                // compositing: the compositing step leaves a pixel outside
+                // unchanged, and the branch cost more than the steps it saved)
 #pragma unroll
                 for (int k = 0; k < PX; ++k) composite_step<LAST>(p[k], pw[k], gb.y, gb.z, gb.w, gcb, pos0 + (uint32_t)j);
             }
