@@ -225,6 +225,7 @@ int gather_groups(int L) {
     return (gl + kLevelGroup - 1) / kLevelGroup + (L - gl);
 }
 constexpr int kMlpBlocksPerCu = 1;    // MLP beside a gather: blocks per CU
+constexpr int kMlpAhead = 4;          // MLP: 16-Gaussian groups whose features load ahead
 constexpr int kNormBlocksPerCu = 2;   // normalisation beside a gather: blocks per CU
 
 __global__ void __launch_bounds__(256) normalize_kernel(DecodeArgs a, const float* pos, int64_t n, float4* xt) {
@@ -499,13 +500,22 @@ __global__ void __launch_bounds__(256) mlp_f16_kernel(DecodeArgs a, const uint32
     };
     // groups of this wave: 64 consecutive Gaussians per turn (four groups), turns nwaves apart
     auto group_at = [&](int64_t k) { return ((k >> 2) * nwaves + wave) * 64 + 16 * (k & 3); };
-    half8_t Zn = wave * 64 < n ? load_z(wave * 64) : half8_t{};
-    for (int64_t k = 0;; ++k) {
+    // The features of the next kMlpAhead groups are in flight while a group
+    // computes (beside a gather, loads wait behind its flood of L2 requests).
+    // Slot i of the ring holds group k + i of the unrolled turn, so no
+    // register is moved while its load is pending.
+    // (load_z clamps its index, so every load is issued unconditionally.)
+    half8_t Zr[kMlpAhead];
+#pragma unroll
+    for (int i = 0; i < kMlpAhead; ++i) Zr[i] = load_z(group_at(i));
+    for (int64_t k0 = 0; group_at(k0) < n; k0 += kMlpAhead)
+#pragma unroll
+    for (int i = 0; i < kMlpAhead; ++i) {
+        const int64_t k = k0 + i;
         const int64_t g0 = group_at(k);
-        if (g0 >= n) break;
-        const half8_t Z = Zn;
-        const int64_t g1 = group_at(k + 1);
-        if (g1 < n) Zn = load_z(g1);  // the next group's features load while this one computes
+        const half8_t Z = Zr[i];
+        Zr[i] = load_z(group_at(k + kMlpAhead));
+        if (g0 >= n) continue;  // wave-uniform
         // ---- trunk layer 1: 32 -> 64
         half8_t H1[2];
 #pragma unroll
