@@ -1,13 +1,22 @@
 // Per-pixel splat arithmetic shared by the forward raster and its backward
 // pass, so that both take exactly the same compositing decisions ("SPIN-4DGS"
-// §3.1, Eq. 1 and Eq. 4).  The conic is pre-scaled by -1/2, -1, -1/2:
-// gz = -A/2, gw = -B, gbx = -C/2, so power = -0.5 (A dx^2 + C dy^2) - B dx dy
-// = (gz dx^2 + gbx dy^2) + gw dx dy with d = pixel centre - mean.
+// §3.1, Eq. 1 and Eq. 4).  The kernels work with the exponent in base 2: the
+// conic is staged pre-scaled by -log2(e)/2, -log2(e), -log2(e)/2 (one fp32
+// rounding each), gz = -A log2(e)/2, gw = -B log2(e), gbx = -C log2(e)/2, so
+// that p2 = (gz dx^2 + gbx dy^2) + gw dx dy = log2(e) power, with power =
+// -0.5 (A dx^2 + C dy^2) - B dx dy and d = pixel centre - mean, and
+// exp(power) = 2^p2 is one hardware exp2.  The 3-sigma bound power >= -4.5 is
+// p2 >= -4.5 log2(e).
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 namespace ia {
+
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kConicScaleA = -0.5f * kLog2e;  // staged A and C factor
+constexpr float kConicScaleB = -kLog2e;          // staged B factor
+constexpr float kPower2Min = -4.5f * kLog2e;     // 3 sigma in base-2 units
 
 // Terms of power that depend on dx only.
 __device__ __forceinline__ void splat_dx_terms(float gz, float gw, float dx, float& ta, float& tb) {
@@ -16,20 +25,24 @@ __device__ __forceinline__ void splat_dx_terms(float gz, float gw, float dx, flo
     tb = gw * dx;
 }
 
+// p2 = log2(e) power from the dx terms and dy.
 __device__ __forceinline__ float splat_power(float ta, float tb, float gbx, float dy) {
 #pragma clang fp contract(fast)
     return (ta + gbx * dy * dy) + tb * dy;
 }
 
+// exp(power) = 2^p2.
+__device__ __forceinline__ float splat_gauss(float p2) { return __builtin_amdgcn_exp2f(p2); }
+
 // alpha = min(0.99, o exp(power)) before the skip rule.
-__device__ __forceinline__ float splat_alpha(float opacity, float power) {
+__device__ __forceinline__ float splat_alpha(float opacity, float p2) {
 #pragma clang fp contract(fast)
-    return fminf(0.99f, opacity * __expf(power));
+    return fminf(0.99f, opacity * splat_gauss(p2));
 }
 
 // Composited unless outside 3 sigma (power outside [-4.5, 0]) or alpha < 1/255.
-__device__ __forceinline__ bool splat_takes(float power, float a0) {
-    return power >= -4.5f && power <= 0.0f && a0 >= (1.0f / 255.0f);
+__device__ __forceinline__ bool splat_takes(float p2, float a0) {
+    return p2 >= kPower2Min && p2 <= 0.0f && a0 >= (1.0f / 255.0f);
 }
 
 // Degree-3 real spherical harmonics (orthonormal, l-major, m = -l..l, the

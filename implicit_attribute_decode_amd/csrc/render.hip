@@ -1116,19 +1116,20 @@ __device__ __forceinline__ void composite_step(Pix& p, float power, float opacit
     if (LAST) p.last = take ? pos : p.last;
 }
 
-// Whether a staged Gaussian (ga = mean, A', B'; gbx = C'; power = A' dx^2 +
-// C' dy^2 + B' dx dy) can pass the per-pixel 3-sigma test at some pixel centre
-// of a wave, whose centres lie in [X0, X1] x [Y0, Y1].  q = -power is convex:
-// its minimum over the box is 0 when the box holds the mean, else it lies on
-// an edge, where q is a parabola in the free coordinate, minimised at its
-// vertex clamped to the edge.  The offsets a pixel computes lie in the box
-// the offsets of its corners span (rounding is monotonic), so a pixel whose
-// computed power is >= -4.5 has q <= 4.5 + e there, and the computed minimum
-// exceeds the exact one by at most e', with e, e' a few units of fp32
-// rounding of M = |A'| dx^2 + |C'| dy^2 + |B' dx dy| over the box (about 15 u
-// M in all, u = 2^-24).  The test allows 4e-6 M + 1e-4: it never rejects a
-// Gaussian the per-pixel test would take, only spares the wave the Gaussians
-// that cannot reach it.  Degenerate or non-finite values pass.
+// Whether a staged Gaussian (ga = mean, A', B'; gbx = C'; p2 = A' dx^2 +
+// C' dy^2 + B' dx dy, the base-2 power) can pass the per-pixel 3-sigma test
+// p2 >= -4.5 log2(e) = -Q at some pixel centre of a wave, whose centres lie
+// in [X0, X1] x [Y0, Y1].  q = -p2 is convex: its minimum over the box is 0
+// when the box holds the mean, else it lies on an edge, where q is a parabola
+// in the free coordinate, minimised at its vertex clamped to the edge.  The
+// offsets a pixel computes lie in the box the offsets of its corners span
+// (rounding is monotonic), so a pixel whose computed p2 is >= -Q has q <= Q +
+// e there, and the computed minimum exceeds the exact one by at most e', with
+// e, e' a few units of fp32 rounding of M = |A'| dx^2 + |C'| dy^2 + |B' dx dy|
+// over the box (about 15 u M in all, u = 2^-24).  The test allows 4e-6 M +
+// 1.5e-4: it never rejects a Gaussian the per-pixel test would take, only
+// spares the wave the Gaussians that cannot reach it.  Degenerate or
+// non-finite values pass.
 __device__ __forceinline__ bool may_reach(float4 ga, float gbx, float X0, float X1, float Y0, float Y1) {
 #pragma clang fp contract(fast)
     const float x0 = X0 - ga.x, x1 = X1 - ga.x, y0 = Y0 - ga.y, y1 = Y1 - ga.y;
@@ -1144,7 +1145,7 @@ __device__ __forceinline__ bool may_reach(float4 ga, float gbx, float X0, float 
     m = fminf(m, q(clampf(-b * y1 * ia, x0, x1), y1));
     const float xm = fmaxf(fabsf(x0), fabsf(x1)), ym = fmaxf(fabsf(y0), fabsf(y1));
     const float M = (a * xm * xm + c * ym * ym) + fabsf(b) * xm * ym;
-    return !(m > 4.5f + 4e-6f * M + 1e-4f);
+    return !(m > -kPower2Min + 4e-6f * M + 1.5e-4f);
 }
 
 // One block per 16x16 tile.  PX = 2: 128 threads, thread (col, row) shades
@@ -1152,8 +1153,8 @@ __device__ __forceinline__ bool may_reach(float4 ga, float gbx, float X0, float 
 // of power, so a wave covers a 16 x 8 pixel block; PX = 1: 256 threads, one
 // pixel each (twice the waves, for launches with few tiles).
 // Gaussians of the tile's list are staged in LDS 256 at a time with the
-// conic pre-scaled by -1/2, -1, -1/2 (exact), so power = A' dx^2 + C' dy^2 +
-// B' dx dy.  After staging, each wave marks with may_reach the batch's
+// conic pre-scaled to the base-2 power (kConicScaleA, kConicScaleB), so p2 =
+// A' dx^2 + C' dy^2 + B' dx dy = log2(e) power.  After staging, each wave marks with may_reach the batch's
 // Gaussians that can reach one of its pixels (four per lane, one ballot per
 // 64) and visits only those, in list order.  A wave leaves a batch once all
 // its pixels are saturated; the block stops once all 256 are.
@@ -1206,8 +1207,8 @@ __global__ void __launch_bounds__(256 / PX) raster_kernel(RasterArgs a) {
                 uint32_t gid = a.vals[idx];
                 if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
                 const float4 pa = a.pa[gid], pb = a.pb[gid];
-                s_a[slot] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
-                s_b[slot] = make_float4(-0.5f * pb.x, pb.y, pb.z, pb.w);
+                s_a[slot] = make_float4(pa.x, pa.y, kConicScaleA * pa.z, kConicScaleB * pa.w);
+                s_b[slot] = make_float4(kConicScaleA * pb.x, pb.y, pb.z, pb.w);
                 s_c[slot].x = a.pc[gid];
             }
         }

@@ -111,8 +111,8 @@ template <int PX>
 __global__ void __launch_bounds__(256 / PX) raster_backward_kernel(RasterBwdArgs a) {
 #pragma clang fp contract(fast)
     constexpr int kThreads = 256 / PX, kWaves = kThreads / 64;
-    __shared__ float4 s_a[kBwdBatch];  // u, v, -A/2, -B
-    __shared__ float4 s_b[kBwdBatch];  // -C/2, o, r, g
+    __shared__ float4 s_a[kBwdBatch];  // u, v, -A log2(e)/2, -B log2(e)
+    __shared__ float4 s_b[kBwdBatch];  // -C log2(e)/2, o, r, g
     __shared__ float s_c[kBwdBatch];   // b
     __shared__ uint32_t s_id[kBwdBatch];
     __shared__ float s_g[kBwdBatch][kGradPerGaussian];
@@ -170,8 +170,8 @@ __global__ void __launch_bounds__(256 / PX) raster_backward_kernel(RasterBwdArgs
                 uint32_t gid = a.vals[rg.x + start + slot];
                 if ((int64_t)gid >= a.N) gid = 0;  // cannot happen for a valid sort; keeps reads in bounds
                 const float4 pa = a.pa[gid], pb = a.pb[gid];
-                s_a[slot] = make_float4(pa.x, pa.y, -0.5f * pa.z, -pa.w);
-                s_b[slot] = make_float4(-0.5f * pb.x, pb.y, pb.z, pb.w);
+                s_a[slot] = make_float4(pa.x, pa.y, kConicScaleA * pa.z, kConicScaleB * pa.w);
+                s_b[slot] = make_float4(kConicScaleA * pb.x, pb.y, pb.z, pb.w);
                 s_c[slot] = a.pc[gid];
                 s_id[slot] = gid;
             }
@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(256 / PX) raster_backward_kernel(RasterBwdArgs
             for (int k = 0; k < PX; ++k) {
                 dy[k] = (float)(py0 + k) + 0.5f - ga.y;
                 pw[k] = splat_power(ta, tb, gb.x, dy[k]);
-                near = near || (pos1 <= P[k].nc && pw[k] >= -4.5f);
+                near = near || (pos1 <= P[k].nc && pw[k] >= kPower2Min);
             }
             if (__ballot(near) == 0ull) continue;
             bool any = false;
@@ -221,12 +221,12 @@ __global__ void __launch_bounds__(256 / PX) raster_backward_kernel(RasterBwdArgs
             if (__ballot(any) == 0ull) continue;
             float gv[kGradPerGaussian];
             const float cb = s_c[j];
-            pixel_grad<true>(P[0], tk[0], al[0], __expf(pw[0]), dx, dy[0], gb.z, gb.w, cb, gv);
+            pixel_grad<true>(P[0], tk[0], al[0], splat_gauss(pw[0]), dx, dy[0], gb.z, gb.w, cb, gv);
             // a further pixel row of the wave (PX > 1) is skipped when none of it composites
 #pragma unroll
             for (int k = 1; k < PX; ++k)
                 if (__ballot(tk[k]) != 0ull)
-                    pixel_grad<false>(P[k], tk[k], al[k], __expf(pw[k]), dx, dy[k], gb.z, gb.w, cb, gv);
+                    pixel_grad<false>(P[k], tk[k], al[k], splat_gauss(pw[k]), dx, dy[k], gb.z, gb.w, cb, gv);
 #pragma unroll
             for (int k = 0; k < kGradPerGaussian; ++k) gv[k] = quad_sum(gv[k]);
             if ((lane & 3) == 0) {
@@ -249,7 +249,8 @@ __global__ void __launch_bounds__(256 / PX) raster_backward_kernel(RasterBwdArgs
                 float v[kGradPerGaussian];
 #pragma unroll
                 for (int k = 0; k < kGradPerGaussian; ++k) v[k] = s_g[slot][k];
-                const float A = -2.0f * s_a[slot].z, B = -s_a[slot].w, C = -2.0f * s_b[slot].x;
+                // the conic as projected (the staged copy is scaled to base 2)
+                const float A = a.pa[s_id[slot]].z, B = a.pa[s_id[slot]].w, C = a.pb[s_id[slot]].x;
                 const float mx = v[0], my = v[1], mxx = v[2], mxy = v[3], myy = v[4];
                 v[0] = A * mx + B * my;
                 v[1] = C * my + B * mx;

@@ -1,11 +1,12 @@
 """The raster's per-wave box test never drops a Gaussian that the per-pixel
 3-sigma test would take (host logic, no GPU).
 
-After staging a batch of Gaussians, each wave of the raster kernel keeps
-only those whose quadratic form q = -power can reach 4.5 on the box of its
-pixel centres (minimum at the mean when the box holds it, else at the
-clamped vertex of the parabola on each edge), with a margin of 4e-6 of the
-box's absolute terms plus 1e-4 for fp32 rounding.  That is an optimisation
+After staging a batch of Gaussians (the conic scaled to the base-2 power
+p2 = log2(e) power), each wave of the raster kernel keeps only those whose
+quadratic form q = -p2 can reach 4.5 log2(e) on the box of its pixel centres
+(minimum at the mean when the box holds it, else at the clamped vertex of
+the parabola on each edge), with a margin of 4e-6 of the box's absolute
+terms plus 1.5e-4 for fp32 rounding.  That is an optimisation
 only if it keeps every Gaussian some pixel of the wave composites.  This
 test evaluates, in fp32 with numpy, the per-pixel power in the kernel's
 operation order and the box test in the order of the kernel's code (with and
@@ -21,6 +22,9 @@ import oracle as O
 from implicit_attribute_decode_amd import scenes as S
 
 f32 = np.float32
+LOG2E = f32(1.44269504088896341)
+SCALE_A, SCALE_B = f32(-0.5) * LOG2E, -LOG2E  # staged A and C factor, B factor
+P2_MIN = f32(f32(-4.5) * LOG2E)               # 3 sigma in base-2 units
 
 
 def _fma(a, b, c):
@@ -66,7 +70,7 @@ def _pairs(pre, b, cams, rows, chunk=8192):
         ty, tx = t // tiles_x, t % tiles_x
         u, v = pre["mean2d"][gi, 0], pre["mean2d"][gi, 1]
         A, B, C = (pre["conic"][gi, j] for j in range(3))
-        gz, gw, gbx = f32(-0.5) * A, -B, f32(-0.5) * C  # the staged A', B', C'
+        gz, gw, gbx = SCALE_A * A, SCALE_B * B, SCALE_A * C  # the staged A', B', C'
         for wv in range(waves):
             X0 = (tx * 16).astype(f32) + f32(0.5)
             Y0 = (ty * 16 + rows * wv).astype(f32) + f32(0.5)
@@ -80,7 +84,7 @@ def _pairs(pre, b, cams, rows, chunk=8192):
             cdy = (gbx[:, None] * dy).astype(f32)
             inner = _fma(dy[:, :, None], cdy[:, :, None], ta[:, None, :])
             power = _fma(tb[:, None, :], dy[:, :, None], inner)
-            passes = (power >= f32(-4.5)).reshape(len(gi), -1).any(axis=1)
+            passes = (power >= P2_MIN).reshape(len(gi), -1).any(axis=1)
             verdict = [_box(u, v, gz, gw, gbx, X0, X0 + f32(15), Y0, Y0 + f32(rows - 1), fused)
                        for fused in (True, False)]
             out.append((passes, verdict[0], verdict[1]))
@@ -116,7 +120,7 @@ def _box(u, v, gz, gw, gbx, X0, X1, Y0, Y1, fused):
         xm, ym = np.maximum(np.abs(x0), np.abs(x1)), np.maximum(np.abs(y0), np.abs(y1))
         M = (((a * xm).astype(f32) * xm + (c * ym).astype(f32) * ym).astype(f32)
              + (np.abs(b) * xm).astype(f32) * ym).astype(f32)
-        keep = ~(m > (f32(4.5) + (f32(4e-6) * M).astype(f32) + f32(1e-4)).astype(f32))
+        keep = ~(m > (-P2_MIN + (f32(4e-6) * M).astype(f32) + f32(1.5e-4)).astype(f32))
     return inside | degenerate | keep
 
 
