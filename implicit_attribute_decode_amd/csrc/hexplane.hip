@@ -254,15 +254,25 @@ __device__ __forceinline__ void hex_sub_batch(const HexArgs& a, const half8_t* W
                 floatx4 acc0[KK], acc1[KK];
 #pragma unroll
                 for (int g = 0; g < K; ++g) acc0[g] = acc1[g] = floatx4{0, 0, 0, 0};
+                // the next k-block's A tiles are read while this one's MFMAs run
+                half8_t A0 = sw[((2 * i) * 6) * kTileHalf8 + lane];
+                half8_t A1 = sw[((2 * i + 1) * 6) * kTileHalf8 + lane];
 #pragma unroll
                 for (int m = 0; m < 6; ++m) {
-                    const half8_t A0 = sw[((2 * i) * 6 + m) * kTileHalf8 + lane];
-                    const half8_t A1 = sw[((2 * i + 1) * 6 + m) * kTileHalf8 + lane];
+                    half8_t N0 = A0, N1 = A1;
+                    if (m < 5) {
+                        N0 = sw[((2 * i) * 6 + m + 1) * kTileHalf8 + lane];
+                        N1 = sw[((2 * i + 1) * 6 + m + 1) * kTileHalf8 + lane];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int g = 0; g < K; ++g) {
                         acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, X[m][g], acc0[g], 0, 0, 0);
                         acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, X[m][g], acc1[g], 0, 0, 0);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
+                    A0 = N0;
+                    A1 = N1;
                 }
 #pragma unroll
                 for (int g = 0; g < K; ++g)
@@ -307,15 +317,24 @@ __device__ __forceinline__ void hex_sub_batch(const HexArgs& a, const half8_t* W
             floatx4 acc0[KK], acc1[KK];
 #pragma unroll
             for (int g = 0; g < K; ++g) acc0[g] = acc1[g] = floatx4{0, 0, 0, 0};
+            half8_t A0 = sw[0 * kTileHalf8 + lane];
+            half8_t A1 = sw[8 * kTileHalf8 + lane];
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                const half8_t A0 = sw[m * kTileHalf8 + lane];
-                const half8_t A1 = sw[(8 + m) * kTileHalf8 + lane];
+                half8_t N0 = A0, N1 = A1;
+                if (m < 7) {
+                    N0 = sw[(m + 1) * kTileHalf8 + lane];
+                    N1 = sw[(8 + m + 1) * kTileHalf8 + lane];
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int g = 0; g < K; ++g) {
                     acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, H1[m][g], acc0[g], 0, 0, 0);
                     acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, H1[m][g], acc1[g], 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                A0 = N0;
+                A1 = N1;
             }
             half8_t H2[KK];
 #pragma unroll
