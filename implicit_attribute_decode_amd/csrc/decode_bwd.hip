@@ -35,19 +35,24 @@
 //       decoder (F = 4, 64 -> 64 -> 64 -> out), one launch per branch: the
 //       branches' encoding gradients add up in dz, each branch's weight
 //       gradients are reduced after its launch.
-//   scatter_kernel  level-major like the gather, four lanes per (Gaussian,
-//       level), each with four of the 16 corners: dtable[corner] += w dz with
-//       float atomics; for positions dz/df_axis = sum_c (+-1) prod_{other
+//   table and position gradients, level-major like the gather, four lanes
+//       per (Gaussian, level), each with four of the 16 corners:
+//       dtable[corner] += w dz (how it is summed: below); for positions dz/df_axis = sum_c (+-1) prod_{other
 //       axes} w table[c] (time carries no gradient), times (res - 1), then the
 //       Jacobian of Eq. 7: each level's share is stored (one 16-byte store per
 //       Gaussian and level, in list order) and pos_reduce_kernel adds the
 //       levels in a fixed order to the position gradient (no atomics).
-//       On levels of at most kAggMaxRes vertices per axis, where the block's
-//       Gaussians share corners, each block first adds its contributions per
-//       table entry in an LDS hash table (open addressing, LDS atomics) and
-//       then issues one pair of global atomics per distinct entry: global
-//       float atomics are served far below L2 speed on this chip, LDS ones
-//       are not.
+//       Global float atomics are served far below L2 speed on this chip, LDS
+//       ones are not.  scatter_kernel: on levels of at most kAggMaxRes
+//       vertices per axis, where the block's Gaussians share corners, each
+//       block first adds its contributions per table entry in an LDS hash
+//       table (open addressing, LDS atomics), then issues one global atomic
+//       per distinct entry and feature.  bucket_scatter_kernel and
+//       bucket_add_kernel: on the finer levels the contributions go as
+//       (entry, value) records into per-bucket runs (2^11 table entries a
+//       bucket) and one block per bucket sums them in LDS and adds them to
+//       the table's gradient with plain stores; with few Gaussians with a
+//       gradient in the chunk, direct float atomics instead.
 // After the last chunk a two-stage reduction sums the partial buffer in a
 // fixed order (deterministic weight and bias gradients).
 #include <hip/hip_runtime.h>
@@ -978,166 +983,388 @@ __device__ __forceinline__ void agg_add(uint32_t* key, float* v, uint32_t idx, c
     for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, a[f]);
 }
 
-// Eq. 9 and Eq. 7 backward, level-major as the gather, levels level0 + 0, 1,
-// ...  Lane s of a group of four takes the x/y corner (s & 1, s >> 1) and its
-// four z/t corners.  F features per table entry (2, or 4 for the paper-scale
-// encoder; gz holds F floats per level and Gaussian).  AGG: combine per entry
-// in LDS first (every thread of a block reaches the final barrier: the only
-// early exit is block-uniform).
-template <int F, bool POS, bool AGG>
+// Eq. 9 and Eq. 7 backward of one (Gaussian, level) for lane s of its group
+// of four: the lane takes the x/y corner (s & 1, s >> 1) and its four z/t
+// corners; emit(idx, w) receives each corner of non-zero weight w (its
+// contribution to table entry idx is w g[f] per feature f).  POS: this
+// level's share of the position gradient, stored by lane 0 of the group.
+// k is the Gaussian's compact index (its upstream gradient row), i its
+// chunk-local index.
+template <int F, bool POS, class Emit>
+__device__ __forceinline__ void scatter_one(const float4 p, const float* pos, int stride, int64_t i, int64_t k,
+                                            int level, const HashLevels& h, const uint32_t* tab, const float (&g)[F],
+                                            int64_t zstride, float4* gpos_part, int s, Emit&& emit) {
+#pragma clang fp contract(fast)
+    const int res = h.res_s[level], res_t = h.res_t[level];
+    const bool dense = h.dense[level] != 0;
+    const int bx = s & 1, by = s >> 1;
+    const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
+    int cx, cy, cz, ct;
+    float fx, fy, fz, ft;
+    cell_axis(p.x, res, cx, fx);
+    cell_axis(p.y, res, cy, fy);
+    cell_axis(p.z, res, cz, fz);
+    cell_axis(p.w, res_t, ct, ft);
+    const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
+    uint32_t txy, tz[2], tt[2];
+    if (dense) {
+        txy = ux + uy * r;
+        tz[0] = (uint32_t)cz * r2;
+        tz[1] = tz[0] + r2;
+        tt[0] = (uint32_t)ct * r3;
+        tt[1] = tt[0] + r3;
+    } else {
+        txy = (ux * kP1) ^ (uy * kP2);
+        tz[0] = (uint32_t)cz * kP3;
+        tz[1] = (uint32_t)(cz + 1) * kP3;
+        tt[0] = (uint32_t)ct * kP4;
+        tt[1] = (uint32_t)(ct + 1) * kP4;
+    }
+    const float wx = bx ? fx : 1.0f - fx, wy = by ? fy : 1.0f - fy;
+    const float sx = bx ? 1.0f : -1.0f, sy = by ? 1.0f : -1.0f;
+    const float wxy = wx * wy;
+    const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
+    // no gradient at this level: nothing to add, no position term (uniform over the four lanes)
+    bool none = true;
+#pragma unroll
+    for (int f = 0; f < F; ++f) none = none && g[f] == 0.0f;
+    if (none) {
+        if (POS && s == 0) gpos_part[(size_t)level * zstride + k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        return;
+    }
+    float dx = 0.0f, dy = 0.0f, dz = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int bz = c & 1, bt = c >> 1;
+        // a corner of zero time weight has zero weight and zero spatial derivatives
+        if (wt[bt] == 0.0f) continue;
+        const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
+        const float w = (wxy * wz[bz]) * wt[bt];
+        if (w != 0.0f) emit(idx, w);
+        if (POS) {
+            // the entry's features times the level's gradient
+            float tg = 0.0f;
+#pragma unroll
+            for (int f = 0; f < F; f += 2) {
+                const uint32_t raw = tab[(F / 2) * (size_t)idx + f / 2];
+                const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
+                const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
+                tg += v0 * g[f] + v1 * g[f + 1];
+            }
+            const float wzt = wz[bz] * wt[bt];
+            dx += tg * (sx * wy) * wzt;
+            dy += tg * (wx * sy) * wzt;
+            dz += tg * wxy * ((bz ? 1.0f : -1.0f) * wt[bt]);
+        }
+    }
+    if (POS) {
+        dx += __shfl_xor(dx, 1, 4);
+        dy += __shfl_xor(dy, 1, 4);
+        dz += __shfl_xor(dz, 1, 4);
+        dx += __shfl_xor(dx, 2, 4);
+        dy += __shfl_xor(dy, 2, 4);
+        dz += __shfl_xor(dz, 2, 4);
+        if (s == 0) {
+            const float sc = (float)(res - 1);
+            const float gx[3] = {dx * sc, dy * sc, dz * sc};
+            const float* mu = pos + i * stride;
+            const float m0 = mu[0], m1 = mu[1], m2 = mu[2];
+            const float nn = sqrtf(m0 * m0 + m1 * m1 + m2 * m2);
+            float out[3];
+            if (nn <= 1.0f) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k) out[k] = 0.25f * gx[k];
+            } else {
+                // x~ = c(mu)/4 + 1/2, c = gn mu, gn = 2/n - 1/n^2: J = gn I + (gn'/n) mu mu^T
+                const float inv = 1.0f / nn;
+                const float gn = (2.0f - inv) * inv;
+                const float gp_n = (-2.0f + 2.0f * inv) * inv * inv * inv;
+                const float md = m0 * gx[0] + m1 * gx[1] + m2 * gx[2];
+                out[0] = 0.25f * (gn * gx[0] + gp_n * m0 * md);
+                out[1] = 0.25f * (gn * gx[1] + gp_n * m1 * md);
+                out[2] = 0.25f * (gn * gx[2] + gp_n * m2 * md);
+            }
+            // this level's share, summed over the levels by pos_reduce_kernel
+            gpos_part[(size_t)level * zstride + k] = make_float4(out[0], out[1], out[2], 0.0f);
+        }
+    }
+}
+
+// The upstream gradient of Gaussian k (compact index) at a level.
+template <int F>
+__device__ __forceinline__ void level_grad(const float* gz, int64_t zstride, int level, int64_t k, float (&g)[F]) {
+    if constexpr (F == 2) {
+        const float2 v = reinterpret_cast<const float2*>(gz)[(size_t)level * zstride + k];
+        g[0] = v.x;
+        g[1] = v.y;
+    } else {
+        const float4 v = reinterpret_cast<const float4*>(gz)[(size_t)level * zstride + k];
+        g[0] = v.x;
+        g[1] = v.y;
+        g[2] = v.z;
+        g[3] = v.w;
+    }
+}
+
+// The coarse levels (at most kAggMaxRes vertices per axis), level-major as the
+// gather, levels level0 + 0, 1, ...: each block adds its contributions per
+// table entry in LDS first, then one global atomic per distinct entry and
+// feature (every thread of a block reaches the final barrier: the only early
+// exit is block-uniform).  F features per table entry (2, or 4 for the
+// paper-scale encoder; gz holds F floats per level and Gaussian).
+template <int F, bool POS>
 __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const float* pos, int stride,
                                                       const uint32_t* list, const uint32_t* count, int nchunk,
                                                       int level0, HashLevels h, const uint32_t* tables,
                                                       const float* gz, int64_t zstride, float* gtab,
                                                       float4* gpos_part) {
-#pragma clang fp contract(fast)
     static_assert(F == 2 || F == 4, "two or four features per entry");
-    __shared__ uint32_t s_key[AGG ? kAggSlots : 1];
-    __shared__ float s_v[AGG ? F * kAggSlots : 1];
+    __shared__ uint32_t s_key[kAggSlots];
+    __shared__ float s_v[F * kAggSlots];
     const int level = level0 + (int)(blockIdx.x / nchunk);
-    constexpr int kRounds = AGG ? kAggRounds : 4;
-    const int64_t first = (int64_t)(blockIdx.x % nchunk) * (64 * kRounds);
+    const int64_t first = (int64_t)(blockIdx.x % nchunk) * (64 * kAggRounds);
     const int64_t n = *count;  // Gaussians with a gradient, compacted
     if (first >= n) return;
-    if constexpr (AGG) {
-        for (int k = threadIdx.x; k < kAggSlots; k += 256) s_key[k] = kAggEmpty;
-        for (int k = threadIdx.x; k < F * kAggSlots; k += 256) s_v[k] = 0.0f;
-        __syncthreads();
-    }
-    const int res = h.res_s[level], res_t = h.res_t[level];
-    const bool dense = h.dense[level] != 0;
+    for (int k = threadIdx.x; k < kAggSlots; k += 256) s_key[k] = kAggEmpty;
+    for (int k = threadIdx.x; k < F * kAggSlots; k += 256) s_v[k] = 0.0f;
+    __syncthreads();
     const uint32_t* tab = tables + (size_t)level * h.T * (F / 2);
     float* gt = gtab + (size_t)level * h.T * F;
-    const int s = threadIdx.x & 3;
-    const int bx = s & 1, by = s >> 1;
-    const int sub = threadIdx.x >> 2;
-    const uint32_t r = (uint32_t)res, r2 = r * r, r3 = r2 * r;
-    for (int j = 0; j < kRounds; ++j) {
+    const int s = threadIdx.x & 3, sub = threadIdx.x >> 2;
+    for (int j = 0; j < kAggRounds; ++j) {
         const int64_t k = first + j * 64 + sub;  // compact index
         if (k >= n) break;  // uniform across each group of four lanes
         const int64_t i = list[k];  // chunk-local Gaussian
-        const float4 p = xt[i];
         float g[F];
-        if constexpr (F == 2) {
-            const float2 v = reinterpret_cast<const float2*>(gz)[(size_t)level * zstride + k];
-            g[0] = v.x;
-            g[1] = v.y;
-        } else {
-            const float4 v = reinterpret_cast<const float4*>(gz)[(size_t)level * zstride + k];
-            g[0] = v.x;
-            g[1] = v.y;
-            g[2] = v.z;
-            g[3] = v.w;
-        }
-        int cx, cy, cz, ct;
-        float fx, fy, fz, ft;
-        cell_axis(p.x, res, cx, fx);
-        cell_axis(p.y, res, cy, fy);
-        cell_axis(p.z, res, cz, fz);
-        cell_axis(p.w, res_t, ct, ft);
-        const uint32_t ux = (uint32_t)(cx + bx), uy = (uint32_t)(cy + by);
-        uint32_t txy, tz[2], tt[2];
-        if (dense) {
-            txy = ux + uy * r;
-            tz[0] = (uint32_t)cz * r2;
-            tz[1] = tz[0] + r2;
-            tt[0] = (uint32_t)ct * r3;
-            tt[1] = tt[0] + r3;
-        } else {
-            txy = (ux * kP1) ^ (uy * kP2);
-            tz[0] = (uint32_t)cz * kP3;
-            tz[1] = (uint32_t)(cz + 1) * kP3;
-            tt[0] = (uint32_t)ct * kP4;
-            tt[1] = (uint32_t)(ct + 1) * kP4;
-        }
-        const float wx = bx ? fx : 1.0f - fx, wy = by ? fy : 1.0f - fy;
-        const float sx = bx ? 1.0f : -1.0f, sy = by ? 1.0f : -1.0f;
-        const float wxy = wx * wy;
-        const float wz[2] = {1.0f - fz, fz}, wt[2] = {1.0f - ft, ft};
-        // no gradient at this level: nothing to add, no position term (uniform over the four lanes)
-        bool none = true;
+        level_grad<F>(gz, zstride, level, k, g);
+        scatter_one<F, POS>(xt[i], pos, stride, i, k, level, h, tab, g, zstride, gpos_part, s,
+                            [&](uint32_t idx, float w) {
+                                float wg[F];
 #pragma unroll
-        for (int f = 0; f < F; ++f) none = none && g[f] == 0.0f;
-        if (none) {
-            if (POS && s == 0) gpos_part[(size_t)level * zstride + k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            continue;
-        }
-        float dx = 0.0f, dy = 0.0f, dz = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int bz = k & 1, bt = k >> 1;
-            // a corner of zero time weight has zero weight and zero spatial derivatives
-            if (wt[bt] == 0.0f) continue;
-            const uint32_t idx = (dense ? (txy + tz[bz] + tt[bt]) : (txy ^ tz[bz] ^ tt[bt])) & h.mask;
-            const float w = (wxy * wz[bz]) * wt[bt];
-            if (w != 0.0f) {
-                if constexpr (AGG) {
-                    float wg[F];
-#pragma unroll
-                    for (int f = 0; f < F; ++f) wg[f] = w * g[f];
-                    agg_add<F>(s_key, s_v, idx, wg, gt);
-                } else {
-#pragma unroll
-                    for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, w * g[f]);
-                }
-            }
-            if (POS) {
-                // the entry's features times the level's gradient
-                float tg = 0.0f;
-#pragma unroll
-                for (int f = 0; f < F; f += 2) {
-                    const uint32_t raw = tab[(F / 2) * (size_t)idx + f / 2];
-                    const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw & 0xffffu));
-                    const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> 16));
-                    tg += v0 * g[f] + v1 * g[f + 1];
-                }
-                const float wzt = wz[bz] * wt[bt];
-                dx += tg * (sx * wy) * wzt;
-                dy += tg * (wx * sy) * wzt;
-                dz += tg * wxy * ((bz ? 1.0f : -1.0f) * wt[bt]);
-            }
-        }
-        if (POS) {
-            dx += __shfl_xor(dx, 1, 4);
-            dy += __shfl_xor(dy, 1, 4);
-            dz += __shfl_xor(dz, 1, 4);
-            dx += __shfl_xor(dx, 2, 4);
-            dy += __shfl_xor(dy, 2, 4);
-            dz += __shfl_xor(dz, 2, 4);
-            if (s == 0) {
-                const float sc = (float)(res - 1);
-                const float gx[3] = {dx * sc, dy * sc, dz * sc};
-                const float* mu = pos + i * stride;
-                const float m0 = mu[0], m1 = mu[1], m2 = mu[2];
-                const float nn = sqrtf(m0 * m0 + m1 * m1 + m2 * m2);
-                float out[3];
-                if (nn <= 1.0f) {
-#pragma unroll
-                    for (int k = 0; k < 3; ++k) out[k] = 0.25f * gx[k];
-                } else {
-                    // x~ = c(mu)/4 + 1/2, c = gn mu, gn = 2/n - 1/n^2: J = gn I + (gn'/n) mu mu^T
-                    const float inv = 1.0f / nn;
-                    const float gn = (2.0f - inv) * inv;
-                    const float gp_n = (-2.0f + 2.0f * inv) * inv * inv * inv;
-                    const float md = m0 * gx[0] + m1 * gx[1] + m2 * gx[2];
-                    out[0] = 0.25f * (gn * gx[0] + gp_n * m0 * md);
-                    out[1] = 0.25f * (gn * gx[1] + gp_n * m1 * md);
-                    out[2] = 0.25f * (gn * gx[2] + gp_n * m2 * md);
-                }
-                // this level's share, summed over the levels by pos_reduce_kernel
-                gpos_part[(size_t)level * zstride + k] = make_float4(out[0], out[1], out[2], 0.0f);
-            }
-        }
+                                for (int f = 0; f < F; ++f) wg[f] = w * g[f];
+                                agg_add<F>(s_key, s_v, idx, wg, gt);
+                            });
     }
-    if constexpr (AGG) {
-        __syncthreads();
-        for (int k = threadIdx.x; k < kAggSlots; k += 256) {
-            const uint32_t idx = s_key[k];
-            if (idx != kAggEmpty)
+    __syncthreads();
+    for (int k = threadIdx.x; k < kAggSlots; k += 256) {
+        const uint32_t idx = s_key[k];
+        if (idx != kAggEmpty)
 #pragma unroll
-                for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, s_v[f * kAggSlots + k]);
-        }
+            for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, s_v[f * kAggSlots + k]);
     }
+}
+
+// The fine levels, where a block's Gaussians rarely share a corner, without
+// global float atomics (served far below L2 speed on this chip): the table is
+// cut into buckets of 2^shift entries, and the contributions to a level go
+// as (entry, w g) records into per-bucket runs of the record buffer, each
+// then summed in LDS by one block of bucket_add_kernel.  One launch of each
+// kernel covers a group of fine levels (all of them when their buckets fit
+// kBktGroupBytes), each level with buckets of its own.
+//   bucket_scatter_kernel (kBktRounds x 64 Gaussians of one level per block,
+//     their inputs loaded once for both passes):
+//     pass 1 counts the block's records per bucket in LDS; one global atomic
+//     per bucket then reserves their places in the bucket's run; pass 2
+//     recomputes the same records (the same arithmetic, so the same set) and
+//     writes each at its bucket's reserved start plus its rank from an LDS
+//     counter.  A record past the run's capacity is added to the table with
+//     global float atomics instead (correct, slower; a run holds 5/4 of its
+//     share of 16 corners per Gaussian, so only a skewed table needs it).
+//     With few Gaussians with a gradient (kBktSparse) every contribution is
+//     a direct float atomic and no bucket is used.
+//   bucket_add_kernel (one block per bucket and level): adds the bucket's
+//     records into an LDS copy of its 2^shift entries, then adds that copy to
+//     the table's gradient (one owner per entry: plain read-modify-writes)
+//     and clears the bucket's count for the next group.
+constexpr int kBktRounds = 8;  // rounds of 64 Gaussians per scatter block: 512 Gaussians
+constexpr int kBktMaxBuckets = 4096;
+constexpr int kBktMaxEntries = 4096;
+
+// Entries per bucket (log2) for a table of 2^log2T entries: 2^11, whole
+// tables below that, and at most kBktMaxBuckets buckets.
+int bucket_shift(uint32_t T) {
+    int lg = 0;
+    while ((1u << lg) < T) ++lg;
+    int sh = lg < 11 ? lg : 11;
+    if (lg - sh > 12) sh = lg - 12;
+    return sh;
+}
+
+// Records per bucket run for a chunk of `chunk` Gaussians.
+int64_t bucket_cap(uint32_t T, int64_t chunk) {
+    const int64_t nb = (int64_t)(T >> bucket_shift(T));
+    return (16 * chunk + nb - 1) / nb * 5 / 4 + 256;
+}
+
+// Bytes of one fine level's buckets (counts, entries, values) for a chunk.
+size_t bucket_level_bytes(uint32_t T, int F, int64_t chunk) {
+    const size_t nb = (size_t)(T >> bucket_shift(T));
+    return nb * 4 + nb * (size_t)bucket_cap(T, chunk) * (size_t)(1 + F) * 4;
+}
+
+// Fine levels per bucket launch: all of them, or as many as fit
+// kBktGroupBytes (at least one).
+constexpr size_t kBktGroupBytes = (size_t)2 << 30;
+int bucket_group_levels(const HashLevels& h, int64_t chunk) {
+    int nagg = 0;
+    while (nagg < h.L && h.res_s[nagg] <= kAggMaxRes) ++nagg;
+    const int nfine = h.L - nagg;
+    if (nfine <= 0) return 1;
+    const size_t per = bucket_level_bytes(h.T, h.F, chunk);
+    int g = (int)(kBktGroupBytes / per);
+    if (g < 1) g = 1;
+    return g < nfine ? g : nfine;
+}
+
+struct BucketArgs {
+    uint32_t* count;  // [nb] records per bucket (zero between levels)
+    uint32_t* slot;   // [nb][cap] entry within the bucket
+    float* val;       // [nb][F][cap] w g[f]
+    int64_t cap;
+    int shift;
+    int nb;
+};
+
+// A chunk with at most kBktSparse Gaussians with a gradient adds its few
+// fine-level contributions with direct float atomics (the buckets would cost
+// more than they save); bucket_add_kernel then finds every bucket empty.
+constexpr int64_t kBktSparse = 65536;
+
+// One launch covers a group of consecutive fine levels level0 ... (block b:
+// level level0 + b / nblk), each with its own buckets.
+template <int F, bool POS>
+__global__ void __launch_bounds__(256) bucket_scatter_kernel(const float4* xt, const float* pos, int stride,
+                                                             const uint32_t* list, const uint32_t* count, int nblk,
+                                                             int level0, HashLevels h, const uint32_t* tables,
+                                                             const float* gz, int64_t zstride, float* gtab,
+                                                             float4* gpos_part, BucketArgs bk) {
+    static_assert(F == 2 || F == 4, "two or four features per entry");
+    __shared__ uint32_t s_cnt[kBktMaxBuckets];
+    __shared__ uint32_t s_base[kBktMaxBuckets];
+    const int lg = (int)(blockIdx.x / nblk);  // level within the group
+    const int level = level0 + lg;
+    const int64_t first = (int64_t)(blockIdx.x % nblk) * (64 * kBktRounds);
+    const int64_t n = *count;  // Gaussians with a gradient, compacted
+    const uint32_t* tab = tables + (size_t)level * h.T * (F / 2);
+    float* gt = gtab + (size_t)level * h.T * F;
+    const int s = threadIdx.x & 3, sub = threadIdx.x >> 2;
+    if (n <= kBktSparse) {
+        // few Gaussians: direct atomics, one round of 64 at a time, spread
+        // over all the level's blocks (no barrier on this path)
+        for (int64_t r = blockIdx.x % nblk; r * 64 < n; r += nblk) {
+            const int64_t k = r * 64 + sub;
+            if (k >= n) break;
+            const int64_t i = list[k];
+            float g[F];
+            level_grad<F>(gz, zstride, level, k, g);
+            scatter_one<F, POS>(xt[i], pos, stride, i, k, level, h, tab, g, zstride, gpos_part, s,
+                                [&](uint32_t idx, float w) {
+#pragma unroll
+                                    for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, w * g[f]);
+                                });
+        }
+        return;
+    }
+    if (first >= n) return;  // block-uniform
+    for (int b = threadIdx.x; b < bk.nb; b += 256) s_cnt[b] = 0u;
+    uint32_t* bcount = bk.count + (size_t)lg * bk.nb;
+    uint32_t* bslot = bk.slot + (size_t)lg * bk.nb * bk.cap;
+    float* bval = bk.val + (size_t)lg * bk.nb * F * bk.cap;
+    // the inputs of every round, loaded once (all in flight together) for both passes
+    uint32_t gi[kBktRounds];
+    float4 gp[kBktRounds];
+    float gg[kBktRounds][F];
+#pragma unroll
+    for (int j = 0; j < kBktRounds; ++j) {
+        int64_t k = first + j * 64 + sub;
+        if (k >= n) k = n - 1;  // a clamped round is skipped below
+        gi[j] = list[k];
+    }
+#pragma unroll
+    for (int j = 0; j < kBktRounds; ++j) {
+        const int64_t k = first + j * 64 + sub < n ? first + j * 64 + sub : n - 1;
+        gp[j] = xt[gi[j]];
+        level_grad<F>(gz, zstride, level, k, gg[j]);
+    }
+    __syncthreads();
+    // pass 1: records per bucket
+#pragma unroll
+    for (int j = 0; j < kBktRounds; ++j) {
+        const int64_t k = first + j * 64 + sub;
+        if (k < n)  // uniform across each group of four lanes
+            scatter_one<F, false>(gp[j], pos, stride, gi[j], k, level, h, tab, gg[j], zstride, gpos_part, s,
+                                  [&](uint32_t idx, float) { atomicAdd(&s_cnt[idx >> bk.shift], 1u); });
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < bk.nb; b += 256) {
+        const uint32_t c = s_cnt[b];
+        s_base[b] = c ? atomicAdd(&bcount[b], c) : 0u;
+        s_cnt[b] = 0u;
+    }
+    __syncthreads();
+    // pass 2: the same records, each at its reserved place
+#pragma unroll
+    for (int j = 0; j < kBktRounds; ++j) {
+        const int64_t k = first + j * 64 + sub;
+        if (k < n)
+            scatter_one<F, POS>(gp[j], pos, stride, gi[j], k, level, h, tab, gg[j], zstride, gpos_part, s,
+                                [&](uint32_t idx, float w) {
+                                    const uint32_t b = idx >> bk.shift;
+                                    const uint64_t at = (uint64_t)s_base[b] + atomicAdd(&s_cnt[b], 1u);
+                                    if (at < (uint64_t)bk.cap) {
+                                        bslot[(size_t)b * bk.cap + at] = idx & ((1u << bk.shift) - 1u);
+#pragma unroll
+                                        for (int f = 0; f < F; ++f)
+                                            bval[((size_t)b * F + f) * bk.cap + at] = w * gg[j][f];
+                                    } else {
+#pragma unroll
+                                        for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, w * gg[j][f]);
+                                    }
+                                });
+    }
+}
+
+// kBktAddThreads threads per bucket, kBktAddPer records per thread and step,
+// loaded before any is added.  Block b: bucket b % nb of level level0 + b / nb.
+constexpr int kBktAddThreads = 1024;
+constexpr int kBktAddPer = 8;
+
+template <int F>
+__global__ void __launch_bounds__(kBktAddThreads) bucket_add_kernel(int level0, uint32_t T, float* gtab, BucketArgs bk) {
+    __shared__ float s_acc[F * kBktMaxEntries];
+    const int lg = (int)(blockIdx.x / bk.nb), b = (int)(blockIdx.x % bk.nb);
+    uint32_t* cnt = bk.count + (size_t)lg * bk.nb + b;
+    uint64_t c = *cnt;
+    if (c == 0) return;  // nothing to add (block-uniform; the count stays zero)
+    if (c > (uint64_t)bk.cap) c = (uint64_t)bk.cap;  // the rest went to the table directly
+    const int E = 1 << bk.shift;  // entries per bucket
+    for (int e = threadIdx.x; e < F * E; e += kBktAddThreads) s_acc[e] = 0.0f;
+    __syncthreads();
+    const uint32_t* sl = bk.slot + ((size_t)lg * bk.nb + b) * bk.cap;
+    const float* va = bk.val + ((size_t)lg * bk.nb + b) * F * bk.cap;
+    for (uint64_t r0 = 0; r0 < c; r0 += kBktAddThreads * kBktAddPer) {
+        uint32_t e[kBktAddPer];
+        float v[kBktAddPer][F];
+#pragma unroll
+        for (int u = 0; u < kBktAddPer; ++u) {
+            uint64_t r = r0 + (uint64_t)u * kBktAddThreads + threadIdx.x;
+            if (r >= c) r = c - 1;  // re-reads the last record, not added
+            e[u] = sl[r];
+#pragma unroll
+            for (int f = 0; f < F; ++f) v[u][f] = va[(size_t)f * bk.cap + r];
+        }
+#pragma unroll
+        for (int u = 0; u < kBktAddPer; ++u)
+            if (r0 + (uint64_t)u * kBktAddThreads + threadIdx.x < c)
+#pragma unroll
+                for (int f = 0; f < F; ++f) atomicAdd(&s_acc[f * E + e[u]], v[u][f]);
+    }
+    __syncthreads();
+    float* gt = gtab + ((size_t)(level0 + lg) * T + (size_t)b * E) * F;
+    for (int e = threadIdx.x; e < E; e += kBktAddThreads)
+#pragma unroll
+        for (int f = 0; f < F; ++f) gt[(size_t)e * F + f] += s_acc[f * E + e];
+    if (threadIdx.x == 0) *cnt = 0u;  // every thread read the count before the first barrier
 }
 
 // Position gradient of the active Gaussians: the levels' shares added in level
@@ -1420,6 +1647,13 @@ DecodeBwdLayout decode_bwd_layout(const HashLevels& h, int64_t N) {
     L.partial = take((size_t)kDecodeBwdPartialFloats * sizeof(float));
     L.sort = take(sort_scratch_bytes(chunk));
     L.pos = take((size_t)h.L * chunk * sizeof(float4));
+    // fine-level buckets of one group of levels, reused group after group
+    const int64_t nb = (int64_t)(h.T >> bucket_shift(h.T));
+    const size_t G = (size_t)bucket_group_levels(h, chunk);
+    L.bcap = bucket_cap(h.T, chunk);
+    L.bcount = take(G * nb * 4);
+    L.bslot = take(G * nb * L.bcap * 4);
+    L.bval = take(G * nb * L.bcap * h.F * sizeof(float));
     L.total = off;
     return L;
 }
@@ -1445,6 +1679,18 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     uint32_t* count = reinterpret_cast<uint32_t*>(b.ws + lay.count);
     float* partial = reinterpret_cast<float*>(b.ws + lay.partial);
     float4* pos_partial = reinterpret_cast<float4*>(b.ws + lay.pos);
+    BucketArgs bk;
+    bk.shift = bucket_shift(a.h.T);
+    bk.nb = (int)(a.h.T >> bk.shift);
+    bk.cap = lay.bcap;
+    bk.count = reinterpret_cast<uint32_t*>(b.ws + lay.bcount);
+    bk.slot = reinterpret_cast<uint32_t*>(b.ws + lay.bslot);
+    bk.val = reinterpret_cast<float*>(b.ws + lay.bval);
+    // the bucket counts start at zero (the workspace arrives uninitialised;
+    // bucket_add_kernel leaves them zero after every group)
+    const int bgroup = bucket_group_levels(a.h, lay.chunk);
+    IA_LAUNCH("decode_bwd_fill_kernel", fill_kernel, dim3(blocks_for((int64_t)bgroup * bk.nb, 256, 8192)), dim3(256),
+              0, s, reinterpret_cast<float*>(bk.count), (int64_t)bgroup * bk.nb, (const float*)nullptr);
     MlpBwdArgs m{};
     for (int k = 0; k < 3; ++k) {
         m.W[k] = (const _Float16*)a.W[k];
@@ -1495,34 +1741,49 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
                                     : (m.gelu ? mlp_bwd_kernel<true, 1> : mlp_bwd_kernel<false, 1>);
             IA_LAUNCH("mlp_bwd_kernel", kernel, dim3(kDecodeBwdBlocks), dim3(kBwdThreads), 0, s, m);
         }
-        const int nchunk = (int)((n + 255) / 256), nchunk_agg = (int)((n + 64 * kAggRounds - 1) / (64 * kAggRounds));
+        const int nchunk_agg = (int)((n + 64 * kAggRounds - 1) / (64 * kAggRounds));
+        const int nblk_bkt = (int)((n + 64 * kBktRounds - 1) / (64 * kBktRounds));
         const float* pos = a.pos + off * a.stride;
         float* gpos = b.g_pos ? b.g_pos + off * 3 : nullptr;
-        // levels [0, nagg) combine in LDS first (resolution grows with the level)
+        // levels [0, nagg) combine in LDS first (resolution grows with the level),
+        // the finer ones go through the buckets
         int nagg = 0;
         while (nagg < a.h.L && a.h.res_s[nagg] <= kAggMaxRes) ++nagg;
-        auto scatter = [&](auto pos_t, auto agg_t, int level0, int levels) {
-            constexpr bool P = decltype(pos_t)::value, G = decltype(agg_t)::value;
-            const int nc = G ? nchunk_agg : nchunk;
-            if (levels <= 0) return;
-            if (F == 4) {
-                IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<4, P, G>),
-                          dim3((unsigned)(levels * nc)), dim3(256), 0, s, xt, pos, a.stride, list, count, nc,
-                          level0, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial);
-            } else {
-                IA_LAUNCH(G ? "scatter_agg_kernel" : "scatter_kernel", (scatter_kernel<2, P, G>),
-                          dim3((unsigned)(levels * nc)), dim3(256), 0, s, xt, pos, a.stride, list, count, nc,
-                          level0, a.h, (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial);
+        auto scatter = [&](auto pos_t) {
+            constexpr bool P = decltype(pos_t)::value;
+            if (nagg > 0) {
+                if (F == 4)
+                    IA_LAUNCH("scatter_agg_kernel", (scatter_kernel<4, P>), dim3((unsigned)(nagg * nchunk_agg)),
+                              dim3(256), 0, s, xt, pos, a.stride, list, count, nchunk_agg, 0, a.h,
+                              (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial);
+                else
+                    IA_LAUNCH("scatter_agg_kernel", (scatter_kernel<2, P>), dim3((unsigned)(nagg * nchunk_agg)),
+                              dim3(256), 0, s, xt, pos, a.stride, list, count, nchunk_agg, 0, a.h,
+                              (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial);
+            }
+            for (int level0 = nagg; level0 < a.h.L; level0 += bgroup) {
+                const int g = a.h.L - level0 < bgroup ? a.h.L - level0 : bgroup;
+                if (F == 4) {
+                    IA_LAUNCH("bucket_scatter_kernel", (bucket_scatter_kernel<4, P>), dim3((unsigned)(g * nblk_bkt)),
+                              dim3(256), 0, s, xt, pos, a.stride, list, count, nblk_bkt, level0, a.h,
+                              (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial, bk);
+                    IA_LAUNCH("bucket_add_kernel", bucket_add_kernel<4>, dim3((unsigned)(g * bk.nb)),
+                              dim3(kBktAddThreads), 0, s, level0, a.h.T, b.g_tables, bk);
+                } else {
+                    IA_LAUNCH("bucket_scatter_kernel", (bucket_scatter_kernel<2, P>), dim3((unsigned)(g * nblk_bkt)),
+                              dim3(256), 0, s, xt, pos, a.stride, list, count, nblk_bkt, level0, a.h,
+                              (const uint32_t*)a.tables, gz, chunk, b.g_tables, pos_partial, bk);
+                    IA_LAUNCH("bucket_add_kernel", bucket_add_kernel<2>, dim3((unsigned)(g * bk.nb)),
+                              dim3(kBktAddThreads), 0, s, level0, a.h.T, b.g_tables, bk);
+                }
             }
         };
         if (b.g_pos) {
-            scatter(std::true_type{}, std::true_type{}, 0, nagg);
-            scatter(std::true_type{}, std::false_type{}, nagg, a.h.L - nagg);
+            scatter(std::true_type{});
             IA_LAUNCH("pos_reduce_kernel", pos_reduce_kernel, dim3(blocks_for(n, 256, 4096)), dim3(256), 0, s, list,
                       count, a.h.L, (const float4*)pos_partial, chunk, gpos);
         } else {
-            scatter(std::false_type{}, std::true_type{}, 0, nagg);
-            scatter(std::false_type{}, std::false_type{}, nagg, a.h.L - nagg);
+            scatter(std::false_type{});
         }
     }
     if (first) {  // N = 0: the weight and bias gradients are zero

@@ -481,3 +481,53 @@ def test_paper_decoder_backward_zero_points_and_sparse():
     out = _gpu_backward(D, pos, up)
     _compare("paper sparse", dec, out, ref)
     assert np.all(host(out["pos"])[idle] == 0.0)
+
+
+# Fine-level table gradient through the buckets: above 65,536 Gaussians with a
+# gradient per backward chunk, the levels finer than 640 vertices per axis
+# write (entry, contribution) records into per-bucket runs that one block per
+# bucket sums in LDS; below it they use direct float atomics.  These cases
+# cross that threshold and compare with the oracle's fp64 gradients.
+
+def test_bucketed_fine_levels_match_oracle():
+    """100,000 points at general times (all 16 corners weighted) and edge
+    positions, two features per entry, 2^19-entry tables (256 buckets of
+    2,048 entries per fine level)."""
+    dec = S.single_decoder()
+    rng = np.random.default_rng(91)
+    n = 100_000
+    pos = _edge_xyzt(rng, n)
+    up = _upstream(rng, n)
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare("bucketed xyzt", dec, out, ref)
+
+
+def test_bucketed_fine_levels_paper_decoder_match_oracle():
+    """The per-attribute decoder (four features per entry) with 70,000 points
+    and 2^17-entry tables (64 buckets per fine level)."""
+    dec = S.paper_decoder(log2T=17, sh=False)
+    rng = np.random.default_rng(92)
+    n = 70_000
+    pos = _edge_xyzt(rng, n)
+    up = _upstream_paper(rng, n, False)
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare("bucketed paper", dec, out, ref)
+
+
+def test_bucket_overflow_goes_to_the_table_directly():
+    """80,000 points on six distinct positions: each fine level's records all
+    fall into a few buckets, far beyond a bucket's capacity (5/4 of an even
+    share), so most of them take the direct-atomic fallback; the gradients
+    still match the oracle."""
+    dec = S.single_decoder()
+    rng = np.random.default_rng(93)
+    n = 80_000
+    base = _edge_xyzt(rng, 6)
+    base[:, 3] = np.float32([0.2, 0.4, 0.6, 0.8, 0.3, 0.7])
+    pos = base[rng.integers(0, 6, n)]
+    up = _upstream(rng, n)
+    ref = O.decode_grad(dec, pos.astype(np.float64), mode=3, grads=up)
+    out = _gpu_backward(Decoder(dec), pos, up)
+    _compare("bucket overflow", dec, out, ref)
