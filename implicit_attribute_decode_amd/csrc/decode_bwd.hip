@@ -1157,7 +1157,8 @@ __global__ void __launch_bounds__(256) scatter_kernel(const float4* xt, const fl
 // The fine levels, where a block's Gaussians rarely share a corner, without
 // global float atomics (served far below L2 speed on this chip): the table is
 // cut into buckets of 2^shift entries, and the contributions to a level go
-// as (entry, w g) records into per-bucket runs of the record buffer, each
+// as (entry, w g) records (1 + F consecutive words) into per-bucket runs of
+// the record buffer, each
 // then summed in LDS by one block of bucket_add_kernel.  One launch of each
 // kernel covers a group of fine levels (all of them when their buckets fit
 // kBktGroupBytes), each level with buckets of its own.
@@ -1217,9 +1218,8 @@ int bucket_group_levels(const HashLevels& h, int64_t chunk) {
 }
 
 struct BucketArgs {
-    uint32_t* count;  // [nb] records per bucket (zero between levels)
-    uint32_t* slot;   // [nb][cap] entry within the bucket
-    float* val;       // [nb][F][cap] w g[f]
+    uint32_t* count;  // [levels][nb] records per bucket (zero between groups)
+    uint32_t* rec;    // [levels][nb][cap] records of 1 + F words: entry within the bucket, w g[f] (fp32 bits)
     int64_t cap;
     int shift;
     int nb;
@@ -1268,8 +1268,7 @@ __global__ void __launch_bounds__(256) bucket_scatter_kernel(const float4* xt, c
     if (first >= n) return;  // block-uniform
     for (int b = threadIdx.x; b < bk.nb; b += 256) s_cnt[b] = 0u;
     uint32_t* bcount = bk.count + (size_t)lg * bk.nb;
-    uint32_t* bslot = bk.slot + (size_t)lg * bk.nb * bk.cap;
-    float* bval = bk.val + (size_t)lg * bk.nb * F * bk.cap;
+    uint32_t* brec = bk.rec + (size_t)lg * bk.nb * bk.cap * (1 + F);
     // the inputs of every round, loaded once (all in flight together) for both passes
     uint32_t gi[kBktRounds];
     float4 gp[kBktRounds];
@@ -1312,10 +1311,11 @@ __global__ void __launch_bounds__(256) bucket_scatter_kernel(const float4* xt, c
                                     const uint32_t b = idx >> bk.shift;
                                     const uint64_t at = (uint64_t)s_base[b] + atomicAdd(&s_cnt[b], 1u);
                                     if (at < (uint64_t)bk.cap) {
-                                        bslot[(size_t)b * bk.cap + at] = idx & ((1u << bk.shift) - 1u);
+                                        // one record: consecutive words, written together
+                                        uint32_t* rp = brec + ((size_t)b * bk.cap + at) * (1 + F);
+                                        rp[0] = idx & ((1u << bk.shift) - 1u);
 #pragma unroll
-                                        for (int f = 0; f < F; ++f)
-                                            bval[((size_t)b * F + f) * bk.cap + at] = w * gg[j][f];
+                                        for (int f = 0; f < F; ++f) rp[1 + f] = __float_as_uint(w * gg[j][f]);
                                     } else {
 #pragma unroll
                                         for (int f = 0; f < F; ++f) atomicAdd(gt + F * (size_t)idx + f, w * gg[j][f]);
@@ -1340,8 +1340,7 @@ __global__ void __launch_bounds__(kBktAddThreads) bucket_add_kernel(int level0, 
     const int E = 1 << bk.shift;  // entries per bucket
     for (int e = threadIdx.x; e < F * E; e += kBktAddThreads) s_acc[e] = 0.0f;
     __syncthreads();
-    const uint32_t* sl = bk.slot + ((size_t)lg * bk.nb + b) * bk.cap;
-    const float* va = bk.val + ((size_t)lg * bk.nb + b) * F * bk.cap;
+    const uint32_t* rb = bk.rec + ((size_t)lg * bk.nb + b) * bk.cap * (1 + F);
     for (uint64_t r0 = 0; r0 < c; r0 += kBktAddThreads * kBktAddPer) {
         uint32_t e[kBktAddPer];
         float v[kBktAddPer][F];
@@ -1349,9 +1348,10 @@ __global__ void __launch_bounds__(kBktAddThreads) bucket_add_kernel(int level0, 
         for (int u = 0; u < kBktAddPer; ++u) {
             uint64_t r = r0 + (uint64_t)u * kBktAddThreads + threadIdx.x;
             if (r >= c) r = c - 1;  // re-reads the last record, not added
-            e[u] = sl[r];
+            const uint32_t* rp = rb + r * (1 + F);
+            e[u] = rp[0];
 #pragma unroll
-            for (int f = 0; f < F; ++f) v[u][f] = va[(size_t)f * bk.cap + r];
+            for (int f = 0; f < F; ++f) v[u][f] = __uint_as_float(rp[1 + f]);
         }
 #pragma unroll
         for (int u = 0; u < kBktAddPer; ++u)
@@ -1652,8 +1652,7 @@ DecodeBwdLayout decode_bwd_layout(const HashLevels& h, int64_t N) {
     const size_t G = (size_t)bucket_group_levels(h, chunk);
     L.bcap = bucket_cap(h.T, chunk);
     L.bcount = take(G * nb * 4);
-    L.bslot = take(G * nb * L.bcap * 4);
-    L.bval = take(G * nb * L.bcap * h.F * sizeof(float));
+    L.brec = take(G * nb * L.bcap * (1 + h.F) * 4);
     L.total = off;
     return L;
 }
@@ -1684,8 +1683,7 @@ hipError_t launch_decode_backward(const DecodeBwdArgs& b, hipStream_t s) {
     bk.nb = (int)(a.h.T >> bk.shift);
     bk.cap = lay.bcap;
     bk.count = reinterpret_cast<uint32_t*>(b.ws + lay.bcount);
-    bk.slot = reinterpret_cast<uint32_t*>(b.ws + lay.bslot);
-    bk.val = reinterpret_cast<float*>(b.ws + lay.bval);
+    bk.rec = reinterpret_cast<uint32_t*>(b.ws + lay.brec);
     // the bucket counts start at zero (the workspace arrives uninitialised;
     // bucket_add_kernel leaves them zero after every group)
     const int bgroup = bucket_group_levels(a.h, lay.chunk);

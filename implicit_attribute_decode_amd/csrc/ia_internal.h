@@ -131,7 +131,7 @@ constexpr int64_t kDecodeBwdPartialFloats = ((int64_t)kDecodeBwdBlocks * 4 + kDe
 // normalised positions, the weight-gradient partials, the spatial sort's
 // buffers and the per-level position shares [L][chunk] float4.
 struct DecodeBwdLayout {
-    size_t z, gz, list, boff, count, xt, partial, sort, pos, bcount, bslot, bval, total;
+    size_t z, gz, list, boff, count, xt, partial, sort, pos, bcount, brec, total;
     int64_t chunk;
     int64_t bcap;  // records per fine-level bucket
 };
