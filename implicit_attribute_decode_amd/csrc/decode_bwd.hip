@@ -957,7 +957,7 @@ constexpr int kAggBits = 11;
 constexpr int kAggSlots = 1 << kAggBits;
 constexpr int kAggProbes = 8;
 constexpr uint32_t kAggEmpty = 0xffffffffu;  // table indices are < 2^24
-constexpr int kAggMaxRes = 640;
+constexpr int kAggMaxRes = 300;  // with the finer levels in buckets: 640 and 200 measured slower
 // rounds of 64 Gaussians per combining block: 384 Gaussians share one
 // 2048-slot LDS table (24 KiB, six blocks per CU); 768 Gaussians on 4096
 // slots, 512 or 768 on 2048, and 192 on 1024 measured slower

@@ -248,7 +248,7 @@ typedef struct {
  * encoding, its gradient, the chunk's active list and spatial sort, the
  * normalised positions and the per-level position shares (484 bytes per
  * Gaussian at L = 16, F = 2; 676 at F = 4), plus 60 MB of weight-gradient
- * partials, plus the table-gradient buckets of the levels finer than 640
+ * partials, plus the table-gradient buckets of the levels finer than 300
  * vertices per axis: per such level 20 (entry, value) records per Gaussian
  * of the chunk, 4 (1 + F) bytes each (240 bytes at F = 2), for as many of
  * those levels at a time as fit 2 GiB (at least one).

@@ -484,7 +484,7 @@ def test_paper_decoder_backward_zero_points_and_sparse():
 
 
 # Fine-level table gradient through the buckets: above 65,536 Gaussians with a
-# gradient per backward chunk, the levels finer than 640 vertices per axis
+# gradient per backward chunk, the levels finer than 300 vertices per axis
 # write (entry, contribution) records into per-bucket runs that one block per
 # bucket sums in LDS; below it they use direct float atomics.  These cases
 # cross that threshold and compare with the oracle's fp64 gradients.
@@ -492,7 +492,7 @@ def test_paper_decoder_backward_zero_points_and_sparse():
 def test_bucketed_fine_levels_match_oracle():
     """100,000 points at general times (all 16 corners weighted) and edge
     positions, two features per entry, 2^19-entry tables (256 buckets of
-    2,048 entries per fine level)."""
+    2,048 entries per level finer than 300 vertices per axis)."""
     dec = S.single_decoder()
     rng = np.random.default_rng(91)
     n = 100_000
